@@ -1,0 +1,82 @@
+"""NF4-quantized frozen linear layer with a LoRA adapter: forward and backward (oracle).
+
+What is computed follows the problem the pages state: the base is frozen and
+4-bit, read block by block, and only the adapters are trained; the backward
+"propagates gradients only to the adapters and block inputs", frozen weights
+are never differentiated ("Poros" research post, the paragraph describing the
+training step; package README, "How it works").
+
+Readings (the pages give only r and alpha -- rank 16, alpha 32 in the README
+"Quickstart" and the A100 "Configuration" table -- and say dropout exists):
+  * y  = x W^T + b + s * (drop(x) A^T) B^T, with s = alpha / r (standard LoRA
+    scaling), dropout on the LoRA input only (inverted dropout, see philox.py)
+  * u  = drop(x) A^T                       (saved for the backward)
+  * du = s * dy B
+  * dB = s * dy^T u
+  * dA = du^T drop(x)
+  * dx = dy W + sigma * keep (.) (du A)
+  * no gradient for W, its absmax, or the bias (frozen).
+W here is the dequantized NF4 matrix.  All contractions run in float64 on
+exactly-represented inputs (bf16 x, fp32 A and B, bf16 dequantized W).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import nf4, philox
+
+
+@dataclass(frozen=True)
+class RngKey:
+    seed: int = 0
+    step: int = 0
+    micro: int = 0
+    layer: int = 0
+    proj: int = 0
+
+
+def lora_input(x: np.ndarray, p: float, key: RngKey) -> np.ndarray:
+    """drop(x) = keep (.) x * sigma in float64."""
+    T, K = x.shape
+    keep = philox.keep_mask(T, K, p, key.seed, key.layer, key.proj, key.step, key.micro)
+    sigma = float(philox.drop_scale(p))
+    return np.where(keep, x.astype(np.float64) * sigma, 0.0), keep, sigma
+
+
+def fwd(x: np.ndarray, codes: np.ndarray, absmax: np.ndarray, bias: Optional[np.ndarray],
+        A: np.ndarray, B: np.ndarray, alpha: float, p: float, key: RngKey):
+    """Returns (y, u) in float64.  r = A.shape[0]; r = 0 means base only."""
+    W = nf4.dequantize(codes, absmax).astype(np.float64)
+    y = x.astype(np.float64) @ W.T
+    if bias is not None:
+        y = y + bias.astype(np.float64)[None, :]
+    r = A.shape[0]
+    if r == 0:
+        return y, np.zeros((x.shape[0], 0))
+    s = alpha / r
+    h, _, _ = lora_input(x, p, key)
+    u = h @ A.astype(np.float64).T
+    y = y + s * (u @ B.astype(np.float64).T)
+    return y, u
+
+
+def bwd(dy: np.ndarray, x: np.ndarray, codes: np.ndarray, absmax: np.ndarray,
+        A: np.ndarray, B: np.ndarray, alpha: float, p: float, key: RngKey):
+    """Returns (dx, dA, dB) in float64, replaying the forward's mask from the key."""
+    W = nf4.dequantize(codes, absmax).astype(np.float64)
+    dy64 = dy.astype(np.float64)
+    dx = dy64 @ W
+    r = A.shape[0]
+    if r == 0:
+        return dx, np.zeros((0, x.shape[1])), np.zeros((W.shape[0], 0))
+    s = alpha / r
+    h, keep, sigma = lora_input(x, p, key)
+    u = h @ A.astype(np.float64).T
+    du = s * (dy64 @ B.astype(np.float64))
+    dB = s * (dy64.T @ u)
+    dA = du.T @ h
+    dx = dx + sigma * np.where(keep, du @ A.astype(np.float64), 0.0)
+    return dx, dA, dB

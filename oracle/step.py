@@ -1,0 +1,93 @@
+"""One training step of the Qwen2.5-shaped stack (oracle).
+
+The step the pages describe ("Poros" research post, the paragraph on the
+training step): the forward runs the blocks in order keeping activations at
+block boundaries; the backward walks the blocks in reverse, recomputes each
+block's forward with the restored RNG, and propagates gradients to the adapters
+and block inputs only; then one optimizer step, identical to a resident run's.
+The learning problem is unchanged by streaming (same paragraph group: same
+attention kernels, optimizer, LoRA configuration, data order, loss).
+
+Readings (the pages name none of these):
+  * frozen bf16 token embedding and untied lm_head, neither quantized nor
+    adapted; a final RMSNorm (eps 1e-6) before the lm_head
+  * loss = mean next-token cross-entropy over the T-1 positions that have a
+    target
+  * global gradient norm over all adapter gradients, float64
+  * AdamW with decoupled weight decay and bias correction (Loshchilov and
+    Hutter, "Decoupled Weight Decay Regularization", ICLR 2019):
+    lr 2e-4, betas (0.9, 0.999), eps 1e-8, weight decay 0.01, constant
+    schedule, no clipping.
+
+Parity status: the loss of a random-weight stack has no printed value on the
+pages, so this composition is parity unpinned against absolute values; its
+parts are pinned individually and the whole is pinned by finite differences.
+"""
+from __future__ import annotations
+
+from typing import Dict, List
+
+import numpy as np
+
+from . import block, lora
+
+LR, BETA1, BETA2, ADAM_EPS, WD = 2e-4, 0.9, 0.999, 1e-8, 0.01
+
+
+def loss_and_dlogits(logits: np.ndarray, tokens: np.ndarray):
+    """Mean CE over positions 0..T-2 predicting tokens[1..T-1]."""
+    T = logits.shape[0]
+    z = logits[:-1]
+    tgt = tokens[1:]
+    zmax = z.max(axis=1, keepdims=True)
+    lse = zmax[:, 0] + np.log(np.exp(z - zmax).sum(axis=1))
+    loss = float(np.mean(lse - z[np.arange(T - 1), tgt]))
+    P = np.exp(z - lse[:, None])
+    P[np.arange(T - 1), tgt] -= 1.0
+    d = np.zeros_like(logits)
+    d[:-1] = P / (T - 1)
+    return loss, d
+
+
+def forward_backward(layers: List[Dict[str, object]], glob: Dict[str, np.ndarray],
+                     toks: np.ndarray, shape, alpha: float, p: float, seed: int, step: int,
+                     micro: int = 0):
+    """Returns (loss, grads[layer][proj] = (dA, dB)).  layers hold quantized params."""
+    rk = lora.RngKey(seed=seed, step=step, micro=micro)
+    h = glob["emb"][toks].astype(np.float64)
+    bounds = []
+    for li, qp in enumerate(layers):
+        bounds.append(h)
+        h, _ = block.forward(h, qp, shape, li, alpha, p, rk)
+    hn, rinv = block.rmsnorm(h, glob["lnf"].astype(np.float64))
+    logits = hn @ glob["lm"].astype(np.float64).T
+    loss, dlog = loss_and_dlogits(logits, toks)
+    dhn = dlog @ glob["lm"].astype(np.float64)
+    dh = block.rmsnorm_bwd(h, glob["lnf"].astype(np.float64), rinv, dhn)
+    grads: List[Dict[str, tuple]] = [None] * len(layers)
+    for li in reversed(range(len(layers))):
+        qp = layers[li]
+        _, cache = block.forward(bounds[li], qp, shape, li, alpha, p, rk)  # recompute
+        dh, grads[li] = block.backward(dh, cache, qp, shape, li, alpha, p, rk)
+    return loss, grads
+
+
+def grad_norm(grads) -> float:
+    s = 0.0
+    for g in grads:
+        for proj in block.PROJS:
+            dA, dB = g[proj]
+            s += float(np.sum(dA.astype(np.float64) ** 2) + np.sum(dB.astype(np.float64) ** 2))
+    return float(np.sqrt(s))
+
+
+def adamw(param: np.ndarray, grad: np.ndarray, m: np.ndarray, v: np.ndarray, t: int,
+          lr: float = LR, b1: float = BETA1, b2: float = BETA2, eps: float = ADAM_EPS,
+          wd: float = WD):
+    """One AdamW update (t counts from 1); float64; returns (param, m, v)."""
+    param = param.astype(np.float64) * (1.0 - lr * wd)
+    m = b1 * m + (1.0 - b1) * grad
+    v = b2 * v + (1.0 - b2) * grad * grad
+    mhat = m / (1.0 - b1 ** t)
+    vhat = v / (1.0 - b2 ** t)
+    return param - lr * mhat / (np.sqrt(vhat) + eps), m, v
