@@ -1,0 +1,230 @@
+/*
+ * msq.h -- C ABI of the MI355X (gfx950) streamed NF4 + LoRA training hot path.
+ *
+ * The operations follow the problem the source pages state: a frozen, 4-bit
+ * (NF4) base is read block by block while only LoRA adapters are trained; the
+ * backward reloads each block, recomputes its forward with the same dropout
+ * masks and differentiates only the adapters and the block input ("Poros"
+ * research post, the paragraphs on streamed residency, RNG state capture and
+ * the training step; package README, "How it works").
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are device pointers unless a comment says "host".
+ *   - bf16 tensors are passed as uint16_t bit patterns; all matrices are dense
+ *     row-major with no padding between rows.
+ *   - msq_stream_t is a hipStream_t (NULL = the legacy null stream).  Every
+ *     compute call is asynchronous on the stream it is given and never
+ *     synchronises the host.
+ *   - The caller owns all device memory (inputs, outputs, workspaces, the
+ *     window arena); the library allocates no device memory.
+ *   - Every function returns 0 on success or a negative MSQ_E_* code.  All
+ *     arguments are validated on the host before any HIP call, so an invalid
+ *     call launches nothing and leaves outputs untouched.  msq_last_error()
+ *     returns a thread-local description of the most recent failure.
+ *   - Results are deterministic: tiling and reduction order depend only on the
+ *     shapes and on r, never on pointers, alignment, timing or free memory, and
+ *     no kernel uses floating-point atomics.  Identical calls on identical bytes
+ *     give identical bytes, wherever the operands live (this is what makes a
+ *     streamed run bit-identical to a resident one).
+ */
+#ifndef MSQ_H
+#define MSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSQ_ABI_VERSION 1
+
+typedef void* msq_stream_t; /* hipStream_t */
+
+enum {
+  MSQ_OK = 0,
+  MSQ_E_INVAL = -1,     /* null pointer, negative size, misaligned pointer, bad flag */
+  MSQ_E_SHAPE = -2,     /* k % 64 != 0, n % 64 != 0, r outside [0, 64], t*k too large */
+  MSQ_E_DROPOUT = -3,   /* p_drop outside [0, 1), or alpha not finite */
+  MSQ_E_WORKSPACE = -4, /* workspace smaller than nf4_lora_workspace_size() */
+  MSQ_E_WINDOW = -5,    /* arena cannot hold two windows; message names the largest
+                           window_blocks that fits */
+  MSQ_E_ORDER = -6,     /* window protocol violated (acquire before prefetch,
+                           prefetch with no free slot, release of a slot not held) */
+  MSQ_E_HIP = -7        /* a HIP runtime call failed; msq_last_error() has its text */
+};
+
+/* ABI version of the loaded library (MSQ_ABI_VERSION). */
+int msq_abi_version(void);
+/* Static description of an error code. */
+const char* msq_strerror(int code);
+/* Thread-local text of the most recent error raised on this thread ("" if none). */
+const char* msq_last_error(void);
+
+/* Host-only: the 16 NF4 levels (ascending, fp32) the kernels use.  out: host,
+ * 16 floats.  The levels are computed by the library itself from the NormalFloat
+ * construction (8 positive and 7 negative normal quantiles plus an exact zero,
+ * normalised to [-1, 1]).  Never touches the GPU. */
+int msq_nf4_codebook(float* out);
+
+/* ------------------------------------------------------------------------- */
+/* NF4 quantization of the frozen base.
+ * The pages name the base format (NF4 via bitsandbytes: "Limitations", "What
+ * 0.00e+00 means"; A100 results, "Configuration") but not its parameters; this
+ * ABI fixes them: blocks of 64 consecutive elements of the row-major matrix,
+ * one fp32 absmax per block, code = nearest level of w/absmax decided exactly
+ * (ties to the lower code; an all-zero block stores absmax 0 and code 7),
+ * two codes per byte with the even element in the high nibble.
+ *
+ *   w      [n, k] bf16, finite values (non-finite input gives unspecified codes)
+ *   codes  [n, k/2] uint8  (output), 16-byte aligned
+ *   absmax [n, k/64] fp32  (output), 4-byte aligned
+ * Requires n >= 0, k % 64 == 0, w 16-byte aligned.  n == 0 is a no-op (pointers
+ * may then be NULL). */
+int nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* absmax,
+                 msq_stream_t stream);
+
+/* Dequantization to bf16: w[i] = bf16_rne(fp32(level[code_i] * absmax_block)).
+ * Same layouts and requirements as nf4_quantize; w is the output. */
+int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t n, int64_t k, uint16_t* w,
+                   msq_stream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Dropout key.  The mask of one projection's LoRA input element (t, kk), with
+ * e = t*k + kk, is word (e & 3) of Philox4x32-10 (Salmon et al., SC'11) at
+ *   counter (e >> 2, (layer << 4) | proj, step, micro), key (seed lo32, seed hi32);
+ * the element is kept iff word >= floor(p_drop * 2^32), and kept elements are
+ * scaled by fp32(1 / fp32(1 - p_drop)).  Replaces the pages' RNG snapshot and
+ * restore ("Poros" research post, RNG state capture): the same key replays the
+ * same mask in the recompute.  proj: q 0, k 1, v 2, o 3, gate 4, up 5, down 6. */
+typedef struct {
+  uint64_t seed;
+  uint32_t step;
+  uint32_t micro;
+  uint32_t layer;
+  uint32_t proj; /* < 16 */
+} msq_rng_key;
+
+/* LoRA adapter configuration: scaling s = alpha / r; r == 0 means base only
+ * (A, B, u are ignored and may be NULL). */
+typedef struct {
+  int32_t r;     /* 0 .. 64 */
+  float alpha;
+  float p_drop;  /* dropout probability on the LoRA input, in [0, 1) */
+} msq_lora_cfg;
+
+/* Bytes of scratch device memory one nf4_lora_fwd or nf4_lora_bwd call with
+ * these shapes needs (split reduction partials, u/du staging).  Depends only on
+ * the shapes.  Returns 0 for invalid shapes. */
+size_t nf4_lora_workspace_size(int64_t t, int64_t k, int64_t n, int32_t r);
+
+/* Fused forward of one NF4 frozen linear with a LoRA adapter:
+ *   u = drop(x) A^T                   (fp32, written to u_out when non-NULL)
+ *   y = x W^T + bias + (alpha/r) u B^T
+ * where W is the dequantized NF4 matrix [n, k] (dequantized in-tile, never
+ * materialised).
+ *   x      [t, k] bf16, 16-byte aligned            t >= 0, k % 64 == 0
+ *   codes  [n, k/2] uint8, absmax [n, k/64] fp32     n % 64 == 0
+ *   bias   [n] bf16 or NULL
+ *   A      [r, k] fp32, B [n, r] fp32  (16-byte aligned)
+ *   y      [t, n] bf16 output (16-byte aligned)
+ *   u_out  [t, r] fp32 output or NULL
+ *   workspace: device scratch of at least nf4_lora_workspace_size(t, k, n, r)
+ *   bytes, 256-byte aligned; contents on entry are ignored.
+ * t == 0 is a no-op (x, y may then be NULL).  t * k must stay below 2^34 (dropout
+ * counter range) and t at most 65535. */
+int nf4_lora_fwd(const uint16_t* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
+                 const float* absmax, const uint16_t* bias, const float* A, const float* B,
+                 msq_lora_cfg cfg, msq_rng_key key, uint16_t* y, float* u_out, void* workspace,
+                 size_t workspace_bytes, msq_stream_t stream);
+
+/* Fused backward of the same layer (no gradient for W, absmax or bias: frozen).
+ *   du = s dy B                       (s = alpha / r)
+ *   dB = s dy^T u
+ *   dA = du^T drop(x)                 (mask replayed from key)
+ *   dx = dy W + sigma * keep (.) (du A)
+ *   dy [t, n] bf16, x [t, k] bf16 (the forward's input)
+ *   u  [t, r] fp32 from the forward (or recompute), or NULL to recompute it here
+ *   dx [t, k] bf16 output; dx_accumulate = 1 adds into the existing dx (in fp32,
+ *      one rounding to bf16), 0 overwrites
+ *   dA [r, k] fp32, dB [n, r] fp32 outputs; dAB_accumulate = 1 adds into them
+ *   dA/dB may be NULL only when r == 0.  With t == 0, dy, x and dx may be NULL and dA,
+ *   dB are set to zero (or left unchanged when accumulating).
+ * Shapes, alignment and workspace as for nf4_lora_fwd. */
+int nf4_lora_bwd(const uint16_t* dy, const uint16_t* x, int64_t t, int64_t k, int64_t n,
+                 const uint8_t* codes, const float* absmax, const float* A, const float* B,
+                 msq_lora_cfg cfg, msq_rng_key key, const float* u, uint16_t* dx,
+                 int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
+                 size_t workspace_bytes, msq_stream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Host-to-device block-prefetch window.
+ * The pages: the forward streams frozen blocks through a small GPU window with
+ * asynchronous prefetch on side streams, the backward reloads each block in
+ * reverse, and eviction is a pointer release because the base is read-only
+ * ("Poros" research post, the training-step paragraph; "Limitations",
+ * "Pretraining is out of scope"; README, "How it works").
+ *
+ * A window groups window_blocks consecutive layers; the caller's device arena
+ * is split into two slots of one window each (double buffering).  Layer blobs
+ * live in pinned host memory (hipHostMalloc or equivalent) and are copied with
+ * hipMemcpyAsync on copy_stream.  Each layer's device address is its offset in
+ * the slot (blob offsets rounded up to 256 bytes).  The window object owns only
+ * events and bookkeeping; it is not thread-safe.
+ *
+ *   host_blobs  host array of n_layers pointers to pinned host memory
+ *   blob_bytes  host array of n_layers sizes
+ *   dev_arena   caller-owned device memory, 256-byte aligned, arena_bytes long;
+ *               needs at least block_stream_arena_bytes(...) bytes, else
+ *               MSQ_E_WINDOW (the message names the largest window that fits).
+ * The arrays are copied; the blobs and the arena must outlive the window. */
+typedef struct msq_window msq_window;
+
+typedef struct {
+  uint64_t bytes_copied;    /* host-to-device bytes issued */
+  uint64_t windows_copied;  /* window loads that issued copies */
+  uint64_t windows_reused;  /* prefetches satisfied by a slot that still held the window */
+} msq_window_stats;
+
+size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks);
+int block_stream_create(msq_window** out, const void* const* host_blobs, const size_t* blob_bytes,
+                        int n_layers, int window_blocks, void* dev_arena, size_t arena_bytes,
+                        msq_stream_t copy_stream);
+/* Start loading the window that begins at first_layer (a multiple of
+ * window_blocks) into the free slot: the copy stream first waits until the
+ * compute stream released that slot, then copies, then marks it ready.  If a
+ * free slot still holds this window's bytes, no copy is issued.  No free slot:
+ * MSQ_E_ORDER. */
+int block_stream_prefetch(msq_window* w, int first_layer);
+/* Make `compute` wait until the window holding `layer` has arrived, and return
+ * the layer's device address.  Window not prefetched: MSQ_E_ORDER. */
+int block_stream_acquire(msq_window* w, int layer, msq_stream_t compute, const void** dev_blob);
+/* Mark the window beginning at first_layer as no longer read by work queued so
+ * far on `compute`; its slot may then be refilled.  Not held: MSQ_E_ORDER. */
+int block_stream_release(msq_window* w, int first_layer, msq_stream_t compute);
+int block_stream_stats(const msq_window* w, msq_window_stats* out);
+/* Waits for the window's outstanding copies, then frees its events. */
+int block_stream_destroy(msq_window* w);
+
+/* ------------------------------------------------------------------------- */
+/* Kernel timing (measurement support).  When enabled, the library brackets
+ * each launch of its dense dequant-MFMA kernels with HIP events on the launch
+ * stream.  msq_timing_collect waits for the recorded events and aggregates, per
+ * kernel name, the launch count, total milliseconds and total algorithmic
+ * flops (2*t*k*n per launch).  Host-side bookkeeping only. */
+typedef struct {
+  char name[48];
+  uint64_t launches;
+  double total_ms;
+  double total_flops;
+} msq_kernel_timing;
+
+int msq_timing_enable(int on);
+/* Fills up to max entries; *n_out = number of kernel names seen.  Resets. */
+int msq_timing_collect(msq_kernel_timing* out, int max, int* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSQ_H */

@@ -1,0 +1,239 @@
+// C-ABI entry points of libmsq: host-side validation, workspace planning and the
+// launch sequence of each call.  Every check happens before the first HIP call, so
+// an invalid call launches nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/msq.h"
+#include "internal.hpp"
+
+namespace msq {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int64_t MAX_T = 65535;          // grid y limit of the epilogue launches
+constexpr int64_t MAX_ELEMS = 1LL << 34;  // t*k: dropout counter word 0 holds e >> 2
+
+Dropout make_dropout(const msq_rng_key& key, float p) {
+  Dropout d;
+  d.k0 = (uint32_t)(key.seed & 0xffffffffu);
+  d.k1 = (uint32_t)(key.seed >> 32);
+  d.c1 = (key.layer << 4) | key.proj;
+  d.c2 = key.step;
+  d.c3 = key.micro;
+  d.threshold = (uint32_t)floor((double)p * 4294967296.0);
+  const float one_minus = 1.0f - p;
+  d.sigma = 1.0f / one_minus;
+  return d;
+}
+
+Dropout no_dropout() {
+  Dropout d;
+  memset(&d, 0, sizeof(d));
+  d.sigma = 1.0f;
+  return d;
+}
+
+int check_linear(const char* fn, int64_t t, int64_t k, int64_t n, const msq_lora_cfg& cfg,
+                 const msq_rng_key& key) {
+  if (t < 0 || k <= 0 || n <= 0) return set_error(MSQ_E_INVAL, "%s: t=%lld k=%lld n=%lld must be t>=0, k>0, n>0", fn, (long long)t, (long long)k, (long long)n);
+  if (k % 64 || n % 64) return set_error(MSQ_E_SHAPE, "%s: k=%lld and n=%lld must be multiples of 64", fn, (long long)k, (long long)n);
+  if (cfg.r < 0 || cfg.r > 64) return set_error(MSQ_E_SHAPE, "%s: r=%d outside [0, 64]", fn, cfg.r);
+  if (t > MAX_T) return set_error(MSQ_E_SHAPE, "%s: t=%lld exceeds %lld", fn, (long long)t, (long long)MAX_T);
+  if (t * k >= MAX_ELEMS || t * n >= MAX_ELEMS) return set_error(MSQ_E_SHAPE, "%s: t*k or t*n reaches 2^34", fn);
+  if (!(cfg.p_drop >= 0.0f && cfg.p_drop < 1.0f)) return set_error(MSQ_E_DROPOUT, "%s: p_drop=%g outside [0, 1)", fn, (double)cfg.p_drop);
+  if (cfg.r > 0 && !isfinite(cfg.alpha)) return set_error(MSQ_E_DROPOUT, "%s: alpha is not finite", fn);
+  if (key.proj >= 16 || key.layer >= (1u << 28)) return set_error(MSQ_E_INVAL, "%s: rng key proj must be < 16 and layer < 2^28", fn);
+  return MSQ_OK;
+}
+
+}  // namespace
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_error(hipError_t e, const char* what) {
+  return set_error(MSQ_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
+  LoraPlan p;
+  p.fwd = gemm_plan(t, n, k);
+  p.bwd = gemm_plan(t, k, n);
+  const size_t tr = (size_t)t * (size_t)r * sizeof(float);
+  size_t o = 0;
+  p.off_part_fwd = o;
+  o = align256(o + (size_t)p.fwd.splits * t * n * sizeof(float));
+  p.off_u_fwd = o;
+  o = align256(o + tr);
+  p.fwd_bytes = o;
+  p.nch = (int)((t + COLGRAD_TCHUNK - 1) / COLGRAD_TCHUNK);
+  o = 0;
+  p.off_part_bwd = o;
+  o = align256(o + (size_t)p.bwd.splits * t * k * sizeof(float));
+  p.off_u_bwd = o;
+  o = align256(o + tr);
+  p.off_du = o;
+  o = align256(o + tr);
+  p.off_pa = o;
+  o = align256(o + (size_t)p.nch * r * k * sizeof(float));
+  p.off_pb = o;
+  o = align256(o + (size_t)p.nch * r * n * sizeof(float));
+  p.bwd_bytes = o;
+  return p;
+}
+
+}  // namespace msq
+
+using namespace msq;
+
+extern "C" {
+
+int msq_abi_version(void) { return MSQ_ABI_VERSION; }
+
+const char* msq_strerror(int code) {
+  switch (code) {
+    case MSQ_OK: return "ok";
+    case MSQ_E_INVAL: return "invalid argument";
+    case MSQ_E_SHAPE: return "unsupported shape";
+    case MSQ_E_DROPOUT: return "invalid dropout probability or LoRA scale";
+    case MSQ_E_WORKSPACE: return "workspace too small";
+    case MSQ_E_WINDOW: return "stream window does not fit the arena";
+    case MSQ_E_ORDER: return "stream window protocol violation";
+    case MSQ_E_HIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+const char* msq_last_error(void) { return g_last_error; }
+
+int msq_nf4_codebook(float* out) {
+  if (!out) return set_error(MSQ_E_INVAL, "msq_nf4_codebook: out is NULL");
+  memcpy(out, nf4_lut().v, sizeof(float) * 16);
+  return MSQ_OK;
+}
+
+int nf4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, float* absmax,
+                 msq_stream_t stream) {
+  if (n < 0 || k <= 0) return set_error(MSQ_E_INVAL, "nf4_quantize: n=%lld k=%lld", (long long)n, (long long)k);
+  if (k % 64) return set_error(MSQ_E_SHAPE, "nf4_quantize: k=%lld is not a multiple of 64", (long long)k);
+  if (n == 0) return MSQ_OK;
+  if (!w || !codes || !absmax) return set_error(MSQ_E_INVAL, "nf4_quantize: null pointer");
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(absmax, 4))
+    return set_error(MSQ_E_INVAL, "nf4_quantize: w and codes must be 16-byte aligned, absmax 4-byte");
+  if (n == 0) return MSQ_OK;
+  const hipError_t e = launch_quantize(w, n * (k / 64), codes, absmax, (hipStream_t)stream);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_quantize launch");
+}
+
+int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t n, int64_t k, uint16_t* w,
+                   msq_stream_t stream) {
+  if (n < 0 || k <= 0) return set_error(MSQ_E_INVAL, "nf4_dequantize: n=%lld k=%lld", (long long)n, (long long)k);
+  if (k % 64) return set_error(MSQ_E_SHAPE, "nf4_dequantize: k=%lld is not a multiple of 64", (long long)k);
+  if (n == 0) return MSQ_OK;
+  if (!w || !codes || !absmax) return set_error(MSQ_E_INVAL, "nf4_dequantize: null pointer");
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(absmax, 4))
+    return set_error(MSQ_E_INVAL, "nf4_dequantize: w and codes must be 16-byte aligned, absmax 4-byte");
+  if (n == 0) return MSQ_OK;
+  const hipError_t e = launch_dequantize(codes, absmax, n * (k / 32), w, (hipStream_t)stream);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_dequantize launch");
+}
+
+size_t nf4_lora_workspace_size(int64_t t, int64_t k, int64_t n, int32_t r) {
+  if (t < 0 || k <= 0 || n <= 0 || k % 64 || n % 64 || r < 0 || r > 64 || t > 65535) return 0;
+  const LoraPlan p = lora_plan(t, k, n, r);
+  return std::max<size_t>(256, std::max(p.fwd_bytes, p.bwd_bytes));  // 0 is reserved for "invalid"
+}
+
+int nf4_lora_fwd(const uint16_t* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
+                 const float* absmax, const uint16_t* bias, const float* A, const float* B,
+                 msq_lora_cfg cfg, msq_rng_key key, uint16_t* y, float* u_out, void* workspace,
+                 size_t workspace_bytes, msq_stream_t stream) {
+  int rc = check_linear("nf4_lora_fwd", t, k, n, cfg, key);
+  if (rc) return rc;
+  if (!codes || !absmax || !workspace || (t > 0 && (!x || !y)))
+    return set_error(MSQ_E_INVAL, "nf4_lora_fwd: null pointer");
+  if (cfg.r > 0 && (!A || !B)) return set_error(MSQ_E_INVAL, "nf4_lora_fwd: r > 0 needs A and B");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(codes, 16) || !aligned(absmax, 4) ||
+      !aligned(bias, 8) || !aligned(A, 16) || !aligned(B, 16) || !aligned(u_out, 4) || !aligned(workspace, 256))
+    return set_error(MSQ_E_INVAL, "nf4_lora_fwd: misaligned pointer (x, y, codes, A, B: 16 bytes; bias 8; workspace 256)");
+  const LoraPlan p = lora_plan(t, k, n, cfg.r);
+  if (workspace_bytes < std::max(p.fwd_bytes, p.bwd_bytes))
+    return set_error(MSQ_E_WORKSPACE, "nf4_lora_fwd: workspace %zu < %zu bytes", workspace_bytes, std::max(p.fwd_bytes, p.bwd_bytes));
+  if (t == 0) return MSQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int r = cfg.r;
+  const Dropout d = make_dropout(key, cfg.p_drop);
+  float* u = u_out ? u_out : (float*)(ws + p.off_u_fwd);
+  float* part = (float*)(ws + p.off_part_fwd);
+  const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
+  hipError_t e = hipSuccess;
+  if (r > 0) e = launch_rowdot(x, t, k, A, 0, r, 1.0f, d, u, s);
+  if (e == hipSuccess) e = launch_gemm(0, x, codes, absmax, t, n, k, p.fwd, part, s);
+  if (e == hipSuccess) e = launch_fwd_epilogue(part, p.fwd.splits, t, n, bias, u, B, r, lscale, y, s);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
+}
+
+int nf4_lora_bwd(const uint16_t* dy, const uint16_t* x, int64_t t, int64_t k, int64_t n,
+                 const uint8_t* codes, const float* absmax, const float* A, const float* B,
+                 msq_lora_cfg cfg, msq_rng_key key, const float* u, uint16_t* dx,
+                 int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
+                 size_t workspace_bytes, msq_stream_t stream) {
+  int rc = check_linear("nf4_lora_bwd", t, k, n, cfg, key);
+  if (rc) return rc;
+  if (!codes || !absmax || !workspace || (t > 0 && (!dy || !x || !dx)))
+    return set_error(MSQ_E_INVAL, "nf4_lora_bwd: null pointer");
+  if (cfg.r > 0 && (!A || !B || !dA || !dB)) return set_error(MSQ_E_INVAL, "nf4_lora_bwd: r > 0 needs A, B, dA, dB");
+  if ((dx_accumulate != 0 && dx_accumulate != 1) || (dAB_accumulate != 0 && dAB_accumulate != 1))
+    return set_error(MSQ_E_INVAL, "nf4_lora_bwd: accumulate flags must be 0 or 1");
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16) || !aligned(codes, 16) || !aligned(absmax, 4) ||
+      !aligned(A, 16) || !aligned(B, 16) || !aligned(u, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
+      !aligned(workspace, 256))
+    return set_error(MSQ_E_INVAL, "nf4_lora_bwd: misaligned pointer (dy, x, dx, codes, A, B: 16 bytes; workspace 256)");
+  const LoraPlan p = lora_plan(t, k, n, cfg.r);
+  if (workspace_bytes < std::max(p.fwd_bytes, p.bwd_bytes))
+    return set_error(MSQ_E_WORKSPACE, "nf4_lora_bwd: workspace %zu < %zu bytes", workspace_bytes, std::max(p.fwd_bytes, p.bwd_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int r = cfg.r;
+  const Dropout d = make_dropout(key, cfg.p_drop);
+  const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
+  hipError_t e = hipSuccess;
+  if (t > 0) {
+    float* part = (float*)(ws + p.off_part_bwd);
+    float* du = (float*)(ws + p.off_du);
+    const float* uu = u;
+    if (r > 0 && !uu) {
+      float* ut = (float*)(ws + p.off_u_bwd);
+      e = launch_rowdot(x, t, k, A, 0, r, 1.0f, d, ut, s);
+      uu = ut;
+    }
+    if (e == hipSuccess && r > 0) e = launch_rowdot(dy, t, n, B, 1, r, lscale, no_dropout(), du, s);
+    if (e == hipSuccess) e = launch_gemm(1, dy, codes, absmax, t, n, k, p.bwd, part, s);
+    if (e == hipSuccess)
+      e = launch_bwd_epilogue(part, p.bwd.splits, t, k, du, A, r, d, dx, dx_accumulate, s);
+    if (e == hipSuccess && r > 0) e = launch_colgrad(x, t, k, du, r, d, p.nch, (float*)(ws + p.off_pa), s);
+    if (e == hipSuccess && r > 0) e = launch_colgrad(dy, t, n, uu, r, no_dropout(), p.nch, (float*)(ws + p.off_pb), s);
+  }
+  if (e == hipSuccess && r > 0)
+    e = launch_colgrad_reduce((float*)(ws + p.off_pa), p.nch, r, k, 1.0f, dA, k, 1, dAB_accumulate, s);
+  if (e == hipSuccess && r > 0)
+    e = launch_colgrad_reduce((float*)(ws + p.off_pb), p.nch, r, n, lscale, dB, 1, r, dAB_accumulate, s);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_bwd launch");
+}
+
+}  // extern "C"

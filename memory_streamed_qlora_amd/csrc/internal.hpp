@@ -1,0 +1,82 @@
+// Host-side internals of libmsq: launch wrappers, planning, errors, timing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace msq {
+
+// ---- errors ---------------------------------------------------------------
+int set_error(int code, const char* fmt, ...);  // records thread-local text, returns code
+int hip_error(hipError_t e, const char* what);   // MSQ_E_HIP with the HIP error string
+
+// ---- codebook (computed on the host from the NormalFloat construction) -----
+const Nf4Lut& nf4_lut();
+const Nf4Mid& nf4_mid();
+
+// ---- workspace planning ----------------------------------------------------
+constexpr int GEMM_BM = 128;
+constexpr int GEMM_BN = 128;
+constexpr int GEMM_BK = 64;
+constexpr int COLGRAD_TCHUNK = 32;
+
+struct GemmPlan {
+  int splits;          // split of the reduction dimension
+  int steps;           // reduction steps of GEMM_BK
+  int steps_per_split;
+};
+GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red);
+
+struct LoraPlan {
+  GemmPlan fwd, bwd;
+  size_t off_part_fwd, off_u_fwd;            // fwd layout
+  size_t off_part_bwd, off_u_bwd, off_du, off_pa, off_pb;  // bwd layout
+  int nch;                                   // T-chunks of the dA/dB reductions
+  size_t fwd_bytes, bwd_bytes;
+};
+LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r);
+
+// ---- launch wrappers (all asynchronous on `s`) -------------------------------
+hipError_t launch_quantize(const uint16_t* w, int64_t nblocks, uint8_t* codes, float* absmax,
+                           hipStream_t s);
+hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t nchunks32,
+                             uint16_t* w, hipStream_t s);
+
+// out[S][M][Nc] fp32 partial sums.
+//   mode 0 (forward):  out[m][n] = sum_k act[m][k] * W[n][k]    act [M][K], Nc = N
+//   mode 1 (backward): out[m][k] = sum_n act[m][n] * W[n][k]    act [M][N], Nc = K
+hipError_t launch_gemm(int mode, const uint16_t* act, const uint8_t* codes, const float* absmax,
+                       int64_t M, int64_t N, int64_t K, const GemmPlan& plan, float* part,
+                       hipStream_t s);
+
+// out[t][j] = scale * sum_c h[t][c] * mat(j, c), h = drop(in) (dropout optional)
+//   mat_kind 0: mat is [r][C] (LoRA A);   mat_kind 1: mat is [C][r] (LoRA B)
+hipError_t launch_rowdot(const uint16_t* in, int64_t T, int64_t C, const float* mat, int mat_kind,
+                         int r, float scale, const Dropout& d, float* out, hipStream_t s);
+
+// part[ch][j][c] = sum_{t in chunk ch} coef[t][j] * h[t][c], h = drop(in)
+hipError_t launch_colgrad(const uint16_t* in, int64_t T, int64_t C, const float* coef, int r,
+                          const Dropout& d, int nch, float* part, hipStream_t s);
+// out(j, c) = [out(j, c) +] scale * sum_ch part[ch][j][c];  out(j,c) = out[j*sj + c*sc]
+hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale,
+                                 float* out, int64_t sj, int64_t sc, int accumulate, hipStream_t s);
+
+// y[t][n] = bf16(sum_s part[s][t][n] + bias[n] + lscale * sum_j u[t][j] B[n][j])
+hipError_t launch_fwd_epilogue(const float* part, int splits, int64_t T, int64_t N,
+                               const uint16_t* bias, const float* u, const float* B, int r,
+                               float lscale, uint16_t* y, hipStream_t s);
+// dx[t][k] = bf16([dx_old +] sum_s part[s][t][k] + sigma*keep(t,k)*sum_j du[t][j] A[j][k])
+hipError_t launch_bwd_epilogue(const float* part, int splits, int64_t T, int64_t K,
+                               const float* du, const float* A, int r, const Dropout& d,
+                               uint16_t* dx, int accumulate, hipStream_t s);
+
+// ---- timing -------------------------------------------------------------------
+bool timing_on();
+// Returns a record id (or -1 when timing is off) to pass to timing_end.
+int timing_begin(const char* name, double flops, hipStream_t s);
+void timing_end(int id, hipStream_t s);
+
+}  // namespace msq

@@ -1,0 +1,107 @@
+// Launch timing of the dense dequant-MFMA kernels with HIP events on the launch
+// stream.  Off by default; when on, every launch is bracketed by two events and
+// msq_timing_collect aggregates elapsed time and algorithmic flops per kernel name.
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/msq.h"
+#include "internal.hpp"
+
+namespace msq {
+namespace {
+
+struct Rec {
+  const char* name;
+  double flops;
+  hipEvent_t a, b;
+};
+
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+hipError_t g_err = hipSuccess;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  const hipError_t err = hipEventCreate(&e);
+  if (err != hipSuccess && g_err == hipSuccess) g_err = err;
+  return err == hipSuccess ? e : nullptr;
+}
+
+}  // namespace
+
+bool timing_on() { return g_on; }
+
+int timing_begin(const char* name, double flops, hipStream_t s) {
+  if (!g_on) return -1;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Rec r{name, flops, take_event(), take_event()};
+  if (!r.a || !r.b) {
+    if (r.a) g_pool.push_back(r.a);
+    if (r.b) g_pool.push_back(r.b);
+    return -1;
+  }
+  (void)hipEventRecord(r.a, s);
+  g_recs.push_back(r);
+  return (int)g_recs.size() - 1;
+}
+
+void timing_end(int id, hipStream_t s) {
+  if (id < 0) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (id < (int)g_recs.size()) (void)hipEventRecord(g_recs[id].b, s);
+}
+
+}  // namespace msq
+
+using namespace msq;
+
+extern "C" {
+
+int msq_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_on = on != 0;
+  return MSQ_OK;
+}
+
+int msq_timing_collect(msq_kernel_timing* out, int max, int* n_out) {
+  if (!n_out || (max > 0 && !out)) return set_error(MSQ_E_INVAL, "msq_timing_collect: null pointer");
+  std::lock_guard<std::mutex> lk(g_mu);
+  std::vector<msq_kernel_timing> agg;
+  hipError_t err = g_err;
+  for (const Rec& r : g_recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    size_t i = 0;
+    while (i < agg.size() && strcmp(agg[i].name, r.name) != 0) ++i;
+    if (i == agg.size()) {
+      msq_kernel_timing t;
+      memset(&t, 0, sizeof(t));
+      strncpy(t.name, r.name, sizeof(t.name) - 1);
+      agg.push_back(t);
+    }
+    agg[i].launches++;
+    agg[i].total_ms += ms;
+    agg[i].total_flops += r.flops;
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  g_err = hipSuccess;
+  *n_out = (int)agg.size();
+  for (int i = 0; i < max && i < (int)agg.size(); ++i) out[i] = agg[i];
+  return err == hipSuccess ? MSQ_OK : hip_error(err, "msq_timing_collect");
+}
+
+}  // extern "C"

@@ -1,0 +1,226 @@
+// Host-to-device block-prefetch window (double-buffered, event-ordered).
+//
+// The pages' forward streams frozen blocks through a small GPU window with
+// asynchronous prefetch on side streams; the backward walks the blocks in reverse and
+// reloads each one; eviction is a pointer release because the base is read-only, so
+// nothing is ever copied back ("Poros" research post, training-step paragraph;
+// "Limitations", "Pretraining is out of scope").  Their block-size sweep (peak memory
+// at block sizes 1..16, "Poros" research post, memory paragraph) grows by two
+// blocks' worth per doubling, consistent with one window computing while the next
+// one loads; this window keeps exactly two slots.
+//
+// Ordering: the copy stream waits on a slot's "freed" event (recorded on the
+// compute stream by release) before overwriting it, and records the slot's "ready"
+// event after its copies; acquire makes the compute stream wait on "ready".  The host
+// never blocks.  A prefetch of a window that a free slot still holds issues no copy
+// (the two windows in the slots at the end of the forward are the first two the
+// backward needs).
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/msq.h"
+#include "internal.hpp"
+
+using namespace msq;
+
+namespace {
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+enum SlotState { SLOT_FREE = 0, SLOT_HELD = 1 };
+}  // namespace
+
+struct msq_window {
+  int n_layers = 0, window_blocks = 0, n_windows = 0;
+  std::vector<const void*> host;
+  std::vector<size_t> bytes;
+  std::vector<size_t> offset;  // offset of each layer inside its window's slot
+  size_t slot_bytes = 0;
+  char* slot_base[2] = {nullptr, nullptr};
+  hipStream_t copy = nullptr;
+  hipEvent_t ready[2] = {nullptr, nullptr};
+  hipEvent_t freed[2] = {nullptr, nullptr};
+  bool freed_recorded[2] = {false, false};
+  int slot_window[2] = {-1, -1};  // window whose bytes the slot holds (or will hold)
+  int state[2] = {SLOT_FREE, SLOT_FREE};
+  uint64_t release_tick[2] = {0, 0};
+  uint64_t tick = 0;
+  msq_window_stats stats = {0, 0, 0};
+};
+
+namespace {
+
+size_t window_bytes(const size_t* blob_bytes, int n_layers, int first, int wb) {
+  size_t s = 0;
+  for (int l = first; l < first + wb && l < n_layers; ++l) s += align256(blob_bytes[l]);
+  return s;
+}
+
+size_t max_window_bytes(const size_t* blob_bytes, int n_layers, int wb) {
+  size_t m = 0;
+  for (int f = 0; f < n_layers; f += wb) m = std::max(m, window_bytes(blob_bytes, n_layers, f, wb));
+  return m;
+}
+
+int find_slot(const msq_window* w, int win, int state) {
+  for (int i = 0; i < 2; ++i)
+    if (w->slot_window[i] == win && w->state[i] == state) return i;
+  return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks) {
+  if (!blob_bytes || n_layers <= 0 || window_blocks <= 0) return 0;
+  return 2 * max_window_bytes(blob_bytes, n_layers, window_blocks);
+}
+
+int block_stream_create(msq_window** out, const void* const* host_blobs, const size_t* blob_bytes,
+                        int n_layers, int window_blocks, void* dev_arena, size_t arena_bytes,
+                        msq_stream_t copy_stream) {
+  if (!out || !host_blobs || !blob_bytes || !dev_arena)
+    return set_error(MSQ_E_INVAL, "block_stream_create: null pointer");
+  *out = nullptr;
+  if (n_layers <= 0 || window_blocks <= 0 || window_blocks > n_layers)
+    return set_error(MSQ_E_INVAL, "block_stream_create: n_layers=%d window_blocks=%d", n_layers, window_blocks);
+  if ((uintptr_t)dev_arena % 256)
+    return set_error(MSQ_E_INVAL, "block_stream_create: arena must be 256-byte aligned");
+  for (int l = 0; l < n_layers; ++l)
+    if (!host_blobs[l] || blob_bytes[l] == 0)
+      return set_error(MSQ_E_INVAL, "block_stream_create: layer %d has no host blob", l);
+  const size_t need = 2 * max_window_bytes(blob_bytes, n_layers, window_blocks);
+  if (arena_bytes < need) {
+    int fit = 0;
+    for (int wb = window_blocks - 1; wb >= 1; --wb)
+      if (2 * max_window_bytes(blob_bytes, n_layers, wb) <= arena_bytes) {
+        fit = wb;
+        break;
+      }
+    if (fit > 0)
+      return set_error(MSQ_E_WINDOW, "block_stream_create: arena %zu bytes < %zu needed for window_blocks=%d; largest window that fits: window_blocks=%d",
+                       arena_bytes, need, window_blocks, fit);
+    return set_error(MSQ_E_WINDOW, "block_stream_create: arena %zu bytes < %zu needed for window_blocks=%d; not even one layer per window fits",
+                     arena_bytes, need, window_blocks);
+  }
+  msq_window* w = new msq_window();
+  w->n_layers = n_layers;
+  w->window_blocks = window_blocks;
+  w->n_windows = (n_layers + window_blocks - 1) / window_blocks;
+  w->host.assign(host_blobs, host_blobs + n_layers);
+  w->bytes.assign(blob_bytes, blob_bytes + n_layers);
+  w->offset.resize(n_layers);
+  for (int f = 0; f < n_layers; f += window_blocks) {
+    size_t o = 0;
+    for (int l = f; l < f + window_blocks && l < n_layers; ++l) {
+      w->offset[l] = o;
+      o += align256(blob_bytes[l]);
+    }
+  }
+  w->slot_bytes = need / 2;
+  w->slot_base[0] = (char*)dev_arena;
+  w->slot_base[1] = (char*)dev_arena + w->slot_bytes;
+  w->copy = (hipStream_t)copy_stream;
+  for (int i = 0; i < 2; ++i) {
+    hipError_t e = hipEventCreateWithFlags(&w->ready[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&w->freed[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      for (int j = 0; j < 2; ++j) {
+        if (w->ready[j]) (void)hipEventDestroy(w->ready[j]);
+        if (w->freed[j]) (void)hipEventDestroy(w->freed[j]);
+      }
+      delete w;
+      return hip_error(e, "block_stream_create: hipEventCreate");
+    }
+  }
+  *out = w;
+  return MSQ_OK;
+}
+
+int block_stream_prefetch(msq_window* w, int first_layer) {
+  if (!w) return set_error(MSQ_E_INVAL, "block_stream_prefetch: null window");
+  if (first_layer < 0 || first_layer >= w->n_layers || first_layer % w->window_blocks)
+    return set_error(MSQ_E_INVAL, "block_stream_prefetch: first_layer=%d is not a window start", first_layer);
+  const int win = first_layer / w->window_blocks;
+  if (find_slot(w, win, SLOT_HELD) >= 0) return MSQ_OK;  // already prefetched and not released
+  int slot = find_slot(w, win, SLOT_FREE);
+  if (slot >= 0) {  // the free slot still holds this window's bytes
+    w->state[slot] = SLOT_HELD;
+    w->stats.windows_reused++;
+    return MSQ_OK;
+  }
+  // least recently released free slot
+  slot = -1;
+  for (int i = 0; i < 2; ++i)
+    if (w->state[i] == SLOT_FREE && (slot < 0 || w->release_tick[i] < w->release_tick[slot])) slot = i;
+  if (slot < 0)
+    return set_error(MSQ_E_ORDER, "block_stream_prefetch: no free slot for window %d (release a window first)", win);
+  hipError_t e = hipSuccess;
+  if (w->freed_recorded[slot]) e = hipStreamWaitEvent(w->copy, w->freed[slot], 0);
+  // the slot's old contents are about to be overwritten
+  w->slot_window[slot] = -1;
+  size_t total = 0;
+  for (int l = first_layer; e == hipSuccess && l < first_layer + w->window_blocks && l < w->n_layers; ++l) {
+    e = hipMemcpyAsync(w->slot_base[slot] + w->offset[l], w->host[l], w->bytes[l], hipMemcpyHostToDevice, w->copy);
+    total += w->bytes[l];
+  }
+  if (e == hipSuccess) e = hipEventRecord(w->ready[slot], w->copy);
+  if (e != hipSuccess) return hip_error(e, "block_stream_prefetch: copy");
+  w->slot_window[slot] = win;
+  w->state[slot] = SLOT_HELD;
+  w->stats.bytes_copied += total;
+  w->stats.windows_copied++;
+  return MSQ_OK;
+}
+
+int block_stream_acquire(msq_window* w, int layer, msq_stream_t compute, const void** dev_blob) {
+  if (!w || !dev_blob) return set_error(MSQ_E_INVAL, "block_stream_acquire: null pointer");
+  if (layer < 0 || layer >= w->n_layers) return set_error(MSQ_E_INVAL, "block_stream_acquire: layer %d out of range", layer);
+  const int win = layer / w->window_blocks;
+  const int slot = find_slot(w, win, SLOT_HELD);
+  if (slot < 0) return set_error(MSQ_E_ORDER, "block_stream_acquire: window %d (layer %d) was not prefetched", win, layer);
+  const hipError_t e = hipStreamWaitEvent((hipStream_t)compute, w->ready[slot], 0);
+  if (e != hipSuccess) return hip_error(e, "block_stream_acquire: hipStreamWaitEvent");
+  *dev_blob = w->slot_base[slot] + w->offset[layer];
+  return MSQ_OK;
+}
+
+int block_stream_release(msq_window* w, int first_layer, msq_stream_t compute) {
+  if (!w) return set_error(MSQ_E_INVAL, "block_stream_release: null window");
+  if (first_layer < 0 || first_layer >= w->n_layers || first_layer % w->window_blocks)
+    return set_error(MSQ_E_INVAL, "block_stream_release: first_layer=%d is not a window start", first_layer);
+  const int win = first_layer / w->window_blocks;
+  const int slot = find_slot(w, win, SLOT_HELD);
+  if (slot < 0) return set_error(MSQ_E_ORDER, "block_stream_release: window %d is not held", win);
+  const hipError_t e = hipEventRecord(w->freed[slot], (hipStream_t)compute);
+  if (e != hipSuccess) return hip_error(e, "block_stream_release: hipEventRecord");
+  w->freed_recorded[slot] = true;
+  w->state[slot] = SLOT_FREE;
+  w->release_tick[slot] = ++w->tick;
+  return MSQ_OK;
+}
+
+int block_stream_stats(const msq_window* w, msq_window_stats* out) {
+  if (!w || !out) return set_error(MSQ_E_INVAL, "block_stream_stats: null pointer");
+  *out = w->stats;
+  return MSQ_OK;
+}
+
+int block_stream_destroy(msq_window* w) {
+  if (!w) return MSQ_OK;
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 2; ++i) {
+    if (w->ready[i]) {
+      const hipError_t e1 = hipEventSynchronize(w->ready[i]);
+      if (e == hipSuccess) e = e1;
+      (void)hipEventDestroy(w->ready[i]);
+    }
+    if (w->freed[i]) (void)hipEventDestroy(w->freed[i]);
+  }
+  delete w;
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "block_stream_destroy");
+}
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+"""Python binding of libmsq with the C-ABI's names.
+
+Argument marshalling only: tensors are checked for device, dtype and layout, their
+addresses and sizes are passed to the library, and any error code is raised as
+MsqError.  Every computation happens in the library's HIP kernels; PyTorch only
+provides device memory and streams.  Outputs not supplied by the caller are
+allocated with torch on the input's device.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _abi
+from ._abi import LoraCfg, RngKey, check, lib
+
+PROJS = ("q", "k", "v", "o", "gate", "up", "down")
+PROJ_ID = {p: i for i, p in enumerate(PROJS)}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _req(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def abi_version() -> int:
+    return lib().msq_abi_version()
+
+
+def nf4_codebook() -> torch.Tensor:
+    """The library's 16 NF4 levels (host, float32)."""
+    out = torch.empty(16, dtype=torch.float32)
+    check("msq_nf4_codebook", lib().msq_nf4_codebook(out.data_ptr()))
+    return out
+
+
+def nf4_quantize(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                 absmax: Optional[torch.Tensor] = None, stream=None):
+    """w bf16 [n, k] -> (codes uint8 [n, k/2], absmax fp32 [n, k/64])."""
+    n, k = w.shape
+    _req(w, "w", torch.bfloat16, (n, k))
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if absmax is None:
+        absmax = torch.empty((n, k // 64), dtype=torch.float32, device=w.device)
+    _req(codes, "codes", torch.uint8, (n, k // 2))
+    _req(absmax, "absmax", torch.float32, (n, k // 64))
+    check("nf4_quantize", lib().nf4_quantize(_ptr(w), n, k, _ptr(codes), _ptr(absmax), _stream(stream)))
+    return codes, absmax
+
+
+def nf4_dequantize(codes: torch.Tensor, absmax: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    n, kh = codes.shape
+    k = 2 * kh
+    _req(codes, "codes", torch.uint8, (n, kh))
+    _req(absmax, "absmax", torch.float32, (n, k // 64))
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=codes.device)
+    _req(out, "out", torch.bfloat16, (n, k))
+    check("nf4_dequantize", lib().nf4_dequantize(_ptr(codes), _ptr(absmax), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def nf4_lora_workspace_size(t: int, k: int, n: int, r: int) -> int:
+    return int(lib().nf4_lora_workspace_size(t, k, n, r))
+
+
+class Workspace:
+    """A growable device scratch buffer for the fused linear calls (one per stream)."""
+
+    def __init__(self, device=None):
+        self.device = torch.device(device or "cuda")
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(device: torch.device, nbytes: int, ws: Optional[Workspace]) -> torch.Tensor:
+    if ws is None:
+        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+        ws = _default_ws.setdefault(key, Workspace(device))
+    return ws.get(nbytes)
+
+
+@dataclass(frozen=True)
+class Lora:
+    r: int = 16
+    alpha: float = 32.0
+    p_drop: float = 0.0
+
+    def c(self) -> LoraCfg:
+        return LoraCfg(self.r, self.alpha, self.p_drop)
+
+
+def rng_key(seed: int = 0, step: int = 0, micro: int = 0, layer: int = 0, proj: int = 0) -> RngKey:
+    return RngKey(seed, step, micro, layer, proj)
+
+
+def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
+                 bias: Optional[torch.Tensor], A: Optional[torch.Tensor], B: Optional[torch.Tensor],
+                 cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
+                 u_out: Optional[torch.Tensor] = None, want_u: bool = True,
+                 workspace: Optional[Workspace] = None, stream=None):
+    """y = x W^T + bias + (alpha/r) drop(x) A^T B^T.  Returns (y, u) (u None if not wanted)."""
+    t, k = x.shape
+    n = codes.shape[0]
+    _req(x, "x", torch.bfloat16, (t, k))
+    _req(codes, "codes", torch.uint8, (n, k // 2))
+    _req(absmax, "absmax", torch.float32, (n, k // 64))
+    if bias is not None:
+        _req(bias, "bias", torch.bfloat16, (n,))
+    r = cfg.r
+    if r > 0:
+        _req(A, "A", torch.float32, (r, k))
+        _req(B, "B", torch.float32, (n, r))
+    if y is None:
+        y = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
+    _req(y, "y", torch.bfloat16, (t, n))
+    if want_u and r > 0 and u_out is None:
+        u_out = torch.empty((t, r), dtype=torch.float32, device=x.device)
+    if u_out is not None:
+        _req(u_out, "u_out", torch.float32, (t, r))
+    need = nf4_lora_workspace_size(t, k, n, r)
+    ws = _workspace(x.device, need, workspace)
+    check("nf4_lora_fwd", lib().nf4_lora_fwd(
+        _ptr(x), t, k, n, _ptr(codes), _ptr(absmax), _ptr(bias), _ptr(A) if r > 0 else None,
+        _ptr(B) if r > 0 else None, cfg.c(), key, _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return y, u_out
+
+
+def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
+                 A: Optional[torch.Tensor], B: Optional[torch.Tensor], cfg: Lora, key: RngKey,
+                 u: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
+                 dx_accumulate: bool = False, dA: Optional[torch.Tensor] = None,
+                 dB: Optional[torch.Tensor] = None, dAB_accumulate: bool = False,
+                 workspace: Optional[Workspace] = None, stream=None):
+    """Returns (dx, dA, dB); dA/dB are None when r == 0."""
+    t, k = x.shape
+    n = codes.shape[0]
+    _req(dy, "dy", torch.bfloat16, (t, n))
+    _req(x, "x", torch.bfloat16, (t, k))
+    _req(codes, "codes", torch.uint8, (n, k // 2))
+    _req(absmax, "absmax", torch.float32, (n, k // 64))
+    r = cfg.r
+    if r > 0:
+        _req(A, "A", torch.float32, (r, k))
+        _req(B, "B", torch.float32, (n, r))
+        if dA is None:
+            dA = torch.empty((r, k), dtype=torch.float32, device=x.device)
+        if dB is None:
+            dB = torch.empty((n, r), dtype=torch.float32, device=x.device)
+        _req(dA, "dA", torch.float32, (r, k))
+        _req(dB, "dB", torch.float32, (n, r))
+        if u is not None:
+            _req(u, "u", torch.float32, (t, r))
+    if dx is None:
+        dx = torch.empty((t, k), dtype=torch.bfloat16, device=x.device)
+    _req(dx, "dx", torch.bfloat16, (t, k))
+    need = nf4_lora_workspace_size(t, k, n, r)
+    ws = _workspace(x.device, need, workspace)
+    check("nf4_lora_bwd", lib().nf4_lora_bwd(
+        _ptr(dy), _ptr(x), t, k, n, _ptr(codes), _ptr(absmax), _ptr(A) if r > 0 else None,
+        _ptr(B) if r > 0 else None, cfg.c(), key, _ptr(u) if r > 0 else None, _ptr(dx),
+        int(dx_accumulate), _ptr(dA) if r > 0 else None, _ptr(dB) if r > 0 else None,
+        int(dAB_accumulate), _ptr(ws), ws.numel(), _stream(stream)))
+    return dx, (dA if r > 0 else None), (dB if r > 0 else None)
+
+
+class BlockStreamWindow:
+    """block_stream_* over pinned host blobs and a caller-owned device arena."""
+
+    def __init__(self, host_blobs: Sequence[torch.Tensor], window_blocks: int,
+                 arena: Optional[torch.Tensor] = None, copy_stream: Optional[torch.cuda.Stream] = None,
+                 device=None):
+        self.n_layers = len(host_blobs)
+        self.window_blocks = int(window_blocks)
+        for i, b in enumerate(host_blobs):
+            if b.device.type != "cpu" or not b.is_pinned() or b.dtype != torch.uint8 or not b.is_contiguous():
+                raise ValueError(f"host blob {i} must be a contiguous pinned uint8 CPU tensor")
+        self.host_blobs = list(host_blobs)
+        self._ptrs = (ctypes.c_void_p * self.n_layers)(*[b.data_ptr() for b in host_blobs])
+        self._sizes = (ctypes.c_size_t * self.n_layers)(*[b.numel() for b in host_blobs])
+        self.arena_bytes_needed = int(lib().block_stream_arena_bytes(self._sizes, self.n_layers,
+                                                                     self.window_blocks))
+        dev = torch.device(device or "cuda")
+        if arena is None:
+            arena = torch.empty(self.arena_bytes_needed, dtype=torch.uint8, device=dev)
+        if arena.device.type != "cuda" or arena.dtype != torch.uint8:
+            raise ValueError("arena must be a device uint8 tensor")
+        self.arena = arena
+        self.copy_stream = copy_stream or torch.cuda.Stream(device=arena.device)
+        h = ctypes.c_void_p()
+        check("block_stream_create", lib().block_stream_create(
+            ctypes.byref(h), self._ptrs, self._sizes, self.n_layers, self.window_blocks,
+            arena.data_ptr(), arena.numel(), self.copy_stream.cuda_stream))
+        self._h = h
+
+    def prefetch(self, first_layer: int) -> None:
+        check("block_stream_prefetch", lib().block_stream_prefetch(self._h, first_layer))
+
+    def acquire(self, layer: int, stream=None) -> int:
+        p = ctypes.c_void_p()
+        check("block_stream_acquire", lib().block_stream_acquire(self._h, layer, _stream(stream),
+                                                                 ctypes.byref(p)))
+        return int(p.value)
+
+    def acquire_view(self, layer: int, stream=None) -> torch.Tensor:
+        """The layer's bytes inside the arena as a uint8 tensor view."""
+        addr = self.acquire(layer, stream)
+        off = addr - self.arena.data_ptr()
+        return self.arena[off: off + self.host_blobs[layer].numel()]
+
+    def release(self, first_layer: int, stream=None) -> None:
+        check("block_stream_release", lib().block_stream_release(self._h, first_layer, _stream(stream)))
+
+    def stats(self) -> dict:
+        s = _abi.WindowStats()
+        check("block_stream_stats", lib().block_stream_stats(self._h, ctypes.byref(s)))
+        return {"bytes_copied": s.bytes_copied, "windows_copied": s.windows_copied,
+                "windows_reused": s.windows_reused}
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            h, self._h = self._h, None
+            check("block_stream_destroy", lib().block_stream_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def timing_enable(on: bool = True) -> None:
+    check("msq_timing_enable", lib().msq_timing_enable(int(on)))
+
+
+def timing_collect() -> dict:
+    arr = (_abi.KernelTiming * 16)()
+    n = ctypes.c_int()
+    check("msq_timing_collect", lib().msq_timing_collect(arr, 16, ctypes.byref(n)))
+    out = {}
+    for i in range(min(n.value, 16)):
+        e = arr[i]
+        out[e.name.decode()] = {"launches": int(e.launches), "total_ms": e.total_ms,
+                                "total_flops": e.total_flops}
+    return out

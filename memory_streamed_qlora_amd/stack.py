@@ -1,0 +1,407 @@
+"""Streamed (and resident) training step of a Qwen2.5-shaped NF4 + LoRA stack.
+
+The step the pages describe ("Poros" research post, the training-step paragraph;
+package README, "How it works"):
+  forward   blocks run in order while their frozen NF4 weights stream through a
+            two-slot device window (block_stream_prefetch on a side stream); only
+            block-boundary activations are kept; each window is released (a pointer
+            release -- the base is read-only) as soon as its blocks have run
+  loss      frozen bf16 lm_head + mean next-token cross-entropy
+  backward  windows in reverse: reload, recompute each block's forward with the same
+            dropout keys (the counter-based masks replay exactly), then differentiate
+            the adapters and the block input only
+  update    one AdamW step on the fp32 adapters, identical to the resident run's.
+Resident mode runs the same code with every layer's blob already in device memory.
+
+Every projection goes through the library (nf4_lora_fwd / nf4_lora_bwd); the glue
+between them -- RMSNorm, RoPE from precomputed tables, causal GQA attention in fp32,
+SwiGLU, residual adds, embedding gather, lm_head and cross-entropy, AdamW -- is
+plain PyTorch and deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and
+optimizer settings are readings of the Qwen2 family and of textbook AdamW; the pages
+name neither.
+"""
+from __future__ import annotations
+
+import math
+import time
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import ops
+
+PROJS = ops.PROJS
+PROJ_ID = ops.PROJ_ID
+EPS = 1e-6
+ROPE_THETA = 1.0e6
+LR, BETAS, ADAM_EPS, WD = 2e-4, (0.9, 0.999), 1e-8, 0.01
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Qwen2.5-family geometry."""
+
+    hidden: int
+    heads: int
+    kv_heads: int
+    head_dim: int
+    inter: int
+    layers: int
+    vocab: int = 152064
+
+    def proj_shape(self, proj: str) -> Tuple[int, int]:
+        """(K = in_features, N = out_features)"""
+        h, q, kv = self.hidden, self.heads * self.head_dim, self.kv_heads * self.head_dim
+        return {"q": (h, q), "k": (h, kv), "v": (h, kv), "o": (q, h), "gate": (h, self.inter),
+                "up": (h, self.inter), "down": (self.inter, h)}[proj]
+
+
+QWEN25_05B = Shape(896, 14, 2, 64, 4864, 24)
+QWEN25_7B = Shape(3584, 28, 4, 128, 18944, 28)
+QWEN25_32B = Shape(5120, 40, 8, 128, 27648, 64)
+QWEN25_72B = Shape(8192, 64, 8, 128, 29568, 80)
+
+
+def _align(x: int, a: int = 256) -> int:
+    return (x + a - 1) // a * a
+
+
+class LayerLayout:
+    """One layer's frozen base as a single contiguous blob (the unit the window
+    streams): for q, k, v, o, gate, up, down in order, packed NF4 codes [N, K/2] then
+    fp32 absmax [N, K/64]; then the bf16 q/k/v biases.  Every segment starts on a
+    256-byte boundary."""
+
+    def __init__(self, shape: Shape):
+        self.segs: Dict[Tuple[str, str], Tuple[int, int, torch.dtype, Tuple[int, ...]]] = {}
+        off = 0
+        for proj in PROJS:
+            K, N = shape.proj_shape(proj)
+            self.segs[(proj, "codes")] = (off, N * K // 2, torch.uint8, (N, K // 2))
+            off = _align(off + N * K // 2)
+            self.segs[(proj, "absmax")] = (off, N * K // 16, torch.float32, (N, K // 64))
+            off = _align(off + N * K // 16)
+        for proj in ("q", "k", "v"):
+            N = shape.proj_shape(proj)[1]
+            self.segs[(proj, "bias")] = (off, 2 * N, torch.bfloat16, (N,))
+            off = _align(off + 2 * N)
+        self.nbytes = off
+
+    def views(self, blob: torch.Tensor) -> Dict[Tuple[str, str], torch.Tensor]:
+        out = {}
+        for key, (off, nb, dt, shp) in self.segs.items():
+            out[key] = blob[off: off + nb].view(dt).view(shp)
+        return out
+
+
+# ---------------------------------------------------------------------------------
+# autograd bridge to the library
+
+class _NF4LoraLinear(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, A, B, codes, absmax, bias, cfg, key):
+        need_u = torch.is_grad_enabled() or A.requires_grad
+        y, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=True)
+        ctx.save_for_backward(x, A, B, u)
+        ctx.codes, ctx.absmax, ctx.cfg, ctx.key = codes, absmax, cfg, key
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, A, B, u = ctx.saved_tensors
+        dx, dA, dB = ops.nf4_lora_bwd(dy.contiguous(), x, ctx.codes, ctx.absmax, A, B, ctx.cfg,
+                                      ctx.key, u=u)
+        return dx, dA, dB, None, None, None, None, None
+
+
+def nf4_lora_linear(x, A, B, codes, absmax, bias, cfg: ops.Lora, key) -> torch.Tensor:
+    if torch.is_grad_enabled() and (x.requires_grad or A.requires_grad or B.requires_grad):
+        return _NF4LoraLinear.apply(x, A, B, codes, absmax, bias, cfg, key)
+    y, _ = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=False)
+    return y
+
+
+# ---------------------------------------------------------------------------------
+# block glue (fp32 except where it feeds the library in bf16)
+
+def rmsnorm(h: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    return h * torch.rsqrt(torch.mean(h * h, dim=-1, keepdim=True) + EPS) * w
+
+
+def rope_tables(T: int, D: int, device) -> Tuple[torch.Tensor, torch.Tensor]:
+    inv = ROPE_THETA ** (-np.arange(0, D, 2, dtype=np.float64) / D)
+    ang = np.arange(T, dtype=np.float64)[:, None] * inv[None, :]
+    cos = np.concatenate([np.cos(ang), np.cos(ang)], 1).astype(np.float32)
+    sin = np.concatenate([np.sin(ang), np.sin(ang)], 1).astype(np.float32)
+    return torch.from_numpy(cos).to(device), torch.from_numpy(sin).to(device)
+
+
+def rope(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor) -> torch.Tensor:
+    """x [T, H, D] with rotate-half pairs (i, i + D/2)."""
+    h = x.shape[-1] // 2
+    rot = torch.cat([-x[..., h:], x[..., :h]], dim=-1)
+    return x * cos[:, None, :] + rot * sin[:, None, :]
+
+
+def causal_gqa_attention(q, k, v, mask_add):
+    """q [T,H,D], k/v [T,KV,D] fp32 -> [T, H*D] fp32."""
+    T, H, D = q.shape
+    KV = k.shape[1]
+    g = H // KV
+    k = k[:, :, None, :].expand(T, KV, g, D).reshape(T, H, D)
+    v = v[:, :, None, :].expand(T, KV, g, D).reshape(T, H, D)
+    qh = q.permute(1, 0, 2).contiguous()
+    kt = k.permute(1, 2, 0).contiguous()
+    vh = v.permute(1, 0, 2).contiguous()
+    s = torch.matmul(qh, kt) * (1.0 / math.sqrt(D)) + mask_add
+    p = torch.softmax(s, dim=-1)
+    o = torch.matmul(p, vh)
+    return o.permute(1, 0, 2).reshape(T, H * D)
+
+
+@dataclass
+class StepResult:
+    loss: float
+    grad_norm: float
+    seconds: float
+    window_stats: Optional[dict] = None
+
+
+class Stack:
+    """A Qwen2.5-shaped NF4 + LoRA stack with streamed or resident frozen base."""
+
+    def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
+                 window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None):
+        assert mode in ("streamed", "resident")
+        self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
+        self.cfg = ops.Lora(r, alpha, p_drop)
+        self.window_blocks = window_blocks
+        self.dev = torch.device(device or "cuda")
+        self.layout = LayerLayout(shape)
+        self.host_blobs: List[torch.Tensor] = []
+        self.dev_blobs: List[torch.Tensor] = []
+        self.window: Optional[ops.BlockStreamWindow] = None
+        self.ln1: List[torch.Tensor] = []
+        self.ln2: List[torch.Tensor] = []
+        self.A: List[Dict[str, torch.nn.Parameter]] = []
+        self.B: List[Dict[str, torch.nn.Parameter]] = []
+        self.emb = self.lm = self.lnf = None
+        self.cos, self.sin = rope_tables(seq, shape.head_dim, self.dev)
+        self.mask_add = torch.triu(torch.full((seq, seq), float("-inf"), device=self.dev), 1)
+        self.opt: Optional[torch.optim.Optimizer] = None
+        self.step_index = 0
+
+    # -- construction ------------------------------------------------------------
+    def _store_layer(self, blob_dev: torch.Tensor) -> None:
+        if self.mode == "resident":
+            self.dev_blobs.append(blob_dev)
+        else:
+            host = torch.empty(blob_dev.numel(), dtype=torch.uint8, pin_memory=True)
+            host.copy_(blob_dev)
+            self.host_blobs.append(host)
+
+    def add_layer(self, W: Dict[str, torch.Tensor], bias: Dict[str, torch.Tensor], A, B, ln1, ln2):
+        """W[proj] bf16 [N, K] on the device -> NF4 into a fresh blob (nf4_quantize)."""
+        blob = torch.zeros(self.layout.nbytes, dtype=torch.uint8, device=self.dev)
+        v = self.layout.views(blob)
+        for proj in PROJS:
+            ops.nf4_quantize(W[proj], v[(proj, "codes")], v[(proj, "absmax")])
+        for proj in ("q", "k", "v"):
+            v[(proj, "bias")].copy_(bias[proj])
+        self._store_layer(blob)
+        self.A.append({p: torch.nn.Parameter(A[p].to(self.dev, torch.float32).contiguous()) for p in PROJS})
+        self.B.append({p: torch.nn.Parameter(B[p].to(self.dev, torch.float32).contiguous()) for p in PROJS})
+        self.ln1.append(ln1.to(self.dev, torch.float32))
+        self.ln2.append(ln2.to(self.dev, torch.float32))
+
+    def set_globals(self, emb: torch.Tensor, lm: torch.Tensor, lnf: torch.Tensor) -> None:
+        self.emb = emb.to(self.dev, torch.bfloat16).contiguous()
+        self.lm = lm.to(self.dev, torch.bfloat16).contiguous()
+        self.lnf = lnf.to(self.dev, torch.float32)
+
+    def finalize(self) -> None:
+        params = [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
+        self.opt = torch.optim.AdamW(params, lr=LR, betas=BETAS, eps=ADAM_EPS, weight_decay=WD,
+                                     foreach=True)
+        if self.mode == "streamed":
+            self.copy_stream = torch.cuda.Stream(device=self.dev)
+            self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks,
+                                                copy_stream=self.copy_stream, device=self.dev)
+
+    @classmethod
+    def random(cls, shape: Shape, seq: int, seed: int = 0, cfg_id: int = 0, w_std: float = 0.02,
+               **kw) -> "Stack":
+        """Random-weight stack generated layer by layer on the device (the base is
+        drawn, quantized with nf4_quantize and, when streamed, moved to pinned host
+        memory one layer at a time, so the device never holds more than one layer)."""
+        st = cls(shape, seq, seed=seed, **kw)
+        dev = st.dev
+        r = st.cfg.r
+
+        def gen(layer, tid):
+            g = torch.Generator(device=dev)
+            g.manual_seed((seed * 1000003 + cfg_id * 10007 + layer * 101 + tid) & 0x7FFFFFFFFFFFFFFF)
+            return g
+
+        for l in range(shape.layers):
+            W, bias, A, B = {}, {}, {}, {}
+            for i, proj in enumerate(PROJS):
+                K, N = shape.proj_shape(proj)
+                W[proj] = (torch.randn(N, K, generator=gen(l, 16 * i), device=dev) * w_std).to(torch.bfloat16)
+                A[proj] = (torch.rand(r, K, generator=gen(l, 16 * i + 2), device=dev) * 2 - 1) / math.sqrt(K)
+                B[proj] = torch.randn(N, r, generator=gen(l, 16 * i + 3), device=dev) * 0.01
+                if proj in ("q", "k", "v"):
+                    bias[proj] = (torch.randn(N, generator=gen(l, 16 * i + 1), device=dev) * 0.02).to(torch.bfloat16)
+            ln1 = 1 + 0.02 * torch.randn(shape.hidden, generator=gen(l, 200), device=dev)
+            ln2 = 1 + 0.02 * torch.randn(shape.hidden, generator=gen(l, 201), device=dev)
+            st.add_layer(W, bias, A, B, ln1, ln2)
+            del W
+        ge = gen(10000, 0)
+        emb = (torch.randn(shape.vocab, shape.hidden, generator=ge, device=dev) * 0.02).to(torch.bfloat16)
+        lm = (torch.randn(shape.vocab, shape.hidden, generator=gen(10000, 1), device=dev) * 0.02).to(torch.bfloat16)
+        lnf = 1 + 0.02 * torch.randn(shape.hidden, generator=gen(10000, 2), device=dev)
+        st.set_globals(emb, lm, lnf)
+        st.finalize()
+        return st
+
+    # -- one layer -----------------------------------------------------------------
+    def _lin(self, x, l, views, proj, step, micro):
+        key = ops.rng_key(self.seed, step, micro, l, PROJ_ID[proj])
+        bias = views.get((proj, "bias"))
+        return nf4_lora_linear(x, self.A[l][proj], self.B[l][proj], views[(proj, "codes")],
+                               views[(proj, "absmax")], bias, self.cfg, key)
+
+    def layer_forward(self, h: torch.Tensor, l: int, views, step: int, micro: int = 0) -> torch.Tensor:
+        sh = self.shape
+        T = h.shape[0]
+        xn = rmsnorm(h, self.ln1[l]).to(torch.bfloat16)
+        q = self._lin(xn, l, views, "q", step, micro).float().view(T, sh.heads, sh.head_dim)
+        k = self._lin(xn, l, views, "k", step, micro).float().view(T, sh.kv_heads, sh.head_dim)
+        v = self._lin(xn, l, views, "v", step, micro).float().view(T, sh.kv_heads, sh.head_dim)
+        cos, sin = self.cos[:T], self.sin[:T]
+        att = causal_gqa_attention(rope(q, cos, sin), rope(k, cos, sin), v, self.mask_add[:T, :T])
+        h1 = h + self._lin(att.to(torch.bfloat16), l, views, "o", step, micro).float()
+        xn2 = rmsnorm(h1, self.ln2[l]).to(torch.bfloat16)
+        g = self._lin(xn2, l, views, "gate", step, micro).float()
+        u = self._lin(xn2, l, views, "up", step, micro).float()
+        a = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+        return h1 + self._lin(a, l, views, "down", step, micro).float()
+
+    # -- base residency --------------------------------------------------------------
+    def _views(self, l: int):
+        if self.mode == "resident":
+            return self.layout.views(self.dev_blobs[l])
+        return self.layout.views(self.window.acquire_view(l))
+
+    def _windows(self) -> List[int]:
+        return list(range(0, self.shape.layers, self.window_blocks))
+
+    # -- the step ----------------------------------------------------------------------
+    def forward_backward(self, tokens: torch.Tensor, step: int, micro: int = 0) -> torch.Tensor:
+        """Accumulates adapter gradients into .grad; returns the loss (device scalar)."""
+        L = self.shape.layers
+        wins = self._windows()
+        streamed = self.mode == "streamed"
+        h = self.emb[tokens].float()
+        bounds: List[torch.Tensor] = []
+        if streamed:
+            for w in wins[:2]:
+                self.window.prefetch(w)
+        with torch.no_grad():
+            for wi, w in enumerate(wins):
+                for l in range(w, min(w + self.window_blocks, L)):
+                    bounds.append(h)
+                    h = self.layer_forward(h, l, self._views(l), step, micro)
+                if streamed:
+                    self.window.release(w)
+                    if wi + 2 < len(wins):
+                        self.window.prefetch(wins[wi + 2])
+        hf = h.detach().requires_grad_()
+        with torch.enable_grad():
+            hn = rmsnorm(hf, self.lnf).to(torch.bfloat16)
+            logits = torch.matmul(hn, self.lm.t()).float()
+            loss = torch.nn.functional.cross_entropy(logits[:-1], tokens[1:])
+            loss.backward()
+        dh = hf.grad
+        del logits
+        rw = wins[::-1]
+        if streamed:
+            for w in rw[:2]:
+                self.window.prefetch(w)
+        for wi, w in enumerate(rw):
+            for l in reversed(range(w, min(w + self.window_blocks, L))):
+                x_in = bounds[l].detach().requires_grad_()
+                with torch.enable_grad():
+                    out = self.layer_forward(x_in, l, self._views(l), step, micro)
+                out.backward(dh)
+                dh = x_in.grad
+                bounds[l] = None
+            if streamed:
+                self.window.release(w)
+                if wi + 2 < len(rw):
+                    self.window.prefetch(rw[wi + 2])
+        return loss.detach()
+
+    def params(self) -> List[torch.nn.Parameter]:
+        return [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
+
+    def grad_norm(self) -> torch.Tensor:
+        grads = [p.grad for p in self.params() if p.grad is not None]
+        return torch.linalg.vector_norm(torch.stack(torch._foreach_norm(grads)))
+
+    def train_step(self, tokens: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+        """One optimizer step on one micro-batch; returns (loss, grad_norm) device scalars."""
+        self.opt.zero_grad(set_to_none=True)
+        loss = self.forward_backward(tokens, self.step_index)
+        gn = self.grad_norm()
+        self.opt.step()
+        self.step_index += 1
+        return loss, gn
+
+    def state_tensors(self) -> Dict[str, torch.Tensor]:
+        """Everything the bitwise gate compares: adapters, grads, AdamW moments."""
+        out = {}
+        for l in range(self.shape.layers):
+            for p in PROJS:
+                for nm, d in (("A", self.A), ("B", self.B)):
+                    prm = d[l][p]
+                    out[f"{l}.{p}.{nm}"] = prm.detach()
+                    if prm.grad is not None:
+                        out[f"{l}.{p}.{nm}.grad"] = prm.grad.detach()
+                    st = self.opt.state.get(prm, {})
+                    for sk in ("exp_avg", "exp_avg_sq"):
+                        if sk in st:
+                            out[f"{l}.{p}.{nm}.{sk}"] = st[sk].detach()
+        return out
+
+    def close(self) -> None:
+        if self.window is not None:
+            self.window.close()
+            self.window = None
+
+
+def random_tokens(seed: int, step: int, T: int, vocab: int, device) -> torch.Tensor:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 7919 + step)
+    return torch.randint(0, vocab, (T,), generator=g).to(device)
+
+
+def smoke_step(device) -> None:
+    """Two tiny layers, one window each: a streamed step must equal the resident one."""
+    sh = Shape(hidden=128, heads=2, kv_heads=1, head_dim=64, inter=256, layers=2, vocab=256)
+    out = []
+    for mode in ("resident", "streamed"):
+        st = Stack.random(sh, 32, seed=3, r=8, alpha=16.0, p_drop=0.1, window_blocks=1, mode=mode,
+                          device=device)
+        toks = random_tokens(3, 0, 32, sh.vocab, st.dev)
+        loss, gn = st.train_step(toks)
+        torch.cuda.synchronize()
+        out.append((loss.item(), gn.item(), st.state_tensors()))
+        st.close()
+    (l0, g0, s0), (l1, g1, s1) = out
+    assert l0 == l1 and g0 == g1, f"streamed step differs from resident: {l0} vs {l1}, {g0} vs {g1}"
+    for k in s0:
+        assert torch.equal(s0[k], s1[k]), f"streamed != resident for {k}"
+    print(f"[smoke] streamed == resident (bitwise): loss {l0:.6f} grad-norm {g0:.6e}", flush=True)

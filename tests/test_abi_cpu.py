@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header
+declares, its host-computed codebook equals the oracle's, and invalid arguments are
+rejected on the host before any HIP call (fake, never-dereferenced addresses)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msq.h")
+
+abi = pytest.importorskip("memory_streamed_qlora_amd._abi")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = abi.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 17
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(abi.EXPORTED)
+    assert lib.msq_abi_version() == 1
+
+
+def test_host_codebook_equals_oracle():
+    from oracle import nf4
+    out = (ctypes.c_float * 16)()
+    assert abi.lib().msq_nf4_codebook(out) == 0
+    got = np.frombuffer(out, dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), nf4.codebook().view(np.uint32))
+
+
+FAKE = 0x10000  # 256-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _err():
+    return abi.lib().msq_last_error().decode()
+
+
+def test_quantize_rejects_bad_arguments():
+    L = abi.lib()
+    assert L.nf4_quantize(FAKE, 4, 96, FAKE, FAKE, None) == abi.MSQ_E_SHAPE
+    assert "multiple of 64" in _err()
+    assert L.nf4_quantize(None, 4, 64, FAKE, FAKE, None) == abi.MSQ_E_INVAL
+    assert L.nf4_quantize(FAKE, -1, 64, FAKE, FAKE, None) == abi.MSQ_E_INVAL
+    assert L.nf4_quantize(FAKE + 2, 4, 64, FAKE, FAKE, None) == abi.MSQ_E_INVAL
+    assert L.nf4_quantize(FAKE, 0, 64, FAKE, FAKE, None) == 0            # empty: no-op
+    assert L.nf4_dequantize(FAKE, FAKE, 4, 32, FAKE, None) == abi.MSQ_E_SHAPE
+
+
+def _fwd(t=8, k=128, n=128, r=16, alpha=32.0, p=0.0, ws=None, x=FAKE, proj=0, layer=0, bias=None):
+    L = abi.lib()
+    need = L.nf4_lora_workspace_size(t, k, n, r)
+    return L.nf4_lora_fwd(x, t, k, n, FAKE, FAKE, bias, FAKE, FAKE, abi.LoraCfg(r, alpha, p),
+                          abi.RngKey(0, 0, 0, layer, proj), FAKE, None, FAKE,
+                          need if ws is None else ws, None)
+
+
+def test_linear_rejects_bad_arguments():
+    assert _fwd(k=96) == abi.MSQ_E_SHAPE
+    assert _fwd(n=100) == abi.MSQ_E_SHAPE
+    assert _fwd(r=65) == abi.MSQ_E_SHAPE
+    assert _fwd(r=-1) == abi.MSQ_E_SHAPE
+    assert _fwd(p=1.0) == abi.MSQ_E_DROPOUT
+    assert _fwd(p=-0.1) == abi.MSQ_E_DROPOUT
+    assert _fwd(p=float("nan")) == abi.MSQ_E_DROPOUT
+    assert _fwd(alpha=float("inf")) == abi.MSQ_E_DROPOUT
+    assert _fwd(ws=1024) == abi.MSQ_E_WORKSPACE
+    assert _fwd(x=FAKE + 8) == abi.MSQ_E_INVAL
+    assert _fwd(bias=FAKE + 2) == abi.MSQ_E_INVAL
+    assert _fwd(proj=16) == abi.MSQ_E_INVAL
+    assert _fwd(t=70000) == abi.MSQ_E_SHAPE
+    assert _fwd(t=0) == 0                                                 # empty: no-op
+    L = abi.lib()
+    need = L.nf4_lora_workspace_size(8, 128, 128, 16)
+    rc = L.nf4_lora_bwd(FAKE, FAKE, 8, 128, 128, FAKE, FAKE, FAKE, FAKE, abi.LoraCfg(16, 32.0, 0.0),
+                        abi.RngKey(), None, FAKE, 2, FAKE, FAKE, 0, FAKE, need, None)
+    assert rc == abi.MSQ_E_INVAL and "accumulate" in _err()
+    rc = L.nf4_lora_bwd(FAKE, FAKE, 8, 128, 128, FAKE, FAKE, FAKE, FAKE, abi.LoraCfg(16, 32.0, 0.0),
+                        abi.RngKey(), None, FAKE, 0, None, FAKE, 0, FAKE, need, None)
+    assert rc == abi.MSQ_E_INVAL
+
+
+def test_workspace_size_depends_on_shape_only():
+    L = abi.lib()
+    a = L.nf4_lora_workspace_size(512, 5120, 27648, 16)
+    b = L.nf4_lora_workspace_size(512, 5120, 27648, 16)
+    assert a == b > 512 * 27648 * 4
+    assert L.nf4_lora_workspace_size(512, 100, 64, 16) == 0
+    assert L.nf4_lora_workspace_size(0, 64, 64, 16) > 0
+
+
+def test_window_rejects_small_arena_and_names_what_fits():
+    L = abi.lib()
+    n = 8
+    ptrs = (ctypes.c_void_p * n)(*([FAKE] * n))
+    sizes = (ctypes.c_size_t * n)(*([1000 * 256] * n))
+    need = L.block_stream_arena_bytes(sizes, n, 4)
+    assert need == 2 * 4 * 1000 * 256
+    h = ctypes.c_void_p()
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, FAKE, need - 1, None)
+    assert rc == abi.MSQ_E_WINDOW
+    assert "window_blocks=3" in _err()
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, FAKE, 1000, None)
+    assert rc == abi.MSQ_E_WINDOW and "not even one layer" in _err()
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 9, FAKE, need, None) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, FAKE + 16, need, None) == abi.MSQ_E_INVAL
+    assert L.block_stream_prefetch(None, 0) == abi.MSQ_E_INVAL
+
+
+def test_timing_collect_without_records():
+    L = abi.lib()
+    n = ctypes.c_int(-1)
+    assert L.msq_timing_collect(None, 0, ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_strerror_covers_every_code():
+    L = abi.lib()
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert L.msq_strerror(code) and L.msq_strerror(code) != b"unknown error"
