@@ -106,11 +106,21 @@ typedef struct {
 } msq_rng_key;
 
 /* LoRA adapter configuration: scaling s = alpha / r; r == 0 means base only
- * (A, B, u are ignored and may be NULL). */
+ * (A, B, u are ignored and may be NULL).
+ * flags selects the activation dtypes:
+ *   MSQ_ACT_F32  x (forward and backward) and dy (backward) are fp32 instead of
+ *                bf16.  The base-weight contraction still runs on bf16 MFMA: the
+ *                library rounds the activation to bf16 (RNE) for that product only;
+ *                the rank-r LoRA products use the fp32 values.
+ *   MSQ_OUT_F32  y (forward) and dx (backward) are written (and, when
+ *                accumulating, read) as fp32 instead of bf16. */
+#define MSQ_ACT_F32 1u
+#define MSQ_OUT_F32 2u
 typedef struct {
-  int32_t r;     /* 0 .. 64 */
+  int32_t r;      /* 0 .. 64 */
   float alpha;
-  float p_drop;  /* dropout probability on the LoRA input, in [0, 1) */
+  float p_drop;   /* dropout probability on the LoRA input, in [0, 1) */
+  uint32_t flags; /* MSQ_ACT_F32 | MSQ_OUT_F32, other bits must be 0 */
 } msq_lora_cfg;
 
 /* Bytes of scratch device memory one nf4_lora_fwd or nf4_lora_bwd call with
@@ -122,20 +132,20 @@ size_t nf4_lora_workspace_size(int64_t t, int64_t k, int64_t n, int32_t r);
  *   u = drop(x) A^T                   (fp32, written to u_out when non-NULL)
  *   y = x W^T + bias + (alpha/r) u B^T
  * where W is the dequantized NF4 matrix [n, k] (dequantized in-tile, never
- * materialised).
- *   x      [t, k] bf16, 16-byte aligned            t >= 0, k % 64 == 0
+ * materialised).  x and y are bf16 unless cfg.flags says fp32 (see msq_lora_cfg).
+ *   x      [t, k], 16-byte aligned                  t >= 0, k % 64 == 0
  *   codes  [n, k/2] uint8, absmax [n, k/64] fp32     n % 64 == 0
  *   bias   [n] bf16 or NULL
  *   A      [r, k] fp32, B [n, r] fp32  (16-byte aligned)
- *   y      [t, n] bf16 output (16-byte aligned)
+ *   y      [t, n] output (16-byte aligned)
  *   u_out  [t, r] fp32 output or NULL
  *   workspace: device scratch of at least nf4_lora_workspace_size(t, k, n, r)
  *   bytes, 256-byte aligned; contents on entry are ignored.
  * t == 0 is a no-op (x, y may then be NULL).  t * k must stay below 2^34 (dropout
  * counter range) and t at most 65535. */
-int nf4_lora_fwd(const uint16_t* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
+int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
                  const float* absmax, const uint16_t* bias, const float* A, const float* B,
-                 msq_lora_cfg cfg, msq_rng_key key, uint16_t* y, float* u_out, void* workspace,
+                 msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out, void* workspace,
                  size_t workspace_bytes, msq_stream_t stream);
 
 /* Fused backward of the same layer (no gradient for W, absmax or bias: frozen).
@@ -143,17 +153,17 @@ int nf4_lora_fwd(const uint16_t* x, int64_t t, int64_t k, int64_t n, const uint8
  *   dB = s dy^T u
  *   dA = du^T drop(x)                 (mask replayed from key)
  *   dx = dy W + sigma * keep (.) (du A)
- *   dy [t, n] bf16, x [t, k] bf16 (the forward's input)
+ *   dy [t, n], x [t, k] (the forward's input): bf16, or fp32 with MSQ_ACT_F32
  *   u  [t, r] fp32 from the forward (or recompute), or NULL to recompute it here
- *   dx [t, k] bf16 output; dx_accumulate = 1 adds into the existing dx (in fp32,
- *      one rounding to bf16), 0 overwrites
+ *   dx [t, k] output (bf16, or fp32 with MSQ_OUT_F32); dx_accumulate = 1 adds into
+ *      the existing dx (the sum is formed in fp32 and rounded once), 0 overwrites
  *   dA [r, k] fp32, dB [n, r] fp32 outputs; dAB_accumulate = 1 adds into them
  *   dA/dB may be NULL only when r == 0.  With t == 0, dy, x and dx may be NULL and dA,
  *   dB are set to zero (or left unchanged when accumulating).
  * Shapes, alignment and workspace as for nf4_lora_fwd. */
-int nf4_lora_bwd(const uint16_t* dy, const uint16_t* x, int64_t t, int64_t k, int64_t n,
+int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
                  const uint8_t* codes, const float* absmax, const float* A, const float* B,
-                 msq_lora_cfg cfg, msq_rng_key key, const float* u, uint16_t* dx,
+                 msq_lora_cfg cfg, msq_rng_key key, const float* u, void* dx,
                  int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
                  size_t workspace_bytes, msq_stream_t stream);
 

@@ -28,8 +28,13 @@ class RngKey(ctypes.Structure):
                 ("layer", ctypes.c_uint32), ("proj", ctypes.c_uint32)]
 
 
+MSQ_ACT_F32 = 1
+MSQ_OUT_F32 = 2
+
+
 class LoraCfg(ctypes.Structure):
-    _fields_ = [("r", ctypes.c_int32), ("alpha", ctypes.c_float), ("p_drop", ctypes.c_float)]
+    _fields_ = [("r", ctypes.c_int32), ("alpha", ctypes.c_float), ("p_drop", ctypes.c_float),
+                ("flags", ctypes.c_uint32)]
 
 
 class WindowStats(ctypes.Structure):

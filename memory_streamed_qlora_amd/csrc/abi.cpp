@@ -52,6 +52,7 @@ int check_linear(const char* fn, int64_t t, int64_t k, int64_t n, const msq_lora
   if (!(cfg.p_drop >= 0.0f && cfg.p_drop < 1.0f)) return set_error(MSQ_E_DROPOUT, "%s: p_drop=%g outside [0, 1)", fn, (double)cfg.p_drop);
   if (cfg.r > 0 && !isfinite(cfg.alpha)) return set_error(MSQ_E_DROPOUT, "%s: alpha is not finite", fn);
   if (key.proj >= 16 || key.layer >= (1u << 28)) return set_error(MSQ_E_INVAL, "%s: rng key proj must be < 16 and layer < 2^28", fn);
+  if (cfg.flags & ~(MSQ_ACT_F32 | MSQ_OUT_F32)) return set_error(MSQ_E_INVAL, "%s: unknown flags 0x%x", fn, cfg.flags);
   return MSQ_OK;
 }
 
@@ -79,6 +80,8 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   o = align256(o + (size_t)p.fwd.splits * t * n * sizeof(float));
   p.off_u_fwd = o;
   o = align256(o + tr);
+  p.off_act_fwd = o;  // bf16 copy of fp32 activations for the MFMA operand
+  o = align256(o + (size_t)t * k * sizeof(uint16_t));
   p.fwd_bytes = o;
   p.nch = (int)((t + COLGRAD_TCHUNK - 1) / COLGRAD_TCHUNK);
   o = 0;
@@ -92,6 +95,8 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   o = align256(o + (size_t)p.nch * r * k * sizeof(float));
   p.off_pb = o;
   o = align256(o + (size_t)p.nch * r * n * sizeof(float));
+  p.off_act_bwd = o;
+  o = align256(o + (size_t)t * n * sizeof(uint16_t));
   p.bwd_bytes = o;
   return p;
 }
@@ -158,9 +163,9 @@ size_t nf4_lora_workspace_size(int64_t t, int64_t k, int64_t n, int32_t r) {
   return std::max<size_t>(256, std::max(p.fwd_bytes, p.bwd_bytes));  // 0 is reserved for "invalid"
 }
 
-int nf4_lora_fwd(const uint16_t* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
+int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
                  const float* absmax, const uint16_t* bias, const float* A, const float* B,
-                 msq_lora_cfg cfg, msq_rng_key key, uint16_t* y, float* u_out, void* workspace,
+                 msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out, void* workspace,
                  size_t workspace_bytes, msq_stream_t stream) {
   int rc = check_linear("nf4_lora_fwd", t, k, n, cfg, key);
   if (rc) return rc;
@@ -178,19 +183,27 @@ int nf4_lora_fwd(const uint16_t* x, int64_t t, int64_t k, int64_t n, const uint8
   char* ws = (char*)workspace;
   const int r = cfg.r;
   const Dropout d = make_dropout(key, cfg.p_drop);
+  const bool act_f32 = cfg.flags & MSQ_ACT_F32, out_f32 = cfg.flags & MSQ_OUT_F32;
   float* u = u_out ? u_out : (float*)(ws + p.off_u_fwd);
   float* part = (float*)(ws + p.off_part_fwd);
   const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
   hipError_t e = hipSuccess;
-  if (r > 0) e = launch_rowdot(x, t, k, A, 0, r, 1.0f, d, u, s);
-  if (e == hipSuccess) e = launch_gemm(0, x, codes, absmax, t, n, k, p.fwd, part, s);
-  if (e == hipSuccess) e = launch_fwd_epilogue(part, p.fwd.splits, t, n, bias, u, B, r, lscale, y, s);
+  const uint16_t* xb = (const uint16_t*)x;
+  if (act_f32) {
+    uint16_t* tmp = (uint16_t*)(ws + p.off_act_fwd);
+    e = launch_cvt_bf16((const float*)x, t * k, tmp, s);
+    xb = tmp;
+  }
+  if (e == hipSuccess && r > 0) e = launch_rowdot(x, act_f32, t, k, A, 0, r, 1.0f, d, u, s);
+  if (e == hipSuccess) e = launch_gemm(0, xb, codes, absmax, t, n, k, p.fwd, part, s);
+  if (e == hipSuccess)
+    e = launch_fwd_epilogue(part, p.fwd.splits, t, n, bias, u, B, r, lscale, y, out_f32, s);
   return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
 }
 
-int nf4_lora_bwd(const uint16_t* dy, const uint16_t* x, int64_t t, int64_t k, int64_t n,
+int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
                  const uint8_t* codes, const float* absmax, const float* A, const float* B,
-                 msq_lora_cfg cfg, msq_rng_key key, const float* u, uint16_t* dx,
+                 msq_lora_cfg cfg, msq_rng_key key, const float* u, void* dx,
                  int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
                  size_t workspace_bytes, msq_stream_t stream) {
   int rc = check_linear("nf4_lora_bwd", t, k, n, cfg, key);
@@ -214,20 +227,29 @@ int nf4_lora_bwd(const uint16_t* dy, const uint16_t* x, int64_t t, int64_t k, in
   const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
   hipError_t e = hipSuccess;
   if (t > 0) {
+    const bool act_f32 = cfg.flags & MSQ_ACT_F32, out_f32 = cfg.flags & MSQ_OUT_F32;
     float* part = (float*)(ws + p.off_part_bwd);
     float* du = (float*)(ws + p.off_du);
     const float* uu = u;
-    if (r > 0 && !uu) {
+    const uint16_t* dyb = (const uint16_t*)dy;
+    if (act_f32) {
+      uint16_t* tmp = (uint16_t*)(ws + p.off_act_bwd);
+      e = launch_cvt_bf16((const float*)dy, t * n, tmp, s);
+      dyb = tmp;
+    }
+    if (e == hipSuccess && r > 0 && !uu) {
       float* ut = (float*)(ws + p.off_u_bwd);
-      e = launch_rowdot(x, t, k, A, 0, r, 1.0f, d, ut, s);
+      e = launch_rowdot(x, act_f32, t, k, A, 0, r, 1.0f, d, ut, s);
       uu = ut;
     }
-    if (e == hipSuccess && r > 0) e = launch_rowdot(dy, t, n, B, 1, r, lscale, no_dropout(), du, s);
-    if (e == hipSuccess) e = launch_gemm(1, dy, codes, absmax, t, n, k, p.bwd, part, s);
+    if (e == hipSuccess && r > 0) e = launch_rowdot(dy, act_f32, t, n, B, 1, r, lscale, no_dropout(), du, s);
+    if (e == hipSuccess) e = launch_gemm(1, dyb, codes, absmax, t, n, k, p.bwd, part, s);
     if (e == hipSuccess)
-      e = launch_bwd_epilogue(part, p.bwd.splits, t, k, du, A, r, d, dx, dx_accumulate, s);
-    if (e == hipSuccess && r > 0) e = launch_colgrad(x, t, k, du, r, d, p.nch, (float*)(ws + p.off_pa), s);
-    if (e == hipSuccess && r > 0) e = launch_colgrad(dy, t, n, uu, r, no_dropout(), p.nch, (float*)(ws + p.off_pb), s);
+      e = launch_bwd_epilogue(part, p.bwd.splits, t, k, du, A, r, d, dx, out_f32, dx_accumulate, s);
+    if (e == hipSuccess && r > 0)
+      e = launch_colgrad(x, act_f32, t, k, du, r, d, p.nch, (float*)(ws + p.off_pa), s);
+    if (e == hipSuccess && r > 0)
+      e = launch_colgrad(dy, act_f32, t, n, uu, r, no_dropout(), p.nch, (float*)(ws + p.off_pb), s);
   }
   if (e == hipSuccess && r > 0)
     e = launch_colgrad_reduce((float*)(ws + p.off_pa), p.nch, r, k, 1.0f, dA, k, 1, dAB_accumulate, s);

@@ -32,8 +32,8 @@ GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red);
 
 struct LoraPlan {
   GemmPlan fwd, bwd;
-  size_t off_part_fwd, off_u_fwd;            // fwd layout
-  size_t off_part_bwd, off_u_bwd, off_du, off_pa, off_pb;  // bwd layout
+  size_t off_part_fwd, off_u_fwd, off_act_fwd;                   // fwd layout
+  size_t off_part_bwd, off_u_bwd, off_du, off_pa, off_pb, off_act_bwd;  // bwd layout
   int nch;                                   // T-chunks of the dA/dB reductions
   size_t fwd_bytes, bwd_bytes;
 };
@@ -52,26 +52,29 @@ hipError_t launch_gemm(int mode, const uint16_t* act, const uint8_t* codes, cons
                        int64_t M, int64_t N, int64_t K, const GemmPlan& plan, float* part,
                        hipStream_t s);
 
+// Activations `in` are bf16 (uint16_t) or fp32 (in_f32).
 // out[t][j] = scale * sum_c h[t][c] * mat(j, c), h = drop(in) (dropout optional)
 //   mat_kind 0: mat is [r][C] (LoRA A);   mat_kind 1: mat is [C][r] (LoRA B)
-hipError_t launch_rowdot(const uint16_t* in, int64_t T, int64_t C, const float* mat, int mat_kind,
-                         int r, float scale, const Dropout& d, float* out, hipStream_t s);
+hipError_t launch_rowdot(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat,
+                         int mat_kind, int r, float scale, const Dropout& d, float* out, hipStream_t s);
 
 // part[ch][j][c] = sum_{t in chunk ch} coef[t][j] * h[t][c], h = drop(in)
-hipError_t launch_colgrad(const uint16_t* in, int64_t T, int64_t C, const float* coef, int r,
+hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
                           const Dropout& d, int nch, float* part, hipStream_t s);
 // out(j, c) = [out(j, c) +] scale * sum_ch part[ch][j][c];  out(j,c) = out[j*sj + c*sc]
 hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale,
                                  float* out, int64_t sj, int64_t sc, int accumulate, hipStream_t s);
 
-// y[t][n] = bf16(sum_s part[s][t][n] + bias[n] + lscale * sum_j u[t][j] B[n][j])
+// y[t][n] = out(sum_s part[s][t][n] + bias[n] + lscale * sum_j u[t][j] B[n][j]); y bf16 or fp32
 hipError_t launch_fwd_epilogue(const float* part, int splits, int64_t T, int64_t N,
                                const uint16_t* bias, const float* u, const float* B, int r,
-                               float lscale, uint16_t* y, hipStream_t s);
-// dx[t][k] = bf16([dx_old +] sum_s part[s][t][k] + sigma*keep(t,k)*sum_j du[t][j] A[j][k])
+                               float lscale, void* y, bool out_f32, hipStream_t s);
+// dx[t][k] = out([dx_old +] sum_s part[s][t][k] + sigma*keep(t,k)*sum_j du[t][j] A[j][k])
 hipError_t launch_bwd_epilogue(const float* part, int splits, int64_t T, int64_t K,
                                const float* du, const float* A, int r, const Dropout& d,
-                               uint16_t* dx, int accumulate, hipStream_t s);
+                               void* dx, bool out_f32, int accumulate, hipStream_t s);
+// out[i] = bf16_rne(in[i]) for n elements (n % 8 == 0)
+hipError_t launch_cvt_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s);
 
 // ---- timing -------------------------------------------------------------------
 bool timing_on();

@@ -7,7 +7,9 @@
 //                   fixed-size chunks and then summed in chunk order
 //   epilogues       sum the split-reduction partials of the base GEMM in split order
 //                   and add bias and the LoRA term (forward) or the masked LoRA input
-//                   gradient (backward), then round once to bf16.
+//                   gradient (backward), then round once to bf16 (or store fp32).
+// Activations may be bf16 or fp32; with fp32 the rank-r products use the fp32
+// values and only the MFMA operand of the base product is rounded to bf16.
 // Every reduction has a fixed shape-determined order and no atomics, so results are
 // bitwise reproducible.  Dropout masks are regenerated from the Philox key wherever
 // they are needed; the same key gives the same mask in the forward, the recompute and
@@ -19,7 +21,8 @@ namespace {
 
 constexpr int RD_THREADS = 256;
 
-// Eight bf16 at 16-byte aligned p -> floats
+// Activation element types: bf16 bit patterns (uint16_t) or fp32.
+// Eight consecutive elements at p (16-byte aligned for bf16, 32 for fp32) -> floats.
 __device__ __forceinline__ void load8(const uint16_t* p, float f[8]) {
   const uint4 q = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -29,10 +32,35 @@ __device__ __forceinline__ void load8(const uint16_t* p, float f[8]) {
     f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
 }
+__device__ __forceinline__ void load8(const float* p, float f[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void load4(const uint16_t* p, float f[4]) {
+  const uint2 raw = *reinterpret_cast<const uint2*>(p);
+  f[0] = bf16_to_f32(raw.x & 0xffffu);
+  f[1] = bf16_to_f32(raw.x >> 16);
+  f[2] = bf16_to_f32(raw.y & 0xffffu);
+  f[3] = bf16_to_f32(raw.y >> 16);
+}
+__device__ __forceinline__ void load4(const float* p, float f[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+}
+// Four output values at p: one rounding to bf16, or stored as fp32.
+__device__ __forceinline__ void store4(uint16_t* p, const float a[4]) {
+  *reinterpret_cast<uint2*>(p) =
+      make_uint2(bf16_rne(a[0]) | (bf16_rne(a[1]) << 16), bf16_rne(a[2]) | (bf16_rne(a[3]) << 16));
+}
+__device__ __forceinline__ void store4(float* p, const float a[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(a[0], a[1], a[2], a[3]);
+}
 
 // out[t][j] = scale * sum_c h[t][c] * mat(j, c); one workgroup per row t.
-template <int RT, int MAT_KIND>
-__global__ __launch_bounds__(RD_THREADS) void lora_rowdot(const uint16_t* __restrict__ in, int64_t C,
+template <int RT, int MAT_KIND, typename TIN>
+__global__ __launch_bounds__(RD_THREADS) void lora_rowdot(const TIN* __restrict__ in, int64_t C,
                                                           const float* __restrict__ mat, int r,
                                                           float scale, Dropout d,
                                                           float* __restrict__ out) {
@@ -41,7 +69,7 @@ __global__ __launch_bounds__(RD_THREADS) void lora_rowdot(const uint16_t* __rest
   float acc[RT];
 #pragma unroll
   for (int j = 0; j < RT; ++j) acc[j] = 0.0f;
-  const uint16_t* row = in + t * C;
+  const TIN* row = in + t * C;
   for (int64_t c = 8 * (int64_t)tid; c < C; c += 8 * RD_THREADS) {
     float h[8];
     load8(row + c, h);
@@ -106,7 +134,8 @@ __global__ __launch_bounds__(RD_THREADS) void lora_rowdot(const uint16_t* __rest
 constexpr int CG_THREADS = 64;
 constexpr int CG_J = 16;
 
-__global__ __launch_bounds__(CG_THREADS) void lora_colgrad(const uint16_t* __restrict__ in, int64_t T,
+template <typename TIN>
+__global__ __launch_bounds__(CG_THREADS) void lora_colgrad(const TIN* __restrict__ in, int64_t T,
                                                            int64_t C, const float* __restrict__ coef,
                                                            int r, Dropout d, int tchunk,
                                                            float* __restrict__ part) {
@@ -129,9 +158,8 @@ __global__ __launch_bounds__(CG_THREADS) void lora_colgrad(const uint16_t* __res
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
   for (int64_t t = t0; t < t1; ++t) {
-    const uint2 raw = *reinterpret_cast<const uint2*>(in + t * C + c);
-    float h[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
-                  bf16_to_f32(raw.y >> 16)};
+    float h[4];
+    load4(in + t * C + c, h);
     if (d.threshold != 0u) {
       const uint32_t keep = keep4(d, (uint64_t)t * (uint64_t)C + (uint64_t)c);
 #pragma unroll
@@ -168,13 +196,14 @@ __global__ __launch_bounds__(256) void lora_colgrad_reduce(const float* __restri
   *o = accumulate ? (*o + s) : s;
 }
 
-// y[t][n..n+3] = bf16(sum_s P + bias + lscale * u[t] . B[n])
+// y[t][n..n+3] = out(sum_s P + bias + lscale * u[t] . B[n])
+template <typename TOUT>
 __global__ __launch_bounds__(256) void lora_fwd_epilogue(const float* __restrict__ part, int splits,
                                                          int64_t T, int64_t N,
                                                          const uint16_t* __restrict__ bias,
                                                          const float* __restrict__ u,
                                                          const float* __restrict__ B, int r,
-                                                         float lscale, uint16_t* __restrict__ y) {
+                                                         float lscale, TOUT* __restrict__ y) {
   const int64_t t = blockIdx.y;
   const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= N) return;
@@ -203,17 +232,16 @@ __global__ __launch_bounds__(256) void lora_fwd_epilogue(const float* __restrict
       a[q] += lscale * l;
     }
   }
-  const uint32_t lo = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
-  const uint32_t hi = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
-  *reinterpret_cast<uint2*>(y + t * N + n) = make_uint2(lo, hi);
+  store4(y + t * N + n, a);
 }
 
-// dx[t][k..k+3] = bf16([dx_old +] (sum_s P + sigma*keep*(du[t] . A[:,k])))
+// dx[t][k..k+3] = out([dx_old +] (sum_s P + sigma*keep*(du[t] . A[:,k])))
+template <typename TOUT>
 __global__ __launch_bounds__(256) void lora_bwd_epilogue(const float* __restrict__ part, int splits,
                                                          int64_t T, int64_t K,
                                                          const float* __restrict__ du,
                                                          const float* __restrict__ A, int r,
-                                                         Dropout d, uint16_t* __restrict__ dx,
+                                                         Dropout d, TOUT* __restrict__ dx,
                                                          int accumulate) {
   const int64_t t = blockIdx.y;
   const int64_t k = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -241,46 +269,64 @@ __global__ __launch_bounds__(256) void lora_bwd_epilogue(const float* __restrict
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] += ((keep >> q) & 1u) ? d.sigma * l[q] : 0.0f;
   }
-  uint2* o = reinterpret_cast<uint2*>(dx + t * K + k);
+  TOUT* o = dx + t * K + k;
   if (accumulate) {
-    const uint2 old = *o;
-    a[0] = bf16_to_f32(old.x & 0xffffu) + a[0];
-    a[1] = bf16_to_f32(old.x >> 16) + a[1];
-    a[2] = bf16_to_f32(old.y & 0xffffu) + a[2];
-    a[3] = bf16_to_f32(old.y >> 16) + a[3];
+    float old[4];
+    load4(o, old);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = old[q] + a[q];
   }
-  *o = make_uint2(bf16_rne(a[0]) | (bf16_rne(a[1]) << 16), bf16_rne(a[2]) | (bf16_rne(a[3]) << 16));
+  store4(o, a);
 }
 
-template <int MAT_KIND>
-hipError_t rowdot_dispatch(const uint16_t* in, int64_t T, int64_t C, const float* mat, int r,
-                           float scale, const Dropout& d, float* out, hipStream_t s) {
+// Round fp32 activations to bf16 (RNE) for the MFMA operand; 8 per thread.
+__global__ __launch_bounds__(256) void cvt_f32_bf16(const float* __restrict__ in, int64_t n8,
+                                                    uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  float f[8];
+  load8(in + 8 * i, f);
+  *reinterpret_cast<uint4*>(out + 8 * i) =
+      make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
+                 bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
+}
+
+template <int MAT_KIND, typename TIN>
+hipError_t rowdot_dispatch(const TIN* in, int64_t T, int64_t C, const float* mat, int r, float scale,
+                           const Dropout& d, float* out, hipStream_t s) {
   const dim3 grid((unsigned)T), block(RD_THREADS);
   if (r <= 16)
-    hipLaunchKernelGGL((lora_rowdot<16, MAT_KIND>), grid, block, 0, s, in, C, mat, r, scale, d, out);
+    hipLaunchKernelGGL((lora_rowdot<16, MAT_KIND, TIN>), grid, block, 0, s, in, C, mat, r, scale, d, out);
   else if (r <= 32)
-    hipLaunchKernelGGL((lora_rowdot<32, MAT_KIND>), grid, block, 0, s, in, C, mat, r, scale, d, out);
+    hipLaunchKernelGGL((lora_rowdot<32, MAT_KIND, TIN>), grid, block, 0, s, in, C, mat, r, scale, d, out);
   else
-    hipLaunchKernelGGL((lora_rowdot<64, MAT_KIND>), grid, block, 0, s, in, C, mat, r, scale, d, out);
+    hipLaunchKernelGGL((lora_rowdot<64, MAT_KIND, TIN>), grid, block, 0, s, in, C, mat, r, scale, d, out);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_rowdot(const uint16_t* in, int64_t T, int64_t C, const float* mat, int mat_kind,
-                         int r, float scale, const Dropout& d, float* out, hipStream_t s) {
+hipError_t launch_rowdot(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat,
+                         int mat_kind, int r, float scale, const Dropout& d, float* out, hipStream_t s) {
   if (T == 0 || r == 0) return hipSuccess;
-  return mat_kind == 0 ? rowdot_dispatch<0>(in, T, C, mat, r, scale, d, out, s)
-                       : rowdot_dispatch<1>(in, T, C, mat, r, scale, d, out, s);
+  if (in_f32)
+    return mat_kind == 0 ? rowdot_dispatch<0>((const float*)in, T, C, mat, r, scale, d, out, s)
+                         : rowdot_dispatch<1>((const float*)in, T, C, mat, r, scale, d, out, s);
+  return mat_kind == 0 ? rowdot_dispatch<0>((const uint16_t*)in, T, C, mat, r, scale, d, out, s)
+                       : rowdot_dispatch<1>((const uint16_t*)in, T, C, mat, r, scale, d, out, s);
 }
 
-hipError_t launch_colgrad(const uint16_t* in, int64_t T, int64_t C, const float* coef, int r,
+hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
                           const Dropout& d, int nch, float* part, hipStream_t s) {
   if (T == 0 || r == 0) return hipSuccess;
   const dim3 grid((unsigned)((C / 4 + CG_THREADS - 1) / CG_THREADS), (unsigned)nch,
                   (unsigned)((r + CG_J - 1) / CG_J));
-  hipLaunchKernelGGL(lora_colgrad, grid, dim3(CG_THREADS), 0, s, in, T, C, coef, r, d,
-                     COLGRAD_TCHUNK, part);
+  if (in_f32)
+    hipLaunchKernelGGL(lora_colgrad<float>, grid, dim3(CG_THREADS), 0, s, (const float*)in, T, C, coef,
+                       r, d, COLGRAD_TCHUNK, part);
+  else
+    hipLaunchKernelGGL(lora_colgrad<uint16_t>, grid, dim3(CG_THREADS), 0, s, (const uint16_t*)in, T, C,
+                       coef, r, d, COLGRAD_TCHUNK, part);
   return hipGetLastError();
 }
 
@@ -295,21 +341,36 @@ hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, f
 
 hipError_t launch_fwd_epilogue(const float* part, int splits, int64_t T, int64_t N,
                                const uint16_t* bias, const float* u, const float* B, int r,
-                               float lscale, uint16_t* y, hipStream_t s) {
+                               float lscale, void* y, bool out_f32, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 grid((unsigned)((N / 4 + 255) / 256), (unsigned)T);
-  hipLaunchKernelGGL(lora_fwd_epilogue, grid, dim3(256), 0, s, part, splits, T, N, bias, u, B, r,
-                     lscale, y);
+  if (out_f32)
+    hipLaunchKernelGGL(lora_fwd_epilogue<float>, grid, dim3(256), 0, s, part, splits, T, N, bias, u, B,
+                       r, lscale, (float*)y);
+  else
+    hipLaunchKernelGGL(lora_fwd_epilogue<uint16_t>, grid, dim3(256), 0, s, part, splits, T, N, bias, u,
+                       B, r, lscale, (uint16_t*)y);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_epilogue(const float* part, int splits, int64_t T, int64_t K,
                                const float* du, const float* A, int r, const Dropout& d,
-                               uint16_t* dx, int accumulate, hipStream_t s) {
+                               void* dx, bool out_f32, int accumulate, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 grid((unsigned)((K / 4 + 255) / 256), (unsigned)T);
-  hipLaunchKernelGGL(lora_bwd_epilogue, grid, dim3(256), 0, s, part, splits, T, K, du, A, r, d, dx,
-                     accumulate);
+  if (out_f32)
+    hipLaunchKernelGGL(lora_bwd_epilogue<float>, grid, dim3(256), 0, s, part, splits, T, K, du, A, r,
+                       d, (float*)dx, accumulate);
+  else
+    hipLaunchKernelGGL(lora_bwd_epilogue<uint16_t>, grid, dim3(256), 0, s, part, splits, T, K, du, A,
+                       r, d, (uint16_t*)dx, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_cvt_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(cvt_f32_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, in, n8, out);
   return hipGetLastError();
 }
 

@@ -119,8 +119,18 @@ class Lora:
     alpha: float = 32.0
     p_drop: float = 0.0
 
-    def c(self) -> LoraCfg:
-        return LoraCfg(self.r, self.alpha, self.p_drop)
+    def c(self, flags: int = 0) -> LoraCfg:
+        return LoraCfg(self.r, self.alpha, self.p_drop, flags)
+
+
+_ACT_DTYPES = (torch.bfloat16, torch.float32)
+
+
+def _flags(act_dtype: torch.dtype, out_dtype: torch.dtype) -> int:
+    if act_dtype not in _ACT_DTYPES or out_dtype not in _ACT_DTYPES:
+        raise TypeError("activations and outputs must be bfloat16 or float32")
+    return (_abi.MSQ_ACT_F32 if act_dtype == torch.float32 else 0) | \
+           (_abi.MSQ_OUT_F32 if out_dtype == torch.float32 else 0)
 
 
 def rng_key(seed: int = 0, step: int = 0, micro: int = 0, layer: int = 0, proj: int = 0) -> RngKey:
@@ -131,11 +141,16 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
                  bias: Optional[torch.Tensor], A: Optional[torch.Tensor], B: Optional[torch.Tensor],
                  cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
                  u_out: Optional[torch.Tensor] = None, want_u: bool = True,
-                 workspace: Optional[Workspace] = None, stream=None):
-    """y = x W^T + bias + (alpha/r) drop(x) A^T B^T.  Returns (y, u) (u None if not wanted)."""
+                 workspace: Optional[Workspace] = None, stream=None,
+                 out_dtype: Optional[torch.dtype] = None):
+    """y = x W^T + bias + (alpha/r) drop(x) A^T B^T.  Returns (y, u) (u None if not wanted).
+
+    x may be bf16 or fp32; y is out_dtype (default: x's dtype, or y's if given)."""
     t, k = x.shape
     n = codes.shape[0]
-    _req(x, "x", torch.bfloat16, (t, k))
+    _req(x, "x", x.dtype, (t, k))
+    out_dtype = out_dtype or (y.dtype if y is not None else x.dtype)
+    flags = _flags(x.dtype, out_dtype)
     _req(codes, "codes", torch.uint8, (n, k // 2))
     _req(absmax, "absmax", torch.float32, (n, k // 64))
     if bias is not None:
@@ -145,8 +160,8 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
         _req(A, "A", torch.float32, (r, k))
         _req(B, "B", torch.float32, (n, r))
     if y is None:
-        y = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
-    _req(y, "y", torch.bfloat16, (t, n))
+        y = torch.empty((t, n), dtype=out_dtype, device=x.device)
+    _req(y, "y", out_dtype, (t, n))
     if want_u and r > 0 and u_out is None:
         u_out = torch.empty((t, r), dtype=torch.float32, device=x.device)
     if u_out is not None:
@@ -155,7 +170,7 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
     ws = _workspace(x.device, need, workspace)
     check("nf4_lora_fwd", lib().nf4_lora_fwd(
         _ptr(x), t, k, n, _ptr(codes), _ptr(absmax), _ptr(bias), _ptr(A) if r > 0 else None,
-        _ptr(B) if r > 0 else None, cfg.c(), key, _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(),
+        _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(),
         _stream(stream)))
     return y, u_out
 
@@ -165,12 +180,16 @@ def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax:
                  u: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
                  dx_accumulate: bool = False, dA: Optional[torch.Tensor] = None,
                  dB: Optional[torch.Tensor] = None, dAB_accumulate: bool = False,
-                 workspace: Optional[Workspace] = None, stream=None):
-    """Returns (dx, dA, dB); dA/dB are None when r == 0."""
+                 workspace: Optional[Workspace] = None, stream=None,
+                 out_dtype: Optional[torch.dtype] = None):
+    """Returns (dx, dA, dB); dA/dB are None when r == 0.  dy and x share one dtype (bf16
+    or fp32); dx is out_dtype (default: dx's dtype if given, else the activations')."""
     t, k = x.shape
     n = codes.shape[0]
-    _req(dy, "dy", torch.bfloat16, (t, n))
-    _req(x, "x", torch.bfloat16, (t, k))
+    _req(x, "x", x.dtype, (t, k))
+    _req(dy, "dy", x.dtype, (t, n))
+    out_dtype = out_dtype or (dx.dtype if dx is not None else x.dtype)
+    flags = _flags(x.dtype, out_dtype)
     _req(codes, "codes", torch.uint8, (n, k // 2))
     _req(absmax, "absmax", torch.float32, (n, k // 64))
     r = cfg.r
@@ -186,13 +205,13 @@ def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax:
         if u is not None:
             _req(u, "u", torch.float32, (t, r))
     if dx is None:
-        dx = torch.empty((t, k), dtype=torch.bfloat16, device=x.device)
-    _req(dx, "dx", torch.bfloat16, (t, k))
+        dx = torch.empty((t, k), dtype=out_dtype, device=x.device)
+    _req(dx, "dx", out_dtype, (t, k))
     need = nf4_lora_workspace_size(t, k, n, r)
     ws = _workspace(x.device, need, workspace)
     check("nf4_lora_bwd", lib().nf4_lora_bwd(
         _ptr(dy), _ptr(x), t, k, n, _ptr(codes), _ptr(absmax), _ptr(A) if r > 0 else None,
-        _ptr(B) if r > 0 else None, cfg.c(), key, _ptr(u) if r > 0 else None, _ptr(dx),
+        _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(u) if r > 0 else None, _ptr(dx),
         int(dx_accumulate), _ptr(dA) if r > 0 else None, _ptr(dB) if r > 0 else None,
         int(dAB_accumulate), _ptr(ws), ws.numel(), _stream(stream)))
     return dx, (dA if r > 0 else None), (dB if r > 0 else None)

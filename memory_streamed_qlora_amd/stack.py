@@ -13,10 +13,11 @@ package README, "How it works"):
   update    one AdamW step on the fp32 adapters, identical to the resident run's.
 Resident mode runs the same code with every layer's blob already in device memory.
 
-Every projection goes through the library (nf4_lora_fwd / nf4_lora_bwd); the glue
-between them -- RMSNorm, RoPE from precomputed tables, causal GQA attention in fp32,
-SwiGLU, residual adds, embedding gather, lm_head and cross-entropy, AdamW -- is
-plain PyTorch and deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and
+Every projection goes through the library (nf4_lora_fwd / nf4_lora_bwd) with fp32
+activations in and out; the library rounds them to bf16 only as the MFMA operand of
+the frozen-base product.  The glue between projections -- RMSNorm, RoPE from
+precomputed tables, causal GQA attention, SwiGLU, residual adds, embedding gather,
+lm_head and cross-entropy, AdamW -- is plain fp32 PyTorch and deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and
 optimizer settings are readings of the Qwen2 family and of textbook AdamW; the pages
 name neither.
 """
@@ -274,20 +275,21 @@ class Stack:
                                views[(proj, "absmax")], bias, self.cfg, key)
 
     def layer_forward(self, h: torch.Tensor, l: int, views, step: int, micro: int = 0) -> torch.Tensor:
+        """Activations stay fp32; the library rounds them to bf16 only as MFMA operands."""
         sh = self.shape
         T = h.shape[0]
-        xn = rmsnorm(h, self.ln1[l]).to(torch.bfloat16)
-        q = self._lin(xn, l, views, "q", step, micro).float().view(T, sh.heads, sh.head_dim)
-        k = self._lin(xn, l, views, "k", step, micro).float().view(T, sh.kv_heads, sh.head_dim)
-        v = self._lin(xn, l, views, "v", step, micro).float().view(T, sh.kv_heads, sh.head_dim)
+        xn = rmsnorm(h, self.ln1[l])
+        q = self._lin(xn, l, views, "q", step, micro).view(T, sh.heads, sh.head_dim)
+        k = self._lin(xn, l, views, "k", step, micro).view(T, sh.kv_heads, sh.head_dim)
+        v = self._lin(xn, l, views, "v", step, micro).view(T, sh.kv_heads, sh.head_dim)
         cos, sin = self.cos[:T], self.sin[:T]
         att = causal_gqa_attention(rope(q, cos, sin), rope(k, cos, sin), v, self.mask_add[:T, :T])
-        h1 = h + self._lin(att.to(torch.bfloat16), l, views, "o", step, micro).float()
-        xn2 = rmsnorm(h1, self.ln2[l]).to(torch.bfloat16)
-        g = self._lin(xn2, l, views, "gate", step, micro).float()
-        u = self._lin(xn2, l, views, "up", step, micro).float()
-        a = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
-        return h1 + self._lin(a, l, views, "down", step, micro).float()
+        h1 = h + self._lin(att, l, views, "o", step, micro)
+        xn2 = rmsnorm(h1, self.ln2[l])
+        g = self._lin(xn2, l, views, "gate", step, micro)
+        u = self._lin(xn2, l, views, "up", step, micro)
+        a = torch.nn.functional.silu(g) * u
+        return h1 + self._lin(a, l, views, "down", step, micro)
 
     # -- base residency --------------------------------------------------------------
     def _views(self, l: int):

@@ -77,6 +77,33 @@ def test_odd_shapes(T, K, N, r):
                           name=f"T{T} K{K} N{N} r{r}")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fp32_activations(out_dtype):
+    """fp32 x and dy (not bf16-representable): the base product sees bf16(x) on MFMA,
+    the LoRA products the fp32 values; outputs in fp32 or bf16."""
+    rng = np.random.default_rng(21)
+    T, K, N, r, p = 300, 512, 384, 16, 0.1
+    inp = mi.linear_inputs(2, 2, 7, "gate", K, N, T, mi.LoraSpec(r, 32.0, p), with_bias=True)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    dy = rng.standard_normal((T, N)).astype(np.float32)
+    codes, a = _quant(inp["W"])
+    key = olora.RngKey(seed=3, step=2, layer=1, proj=4)
+    c_d, a_d = torch.from_numpy(codes).cuda(), dev_f32(a)
+    A, B, b = dev_f32(inp["A"]), dev_f32(inp["B"]), dev_bf16(inp["bias"])
+    cfg, k = msq.Lora(r, 32.0, p), msq.rng_key(3, 2, 0, 1, 4)
+    y, u = msq.nf4_lora_fwd(dev_f32(x), c_d, a_d, b, A, B, cfg, k, out_dtype=out_dtype)
+    dx, dA, dB = msq.nf4_lora_bwd(dev_f32(dy), dev_f32(x), c_d, a_d, A, B, cfg, k, u=u, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert y.dtype == out_dtype and dx.dtype == out_dtype
+    ry, ru = olora.fwd(x, codes, a, inp["bias"], inp["A"], inp["B"], 32.0, p, key)
+    rdx, rdA, rdB = olora.bwd(dy, x, codes, a, inp["A"], inp["B"], 32.0, p, key)
+    r_ = {n_: assert_parity(host_f64(g), rf, name=n_) for n_, g, rf in
+          (("y", y, ry), ("u", u, ru), ("dx", dx, rdx), ("dA", dA, rdA), ("dB", dB, rdB))}
+    print("fp32 activations", out_dtype, {k_: f"{v:.2e}" for k_, v in r_.items()}, flush=True)
+    # the LoRA path sees the fp32 values: u is far more accurate than a bf16 input allows
+    assert r_["u"] < 1e-4
+
+
 def test_b_zero_equals_base_only_call():
     inp = mi.cfg1_inputs()
     inp = dict(inp, B=np.zeros_like(inp["B"]))
