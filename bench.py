@@ -1,0 +1,240 @@
+"""Benchmark: streamed NF4 + LoRA training step of a Qwen2.5-32B-shaped stack on one GPU.
+
+Workload: 64 decoder layers (hidden 5120, 40/8 heads, SwiGLU 27648), random N(0, 0.02)
+base quantized to NF4 and held in pinned host memory, streamed through a two-slot
+device window of 4 blocks; LoRA r16 alpha32 dropout 0.0 on all seven projections;
+batch 1 x 512 random tokens over a 152064-entry vocabulary; one AdamW step per
+training step.  A step is the whole hot path: forward with streaming, loss, backward
+with reload + recompute, AdamW.  tokens/s = 512 * steps / timed seconds.
+
+Prints one JSON line (see the fields below); --gpus N > 1 exits: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/s (s/step) streamed NF4-LoRA fwd+bwd, 32B shape; MFMA util"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+PAGES_A100_S_PER_STEP = 2.0489  # Official A100 results, Benchmark matrix, Qwen2.5-32B streamed
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def h2d_ceiling_gbps(torch, nbytes=1 << 30, reps=10) -> float:
+    """Median pinned host->device copy rate of one 1 GiB buffer with nothing else running."""
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    h.fill_(1)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    ts = []
+    for i in range(reps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record()
+            d.copy_(h, non_blocking=True)
+            e1.record()
+        e1.synchronize()
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    del h, d
+    return nbytes / 1e6 / ts[len(ts) // 2]
+
+
+def copy_calibration(torch, nbytes=256 << 20) -> None:
+    """A plain device copy of known size (256 MiB read + 256 MiB write) so hardware byte
+    counters of the same run can be scaled."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(3)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(seconds_hint=True) -> dict:
+    """The oracle, untuned, on a bounded sample of the same workload: one Qwen2.5-32B-
+    shaped layer at 512 tokens -- its first forward, the recompute and the backward
+    (all seven NF4 + LoRA projections plus the block glue) -- then scaled to the step
+    (64 layers; the lm_head and loss are added from one timed fp64 lm_head pass)."""
+    import numpy as np
+
+    import msq_inputs as mi
+    from oracle import block as oblock
+    from oracle import lora as olora
+    from oracle import step as ostep
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    sh, T = mi.QWEN25_32B, 512
+    lo = mi.LoraSpec(16, 32.0, 0.0)
+    t_setup = time.time()
+    prm = mi.block_params(0, 4, 0, sh, lo)
+    qp = oblock.quantize_params(prm)
+    io = mi.block_io(0, 4, sh, T)
+    log(f"cpu baseline setup {time.time() - t_setup:.1f}s")
+    rk = olora.RngKey(seed=0, step=0)
+    t0 = time.perf_counter()
+    oblock.forward(io["x"], qp, sh, 0, lo.alpha, lo.p_drop, rk)
+    _, cache = oblock.forward(io["x"], qp, sh, 0, lo.alpha, lo.p_drop, rk)
+    oblock.backward(io["dy"], cache, qp, sh, 0, lo.alpha, lo.p_drop, rk)
+    t_layer = time.perf_counter() - t0
+    # lm_head + loss + its input gradient, on a 1/16 slice of the vocabulary, scaled
+    V = sh.vocab // 16
+    rng = np.random.default_rng(0)
+    lm = mi.round_to_bf16((0.02 * rng.standard_normal((V, sh.hidden))).astype(np.float32))
+    h = io["x"].astype(np.float64)
+    t1 = time.perf_counter()
+    logits = h @ lm.astype(np.float64).T
+    toks = rng.integers(0, V, T)
+    _, dlog = ostep.loss_and_dlogits(logits, toks)
+    dlog @ lm.astype(np.float64)
+    t_head = (time.perf_counter() - t1) * 16
+    step_s = sh.layers * t_layer + t_head
+    return {"value": T / step_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"one Qwen2.5-32B-shaped layer at 512 tokens (forward, recompute, backward; "
+                       f"{t_layer:.1f}s) x 64 layers + lm_head/loss on 1/16 of the vocabulary x 16 "
+                       f"({t_head:.1f}s); extrapolated s/step {step_s:.0f}"),
+            "s_per_step_extrapolated": step_s}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=64, help="stack depth (64 = the 32B shape)")
+    ap.add_argument("--no-resident", action="store_true", help="skip the resident comparison run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs the hot path on one GPU only; --gpus must be 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from memory_streamed_qlora_amd import ops, stack as S
+
+    torch.cuda.set_device(0)
+    shape = S.Shape(5120, 40, 8, 128, 27648, args.layers)
+    T = 512
+    ceiling = h2d_ceiling_gbps(torch)
+    log(f"H2D ceiling (1 GiB pinned, median of 10): {ceiling:.1f} GB/s")
+    copy_calibration(torch)
+
+    def run(mode: str):
+        t_build = time.time()
+        st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=0.0, window_blocks=4,
+                            mode=mode)
+        torch.cuda.synchronize()
+        log(f"{mode}: built {args.layers} layers in {time.time() - t_build:.1f}s "
+            f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
+        for w in range(args.warmup):
+            loss, gn = st.train_step(S.random_tokens(0, w, T, shape.vocab, st.dev))
+            torch.cuda.synchronize()
+            log(f"{mode}: warmup step {w} loss {loss.item():.4f} grad-norm {gn.item():.4e}")
+        toks = [S.random_tokens(0, 1000 + s, T, shape.vocab, st.dev) for s in range(args.steps)]
+        stats0 = st.window.stats() if st.window else None
+        torch.cuda.reset_peak_memory_stats()
+        ops.timing_enable(True)
+        ops.timing_collect()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        losses = []
+        for s in range(args.steps):
+            loss, gn = st.train_step(toks[s])
+            losses.append(loss)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        ops.timing_enable(False)
+        kt = ops.timing_collect()
+        stats1 = st.window.stats() if st.window else None
+        out = {"seconds": dt, "losses": [l.item() for l in losses], "kernels": kt,
+               "peak_alloc_gb": torch.cuda.max_memory_allocated() / 1e9,
+               "window": None}
+        if stats0:
+            out["window"] = {k: (stats1[k] - stats0[k]) / args.steps for k in stats1}
+        log(f"{mode}: {args.steps} steps in {dt:.3f}s -> {dt / args.steps * 1e3:.1f} ms/step; "
+            f"losses {[round(x, 4) for x in out['losses']]}")
+        st.close()
+        del st
+        torch.cuda.empty_cache()
+        return out
+
+    streamed = run("streamed")
+    resident = None if args.no_resident else run("resident")
+
+    ms = streamed["seconds"] / args.steps * 1e3
+    value = T * args.steps / streamed["seconds"]
+    # roofline: the dense dequant-MFMA kernel with the most time in the timed region
+    kt = streamed["kernels"]
+    name = max(kt, key=lambda k: kt[k]["total_ms"])
+    k = kt[name]
+    avg_ms = k["total_ms"] / k["launches"]
+    avg_flops = k["total_flops"] / k["launches"]
+    achieved = avg_flops / (avg_ms * 1e-3) / 1e12
+    kernels = {n: {"launches": v["launches"], "avg_ms": v["total_ms"] / v["launches"],
+                   "tflops": v["total_flops"] / (v["total_ms"] * 1e-3) / 1e12,
+                   "ms_per_step": v["total_ms"] / args.steps} for n, v in kt.items()}
+    h2d_bytes = streamed["window"]["bytes_copied"] if streamed["window"] else 0
+    h2d_rate = h2d_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (T / PAGES_A100_S_PER_STEP), 3) if args.layers == 64 else None,
+        "dtype": "bf16",
+        "data": "synthetic (random N(0,0.02) NF4 base, random adapters, random tokens)",
+        "config": {"workload": "Qwen2.5-32B-shaped streamed NF4+LoRA train step", "layers": args.layers,
+                   "hidden": 5120, "heads": 40, "kv_heads": 8, "intermediate": 27648, "vocab": 152064,
+                   "seq_len": T, "batch": 1, "window_blocks": 4, "lora_r": 16, "lora_alpha": 32,
+                   "dropout": 0.0, "optimizer": "AdamW", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(avg_ms, 4),
+                     "algorithmic_gflop_per_launch": round(avg_flops / 1e9, 3)},
+        "h2d": {"bytes_per_step": int(h2d_bytes), "achieved_GBps": round(h2d_rate, 1),
+                "ceiling_GBps": round(ceiling, 1), "frac": round(h2d_rate / ceiling, 3),
+                "windows_copied_per_step": streamed["window"]["windows_copied"] if streamed["window"] else 0,
+                "windows_reused_per_step": streamed["window"]["windows_reused"] if streamed["window"] else 0},
+        "kernels": kernels,
+        "peak_vram_gb": round(streamed["peak_alloc_gb"], 2),
+        "baseline_context": {"value": round(T / PAGES_A100_S_PER_STEP, 1), "unit": "tokens/s",
+                             "hardware": "NVIDIA A100 80GB PCIe", "s_per_step": PAGES_A100_S_PER_STEP},
+    }
+    if resident:
+        rms = resident["seconds"] / args.steps * 1e3
+        result["resident"] = {"ms_per_step": round(rms, 2), "tokens_per_s": round(T * args.steps / resident["seconds"], 2),
+                              "peak_vram_gb": round(resident["peak_alloc_gb"], 2),
+                              "streamed_over_resident": round(ms / rms, 3),
+                              "losses_equal": resident["losses"] == streamed["losses"]}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    result["host"] = {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -82,6 +82,8 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   o = align256(o + tr);
   p.off_act_fwd = o;  // bf16 copy of fp32 activations for the MFMA operand
   o = align256(o + (size_t)t * k * sizeof(uint16_t));
+  p.off_sk_fwd = o;   // chunk partials of the rank-r skinny products
+  o = align256(o + (size_t)((k + SKINNY_CHUNK - 1) / SKINNY_CHUNK) * t * r * sizeof(float));
   p.fwd_bytes = o;
   p.nch = (int)((t + COLGRAD_TCHUNK - 1) / COLGRAD_TCHUNK);
   o = 0;
@@ -97,6 +99,8 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   o = align256(o + (size_t)p.nch * r * n * sizeof(float));
   p.off_act_bwd = o;
   o = align256(o + (size_t)t * n * sizeof(uint16_t));
+  p.off_sk_bwd = o;
+  o = align256(o + (size_t)((std::max(k, n) + SKINNY_CHUNK - 1) / SKINNY_CHUNK) * t * r * sizeof(float));
   p.bwd_bytes = o;
   return p;
 }
@@ -194,10 +198,31 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
     e = launch_cvt_bf16((const float*)x, t * k, tmp, s);
     xb = tmp;
   }
-  if (e == hipSuccess && r > 0) e = launch_rowdot(x, act_f32, t, k, A, 0, r, 1.0f, d, u, s);
-  if (e == hipSuccess) e = launch_gemm(0, xb, codes, absmax, t, n, k, p.fwd, part, s);
-  if (e == hipSuccess)
-    e = launch_fwd_epilogue(part, p.fwd.splits, t, n, bias, u, B, r, lscale, y, out_f32, s);
+  if (e == hipSuccess && r > 0)
+    e = launch_skinny(x, act_f32, t, k, A, 0, r, 1.0f, d, (float*)(ws + p.off_sk_fwd), u, s);
+  if (e == hipSuccess) {
+    GemmLaunch L;
+    L.mode = 0;
+    L.act = xb;
+    L.codes = codes;
+    L.absmax = absmax;
+    L.M = t;
+    L.N = n;
+    L.K = k;
+    L.plan = p.fwd;
+    L.lu = u;
+    L.lw = B;
+    L.r = r;
+    L.lscale = lscale;
+    L.drop = no_dropout();
+    L.bias = bias;
+    L.out = p.fwd.splits == 1 ? y : (void*)part;
+    L.out_f32 = out_f32;
+    L.accumulate = 0;
+    e = launch_gemm(L, s);
+  }
+  if (e == hipSuccess && p.fwd.splits > 1)
+    e = launch_split_reduce(part, p.fwd.splits, t, n, bias, y, out_f32, 0, s);
   return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
 }
 
@@ -230,6 +255,7 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
     const bool act_f32 = cfg.flags & MSQ_ACT_F32, out_f32 = cfg.flags & MSQ_OUT_F32;
     float* part = (float*)(ws + p.off_part_bwd);
     float* du = (float*)(ws + p.off_du);
+    float* sk = (float*)(ws + p.off_sk_bwd);
     const float* uu = u;
     const uint16_t* dyb = (const uint16_t*)dy;
     if (act_f32) {
@@ -239,13 +265,33 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
     }
     if (e == hipSuccess && r > 0 && !uu) {
       float* ut = (float*)(ws + p.off_u_bwd);
-      e = launch_rowdot(x, act_f32, t, k, A, 0, r, 1.0f, d, ut, s);
+      e = launch_skinny(x, act_f32, t, k, A, 0, r, 1.0f, d, sk, ut, s);
       uu = ut;
     }
-    if (e == hipSuccess && r > 0) e = launch_rowdot(dy, act_f32, t, n, B, 1, r, lscale, no_dropout(), du, s);
-    if (e == hipSuccess) e = launch_gemm(1, dyb, codes, absmax, t, n, k, p.bwd, part, s);
-    if (e == hipSuccess)
-      e = launch_bwd_epilogue(part, p.bwd.splits, t, k, du, A, r, d, dx, out_f32, dx_accumulate, s);
+    if (e == hipSuccess && r > 0) e = launch_skinny(dy, act_f32, t, n, B, 1, r, lscale, no_dropout(), sk, du, s);
+    if (e == hipSuccess) {
+      GemmLaunch L;
+      L.mode = 1;
+      L.act = dyb;
+      L.codes = codes;
+      L.absmax = absmax;
+      L.M = t;
+      L.N = n;
+      L.K = k;
+      L.plan = p.bwd;
+      L.lu = du;
+      L.lw = A;
+      L.r = r;
+      L.lscale = 1.0f;
+      L.drop = d;
+      L.bias = nullptr;
+      L.out = p.bwd.splits == 1 ? dx : (void*)part;
+      L.out_f32 = out_f32;
+      L.accumulate = dx_accumulate;
+      e = launch_gemm(L, s);
+    }
+    if (e == hipSuccess && p.bwd.splits > 1)
+      e = launch_split_reduce(part, p.bwd.splits, t, k, nullptr, dx, out_f32, dx_accumulate, s);
     if (e == hipSuccess && r > 0)
       e = launch_colgrad(x, act_f32, t, k, du, r, d, p.nch, (float*)(ws + p.off_pa), s);
     if (e == hipSuccess && r > 0)

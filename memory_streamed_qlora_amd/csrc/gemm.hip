@@ -12,8 +12,13 @@
 //
 // Tile: BM=128 rows of t x BN=128 output columns x BK=64 reduction, 256 threads =
 // 4 waves in a 2x2 grid, each wave owns a 64x64 sub-tile = 2x2 MFMA 32x32 blocks.
-// The reduction can be split over gridDim.z; partial tiles go to a workspace and a
-// separate epilogue sums them in split order, so results never depend on timing.
+// The rank-r LoRA term of the same output tile is one more MFMA k-step per 16 ranks
+// (operands split into bf16 hi/lo pairs for ~fp32 accuracy); in the backward it goes
+// to a second accumulator so the dropout keep-mask can be applied per element.
+// Unsplit launches write the final output (bias or the old dx added, rounded once);
+// the reduction can instead be split over gridDim.z, in which case split 0 carries
+// the LoRA term and fp32 partial tiles go to a workspace summed in split order by a
+// separate kernel, so results never depend on timing.
 #include "internal.hpp"
 
 namespace msq {
@@ -25,17 +30,36 @@ constexpr int LDW = BK + PAD;       // LDS row pitch in bf16 elements (144 bytes
 constexpr int THREADS = 256;
 
 struct GemmArgs {
-  const uint16_t* act;   // [M][R]
+  const uint16_t* act;   // [M][R] bf16
   const uint8_t* codes;  // [N][K/2]
   const float* absmax;   // [N][K/64]
-  float* part;           // [S][M][Nc]
   int64_t M, N, K;       // W is [N][K]
   int64_t R, Nc;         // reduction length and output columns
-  int steps, steps_per_split;
+  int steps, steps_per_split, splits;
   Nf4Lut lut;
+  // LoRA term, added once (by split 0):
+  //   forward  lscale * lu[m][:] . lw[n][:]          lu = u [M][r], lw = B [N][r]
+  //   backward keep(m,k) * sigma * lu[m][:] . lw[:][k]  lu = du [M][r], lw = A [r][K]
+  const float* lu;
+  const float* lw;
+  int r;
+  float lscale;
+  Dropout drop;
+  // output: splits == 1 -> y / dx directly (bf16 or fp32, + bias / + old dx);
+  //         splits  > 1 -> fp32 partials [splits][M][Nc]
+  const uint16_t* bias;
+  void* out;
+  int out_f32, accumulate;
 };
 
-template <int MODE>
+// fp32 -> (hi, lo) bf16 pair with hi + lo = v to ~2^-16 relative; products of the
+// pairs are exact in fp32, so hi*hi + hi*lo + lo*hi carries ~fp32 accuracy on MFMA.
+__device__ __forceinline__ void split_bf16(float v, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_rne(v);
+  lo = bf16_rne(v - bf16_to_f32(hi));
+}
+
+template <int MODE, bool DROP>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDW];
   __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDW];
@@ -128,23 +152,123 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
     __syncthreads();
   }
-  // ---- partial tile -> workspace ------------------------------------------------------
-  float* P = g.part + (int64_t)split * g.M * g.Nc;
+
+  // ---- LoRA term: one extra MFMA k-step per 16 ranks, operands split hi/lo ---------------
+  f32x16_t acc2[2][2];
+  if (DROP) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc2[i][j][v] = 0.0f;
+  }
+  if (split == 0 && g.r > 0) {
+    for (int rc = 0; rc < g.r; rc += 16) {
+      {
+        const int row = tid >> 1, jh = (tid & 1) * 8;
+        const int64_t gm = m0 + row;
+        const int64_t gc = n0 + row;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = rc + jh + jj;
+          float a = 0.0f, b = 0.0f;
+          if (j < g.r) {
+            if (gm < g.M) a = g.lscale * g.lu[gm * g.r + j];
+            if (gc < g.Nc) b = (MODE == 0) ? g.lw[gc * g.r + j] : g.lw[(int64_t)j * g.K + gc];
+          }
+          uint32_t hi, lo;
+          split_bf16(a, hi, lo);
+          sA[row * LDW + jh + jj] = (uint16_t)hi;
+          sA[row * LDW + 16 + jh + jj] = (uint16_t)lo;
+          split_bf16(b, hi, lo);
+          sB[row * LDW + jh + jj] = (uint16_t)hi;
+          sB[row * LDW + 16 + jh + jj] = (uint16_t)lo;
+        }
+      }
+      __syncthreads();
+      const int kof = 8 * (lane >> 5);
+      bf16x8_t ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rw = (wm * 64 + i * 32 + (lane & 31)) * LDW;
+        ah[i] = *reinterpret_cast<const bf16x8_t*>(&sA[rw + kof]);
+        al[i] = *reinterpret_cast<const bf16x8_t*>(&sA[rw + 16 + kof]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rw = (wn * 64 + j * 32 + (lane & 31)) * LDW;
+        bh[j] = *reinterpret_cast<const bf16x8_t*>(&sB[rw + kof]);
+        bl[j] = *reinterpret_cast<const bf16x8_t*>(&sB[rw + 16 + kof]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          f32x16_t t = DROP ? acc2[i][j] : acc[i][j];
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], t, 0, 0, 0);
+          if (DROP)
+            acc2[i][j] = t;
+          else
+            acc[i][j] = t;
+        }
+      __syncthreads();
+    }
+    if (DROP) {  // masked LoRA input gradient: acc += keep * sigma * acc2
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (m < g.M && n < g.Nc) {
+              const uint64_t e = (uint64_t)m * (uint64_t)g.Nc + (uint64_t)n;
+              const uint32_t keep = (keep4(g.drop, e & ~(uint64_t)3) >> (e & 3)) & 1u;
+              if (keep) acc[i][j][v] += g.drop.sigma * acc2[i][j][v];
+            }
+          }
+        }
+    }
+  }
+
+  // ---- output ---------------------------------------------------------------------------
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (n >= g.Nc) continue;
+      const float bn = (MODE == 0 && g.splits == 1 && g.bias) ? bf16_to_f32(g.bias[n]) : 0.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m < g.M && n < g.Nc) P[m * g.Nc + n] = acc[i][j][v];
+        if (m >= g.M) continue;
+        float val = acc[i][j][v];
+        if (g.splits > 1) {
+          reinterpret_cast<float*>(g.out)[((int64_t)split * g.M + m) * g.Nc + n] = val;
+          continue;
+        }
+        const int64_t o = m * g.Nc + n;
+        if (MODE == 0) val += bn;
+        if (g.out_f32) {
+          float* po = reinterpret_cast<float*>(g.out);
+          po[o] = (MODE == 1 && g.accumulate) ? po[o] + val : val;
+        } else {
+          uint16_t* po = reinterpret_cast<uint16_t*>(g.out);
+          if (MODE == 1 && g.accumulate) val = bf16_to_f32(po[o]) + val;
+          po[o] = (uint16_t)bf16_rne(val);
+        }
       }
     }
 }
 
-__global__ __launch_bounds__(THREADS) void nf4_fwd_gemm(GemmArgs g) { gemm_body<0>(g); }
-__global__ __launch_bounds__(THREADS) void nf4_bwd_gemm(GemmArgs g) { gemm_body<1>(g); }
+__global__ __launch_bounds__(THREADS) void nf4_fwd_gemm(GemmArgs g) { gemm_body<0, false>(g); }
+__global__ __launch_bounds__(THREADS) void nf4_bwd_gemm(GemmArgs g) { gemm_body<1, false>(g); }
+__global__ __launch_bounds__(THREADS) void nf4_bwd_gemm_dropout(GemmArgs g) { gemm_body<1, true>(g); }
 
 }  // namespace
 
@@ -159,28 +283,38 @@ GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red) {
   return p;
 }
 
-hipError_t launch_gemm(int mode, const uint16_t* act, const uint8_t* codes, const float* absmax,
-                       int64_t M, int64_t N, int64_t K, const GemmPlan& plan, float* part,
-                       hipStream_t s) {
+hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   GemmArgs g;
-  g.act = act;
-  g.codes = codes;
-  g.absmax = absmax;
-  g.part = part;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  g.R = mode == 0 ? K : N;
-  g.Nc = mode == 0 ? N : K;
-  g.steps = plan.steps;
-  g.steps_per_split = plan.steps_per_split;
+  g.act = L.act;
+  g.codes = L.codes;
+  g.absmax = L.absmax;
+  g.M = L.M;
+  g.N = L.N;
+  g.K = L.K;
+  g.R = L.mode == 0 ? L.K : L.N;
+  g.Nc = L.mode == 0 ? L.N : L.K;
+  g.steps = L.plan.steps;
+  g.steps_per_split = L.plan.steps_per_split;
+  g.splits = L.plan.splits;
   g.lut = nf4_lut();
-  const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)plan.splits);
-  const double flops = 2.0 * (double)M * (double)N * (double)K;
+  g.lu = L.lu;
+  g.lw = L.lw;
+  g.r = L.r;
+  g.lscale = L.lscale;
+  g.drop = L.drop;
+  g.bias = L.bias;
+  g.out = L.out;
+  g.out_f32 = L.out_f32;
+  g.accumulate = L.accumulate;
+  const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)g.splits);
+  const double flops = 2.0 * (double)g.M * (double)g.N * (double)g.K;
   int rec;
-  if (mode == 0) {
+  if (L.mode == 0) {
     rec = timing_begin("nf4_fwd_gemm", flops, s);
     hipLaunchKernelGGL(nf4_fwd_gemm, grid, dim3(THREADS), 0, s, g);
+  } else if (L.r > 0 && L.drop.threshold != 0u) {
+    rec = timing_begin("nf4_bwd_gemm", flops, s);
+    hipLaunchKernelGGL(nf4_bwd_gemm_dropout, grid, dim3(THREADS), 0, s, g);
   } else {
     rec = timing_begin("nf4_bwd_gemm", flops, s);
     hipLaunchKernelGGL(nf4_bwd_gemm, grid, dim3(THREADS), 0, s, g);

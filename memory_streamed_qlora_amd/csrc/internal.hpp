@@ -32,8 +32,8 @@ GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red);
 
 struct LoraPlan {
   GemmPlan fwd, bwd;
-  size_t off_part_fwd, off_u_fwd, off_act_fwd;                   // fwd layout
-  size_t off_part_bwd, off_u_bwd, off_du, off_pa, off_pb, off_act_bwd;  // bwd layout
+  size_t off_part_fwd, off_u_fwd, off_act_fwd, off_sk_fwd;                   // fwd layout
+  size_t off_part_bwd, off_u_bwd, off_du, off_pa, off_pb, off_act_bwd, off_sk_bwd;  // bwd layout
   int nch;                                   // T-chunks of the dA/dB reductions
   size_t fwd_bytes, bwd_bytes;
 };
@@ -45,18 +45,38 @@ hipError_t launch_quantize(const uint16_t* w, int64_t nblocks, uint8_t* codes, f
 hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t nchunks32,
                              uint16_t* w, hipStream_t s);
 
-// out[S][M][Nc] fp32 partial sums.
-//   mode 0 (forward):  out[m][n] = sum_k act[m][k] * W[n][k]    act [M][K], Nc = N
-//   mode 1 (backward): out[m][k] = sum_n act[m][n] * W[n][k]    act [M][N], Nc = K
-hipError_t launch_gemm(int mode, const uint16_t* act, const uint8_t* codes, const float* absmax,
-                       int64_t M, int64_t N, int64_t K, const GemmPlan& plan, float* part,
-                       hipStream_t s);
+// Fused dequant-MFMA product with the LoRA term of the same tile.
+//   mode 0 (forward):  y[m][n]  = sum_k act[m][k] W[n][k] + lscale * lu[m] . lw[n] + bias[n]
+//   mode 1 (backward): dx[m][k] = [dx +] sum_n act[m][n] W[n][k] + keep*sigma * lu[m] . lw[:,k]
+// With plan.splits > 1, `out` receives fp32 partials [splits][M][Nc] instead (split 0
+// carrying the LoRA term) and launch_split_reduce finishes the output.
+struct GemmLaunch {
+  int mode;
+  const uint16_t* act;
+  const uint8_t* codes;
+  const float* absmax;
+  int64_t M, N, K;
+  GemmPlan plan;
+  const float* lu;
+  const float* lw;
+  int r;
+  float lscale;
+  Dropout drop;
+  const uint16_t* bias;
+  void* out;
+  int out_f32, accumulate;
+};
+hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s);
 
 // Activations `in` are bf16 (uint16_t) or fp32 (in_f32).
 // out[t][j] = scale * sum_c h[t][c] * mat(j, c), h = drop(in) (dropout optional)
 //   mat_kind 0: mat is [r][C] (LoRA A);   mat_kind 1: mat is [C][r] (LoRA B)
-hipError_t launch_rowdot(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat,
-                         int mat_kind, int r, float scale, const Dropout& d, float* out, hipStream_t s);
+// Tiled over 16 tokens x SKINNY_CHUNK columns; part holds the per-chunk partials
+// ([ceil(C / SKINNY_CHUNK)][T][r] floats), summed in chunk order.
+constexpr int SKINNY_CHUNK = 512;
+hipError_t launch_skinny(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat,
+                         int mat_kind, int r, float scale, const Dropout& d, float* part, float* out,
+                         hipStream_t s);
 
 // part[ch][j][c] = sum_{t in chunk ch} coef[t][j] * h[t][c], h = drop(in)
 hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
@@ -65,14 +85,11 @@ hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, con
 hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale,
                                  float* out, int64_t sj, int64_t sc, int accumulate, hipStream_t s);
 
-// y[t][n] = out(sum_s part[s][t][n] + bias[n] + lscale * sum_j u[t][j] B[n][j]); y bf16 or fp32
-hipError_t launch_fwd_epilogue(const float* part, int splits, int64_t T, int64_t N,
-                               const uint16_t* bias, const float* u, const float* B, int r,
-                               float lscale, void* y, bool out_f32, hipStream_t s);
-// dx[t][k] = out([dx_old +] sum_s part[s][t][k] + sigma*keep(t,k)*sum_j du[t][j] A[j][k])
-hipError_t launch_bwd_epilogue(const float* part, int splits, int64_t T, int64_t K,
-                               const float* du, const float* A, int r, const Dropout& d,
-                               void* dx, bool out_f32, int accumulate, hipStream_t s);
+// Sum of split partials [splits][T][N] in split order, then + bias[n] (bias may be NULL)
+// or + the old output (accumulate), one rounding into bf16 or a fp32 store.
+hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
+                               const uint16_t* bias, void* out, bool out_f32, int accumulate,
+                               hipStream_t s);
 // out[i] = bf16_rne(in[i]) for n elements (n % 8 == 0)
 hipError_t launch_cvt_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s);
 

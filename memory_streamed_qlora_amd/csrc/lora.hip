@@ -2,12 +2,14 @@
 //
 // The rank-r products of the adapter are skinny (r = 16 against K, N in the
 // thousands) and bound by HBM/L2 traffic, not by MFMA:
-//   rowdot          u = drop(x) A^T  (forward, recompute)  and  du = s dy B  (backward)
+//   skinny(+reduce)  u = drop(x) A^T  (forward, recompute)  and  du = s dy B  (backward),
+//                   tiled over 16 tokens x 512 columns, chunk partials summed in order
 //   colgrad(+reduce) dA = du^T drop(x)  and  dB = s dy^T u, reduced over tokens in
 //                   fixed-size chunks and then summed in chunk order
-//   epilogues       sum the split-reduction partials of the base GEMM in split order
-//                   and add bias and the LoRA term (forward) or the masked LoRA input
-//                   gradient (backward), then round once to bf16 (or store fp32).
+//   split_reduce    sums split-reduction partials of the base GEMM in split order and
+//                   adds the bias (forward) or the old dx (accumulating backward), then
+//                   rounds once to bf16 (or stores fp32); the LoRA term itself is folded
+//                   into the GEMM's output tiles.
 // Activations may be bf16 or fp32; with fp32 the rank-r products use the fp32
 // values and only the MFMA operand of the base product is rounded to bf16.
 // Every reduction has a fixed shape-determined order and no atomics, so results are
@@ -19,7 +21,6 @@
 namespace msq {
 namespace {
 
-constexpr int RD_THREADS = 256;
 
 // Activation element types: bf16 bit patterns (uint16_t) or fp32.
 // Eight consecutive elements at p (16-byte aligned for bf16, 32 for fp32) -> floats.
@@ -58,75 +59,81 @@ __device__ __forceinline__ void store4(float* p, const float a[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(a[0], a[1], a[2], a[3]);
 }
 
-// out[t][j] = scale * sum_c h[t][c] * mat(j, c); one workgroup per row t.
-template <int RT, int MAT_KIND, typename TIN>
-__global__ __launch_bounds__(RD_THREADS) void lora_rowdot(const TIN* __restrict__ in, int64_t C,
-                                                          const float* __restrict__ mat, int r,
-                                                          float scale, Dropout d,
-                                                          float* __restrict__ out) {
-  const int64_t t = blockIdx.x;
+// Skinny product out[t][j] = scale * sum_c h[t][c] * M(c, j) for r <= 64 ranks.
+// Workgroup: 16 tokens x SKINNY_CHUNK columns x 16 ranks (grid z over rank groups);
+// the input tile (dropout applied while staging) and the matrix chunk are staged in
+// LDS, each thread owns one (token, rank) pair and reduces over the chunk; the chunk
+// partials go to part[chunk][t][j] and skinny_reduce sums them in chunk order.
+constexpr int SK_T = 16, SK_J = 16, SK_LD = SKINNY_CHUNK + 4;
+
+template <typename TIN, int MAT_KIND>
+__global__ __launch_bounds__(256) void lora_skinny(const TIN* __restrict__ in, int64_t T, int64_t C,
+                                                   const float* __restrict__ mat, int r, Dropout d,
+                                                   float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float xs[SK_T * SK_LD];
+  __shared__ __attribute__((aligned(16))) float ms[SK_J * SK_LD];
   const int tid = threadIdx.x;
-  float acc[RT];
+  const int64_t t0 = (int64_t)blockIdx.x * SK_T;
+  const int64_t c0 = (int64_t)blockIdx.y * SKINNY_CHUNK;
+  const int j0 = blockIdx.z * SK_J;
+  // input tile [16][CHUNK], 4 consecutive columns per load
+  for (int idx = tid; idx < SK_T * SKINNY_CHUNK / 4; idx += 256) {
+    const int row = idx / (SKINNY_CHUNK / 4), c4 = idx % (SKINNY_CHUNK / 4);
+    const int64_t t = t0 + row, c = c0 + 4 * c4;
+    float h[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < T && c < C) {
+      load4(in + t * C + c, h);
+      if (d.threshold != 0u) {
+        const uint32_t keep = keep4(d, (uint64_t)t * (uint64_t)C + (uint64_t)c);
 #pragma unroll
-  for (int j = 0; j < RT; ++j) acc[j] = 0.0f;
-  const TIN* row = in + t * C;
-  for (int64_t c = 8 * (int64_t)tid; c < C; c += 8 * RD_THREADS) {
-    float h[8];
-    load8(row + c, h);
-    if (d.threshold != 0u) {
-      const uint64_t e0 = (uint64_t)t * (uint64_t)C + (uint64_t)c;
-      const uint32_t keep = keep4(d, e0) | (keep4(d, e0 + 4) << 4);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) h[q] = ((keep >> q) & 1u) ? h[q] * d.sigma : 0.0f;
-    }
-    if (MAT_KIND == 0) {  // mat [r][C]
-#pragma unroll
-      for (int j = 0; j < RT; ++j) {
-        if (j < r) {
-          const float4 m0 = *reinterpret_cast<const float4*>(mat + (int64_t)j * C + c);
-          const float4 m1 = *reinterpret_cast<const float4*>(mat + (int64_t)j * C + c + 4);
-          float s = acc[j];
-          s = fmaf(h[0], m0.x, s);
-          s = fmaf(h[1], m0.y, s);
-          s = fmaf(h[2], m0.z, s);
-          s = fmaf(h[3], m0.w, s);
-          s = fmaf(h[4], m1.x, s);
-          s = fmaf(h[5], m1.y, s);
-          s = fmaf(h[6], m1.z, s);
-          s = fmaf(h[7], m1.w, s);
-          acc[j] = s;
-        }
-      }
-    } else {  // mat [C][r]
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float* mr = mat + (c + q) * (int64_t)r;
-#pragma unroll
-        for (int j = 0; j < RT; ++j)
-          if (j < r) acc[j] = fmaf(h[q], mr[j], acc[j]);
+        for (int q = 0; q < 4; ++q) h[q] = ((keep >> q) & 1u) ? h[q] * d.sigma : 0.0f;
       }
     }
+    *reinterpret_cast<float4*>(&xs[row * SK_LD + 4 * c4]) = make_float4(h[0], h[1], h[2], h[3]);
   }
-  // wave reduction (butterfly, fixed order), then across the 4 waves in order
-  __shared__ float red[RD_THREADS / 64][RT];
-#pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    float v = acc[j];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    acc[j] = v;
-  }
-  if ((tid & 63) == 0) {
-#pragma unroll
-    for (int j = 0; j < RT; ++j) red[tid >> 6][j] = acc[j];
+  // matrix chunk, stored [rank][column]
+  if (MAT_KIND == 0) {  // mat [r][C]
+    for (int idx = tid; idx < SK_J * SKINNY_CHUNK / 4; idx += 256) {
+      const int j = idx / (SKINNY_CHUNK / 4), c4 = idx % (SKINNY_CHUNK / 4);
+      const int64_t c = c0 + 4 * c4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + j < r && c < C) v = *reinterpret_cast<const float4*>(mat + (int64_t)(j0 + j) * C + c);
+      *reinterpret_cast<float4*>(&ms[j * SK_LD + 4 * c4]) = v;
+    }
+  } else {  // mat [C][r]
+    for (int idx = tid; idx < SK_J * SKINNY_CHUNK; idx += 256) {
+      const int c = idx / SK_J, j = idx % SK_J;
+      float v = 0.0f;
+      if (j0 + j < r && c0 + c < C) v = mat[(c0 + c) * (int64_t)r + j0 + j];
+      ms[j * SK_LD + c] = v;
+    }
   }
   __syncthreads();
-  if (tid < r) {
-    float v = red[0][tid];
-#pragma unroll
-    for (int w = 1; w < RD_THREADS / 64; ++w) v += red[w][tid];
-    out[t * r + tid] = scale * v;
+  const int row = tid / SK_J, j = tid % SK_J;
+  const float* xr = &xs[row * SK_LD];
+  const float* mr = &ms[j * SK_LD];
+  float acc = 0.0f;
+#pragma unroll 8
+  for (int c = 0; c < SKINNY_CHUNK; c += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(xr + c);
+    const float4 b = *reinterpret_cast<const float4*>(mr + c);
+    acc = fmaf(a.x, b.x, acc);
+    acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc);
+    acc = fmaf(a.w, b.w, acc);
   }
+  const int64_t t = t0 + row;
+  if (t < T && j0 + j < r) part[((int64_t)blockIdx.y * T + t) * r + j0 + j] = acc;
+}
+
+__global__ __launch_bounds__(256) void lora_skinny_reduce(const float* __restrict__ part, int nck,
+                                                          int64_t n, float scale,
+                                                          float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int c = 0; c < nck; ++c) s += part[(int64_t)c * n + i];
+  out[i] = scale * s;
 }
 
 // part[ch][j][c] = sum_{t in chunk} coef[t][j] * h[t][c], for j in [j0, j0+16)
@@ -196,87 +203,38 @@ __global__ __launch_bounds__(256) void lora_colgrad_reduce(const float* __restri
   *o = accumulate ? (*o + s) : s;
 }
 
-// y[t][n..n+3] = out(sum_s P + bias + lscale * u[t] . B[n])
+// out[t][n..n+3] = sum_s P[s][t][n..n+3] (+ bias[n..n+3]) (+ old out), one rounding.
 template <typename TOUT>
-__global__ __launch_bounds__(256) void lora_fwd_epilogue(const float* __restrict__ part, int splits,
-                                                         int64_t T, int64_t N,
-                                                         const uint16_t* __restrict__ bias,
-                                                         const float* __restrict__ u,
-                                                         const float* __restrict__ B, int r,
-                                                         float lscale, TOUT* __restrict__ y) {
-  const int64_t t = blockIdx.y;
-  const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (n >= N) return;
+__global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ part, int splits,
+                                                    int64_t T, int64_t N,
+                                                    const uint16_t* __restrict__ bias,
+                                                    TOUT* __restrict__ out, int accumulate) {
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i4 * 4 >= T * N) return;
+  const int64_t o = i4 * 4;
+  const int64_t n = o % N;
+  const int64_t plane = T * N;
   float a[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < splits; ++s) {
-    const float4 p = *reinterpret_cast<const float4*>(part + ((int64_t)s * T + t) * N + n);
+    const float4 p = *reinterpret_cast<const float4*>(part + s * plane + o);
     a[0] += p.x;
     a[1] += p.y;
     a[2] += p.z;
     a[3] += p.w;
   }
   if (bias) {
-    const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
-    a[0] += bf16_to_f32(b.x & 0xffffu);
-    a[1] += bf16_to_f32(b.x >> 16);
-    a[2] += bf16_to_f32(b.y & 0xffffu);
-    a[3] += bf16_to_f32(b.y >> 16);
-  }
-  if (r > 0) {
-    const float* ur = u + t * r;
+    float b[4];
+    load4(bias + n, b);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float* br = B + (n + q) * (int64_t)r;
-      float l = 0.0f;
-      for (int j = 0; j < r; ++j) l = fmaf(ur[j], br[j], l);
-      a[q] += lscale * l;
-    }
+    for (int q = 0; q < 4; ++q) a[q] += b[q];
   }
-  store4(y + t * N + n, a);
-}
-
-// dx[t][k..k+3] = out([dx_old +] (sum_s P + sigma*keep*(du[t] . A[:,k])))
-template <typename TOUT>
-__global__ __launch_bounds__(256) void lora_bwd_epilogue(const float* __restrict__ part, int splits,
-                                                         int64_t T, int64_t K,
-                                                         const float* __restrict__ du,
-                                                         const float* __restrict__ A, int r,
-                                                         Dropout d, TOUT* __restrict__ dx,
-                                                         int accumulate) {
-  const int64_t t = blockIdx.y;
-  const int64_t k = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (k >= K) return;
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const float4 p = *reinterpret_cast<const float4*>(part + ((int64_t)s * T + t) * K + k);
-    a[0] += p.x;
-    a[1] += p.y;
-    a[2] += p.z;
-    a[3] += p.w;
-  }
-  if (r > 0) {
-    float l[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* dur = du + t * r;
-    for (int j = 0; j < r; ++j) {
-      const float4 av = *reinterpret_cast<const float4*>(A + (int64_t)j * K + k);
-      const float dj = dur[j];
-      l[0] = fmaf(dj, av.x, l[0]);
-      l[1] = fmaf(dj, av.y, l[1]);
-      l[2] = fmaf(dj, av.z, l[2]);
-      l[3] = fmaf(dj, av.w, l[3]);
-    }
-    const uint32_t keep = keep4(d, (uint64_t)t * (uint64_t)K + (uint64_t)k);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] += ((keep >> q) & 1u) ? d.sigma * l[q] : 0.0f;
-  }
-  TOUT* o = dx + t * K + k;
   if (accumulate) {
     float old[4];
-    load4(o, old);
+    load4(out + o, old);
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = old[q] + a[q];
   }
-  store4(o, a);
+  store4(out + o, a);
 }
 
 // Round fp32 activations to bf16 (RNE) for the MFMA operand; 8 per thread.
@@ -291,29 +249,34 @@ __global__ __launch_bounds__(256) void cvt_f32_bf16(const float* __restrict__ in
                  bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
 }
 
-template <int MAT_KIND, typename TIN>
-hipError_t rowdot_dispatch(const TIN* in, int64_t T, int64_t C, const float* mat, int r, float scale,
-                           const Dropout& d, float* out, hipStream_t s) {
-  const dim3 grid((unsigned)T), block(RD_THREADS);
-  if (r <= 16)
-    hipLaunchKernelGGL((lora_rowdot<16, MAT_KIND, TIN>), grid, block, 0, s, in, C, mat, r, scale, d, out);
-  else if (r <= 32)
-    hipLaunchKernelGGL((lora_rowdot<32, MAT_KIND, TIN>), grid, block, 0, s, in, C, mat, r, scale, d, out);
-  else
-    hipLaunchKernelGGL((lora_rowdot<64, MAT_KIND, TIN>), grid, block, 0, s, in, C, mat, r, scale, d, out);
+template <typename TIN, int MAT_KIND>
+hipError_t skinny_dispatch(const TIN* in, int64_t T, int64_t C, const float* mat, int r,
+                           const Dropout& d, float* part, hipStream_t s) {
+  const dim3 grid((unsigned)((T + SK_T - 1) / SK_T), (unsigned)((C + SKINNY_CHUNK - 1) / SKINNY_CHUNK),
+                  (unsigned)((r + SK_J - 1) / SK_J));
+  hipLaunchKernelGGL((lora_skinny<TIN, MAT_KIND>), grid, dim3(256), 0, s, in, T, C, mat, r, d, part);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_rowdot(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat,
-                         int mat_kind, int r, float scale, const Dropout& d, float* out, hipStream_t s) {
+hipError_t launch_skinny(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat,
+                         int mat_kind, int r, float scale, const Dropout& d, float* part, float* out,
+                         hipStream_t s) {
   if (T == 0 || r == 0) return hipSuccess;
+  hipError_t e;
   if (in_f32)
-    return mat_kind == 0 ? rowdot_dispatch<0>((const float*)in, T, C, mat, r, scale, d, out, s)
-                         : rowdot_dispatch<1>((const float*)in, T, C, mat, r, scale, d, out, s);
-  return mat_kind == 0 ? rowdot_dispatch<0>((const uint16_t*)in, T, C, mat, r, scale, d, out, s)
-                       : rowdot_dispatch<1>((const uint16_t*)in, T, C, mat, r, scale, d, out, s);
+    e = mat_kind == 0 ? skinny_dispatch<float, 0>((const float*)in, T, C, mat, r, d, part, s)
+                      : skinny_dispatch<float, 1>((const float*)in, T, C, mat, r, d, part, s);
+  else
+    e = mat_kind == 0 ? skinny_dispatch<uint16_t, 0>((const uint16_t*)in, T, C, mat, r, d, part, s)
+                      : skinny_dispatch<uint16_t, 1>((const uint16_t*)in, T, C, mat, r, d, part, s);
+  if (e != hipSuccess) return e;
+  const int nck = (int)((C + SKINNY_CHUNK - 1) / SKINNY_CHUNK);
+  const int64_t n = T * r;
+  hipLaunchKernelGGL(lora_skinny_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, nck,
+                     n, scale, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
@@ -339,31 +302,18 @@ hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, f
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_epilogue(const float* part, int splits, int64_t T, int64_t N,
-                               const uint16_t* bias, const float* u, const float* B, int r,
-                               float lscale, void* y, bool out_f32, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const dim3 grid((unsigned)((N / 4 + 255) / 256), (unsigned)T);
+hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
+                               const uint16_t* bias, void* out, bool out_f32, int accumulate,
+                               hipStream_t s) {
+  const int64_t n4 = T * N / 4;
+  if (n4 == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n4 + 255) / 256));
   if (out_f32)
-    hipLaunchKernelGGL(lora_fwd_epilogue<float>, grid, dim3(256), 0, s, part, splits, T, N, bias, u, B,
-                       r, lscale, (float*)y);
+    hipLaunchKernelGGL(split_reduce<float>, grid, dim3(256), 0, s, part, splits, T, N, bias, (float*)out,
+                       accumulate);
   else
-    hipLaunchKernelGGL(lora_fwd_epilogue<uint16_t>, grid, dim3(256), 0, s, part, splits, T, N, bias, u,
-                       B, r, lscale, (uint16_t*)y);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_epilogue(const float* part, int splits, int64_t T, int64_t K,
-                               const float* du, const float* A, int r, const Dropout& d,
-                               void* dx, bool out_f32, int accumulate, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const dim3 grid((unsigned)((K / 4 + 255) / 256), (unsigned)T);
-  if (out_f32)
-    hipLaunchKernelGGL(lora_bwd_epilogue<float>, grid, dim3(256), 0, s, part, splits, T, K, du, A, r,
-                       d, (float*)dx, accumulate);
-  else
-    hipLaunchKernelGGL(lora_bwd_epilogue<uint16_t>, grid, dim3(256), 0, s, part, splits, T, K, du, A,
-                       r, d, (uint16_t*)dx, accumulate);
+    hipLaunchKernelGGL(split_reduce<uint16_t>, grid, dim3(256), 0, s, part, splits, T, N, bias,
+                       (uint16_t*)out, accumulate);
   return hipGetLastError();
 }
 
