@@ -72,17 +72,23 @@ struct Nf4Planes {
   uint32_t lo[4], hi[4];
 };
 
+// Two floats -> packed bf16 pair (RNE), element a in the low half.  On gfx950 the
+// compiler emits one v_cvt_pk_bf16_f32 for the pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
 __device__ __forceinline__ Nf4Planes nf4_planes(const Nf4Lut& lut, float a) {
-  uint32_t b[16];
+  uint32_t pk[8];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) b[c] = bf16_rne(lut.v[c] * a);
+  for (int i = 0; i < 8; ++i) pk[i] = pack_bf16x2(lut.v[2 * i] * a, lut.v[2 * i + 1] * a);
   Nf4Planes P;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    P.lo[i] = (b[4 * i] & 0xffu) | ((b[4 * i + 1] & 0xffu) << 8) | ((b[4 * i + 2] & 0xffu) << 16) |
-              ((b[4 * i + 3] & 0xffu) << 24);
-    P.hi[i] = (b[4 * i] >> 8) | ((b[4 * i + 1] >> 8) << 8) | ((b[4 * i + 2] >> 8) << 16) |
-              ((b[4 * i + 3] >> 8) << 24);
+    // pk[2i] holds codes 4i, 4i+1; pk[2i+1] holds 4i+2, 4i+3 (bytes lo, hi, lo, hi)
+    P.lo[i] = __builtin_amdgcn_perm(pk[2 * i + 1], pk[2 * i], 0x06040200u);
+    P.hi[i] = __builtin_amdgcn_perm(pk[2 * i + 1], pk[2 * i], 0x07050301u);
   }
   return P;
 }

@@ -59,18 +59,34 @@ __device__ __forceinline__ void split_bf16(float v, uint32_t& hi, uint32_t& lo) 
   lo = bf16_rne(v - bf16_to_f32(hi));
 }
 
+// Launch order -> output tile.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup g runs on XCD g % 8), each with its own L2.  Tiles are listed m-fastest
+// (the M-tiles of one weight tile are neighbours) and handed to the XCDs in 8
+// contiguous ranges, so the workgroups that read the same NF4 tile share an L2.
+__device__ __forceinline__ void tile_of(int64_t& n0, int64_t& m0, int& split) {
+  const int64_t Mt = gridDim.y, Nt = gridDim.x;
+  const int64_t Q = Mt * Nt * gridDim.z;
+  const int64_t g = (int64_t)blockIdx.x + (int64_t)gridDim.x * ((int64_t)blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t x = g % 8, j = g / 8, q = Q / 8, rem = Q % 8;
+  const int64_t t = x * q + (x < rem ? x : rem) + j;
+  const int64_t m = t % Mt, rest = t / Mt;
+  n0 = (rest % Nt) * BN;
+  split = (int)(rest / Nt);
+  m0 = m * BM;
+}
+
 template <int MODE, bool DROP>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDW];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDW];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDW];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int split = blockIdx.z;
+  int64_t n0, m0;
+  int split;
+  tile_of(n0, m0, split);
   const int s_begin = split * g.steps_per_split;
   const int s_end = min(g.steps, s_begin + g.steps_per_split);
 
@@ -84,74 +100,88 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
   const int64_t kw_half = g.K / 2, kw_blk = g.K / 64;
 
-  for (int step = s_begin; step < s_end; ++step) {
+  // Per-thread share of one k-step's global data, prefetched one step ahead.
+  uint4 ra[4];   // activations: 4 x 8 bf16
+  uint4 rq;      // 32 NF4 codes of one (row, 64-block)
+  float rs;      // that block's absmax
+  // fixed per-thread coordinates
+  const int w_row = MODE == 0 ? (tid >> 1) : (tid >> 2);      // fwd: W row in tile; bwd: reduction row
+  const int w_sub = MODE == 0 ? (tid & 1) : (tid & 3);        // fwd: 32-code half; bwd: 32-col quarter
+  const int64_t w_col = MODE == 0 ? (n0 + w_row) : (n0 + 32 * w_sub);  // fwd: W row; bwd: W column
+  const bool w_ok = w_col < g.Nc;
+
+  auto gload = [&](int step) {
     const int64_t r0 = (int64_t)step * BK;
-    // ---- activations tile [BM][BK] -> sA ---------------------------------------
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int idx = tid + THREADS * c;
       const int row = idx >> 3, c8 = idx & 7;
       const int64_t gm = m0 + row;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (gm < g.M) v = *reinterpret_cast<const uint4*>(g.act + gm * g.R + r0 + c8 * 8);
-      *reinterpret_cast<uint4*>(&sA[row * LDW + c8 * 8]) = v;
+      ra[c] = gm < g.M ? *reinterpret_cast<const uint4*>(g.act + gm * g.R + r0 + c8 * 8)
+                       : make_uint4(0u, 0u, 0u, 0u);
     }
-    // ---- dequantized weight tile -> sB[out col][reduction] -------------------------
-    if (MODE == 0) {
-      // rows n0..n0+127 of W, columns r0..r0+63 (exactly one absmax block per row)
-      const int row = tid >> 1, half = tid & 1;
-      const int64_t gn = n0 + row;
-      uint32_t out[16];
-      if (gn < g.Nc) {
-        const uint4 q = *reinterpret_cast<const uint4*>(g.codes + gn * kw_half + r0 / 2 + half * 16);
-        const Nf4Planes P = nf4_planes(g.lut, g.absmax[gn * kw_blk + r0 / 64]);
-        nf4_dequant32(P, q, out);
+    if (w_ok) {
+      if (MODE == 0) {
+        rq = *reinterpret_cast<const uint4*>(g.codes + w_col * kw_half + r0 / 2 + w_sub * 16);
+        rs = g.absmax[w_col * kw_blk + r0 / 64];
       } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) out[i] = 0u;
+        rq = *reinterpret_cast<const uint4*>(g.codes + (r0 + w_row) * kw_half + w_col / 2);
+        rs = g.absmax[(r0 + w_row) * kw_blk + w_col / 64];
       }
-      uint4* dst = reinterpret_cast<uint4*>(&sB[row * LDW + half * 32]);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = tid + THREADS * c;
+      const int row = idx >> 3, c8 = idx & 7;
+      *reinterpret_cast<uint4*>(&sA[buf][row * LDW + c8 * 8]) = ra[c];
+    }
+    uint32_t out[16];
+    if (w_ok) {
+      const Nf4Planes P = nf4_planes(g.lut, rs);
+      nf4_dequant32(P, rq, out);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) out[i] = 0u;
+    }
+    if (MODE == 0) {
+      uint4* dst = reinterpret_cast<uint4*>(&sB[buf][w_row * LDW + w_sub * 32]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
     } else {
-      // rows r0..r0+63 of W (reduction), columns n0..n0+127 (output), stored transposed
-      const int row = tid >> 2, q4 = tid & 3;
-      const int64_t kc = n0 + 32 * q4;
-      uint32_t out[16];
-      if (kc < g.Nc) {
-        const uint4 q = *reinterpret_cast<const uint4*>(g.codes + (r0 + row) * kw_half + kc / 2);
-        const Nf4Planes P = nf4_planes(g.lut, g.absmax[(r0 + row) * kw_blk + kc / 64]);
-        nf4_dequant32(P, q, out);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) out[i] = 0u;
-      }
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const uint32_t v = (j & 1) ? (out[j >> 1] >> 16) : (out[j >> 1] & 0xffffu);
-        sB[(32 * q4 + j) * LDW + row] = (uint16_t)v;
+        sB[buf][(32 * w_sub + j) * LDW + w_row] = (uint16_t)v;
       }
     }
+  };
+
+  if (s_begin < s_end) gload(s_begin);
+  for (int step = s_begin; step < s_end; ++step) {
+    const int buf = (step - s_begin) & 1;
+    lstore(buf);
     __syncthreads();
-    // ---- MFMA over the tile --------------------------------------------------------
+    if (step + 1 < s_end) gload(step + 1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kof = ks * 16 + 8 * (lane >> 5);
       bf16x8_t af[2], bfr[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[(wm * 64 + i * 32 + (lane & 31)) * LDW + kof]);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * LDW + kof]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[(wn * 64 + j * 32 + (lane & 31)) * LDW + kof]);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LDW + kof]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // ---- LoRA term: one extra MFMA k-step per 16 ranks, operands split hi/lo ---------------
   f32x16_t acc2[2][2];
@@ -179,11 +209,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           }
           uint32_t hi, lo;
           split_bf16(a, hi, lo);
-          sA[row * LDW + jh + jj] = (uint16_t)hi;
-          sA[row * LDW + 16 + jh + jj] = (uint16_t)lo;
+          sA[0][row * LDW + jh + jj] = (uint16_t)hi;
+          sA[0][row * LDW + 16 + jh + jj] = (uint16_t)lo;
           split_bf16(b, hi, lo);
-          sB[row * LDW + jh + jj] = (uint16_t)hi;
-          sB[row * LDW + 16 + jh + jj] = (uint16_t)lo;
+          sB[0][row * LDW + jh + jj] = (uint16_t)hi;
+          sB[0][row * LDW + 16 + jh + jj] = (uint16_t)lo;
         }
       }
       __syncthreads();
@@ -192,14 +222,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int rw = (wm * 64 + i * 32 + (lane & 31)) * LDW;
-        ah[i] = *reinterpret_cast<const bf16x8_t*>(&sA[rw + kof]);
-        al[i] = *reinterpret_cast<const bf16x8_t*>(&sA[rw + 16 + kof]);
+        ah[i] = *reinterpret_cast<const bf16x8_t*>(&sA[0][rw + kof]);
+        al[i] = *reinterpret_cast<const bf16x8_t*>(&sA[0][rw + 16 + kof]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int rw = (wn * 64 + j * 32 + (lane & 31)) * LDW;
-        bh[j] = *reinterpret_cast<const bf16x8_t*>(&sB[rw + kof]);
-        bl[j] = *reinterpret_cast<const bf16x8_t*>(&sB[rw + 16 + kof]);
+        bh[j] = *reinterpret_cast<const bf16x8_t*>(&sB[0][rw + kof]);
+        bl[j] = *reinterpret_cast<const bf16x8_t*>(&sB[0][rw + 16 + kof]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
