@@ -1,8 +1,9 @@
 """Benchmark: streamed NF4 + LoRA training step of a Qwen2.5-32B-shaped stack on one GPU.
 
 Workload: 64 decoder layers (hidden 5120, 40/8 heads, SwiGLU 27648), random N(0, 0.02)
-base quantized to NF4 and held in pinned host memory, streamed through a two-slot
-device window of 4 blocks; LoRA r16 alpha32 dropout 0.0 on all seven projections;
+base quantized to NF4 and held in pinned host memory, streamed in windows of 4 blocks
+through a device arena of 3 window slots (one computing, two prefetching); LoRA r16
+alpha32 dropout 0.0 on all seven projections;
 batch 1 x 512 random tokens over a 152064-entry vocabulary; one AdamW step per
 training step.  A step is the whole hot path: forward with streaming, loss, backward
 with reload + recompute, AdamW.  tokens/s = 512 * steps / timed seconds.
@@ -119,6 +120,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=64, help="stack depth (64 = the 32B shape)")
+    ap.add_argument("--window-blocks", type=int, default=4,
+                    help="layers per window slot (blocks per streamed window)")
+    ap.add_argument("--slots", type=int, default=3, help="window slots in the device arena (prefetch depth + 1)")
     ap.add_argument("--no-resident", action="store_true", help="skip the resident comparison run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -139,8 +143,8 @@ def main() -> int:
 
     def run(mode: str):
         t_build = time.time()
-        st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=0.0, window_blocks=4,
-                            mode=mode)
+        st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=0.0,
+                            window_blocks=args.window_blocks, n_slots=args.slots, mode=mode)
         torch.cuda.synchronize()
         log(f"{mode}: built {args.layers} layers in {time.time() - t_build:.1f}s "
             f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
@@ -208,7 +212,10 @@ def main() -> int:
         "data": "synthetic (random N(0,0.02) NF4 base, random adapters, random tokens)",
         "config": {"workload": "Qwen2.5-32B-shaped streamed NF4+LoRA train step", "layers": args.layers,
                    "hidden": 5120, "heads": 40, "kv_heads": 8, "intermediate": 27648, "vocab": 152064,
-                   "seq_len": T, "batch": 1, "window_blocks": 4, "lora_r": 16, "lora_alpha": 32,
+                   "seq_len": T, "batch": 1,
+                   "window": {"layers_resident": args.window_blocks * args.slots,
+                              "slots": args.slots, "layers_per_slot": args.window_blocks},
+                   "lora_r": 16, "lora_alpha": 32,
                    "dropout": 0.0, "optimizer": "AdamW", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -47,8 +47,8 @@ enum {
   MSQ_E_SHAPE = -2,     /* k % 64 != 0, n % 64 != 0, r outside [0, 64], t*k too large */
   MSQ_E_DROPOUT = -3,   /* p_drop outside [0, 1), or alpha not finite */
   MSQ_E_WORKSPACE = -4, /* workspace smaller than nf4_lora_workspace_size() */
-  MSQ_E_WINDOW = -5,    /* arena cannot hold two windows; message names the largest
-                           window_blocks that fits */
+  MSQ_E_WINDOW = -5,    /* arena cannot hold n_slots windows; message names the
+                           largest window_blocks that fits */
   MSQ_E_ORDER = -6,     /* window protocol violated (acquire before prefetch,
                            prefetch with no free slot, release of a slot not held) */
   MSQ_E_HIP = -7        /* a HIP runtime call failed; msq_last_error() has its text */
@@ -113,14 +113,19 @@ typedef struct {
  *                library rounds the activation to bf16 (RNE) for that product only;
  *                the rank-r LoRA products use the fp32 values.
  *   MSQ_OUT_F32  y (forward) and dx (backward) are written (and, when
- *                accumulating, read) as fp32 instead of bf16. */
+ *                accumulating, read) as fp32 instead of bf16.
+ *   MSQ_U_ONLY   forward only: compute u = drop(x) A^T and skip y (y may be NULL).
+ *                For the recompute of a projection whose output the backward never
+ *                reads (the last projection of a block): its backward needs only its
+ *                input and u. */
 #define MSQ_ACT_F32 1u
 #define MSQ_OUT_F32 2u
+#define MSQ_U_ONLY 4u
 typedef struct {
   int32_t r;      /* 0 .. 64 */
   float alpha;
   float p_drop;   /* dropout probability on the LoRA input, in [0, 1) */
-  uint32_t flags; /* MSQ_ACT_F32 | MSQ_OUT_F32, other bits must be 0 */
+  uint32_t flags; /* MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY, other bits must be 0 */
 } msq_lora_cfg;
 
 /* Bytes of scratch device memory one nf4_lora_fwd or nf4_lora_bwd call with
@@ -175,12 +180,15 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
  * ("Poros" research post, the training-step paragraph; "Limitations",
  * "Pretraining is out of scope"; README, "How it works").
  *
- * A window groups window_blocks consecutive layers; the caller's device arena
- * is split into two slots of one window each (double buffering).  Layer blobs
- * live in pinned host memory (hipHostMalloc or equivalent) and are copied with
- * hipMemcpyAsync on copy_stream.  Each layer's device address is its offset in
- * the slot (blob offsets rounded up to 256 bytes).  The window object owns only
- * events and bookkeeping; it is not thread-safe.
+ * A window groups window_blocks consecutive layers; the caller's device arena is
+ * split into n_slots slots of one window each (n_slots >= 2: one computing while
+ * the next loads; more slots let the copies run further ahead).  With
+ * window_blocks = 1 and n_slots = 2B the same arena as B-block windows double
+ * buffered becomes a ring of single-layer slots, released and refilled layer by
+ * layer.  Layer blobs live in pinned host memory (hipHostMalloc or equivalent) and
+ * are copied with hipMemcpyAsync on copy_stream.  Each layer's device address is
+ * its offset in the slot (blob offsets rounded up to 256 bytes).  The window object
+ * owns only events and bookkeeping; it is not thread-safe.
  *
  *   host_blobs  host array of n_layers pointers to pinned host memory
  *   blob_bytes  host array of n_layers sizes
@@ -196,15 +204,16 @@ typedef struct {
   uint64_t windows_reused;  /* prefetches satisfied by a slot that still held the window */
 } msq_window_stats;
 
-size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks);
+size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks,
+                                int n_slots);
 int block_stream_create(msq_window** out, const void* const* host_blobs, const size_t* blob_bytes,
-                        int n_layers, int window_blocks, void* dev_arena, size_t arena_bytes,
-                        msq_stream_t copy_stream);
+                        int n_layers, int window_blocks, int n_slots, void* dev_arena,
+                        size_t arena_bytes, msq_stream_t copy_stream);
 /* Start loading the window that begins at first_layer (a multiple of
- * window_blocks) into the free slot: the copy stream first waits until the
- * compute stream released that slot, then copies, then marks it ready.  If a
- * free slot still holds this window's bytes, no copy is issued.  No free slot:
- * MSQ_E_ORDER. */
+ * window_blocks) into a free slot (the least recently released one): the copy
+ * stream first waits until the compute stream released that slot, then copies,
+ * then marks it ready.  If a free slot still holds this window's bytes, no copy is
+ * issued.  No free slot: MSQ_E_ORDER. */
 int block_stream_prefetch(msq_window* w, int first_layer);
 /* Make `compute` wait until the window holding `layer` has arrived, and return
  * the layer's device address.  Window not prefetched: MSQ_E_ORDER. */

@@ -30,6 +30,7 @@ class RngKey(ctypes.Structure):
 
 MSQ_ACT_F32 = 1
 MSQ_OUT_F32 = 2
+MSQ_U_ONLY = 4
 
 
 class LoraCfg(ctypes.Structure):
@@ -69,8 +70,8 @@ _SIG = {
     "nf4_lora_bwd": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, LoraCfg, RngKey, _P,
                                     _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
                                     _P]),
-    "block_stream_arena_bytes": (ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int]),
-    "block_stream_create": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.c_int, _P,
+    "block_stream_arena_bytes": (ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "block_stream_create": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
                                            ctypes.c_size_t, _P]),
     "block_stream_prefetch": (ctypes.c_int, [_P, ctypes.c_int]),
     "block_stream_acquire": (ctypes.c_int, [_P, ctypes.c_int, _P, _P]),

@@ -52,7 +52,7 @@ int check_linear(const char* fn, int64_t t, int64_t k, int64_t n, const msq_lora
   if (!(cfg.p_drop >= 0.0f && cfg.p_drop < 1.0f)) return set_error(MSQ_E_DROPOUT, "%s: p_drop=%g outside [0, 1)", fn, (double)cfg.p_drop);
   if (cfg.r > 0 && !isfinite(cfg.alpha)) return set_error(MSQ_E_DROPOUT, "%s: alpha is not finite", fn);
   if (key.proj >= 16 || key.layer >= (1u << 28)) return set_error(MSQ_E_INVAL, "%s: rng key proj must be < 16 and layer < 2^28", fn);
-  if (cfg.flags & ~(MSQ_ACT_F32 | MSQ_OUT_F32)) return set_error(MSQ_E_INVAL, "%s: unknown flags 0x%x", fn, cfg.flags);
+  if (cfg.flags & ~(MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY)) return set_error(MSQ_E_INVAL, "%s: unknown flags 0x%x", fn, cfg.flags);
   return MSQ_OK;
 }
 
@@ -173,8 +173,11 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
                  size_t workspace_bytes, msq_stream_t stream) {
   int rc = check_linear("nf4_lora_fwd", t, k, n, cfg, key);
   if (rc) return rc;
-  if (!codes || !absmax || !workspace || (t > 0 && (!x || !y)))
+  const bool u_only = cfg.flags & MSQ_U_ONLY;
+  if (!codes || !absmax || !workspace || (t > 0 && (!x || (!y && !u_only))))
     return set_error(MSQ_E_INVAL, "nf4_lora_fwd: null pointer");
+  if (u_only && (cfg.r == 0 || !u_out))
+    return set_error(MSQ_E_INVAL, "nf4_lora_fwd: MSQ_U_ONLY needs r > 0 and u_out");
   if (cfg.r > 0 && (!A || !B)) return set_error(MSQ_E_INVAL, "nf4_lora_fwd: r > 0 needs A and B");
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(codes, 16) || !aligned(absmax, 4) ||
       !aligned(bias, 8) || !aligned(A, 16) || !aligned(B, 16) || !aligned(u_out, 4) || !aligned(workspace, 256))
@@ -192,14 +195,14 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
   float* part = (float*)(ws + p.off_part_fwd);
   const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
   hipError_t e = hipSuccess;
+  if (r > 0) e = launch_skinny(x, act_f32, t, k, A, 0, r, 1.0f, d, (float*)(ws + p.off_sk_fwd), u, s);
+  if (u_only) return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
   const uint16_t* xb = (const uint16_t*)x;
-  if (act_f32) {
+  if (e == hipSuccess && act_f32) {
     uint16_t* tmp = (uint16_t*)(ws + p.off_act_fwd);
     e = launch_cvt_bf16((const float*)x, t * k, tmp, s);
     xb = tmp;
   }
-  if (e == hipSuccess && r > 0)
-    e = launch_skinny(x, act_f32, t, k, A, 0, r, 1.0f, d, (float*)(ws + p.off_sk_fwd), u, s);
   if (e == hipSuccess) {
     GemmLaunch L;
     L.mode = 0;
@@ -236,6 +239,7 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
   if (!codes || !absmax || !workspace || (t > 0 && (!dy || !x || !dx)))
     return set_error(MSQ_E_INVAL, "nf4_lora_bwd: null pointer");
   if (cfg.r > 0 && (!A || !B || !dA || !dB)) return set_error(MSQ_E_INVAL, "nf4_lora_bwd: r > 0 needs A, B, dA, dB");
+  if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "nf4_lora_bwd: MSQ_U_ONLY is a forward flag");
   if ((dx_accumulate != 0 && dx_accumulate != 1) || (dAB_accumulate != 0 && dAB_accumulate != 1))
     return set_error(MSQ_E_INVAL, "nf4_lora_bwd: accumulate flags must be 0 or 1");
   if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16) || !aligned(codes, 16) || !aligned(absmax, 4) ||

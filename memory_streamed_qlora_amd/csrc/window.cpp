@@ -7,7 +7,8 @@
 // "Limitations", "Pretraining is out of scope").  Their block-size sweep (peak memory
 // at block sizes 1..16, "Poros" research post, memory paragraph) grows by two
 // blocks' worth per doubling, consistent with one window computing while the next
-// one loads; this window keeps exactly two slots.
+// one loads: the default is two slots.  More slots let the copies run further ahead,
+// and single-layer slots let a slot be refilled as soon as its one layer is done.
 //
 // Ordering: the copy stream waits on a slot's "freed" event (recorded on the
 // compute stream by release) before overwriting it, and records the slot's "ready"
@@ -32,19 +33,18 @@ enum SlotState { SLOT_FREE = 0, SLOT_HELD = 1 };
 }  // namespace
 
 struct msq_window {
-  int n_layers = 0, window_blocks = 0, n_windows = 0;
+  int n_layers = 0, window_blocks = 0, n_windows = 0, n_slots = 0;
   std::vector<const void*> host;
   std::vector<size_t> bytes;
   std::vector<size_t> offset;  // offset of each layer inside its window's slot
   size_t slot_bytes = 0;
-  char* slot_base[2] = {nullptr, nullptr};
+  std::vector<char*> slot_base;
   hipStream_t copy = nullptr;
-  hipEvent_t ready[2] = {nullptr, nullptr};
-  hipEvent_t freed[2] = {nullptr, nullptr};
-  bool freed_recorded[2] = {false, false};
-  int slot_window[2] = {-1, -1};  // window whose bytes the slot holds (or will hold)
-  int state[2] = {SLOT_FREE, SLOT_FREE};
-  uint64_t release_tick[2] = {0, 0};
+  std::vector<hipEvent_t> ready, freed;
+  std::vector<char> freed_recorded;
+  std::vector<int> slot_window;  // window whose bytes the slot holds (or will hold)
+  std::vector<int> state;
+  std::vector<uint64_t> release_tick;
   uint64_t tick = 0;
   msq_window_stats stats = {0, 0, 0};
 };
@@ -64,7 +64,7 @@ size_t max_window_bytes(const size_t* blob_bytes, int n_layers, int wb) {
 }
 
 int find_slot(const msq_window* w, int win, int state) {
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < w->n_slots; ++i)
     if (w->slot_window[i] == win && w->state[i] == state) return i;
   return -1;
 }
@@ -73,29 +73,31 @@ int find_slot(const msq_window* w, int win, int state) {
 
 extern "C" {
 
-size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks) {
-  if (!blob_bytes || n_layers <= 0 || window_blocks <= 0) return 0;
-  return 2 * max_window_bytes(blob_bytes, n_layers, window_blocks);
+size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks,
+                                int n_slots) {
+  if (!blob_bytes || n_layers <= 0 || window_blocks <= 0 || n_slots < 2) return 0;
+  return (size_t)n_slots * max_window_bytes(blob_bytes, n_layers, window_blocks);
 }
 
 int block_stream_create(msq_window** out, const void* const* host_blobs, const size_t* blob_bytes,
-                        int n_layers, int window_blocks, void* dev_arena, size_t arena_bytes,
-                        msq_stream_t copy_stream) {
+                        int n_layers, int window_blocks, int n_slots, void* dev_arena,
+                        size_t arena_bytes, msq_stream_t copy_stream) {
   if (!out || !host_blobs || !blob_bytes || !dev_arena)
     return set_error(MSQ_E_INVAL, "block_stream_create: null pointer");
   *out = nullptr;
-  if (n_layers <= 0 || window_blocks <= 0 || window_blocks > n_layers)
-    return set_error(MSQ_E_INVAL, "block_stream_create: n_layers=%d window_blocks=%d", n_layers, window_blocks);
+  if (n_layers <= 0 || window_blocks <= 0 || window_blocks > n_layers || n_slots < 2 || n_slots > 1024)
+    return set_error(MSQ_E_INVAL, "block_stream_create: n_layers=%d window_blocks=%d n_slots=%d", n_layers,
+                     window_blocks, n_slots);
   if ((uintptr_t)dev_arena % 256)
     return set_error(MSQ_E_INVAL, "block_stream_create: arena must be 256-byte aligned");
   for (int l = 0; l < n_layers; ++l)
     if (!host_blobs[l] || blob_bytes[l] == 0)
       return set_error(MSQ_E_INVAL, "block_stream_create: layer %d has no host blob", l);
-  const size_t need = 2 * max_window_bytes(blob_bytes, n_layers, window_blocks);
+  const size_t need = (size_t)n_slots * max_window_bytes(blob_bytes, n_layers, window_blocks);
   if (arena_bytes < need) {
     int fit = 0;
     for (int wb = window_blocks - 1; wb >= 1; --wb)
-      if (2 * max_window_bytes(blob_bytes, n_layers, wb) <= arena_bytes) {
+      if ((size_t)n_slots * max_window_bytes(blob_bytes, n_layers, wb) <= arena_bytes) {
         fit = wb;
         break;
       }
@@ -119,15 +121,22 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
       o += align256(blob_bytes[l]);
     }
   }
-  w->slot_bytes = need / 2;
-  w->slot_base[0] = (char*)dev_arena;
-  w->slot_base[1] = (char*)dev_arena + w->slot_bytes;
+  w->n_slots = n_slots;
+  w->slot_bytes = need / n_slots;
+  w->slot_base.resize(n_slots);
+  for (int i = 0; i < n_slots; ++i) w->slot_base[i] = (char*)dev_arena + (size_t)i * w->slot_bytes;
+  w->ready.assign(n_slots, nullptr);
+  w->freed.assign(n_slots, nullptr);
+  w->freed_recorded.assign(n_slots, 0);
+  w->slot_window.assign(n_slots, -1);
+  w->state.assign(n_slots, SLOT_FREE);
+  w->release_tick.assign(n_slots, 0);
   w->copy = (hipStream_t)copy_stream;
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < n_slots; ++i) {
     hipError_t e = hipEventCreateWithFlags(&w->ready[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&w->freed[i], hipEventDisableTiming);
     if (e != hipSuccess) {
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < n_slots; ++j) {
         if (w->ready[j]) (void)hipEventDestroy(w->ready[j]);
         if (w->freed[j]) (void)hipEventDestroy(w->freed[j]);
       }
@@ -153,7 +162,7 @@ int block_stream_prefetch(msq_window* w, int first_layer) {
   }
   // least recently released free slot
   slot = -1;
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < w->n_slots; ++i)
     if (w->state[i] == SLOT_FREE && (slot < 0 || w->release_tick[i] < w->release_tick[slot])) slot = i;
   if (slot < 0)
     return set_error(MSQ_E_ORDER, "block_stream_prefetch: no free slot for window %d (release a window first)", win);
@@ -196,7 +205,7 @@ int block_stream_release(msq_window* w, int first_layer, msq_stream_t compute) {
   if (slot < 0) return set_error(MSQ_E_ORDER, "block_stream_release: window %d is not held", win);
   const hipError_t e = hipEventRecord(w->freed[slot], (hipStream_t)compute);
   if (e != hipSuccess) return hip_error(e, "block_stream_release: hipEventRecord");
-  w->freed_recorded[slot] = true;
+  w->freed_recorded[slot] = 1;
   w->state[slot] = SLOT_FREE;
   w->release_tick[slot] = ++w->tick;
   return MSQ_OK;
@@ -211,7 +220,7 @@ int block_stream_stats(const msq_window* w, msq_window_stats* out) {
 int block_stream_destroy(msq_window* w) {
   if (!w) return MSQ_OK;
   hipError_t e = hipSuccess;
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < w->n_slots; ++i) {
     if (w->ready[i]) {
       const hipError_t e1 = hipEventSynchronize(w->ready[i]);
       if (e == hipSuccess) e = e1;

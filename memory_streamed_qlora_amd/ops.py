@@ -142,10 +142,11 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
                  cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
                  u_out: Optional[torch.Tensor] = None, want_u: bool = True,
                  workspace: Optional[Workspace] = None, stream=None,
-                 out_dtype: Optional[torch.dtype] = None):
+                 out_dtype: Optional[torch.dtype] = None, u_only: bool = False):
     """y = x W^T + bias + (alpha/r) drop(x) A^T B^T.  Returns (y, u) (u None if not wanted).
 
-    x may be bf16 or fp32; y is out_dtype (default: x's dtype, or y's if given)."""
+    x may be bf16 or fp32; y is out_dtype (default: x's dtype, or y's if given).
+    u_only: compute only u (y is None)."""
     t, k = x.shape
     n = codes.shape[0]
     _req(x, "x", x.dtype, (t, k))
@@ -159,9 +160,16 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
     if r > 0:
         _req(A, "A", torch.float32, (r, k))
         _req(B, "B", torch.float32, (n, r))
-    if y is None:
-        y = torch.empty((t, n), dtype=out_dtype, device=x.device)
-    _req(y, "y", out_dtype, (t, n))
+    if u_only:
+        if r == 0:
+            raise ValueError("u_only needs r > 0")
+        flags |= _abi.MSQ_U_ONLY
+        want_u = True
+        y = None
+    else:
+        if y is None:
+            y = torch.empty((t, n), dtype=out_dtype, device=x.device)
+        _req(y, "y", out_dtype, (t, n))
     if want_u and r > 0 and u_out is None:
         u_out = torch.empty((t, r), dtype=torch.float32, device=x.device)
     if u_out is not None:
@@ -220,11 +228,12 @@ def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax:
 class BlockStreamWindow:
     """block_stream_* over pinned host blobs and a caller-owned device arena."""
 
-    def __init__(self, host_blobs: Sequence[torch.Tensor], window_blocks: int,
+    def __init__(self, host_blobs: Sequence[torch.Tensor], window_blocks: int, n_slots: int = 2,
                  arena: Optional[torch.Tensor] = None, copy_stream: Optional[torch.cuda.Stream] = None,
                  device=None):
         self.n_layers = len(host_blobs)
         self.window_blocks = int(window_blocks)
+        self.n_slots = int(n_slots)
         for i, b in enumerate(host_blobs):
             if b.device.type != "cpu" or not b.is_pinned() or b.dtype != torch.uint8 or not b.is_contiguous():
                 raise ValueError(f"host blob {i} must be a contiguous pinned uint8 CPU tensor")
@@ -232,7 +241,7 @@ class BlockStreamWindow:
         self._ptrs = (ctypes.c_void_p * self.n_layers)(*[b.data_ptr() for b in host_blobs])
         self._sizes = (ctypes.c_size_t * self.n_layers)(*[b.numel() for b in host_blobs])
         self.arena_bytes_needed = int(lib().block_stream_arena_bytes(self._sizes, self.n_layers,
-                                                                     self.window_blocks))
+                                                                     self.window_blocks, self.n_slots))
         dev = torch.device(device or "cuda")
         if arena is None:
             arena = torch.empty(self.arena_bytes_needed, dtype=torch.uint8, device=dev)
@@ -242,7 +251,7 @@ class BlockStreamWindow:
         self.copy_stream = copy_stream or torch.cuda.Stream(device=arena.device)
         h = ctypes.c_void_p()
         check("block_stream_create", lib().block_stream_create(
-            ctypes.byref(h), self._ptrs, self._sizes, self.n_layers, self.window_blocks,
+            ctypes.byref(h), self._ptrs, self._sizes, self.n_layers, self.window_blocks, self.n_slots,
             arena.data_ptr(), arena.numel(), self.copy_stream.cuda_stream))
         self._h = h
 

@@ -3,7 +3,7 @@
 The step the pages describe ("Poros" research post, the training-step paragraph;
 package README, "How it works"):
   forward   blocks run in order while their frozen NF4 weights stream through a
-            two-slot device window (block_stream_prefetch on a side stream); only
+            device window of n_slots slots (block_stream_prefetch on a side stream); only
             block-boundary activations are kept; each window is released (a pointer
             release -- the base is read-only) as soon as its blocks have run
   loss      frozen bf16 lm_head + mean next-token cross-entropy
@@ -102,9 +102,14 @@ class LayerLayout:
 
 class _NF4LoraLinear(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, A, B, codes, absmax, bias, cfg, key):
-        need_u = torch.is_grad_enabled() or A.requires_grad
-        y, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=True)
+    def forward(ctx, x, A, B, codes, absmax, bias, cfg, key, value_unused):
+        if value_unused:
+            # selective recompute: the backward reads only x and u, never y, so the
+            # frozen-base product is skipped and y is a zero placeholder
+            _, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, u_only=True)
+            y = x.new_zeros(()).expand(x.shape[0], codes.shape[0])
+        else:
+            y, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=True)
         ctx.save_for_backward(x, A, B, u)
         ctx.codes, ctx.absmax, ctx.cfg, ctx.key = codes, absmax, cfg, key
         return y
@@ -114,12 +119,14 @@ class _NF4LoraLinear(torch.autograd.Function):
         x, A, B, u = ctx.saved_tensors
         dx, dA, dB = ops.nf4_lora_bwd(dy.contiguous(), x, ctx.codes, ctx.absmax, A, B, ctx.cfg,
                                       ctx.key, u=u)
-        return dx, dA, dB, None, None, None, None, None
+        return dx, dA, dB, None, None, None, None, None, None
 
 
-def nf4_lora_linear(x, A, B, codes, absmax, bias, cfg: ops.Lora, key) -> torch.Tensor:
+def nf4_lora_linear(x, A, B, codes, absmax, bias, cfg: ops.Lora, key,
+                    value_unused: bool = False) -> torch.Tensor:
     if torch.is_grad_enabled() and (x.requires_grad or A.requires_grad or B.requires_grad):
-        return _NF4LoraLinear.apply(x, A, B, codes, absmax, bias, cfg, key)
+        return _NF4LoraLinear.apply(x, A, B, codes, absmax, bias, cfg, key,
+                                    value_unused and cfg.r > 0)
     y, _ = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=False)
     return y
 
@@ -174,11 +181,13 @@ class Stack:
     """A Qwen2.5-shaped NF4 + LoRA stack with streamed or resident frozen base."""
 
     def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
-                 window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None):
+                 window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
+                 n_slots: int = 2):
         assert mode in ("streamed", "resident")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
         self.cfg = ops.Lora(r, alpha, p_drop)
         self.window_blocks = window_blocks
+        self.n_slots = n_slots
         self.dev = torch.device(device or "cuda")
         self.layout = LayerLayout(shape)
         self.host_blobs: List[torch.Tensor] = []
@@ -228,7 +237,7 @@ class Stack:
                                      foreach=True)
         if self.mode == "streamed":
             self.copy_stream = torch.cuda.Stream(device=self.dev)
-            self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks,
+            self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks, self.n_slots,
                                                 copy_stream=self.copy_stream, device=self.dev)
 
     @classmethod
@@ -268,14 +277,19 @@ class Stack:
         return st
 
     # -- one layer -----------------------------------------------------------------
-    def _lin(self, x, l, views, proj, step, micro):
+    def _lin(self, x, l, views, proj, step, micro, value_unused=False):
         key = ops.rng_key(self.seed, step, micro, l, PROJ_ID[proj])
         bias = views.get((proj, "bias"))
         return nf4_lora_linear(x, self.A[l][proj], self.B[l][proj], views[(proj, "codes")],
-                               views[(proj, "absmax")], bias, self.cfg, key)
+                               views[(proj, "absmax")], bias, self.cfg, key, value_unused)
 
-    def layer_forward(self, h: torch.Tensor, l: int, views, step: int, micro: int = 0) -> torch.Tensor:
-        """Activations stay fp32; the library rounds them to bf16 only as MFMA operands."""
+    def layer_forward(self, h: torch.Tensor, l: int, views, step: int, micro: int = 0,
+                      recompute: bool = False) -> torch.Tensor:
+        """Activations stay fp32; the library rounds them to bf16 only as MFMA operands.
+
+        recompute=True (the backward's rerun, with autograd recording): the layer's
+        output value is never read -- only its graph is -- so the down projection's
+        frozen-base product is skipped and the returned value is not the layer output."""
         sh = self.shape
         T = h.shape[0]
         xn = rmsnorm(h, self.ln1[l])
@@ -289,7 +303,7 @@ class Stack:
         g = self._lin(xn2, l, views, "gate", step, micro)
         u = self._lin(xn2, l, views, "up", step, micro)
         a = torch.nn.functional.silu(g) * u
-        return h1 + self._lin(a, l, views, "down", step, micro)
+        return h1 + self._lin(a, l, views, "down", step, micro, value_unused=recompute)
 
     # -- base residency --------------------------------------------------------------
     def _views(self, l: int):
@@ -308,8 +322,9 @@ class Stack:
         streamed = self.mode == "streamed"
         h = self.emb[tokens].float()
         bounds: List[torch.Tensor] = []
+        ahead = self.n_slots
         if streamed:
-            for w in wins[:2]:
+            for w in wins[:ahead]:
                 self.window.prefetch(w)
         with torch.no_grad():
             for wi, w in enumerate(wins):
@@ -318,8 +333,8 @@ class Stack:
                     h = self.layer_forward(h, l, self._views(l), step, micro)
                 if streamed:
                     self.window.release(w)
-                    if wi + 2 < len(wins):
-                        self.window.prefetch(wins[wi + 2])
+                    if wi + ahead < len(wins):
+                        self.window.prefetch(wins[wi + ahead])
         hf = h.detach().requires_grad_()
         with torch.enable_grad():
             hn = rmsnorm(hf, self.lnf).to(torch.bfloat16)
@@ -330,20 +345,20 @@ class Stack:
         del logits
         rw = wins[::-1]
         if streamed:
-            for w in rw[:2]:
+            for w in rw[:ahead]:
                 self.window.prefetch(w)
         for wi, w in enumerate(rw):
             for l in reversed(range(w, min(w + self.window_blocks, L))):
                 x_in = bounds[l].detach().requires_grad_()
                 with torch.enable_grad():
-                    out = self.layer_forward(x_in, l, self._views(l), step, micro)
+                    out = self.layer_forward(x_in, l, self._views(l), step, micro, recompute=True)
                 out.backward(dh)
                 dh = x_in.grad
                 bounds[l] = None
             if streamed:
                 self.window.release(w)
-                if wi + 2 < len(rw):
-                    self.window.prefetch(rw[wi + 2])
+                if wi + ahead < len(rw):
+                    self.window.prefetch(rw[wi + ahead])
         return loss.detach()
 
     def params(self) -> List[torch.nn.Parameter]:

@@ -105,16 +105,20 @@ def test_window_rejects_small_arena_and_names_what_fits():
     n = 8
     ptrs = (ctypes.c_void_p * n)(*([FAKE] * n))
     sizes = (ctypes.c_size_t * n)(*([1000 * 256] * n))
-    need = L.block_stream_arena_bytes(sizes, n, 4)
+    need = L.block_stream_arena_bytes(sizes, n, 4, 2)
     assert need == 2 * 4 * 1000 * 256
+    assert L.block_stream_arena_bytes(sizes, n, 1, 8) == need          # ring of 8 single layers
+    assert L.block_stream_arena_bytes(sizes, n, 2, 3) == 3 * 2 * 1000 * 256
+    assert L.block_stream_arena_bytes(sizes, n, 4, 1) == 0
     h = ctypes.c_void_p()
-    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, FAKE, need - 1, None)
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need - 1, None)
     assert rc == abi.MSQ_E_WINDOW
     assert "window_blocks=3" in _err()
-    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, FAKE, 1000, None)
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, 1000, None)
     assert rc == abi.MSQ_E_WINDOW and "not even one layer" in _err()
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 9, FAKE, need, None) == abi.MSQ_E_INVAL
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, FAKE + 16, need, None) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 9, 2, FAKE, need, None) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 1, FAKE, need, None) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE + 16, need, None) == abi.MSQ_E_INVAL
     assert L.block_stream_prefetch(None, 0) == abi.MSQ_E_INVAL
 
 

@@ -23,9 +23,10 @@ def _shape(sh: mi.BlockShape) -> S.Shape:
     return S.Shape(sh.hidden, sh.heads, sh.kv_heads, sh.head_dim, sh.inter, sh.layers, sh.vocab)
 
 
-def _build(sh: mi.BlockShape, seq, layers_np, glob_np, lora: mi.LoraSpec, mode, window_blocks, seed):
+def _build(sh: mi.BlockShape, seq, layers_np, glob_np, lora: mi.LoraSpec, mode, window_blocks, seed,
+           n_slots=2):
     st = S.Stack(_shape(sh), seq, r=lora.r, alpha=lora.alpha, p_drop=lora.p_drop,
-                 window_blocks=window_blocks, mode=mode, seed=seed)
+                 window_blocks=window_blocks, mode=mode, seed=seed, n_slots=n_slots)
     for p in layers_np:
         W = {proj: dev_bf16(p[proj]["W"]) for proj in S.PROJS}
         bias = {proj: dev_bf16(p[proj]["bias"]) for proj in ("q", "k", "v")}
@@ -122,8 +123,8 @@ def test_tiny_stack_step_vs_oracle():
     st.close()
 
 
-def _run_steps(sh, layers, glob, lo, mode, window_blocks, seed, steps, T):
-    st = _build(sh, T, layers, glob, lo, mode, window_blocks, seed)
+def _run_steps(sh, layers, glob, lo, mode, window_blocks, seed, steps, T, n_slots=2):
+    st = _build(sh, T, layers, glob, lo, mode, window_blocks, seed, n_slots)
     losses, norms = [], []
     for s in range(steps):
         toks = torch.from_numpy(mi.tokens(seed, 3, s, T, sh.vocab)).cuda()
@@ -147,26 +148,28 @@ def _assert_bitwise(a, b):
         assert torch.equal(sa[k], sb[k]), f"streamed != resident for {k}"
 
 
-@pytest.mark.parametrize("window_blocks", [1, 2])
-def test_tiny_streamed_equals_resident_bitwise(window_blocks):
+@pytest.mark.parametrize("window_blocks,n_slots", [(1, 2), (2, 2), (1, 3)])
+def test_tiny_streamed_equals_resident_bitwise(window_blocks, n_slots):
     lo, seed, T = mi.LoraSpec(8, 16.0, 0.1), 2, 32
     layers, glob = _tiny(seed, lo)
     res = _run_steps(TINY, layers, glob, lo, "resident", window_blocks, seed, 12, T)
-    stm = _run_steps(TINY, layers, glob, lo, "streamed", window_blocks, seed, 12, T)
+    stm = _run_steps(TINY, layers, glob, lo, "streamed", window_blocks, seed, 12, T, n_slots)
     _assert_bitwise(res, stm)
     assert res[0][0] != res[0][-1]           # the adapters actually train
     print("window stats", stm[3], flush=True)
 
 
-def test_qwen7b_streamed_equals_resident_bitwise():
-    """Qwen2.5-7B-shaped stack (28 layers) streamed in windows of 4 blocks from pinned
-    host memory, LoRA r16 alpha32 dropout 0.1, 512 tokens: 3 AdamW steps, every
-    parity surface compared with torch.equal."""
+@pytest.mark.parametrize("window_blocks,n_slots", [(4, 2), (1, 8)])
+def test_qwen7b_streamed_equals_resident_bitwise(window_blocks, n_slots):
+    """Qwen2.5-7B-shaped stack (28 layers) streamed from pinned host memory through a
+    window of 2 x 4 blocks (two 4-layer slots, or a ring of 8 one-layer slots), LoRA
+    r16 alpha32 dropout 0.1, 512 tokens: 3 AdamW steps, every parity surface compared
+    with torch.equal."""
     sh = S.QWEN25_7B
     out = []
     for mode in ("resident", "streamed"):
-        st = S.Stack.random(sh, 512, seed=0, cfg_id=3, r=16, alpha=32.0, p_drop=0.1, window_blocks=4,
-                            mode=mode)
+        st = S.Stack.random(sh, 512, seed=0, cfg_id=3, r=16, alpha=32.0, p_drop=0.1,
+                            window_blocks=window_blocks, n_slots=n_slots, mode=mode)
         losses, norms = [], []
         for s in range(3):
             loss, gn = st.train_step(S.random_tokens(0, s, 512, sh.vocab, st.dev))
@@ -180,11 +183,11 @@ def test_qwen7b_streamed_equals_resident_bitwise():
         torch.cuda.empty_cache()
     _assert_bitwise(out[0], out[1])
     stats = out[1][3]
-    n_win, steps = 7, 3
+    n_win, steps = 28 // window_blocks, 3
     assert stats["windows_copied"] + stats["windows_reused"] == steps * 2 * n_win
-    # the two windows left in the slots at each turnaround (end of forward, end of the
+    # the windows left in the slots at each turnaround (end of forward, end of the
     # previous step's backward) are not copied again
-    assert stats["windows_reused"] == 2 + 4 * (steps - 1)
+    assert stats["windows_reused"] == n_slots + 2 * n_slots * (steps - 1)
 
 
 def test_window_protocol():
@@ -220,3 +223,28 @@ def test_window_protocol():
     w.release(2)
     w.release(4)
     w.close()
+
+
+def test_selective_recompute_gives_identical_gradients():
+    """The backward's rerun skips the last projection's frozen-base product (its output
+    is never read); gradients must be bit-identical to a full recompute."""
+    sh, T, lo, seed, step = mi.QWEN25_05B, 256, mi.LoraSpec(16, 32.0, 0.1), 0, 1
+    prm = mi.block_params(seed, 5, 0, sh, lo)
+    io = mi.block_io(seed, 5, sh, T)
+    st = _build(sh, T, [prm], None, lo, "resident", 1, seed)
+    views = st._views(0)
+    dy = torch.from_numpy(io["dy"]).cuda()
+    grads = []
+    for recompute in (False, True):
+        for d in (st.A[0], st.B[0]):
+            for p in d.values():
+                p.grad = None
+        x = torch.from_numpy(io["x"]).cuda().requires_grad_()
+        out = st.layer_forward(x, 0, views, step, recompute=recompute)
+        out.backward(dy)
+        torch.cuda.synchronize()
+        grads.append([x.grad.clone()] + [st.A[0][p].grad.clone() for p in S.PROJS]
+                     + [st.B[0][p].grad.clone() for p in S.PROJS])
+    for a, b in zip(*grads):
+        assert torch.equal(a, b)
+    st.close()
