@@ -28,6 +28,32 @@ METRIC = "train tokens/s (s/step) streamed NF4-LoRA fwd+bwd, 32B shape; MFMA uti
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 PAGES_A100_S_PER_STEP = 2.0489  # Official A100 results, Benchmark matrix, Qwen2.5-32B streamed
+GEMM_SOURCES = ("memory_streamed_qlora_amd/csrc/gemm.hip", "memory_streamed_qlora_amd/csrc/device_common.hpp")
+COUNTERS_FILE = "profiles/nf4_gemm_qwen32b_step_counters.md"
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, COUNTERS_FILE)
+    if not os.path.exists(path):
+        return None
+    want = gemm_source_hash()
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 5 and parts[0] == "traffic_bytes_per_launch" and parts[1] == kernel:
+            if parts[3] == "sources" and parts[4] == want:
+                return float(parts[2])
+    return None
 
 
 def log(*a):
@@ -114,7 +140,41 @@ def cpu_baseline(seconds_hint=True) -> dict:
             "s_per_step_extrapolated": step_s}
 
 
+def rocprof_summary(d: str) -> int:
+    """Summarise rocprofv3 CSV output found under directory d (kernel stats and/or
+    per-dispatch counter collections) as markdown on stdout."""
+    import csv
+    import glob
+
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        rows = list(csv.DictReader(open(path)))
+        tot = sum(float(r["TotalDurationNs"]) for r in rows)
+        print(f"### kernel stats ({os.path.relpath(path, d)})\n")
+        print("| kernel | calls | avg us | total ms | % |")
+        print("|---|---|---|---|---|")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:25]:
+            print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                  f"{float(r['TotalDurationNs']) / 1e6:.1f} | {100 * float(r['TotalDurationNs']) / tot:.1f} |")
+        print()
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        agg = {}
+        for r in csv.DictReader(open(path)):
+            k = (r["Kernel_Name"][:90], r["Counter_Name"])
+            a = agg.setdefault(k, [0, 0.0, set()])
+            a[2].add(r.get("Dispatch_Id"))
+            a[1] += float(r["Counter_Value"])
+        print(f"### counters ({os.path.relpath(path, d)})\n")
+        print("| kernel | counter | dispatches | avg per dispatch |")
+        print("|---|---|---|---|")
+        for (kname, cname), (_, total, disp) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:30]:
+            print(f"| {kname} | {cname} | {len(disp)} | {total / max(1, len(disp)):.1f} |")
+        print()
+    return 0
+
+
 def main() -> int:
+    if len(sys.argv) == 3 and sys.argv[1] == "--rocprof-summary":
+        return rocprof_summary(sys.argv[2])
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
@@ -123,7 +183,8 @@ def main() -> int:
     ap.add_argument("--window-blocks", type=int, default=4,
                     help="layers per window slot (blocks per streamed window)")
     ap.add_argument("--slots", type=int, default=3, help="window slots in the device arena (prefetch depth + 1)")
-    ap.add_argument("--no-resident", action="store_true", help="skip the resident comparison run")
+    ap.add_argument("--resident", action="store_true",
+                    help="also time the same step with the whole base resident in device memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -181,7 +242,7 @@ def main() -> int:
         return out
 
     streamed = run("streamed")
-    resident = None if args.no_resident else run("resident")
+    resident = run("resident") if args.resident else None
 
     ms = streamed["seconds"] / args.steps * 1e3
     value = T * args.steps / streamed["seconds"]
@@ -219,7 +280,7 @@ def main() -> int:
                    "dropout": 0.0, "optimizer": "AdamW", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "avg_launch_ms": round(avg_ms, 4),
+                     "traffic": measured_traffic(name), "avg_launch_ms": round(avg_ms, 4),
                      "algorithmic_gflop_per_launch": round(avg_flops / 1e9, 3)},
         "h2d": {"bytes_per_step": int(h2d_bytes), "achieved_GBps": round(h2d_rate, 1),
                 "ceiling_GBps": round(ceiling, 1), "frac": round(h2d_rate / ceiling, 3),
