@@ -80,8 +80,8 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   o = align256(o + (size_t)p.fwd.splits * t * n * sizeof(float));
   p.off_u_fwd = o;
   o = align256(o + tr);
-  p.off_act_fwd = o;  // bf16 copy of fp32 activations for the MFMA operand
-  o = align256(o + (size_t)t * k * sizeof(uint16_t));
+  p.off_act_fwd = o;  // x packed into MFMA-fragment order (bf16)
+  o = align256(o + (size_t)frag_rows(t) * k * sizeof(uint16_t));
   p.off_sk_fwd = o;   // chunk partials of the rank-r skinny products
   o = align256(o + (size_t)((k + SKINNY_CHUNK - 1) / SKINNY_CHUNK) * t * r * sizeof(float));
   p.fwd_bytes = o;
@@ -97,8 +97,8 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   o = align256(o + (size_t)p.nch * r * k * sizeof(float));
   p.off_pb = o;
   o = align256(o + (size_t)p.nch * r * n * sizeof(float));
-  p.off_act_bwd = o;
-  o = align256(o + (size_t)t * n * sizeof(uint16_t));
+  p.off_act_bwd = o;  // dy packed into MFMA-fragment order (bf16)
+  o = align256(o + (size_t)frag_rows(t) * n * sizeof(uint16_t));
   p.off_sk_bwd = o;
   o = align256(o + (size_t)((std::max(k, n) + SKINNY_CHUNK - 1) / SKINNY_CHUNK) * t * r * sizeof(float));
   p.bwd_bytes = o;
@@ -197,12 +197,8 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
   hipError_t e = hipSuccess;
   if (r > 0) e = launch_skinny(x, act_f32, t, k, A, 0, r, 1.0f, d, (float*)(ws + p.off_sk_fwd), u, s);
   if (u_only) return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
-  const uint16_t* xb = (const uint16_t*)x;
-  if (e == hipSuccess && act_f32) {
-    uint16_t* tmp = (uint16_t*)(ws + p.off_act_fwd);
-    e = launch_cvt_bf16((const float*)x, t * k, tmp, s);
-    xb = tmp;
-  }
+  uint16_t* xb = (uint16_t*)(ws + p.off_act_fwd);
+  if (e == hipSuccess) e = launch_pack_frag(x, act_f32, t, k, xb, s);
   if (e == hipSuccess) {
     GemmLaunch L;
     L.mode = 0;
@@ -261,12 +257,8 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
     float* du = (float*)(ws + p.off_du);
     float* sk = (float*)(ws + p.off_sk_bwd);
     const float* uu = u;
-    const uint16_t* dyb = (const uint16_t*)dy;
-    if (act_f32) {
-      uint16_t* tmp = (uint16_t*)(ws + p.off_act_bwd);
-      e = launch_cvt_bf16((const float*)dy, t * n, tmp, s);
-      dyb = tmp;
-    }
+    uint16_t* dyb = (uint16_t*)(ws + p.off_act_bwd);
+    e = launch_pack_frag(dy, act_f32, t, n, dyb, s);
     if (e == hipSuccess && r > 0 && !uu) {
       float* ut = (float*)(ws + p.off_u_bwd);
       e = launch_skinny(x, act_f32, t, k, A, 0, r, 1.0f, d, sk, ut, s);

@@ -72,11 +72,13 @@ struct Nf4Planes {
   uint32_t lo[4], hi[4];
 };
 
-// Two floats -> packed bf16 pair (RNE), element a in the low half.  On gfx950 the
-// compiler emits one v_cvt_pk_bf16_f32 for the pair.
+// Two floats -> packed bf16 pair (RNE), element a in the low half: one
+// v_cvt_pk_bf16_f32 on gfx950 (the vector conversion keeps the pair together).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ Nf4Planes nf4_planes(const Nf4Lut& lut, float a) {
@@ -93,29 +95,27 @@ __device__ __forceinline__ Nf4Planes nf4_planes(const Nf4Lut& lut, float a) {
   return P;
 }
 
-// sel: four selector bytes, each a code 0..15.  Returns the four bf16 values as
-// two dwords (element 0 in the low half of .x).
+// sel: four selector bytes whose low nibbles are codes 0..15 (high nibbles are
+// ignored).  Returns the four bf16 values as two dwords (element 0 in the low half
+// of .x).  Each plane is looked up in both 8-entry halves of the table; a third
+// v_perm then takes byte i from the upper half when bit 3 of code i is set.
 __device__ __forceinline__ uint2 nf4_lookup4(const Nf4Planes& P, uint32_t sel) {
   const uint32_t s7 = sel & 0x07070707u;
-  const uint32_t upper = ((sel >> 3) & 0x01010101u) * 0xffu;  // 0xff bytes where code >= 8
-  const uint32_t lo_a = __builtin_amdgcn_perm(P.lo[1], P.lo[0], s7);
-  const uint32_t lo_b = __builtin_amdgcn_perm(P.lo[3], P.lo[2], s7);
-  const uint32_t hi_a = __builtin_amdgcn_perm(P.hi[1], P.hi[0], s7);
-  const uint32_t hi_b = __builtin_amdgcn_perm(P.hi[3], P.hi[2], s7);
-  const uint32_t lo = (lo_b & upper) | (lo_a & ~upper);
-  const uint32_t hi = (hi_b & upper) | (hi_a & ~upper);
+  const uint32_t pick = ((sel >> 1) & 0x04040404u) | 0x03020100u;  // byte i: i, or 4+i if code >= 8
+  const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(P.lo[3], P.lo[2], s7),
+                                            __builtin_amdgcn_perm(P.lo[1], P.lo[0], s7), pick);
+  const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(P.hi[3], P.hi[2], s7),
+                                            __builtin_amdgcn_perm(P.hi[1], P.hi[0], s7), pick);
   return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
 }
 
 // Eight codes of one packed dword (bytes b0..b3, even element in the high nibble)
-// -> eight bf16 values in four dwords.
+// -> eight bf16 values in four dwords.  u = w >> 4 carries the high nibbles in its
+// byte-wise low nibbles, so two v_perm interleave [b0.hi, b0.lo, b1.hi, b1.lo] etc.
 __device__ __forceinline__ void nf4_dequant8(const Nf4Planes& P, uint32_t w, uint32_t out[4]) {
-  const uint32_t x0 = __builtin_amdgcn_perm(0u, w, 0x01010000u);  // [b0, b0, b1, b1]
-  const uint32_t x1 = __builtin_amdgcn_perm(0u, w, 0x03030202u);  // [b2, b2, b3, b3]
-  const uint32_t s0 = ((x0 >> 4) & 0x000f000fu) | (x0 & 0x0f000f00u);
-  const uint32_t s1 = ((x1 >> 4) & 0x000f000fu) | (x1 & 0x0f000f00u);
-  const uint2 r0 = nf4_lookup4(P, s0);
-  const uint2 r1 = nf4_lookup4(P, s1);
+  const uint32_t u = w >> 4;
+  const uint2 r0 = nf4_lookup4(P, __builtin_amdgcn_perm(w, u, 0x05010400u));
+  const uint2 r1 = nf4_lookup4(P, __builtin_amdgcn_perm(w, u, 0x07030602u));
   out[0] = r0.x;
   out[1] = r0.y;
   out[2] = r1.x;

@@ -3,22 +3,26 @@
 // Forward:  P[s][t][n] = sum_{k in split s} x[t][k]  * W[n][k]    ("NT")
 // Backward: P[s][t][k] = sum_{n in split s} dy[t][n] * W[n][k]    ("NN", dx of the base)
 // W is never materialised: each workgroup reads NF4 codes and per-64 absmax straight
-// from HBM (coalesced 16-byte loads), builds the block's 16-entry bf16 table
-// bf16_rne(L[c] * absmax), looks codes up four at a time with v_perm, and writes the
-// bf16 tile into LDS in the layout the MFMA operand reads want; the contraction
-// runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The pages' base is
-// frozen (never differentiated: "Poros" research post, training-step paragraph),
-// so there is no dW kernel.
+// from HBM, builds the block's 16-entry bf16 table bf16_rne(L[c] * absmax), looks codes
+// up four at a time with v_perm, and writes the bf16 tile into LDS in the layout the
+// MFMA operand reads want; the contraction runs on v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation.  The pages' base is frozen (never differentiated: "Poros" research
+// post, training-step paragraph), so there is no dW kernel.
 //
-// Tile: BM=128 rows of t x BN=128 output columns x BK=64 reduction, 256 threads =
-// 4 waves in a 2x2 grid, each wave owns a 64x64 sub-tile = 2x2 MFMA 32x32 blocks.
+// Tile: BM=256 rows of t x BN=128 output columns x BK=64 reduction, 256 threads = 4
+// waves; wave w owns rows 64w..64w+63 and all 128 columns (2x4 MFMA 32x32 blocks).
+// The activation operand comes straight from global memory into registers, packed in
+// MFMA-fragment order beforehand (launch_pack_frag) so that each load is one contiguous
+// 1 KB block; only the dequantized W tile goes through LDS (double-buffered, one
+// barrier per k-step), and each dequantized element feeds 256 rows.  Within a k-step,
+// the dequantization of the next tile is interleaved with the MFMAs of this one.
 // The rank-r LoRA term of the same output tile is one more MFMA k-step per 16 ranks
-// (operands split into bf16 hi/lo pairs for ~fp32 accuracy); in the backward it goes
-// to a second accumulator so the dropout keep-mask can be applied per element.
-// Unsplit launches write the final output (bias or the old dx added, rounded once);
-// the reduction can instead be split over gridDim.z, in which case split 0 carries
-// the LoRA term and fp32 partial tiles go to a workspace summed in split order by a
-// separate kernel, so results never depend on timing.
+// (operands split into bf16 hi/lo pairs for ~fp32 accuracy); in the backward the
+// dropout keep-mask is applied per element of that term.  Unsplit launches write the
+// final output (bias or the old dx added, rounded once); the reduction can instead be
+// split over gridDim.z, in which case split 0 carries the LoRA term and fp32 partial
+// tiles go to a workspace summed in split order by a separate kernel, so results never
+// depend on timing.
 #include "internal.hpp"
 
 namespace msq {
@@ -27,6 +31,7 @@ namespace {
 constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
 constexpr int PAD = 8;              // bf16 elements of row padding in LDS
 constexpr int LDW = BK + PAD;       // LDS row pitch in bf16 elements (144 bytes)
+static_assert(BM == 256 && BN == 128 && BK == 64, "the thread mappings below assume this tile");
 constexpr int THREADS = 256;
 
 struct GemmArgs {
@@ -52,11 +57,18 @@ struct GemmArgs {
   int out_f32, accumulate;
 };
 
-// fp32 -> (hi, lo) bf16 pair with hi + lo = v to ~2^-16 relative; products of the
-// pairs are exact in fp32, so hi*hi + hi*lo + lo*hi carries ~fp32 accuracy on MFMA.
-__device__ __forceinline__ void split_bf16(float v, uint32_t& hi, uint32_t& lo) {
-  hi = bf16_rne(v);
-  lo = bf16_rne(v - bf16_to_f32(hi));
+// Eight fp32 values -> hi and lo bf16 MFMA operands, hi = rne(v), lo = rne(v - hi), so
+// hi + lo = v to ~2^-16 relative; products of the pairs are exact in fp32, so
+// hi*hi + hi*lo + lo*hi carries ~fp32 accuracy on the MFMA.
+__device__ __forceinline__ void split8(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    l[i] = pack_bf16x2(v[2 * i] - bf16_to_f32(h[i] & 0xffffu), v[2 * i + 1] - bf16_to_f32(h[i] >> 16));
+  }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 // Launch order -> output tile.  Workgroups are dispatched round-robin over the 8 XCDs
@@ -75,241 +87,313 @@ __device__ __forceinline__ void tile_of(int64_t& n0, int64_t& m0, int& split) {
   m0 = m * BM;
 }
 
+// Keep bits of the 16 accumulator rows a lane holds in one 32x32 block (bit v for
+// register v), for output column n.  Element (m, n) draws word (m*Nc + n) % 4 of the
+// Philox block (m*Nc + n) / 4; since Nc % 4 == 0, the four lanes of a quad (columns
+// 4q..4q+3) share each row's block.  Lane p of the quad draws the blocks of rows
+// 4p..4p+3 of the lane's register layout and the quad swaps results through DPP.
+__device__ __forceinline__ uint32_t keep_rows16(const Dropout& d, int64_t mrow0, int hk, int64_t ncol,
+                                                int64_t Nc, int lane) {
+  const int p = lane & 3;
+  const int64_t nq = ncol & ~(int64_t)3;
+  uint32_t w = 0;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int64_t m = mrow0 + 8 * p + 4 * hk + x;  // register v = 4p + x
+    w |= keep4(d, (uint64_t)m * (uint64_t)Nc + (uint64_t)nq) << (4 * x);
+  }
+  const uint32_t w0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x00, 0xf, 0xf, false);
+  const uint32_t w1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x55, 0xf, 0xf, false);
+  const uint32_t w2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xaa, 0xf, 0xf, false);
+  const uint32_t w3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xff, 0xf, 0xf, false);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    bits |= ((w0 >> (4 * x + p)) & 1u) << x;
+    bits |= ((w1 >> (4 * x + p)) & 1u) << (4 + x);
+    bits |= ((w2 >> (4 * x + p)) & 1u) << (8 + x);
+    bits |= ((w3 >> (4 * x + p)) & 1u) << (12 + x);
+  }
+  return bits;
+}
+
 template <int MODE, bool DROP>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDW];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int hk = lane >> 5, r32 = lane & 31;
   int64_t n0, m0;
   int split;
   tile_of(n0, m0, split);
   const int s_begin = split * g.steps_per_split;
   const int s_end = min(g.steps, s_begin + g.steps_per_split);
+  const int64_t mw = m0 + 64 * wave;  // first row of this wave
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int64_t kw_half = g.K / 2, kw_blk = g.K / 64;
+  if (s_begin < s_end) {
+    // Activation operand, straight from global memory into MFMA registers.  The operand
+    // is packed in fragment order: within a k-step, MFMA sub-step c of lane half hk
+    // reduces over k = 32*hk + 8*c + (0..7), and the 64 lanes' 16-byte pieces of one
+    // (32-row group, k-step, sub-step) are one contiguous 1 KB block, so every load is
+    // fully coalesced.  The W tile is read from LDS in the same k order.  Row groups past
+    // the packed rows are clamped onto the last one: they only feed accumulator rows
+    // that are never stored.
+    const int64_t ngrp = (g.M + 31) / 32;
+    const uint16_t* ap0 = g.act + min(mw / 32, ngrp - 1) * g.steps * 2048 + lane * 8;
+    const uint16_t* ap1 = g.act + min(mw / 32 + 1, ngrp - 1) * g.steps * 2048 + lane * 8;
 
-  // Per-thread share of one k-step's global data, prefetched one step ahead.
-  uint4 ra[4];   // activations: 4 x 8 bf16
-  uint4 rq;      // 32 NF4 codes of one (row, 64-block)
-  float rs;      // that block's absmax
-  // fixed per-thread coordinates
-  const int w_row = MODE == 0 ? (tid >> 1) : (tid >> 2);      // fwd: W row in tile; bwd: reduction row
-  const int w_sub = MODE == 0 ? (tid & 1) : (tid & 3);        // fwd: 32-code half; bwd: 32-col quarter
-  const int64_t w_col = MODE == 0 ? (n0 + w_row) : (n0 + 32 * w_sub);  // fwd: W row; bwd: W column
-  const bool w_ok = w_col < g.Nc;
-
-  auto gload = [&](int step) {
-    const int64_t r0 = (int64_t)step * BK;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + THREADS * c;
-      const int row = idx >> 3, c8 = idx & 7;
-      const int64_t gm = m0 + row;
-      ra[c] = gm < g.M ? *reinterpret_cast<const uint4*>(g.act + gm * g.R + r0 + c8 * 8)
-                       : make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (w_ok) {
-      if (MODE == 0) {
-        rq = *reinterpret_cast<const uint4*>(g.codes + w_col * kw_half + r0 / 2 + w_sub * 16);
-        rs = g.absmax[w_col * kw_blk + r0 / 64];
-      } else {
-        rq = *reinterpret_cast<const uint4*>(g.codes + (r0 + w_row) * kw_half + w_col / 2);
-        rs = g.absmax[(r0 + w_row) * kw_blk + w_col / 64];
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + THREADS * c;
-      const int row = idx >> 3, c8 = idx & 7;
-      *reinterpret_cast<uint4*>(&sA[buf][row * LDW + c8 * 8]) = ra[c];
-    }
-    uint32_t out[16];
-    if (w_ok) {
-      const Nf4Planes P = nf4_planes(g.lut, rs);
-      nf4_dequant32(P, rq, out);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) out[i] = 0u;
-    }
+    // NF4 source of this thread's share of the W tile (clamped like the rows above).
+    //   forward:  W row n0 + (tid >> 1), 32 codes = half (tid & 1) of the step's block
+    //   backward: reduction row `lane` of the step, output columns n0 + 32*wave .. +31
+    const uint8_t* cbase;
+    const float* sbase;
+    int64_t cstride, sstride;
     if (MODE == 0) {
-      uint4* dst = reinterpret_cast<uint4*>(&sB[buf][w_row * LDW + w_sub * 32]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+      const int64_t wn = min(n0 + (tid >> 1), g.Nc - 1);
+      cbase = g.codes + wn * (g.K / 2) + 16 * (tid & 1);
+      sbase = g.absmax + wn * (g.K / 64);
+      cstride = BK / 2;
+      sstride = 1;
     } else {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const uint32_t v = (j & 1) ? (out[j >> 1] >> 16) : (out[j >> 1] & 0xffffu);
-        sB[buf][(32 * w_sub + j) * LDW + w_row] = (uint16_t)v;
-      }
+      const int64_t col = n0 + 32 * wave < g.Nc ? n0 + 32 * wave : 0;
+      cbase = g.codes + (int64_t)lane * (g.K / 2) + col / 2;
+      sbase = g.absmax + (int64_t)lane * (g.K / 64) + col / 64;
+      cstride = (int64_t)BK * (g.K / 2);
+      sstride = (int64_t)BK * (g.K / 64);
     }
-  };
 
-  if (s_begin < s_end) gload(s_begin);
-  for (int step = s_begin; step < s_end; ++step) {
-    const int buf = (step - s_begin) & 1;
-    lstore(buf);
-    __syncthreads();
-    if (step + 1 < s_end) gload(step + 1);
+    uint4 a[2][4];     // activation operand of the current k-step, refilled per sub-step
+    uint4 qa, qb;      // NF4 codes of this thread's share, alternating between k-steps ...
+    float sa, sb;      // ... and their block's absmax
+    auto load_a = [&](int step, int c) {
+      const int64_t o = ((int64_t)step * 4 + c) * 512;
+      a[0][c] = *reinterpret_cast<const uint4*>(ap0 + o);
+      a[1][c] = *reinterpret_cast<const uint4*>(ap1 + o);
+    };
+    auto load_w = [&](uint4& q, float& qs, int step) {
+      q = *reinterpret_cast<const uint4*>(cbase + (int64_t)step * cstride);
+      qs = sbase[(int64_t)step * sstride];
+    };
+    // Eight codes (dword c of this thread's share) -> bf16 into LDS buffer `buf`.
+    auto dequant_store = [&](const Nf4Planes& P, uint32_t w, int c, int buf) {
+      uint32_t out[4];
+      nf4_dequant8(P, w, out);
+      if (MODE == 0) {
+        *reinterpret_cast<uint4*>(&sB[buf][(tid >> 1) * LDW + 32 * (tid & 1) + 8 * c]) =
+            make_uint4(out[0], out[1], out[2], out[3]);
+      } else {
+        // transpose into [output column][reduction row]
+        uint16_t* dst = &sB[buf][(32 * wave + 8 * c) * LDW + lane];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kof = ks * 16 + 8 * (lane >> 5);
-      bf16x8_t af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * LDW + kof]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LDW + kof]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
-  __syncthreads();
-
-  // ---- LoRA term: one extra MFMA k-step per 16 ranks, operands split hi/lo ---------------
-  f32x16_t acc2[2][2];
-  if (DROP) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc2[i][j][v] = 0.0f;
-  }
-  if (split == 0 && g.r > 0) {
-    for (int rc = 0; rc < g.r; rc += 16) {
-      {
-        const int row = tid >> 1, jh = (tid & 1) * 8;
-        const int64_t gm = m0 + row;
-        const int64_t gc = n0 + row;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int j = rc + jh + jj;
-          float a = 0.0f, b = 0.0f;
-          if (j < g.r) {
-            if (gm < g.M) a = g.lscale * g.lu[gm * g.r + j];
-            if (gc < g.Nc) b = (MODE == 0) ? g.lw[gc * g.r + j] : g.lw[(int64_t)j * g.K + gc];
-          }
-          uint32_t hi, lo;
-          split_bf16(a, hi, lo);
-          sA[0][row * LDW + jh + jj] = (uint16_t)hi;
-          sA[0][row * LDW + 16 + jh + jj] = (uint16_t)lo;
-          split_bf16(b, hi, lo);
-          sB[0][row * LDW + jh + jj] = (uint16_t)hi;
-          sB[0][row * LDW + 16 + jh + jj] = (uint16_t)lo;
-        }
+        for (int e = 0; e < 8; ++e) dst[e * LDW] = (uint16_t)((e & 1) ? (out[e >> 1] >> 16) : out[e >> 1]);
       }
-      __syncthreads();
-      const int kof = 8 * (lane >> 5);
-      bf16x8_t ah[2], al[2], bh[2], bl[2];
+    };
+    auto read_b = [&](bf16x8_t(&b)[4], int c, int buf) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][(32 * j + r32) * LDW + 32 * hk + 8 * c]);
+    };
+    auto mfma_sub = [&](const bf16x8_t(&b)[4], int c) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int rw = (wm * 64 + i * 32 + (lane & 31)) * LDW;
-        ah[i] = *reinterpret_cast<const bf16x8_t*>(&sA[0][rw + kof]);
-        al[i] = *reinterpret_cast<const bf16x8_t*>(&sA[0][rw + 16 + kof]);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[i][c]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[j], acc[i][j], 0, 0, 0);
       }
+    };
+    // One k-step in four sub-steps.  Sub-step c multiplies with operand column c,
+    // then refills a[][c] with the next k-step's activations (a full k-step ahead of
+    // their use) and dequantizes dword c of the next k-step's codes (qc, fetched one
+    // k-step earlier) into the other LDS buffer, so one wave's VALU work sits between
+    // its MFMAs.  The codes two k-steps ahead go to the other register set (qn): no
+    // register copies, so no wait on loads issued in this k-step.  The sub-steps are
+    // fenced off from each other for the scheduler; nothing branches (past-the-end
+    // fetches are clamped onto the last step and never read).
+    // The LDS operand of sub-step c+1 is read while sub-step c multiplies.
+    auto kstep = [&](int step, int buf, const uint4& qc, float qsc, uint4& qn, float& qsn) {
+      const int nxt = min(step + 1, s_end - 1);
+      load_w(qn, qsn, min(step + 2, s_end - 1));
+      const uint32_t qw[4] = {qc.x, qc.y, qc.z, qc.w};
+      Nf4Planes P;
+      bf16x8_t b0[4], b1[4];
+      read_b(b0, 0, buf);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int rw = (wn * 64 + j * 32 + (lane & 31)) * LDW;
-        bh[j] = *reinterpret_cast<const bf16x8_t*>(&sB[0][rw + kof]);
-        bl[j] = *reinterpret_cast<const bf16x8_t*>(&sB[0][rw + 16 + kof]);
+      for (int c = 0; c < 4; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (c == 0) P = nf4_planes(g.lut, qsc);
+        if (c < 3) read_b((c & 1) ? b0 : b1, c + 1, buf);
+        mfma_sub((c & 1) ? b1 : b0, c);
+        load_a(nxt, c);
+        dequant_store(P, qw[c], c, buf ^ 1);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          f32x16_t t = DROP ? acc2[i][j] : acc[i][j];
-          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], t, 0, 0, 0);
-          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], t, 0, 0, 0);
-          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], t, 0, 0, 0);
-          if (DROP)
-            acc2[i][j] = t;
-          else
-            acc[i][j] = t;
-        }
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
+    };
+
+    // Prologue.  The loads are issued in the order the loop keeps them in flight (codes
+    // of the next k-step older than the activations), so the wait counts the compiler
+    // derives at the loop head hold on entry as well as on the back edge.
+    load_w(qb, sb, s_begin);
+    load_w(qa, sa, min(s_begin + 1, s_end - 1));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) load_a(s_begin, c);
+    {
+      const Nf4Planes P = nf4_planes(g.lut, sb);
+      const uint32_t qw[4] = {qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dequant_store(P, qw[c], c, 0);
     }
-    if (DROP) {  // masked LoRA input gradient: acc += keep * sigma * acc2
+    __syncthreads();
+    int step = s_begin;
+    for (; step + 1 < s_end; step += 2) {
+      kstep(step, 0, qa, sa, qb, sb);
+      kstep(step + 1, 1, qb, sb, qa, sa);
+    }
+    if (step < s_end) kstep(step, 0, qa, sa, qb, sb);
+  }
+
+  // ---- LoRA term: one extra MFMA k-step per 16 ranks, operands split hi/lo ---------------
+  // Operands come straight from global memory in the MFMA lane layout: lane half hk
+  // holds ranks rc + 8*hk .. +7 of its row (u side) or column (B / A side).
+  if (split == 0 && g.r > 0) {
+    for (int rc = 0; rc < g.r; rc += 16) {
+      bf16x8_t ah[2], al[2], bh[4], bl[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t m = min(mw + 32 * i + r32, g.M - 1);
+        float v[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = rc + 8 * hk + jj;
+          const float x = g.lu[m * g.r + min(j, g.r - 1)];
+          v[jj] = j < g.r ? g.lscale * x : 0.0f;
+        }
+        split8(v, ah[i], al[i]);
+      }
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const int64_t n = min(n0 + 32 * jn + r32, g.Nc - 1);
+        float v[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = rc + 8 * hk + jj;
+          const int jc = min(j, g.r - 1);
+          const float x = (MODE == 0) ? g.lw[n * g.r + jc] : g.lw[(int64_t)jc * g.K + n];
+          v[jj] = j < g.r ? x : 0.0f;
+        }
+        split8(v, bh[jn], bl[jn]);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        for (int jn = 0; jn < 4; ++jn) {
+          if (!DROP) {
+            f32x16_t t = acc[i][jn];
+            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[jn], t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[jn], t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[jn], t, 0, 0, 0);
+            acc[i][jn] = t;
+          } else {
+            // masked LoRA input gradient: acc += keep * sigma * (du . A)
+            f32x16_t t;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (m < g.M && n < g.Nc) {
-              const uint64_t e = (uint64_t)m * (uint64_t)g.Nc + (uint64_t)n;
-              const uint32_t keep = (keep4(g.drop, e & ~(uint64_t)3) >> (e & 3)) & 1u;
-              if (keep) acc[i][j][v] += g.drop.sigma * acc2[i][j][v];
-            }
+            for (int v = 0; v < 16; ++v) t[v] = 0.0f;
+            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[jn], t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[jn], t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[jn], t, 0, 0, 0);
+            const uint32_t keep = keep_rows16(g.drop, mw + 32 * i, hk, n0 + 32 * jn + r32, g.Nc, lane);
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if ((keep >> v) & 1u) acc[i][jn][v] += g.drop.sigma * t[v];
           }
         }
     }
   }
 
   // ---- output ---------------------------------------------------------------------------
+  // One 32x32 block at a time (fenced for the scheduler so the accumulators are not all
+  // copied out at once); the in-range test is skipped for blocks wholly inside [M, Nc).
+  const bool rows_in = mw + 64 <= g.M;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
-      if (n >= g.Nc) continue;
-      const float bn = (MODE == 0 && g.splits == 1 && g.bias) ? bf16_to_f32(g.bias[n]) : 0.0f;
+    for (int jn = 0; jn < 4; ++jn) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int64_t n = n0 + 32 * jn + r32;
+      const bool all_in = rows_in && n0 + 32 * jn + 32 <= g.Nc;
+      if (!all_in && n >= g.Nc) continue;
+      const int64_t mb = mw + 32 * i + 4 * hk;
+      if (g.splits > 1) {
+        float* po = reinterpret_cast<float*>(g.out) + ((int64_t)split * g.M) * g.Nc + n;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m >= g.M) continue;
-        float val = acc[i][j][v];
-        if (g.splits > 1) {
-          reinterpret_cast<float*>(g.out)[((int64_t)split * g.M + m) * g.Nc + n] = val;
-          continue;
+        for (int v = 0; v < 16; ++v) {
+          const int64_t m = mb + 8 * (v >> 2) + (v & 3);
+          if (all_in || m < g.M) po[m * g.Nc] = acc[i][jn][v];
         }
-        const int64_t o = m * g.Nc + n;
-        if (MODE == 0) val += bn;
-        if (g.out_f32) {
-          float* po = reinterpret_cast<float*>(g.out);
-          po[o] = (MODE == 1 && g.accumulate) ? po[o] + val : val;
-        } else {
-          uint16_t* po = reinterpret_cast<uint16_t*>(g.out);
-          if (MODE == 1 && g.accumulate) val = bf16_to_f32(po[o]) + val;
-          po[o] = (uint16_t)bf16_rne(val);
+        continue;
+      }
+      const float bn = (MODE == 0 && g.bias) ? bf16_to_f32(g.bias[n]) : 0.0f;
+      if (g.out_f32) {
+        float* po = reinterpret_cast<float*>(g.out) + n;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t m = mb + 8 * (v >> 2) + (v & 3);
+          if (!(all_in || m < g.M)) continue;
+          const float val = acc[i][jn][v] + bn;
+          po[m * g.Nc] = (MODE == 1 && g.accumulate) ? po[m * g.Nc] + val : val;
+        }
+      } else {
+        uint16_t* po = reinterpret_cast<uint16_t*>(g.out) + n;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t m = mb + 8 * (v >> 2) + (v & 3);
+          if (!(all_in || m < g.M)) continue;
+          float val = acc[i][jn][v] + bn;
+          if (MODE == 1 && g.accumulate) val = bf16_to_f32(po[m * g.Nc]) + val;
+          po[m * g.Nc] = (uint16_t)bf16_rne(val);
         }
       }
     }
 }
 
-__global__ __launch_bounds__(THREADS) void nf4_fwd_gemm(GemmArgs g) { gemm_body<0, false>(g); }
-__global__ __launch_bounds__(THREADS) void nf4_bwd_gemm(GemmArgs g) { gemm_body<1, false>(g); }
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nf4_fwd_gemm(GemmArgs g) { gemm_body<0, false>(g); }
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nf4_bwd_gemm(GemmArgs g) { gemm_body<1, false>(g); }
 __global__ __launch_bounds__(THREADS) void nf4_bwd_gemm_dropout(GemmArgs g) { gemm_body<1, true>(g); }
 
 }  // namespace
 
+// Split of the reduction dimension.  Cost model per candidate split S: a k-step of one
+// workgroup keeps its CU's matrix cores busy for ~0.5 us (32 MFMAs per SIMD), the
+// workgroups spread evenly over the 256 CUs, and every extra split writes and re-reads
+// an fp32 partial tile (~4 TB/s).  The cheapest S wins; S = 1 on ties.
 GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red) {
   GemmPlan p;
   p.steps = (int)(red / BK);
   const int64_t tiles = ((m + BM - 1) / BM) * ((nc + BN - 1) / BN);
-  int s = 1;
-  while (tiles * s < 512 && (int64_t)p.steps >= 8 * s) s *= 2;
-  p.splits = s;
-  p.steps_per_split = (p.steps + s - 1) / s;
+  double best = 0.0;
+  int best_s = 1;
+  for (int s = 1; s <= 32 && s <= p.steps; ++s) {
+    const int64_t per = (p.steps + s - 1) / s;
+    if (s > 1 && (per < 4 || (int64_t)(s - 1) * per >= p.steps)) continue;  // no empty or tiny splits
+    const double per_cu = (double)((tiles * s + 255) / 256);
+    const double t = per_cu * (double)per * 0.5 + (s > 1 ? (double)s * (double)m * (double)nc * 8.0 / 4e6 : 0.0);
+    if (s == 1 || t < best) {
+      best = t;
+      best_s = s;
+    }
+  }
+  p.splits = best_s;
+  p.steps_per_split = (p.steps + best_s - 1) / best_s;
   return p;
 }
 
@@ -336,6 +420,8 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   g.out = L.out;
   g.out_f32 = L.out_f32;
   g.accumulate = L.accumulate;
+  // The kernel clamps rows and columns onto [0, M) x [0, Nc) and reads whole k-steps.
+  if (g.M < 1 || g.Nc < 1 || g.R % BK || g.K % 64 || g.steps != (int)(g.R / BK)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)g.splits);
   const double flops = 2.0 * (double)g.M * (double)g.N * (double)g.K;
   int rec;

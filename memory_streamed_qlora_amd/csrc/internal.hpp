@@ -18,7 +18,7 @@ const Nf4Lut& nf4_lut();
 const Nf4Mid& nf4_mid();
 
 // ---- workspace planning ----------------------------------------------------
-constexpr int GEMM_BM = 128;
+constexpr int GEMM_BM = 256;
 constexpr int GEMM_BN = 128;
 constexpr int GEMM_BK = 64;
 constexpr int COLGRAD_TCHUNK = 32;
@@ -52,7 +52,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 // carrying the LoRA term) and launch_split_reduce finishes the output.
 struct GemmLaunch {
   int mode;
-  const uint16_t* act;
+  const uint16_t* act;  // packed by launch_pack_frag
   const uint8_t* codes;
   const float* absmax;
   int64_t M, N, K;
@@ -90,8 +90,13 @@ hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, f
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
                                const uint16_t* bias, void* out, bool out_f32, int accumulate,
                                hipStream_t s);
-// out[i] = bf16_rne(in[i]) for n elements (n % 8 == 0)
-hipError_t launch_cvt_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s);
+// Activation operand [M][R] (bf16, or fp32 rounded to bf16) in MFMA-fragment order: block
+// (g, s, c) of 512 bf16 holds, for lane l = 0..63, the 8 values of row 32*g + (l & 31) at
+// reduction index 64*s + 32*(l >> 5) + 8*c + (0..7).  Blocks are ordered g, then s, then c,
+// so the GEMM loads each 32-row operand fragment as one contiguous 1 KB piece.  Rows are
+// padded with zeros up to a multiple of 32; R % 64 == 0.  `out` holds frag_rows(M) * R bf16.
+inline int64_t frag_rows(int64_t M) { return (M + 31) / 32 * 32; }
+hipError_t launch_pack_frag(const void* in, bool in_f32, int64_t M, int64_t R, uint16_t* out, hipStream_t s);
 
 // ---- timing -------------------------------------------------------------------
 bool timing_on();

@@ -238,15 +238,25 @@ __global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ pa
 }
 
 // Round fp32 activations to bf16 (RNE) for the MFMA operand; 8 per thread.
-__global__ __launch_bounds__(256) void cvt_f32_bf16(const float* __restrict__ in, int64_t n8,
-                                                    uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  float f[8];
-  load8(in + 8 * i, f);
-  *reinterpret_cast<uint4*>(out + 8 * i) =
-      make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
-                 bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
+// Activation operand of the fused GEMM in MFMA-fragment order (see launch_pack_frag).
+// One workgroup packs one block of 32 rows x 64 reduction columns: thread t reads
+// 8 consecutive elements (row t >> 3, chunk t & 7) with coalesced loads and stores them
+// as lane (row + 32 * (chunk >> 2)) of sub-step (chunk & 3).
+template <typename TIN>
+__global__ __launch_bounds__(256) void pack_frag(const TIN* __restrict__ in, int64_t M, int64_t R, int steps,
+                                                 uint16_t* __restrict__ out) {
+  const int grp = blockIdx.y, step = blockIdx.x;
+  const int t = threadIdx.x, row = t >> 3, chunk = t & 7;
+  const int64_t m = (int64_t)grp * 32 + row;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (m < M) {
+    float f[8];
+    load8(in + m * R + (int64_t)step * 64 + chunk * 8, f);
+    v = make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
+                   bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
+  }
+  const int lane = row + 32 * (chunk >> 2), c = chunk & 3;
+  *reinterpret_cast<uint4*>(out + (((int64_t)grp * steps + step) * 4 + c) * 512 + lane * 8) = v;
 }
 
 template <typename TIN, int MAT_KIND>
@@ -317,10 +327,14 @@ hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_cvt_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  const int64_t n8 = n / 8;
-  hipLaunchKernelGGL(cvt_f32_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, in, n8, out);
+hipError_t launch_pack_frag(const void* in, bool in_f32, int64_t M, int64_t R, uint16_t* out, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int steps = (int)(R / 64);
+  const dim3 grid((unsigned)steps, (unsigned)((M + 31) / 32));
+  if (in_f32)
+    hipLaunchKernelGGL(pack_frag<float>, grid, dim3(256), 0, s, (const float*)in, M, R, steps, out);
+  else
+    hipLaunchKernelGGL(pack_frag<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)in, M, R, steps, out);
   return hipGetLastError();
 }
 
