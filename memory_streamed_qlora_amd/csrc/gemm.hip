@@ -9,12 +9,12 @@
 // accumulation.  The pages' base is frozen (never differentiated: "Poros" research
 // post, training-step paragraph), so there is no dW kernel.
 //
-// Tile: BM=256 rows of t x BN=128 output columns x BK=64 reduction, 256 threads = 4
+// Tile: BM=512 rows of t x BN=128 output columns x BK=64 reduction, 512 threads = 8
 // waves; wave w owns rows 64w..64w+63 and all 128 columns (2x4 MFMA 32x32 blocks).
 // The activation operand comes straight from global memory into registers, packed in
 // MFMA-fragment order beforehand (launch_pack_frag) so that each load is one contiguous
-// 1 KB block; only the dequantized W tile goes through LDS (double-buffered, one
-// barrier per k-step), and each dequantized element feeds 256 rows.  Within a k-step,
+// 1 KB block; only the dequantized W tile goes through LDS (three buffers, one
+// barrier per k-step), and each dequantized element feeds all 512 rows.  Within a k-step,
 // the dequantization of the next tile is interleaved with the MFMAs of this one.
 // The rank-r LoRA term of the same output tile is one more MFMA k-step per 16 ranks
 // (operands split into bf16 hi/lo pairs for ~fp32 accuracy); in the backward the
@@ -31,8 +31,8 @@ namespace {
 constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
 constexpr int PAD = 8;              // bf16 elements of row padding in LDS
 constexpr int LDW = BK + PAD;       // LDS row pitch in bf16 elements (144 bytes)
-static_assert(BM == 256 && BN == 128 && BK == 64, "the thread mappings below assume this tile");
-constexpr int THREADS = 256;
+static_assert(BM == 512 && BN == 128 && BK == 64, "the thread mappings below assume this tile");
+constexpr int THREADS = 512;  // 8 waves, one per 64 rows
 
 struct GemmArgs {
   const uint16_t* act;   // [M][R] bf16
@@ -119,7 +119,7 @@ __device__ __forceinline__ uint32_t keep_rows16(const Dropout& d, int64_t mrow0,
 
 template <int MODE, bool DROP>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDW];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[3][BN * LDW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,20 +152,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const uint16_t* ap0 = g.act + min(mw / 32, ngrp - 1) * g.steps * 2048 + lane * 8;
     const uint16_t* ap1 = g.act + min(mw / 32 + 1, ngrp - 1) * g.steps * 2048 + lane * 8;
 
-    // NF4 source of this thread's share of the W tile (clamped like the rows above).
-    //   forward:  W row n0 + (tid >> 1), 32 codes = half (tid & 1) of the step's block
-    //   backward: reduction row `lane` of the step, output columns n0 + 32*wave .. +31
+    // NF4 source of this thread's share of the W tile (clamped like the rows above):
+    // 16 codes, one 8-byte load per k-step.
+    //   forward:  W row n0 + (tid >> 2), codes 16*(tid & 3) .. +15 of the step's block
+    //   backward: reduction row `lane` of the step, output columns n0 + 16*wave .. +15
     const uint8_t* cbase;
     const float* sbase;
     int64_t cstride, sstride;
     if (MODE == 0) {
-      const int64_t wn = min(n0 + (tid >> 1), g.Nc - 1);
-      cbase = g.codes + wn * (g.K / 2) + 16 * (tid & 1);
+      const int64_t wn = min(n0 + (tid >> 2), g.Nc - 1);
+      cbase = g.codes + wn * (g.K / 2) + 8 * (tid & 3);
       sbase = g.absmax + wn * (g.K / 64);
       cstride = BK / 2;
       sstride = 1;
     } else {
-      const int64_t col = n0 + 32 * wave < g.Nc ? n0 + 32 * wave : 0;
+      const int64_t col = n0 + 16 * wave < g.Nc ? n0 + 16 * wave : 0;
       cbase = g.codes + (int64_t)lane * (g.K / 2) + col / 2;
       sbase = g.absmax + (int64_t)lane * (g.K / 64) + col / 64;
       cstride = (int64_t)BK * (g.K / 2);
@@ -173,27 +174,27 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
 
     uint4 a[2][4];     // activation operand of the current k-step, refilled per sub-step
-    uint4 qa, qb;      // NF4 codes of this thread's share, alternating between k-steps ...
+    uint2 qa, qb;      // NF4 codes of this thread's share, alternating between k-steps ...
     float sa, sb;      // ... and their block's absmax
     auto load_a = [&](int step, int c) {
       const int64_t o = ((int64_t)step * 4 + c) * 512;
       a[0][c] = *reinterpret_cast<const uint4*>(ap0 + o);
       a[1][c] = *reinterpret_cast<const uint4*>(ap1 + o);
     };
-    auto load_w = [&](uint4& q, float& qs, int step) {
-      q = *reinterpret_cast<const uint4*>(cbase + (int64_t)step * cstride);
+    auto load_w = [&](uint2& q, float& qs, int step) {
+      q = *reinterpret_cast<const uint2*>(cbase + (int64_t)step * cstride);
       qs = sbase[(int64_t)step * sstride];
     };
-    // Eight codes (dword c of this thread's share) -> bf16 into LDS buffer `buf`.
-    auto dequant_store = [&](const Nf4Planes& P, uint32_t w, int c, int buf) {
+    // Eight codes (dword h of this thread's share) -> bf16 into LDS buffer `buf`.
+    auto dequant_store = [&](const Nf4Planes& P, uint32_t w, int h, int buf) {
       uint32_t out[4];
       nf4_dequant8(P, w, out);
       if (MODE == 0) {
-        *reinterpret_cast<uint4*>(&sB[buf][(tid >> 1) * LDW + 32 * (tid & 1) + 8 * c]) =
+        *reinterpret_cast<uint4*>(&sB[buf][(tid >> 2) * LDW + 16 * (tid & 3) + 8 * h]) =
             make_uint4(out[0], out[1], out[2], out[3]);
       } else {
         // transpose into [output column][reduction row]
-        uint16_t* dst = &sB[buf][(32 * wave + 8 * c) * LDW + lane];
+        uint16_t* dst = &sB[buf][(16 * wave + 8 * h) * LDW + lane];
 #pragma unroll
         for (int e = 0; e < 8; ++e) dst[e * LDW] = (uint16_t)((e & 1) ? (out[e >> 1] >> 16) : out[e >> 1]);
       }
@@ -211,55 +212,70 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[j], acc[i][j], 0, 0, 0);
       }
     };
-    // One k-step in four sub-steps.  Sub-step c multiplies with operand column c,
+    // One k-step in four sub-steps.  The dequantized W tiles rotate through three LDS
+    // buffers: k-step s multiplies on tile s while dequantizing tile s+2 (codes fetched
+    // one k-step earlier) into the buffer tile s-1 has left, so tile s+1 is complete a
+    // whole k-step before it is needed.  Sub-step c multiplies with operand column c
+    // while the LDS operand of sub-step c+1 is read (for c = 3: sub-step 0 of tile s+1),
     // then refills a[][c] with the next k-step's activations (a full k-step ahead of
-    // their use) and dequantizes dword c of the next k-step's codes (qc, fetched one
-    // k-step earlier) into the other LDS buffer, so one wave's VALU work sits between
-    // its MFMAs.  The codes two k-steps ahead go to the other register set (qn): no
-    // register copies, so no wait on loads issued in this k-step.  The sub-steps are
+    // their use); sub-step 0 builds tile s+2's lookup table and sub-steps 1 and 2
+    // dequantize its codes, so one wave's VALU work sits between its MFMAs.  The codes of tile s+3 go to the other register set (qn):
+    // no register copies, so no wait on loads issued in this k-step.  Sub-steps are
     // fenced off from each other for the scheduler; nothing branches (past-the-end
     // fetches are clamped onto the last step and never read).
-    // The LDS operand of sub-step c+1 is read while sub-step c multiplies.
-    auto kstep = [&](int step, int buf, const uint4& qc, float qsc, uint4& qn, float& qsn) {
+    bf16x8_t b0[4];
+    int cur = 0;  // LDS buffer of the current tile
+    auto kstep = [&](int step, const uint2& qc, float qsc, uint2& qn, float& qsn) {
       const int nxt = min(step + 1, s_end - 1);
-      load_w(qn, qsn, min(step + 2, s_end - 1));
-      const uint32_t qw[4] = {qc.x, qc.y, qc.z, qc.w};
+      const int b_next = cur == 2 ? 0 : cur + 1, b_fill = b_next == 2 ? 0 : b_next + 1;
+      load_w(qn, qsn, min(step + 3, s_end - 1));
       Nf4Planes P;
-      bf16x8_t b0[4], b1[4];
-      read_b(b0, 0, buf);
+      bf16x8_t b1[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         __builtin_amdgcn_sched_barrier(0);
         if (c == 0) P = nf4_planes(g.lut, qsc);
-        if (c < 3) read_b((c & 1) ? b0 : b1, c + 1, buf);
+        if (c < 3)
+          read_b((c & 1) ? b0 : b1, c + 1, cur);
+        else
+          read_b(b0, 0, b_next);  // tile s+1 is complete: its first operands load under these MFMAs
         mfma_sub((c & 1) ? b1 : b0, c);
         load_a(nxt, c);
-        dequant_store(P, qw[c], c, buf ^ 1);
+        if (c == 1) dequant_store(P, qc.x, 0, b_fill);
+        if (c == 2) dequant_store(P, qc.y, 1, b_fill);
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
+      cur = b_next;
     };
 
-    // Prologue.  The loads are issued in the order the loop keeps them in flight (codes
-    // of the next k-step older than the activations), so the wait counts the compiler
-    // derives at the loop head hold on entry as well as on the back edge.
-    load_w(qb, sb, s_begin);
-    load_w(qa, sa, min(s_begin + 1, s_end - 1));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) load_a(s_begin, c);
+    // Prologue: tiles s_begin and s_begin+1 into buffers 0 and 1; the codes of tile
+    // s_begin+2 are fetched before the activations, the order the loop keeps them in
+    // flight, so the wait counts the compiler derives at the loop head hold on entry
+    // as well as on the back edge.
     {
-      const Nf4Planes P = nf4_planes(g.lut, sb);
-      const uint32_t qw[4] = {qb.x, qb.y, qb.z, qb.w};
+      uint2 t0, t1;
+      float ts0, ts1;
+      load_w(t0, ts0, s_begin);
+      load_w(t1, ts1, min(s_begin + 1, s_end - 1));
+      load_w(qa, sa, min(s_begin + 2, s_end - 1));
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dequant_store(P, qw[c], c, 0);
+      for (int c = 0; c < 4; ++c) load_a(s_begin, c);
+      const Nf4Planes P0 = nf4_planes(g.lut, ts0);
+      dequant_store(P0, t0.x, 0, 0);
+      dequant_store(P0, t0.y, 1, 0);
+      const Nf4Planes P1 = nf4_planes(g.lut, ts1);
+      dequant_store(P1, t1.x, 0, 1);
+      dequant_store(P1, t1.y, 1, 1);
     }
     __syncthreads();
+    read_b(b0, 0, 0);
     int step = s_begin;
     for (; step + 1 < s_end; step += 2) {
-      kstep(step, 0, qa, sa, qb, sb);
-      kstep(step + 1, 1, qb, sb, qa, sa);
+      kstep(step, qa, sa, qb, sb);
+      kstep(step + 1, qb, sb, qa, sa);
     }
-    if (step < s_end) kstep(step, 0, qa, sa, qb, sb);
+    if (step < s_end) kstep(step, qa, sa, qb, sb);
   }
 
   // ---- LoRA term: one extra MFMA k-step per 16 ranks, operands split hi/lo ---------------
@@ -368,12 +384,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nf4_fwd_gemm(GemmArgs g) { gemm_body<0, false>(g); }
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nf4_bwd_gemm(GemmArgs g) { gemm_body<1, false>(g); }
-__global__ __launch_bounds__(THREADS) void nf4_bwd_gemm_dropout(GemmArgs g) { gemm_body<1, true>(g); }
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nf4_bwd_gemm_dropout(GemmArgs g) { gemm_body<1, true>(g); }
 
 }  // namespace
 
 // Split of the reduction dimension.  Cost model per candidate split S: a k-step of one
-// workgroup keeps its CU's matrix cores busy for ~0.5 us (32 MFMAs per SIMD), the
+// workgroup keeps its CU's matrix cores busy for ~1 us (64 MFMAs per SIMD), the
 // workgroups spread evenly over the 256 CUs, and every extra split writes and re-reads
 // an fp32 partial tile (~4 TB/s).  The cheapest S wins; S = 1 on ties.
 GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red) {
@@ -386,7 +402,7 @@ GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red) {
     const int64_t per = (p.steps + s - 1) / s;
     if (s > 1 && (per < 4 || (int64_t)(s - 1) * per >= p.steps)) continue;  // no empty or tiny splits
     const double per_cu = (double)((tiles * s + 255) / 256);
-    const double t = per_cu * (double)per * 0.5 + (s > 1 ? (double)s * (double)m * (double)nc * 8.0 / 4e6 : 0.0);
+    const double t = per_cu * (double)per * 1.0 + (s > 1 ? (double)s * (double)m * (double)nc * 8.0 / 4e6 : 0.0);
     if (s == 1 || t < best) {
       best = t;
       best_s = s;

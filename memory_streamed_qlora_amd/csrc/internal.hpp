@@ -18,7 +18,7 @@ const Nf4Lut& nf4_lut();
 const Nf4Mid& nf4_mid();
 
 // ---- workspace planning ----------------------------------------------------
-constexpr int GEMM_BM = 256;
+constexpr int GEMM_BM = 512;
 constexpr int GEMM_BN = 128;
 constexpr int GEMM_BK = 64;
 constexpr int COLGRAD_TCHUNK = 32;
