@@ -132,6 +132,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const int s_end = min(g.steps, s_begin + g.steps_per_split);
   const int64_t mw = m0 + 64 * wave;  // first row of this wave
 
+  // An asm operand in an AGPR lets the compiler place the MFMA accumulators in AGPRs
+  // (128 AGPR + 128 VGPR at two waves per SIMD), which keeps the accumulator traffic of
+  // every MFMA off the VGPR file that the dequantization and the loads use.  The
+  // dropout variant needs more VGPRs in its epilogue and keeps them in VGPRs.
+  if constexpr (!DROP) asm volatile("; mfma accumulators in AGPRs" ::"a"(0.0f));
   f32x16_t acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -204,13 +209,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       for (int j = 0; j < 4; ++j)
         b[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][(32 * j + r32) * LDW + 32 * hk + 8 * c]);
     };
+    // Column-major MFMA order: operand b[j] is dead after its second MFMA, so the LDS
+    // read that refills it for the next sub-step can be issued six MFMAs before use.
     auto mfma_sub = [&](const bf16x8_t(&b)[4], int c) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[i][c]);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[j], acc[i][j], 0, 0, 0);
-      }
+        for (int i = 0; i < 2; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i][c]), b[j], acc[i][j],
+                                                              0, 0, 0);
     };
     // One k-step in four sub-steps.  The dequantized W tiles rotate through three LDS
     // buffers: k-step s multiplies on tile s while dequantizing tile s+2 (codes fetched
