@@ -23,6 +23,8 @@
 // split over gridDim.z, in which case split 0 carries the LoRA term and fp32 partial
 // tiles go to a workspace summed in split order by a separate kernel, so results never
 // depend on timing.
+#include <hip/hip_ext.h>
+
 #include "internal.hpp"
 
 namespace msq {
@@ -447,20 +449,25 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   if (g.M < 1 || g.Nc < 1 || g.R % BK || g.K % 64 || g.steps != (int)(g.R / BK)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)g.splits);
   const double flops = 2.0 * (double)g.M * (double)g.N * (double)g.K;
-  int rec;
+  void (*kern)(GemmArgs);
+  const char* name;
   if (L.mode == 0) {
-    rec = timing_begin("nf4_fwd_gemm", flops, s);
-    hipLaunchKernelGGL(nf4_fwd_gemm, grid, dim3(THREADS), 0, s, g);
+    kern = nf4_fwd_gemm;
+    name = "nf4_fwd_gemm";
   } else if (L.r > 0 && L.drop.threshold != 0u) {
-    rec = timing_begin("nf4_bwd_gemm", flops, s);
-    hipLaunchKernelGGL(nf4_bwd_gemm_dropout, grid, dim3(THREADS), 0, s, g);
+    kern = nf4_bwd_gemm_dropout;
+    name = "nf4_bwd_gemm";
   } else {
-    rec = timing_begin("nf4_bwd_gemm", flops, s);
-    hipLaunchKernelGGL(nf4_bwd_gemm, grid, dim3(THREADS), 0, s, g);
+    kern = nf4_bwd_gemm;
+    name = "nf4_bwd_gemm";
   }
-  const hipError_t e = hipGetLastError();
-  timing_end(rec, s);
-  return e;
+  hipEvent_t e0, e1;
+  timing_begin(name, flops, &e0, &e1);
+  if (e0)
+    hipExtLaunchKernelGGL(kern, grid, dim3(THREADS), 0, s, e0, e1, 0, g);
+  else
+    hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, s, g);
+  return hipGetLastError();
 }
 
 }  // namespace msq

@@ -100,8 +100,8 @@ hipError_t launch_pack_frag(const void* in, bool in_f32, int64_t M, int64_t R, u
 
 // ---- timing -------------------------------------------------------------------
 bool timing_on();
-// Returns a record id (or -1 when timing is off) to pass to timing_end.
-int timing_begin(const char* name, double flops, hipStream_t s);
-void timing_end(int id, hipStream_t s);
+// When timing is on, returns a record id and the two events the launch must record
+// (hipExtLaunchKernelGGL start/stop); otherwise -1 and null events.
+int timing_begin(const char* name, double flops, hipEvent_t* start, hipEvent_t* stop);
 
 }  // namespace msq

@@ -1,6 +1,8 @@
 // Launch timing of the dense dequant-MFMA kernels with HIP events on the launch
-// stream.  Off by default; when on, every launch is bracketed by two events and
-// msq_timing_collect aggregates elapsed time and algorithmic flops per kernel name.
+// stream.  Off by default; when on, every launch carries a start and a stop event that
+// the dispatch itself records (hipExtLaunchKernelGGL), so the elapsed time is the
+// kernel's own, and msq_timing_collect aggregates it with the algorithmic flops per
+// kernel name.
 #include <string.h>
 
 #include <mutex>
@@ -31,8 +33,10 @@ hipEvent_t take_event() {
     g_pool.pop_back();
     return e;
   }
+  // No system-scope fence when the event is recorded: a timing event only needs the
+  // timestamp, and the fence (cache writeback) would be counted in the kernel's time.
   hipEvent_t e = nullptr;
-  const hipError_t err = hipEventCreate(&e);
+  const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
   if (err != hipSuccess && g_err == hipSuccess) g_err = err;
   return err == hipSuccess ? e : nullptr;
 }
@@ -41,7 +45,8 @@ hipEvent_t take_event() {
 
 bool timing_on() { return g_on; }
 
-int timing_begin(const char* name, double flops, hipStream_t s) {
+int timing_begin(const char* name, double flops, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
   if (!g_on) return -1;
   std::lock_guard<std::mutex> lk(g_mu);
   Rec r{name, flops, take_event(), take_event()};
@@ -50,15 +55,10 @@ int timing_begin(const char* name, double flops, hipStream_t s) {
     if (r.b) g_pool.push_back(r.b);
     return -1;
   }
-  (void)hipEventRecord(r.a, s);
   g_recs.push_back(r);
+  *start = r.a;
+  *stop = r.b;
   return (int)g_recs.size() - 1;
-}
-
-void timing_end(int id, hipStream_t s) {
-  if (id < 0) return;
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (id < (int)g_recs.size()) (void)hipEventRecord(g_recs[id].b, s);
 }
 
 }  // namespace msq
