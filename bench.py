@@ -56,6 +56,33 @@ def measured_traffic(kernel: str):
     return None
 
 
+PROJ_NAMES = {(5120, 5120): "q/o", (1024, 5120): "k/v", (27648, 5120): "gate/up", (5120, 27648): "down"}
+
+
+def by_kernel(kt: dict) -> dict:
+    """Aggregate the per-label timing ("<kernel> <t>x<n>x<k>") per kernel."""
+    agg = {}
+    for label, v in kt.items():
+        a = agg.setdefault(label.split(" ")[0], {"launches": 0, "total_ms": 0.0, "total_flops": 0.0})
+        for f in a:
+            a[f] += v[f]
+    return agg
+
+
+def gemm_shapes(kt: dict, steps: int) -> list:
+    """MFMA utilisation of every projection shape and direction in the timed region."""
+    out = []
+    for label, v in sorted(kt.items()):
+        kern, shape = label.split(" ")
+        t, n, k = (int(x) for x in shape.split("x"))
+        tf = v["total_flops"] / (v["total_ms"] * 1e-3) / 1e12
+        out.append({"kernel": kern, "projection": PROJ_NAMES.get((n, k), f"{n}x{k}"), "t": t, "n": n, "k": k,
+                    "launches_per_step": v["launches"] / steps,
+                    "avg_us": round(v["total_ms"] / v["launches"] * 1e3, 1),
+                    "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+    return out
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -247,7 +274,8 @@ def main() -> int:
     ms = streamed["seconds"] / args.steps * 1e3
     value = T * args.steps / streamed["seconds"]
     # roofline: the dense dequant-MFMA kernel with the most time in the timed region
-    kt = streamed["kernels"]
+    shapes = gemm_shapes(streamed["kernels"], args.steps)
+    kt = by_kernel(streamed["kernels"])
     name = max(kt, key=lambda k: kt[k]["total_ms"])
     k = kt[name]
     avg_ms = k["total_ms"] / k["launches"]
@@ -287,6 +315,7 @@ def main() -> int:
                 "windows_copied_per_step": streamed["window"]["windows_copied"] if streamed["window"] else 0,
                 "windows_reused_per_step": streamed["window"]["windows_reused"] if streamed["window"] else 0},
         "kernels": kernels,
+        "gemm_shapes": shapes,
         "peak_vram_gb": round(streamed["peak_alloc_gb"], 2),
         "baseline_context": {"value": round(T / PAGES_A100_S_PER_STEP, 1), "unit": "tokens/s",
                              "hardware": "NVIDIA A100 80GB PCIe", "s_per_step": PAGES_A100_S_PER_STEP},

@@ -226,11 +226,12 @@ int block_stream_stats(const msq_window* w, msq_window_stats* out);
 int block_stream_destroy(msq_window* w);
 
 /* ------------------------------------------------------------------------- */
-/* Kernel timing (measurement support).  When enabled, the library brackets
- * each launch of its dense dequant-MFMA kernels with HIP events on the launch
- * stream.  msq_timing_collect waits for the recorded events and aggregates, per
- * kernel name, the launch count, total milliseconds and total algorithmic
- * flops (2*t*k*n per launch).  Host-side bookkeeping only. */
+/* Kernel timing (measurement support).  When enabled, every launch of the dense
+ * dequant-MFMA kernels carries a start and a stop HIP event recorded by the dispatch
+ * on the launch stream.  msq_timing_collect waits for the recorded events and
+ * aggregates, per label "<kernel> <t>x<n>x<k>" (kernel name and projection shape),
+ * the launch count, total milliseconds and total algorithmic flops (2*t*k*n per
+ * launch).  Host-side bookkeeping only. */
 typedef struct {
   char name[48];
   uint64_t launches;

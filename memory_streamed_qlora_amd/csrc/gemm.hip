@@ -24,6 +24,7 @@
 // tiles go to a workspace summed in split order by a separate kernel, so results never
 // depend on timing.
 #include <hip/hip_ext.h>
+#include <stdio.h>
 
 #include "internal.hpp"
 
@@ -461,8 +462,12 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
     kern = nf4_bwd_gemm;
     name = "nf4_bwd_gemm";
   }
-  hipEvent_t e0, e1;
-  timing_begin(name, flops, &e0, &e1);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timing_on()) {
+    char label[48];  // kernel and projection shape: "<kernel> <t>x<n>x<k>"
+    snprintf(label, sizeof(label), "%s %lldx%lldx%lld", name, (long long)L.M, (long long)L.N, (long long)L.K);
+    timing_begin(label, flops, &e0, &e1);
+  }
   if (e0)
     hipExtLaunchKernelGGL(kern, grid, dim3(THREADS), 0, s, e0, e1, 0, g);
   else

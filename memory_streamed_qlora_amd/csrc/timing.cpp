@@ -3,6 +3,7 @@
 // the dispatch itself records (hipExtLaunchKernelGGL), so the elapsed time is the
 // kernel's own, and msq_timing_collect aggregates it with the algorithmic flops per
 // kernel name.
+#include <stdio.h>
 #include <string.h>
 
 #include <mutex>
@@ -16,7 +17,7 @@ namespace msq {
 namespace {
 
 struct Rec {
-  const char* name;
+  char name[48];
   double flops;
   hipEvent_t a, b;
 };
@@ -49,7 +50,11 @@ int timing_begin(const char* name, double flops, hipEvent_t* start, hipEvent_t* 
   *start = *stop = nullptr;
   if (!g_on) return -1;
   std::lock_guard<std::mutex> lk(g_mu);
-  Rec r{name, flops, take_event(), take_event()};
+  Rec r;
+  snprintf(r.name, sizeof(r.name), "%s", name);
+  r.flops = flops;
+  r.a = take_event();
+  r.b = take_event();
   if (!r.a || !r.b) {
     if (r.a) g_pool.push_back(r.a);
     if (r.b) g_pool.push_back(r.b);

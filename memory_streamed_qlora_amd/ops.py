@@ -296,11 +296,13 @@ def timing_enable(on: bool = True) -> None:
 
 
 def timing_collect() -> dict:
-    arr = (_abi.KernelTiming * 16)()
+    """Per label "<kernel> <t>x<n>x<k>": launches, total_ms, total_flops (then reset)."""
+    cap = 256
+    arr = (_abi.KernelTiming * cap)()
     n = ctypes.c_int()
-    check("msq_timing_collect", lib().msq_timing_collect(arr, 16, ctypes.byref(n)))
+    check("msq_timing_collect", lib().msq_timing_collect(arr, cap, ctypes.byref(n)))
     out = {}
-    for i in range(min(n.value, 16)):
+    for i in range(min(n.value, cap)):
         e = arr[i]
         out[e.name.decode()] = {"launches": int(e.launches), "total_ms": e.total_ms,
                                 "total_flops": e.total_flops}
