@@ -60,19 +60,36 @@ PROJ_NAMES = {(5120, 5120): "q/o", (1024, 5120): "k/v", (27648, 5120): "gate/up"
 
 
 def by_kernel(kt: dict) -> dict:
-    """Aggregate the per-label timing ("<kernel> <t>x<n>x<k>") per kernel."""
+    """Aggregate the per-label timing ("<kernel> <shape>") per kernel."""
     agg = {}
     for label, v in kt.items():
-        a = agg.setdefault(label.split(" ")[0], {"launches": 0, "total_ms": 0.0, "total_flops": 0.0})
+        a = agg.setdefault(label.split(" ")[0], {"launches": 0, "total_ms": 0.0, "total_flops": 0.0,
+                                                 "total_bytes": 0.0})
         for f in a:
             a[f] += v[f]
     return agg
+
+
+def hbm_kernels(kt: dict, steps: int) -> dict:
+    """Achieved HBM bandwidth (algorithmic bytes / time) of the memory-bound kernels."""
+    out = {}
+    for name, v in sorted(by_kernel(kt).items()):
+        if v["total_flops"] > 0:
+            continue
+        gbs = v["total_bytes"] / (v["total_ms"] * 1e-3) / 1e9
+        out[name] = {"launches_per_step": v["launches"] / steps, "ms_per_step": round(v["total_ms"] / steps, 2),
+                     "avg_us": round(v["total_ms"] / v["launches"] * 1e3, 1),
+                     "algorithmic_MB_per_launch": round(v["total_bytes"] / v["launches"] / 1e6, 2),
+                     "GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+    return out
 
 
 def gemm_shapes(kt: dict, steps: int) -> list:
     """MFMA utilisation of every projection shape and direction in the timed region."""
     out = []
     for label, v in sorted(kt.items()):
+        if v["total_flops"] == 0:
+            continue
         kern, shape = label.split(" ")
         t, n, k = (int(x) for x in shape.split("x"))
         tf = v["total_flops"] / (v["total_ms"] * 1e-3) / 1e12
@@ -273,8 +290,10 @@ def main() -> int:
 
     ms = streamed["seconds"] / args.steps * 1e3
     value = T * args.steps / streamed["seconds"]
-    # roofline: the dense dequant-MFMA kernel with the most time in the timed region
+    # roofline: the kernel with the most time in the timed region (a dense dequant-MFMA
+    # GEMM at this shape), against the MFMA bf16 peak
     shapes = gemm_shapes(streamed["kernels"], args.steps)
+    hbm = hbm_kernels(streamed["kernels"], args.steps)
     kt = by_kernel(streamed["kernels"])
     name = max(kt, key=lambda k: kt[k]["total_ms"])
     k = kt[name]
@@ -283,7 +302,8 @@ def main() -> int:
     achieved = avg_flops / (avg_ms * 1e-3) / 1e12
     kernels = {n: {"launches": v["launches"], "avg_ms": v["total_ms"] / v["launches"],
                    "tflops": v["total_flops"] / (v["total_ms"] * 1e-3) / 1e12,
-                   "ms_per_step": v["total_ms"] / args.steps} for n, v in kt.items()}
+                   "algorithmic_MB_per_launch": v["total_bytes"] / v["launches"] / 1e6,
+                   "ms_per_step": v["total_ms"] / args.steps} for n, v in kt.items() if v["total_flops"] > 0}
     h2d_bytes = streamed["window"]["bytes_copied"] if streamed["window"] else 0
     h2d_rate = h2d_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -306,7 +326,7 @@ def main() -> int:
                               "slots": args.slots, "layers_per_slot": args.window_blocks},
                    "lora_r": 16, "lora_alpha": 32,
                    "dropout": 0.0, "optimizer": "AdamW", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma" if avg_flops > 0 else "hbm", "kernel": name, "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(name), "avg_launch_ms": round(avg_ms, 4),
                      "algorithmic_gflop_per_launch": round(avg_flops / 1e9, 3)},
@@ -316,6 +336,7 @@ def main() -> int:
                 "windows_reused_per_step": streamed["window"]["windows_reused"] if streamed["window"] else 0},
         "kernels": kernels,
         "gemm_shapes": shapes,
+        "hbm_kernels": hbm,
         "peak_vram_gb": round(streamed["peak_alloc_gb"], 2),
         "baseline_context": {"value": round(T / PAGES_A100_S_PER_STEP, 1), "unit": "tokens/s",
                              "hardware": "NVIDIA A100 80GB PCIe", "s_per_step": PAGES_A100_S_PER_STEP},

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 1
+#define MSQ_ABI_VERSION 2
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -226,17 +226,19 @@ int block_stream_stats(const msq_window* w, msq_window_stats* out);
 int block_stream_destroy(msq_window* w);
 
 /* ------------------------------------------------------------------------- */
-/* Kernel timing (measurement support).  When enabled, every launch of the dense
- * dequant-MFMA kernels carries a start and a stop HIP event recorded by the dispatch
- * on the launch stream.  msq_timing_collect waits for the recorded events and
- * aggregates, per label "<kernel> <t>x<n>x<k>" (kernel name and projection shape),
- * the launch count, total milliseconds and total algorithmic flops (2*t*k*n per
- * launch).  Host-side bookkeeping only. */
+/* Kernel timing (measurement support).  When enabled, every kernel launch of the
+ * library carries a start and a stop HIP event recorded by the dispatch on the launch
+ * stream.  msq_timing_collect waits for the recorded events and aggregates, per label
+ * "<kernel> <shape>" (the dense GEMMs: "<t>x<n>x<k>"; the memory-bound LoRA-side
+ * kernels: their token and column counts), the launch count, total milliseconds, total
+ * algorithmic flops (2*t*k*n per GEMM launch) and total algorithmic bytes.  Host-side
+ * bookkeeping only. */
 typedef struct {
   char name[48];
   uint64_t launches;
   double total_ms;
-  double total_flops;
+  double total_flops;  /* algorithmic flops (dense MFMA kernels) */
+  double total_bytes;  /* algorithmic HBM bytes: every input read once, every output written once */
 } msq_kernel_timing;
 
 int msq_timing_enable(int on);

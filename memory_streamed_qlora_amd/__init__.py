@@ -2,12 +2,16 @@
 
 The compute lives in libmsq.so (C ABI: include/msq.h, HIP kernels under csrc/);
 ``ops`` is its thin Python binding and ``stack`` the Qwen2.5-shaped training step
-that drives it.  Importing the package loads the library and raises if it has not
-been built -- there is no CPU fallback.
+that drives it.  Importing the package loads the library; if it is missing or was
+built for another ABI version, the import still succeeds (so that the build module can
+run) but every call into the library raises -- there is no CPU fallback.
 """
 from ._abi import MsqError, lib as _load_library  # noqa: F401
 from .ops import (BlockStreamWindow, Lora, Workspace, abi_version, nf4_codebook,  # noqa: F401
                   nf4_dequantize, nf4_lora_bwd, nf4_lora_fwd, nf4_lora_workspace_size,
                   nf4_quantize, rng_key, timing_collect, timing_enable)
 
-_load_library()
+try:
+    _load_library()
+except ImportError:  # not built yet, or stale: every call into the library raises the same error
+    pass

@@ -45,7 +45,8 @@ class WindowStats(ctypes.Structure):
 
 class KernelTiming(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_uint64),
-                ("total_ms", ctypes.c_double), ("total_flops", ctypes.c_double)]
+                ("total_ms", ctypes.c_double), ("total_flops", ctypes.c_double),
+                ("total_bytes", ctypes.c_double)]
 
 
 class MsqError(RuntimeError):
@@ -83,6 +84,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
+ABI_VERSION = 2  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 
@@ -99,6 +101,9 @@ def lib() -> ctypes.CDLL:
             f = getattr(h, name)
             f.restype = res
             f.argtypes = args
+        if h.msq_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI version {h.msq_abi_version()}, this binding expects "
+                              f"{ABI_VERSION}: rebuild it with `python -m memory_streamed_qlora_amd.build`")
         _lib = h
     return _lib
 

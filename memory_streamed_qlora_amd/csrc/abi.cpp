@@ -83,7 +83,7 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   p.off_act_fwd = o;  // x packed into MFMA-fragment order (bf16)
   o = align256(o + (size_t)frag_rows(t) * k * sizeof(uint16_t));
   p.off_sk_fwd = o;   // chunk partials of the rank-r skinny products
-  o = align256(o + (size_t)((k + SKINNY_CHUNK - 1) / SKINNY_CHUNK) * t * r * sizeof(float));
+  o = align256(o + (size_t)((k + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
   p.fwd_bytes = o;
   p.nch = (int)((t + COLGRAD_TCHUNK - 1) / COLGRAD_TCHUNK);
   o = 0;
@@ -100,7 +100,7 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   p.off_act_bwd = o;  // dy packed into MFMA-fragment order (bf16)
   o = align256(o + (size_t)frag_rows(t) * n * sizeof(uint16_t));
   p.off_sk_bwd = o;
-  o = align256(o + (size_t)((std::max(k, n) + SKINNY_CHUNK - 1) / SKINNY_CHUNK) * t * r * sizeof(float));
+  o = align256(o + (size_t)((std::max(k, n) + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
   p.bwd_bytes = o;
   return p;
 }
@@ -195,10 +195,10 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
   float* part = (float*)(ws + p.off_part_fwd);
   const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
   hipError_t e = hipSuccess;
-  if (r > 0) e = launch_skinny(x, act_f32, t, k, A, 0, r, 1.0f, d, (float*)(ws + p.off_sk_fwd), u, s);
+  uint16_t* xb = u_only ? nullptr : (uint16_t*)(ws + p.off_act_fwd);
+  e = launch_pack_lora(x, act_f32, t, k, A, 0, r, 1.0f, d, xb, (float*)(ws + p.off_sk_fwd), u, s);
   if (u_only) return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
-  uint16_t* xb = (uint16_t*)(ws + p.off_act_fwd);
-  if (e == hipSuccess) e = launch_pack_frag(x, act_f32, t, k, xb, s);
+
   if (e == hipSuccess) {
     GemmLaunch L;
     L.mode = 0;
@@ -258,13 +258,12 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
     float* sk = (float*)(ws + p.off_sk_bwd);
     const float* uu = u;
     uint16_t* dyb = (uint16_t*)(ws + p.off_act_bwd);
-    e = launch_pack_frag(dy, act_f32, t, n, dyb, s);
     if (e == hipSuccess && r > 0 && !uu) {
       float* ut = (float*)(ws + p.off_u_bwd);
-      e = launch_skinny(x, act_f32, t, k, A, 0, r, 1.0f, d, sk, ut, s);
+      e = launch_pack_lora(x, act_f32, t, k, A, 0, r, 1.0f, d, nullptr, sk, ut, s);
       uu = ut;
     }
-    if (e == hipSuccess && r > 0) e = launch_skinny(dy, act_f32, t, n, B, 1, r, lscale, no_dropout(), sk, du, s);
+    if (e == hipSuccess) e = launch_pack_lora(dy, act_f32, t, n, B, 1, r, lscale, no_dropout(), dyb, sk, du, s);
     if (e == hipSuccess) {
       GemmLaunch L;
       L.mode = 1;

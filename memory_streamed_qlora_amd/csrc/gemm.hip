@@ -12,7 +12,7 @@
 // Tile: BM=512 rows of t x BN=128 output columns x BK=64 reduction, 512 threads = 8
 // waves; wave w owns rows 64w..64w+63 and all 128 columns (2x4 MFMA 32x32 blocks).
 // The activation operand comes straight from global memory into registers, packed in
-// MFMA-fragment order beforehand (launch_pack_frag) so that each load is one contiguous
+// MFMA-fragment order beforehand (launch_pack_lora) so that each load is one contiguous
 // 1 KB block; only the dequantized W tile goes through LDS (three buffers, one
 // barrier per k-step), and each dequantized element feeds all 512 rows.  Within a k-step,
 // the dequantization of the next tile is interleaved with the MFMAs of this one.
@@ -23,9 +23,6 @@
 // split over gridDim.z, in which case split 0 carries the LoRA term and fp32 partial
 // tiles go to a workspace summed in split order by a separate kernel, so results never
 // depend on timing.
-#include <hip/hip_ext.h>
-#include <stdio.h>
-
 #include "internal.hpp"
 
 namespace msq {
@@ -462,17 +459,12 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
     kern = nf4_bwd_gemm;
     name = "nf4_bwd_gemm";
   }
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (timing_on()) {
-    char label[48];  // kernel and projection shape: "<kernel> <t>x<n>x<k>"
-    snprintf(label, sizeof(label), "%s %lldx%lldx%lld", name, (long long)L.M, (long long)L.N, (long long)L.K);
-    timing_begin(label, flops, &e0, &e1);
-  }
-  if (e0)
-    hipExtLaunchKernelGGL(kern, grid, dim3(THREADS), 0, s, e0, e1, 0, g);
-  else
-    hipLaunchKernelGGL(kern, grid, dim3(THREADS), 0, s, g);
-  return hipGetLastError();
+  // algorithmic bytes: NF4 codes + scales, the packed activation, the output (or split partials)
+  const double bytes = (double)g.N * g.K * 0.5625 + (double)frag_rows(g.M) * g.R * 2 +
+                       (double)g.M * g.Nc * (g.splits > 1 ? 4.0 * g.splits : (g.out_f32 ? 4.0 : 2.0));
+  char shape[32];
+  snprintf(shape, sizeof(shape), "%lldx%lldx%lld", (long long)L.M, (long long)L.N, (long long)L.K);
+  return timed_launch(name, shape, flops, bytes, kern, grid, dim3(THREADS), s, g);
 }
 
 }  // namespace msq

@@ -1,9 +1,11 @@
 // Host-side internals of libmsq: launch wrappers, planning, errors, timing.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdio.h>
 
 #include "device_common.hpp"
 
@@ -21,7 +23,7 @@ const Nf4Mid& nf4_mid();
 constexpr int GEMM_BM = 512;
 constexpr int GEMM_BN = 128;
 constexpr int GEMM_BK = 64;
-constexpr int COLGRAD_TCHUNK = 32;
+constexpr int COLGRAD_TCHUNK = 64;
 
 struct GemmPlan {
   int splits;          // split of the reduction dimension
@@ -52,7 +54,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 // carrying the LoRA term) and launch_split_reduce finishes the output.
 struct GemmLaunch {
   int mode;
-  const uint16_t* act;  // packed by launch_pack_frag
+  const uint16_t* act;  // packed by launch_pack_lora
   const uint8_t* codes;
   const float* absmax;
   int64_t M, N, K;
@@ -68,15 +70,21 @@ struct GemmLaunch {
 };
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s);
 
-// Activations `in` are bf16 (uint16_t) or fp32 (in_f32).
-// out[t][j] = scale * sum_c h[t][c] * mat(j, c), h = drop(in) (dropout optional)
-//   mat_kind 0: mat is [r][C] (LoRA A);   mat_kind 1: mat is [C][r] (LoRA B)
-// Tiled over 16 tokens x SKINNY_CHUNK columns; part holds the per-chunk partials
-// ([ceil(C / SKINNY_CHUNK)][T][r] floats), summed in chunk order.
-constexpr int SKINNY_CHUNK = 512;
-hipError_t launch_skinny(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat,
-                         int mat_kind, int r, float scale, const Dropout& d, float* part, float* out,
-                         hipStream_t s);
+// One pass over an activation in [T][C] (bf16, or fp32 with in_f32; C % 64 == 0):
+//  - if `packed`, writes its bf16 copy in MFMA-fragment order: block (g, s, c) of 512 bf16
+//    holds, for lane l = 0..63, the 8 values of row 32*g + (l & 31) at reduction index
+//    64*s + 32*(l >> 5) + 8*c + (0..7); blocks ordered g, then s, then c, so the GEMM loads
+//    each 32-row operand fragment as one contiguous 1 KB piece; rows padded with zeros up
+//    to a multiple of 32 (`packed` holds frag_rows(T) * C bf16);
+//  - if r > 0, out[t][j] = scale * sum_c h[t][c] * mat(j, c), h = drop(in) (the dropout
+//    mask only touches this rank-r copy); mat_kind 0: mat is [r][C] (LoRA A), 1: [C][r]
+//    (LoRA B).  Partials per LORA_CHUNK columns go to part ([ceil(C / LORA_CHUNK)][T][r]
+//    floats) and are summed in chunk order.
+constexpr int LORA_CHUNK = 256;
+inline int64_t frag_rows(int64_t M) { return (M + 31) / 32 * 32; }
+hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat, int mat_kind,
+                            int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
+                            hipStream_t s);
 
 // part[ch][j][c] = sum_{t in chunk ch} coef[t][j] * h[t][c], h = drop(in)
 hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
@@ -90,18 +98,31 @@ hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, f
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
                                const uint16_t* bias, void* out, bool out_f32, int accumulate,
                                hipStream_t s);
-// Activation operand [M][R] (bf16, or fp32 rounded to bf16) in MFMA-fragment order: block
-// (g, s, c) of 512 bf16 holds, for lane l = 0..63, the 8 values of row 32*g + (l & 31) at
-// reduction index 64*s + 32*(l >> 5) + 8*c + (0..7).  Blocks are ordered g, then s, then c,
-// so the GEMM loads each 32-row operand fragment as one contiguous 1 KB piece.  Rows are
-// padded with zeros up to a multiple of 32; R % 64 == 0.  `out` holds frag_rows(M) * R bf16.
-inline int64_t frag_rows(int64_t M) { return (M + 31) / 32 * 32; }
-hipError_t launch_pack_frag(const void* in, bool in_f32, int64_t M, int64_t R, uint16_t* out, hipStream_t s);
+
 
 // ---- timing -------------------------------------------------------------------
 bool timing_on();
 // When timing is on, returns a record id and the two events the launch must record
-// (hipExtLaunchKernelGGL start/stop); otherwise -1 and null events.
-int timing_begin(const char* name, double flops, hipEvent_t* start, hipEvent_t* stop);
+// (hipExtLaunchKernelGGL start/stop); otherwise -1 and null events.  flops and bytes
+// are the launch's algorithmic work (0 where it does not apply).
+int timing_begin(const char* label, double flops, double bytes, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch `kern` on `s`; when timing is on, under a record labelled "<name> <shape>" whose
+// start/stop events the dispatch itself records.
+template <typename F, typename... Args>
+inline hipError_t timed_launch(const char* name, const char* shape, double flops, double bytes, F kern, dim3 grid,
+                               dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timing_on()) {
+    char label[48];
+    snprintf(label, sizeof(label), "%s %s", name, shape);
+    timing_begin(label, flops, bytes, &e0, &e1);
+  }
+  if (e0)
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
 
 }  // namespace msq

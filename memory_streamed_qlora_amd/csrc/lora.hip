@@ -2,8 +2,10 @@
 //
 // The rank-r products of the adapter are skinny (r = 16 against K, N in the
 // thousands) and bound by HBM/L2 traffic, not by MFMA:
-//   skinny(+reduce)  u = drop(x) A^T  (forward, recompute)  and  du = s dy B  (backward),
-//                   tiled over 16 tokens x 512 columns, chunk partials summed in order
+//   pack_lora(+reduce) one coalesced pass over an activation that writes its bf16 copy
+//                   in MFMA-fragment order for the base GEMM and forms the rank-r product
+//                   u = drop(x) A^T (forward, recompute) or du = s dy B (backward) in
+//                   LORA_CHUNK-column partials, summed in chunk order
 //   colgrad(+reduce) dA = du^T drop(x)  and  dB = s dy^T u, reduced over tokens in
 //                   fixed-size chunks and then summed in chunk order
 //   split_reduce    sums split-reduction partials of the base GEMM in split order and
@@ -59,71 +61,107 @@ __device__ __forceinline__ void store4(float* p, const float a[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(a[0], a[1], a[2], a[3]);
 }
 
-// Skinny product out[t][j] = scale * sum_c h[t][c] * M(c, j) for r <= 64 ranks.
-// Workgroup: 16 tokens x SKINNY_CHUNK columns x 16 ranks (grid z over rank groups);
-// the input tile (dropout applied while staging) and the matrix chunk are staged in
-// LDS, each thread owns one (token, rank) pair and reduces over the chunk; the chunk
-// partials go to part[chunk][t][j] and skinny_reduce sums them in chunk order.
-constexpr int SK_T = 16, SK_J = 16, SK_LD = SKINNY_CHUNK + 4;
+// Packing pass over an activation [T][C] (bf16 or fp32), fused with its rank-r product.
+// One workgroup covers 32 rows x LORA_CHUNK columns (4 k-steps of 64) and ranks
+// j0..j0+15 (grid z over rank groups).  Thread t handles row t >> 3 and 8 consecutive
+// columns (t & 7) of every k-step, loaded coalesced, and
+//   - writes them as bf16 in MFMA-fragment order (rank group 0 only, if `packed`):
+//     lane (row + 32 * (chunk >> 2)) of sub-step (chunk & 3), see launch_pack_frag;
+//   - accumulates h[t][c] * M(c, j) for its 16 ranks, h = drop(in) (dropout applied to
+//     the rank-r copy only), the adapter chunk staged in LDS rank-major;
+// then the 8 threads of a row combine their partials with a fixed butterfly and the
+// chunk partial goes to part[chunk][t][j]; skinny_reduce sums the chunks in order.
+constexpr int PK_STEPS = LORA_CHUNK / 64;
 
 template <typename TIN, int MAT_KIND>
-__global__ __launch_bounds__(256) void lora_skinny(const TIN* __restrict__ in, int64_t T, int64_t C,
-                                                   const float* __restrict__ mat, int r, Dropout d,
-                                                   float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) float xs[SK_T * SK_LD];
-  __shared__ __attribute__((aligned(16))) float ms[SK_J * SK_LD];
-  const int tid = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * SK_T;
-  const int64_t c0 = (int64_t)blockIdx.y * SKINNY_CHUNK;
-  const int j0 = blockIdx.z * SK_J;
-  // input tile [16][CHUNK], 4 consecutive columns per load
-  for (int idx = tid; idx < SK_T * SKINNY_CHUNK / 4; idx += 256) {
-    const int row = idx / (SKINNY_CHUNK / 4), c4 = idx % (SKINNY_CHUNK / 4);
-    const int64_t t = t0 + row, c = c0 + 4 * c4;
-    float h[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < T && c < C) {
-      load4(in + t * C + c, h);
-      if (d.threshold != 0u) {
-        const uint32_t keep = keep4(d, (uint64_t)t * (uint64_t)C + (uint64_t)c);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = ((keep >> q) & 1u) ? h[q] * d.sigma : 0.0f;
+__global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int64_t T, int64_t C, int steps,
+                                                 const float* __restrict__ mat, int r, Dropout d,
+                                                 uint16_t* __restrict__ packed, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float ms[16][LORA_CHUNK + 4];
+  const int tid = threadIdx.x, row = tid >> 3, ch = tid & 7;
+  const int grp = blockIdx.y, s0 = blockIdx.x * PK_STEPS;
+  const int nst = min(PK_STEPS, steps - s0);
+  const int j0 = blockIdx.z * 16;
+  const int64_t m = (int64_t)grp * 32 + row;
+  const int64_t c0 = (int64_t)s0 * 64;
+  if (r > 0) {
+    const int ncol = nst * 64;
+    if (MAT_KIND == 0) {  // mat [r][C]
+      for (int idx = tid; idx < 16 * LORA_CHUNK / 4; idx += 256) {
+        const int j = idx / (LORA_CHUNK / 4), c4 = 4 * (idx % (LORA_CHUNK / 4));
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j0 + j < r && c4 < ncol) v = *reinterpret_cast<const float4*>(mat + (int64_t)(j0 + j) * C + c0 + c4);
+        *reinterpret_cast<float4*>(&ms[j][c4]) = v;
+      }
+    } else {  // mat [C][r]
+      for (int idx = tid; idx < 16 * LORA_CHUNK; idx += 256) {
+        const int c = idx / 16, j = idx % 16;
+        ms[j][c] = (j0 + j < r && c < ncol) ? mat[(c0 + c) * (int64_t)r + j0 + j] : 0.0f;
       }
     }
-    *reinterpret_cast<float4*>(&xs[row * SK_LD + 4 * c4]) = make_float4(h[0], h[1], h[2], h[3]);
+    __syncthreads();
   }
-  // matrix chunk, stored [rank][column]
-  if (MAT_KIND == 0) {  // mat [r][C]
-    for (int idx = tid; idx < SK_J * SKINNY_CHUNK / 4; idx += 256) {
-      const int j = idx / (SKINNY_CHUNK / 4), c4 = idx % (SKINNY_CHUNK / 4);
-      const int64_t c = c0 + 4 * c4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j0 + j < r && c < C) v = *reinterpret_cast<const float4*>(mat + (int64_t)(j0 + j) * C + c);
-      *reinterpret_cast<float4*>(&ms[j * SK_LD + 4 * c4]) = v;
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  for (int b = 0; b < nst; ++b) {
+    const int step = s0 + b;
+    const int64_t c = (int64_t)step * 64 + ch * 8;
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (m < T) load8(in + m * C + c, f);
+    if (packed && blockIdx.z == 0) {
+      const uint4 v = make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
+                                 bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
+      const int lane = row + 32 * (ch >> 2), sub = ch & 3;
+      *reinterpret_cast<uint4*>(packed + (((int64_t)grp * steps + step) * 4 + sub) * 512 + lane * 8) = v;
     }
-  } else {  // mat [C][r]
-    for (int idx = tid; idx < SK_J * SKINNY_CHUNK; idx += 256) {
-      const int c = idx / SK_J, j = idx % SK_J;
+    if (r > 0) {
+      if (d.threshold != 0u && m < T) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t keep = keep4(d, (uint64_t)m * (uint64_t)C + (uint64_t)(c + 4 * h));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) f[4 * h + q] = ((keep >> q) & 1u) ? f[4 * h + q] * d.sigma : 0.0f;
+        }
+      }
+      const int cl = b * 64 + ch * 8;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 a0 = *reinterpret_cast<const float4*>(&ms[j][cl]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&ms[j][cl + 4]);
+        float v = acc[j];
+        v = fmaf(f[0], a0.x, v);
+        v = fmaf(f[1], a0.y, v);
+        v = fmaf(f[2], a0.z, v);
+        v = fmaf(f[3], a0.w, v);
+        v = fmaf(f[4], a1.x, v);
+        v = fmaf(f[5], a1.y, v);
+        v = fmaf(f[6], a1.z, v);
+        v = fmaf(f[7], a1.w, v);
+        acc[j] = v;
+      }
+    }
+  }
+  if (r == 0) return;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float v = acc[j];
+    v += __shfl_xor(v, 1, 8);
+    v += __shfl_xor(v, 2, 8);
+    v += __shfl_xor(v, 4, 8);
+    acc[j] = v;
+  }
+  if (m < T) {
+    // lane ch writes ranks 2*ch, 2*ch+1 of the row
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = 2 * ch + q;
       float v = 0.0f;
-      if (j0 + j < r && c0 + c < C) v = mat[(c0 + c) * (int64_t)r + j0 + j];
-      ms[j * SK_LD + c] = v;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) v = (jj == j) ? acc[jj] : v;
+      if (j0 + j < r) part[((int64_t)blockIdx.x * T + m) * r + j0 + j] = v;
     }
   }
-  __syncthreads();
-  const int row = tid / SK_J, j = tid % SK_J;
-  const float* xr = &xs[row * SK_LD];
-  const float* mr = &ms[j * SK_LD];
-  float acc = 0.0f;
-#pragma unroll 8
-  for (int c = 0; c < SKINNY_CHUNK; c += 4) {
-    const float4 a = *reinterpret_cast<const float4*>(xr + c);
-    const float4 b = *reinterpret_cast<const float4*>(mr + c);
-    acc = fmaf(a.x, b.x, acc);
-    acc = fmaf(a.y, b.y, acc);
-    acc = fmaf(a.z, b.z, acc);
-    acc = fmaf(a.w, b.w, acc);
-  }
-  const int64_t t = t0 + row;
-  if (t < T && j0 + j < r) part[((int64_t)blockIdx.y * T + t) * r + j0 + j] = acc;
 }
 
 __global__ __launch_bounds__(256) void lora_skinny_reduce(const float* __restrict__ part, int nck,
@@ -136,21 +174,25 @@ __global__ __launch_bounds__(256) void lora_skinny_reduce(const float* __restric
   out[i] = scale * s;
 }
 
-// part[ch][j][c] = sum_{t in chunk} coef[t][j] * h[t][c], for j in [j0, j0+16)
-// grid (ceil(C/256), nch, ceil(r/16)), 64 threads, 4 columns per thread.
-constexpr int CG_THREADS = 64;
+// part[ch][j][c] = sum_{t in chunk} coef[t][j] * h[t][c], for j in [j0, j0+16).
+// grid (ceil(C / CG_COLS), nch, ceil(r/16)), 256 threads, 4 columns per thread; the
+// token loop runs in order with CG_UNROLL rows loaded ahead of their use, so each
+// thread keeps that many 16-byte (fp32) loads in flight.
+constexpr int CG_THREADS = 256;
+constexpr int CG_COLS = 4 * CG_THREADS;
 constexpr int CG_J = 16;
+constexpr int CG_UNROLL = 8;
+static_assert(COLGRAD_TCHUNK % CG_UNROLL == 0, "token chunks are whole unroll groups");
 
 template <typename TIN>
 __global__ __launch_bounds__(CG_THREADS) void lora_colgrad(const TIN* __restrict__ in, int64_t T,
                                                            int64_t C, const float* __restrict__ coef,
-                                                           int r, Dropout d, int tchunk,
-                                                           float* __restrict__ part) {
+                                                           int r, Dropout d, float* __restrict__ part) {
   const int64_t c = ((int64_t)blockIdx.x * CG_THREADS + threadIdx.x) * 4;
   const int ch = blockIdx.y;
   const int j0 = blockIdx.z * CG_J;
-  const int64_t t0 = (int64_t)ch * tchunk;
-  const int64_t t1 = min(T, t0 + tchunk);
+  const int64_t t0 = (int64_t)ch * COLGRAD_TCHUNK;
+  const int64_t t1 = min(T, t0 + COLGRAD_TCHUNK);
   __shared__ float sc[COLGRAD_TCHUNK][CG_J];
   for (int i = threadIdx.x; i < COLGRAD_TCHUNK * CG_J; i += CG_THREADS) {
     const int tt = i / CG_J, jj = i % CG_J;
@@ -164,20 +206,28 @@ __global__ __launch_bounds__(CG_THREADS) void lora_colgrad(const TIN* __restrict
   for (int j = 0; j < CG_J; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
-  for (int64_t t = t0; t < t1; ++t) {
-    float h[4];
-    load4(in + t * C + c, h);
-    if (d.threshold != 0u) {
-      const uint32_t keep = keep4(d, (uint64_t)t * (uint64_t)C + (uint64_t)c);
+  for (int64_t tb = t0; tb < t1; tb += CG_UNROLL) {
+    float h[CG_UNROLL][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[q] = ((keep >> q) & 1u) ? h[q] * d.sigma : 0.0f;
+    for (int u = 0; u < CG_UNROLL; ++u) {
+      const int64_t t = min(tb + u, t1 - 1);  // rows past the chunk are loaded but weighted 0
+      load4(in + t * C + c, h[u]);
     }
-    const int tt = (int)(t - t0);
 #pragma unroll
-    for (int j = 0; j < CG_J; ++j) {
-      const float cj = sc[tt][j];
+    for (int u = 0; u < CG_UNROLL; ++u) {
+      const int64_t t = tb + u;
+      if (d.threshold != 0u) {
+        const uint32_t keep = keep4(d, (uint64_t)min(t, t1 - 1) * (uint64_t)C + (uint64_t)c);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(cj, h[q], acc[j][q]);
+        for (int q = 0; q < 4; ++q) h[u][q] = ((keep >> q) & 1u) ? h[u][q] * d.sigma : 0.0f;
+      }
+      const int tt = (int)(t - t0);
+#pragma unroll
+      for (int j = 0; j < CG_J; ++j) {
+        const float cj = sc[tt][j];  // 0 for rows past the chunk
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(cj, h[u][q], acc[j][q]);
+      }
     }
   }
 #pragma unroll
@@ -237,79 +287,66 @@ __global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ pa
   store4(out + o, a);
 }
 
-// Round fp32 activations to bf16 (RNE) for the MFMA operand; 8 per thread.
-// Activation operand of the fused GEMM in MFMA-fragment order (see launch_pack_frag).
-// One workgroup packs one block of 32 rows x 64 reduction columns: thread t reads
-// 8 consecutive elements (row t >> 3, chunk t & 7) with coalesced loads and stores them
-// as lane (row + 32 * (chunk >> 2)) of sub-step (chunk & 3).
-template <typename TIN>
-__global__ __launch_bounds__(256) void pack_frag(const TIN* __restrict__ in, int64_t M, int64_t R, int steps,
-                                                 uint16_t* __restrict__ out) {
-  const int grp = blockIdx.y, step = blockIdx.x;
-  const int t = threadIdx.x, row = t >> 3, chunk = t & 7;
-  const int64_t m = (int64_t)grp * 32 + row;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (m < M) {
-    float f[8];
-    load8(in + m * R + (int64_t)step * 64 + chunk * 8, f);
-    v = make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
-                   bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
-  }
-  const int lane = row + 32 * (chunk >> 2), c = chunk & 3;
-  *reinterpret_cast<uint4*>(out + (((int64_t)grp * steps + step) * 4 + c) * 512 + lane * 8) = v;
-}
-
 template <typename TIN, int MAT_KIND>
-hipError_t skinny_dispatch(const TIN* in, int64_t T, int64_t C, const float* mat, int r,
-                           const Dropout& d, float* part, hipStream_t s) {
-  const dim3 grid((unsigned)((T + SK_T - 1) / SK_T), (unsigned)((C + SKINNY_CHUNK - 1) / SKINNY_CHUNK),
-                  (unsigned)((r + SK_J - 1) / SK_J));
-  hipLaunchKernelGGL((lora_skinny<TIN, MAT_KIND>), grid, dim3(256), 0, s, in, T, C, mat, r, d, part);
-  return hipGetLastError();
+hipError_t pack_lora_dispatch(const TIN* in, int64_t T, int64_t C, const float* mat, int r, const Dropout& d,
+                              uint16_t* packed, float* part, hipStream_t s) {
+  const int steps = (int)(C / 64);
+  const dim3 grid((unsigned)((steps + PK_STEPS - 1) / PK_STEPS), (unsigned)((T + 31) / 32),
+                  (unsigned)(r > 0 ? (r + 15) / 16 : 1));
+  const double nck = (double)((C + LORA_CHUNK - 1) / LORA_CHUNK);
+  const double bytes = (double)T * C * sizeof(TIN) + (packed ? (double)frag_rows(T) * C * 2 : 0.0) +
+                       (r > 0 ? (double)r * C * 4 + nck * T * r * 4 : 0.0);
+  char shape[32];
+  snprintf(shape, sizeof(shape), "%lldx%lld r%d", (long long)T, (long long)C, r);
+  return timed_launch(packed ? "pack_lora" : "lora_product", shape, 0.0, bytes, pack_lora<TIN, MAT_KIND>, grid,
+                      dim3(256), s, in, T, C, steps, mat, r, d, packed, part);
 }
 
 }  // namespace
 
-hipError_t launch_skinny(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat,
-                         int mat_kind, int r, float scale, const Dropout& d, float* part, float* out,
-                         hipStream_t s) {
-  if (T == 0 || r == 0) return hipSuccess;
+hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat, int mat_kind,
+                            int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
+                            hipStream_t s) {
+  if (T == 0 || (r == 0 && !packed)) return hipSuccess;
   hipError_t e;
   if (in_f32)
-    e = mat_kind == 0 ? skinny_dispatch<float, 0>((const float*)in, T, C, mat, r, d, part, s)
-                      : skinny_dispatch<float, 1>((const float*)in, T, C, mat, r, d, part, s);
+    e = mat_kind == 0 ? pack_lora_dispatch<float, 0>((const float*)in, T, C, mat, r, d, packed, part, s)
+                      : pack_lora_dispatch<float, 1>((const float*)in, T, C, mat, r, d, packed, part, s);
   else
-    e = mat_kind == 0 ? skinny_dispatch<uint16_t, 0>((const uint16_t*)in, T, C, mat, r, d, part, s)
-                      : skinny_dispatch<uint16_t, 1>((const uint16_t*)in, T, C, mat, r, d, part, s);
-  if (e != hipSuccess) return e;
-  const int nck = (int)((C + SKINNY_CHUNK - 1) / SKINNY_CHUNK);
+    e = mat_kind == 0 ? pack_lora_dispatch<uint16_t, 0>((const uint16_t*)in, T, C, mat, r, d, packed, part, s)
+                      : pack_lora_dispatch<uint16_t, 1>((const uint16_t*)in, T, C, mat, r, d, packed, part, s);
+  if (e != hipSuccess || r == 0) return e;
+  const int nck = (int)((C + LORA_CHUNK - 1) / LORA_CHUNK);
   const int64_t n = T * r;
-  hipLaunchKernelGGL(lora_skinny_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, nck,
-                     n, scale, out);
-  return hipGetLastError();
+  char shape[32];
+  snprintf(shape, sizeof(shape), "%lldx%d c%d", (long long)T, r, nck);
+  return timed_launch("lora_product_reduce", shape, 0.0, (double)(nck + 1) * n * 4, lora_skinny_reduce,
+                      dim3((unsigned)((n + 255) / 256)), dim3(256), s, (const float*)part, nck, n, scale, out);
 }
 
 hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
                           const Dropout& d, int nch, float* part, hipStream_t s) {
   if (T == 0 || r == 0) return hipSuccess;
-  const dim3 grid((unsigned)((C / 4 + CG_THREADS - 1) / CG_THREADS), (unsigned)nch,
-                  (unsigned)((r + CG_J - 1) / CG_J));
+  const dim3 grid((unsigned)((C + CG_COLS - 1) / CG_COLS), (unsigned)nch, (unsigned)((r + CG_J - 1) / CG_J));
+  const double bytes = (double)T * C * (in_f32 ? 4 : 2) + (double)T * r * 4 + (double)nch * r * C * 4;
+  char shape[32];
+  snprintf(shape, sizeof(shape), "%lldx%lld r%d", (long long)T, (long long)C, r);
   if (in_f32)
-    hipLaunchKernelGGL(lora_colgrad<float>, grid, dim3(CG_THREADS), 0, s, (const float*)in, T, C, coef,
-                       r, d, COLGRAD_TCHUNK, part);
-  else
-    hipLaunchKernelGGL(lora_colgrad<uint16_t>, grid, dim3(CG_THREADS), 0, s, (const uint16_t*)in, T, C,
-                       coef, r, d, COLGRAD_TCHUNK, part);
-  return hipGetLastError();
+    return timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float>, grid, dim3(CG_THREADS), s,
+                        (const float*)in, T, C, coef, r, d, part);
+  return timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t>, grid, dim3(CG_THREADS), s,
+                      (const uint16_t*)in, T, C, coef, r, d, part);
 }
 
 hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale,
                                  float* out, int64_t sj, int64_t sc, int accumulate, hipStream_t s) {
   const int64_t n = (int64_t)r * C;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(lora_colgrad_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
-                     nch, r, C, scale, out, sj, sc, accumulate);
-  return hipGetLastError();
+  char shape[32];
+  snprintf(shape, sizeof(shape), "%dx%lld c%d", r, (long long)C, nch);
+  return timed_launch("lora_colgrad_reduce", shape, 0.0, (double)(nch + 1 + (accumulate ? 1 : 0)) * n * 4,
+                      lora_colgrad_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), s, part, nch, r, C, scale,
+                      out, sj, sc, accumulate);
 }
 
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
@@ -318,24 +355,15 @@ hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t
   const int64_t n4 = T * N / 4;
   if (n4 == 0) return hipSuccess;
   const dim3 grid((unsigned)((n4 + 255) / 256));
+  const double ob = out_f32 ? 4.0 : 2.0;
+  const double bytes = (double)splits * T * N * 4 + (double)T * N * ob * (accumulate ? 2 : 1) + (bias ? 2.0 * N : 0.0);
+  char shape[32];
+  snprintf(shape, sizeof(shape), "%lldx%lld s%d", (long long)T, (long long)N, splits);
   if (out_f32)
-    hipLaunchKernelGGL(split_reduce<float>, grid, dim3(256), 0, s, part, splits, T, N, bias, (float*)out,
-                       accumulate);
-  else
-    hipLaunchKernelGGL(split_reduce<uint16_t>, grid, dim3(256), 0, s, part, splits, T, N, bias,
-                       (uint16_t*)out, accumulate);
-  return hipGetLastError();
-}
-
-hipError_t launch_pack_frag(const void* in, bool in_f32, int64_t M, int64_t R, uint16_t* out, hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  const int steps = (int)(R / 64);
-  const dim3 grid((unsigned)steps, (unsigned)((M + 31) / 32));
-  if (in_f32)
-    hipLaunchKernelGGL(pack_frag<float>, grid, dim3(256), 0, s, (const float*)in, M, R, steps, out);
-  else
-    hipLaunchKernelGGL(pack_frag<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)in, M, R, steps, out);
-  return hipGetLastError();
+    return timed_launch("split_reduce", shape, 0.0, bytes, split_reduce<float>, grid, dim3(256), s, part, splits, T,
+                        N, bias, (float*)out, accumulate);
+  return timed_launch("split_reduce", shape, 0.0, bytes, split_reduce<uint16_t>, grid, dim3(256), s, part, splits,
+                      T, N, bias, (uint16_t*)out, accumulate);
 }
 
 }  // namespace msq

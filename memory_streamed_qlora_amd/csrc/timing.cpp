@@ -18,7 +18,7 @@ namespace {
 
 struct Rec {
   char name[48];
-  double flops;
+  double flops, bytes;
   hipEvent_t a, b;
 };
 
@@ -46,13 +46,14 @@ hipEvent_t take_event() {
 
 bool timing_on() { return g_on; }
 
-int timing_begin(const char* name, double flops, hipEvent_t* start, hipEvent_t* stop) {
+int timing_begin(const char* name, double flops, double bytes, hipEvent_t* start, hipEvent_t* stop) {
   *start = *stop = nullptr;
   if (!g_on) return -1;
   std::lock_guard<std::mutex> lk(g_mu);
   Rec r;
   snprintf(r.name, sizeof(r.name), "%s", name);
   r.flops = flops;
+  r.bytes = bytes;
   r.a = take_event();
   r.b = take_event();
   if (!r.a || !r.b) {
@@ -99,6 +100,7 @@ int msq_timing_collect(msq_kernel_timing* out, int max, int* n_out) {
     agg[i].launches++;
     agg[i].total_ms += ms;
     agg[i].total_flops += r.flops;
+    agg[i].total_bytes += r.bytes;
     g_pool.push_back(r.a);
     g_pool.push_back(r.b);
   }

@@ -296,7 +296,7 @@ def timing_enable(on: bool = True) -> None:
 
 
 def timing_collect() -> dict:
-    """Per label "<kernel> <t>x<n>x<k>": launches, total_ms, total_flops (then reset)."""
+    """Per label "<kernel> <shape>": launches, total_ms, total_flops, total_bytes (then reset)."""
     cap = 256
     arr = (_abi.KernelTiming * cap)()
     n = ctypes.c_int()
@@ -305,5 +305,5 @@ def timing_collect() -> dict:
     for i in range(min(n.value, cap)):
         e = arr[i]
         out[e.name.decode()] = {"launches": int(e.launches), "total_ms": e.total_ms,
-                                "total_flops": e.total_flops}
+                                "total_flops": e.total_flops, "total_bytes": e.total_bytes}
     return out

@@ -29,7 +29,9 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(abi.EXPORTED)
-    assert lib.msq_abi_version() == 1
+    header = open(os.path.join(ROOT, "include", "msq.h")).read()
+    assert lib.msq_abi_version() == int(re.search(r"#define MSQ_ABI_VERSION (\d+)", header).group(1))
+    assert lib.msq_abi_version() == abi.ABI_VERSION
 
 
 def test_host_codebook_equals_oracle():
@@ -133,3 +135,22 @@ def test_strerror_covers_every_code():
     L = abi.lib()
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.msq_strerror(code) and L.msq_strerror(code) != b"unknown error"
+
+
+def test_missing_library_raises_on_use(tmp_path):
+    """Without libmsq.so the package still imports (so the build module can run), and
+    the first call into the library raises: nothing falls back to the CPU."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = tmp_path / "memory_streamed_qlora_amd"
+    pkg.mkdir()
+    for f in os.listdir(os.path.join(ROOT, "memory_streamed_qlora_amd")):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(ROOT, "memory_streamed_qlora_amd", f), pkg / f)
+    code = ("import sys; sys.path.insert(0, %r); import memory_streamed_qlora_amd as m; "
+            "import memory_streamed_qlora_amd.build; m.nf4_codebook()" % str(tmp_path))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "libmsq.so not found" in r.stderr
