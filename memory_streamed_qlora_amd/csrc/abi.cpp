@@ -288,14 +288,14 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
     if (e == hipSuccess && p.bwd.splits > 1)
       e = launch_split_reduce(part, p.bwd.splits, t, k, nullptr, dx, out_f32, dx_accumulate, s);
     if (e == hipSuccess && r > 0)
-      e = launch_colgrad(x, act_f32, t, k, du, r, d, p.nch, (float*)(ws + p.off_pa), s);
+      e = launch_colgrad(x, act_f32, t, k, du, r, d, p.nch, false, (float*)(ws + p.off_pa), s);
     if (e == hipSuccess && r > 0)
-      e = launch_colgrad(dy, act_f32, t, n, uu, r, no_dropout(), p.nch, (float*)(ws + p.off_pb), s);
+      e = launch_colgrad(dy, act_f32, t, n, uu, r, no_dropout(), p.nch, true, (float*)(ws + p.off_pb), s);
   }
   if (e == hipSuccess && r > 0)
-    e = launch_colgrad_reduce((float*)(ws + p.off_pa), p.nch, r, k, 1.0f, dA, k, 1, dAB_accumulate, s);
+    e = launch_colgrad_reduce((float*)(ws + p.off_pa), p.nch, r, k, 1.0f, false, dA, dAB_accumulate, s);
   if (e == hipSuccess && r > 0)
-    e = launch_colgrad_reduce((float*)(ws + p.off_pb), p.nch, r, n, lscale, dB, 1, r, dAB_accumulate, s);
+    e = launch_colgrad_reduce((float*)(ws + p.off_pb), p.nch, r, n, lscale, true, dB, dAB_accumulate, s);
   return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_bwd launch");
 }
 

@@ -86,12 +86,14 @@ hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, c
                             int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
                             hipStream_t s);
 
-// part[ch][j][c] = sum_{t in chunk ch} coef[t][j] * h[t][c], h = drop(in)
+// Column gradients in two passes, reduced over tokens in fixed-size chunks:
+// partials P(ch, j, c) = sum_{t in chunk ch} coef[t][j] * h[t][c], h = drop(in), laid out
+// [nch][r][C] (out_cr false: the output is [r][C], LoRA dA) or [nch][C][r] (out_cr true:
+// output [C][r], LoRA dB), then out = [out +] scale * sum_ch P in chunk order.
 hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
-                          const Dropout& d, int nch, float* part, hipStream_t s);
-// out(j, c) = [out(j, c) +] scale * sum_ch part[ch][j][c];  out(j,c) = out[j*sj + c*sc]
-hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale,
-                                 float* out, int64_t sj, int64_t sc, int accumulate, hipStream_t s);
+                          const Dropout& d, int nch, bool out_cr, float* part, hipStream_t s);
+hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale, bool out_cr,
+                                 float* out, int accumulate, hipStream_t s);
 
 // Sum of split partials [splits][T][N] in split order, then + bias[n] (bias may be NULL)
 // or + the old output (accumulate), one rounding into bf16 or a fp32 store.

@@ -104,11 +104,20 @@ __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int
   float acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-  for (int b = 0; b < nst; ++b) {
+  // all of this thread's loads first (PK_STEPS x 8 elements in flight), then the work
+  float fa[PK_STEPS][8];
+#pragma unroll
+  for (int b = 0; b < PK_STEPS; ++b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fa[b][e] = 0.0f;
+    if (b < nst && m < T) load8(in + m * C + (int64_t)(s0 + b) * 64 + ch * 8, fa[b]);
+  }
+#pragma unroll
+  for (int b = 0; b < PK_STEPS; ++b) {
+    if (b >= nst) break;
     const int step = s0 + b;
     const int64_t c = (int64_t)step * 64 + ch * 8;
-    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (m < T) load8(in + m * C + c, f);
+    float* f = fa[b];
     if (packed && blockIdx.z == 0) {
       const uint4 v = make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
                                  bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
@@ -164,93 +173,151 @@ __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int
   }
 }
 
+// out[i] = scale * sum_c part[c][i] for i < n.  A workgroup owns 64 outputs; its four
+// waves sum four contiguous ranges of chunks in order (loads issued ahead of the adds)
+// and the four range sums are added in range order, so the result is fixed.
 __global__ __launch_bounds__(256) void lora_skinny_reduce(const float* __restrict__ part, int nck,
                                                           int64_t n, float scale,
                                                           float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+  __shared__ float red[4][64];
+  const int g = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int q = (nck + 3) / 4, c0 = g * q, c1 = min(nck, c0 + q);
   float s = 0.0f;
-  for (int c = 0; c < nck; ++c) s += part[(int64_t)c * n + i];
-  out[i] = scale * s;
+  if (i < n) {
+    int c = c0;
+    for (; c + 4 <= c1; c += 4) {
+      const float a0 = part[(int64_t)c * n + i], a1 = part[(int64_t)(c + 1) * n + i];
+      const float a2 = part[(int64_t)(c + 2) * n + i], a3 = part[(int64_t)(c + 3) * n + i];
+      s += a0;
+      s += a1;
+      s += a2;
+      s += a3;
+    }
+    for (; c < c1; ++c) s += part[(int64_t)c * n + i];
+  }
+  red[g][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (g == 0 && i < n) out[i] = scale * (((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x]);
 }
 
-// part[ch][j][c] = sum_{t in chunk} coef[t][j] * h[t][c], for j in [j0, j0+16).
-// grid (ceil(C / CG_COLS), nch, ceil(r/16)), 256 threads, 4 columns per thread; the
-// token loop runs in order with CG_UNROLL rows loaded ahead of their use, so each
-// thread keeps that many 16-byte (fp32) loads in flight.
+// Partial column gradients over one chunk of COLGRAD_TCHUNK tokens:
+//   P(ch, j, c) = sum_{t in chunk} coef[t][j] * h[t][c],  j in [j0, j0 + 16), h = drop(in),
+// stored part[ch][j][c] (OUT_CR = 0, for an output laid out [r][C]) or part[ch][c][j]
+// (OUT_CR = 1, output [C][r]) so that both the stores here and the reduction read and
+// write contiguously.  Workgroup: CG_COLS columns x the chunk; thread = (4 columns, token
+// quarter = wave); each wave runs over its quarter of the tokens in order with CG_UNROLL
+// rows loaded ahead of their use, then the quarter sums are added in quarter order
+// through LDS (quarter 0 stores, 1 and 2 add, 3 adds and writes the partial).
 constexpr int CG_THREADS = 256;
-constexpr int CG_COLS = 4 * CG_THREADS;
+constexpr int CG_COLS = 256;
 constexpr int CG_J = 16;
-constexpr int CG_UNROLL = 8;
-static_assert(COLGRAD_TCHUNK % CG_UNROLL == 0, "token chunks are whole unroll groups");
+constexpr int CG_UNROLL = 4;
+constexpr int CG_TQ = COLGRAD_TCHUNK / 4;  // tokens per quarter
+static_assert(CG_TQ % CG_UNROLL == 0, "token quarters are whole unroll groups");
 
-template <typename TIN>
+template <typename TIN, int OUT_CR>
 __global__ __launch_bounds__(CG_THREADS) void lora_colgrad(const TIN* __restrict__ in, int64_t T,
                                                            int64_t C, const float* __restrict__ coef,
                                                            int r, Dropout d, float* __restrict__ part) {
-  const int64_t c = ((int64_t)blockIdx.x * CG_THREADS + threadIdx.x) * 4;
+  __shared__ float sc[COLGRAD_TCHUNK][CG_J];
+  __shared__ __attribute__((aligned(16))) float red[CG_J][CG_COLS];
+  const int quad = threadIdx.x & 63, quarter = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * CG_COLS + 4 * quad;
   const int ch = blockIdx.y;
   const int j0 = blockIdx.z * CG_J;
   const int64_t t0 = (int64_t)ch * COLGRAD_TCHUNK;
   const int64_t t1 = min(T, t0 + COLGRAD_TCHUNK);
-  __shared__ float sc[COLGRAD_TCHUNK][CG_J];
   for (int i = threadIdx.x; i < COLGRAD_TCHUNK * CG_J; i += CG_THREADS) {
     const int tt = i / CG_J, jj = i % CG_J;
     const int64_t t = t0 + tt;
     sc[tt][jj] = (t < t1 && j0 + jj < r) ? coef[t * r + j0 + jj] : 0.0f;
   }
   __syncthreads();
-  if (c >= C) return;
   float acc[CG_J][4];
 #pragma unroll
   for (int j = 0; j < CG_J; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
-  for (int64_t tb = t0; tb < t1; tb += CG_UNROLL) {
-    float h[CG_UNROLL][4];
+  const bool live = c < C;
+  const int64_t tq0 = t0 + (int64_t)quarter * CG_TQ;
+  if (live) {
+    for (int64_t tb = tq0; tb < tq0 + CG_TQ; tb += CG_UNROLL) {
+      float h[CG_UNROLL][4];
 #pragma unroll
-    for (int u = 0; u < CG_UNROLL; ++u) {
-      const int64_t t = min(tb + u, t1 - 1);  // rows past the chunk are loaded but weighted 0
-      load4(in + t * C + c, h[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < CG_UNROLL; ++u) {
-      const int64_t t = tb + u;
-      if (d.threshold != 0u) {
-        const uint32_t keep = keep4(d, (uint64_t)min(t, t1 - 1) * (uint64_t)C + (uint64_t)c);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[u][q] = ((keep >> q) & 1u) ? h[u][q] * d.sigma : 0.0f;
+      for (int u = 0; u < CG_UNROLL; ++u) {
+        const int64_t t = min(tb + u, t1 - 1);  // rows past the chunk are loaded but weighted 0
+        load4(in + t * C + c, h[u]);
       }
-      const int tt = (int)(t - t0);
 #pragma unroll
-      for (int j = 0; j < CG_J; ++j) {
-        const float cj = sc[tt][j];  // 0 for rows past the chunk
+      for (int u = 0; u < CG_UNROLL; ++u) {
+        const int64_t t = tb + u;
+        if (d.threshold != 0u) {
+          const uint32_t keep = keep4(d, (uint64_t)min(t, t1 - 1) * (uint64_t)C + (uint64_t)c);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(cj, h[u][q], acc[j][q]);
+          for (int q = 0; q < 4; ++q) h[u][q] = ((keep >> q) & 1u) ? h[u][q] * d.sigma : 0.0f;
+        }
+        const int tt = (int)(t - t0);  // < COLGRAD_TCHUNK; coefficients are 0 past the chunk
+#pragma unroll
+        for (int j = 0; j < CG_J; ++j) {
+          const float cj = sc[tt][j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(cj, h[u][q], acc[j][q]);
+        }
       }
     }
   }
+  for (int g = 0; g < 4; ++g) {
+    if (quarter == g) {
 #pragma unroll
-  for (int j = 0; j < CG_J; ++j) {
-    if (j0 + j < r) {
-      float4 v = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-      *reinterpret_cast<float4*>(part + ((int64_t)ch * r + j0 + j) * C + c) = v;
+      for (int j = 0; j < CG_J; ++j) {
+        float4* rp = reinterpret_cast<float4*>(&red[j][4 * quad]);
+        float4 v = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        if (g > 0) {
+          const float4 w = *rp;
+          v = make_float4(w.x + v.x, w.y + v.y, w.z + v.z, w.w + v.w);
+        }
+        if (g < 3) {
+          *rp = v;
+        } else if (live) {
+          acc[j][0] = v.x;
+          acc[j][1] = v.y;
+          acc[j][2] = v.z;
+          acc[j][3] = v.w;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (quarter != 3 || !live) return;
+  if (OUT_CR == 0) {
+#pragma unroll
+    for (int j = 0; j < CG_J; ++j)
+      if (j0 + j < r)
+        *reinterpret_cast<float4*>(part + ((int64_t)ch * r + j0 + j) * C + c) =
+            make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float* p = part + ((int64_t)ch * C + c + q) * r + j0;
+#pragma unroll
+      for (int j = 0; j < CG_J; ++j)
+        if (j0 + j < r) p[j] = acc[j][q];
     }
   }
 }
 
+// out[i] = [out[i] +] scale * sum_ch part[ch][i], chunks in order.  The partials share the
+// output's layout ([r][C] or [C][r]), so reads and writes are contiguous either way.
 __global__ __launch_bounds__(256) void lora_colgrad_reduce(const float* __restrict__ part, int nch,
-                                                           int r, int64_t C, float scale,
-                                                           float* __restrict__ out, int64_t sj,
-                                                           int64_t sc, int accumulate) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over r*C, c fastest
-  if (i >= (int64_t)r * C) return;
-  const int64_t j = i / C, c = i % C;
+                                                           int64_t n, float scale,
+                                                           float* __restrict__ out, int accumulate) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
   float s = 0.0f;
-  for (int ch = 0; ch < nch; ++ch) s += part[((int64_t)ch * r + j) * C + c];
+  for (int ch = 0; ch < nch; ++ch) s += part[(int64_t)ch * n + i];
   s *= scale;
-  float* o = out + j * sj + c * sc;
-  *o = accumulate ? (*o + s) : s;
+  out[i] = accumulate ? (out[i] + s) : s;
 }
 
 // out[t][n..n+3] = sum_s P[s][t][n..n+3] (+ bias[n..n+3]) (+ old out), one rounding.
@@ -321,32 +388,42 @@ hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, c
   char shape[32];
   snprintf(shape, sizeof(shape), "%lldx%d c%d", (long long)T, r, nck);
   return timed_launch("lora_product_reduce", shape, 0.0, (double)(nck + 1) * n * 4, lora_skinny_reduce,
-                      dim3((unsigned)((n + 255) / 256)), dim3(256), s, (const float*)part, nck, n, scale, out);
+                      dim3((unsigned)((n + 63) / 64)), dim3(256), s, (const float*)part, nck, n, scale, out);
 }
 
 hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
-                          const Dropout& d, int nch, float* part, hipStream_t s) {
+                          const Dropout& d, int nch, bool out_cr, float* part, hipStream_t s) {
   if (T == 0 || r == 0) return hipSuccess;
   const dim3 grid((unsigned)((C + CG_COLS - 1) / CG_COLS), (unsigned)nch, (unsigned)((r + CG_J - 1) / CG_J));
   const double bytes = (double)T * C * (in_f32 ? 4 : 2) + (double)T * r * 4 + (double)nch * r * C * 4;
   char shape[32];
   snprintf(shape, sizeof(shape), "%lldx%lld r%d", (long long)T, (long long)C, r);
-  if (in_f32)
-    return timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float>, grid, dim3(CG_THREADS), s,
-                        (const float*)in, T, C, coef, r, d, part);
-  return timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t>, grid, dim3(CG_THREADS), s,
-                      (const uint16_t*)in, T, C, coef, r, d, part);
+  const dim3 blk(CG_THREADS);
+  if (in_f32) {
+    const float* x = (const float*)in;
+    return out_cr ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float, 1>, grid, blk, s, x, T, C,
+                                 coef, r, d, part)
+                  : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float, 0>, grid, blk, s, x, T, C,
+                                 coef, r, d, part);
+  }
+  const uint16_t* x = (const uint16_t*)in;
+  return out_cr ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t, 1>, grid, blk, s, x, T, C,
+                               coef, r, d, part)
+                : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t, 0>, grid, blk, s, x, T, C,
+                               coef, r, d, part);
 }
 
-hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale,
-                                 float* out, int64_t sj, int64_t sc, int accumulate, hipStream_t s) {
+hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale, bool out_cr,
+                                 float* out, int accumulate, hipStream_t s) {
   const int64_t n = (int64_t)r * C;
   if (n == 0) return hipSuccess;
   char shape[32];
   snprintf(shape, sizeof(shape), "%dx%lld c%d", r, (long long)C, nch);
-  return timed_launch("lora_colgrad_reduce", shape, 0.0, (double)(nch + 1 + (accumulate ? 1 : 0)) * n * 4,
-                      lora_colgrad_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), s, part, nch, r, C, scale,
-                      out, sj, sc, accumulate);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  const double bytes = (double)(nch + 1 + (accumulate ? 1 : 0)) * n * 4;
+  (void)out_cr;  // the partials already carry the output's layout
+  return timed_launch("lora_colgrad_reduce", shape, 0.0, bytes, lora_colgrad_reduce, grid, dim3(256), s, part, nch, n,
+                      scale, out, accumulate);
 }
 
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
