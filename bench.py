@@ -229,6 +229,8 @@ def main() -> int:
     ap.add_argument("--slots", type=int, default=3, help="window slots in the device arena (prefetch depth + 1)")
     ap.add_argument("--resident", action="store_true",
                     help="also time the same step with the whole base resident in device memory")
+    ap.add_argument("--glue", choices=("native", "torch"), default="native",
+                    help="pointwise block glue: the library's fused kernels, or the unfused PyTorch chain")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -249,7 +251,7 @@ def main() -> int:
     def run(mode: str):
         t_build = time.time()
         st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=0.0,
-                            window_blocks=args.window_blocks, n_slots=args.slots, mode=mode)
+                            window_blocks=args.window_blocks, n_slots=args.slots, mode=mode, glue=args.glue)
         torch.cuda.synchronize()
         log(f"{mode}: built {args.layers} layers in {time.time() - t_build:.1f}s "
             f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
@@ -325,7 +327,7 @@ def main() -> int:
                    "window": {"layers_resident": args.window_blocks * args.slots,
                               "slots": args.slots, "layers_per_slot": args.window_blocks},
                    "lora_r": 16, "lora_alpha": 32,
-                   "dropout": 0.0, "optimizer": "AdamW", "parallelism": "single GPU"},
+                   "dropout": 0.0, "optimizer": "AdamW", "glue": args.glue, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma" if avg_flops > 0 else "hbm", "kernel": name, "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(name), "avg_launch_ms": round(avg_ms, 4),

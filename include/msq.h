@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 2
+#define MSQ_ABI_VERSION 3
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -141,6 +141,12 @@ size_t nf4_lora_workspace_size(int64_t t, int64_t k, int64_t n, int32_t r);
  *   x      [t, k], 16-byte aligned                  t >= 0, k % 64 == 0
  *   codes  [n, k/2] uint8, absmax [n, k/64] fp32     n % 64 == 0
  *   bias   [n] bf16 or NULL
+ *   residual [t, n] in y's type, 16-byte aligned, or NULL.  When set, the output is
+ *          residual + (the y above), the residual connection of a decoder block fused
+ *          into this output pass (a pointwise fusion of the kind the pages allow for
+ *          kernels around the engine, "Poros" README, Roadmap, "The Poros kernel"): y
+ *          is formed and rounded to y's type as without it, and the one addition is
+ *          the same rounded operation as a separate residual add.  May equal y.
  *   A      [r, k] fp32, B [n, r] fp32  (16-byte aligned)
  *   y      [t, n] output (16-byte aligned)
  *   u_out  [t, r] fp32 output or NULL
@@ -149,9 +155,9 @@ size_t nf4_lora_workspace_size(int64_t t, int64_t k, int64_t n, int32_t r);
  * t == 0 is a no-op (x, y may then be NULL).  t * k must stay below 2^34 (dropout
  * counter range) and t at most 65535. */
 int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
-                 const float* absmax, const uint16_t* bias, const float* A, const float* B,
-                 msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out, void* workspace,
-                 size_t workspace_bytes, msq_stream_t stream);
+                 const float* absmax, const uint16_t* bias, const void* residual, const float* A,
+                 const float* B, msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out,
+                 void* workspace, size_t workspace_bytes, msq_stream_t stream);
 
 /* Fused backward of the same layer (no gradient for W, absmax or bias: frozen).
  *   du = s dy B                       (s = alpha / r)
@@ -171,6 +177,39 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
                  msq_lora_cfg cfg, msq_rng_key key, const float* u, void* dx,
                  int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
                  size_t workspace_bytes, msq_stream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Pointwise block glue of a Qwen2.5-style decoder block, fp32.
+ * The pages allow fusing kernels around the engine only where the fused chain is
+ * pointwise and yields the same per-element values as the unfused one, naming the
+ * SwiGLU multiply, residual adds and rotary embedding with precomputed tables
+ * ("Poros" README, Roadmap, "The Poros kernel"); reductions (RMSNorm, softmax) stay
+ * unfused.  Each entry evaluates the unfused chain's operations in the same order
+ * with the same fp32 roundings (products rounded where the unfused chain stores them;
+ * the one multiply-add it fuses, in the SiLU derivative, fused here too), so its result
+ * is that chain's element for element.  All tensors are contiguous device fp32, 16-byte
+ * aligned; outputs may not alias inputs.  n == 0 (t == 0) is a no-op; n (t*heads*d)
+ * above 2^40 is MSQ_E_SHAPE, a null or misaligned pointer MSQ_E_INVAL.
+ *
+ * msq_swiglu_fwd:  a = silu(g) * u,  silu(g) = g / (1 + exp(-g)), n elements.
+ * msq_swiglu_bwd:  du = da * silu(g);  dg = ((da * u) * s) * (1 + g * (1 - s)),
+ *                  s = 1 / (1 + exp(-g)), with 1 + g * (1 - s) one fused multiply-add
+ *                  -- the product rule followed by the SiLU derivative, as the two
+ *                  unfused steps compute them. */
+int msq_swiglu_fwd(const float* g, const float* u, int64_t n, float* a, msq_stream_t stream);
+int msq_swiglu_bwd(const float* da, const float* g, const float* u, int64_t n, float* dg,
+                   float* du, msq_stream_t stream);
+
+/* Rotary position embedding, rotate-half pairing (element i with i + d/2):
+ *   x, y   [t, heads, d] (d even; heads, d >= 1), cos_t, sin_t [t, d] tables
+ *   forward   y_i = x_i cos_i + (-x_{i+d/2}) sin_i,  y_{i+d/2} = x_{i+d/2} cos_{i+d/2} + x_i sin_{i+d/2}
+ *   backward  dx_i = dy_i cos_i + dy_{i+d/2} sin_{i+d/2},
+ *             dx_{i+d/2} = dy_{i+d/2} cos_{i+d/2} + (-(dy_i sin_i))
+ * (msq_rope_bwd takes dy in x and writes dx in y). */
+int msq_rope_fwd(const float* x, const float* cos_t, const float* sin_t, int64_t t, int32_t heads,
+                 int32_t d, float* y, msq_stream_t stream);
+int msq_rope_bwd(const float* dy, const float* cos_t, const float* sin_t, int64_t t, int32_t heads,
+                 int32_t d, float* dx, msq_stream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Host-to-device block-prefetch window.

@@ -66,11 +66,15 @@ _SIG = {
     "nf4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "nf4_dequantize": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "nf4_lora_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, ctypes.c_int32]),
-    "nf4_lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, LoraCfg, RngKey, _P,
-                                    _P, _P, ctypes.c_size_t, _P]),
+    "nf4_lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, LoraCfg, RngKey,
+                                    _P, _P, _P, ctypes.c_size_t, _P]),
     "nf4_lora_bwd": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, LoraCfg, RngKey, _P,
                                     _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
                                     _P]),
+    "msq_swiglu_fwd": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "msq_swiglu_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P]),
+    "msq_rope_fwd": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    "msq_rope_bwd": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "block_stream_arena_bytes": (ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "block_stream_create": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
                                            ctypes.c_size_t, _P]),
@@ -84,7 +88,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 2  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 3  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 
@@ -97,13 +101,19 @@ def lib() -> ctypes.CDLL:
                 f"libmsq.so not found at {LIB_PATH}: build it with "
                 "`python -m memory_streamed_qlora_amd.build` (there is no CPU fallback)")
         h = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIG.items():
-            f = getattr(h, name)
-            f.restype = res
-            f.argtypes = args
+        h.msq_abi_version.restype = ctypes.c_int
+        h.msq_abi_version.argtypes = []
         if h.msq_abi_version() != ABI_VERSION:
             raise ImportError(f"{LIB_PATH} has ABI version {h.msq_abi_version()}, this binding expects "
                               f"{ABI_VERSION}: rebuild it with `python -m memory_streamed_qlora_amd.build`")
+        for name, (res, args) in _SIG.items():
+            try:
+                f = getattr(h, name)
+            except AttributeError as e:
+                raise ImportError(f"{LIB_PATH} lacks {name}: rebuild it with "
+                                  "`python -m memory_streamed_qlora_amd.build`") from e
+            f.restype = res
+            f.argtypes = args
         _lib = h
     return _lib
 

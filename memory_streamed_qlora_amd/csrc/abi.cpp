@@ -168,9 +168,9 @@ size_t nf4_lora_workspace_size(int64_t t, int64_t k, int64_t n, int32_t r) {
 }
 
 int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
-                 const float* absmax, const uint16_t* bias, const float* A, const float* B,
-                 msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out, void* workspace,
-                 size_t workspace_bytes, msq_stream_t stream) {
+                 const float* absmax, const uint16_t* bias, const void* residual, const float* A,
+                 const float* B, msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out,
+                 void* workspace, size_t workspace_bytes, msq_stream_t stream) {
   int rc = check_linear("nf4_lora_fwd", t, k, n, cfg, key);
   if (rc) return rc;
   const bool u_only = cfg.flags & MSQ_U_ONLY;
@@ -179,9 +179,10 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
   if (u_only && (cfg.r == 0 || !u_out))
     return set_error(MSQ_E_INVAL, "nf4_lora_fwd: MSQ_U_ONLY needs r > 0 and u_out");
   if (cfg.r > 0 && (!A || !B)) return set_error(MSQ_E_INVAL, "nf4_lora_fwd: r > 0 needs A and B");
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(codes, 16) || !aligned(absmax, 4) ||
-      !aligned(bias, 8) || !aligned(A, 16) || !aligned(B, 16) || !aligned(u_out, 4) || !aligned(workspace, 256))
-    return set_error(MSQ_E_INVAL, "nf4_lora_fwd: misaligned pointer (x, y, codes, A, B: 16 bytes; bias 8; workspace 256)");
+  if (u_only && residual) return set_error(MSQ_E_INVAL, "nf4_lora_fwd: MSQ_U_ONLY writes no y to add a residual to");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(codes, 16) || !aligned(absmax, 4) || !aligned(bias, 8) ||
+      !aligned(residual, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(u_out, 4) || !aligned(workspace, 256))
+    return set_error(MSQ_E_INVAL, "nf4_lora_fwd: misaligned pointer (x, y, residual, codes, A, B: 16 bytes; bias 8; workspace 256)");
   const LoraPlan p = lora_plan(t, k, n, cfg.r);
   if (workspace_bytes < std::max(p.fwd_bytes, p.bwd_bytes))
     return set_error(MSQ_E_WORKSPACE, "nf4_lora_fwd: workspace %zu < %zu bytes", workspace_bytes, std::max(p.fwd_bytes, p.bwd_bytes));
@@ -215,13 +216,13 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
     L.lscale = lscale;
     L.drop = no_dropout();
     L.bias = bias;
+    L.addend = p.fwd.splits == 1 ? residual : nullptr;
     L.out = p.fwd.splits == 1 ? y : (void*)part;
     L.out_f32 = out_f32;
-    L.accumulate = 0;
     e = launch_gemm(L, s);
   }
   if (e == hipSuccess && p.fwd.splits > 1)
-    e = launch_split_reduce(part, p.fwd.splits, t, n, bias, y, out_f32, 0, s);
+    e = launch_split_reduce(part, p.fwd.splits, t, n, bias, residual, true, y, out_f32, s);
   return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
 }
 
@@ -280,13 +281,14 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
       L.lscale = 1.0f;
       L.drop = d;
       L.bias = nullptr;
+      L.addend = dx_accumulate && p.bwd.splits == 1 ? dx : nullptr;
       L.out = p.bwd.splits == 1 ? dx : (void*)part;
       L.out_f32 = out_f32;
-      L.accumulate = dx_accumulate;
       e = launch_gemm(L, s);
     }
     if (e == hipSuccess && p.bwd.splits > 1)
-      e = launch_split_reduce(part, p.bwd.splits, t, k, nullptr, dx, out_f32, dx_accumulate, s);
+      e = launch_split_reduce(part, p.bwd.splits, t, k, nullptr, dx_accumulate ? dx : nullptr, false, dx, out_f32,
+                              s);
     if (e == hipSuccess && r > 0)
       e = launch_colgrad(x, act_f32, t, k, du, r, d, p.nch, false, (float*)(ws + p.off_pa), s);
     if (e == hipSuccess && r > 0)
@@ -297,6 +299,50 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
   if (e == hipSuccess && r > 0)
     e = launch_colgrad_reduce((float*)(ws + p.off_pb), p.nch, r, n, lscale, true, dB, dAB_accumulate, s);
   return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_bwd launch");
+}
+
+int msq_swiglu_fwd(const float* g, const float* u, int64_t n, float* a, msq_stream_t stream) {
+  if (n < 0 || n > (int64_t(1) << 40)) return set_error(MSQ_E_SHAPE, "msq_swiglu_fwd: n = %lld outside [0, 2^40]", (long long)n);
+  if (n == 0) return MSQ_OK;
+  if (!g || !u || !a) return set_error(MSQ_E_INVAL, "msq_swiglu_fwd: null pointer");
+  if (!aligned(g, 16) || !aligned(u, 16) || !aligned(a, 16))
+    return set_error(MSQ_E_INVAL, "msq_swiglu_fwd: misaligned pointer (16 bytes)");
+  const hipError_t e = launch_swiglu_fwd(g, u, n, a, (hipStream_t)stream);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "msq_swiglu_fwd launch");
+}
+
+int msq_swiglu_bwd(const float* da, const float* g, const float* u, int64_t n, float* dg, float* du,
+                   msq_stream_t stream) {
+  if (n < 0 || n > (int64_t(1) << 40)) return set_error(MSQ_E_SHAPE, "msq_swiglu_bwd: n = %lld outside [0, 2^40]", (long long)n);
+  if (n == 0) return MSQ_OK;
+  if (!da || !g || !u || !dg || !du) return set_error(MSQ_E_INVAL, "msq_swiglu_bwd: null pointer");
+  if (!aligned(da, 16) || !aligned(g, 16) || !aligned(u, 16) || !aligned(dg, 16) || !aligned(du, 16))
+    return set_error(MSQ_E_INVAL, "msq_swiglu_bwd: misaligned pointer (16 bytes)");
+  const hipError_t e = launch_swiglu_bwd(da, g, u, n, dg, du, (hipStream_t)stream);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "msq_swiglu_bwd launch");
+}
+
+static int rope_entry(const char* fn, bool backward, const float* x, const float* cs, const float* sn, int64_t t,
+                      int32_t heads, int32_t d, float* y, msq_stream_t stream) {
+  if (t < 0 || heads < 1 || d < 2 || d % 2 || (double)t * heads * d > (double)(int64_t(1) << 40))
+    return set_error(MSQ_E_SHAPE, "%s: t = %lld, heads = %d, d = %d (need t >= 0, heads >= 1, even d >= 2, t*heads*d <= 2^40)",
+                     fn, (long long)t, heads, d);
+  if (t == 0) return MSQ_OK;
+  if (!x || !cs || !sn || !y) return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(cs, 16) || !aligned(sn, 16) || !aligned(y, 16))
+    return set_error(MSQ_E_INVAL, "%s: misaligned pointer (16 bytes)", fn);
+  const hipError_t e = launch_rope(backward, x, cs, sn, t, heads, d, y, (hipStream_t)stream);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
+}
+
+int msq_rope_fwd(const float* x, const float* cos_t, const float* sin_t, int64_t t, int32_t heads, int32_t d,
+                 float* y, msq_stream_t stream) {
+  return rope_entry("msq_rope_fwd", false, x, cos_t, sin_t, t, heads, d, y, stream);
+}
+
+int msq_rope_bwd(const float* dy, const float* cos_t, const float* sin_t, int64_t t, int32_t heads, int32_t d,
+                 float* dx, msq_stream_t stream) {
+  return rope_entry("msq_rope_bwd", true, dy, cos_t, sin_t, t, heads, d, dx, stream);
 }
 
 }  // extern "C"

@@ -19,10 +19,10 @@
 // The rank-r LoRA term of the same output tile is one more MFMA k-step per 16 ranks
 // (operands split into bf16 hi/lo pairs for ~fp32 accuracy); in the backward the
 // dropout keep-mask is applied per element of that term.  Unsplit launches write the
-// final output (bias or the old dx added, rounded once); the reduction can instead be
-// split over gridDim.z, in which case split 0 carries the LoRA term and fp32 partial
-// tiles go to a workspace summed in split order by a separate kernel, so results never
-// depend on timing.
+// final output (bias added, then a residual or the old dx, rounded once); the reduction
+// can instead be split over gridDim.z, in which case split 0 carries the LoRA term and
+// fp32 partial tiles go to a workspace summed in split order by a separate kernel, so
+// results never depend on timing.
 #include "internal.hpp"
 
 namespace msq {
@@ -50,11 +50,14 @@ struct GemmArgs {
   int r;
   float lscale;
   Dropout drop;
-  // output: splits == 1 -> y / dx directly (bf16 or fp32, + bias / + old dx);
+  // output: splits == 1 -> y / dx directly (bf16 or fp32): acc + bias, then addend + that
+  //         when addend is set (forward: a residual input, added to y after y's own
+  //         rounding; backward: the old dx, one rounding of the sum);
   //         splits  > 1 -> fp32 partials [splits][M][Nc]
   const uint16_t* bias;
+  const void* addend;  // [M][Nc] in the output's type, may equal out
   void* out;
-  int out_f32, accumulate;
+  int out_f32;
 };
 
 // Eight fp32 values -> hi and lo bf16 MFMA operands, hi = rne(v), lo = rne(v - hi), so
@@ -368,21 +371,28 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       const float bn = (MODE == 0 && g.bias) ? bf16_to_f32(g.bias[n]) : 0.0f;
       if (g.out_f32) {
         float* po = reinterpret_cast<float*>(g.out) + n;
+        const float* pa = reinterpret_cast<const float*>(g.addend) + n;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t m = mb + 8 * (v >> 2) + (v & 3);
           if (!(all_in || m < g.M)) continue;
           const float val = acc[i][jn][v] + bn;
-          po[m * g.Nc] = (MODE == 1 && g.accumulate) ? po[m * g.Nc] + val : val;
+          po[m * g.Nc] = g.addend ? pa[m * g.Nc] + val : val;
         }
       } else {
         uint16_t* po = reinterpret_cast<uint16_t*>(g.out) + n;
+        const uint16_t* pa = reinterpret_cast<const uint16_t*>(g.addend) + n;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t m = mb + 8 * (v >> 2) + (v & 3);
           if (!(all_in || m < g.M)) continue;
           float val = acc[i][jn][v] + bn;
-          if (MODE == 1 && g.accumulate) val = bf16_to_f32(po[m * g.Nc]) + val;
+          if (g.addend) {
+            // forward residual: y is rounded first, as a separate add would see it;
+            // backward accumulate: one rounding of the fp32 sum
+            if (MODE == 0) val = bf16_to_f32(bf16_rne(val));
+            val = bf16_to_f32(pa[m * g.Nc]) + val;
+          }
           po[m * g.Nc] = (uint16_t)bf16_rne(val);
         }
       }
@@ -440,9 +450,9 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   g.lscale = L.lscale;
   g.drop = L.drop;
   g.bias = L.bias;
+  g.addend = L.addend;
   g.out = L.out;
   g.out_f32 = L.out_f32;
-  g.accumulate = L.accumulate;
   // The kernel clamps rows and columns onto [0, M) x [0, Nc) and reads whole k-steps.
   if (g.M < 1 || g.Nc < 1 || g.R % BK || g.K % 64 || g.steps != (int)(g.R / BK)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)g.splits);
@@ -461,7 +471,7 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   }
   // algorithmic bytes: NF4 codes + scales, the packed activation, the output (or split partials)
   const double bytes = (double)g.N * g.K * 0.5625 + (double)frag_rows(g.M) * g.R * 2 +
-                       (double)g.M * g.Nc * (g.splits > 1 ? 4.0 * g.splits : (g.out_f32 ? 4.0 : 2.0));
+                       (double)g.M * g.Nc * (g.splits > 1 ? 4.0 * g.splits : (g.out_f32 ? 4.0 : 2.0) * (g.addend ? 2 : 1));
   char shape[32];
   snprintf(shape, sizeof(shape), "%lldx%lldx%lld", (long long)L.M, (long long)L.N, (long long)L.K);
   return timed_launch(name, shape, flops, bytes, kern, grid, dim3(THREADS), s, g);

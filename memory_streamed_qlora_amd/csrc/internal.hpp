@@ -48,8 +48,9 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
                              uint16_t* w, hipStream_t s);
 
 // Fused dequant-MFMA product with the LoRA term of the same tile.
-//   mode 0 (forward):  y[m][n]  = sum_k act[m][k] W[n][k] + lscale * lu[m] . lw[n] + bias[n]
-//   mode 1 (backward): dx[m][k] = [dx +] sum_n act[m][n] W[n][k] + keep*sigma * lu[m] . lw[:,k]
+//   mode 0 (forward):  y[m][n]  = [addend +] (sum_k act[m][k] W[n][k] + lscale * lu[m] . lw[n] + bias[n])
+//   mode 1 (backward): dx[m][k] = [addend +] (sum_n act[m][n] W[n][k] + keep*sigma * lu[m] . lw[:,k])
+// addend ([M][Nc] in the output's type, NULL for none) may be `out` itself.
 // With plan.splits > 1, `out` receives fp32 partials [splits][M][Nc] instead (split 0
 // carrying the LoRA term) and launch_split_reduce finishes the output.
 struct GemmLaunch {
@@ -65,8 +66,9 @@ struct GemmLaunch {
   float lscale;
   Dropout drop;
   const uint16_t* bias;
+  const void* addend;
   void* out;
-  int out_f32, accumulate;
+  int out_f32;
 };
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s);
 
@@ -95,11 +97,19 @@ hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, con
 hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale, bool out_cr,
                                  float* out, int accumulate, hipStream_t s);
 
-// Sum of split partials [splits][T][N] in split order, then + bias[n] (bias may be NULL)
-// or + the old output (accumulate), one rounding into bf16 or a fp32 store.
+// Sum of split partials [splits][T][N] in split order, then + bias[n] (bias may be NULL),
+// then addend + that (addend [T][N] in the output's type, may be `out`, NULL for none),
+// rounded into bf16 or stored as fp32.  round_first (bf16 output): the pre-addend value is
+// rounded to bf16 before the add, as a separate add of a rounded output would do.
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
-                               const uint16_t* bias, void* out, bool out_f32, int accumulate,
-                               hipStream_t s);
+                               const uint16_t* bias, const void* addend, bool round_first, void* out,
+                               bool out_f32, hipStream_t s);
+// Pointwise block glue (glue.hip), fp32 throughout.
+hipError_t launch_swiglu_fwd(const float* g, const float* u, int64_t n, float* a, hipStream_t s);
+hipError_t launch_swiglu_bwd(const float* da, const float* g, const float* u, int64_t n, float* dg, float* du,
+                             hipStream_t s);
+hipError_t launch_rope(bool backward, const float* x, const float* cs, const float* sn, int64_t T, int H, int D,
+                       float* y, hipStream_t s);
 
 
 // ---- timing -------------------------------------------------------------------

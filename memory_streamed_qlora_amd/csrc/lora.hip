@@ -8,10 +8,11 @@
 //                   LORA_CHUNK-column partials, summed in chunk order
 //   colgrad(+reduce) dA = du^T drop(x)  and  dB = s dy^T u, reduced over tokens in
 //                   fixed-size chunks and then summed in chunk order
-//   split_reduce    sums split-reduction partials of the base GEMM in split order and
-//                   adds the bias (forward) or the old dx (accumulating backward), then
-//                   rounds once to bf16 (or stores fp32); the LoRA term itself is folded
-//                   into the GEMM's output tiles.
+//   split_reduce    sums split-reduction partials of the base GEMM in split order,
+//                   adds the bias (forward), then adds that to a residual (forward) or
+//                   to the old dx (accumulating backward), and rounds once to bf16 (or
+//                   stores fp32); the LoRA term itself is folded into the GEMM's output
+//                   tiles.
 // Activations may be bf16 or fp32; with fp32 the rank-r products use the fp32
 // values and only the MFMA operand of the base product is rounded to bf16.
 // Every reduction has a fixed shape-determined order and no atomics, so results are
@@ -60,6 +61,12 @@ __device__ __forceinline__ void store4(uint16_t* p, const float a[4]) {
 __device__ __forceinline__ void store4(float* p, const float a[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(a[0], a[1], a[2], a[3]);
 }
+// The values a store4 to an output of p's type would hold (the pointer only selects it).
+__device__ __forceinline__ void round4(const uint16_t*, float a[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) a[q] = bf16_to_f32(bf16_rne(a[q]));
+}
+__device__ __forceinline__ void round4(const float*, float[4]) {}
 
 // Packing pass over an activation [T][C] (bf16 or fp32), fused with its rank-r product.
 // One workgroup covers 32 rows x LORA_CHUNK columns (4 k-steps of 64) and ranks
@@ -325,7 +332,8 @@ template <typename TOUT>
 __global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ part, int splits,
                                                     int64_t T, int64_t N,
                                                     const uint16_t* __restrict__ bias,
-                                                    TOUT* __restrict__ out, int accumulate) {
+                                                    const TOUT* addend, int round_first,
+                                                    TOUT* out) {  // addend may alias out
   const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i4 * 4 >= T * N) return;
   const int64_t o = i4 * 4;
@@ -345,9 +353,10 @@ __global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ pa
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] += b[q];
   }
-  if (accumulate) {
+  if (addend) {
     float old[4];
-    load4(out + o, old);
+    load4(addend + o, old);
+    if (round_first) round4(out, a);
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = old[q] + a[q];
   }
@@ -427,20 +436,20 @@ hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, f
 }
 
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
-                               const uint16_t* bias, void* out, bool out_f32, int accumulate,
-                               hipStream_t s) {
+                               const uint16_t* bias, const void* addend, bool round_first, void* out,
+                               bool out_f32, hipStream_t s) {
   const int64_t n4 = T * N / 4;
   if (n4 == 0) return hipSuccess;
   const dim3 grid((unsigned)((n4 + 255) / 256));
   const double ob = out_f32 ? 4.0 : 2.0;
-  const double bytes = (double)splits * T * N * 4 + (double)T * N * ob * (accumulate ? 2 : 1) + (bias ? 2.0 * N : 0.0);
+  const double bytes = (double)splits * T * N * 4 + (double)T * N * ob * (addend ? 2 : 1) + (bias ? 2.0 * N : 0.0);
   char shape[32];
   snprintf(shape, sizeof(shape), "%lldx%lld s%d", (long long)T, (long long)N, splits);
   if (out_f32)
     return timed_launch("split_reduce", shape, 0.0, bytes, split_reduce<float>, grid, dim3(256), s, part, splits, T,
-                        N, bias, (float*)out, accumulate);
+                        N, bias, (const float*)addend, (int)round_first, (float*)out);
   return timed_launch("split_reduce", shape, 0.0, bytes, split_reduce<uint16_t>, grid, dim3(256), s, part, splits,
-                      T, N, bias, (uint16_t*)out, accumulate);
+                      T, N, bias, (const uint16_t*)addend, (int)round_first, (uint16_t*)out);
 }
 
 }  // namespace msq

@@ -142,10 +142,13 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
                  cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
                  u_out: Optional[torch.Tensor] = None, want_u: bool = True,
                  workspace: Optional[Workspace] = None, stream=None,
-                 out_dtype: Optional[torch.dtype] = None, u_only: bool = False):
-    """y = x W^T + bias + (alpha/r) drop(x) A^T B^T.  Returns (y, u) (u None if not wanted).
+                 out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
+                 residual: Optional[torch.Tensor] = None):
+    """y = [residual +] (x W^T + bias + (alpha/r) drop(x) A^T B^T).  Returns (y, u) (u None
+    if not wanted).
 
     x may be bf16 or fp32; y is out_dtype (default: x's dtype, or y's if given).
+    residual ([t, n], y's dtype) is added in the output pass, rounded as a separate add.
     u_only: compute only u (y is None)."""
     t, k = x.shape
     n = codes.shape[0]
@@ -170,6 +173,10 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
         if y is None:
             y = torch.empty((t, n), dtype=out_dtype, device=x.device)
         _req(y, "y", out_dtype, (t, n))
+    if residual is not None:
+        if u_only:
+            raise ValueError("u_only computes no y to add a residual to")
+        _req(residual, "residual", out_dtype, (t, n))
     if want_u and r > 0 and u_out is None:
         u_out = torch.empty((t, r), dtype=torch.float32, device=x.device)
     if u_out is not None:
@@ -177,7 +184,8 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
     need = nf4_lora_workspace_size(t, k, n, r)
     ws = _workspace(x.device, need, workspace)
     check("nf4_lora_fwd", lib().nf4_lora_fwd(
-        _ptr(x), t, k, n, _ptr(codes), _ptr(absmax), _ptr(bias), _ptr(A) if r > 0 else None,
+        _ptr(x), t, k, n, _ptr(codes), _ptr(absmax), _ptr(bias), _ptr(residual),
+        _ptr(A) if r > 0 else None,
         _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(),
         _stream(stream)))
     return y, u_out
@@ -223,6 +231,50 @@ def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax:
         int(dx_accumulate), _ptr(dA) if r > 0 else None, _ptr(dB) if r > 0 else None,
         int(dAB_accumulate), _ptr(ws), ws.numel(), _stream(stream)))
     return dx, (dA if r > 0 else None), (dB if r > 0 else None)
+
+# ---------------------------------------------------------------------------------
+# pointwise block glue (fp32, contiguous)
+
+def swiglu_fwd(g: torch.Tensor, u: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """a = silu(g) * u, element for element the value of the unfused two-step chain."""
+    _req(g, "g", torch.float32, tuple(g.shape))
+    _req(u, "u", torch.float32, tuple(g.shape))
+    a = torch.empty_like(g) if out is None else out
+    _req(a, "a", torch.float32, tuple(g.shape))
+    check("msq_swiglu_fwd", lib().msq_swiglu_fwd(_ptr(g), _ptr(u), g.numel(), _ptr(a), _stream(stream)))
+    return a
+
+
+def swiglu_bwd(da: torch.Tensor, g: torch.Tensor, u: torch.Tensor, stream=None):
+    """(dg, du) of a = silu(g) * u."""
+    for nm, t in (("da", da), ("g", g), ("u", u)):
+        _req(t, nm, torch.float32, tuple(g.shape))
+    dg, du = torch.empty_like(g), torch.empty_like(g)
+    check("msq_swiglu_bwd", lib().msq_swiglu_bwd(_ptr(da), _ptr(g), _ptr(u), g.numel(), _ptr(dg), _ptr(du),
+                                                 _stream(stream)))
+    return dg, du
+
+
+def _rope(fn: str, x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, stream) -> torch.Tensor:
+    if x.dim() != 3:
+        raise ValueError(f"{fn}: x must be [t, heads, d], got {tuple(x.shape)}")
+    t, h, d = x.shape
+    _req(x, "x", torch.float32, (t, h, d))
+    _req(cos, "cos", torch.float32, (t, d))
+    _req(sin, "sin", torch.float32, (t, d))
+    y = torch.empty_like(x)
+    check(fn, getattr(lib(), fn)(_ptr(x), _ptr(cos), _ptr(sin), t, h, d, _ptr(y), _stream(stream)))
+    return y
+
+
+def rope_fwd(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, stream=None) -> torch.Tensor:
+    """Rotary embedding of x [t, heads, d] (rotate-half pairs) with tables cos, sin [t, d]."""
+    return _rope("msq_rope_fwd", x, cos, sin, stream)
+
+
+def rope_bwd(dy: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, stream=None) -> torch.Tensor:
+    """Gradient of rope_fwd with respect to x."""
+    return _rope("msq_rope_bwd", dy, cos, sin, stream)
 
 
 class BlockStreamWindow:

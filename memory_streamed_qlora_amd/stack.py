@@ -15,11 +15,15 @@ Resident mode runs the same code with every layer's blob already in device memor
 
 Every projection goes through the library (nf4_lora_fwd / nf4_lora_bwd) with fp32
 activations in and out; the library rounds them to bf16 only as the MFMA operand of
-the frozen-base product.  The glue between projections -- RMSNorm, RoPE from
-precomputed tables, causal GQA attention, SwiGLU, residual adds, embedding gather,
-lm_head and cross-entropy, AdamW -- is plain fp32 PyTorch and deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and
-optimizer settings are readings of the Qwen2 family and of textbook AdamW; the pages
-name neither.
+the frozen-base product.  The pointwise glue -- the SwiGLU product, rotary embedding
+from precomputed tables and the two residual adds per block (fused into the output
+pass of the o and down projections) -- runs in the library too (glue="native"); each
+fused chain reproduces the unfused PyTorch chain element for element (the pages allow
+only such fusions, "Poros" README, Roadmap, "The Poros kernel"), and glue="torch" runs
+that unfused chain.  The rest -- RMSNorm, causal GQA attention, embedding gather,
+lm_head and cross-entropy, AdamW -- holds reductions, so it stays unfused fp32 PyTorch,
+deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and optimizer settings are
+readings of the Qwen2 family and of textbook AdamW; the pages name neither.
 """
 from __future__ import annotations
 
@@ -102,14 +106,15 @@ class LayerLayout:
 
 class _NF4LoraLinear(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, A, B, codes, absmax, bias, cfg, key, value_unused):
+    def forward(ctx, x, A, B, codes, absmax, bias, residual, cfg, key, value_unused):
         if value_unused:
             # selective recompute: the backward reads only x and u, never y, so the
             # frozen-base product is skipped and y is a zero placeholder
             _, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, u_only=True)
             y = x.new_zeros(()).expand(x.shape[0], codes.shape[0])
         else:
-            y, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=True)
+            y, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=True,
+                                    residual=residual)
         ctx.save_for_backward(x, A, B, u)
         ctx.codes, ctx.absmax, ctx.cfg, ctx.key = codes, absmax, cfg, key
         return y
@@ -117,18 +122,47 @@ class _NF4LoraLinear(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy):
         x, A, B, u = ctx.saved_tensors
-        dx, dA, dB = ops.nf4_lora_bwd(dy.contiguous(), x, ctx.codes, ctx.absmax, A, B, ctx.cfg,
-                                      ctx.key, u=u)
-        return dx, dA, dB, None, None, None, None, None, None
+        dy = dy.contiguous()
+        dx, dA, dB = ops.nf4_lora_bwd(dy, x, ctx.codes, ctx.absmax, A, B, ctx.cfg, ctx.key, u=u)
+        # y = residual + (...): the residual's gradient is dy itself
+        dres = dy if ctx.needs_input_grad[6] else None
+        return dx, dA, dB, None, None, None, dres, None, None, None
 
 
 def nf4_lora_linear(x, A, B, codes, absmax, bias, cfg: ops.Lora, key,
-                    value_unused: bool = False) -> torch.Tensor:
-    if torch.is_grad_enabled() and (x.requires_grad or A.requires_grad or B.requires_grad):
-        return _NF4LoraLinear.apply(x, A, B, codes, absmax, bias, cfg, key,
+                    value_unused: bool = False, residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[residual +] the projection; with a residual the add happens in the library's
+    output pass."""
+    if torch.is_grad_enabled() and (x.requires_grad or A.requires_grad or B.requires_grad or
+                                    (residual is not None and residual.requires_grad)):
+        return _NF4LoraLinear.apply(x, A, B, codes, absmax, bias, residual, cfg, key,
                                     value_unused and cfg.r > 0)
-    y, _ = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=False)
+    y, _ = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=False, residual=residual)
     return y
+
+
+class _SwiGLU(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, g, u):
+        ctx.save_for_backward(g, u)
+        return ops.swiglu_fwd(g, u)
+
+    @staticmethod
+    def backward(ctx, da):
+        g, u = ctx.saved_tensors
+        return ops.swiglu_bwd(da.contiguous(), g, u)
+
+
+class _RoPE(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, cos, sin):
+        ctx.save_for_backward(cos, sin)
+        return ops.rope_fwd(x, cos, sin)
+
+    @staticmethod
+    def backward(ctx, dy):
+        cos, sin = ctx.saved_tensors
+        return ops.rope_bwd(dy.contiguous(), cos, sin), None, None
 
 
 # ---------------------------------------------------------------------------------
@@ -147,7 +181,7 @@ def rope_tables(T: int, D: int, device) -> Tuple[torch.Tensor, torch.Tensor]:
 
 
 def rope(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor) -> torch.Tensor:
-    """x [T, H, D] with rotate-half pairs (i, i + D/2)."""
+    """x [T, H, D] with rotate-half pairs (i, i + D/2); the unfused PyTorch chain."""
     h = x.shape[-1] // 2
     rot = torch.cat([-x[..., h:], x[..., :h]], dim=-1)
     return x * cos[:, None, :] + rot * sin[:, None, :]
@@ -182,9 +216,11 @@ class Stack:
 
     def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
                  window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
-                 n_slots: int = 2):
+                 n_slots: int = 2, glue: str = "native"):
         assert mode in ("streamed", "resident")
+        assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
+        self.glue = glue
         self.cfg = ops.Lora(r, alpha, p_drop)
         self.window_blocks = window_blocks
         self.n_slots = n_slots
@@ -277,11 +313,14 @@ class Stack:
         return st
 
     # -- one layer -----------------------------------------------------------------
-    def _lin(self, x, l, views, proj, step, micro, value_unused=False):
+    def _lin(self, x, l, views, proj, step, micro, value_unused=False, residual=None):
         key = ops.rng_key(self.seed, step, micro, l, PROJ_ID[proj])
         bias = views.get((proj, "bias"))
+        if residual is not None and self.glue == "torch":
+            return residual + nf4_lora_linear(x, self.A[l][proj], self.B[l][proj], views[(proj, "codes")],
+                                              views[(proj, "absmax")], bias, self.cfg, key, value_unused)
         return nf4_lora_linear(x, self.A[l][proj], self.B[l][proj], views[(proj, "codes")],
-                               views[(proj, "absmax")], bias, self.cfg, key, value_unused)
+                               views[(proj, "absmax")], bias, self.cfg, key, value_unused, residual)
 
     def layer_forward(self, h: torch.Tensor, l: int, views, step: int, micro: int = 0,
                       recompute: bool = False) -> torch.Tensor:
@@ -297,13 +336,17 @@ class Stack:
         k = self._lin(xn, l, views, "k", step, micro).view(T, sh.kv_heads, sh.head_dim)
         v = self._lin(xn, l, views, "v", step, micro).view(T, sh.kv_heads, sh.head_dim)
         cos, sin = self.cos[:T], self.sin[:T]
-        att = causal_gqa_attention(rope(q, cos, sin), rope(k, cos, sin), v, self.mask_add[:T, :T])
-        h1 = h + self._lin(att, l, views, "o", step, micro)
+        if self.glue == "native":
+            q, k = _RoPE.apply(q, cos, sin), _RoPE.apply(k, cos, sin)
+        else:
+            q, k = rope(q, cos, sin), rope(k, cos, sin)
+        att = causal_gqa_attention(q, k, v, self.mask_add[:T, :T])
+        h1 = self._lin(att, l, views, "o", step, micro, residual=h)
         xn2 = rmsnorm(h1, self.ln2[l])
         g = self._lin(xn2, l, views, "gate", step, micro)
         u = self._lin(xn2, l, views, "up", step, micro)
-        a = torch.nn.functional.silu(g) * u
-        return h1 + self._lin(a, l, views, "down", step, micro, value_unused=recompute)
+        a = _SwiGLU.apply(g, u) if self.glue == "native" else torch.nn.functional.silu(g) * u
+        return self._lin(a, l, views, "down", step, micro, value_unused=recompute, residual=h1)
 
     # -- base residency --------------------------------------------------------------
     def _views(self, l: int):

@@ -63,7 +63,7 @@ def test_quantize_rejects_bad_arguments():
 def _fwd(t=8, k=128, n=128, r=16, alpha=32.0, p=0.0, ws=None, x=FAKE, proj=0, layer=0, bias=None):
     L = abi.lib()
     need = L.nf4_lora_workspace_size(t, k, n, r)
-    return L.nf4_lora_fwd(x, t, k, n, FAKE, FAKE, bias, FAKE, FAKE, abi.LoraCfg(r, alpha, p),
+    return L.nf4_lora_fwd(x, t, k, n, FAKE, FAKE, bias, None, FAKE, FAKE, abi.LoraCfg(r, alpha, p),
                           abi.RngKey(0, 0, 0, layer, proj), FAKE, None, FAKE,
                           need if ws is None else ws, None)
 
@@ -91,6 +91,40 @@ def test_linear_rejects_bad_arguments():
     rc = L.nf4_lora_bwd(FAKE, FAKE, 8, 128, 128, FAKE, FAKE, FAKE, FAKE, abi.LoraCfg(16, 32.0, 0.0),
                         abi.RngKey(), None, FAKE, 0, None, FAKE, 0, FAKE, need, None)
     assert rc == abi.MSQ_E_INVAL
+
+
+def test_linear_rejects_bad_residual():
+    L = abi.lib()
+    need = L.nf4_lora_workspace_size(8, 128, 128, 16)
+    args = lambda res, flags: (FAKE, 8, 128, 128, FAKE, FAKE, None, res, FAKE, FAKE,  # noqa: E731
+                               abi.LoraCfg(16, 32.0, 0.0, flags), abi.RngKey(0, 0, 0, 0, 0), FAKE, FAKE,
+                               FAKE, need, None)
+    assert L.nf4_lora_fwd(*args(FAKE + 8, 0)) == abi.MSQ_E_INVAL
+    assert "misaligned" in _err()
+    assert L.nf4_lora_fwd(*args(FAKE, abi.MSQ_U_ONLY)) == abi.MSQ_E_INVAL
+    assert "residual" in _err()
+
+
+def test_glue_rejects_bad_arguments():
+    """The pointwise glue entries validate on the host; n == 0 / t == 0 is a no-op that
+    touches no pointer."""
+    L = abi.lib()
+    assert L.msq_swiglu_fwd(None, None, 0, None, None) == 0
+    assert L.msq_swiglu_bwd(None, None, None, 0, None, None, None) == 0
+    assert L.msq_swiglu_fwd(FAKE, FAKE, -1, FAKE, None) == abi.MSQ_E_SHAPE
+    assert L.msq_swiglu_fwd(FAKE, FAKE, (1 << 40) + 1, FAKE, None) == abi.MSQ_E_SHAPE
+    assert L.msq_swiglu_fwd(FAKE, None, 8, FAKE, None) == abi.MSQ_E_INVAL
+    assert L.msq_swiglu_fwd(FAKE, FAKE + 4, 8, FAKE, None) == abi.MSQ_E_INVAL
+    assert "misaligned" in _err()
+    assert L.msq_swiglu_bwd(FAKE, FAKE, FAKE, 8, FAKE, None, None) == abi.MSQ_E_INVAL
+    for fn in (L.msq_rope_fwd, L.msq_rope_bwd):
+        assert fn(None, None, None, 0, 1, 64, None, None) == 0
+        assert fn(FAKE, FAKE, FAKE, 4, 2, 63, FAKE, None) == abi.MSQ_E_SHAPE
+        assert fn(FAKE, FAKE, FAKE, 4, 0, 64, FAKE, None) == abi.MSQ_E_SHAPE
+        assert fn(FAKE, FAKE, FAKE, -1, 2, 64, FAKE, None) == abi.MSQ_E_SHAPE
+        assert fn(FAKE, FAKE, FAKE, 1 << 30, 1 << 10, 1 << 10, FAKE, None) == abi.MSQ_E_SHAPE
+        assert fn(FAKE, None, FAKE, 4, 2, 64, FAKE, None) == abi.MSQ_E_INVAL
+        assert fn(FAKE, FAKE, FAKE + 8, 4, 2, 64, FAKE, None) == abi.MSQ_E_INVAL
 
 
 def test_workspace_size_depends_on_shape_only():
