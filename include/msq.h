@@ -183,8 +183,8 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
  * The pages allow fusing kernels around the engine only where the fused chain is
  * pointwise and yields the same per-element values as the unfused one, naming the
  * SwiGLU multiply, residual adds and rotary embedding with precomputed tables
- * ("Poros" README, Roadmap, "The Poros kernel"); reductions (RMSNorm, softmax) stay
- * unfused.  Each entry evaluates the unfused chain's operations in the same order
+ * ("Poros" README, Roadmap, "The Poros kernel"); reductions (RMSNorm's mean, softmax)
+ * stay unfused.  Each entry evaluates the unfused chain's operations in the same order
  * with the same fp32 roundings (products rounded where the unfused chain stores them;
  * the one multiply-add it fuses, in the SiLU derivative, fused here too), so its result
  * is that chain's element for element.  All tensors are contiguous device fp32, 16-byte
@@ -210,6 +210,19 @@ int msq_rope_fwd(const float* x, const float* cos_t, const float* sin_t, int64_t
                  int32_t d, float* y, msq_stream_t stream);
 int msq_rope_bwd(const float* dy, const float* cos_t, const float* sin_t, int64_t t, int32_t heads,
                  int32_t d, float* dx, msq_stream_t stream);
+
+/* RMSNorm's pointwise tail.  r[t] = rsqrt(mean_c h[t][c]^2 + eps) is formed by the
+ * caller: it holds a reduction, which stays unfused.
+ *   h, y, dy, dh, hdot [t, d] (d % 4 == 0, d >= 4), r [t] (4-byte aligned), w [d] weights
+ *   forward   y = (h * r) * w
+ *   backward  g = dy * w;  dh = g * r;  hdot = g * h
+ * dh is the norm input's gradient through the scaling (its other part runs through r);
+ * the caller sums hdot over each row to get dr, the gradient of r.  The weights are
+ * frozen: no gradient for w. */
+int msq_rmsnorm_apply_fwd(const float* h, const float* r, const float* w, int64_t t, int64_t d,
+                          float* y, msq_stream_t stream);
+int msq_rmsnorm_apply_bwd(const float* dy, const float* h, const float* r, const float* w, int64_t t,
+                          int64_t d, float* dh, float* hdot, msq_stream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Host-to-device block-prefetch window.

@@ -9,7 +9,8 @@ run) but every call into the library raises -- there is no CPU fallback.
 from ._abi import MsqError, lib as _load_library  # noqa: F401
 from .ops import (BlockStreamWindow, Lora, Workspace, abi_version, nf4_codebook,  # noqa: F401
                   nf4_dequantize, nf4_lora_bwd, nf4_lora_fwd, nf4_lora_workspace_size,
-                  nf4_quantize, rng_key, rope_bwd, rope_fwd, swiglu_bwd, swiglu_fwd,
+                  nf4_quantize, rmsnorm_apply_bwd, rmsnorm_apply_fwd, rng_key, rope_bwd, rope_fwd,
+                  swiglu_bwd, swiglu_fwd,
                   timing_collect, timing_enable)
 
 try:

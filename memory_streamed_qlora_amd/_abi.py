@@ -75,6 +75,8 @@ _SIG = {
     "msq_swiglu_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P]),
     "msq_rope_fwd": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "msq_rope_bwd": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    "msq_rmsnorm_apply_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "msq_rmsnorm_apply_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P, _P, _P]),
     "block_stream_arena_bytes": (ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "block_stream_create": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
                                            ctypes.c_size_t, _P]),

@@ -345,4 +345,28 @@ int msq_rope_bwd(const float* dy, const float* cos_t, const float* sin_t, int64_
   return rope_entry("msq_rope_bwd", true, dy, cos_t, sin_t, t, heads, d, dx, stream);
 }
 
+static int rmsnorm_entry(const char* fn, bool backward, const float* dy, const float* h, const float* r,
+                         const float* w, int64_t t, int64_t d, float* out, float* hdot, msq_stream_t stream) {
+  if (t < 0 || d < 4 || d % 4 || (double)t * d > (double)(int64_t(1) << 40))
+    return set_error(MSQ_E_SHAPE, "%s: t = %lld, d = %lld (need t >= 0, d >= 4, d %% 4 == 0, t*d <= 2^40)", fn,
+                     (long long)t, (long long)d);
+  if (t == 0) return MSQ_OK;
+  if (!h || !r || !w || !out || (backward && (!dy || !hdot))) return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
+  if (!aligned(h, 16) || !aligned(r, 4) || !aligned(w, 16) || !aligned(out, 16) || !aligned(dy, 16) ||
+      !aligned(hdot, 16))
+    return set_error(MSQ_E_INVAL, "%s: misaligned pointer (16 bytes; r 4)", fn);
+  const hipError_t e = launch_rmsnorm_apply(backward, dy, h, r, w, t, d, out, hdot, (hipStream_t)stream);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
+}
+
+int msq_rmsnorm_apply_fwd(const float* h, const float* r, const float* w, int64_t t, int64_t d, float* y,
+                          msq_stream_t stream) {
+  return rmsnorm_entry("msq_rmsnorm_apply_fwd", false, nullptr, h, r, w, t, d, y, nullptr, stream);
+}
+
+int msq_rmsnorm_apply_bwd(const float* dy, const float* h, const float* r, const float* w, int64_t t, int64_t d,
+                          float* dh, float* hdot, msq_stream_t stream) {
+  return rmsnorm_entry("msq_rmsnorm_apply_bwd", true, dy, h, r, w, t, d, dh, hdot, stream);
+}
+
 }  // extern "C"

@@ -1,7 +1,8 @@
 // Pointwise block glue of the Qwen2.5 decoder layer, fused under the pages' rule for
 // kernels around the engine ("Poros" README, Roadmap, "The Poros kernel"): only
 // pointwise chains whose fused form yields the same per-element values qualify -- the
-// SwiGLU multiply, residual adds, rotary with precomputed tables.
+// SwiGLU multiply, residual adds, rotary with precomputed tables, and here also the
+// pointwise tail of RMSNorm (its mean stays an unfused reduction).
 //
 // Each kernel evaluates exactly the operations of the unfused chain it replaces, in the
 // same order and with the same roundings.  Contraction into fused multiply-adds is off
@@ -104,6 +105,39 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(const float* __restrict__
   dx[th * D + i + half] = g2 * cr[i + half] + (-(g1 * sr[i]));
 }
 
+// RMSNorm's pointwise tail, with r[t] = rsqrt(mean_c h[t][c]^2 + eps) formed outside (a
+// reduction, left unfused):  y = (h * r) * w.  Its backward, as the two unfused products'
+// gradients compute it: g = dy * w, dh = g * r, hdot = g * h (hdot is summed over c by the
+// caller into dr).  Rows of d elements, d % 4 == 0; thread i covers elements 4i .. 4i+3.
+__global__ __launch_bounds__(256) void rmsnorm_apply_fwd_kernel(const float* __restrict__ h,
+                                                                const float* __restrict__ r,
+                                                                const float* __restrict__ w, int64_t n, int64_t d,
+                                                                float* __restrict__ y) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  const float rt = r[e / d];
+  const float4 hv = *reinterpret_cast<const float4*>(h + e);
+  const float4 wv = *reinterpret_cast<const float4*>(w + e % d);
+  *reinterpret_cast<float4*>(y + e) =
+      make_float4((hv.x * rt) * wv.x, (hv.y * rt) * wv.y, (hv.z * rt) * wv.z, (hv.w * rt) * wv.w);
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_apply_bwd_kernel(const float* __restrict__ dy,
+                                                                const float* __restrict__ h,
+                                                                const float* __restrict__ r,
+                                                                const float* __restrict__ w, int64_t n, int64_t d,
+                                                                float* __restrict__ dh, float* __restrict__ hdot) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  const float rt = r[e / d];
+  const float4 gv = *reinterpret_cast<const float4*>(dy + e);
+  const float4 hv = *reinterpret_cast<const float4*>(h + e);
+  const float4 wv = *reinterpret_cast<const float4*>(w + e % d);
+  const float4 g = make_float4(gv.x * wv.x, gv.y * wv.y, gv.z * wv.z, gv.w * wv.w);
+  *reinterpret_cast<float4*>(dh + e) = make_float4(g.x * rt, g.y * rt, g.z * rt, g.w * rt);
+  *reinterpret_cast<float4*>(hdot + e) = make_float4(g.x * hv.x, g.y * hv.y, g.z * hv.z, g.w * hv.w);
+}
+
 }  // namespace
 
 // Algorithmic bytes: each fp32 operand read once and each result written once.
@@ -136,6 +170,20 @@ hipError_t launch_rope(bool backward, const float* x, const float* cs, const flo
                                  D, y)
                   : timed_launch("rope_fwd", shape, 0.0, bytes, rope_fwd_kernel, grid, dim3(256), s, x, cs, sn, T, H,
                                  D, y);
+}
+
+hipError_t launch_rmsnorm_apply(bool backward, const float* dy, const float* h, const float* r, const float* w,
+                                int64_t T, int64_t D, float* out, float* hdot, hipStream_t s) {
+  const int64_t n = T * D;
+  if (n == 0) return hipSuccess;
+  char shape[32];
+  snprintf(shape, sizeof(shape), "%lldx%lld", (long long)T, (long long)D);
+  const dim3 grid((unsigned)((n / 4 + 255) / 256));
+  if (backward)
+    return timed_launch("rmsnorm_apply_bwd", shape, 0.0, 16.0 * n + 4.0 * (T + D), rmsnorm_apply_bwd_kernel, grid,
+                        dim3(256), s, dy, h, r, w, n, D, out, hdot);
+  return timed_launch("rmsnorm_apply_fwd", shape, 0.0, 8.0 * n + 4.0 * (T + D), rmsnorm_apply_fwd_kernel, grid,
+                      dim3(256), s, h, r, w, n, D, out);
 }
 
 }  // namespace msq

@@ -110,6 +110,8 @@ hipError_t launch_swiglu_bwd(const float* da, const float* g, const float* u, in
                              hipStream_t s);
 hipError_t launch_rope(bool backward, const float* x, const float* cs, const float* sn, int64_t T, int H, int D,
                        float* y, hipStream_t s);
+hipError_t launch_rmsnorm_apply(bool backward, const float* dy, const float* h, const float* r, const float* w,
+                                int64_t T, int64_t D, float* out, float* hdot, hipStream_t s);
 
 
 // ---- timing -------------------------------------------------------------------

@@ -277,6 +277,31 @@ def rope_bwd(dy: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, stream=None
     return _rope("msq_rope_bwd", dy, cos, sin, stream)
 
 
+
+def rmsnorm_apply_fwd(h: torch.Tensor, r: torch.Tensor, w: torch.Tensor, stream=None) -> torch.Tensor:
+    """y = (h * r) * w for h [t, d], r [t, 1] (the row's reciprocal RMS), w [d]."""
+    t, d = h.shape
+    _req(h, "h", torch.float32, (t, d))
+    _req(r, "r", torch.float32, (t, 1))
+    _req(w, "w", torch.float32, (d,))
+    y = torch.empty_like(h)
+    check("msq_rmsnorm_apply_fwd", lib().msq_rmsnorm_apply_fwd(_ptr(h), _ptr(r), _ptr(w), t, d, _ptr(y),
+                                                               _stream(stream)))
+    return y
+
+
+def rmsnorm_apply_bwd(dy: torch.Tensor, h: torch.Tensor, r: torch.Tensor, w: torch.Tensor, stream=None):
+    """(dh, hdot): dh = (dy * w) * r, hdot = (dy * w) * h; the caller sums hdot per row for dr."""
+    t, d = h.shape
+    _req(dy, "dy", torch.float32, (t, d))
+    _req(h, "h", torch.float32, (t, d))
+    _req(r, "r", torch.float32, (t, 1))
+    _req(w, "w", torch.float32, (d,))
+    dh, hdot = torch.empty_like(h), torch.empty_like(h)
+    check("msq_rmsnorm_apply_bwd", lib().msq_rmsnorm_apply_bwd(_ptr(dy), _ptr(h), _ptr(r), _ptr(w), t, d,
+                                                               _ptr(dh), _ptr(hdot), _stream(stream)))
+    return dh, hdot
+
 class BlockStreamWindow:
     """block_stream_* over pinned host blobs and a caller-owned device arena."""
 

@@ -16,13 +16,14 @@ Resident mode runs the same code with every layer's blob already in device memor
 Every projection goes through the library (nf4_lora_fwd / nf4_lora_bwd) with fp32
 activations in and out; the library rounds them to bf16 only as the MFMA operand of
 the frozen-base product.  The pointwise glue -- the SwiGLU product, rotary embedding
-from precomputed tables and the two residual adds per block (fused into the output
-pass of the o and down projections) -- runs in the library too (glue="native"); each
+from precomputed tables, RMSNorm's scaling by the row's reciprocal RMS and the weights,
+and the two residual adds per block (fused into the output pass of the o and down
+projections) -- runs in the library too (glue="native"); each
 fused chain reproduces the unfused PyTorch chain element for element (the pages allow
 only such fusions, "Poros" README, Roadmap, "The Poros kernel"), and glue="torch" runs
-that unfused chain.  The rest -- RMSNorm, causal GQA attention, embedding gather,
-lm_head and cross-entropy, AdamW -- holds reductions, so it stays unfused fp32 PyTorch,
-deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and optimizer settings are
+that unfused chain.  The rest -- RMSNorm's mean, causal GQA attention, embedding
+gather, lm_head and cross-entropy, AdamW -- holds reductions, so it stays unfused fp32
+PyTorch, deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and optimizer settings are
 readings of the Qwen2 family and of textbook AdamW; the pages name neither.
 """
 from __future__ import annotations
@@ -153,6 +154,23 @@ class _SwiGLU(torch.autograd.Function):
         return ops.swiglu_bwd(da.contiguous(), g, u)
 
 
+class _RMSNormApply(torch.autograd.Function):
+    """y = (h * r) * w with r = the row's reciprocal RMS, computed outside by PyTorch."""
+
+    @staticmethod
+    def forward(ctx, h, r, w):
+        ctx.save_for_backward(h, r, w)
+        return ops.rmsnorm_apply_fwd(h, r, w)
+
+    @staticmethod
+    def backward(ctx, dy):
+        h, r, w = ctx.saved_tensors
+        dh, hdot = ops.rmsnorm_apply_bwd(dy.contiguous(), h, r, w)
+        # r's gradient: the row sum the product's own gradient takes (a reduction, in PyTorch)
+        dr = hdot.sum(-1, keepdim=True) if ctx.needs_input_grad[1] else None
+        return dh, dr, None
+
+
 class _RoPE(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, cos, sin):
@@ -169,7 +187,15 @@ class _RoPE(torch.autograd.Function):
 # block glue (fp32 except where it feeds the library in bf16)
 
 def rmsnorm(h: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """The unfused PyTorch chain."""
     return h * torch.rsqrt(torch.mean(h * h, dim=-1, keepdim=True) + EPS) * w
+
+
+def rmsnorm_native(h: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """The same chain with its pointwise tail fused in the library; the mean and rsqrt
+    (over [T, 1]) stay in PyTorch."""
+    r = torch.rsqrt(torch.mean(h * h, dim=-1, keepdim=True) + EPS)
+    return _RMSNormApply.apply(h, r, w)
 
 
 def rope_tables(T: int, D: int, device) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -331,7 +357,8 @@ class Stack:
         frozen-base product is skipped and the returned value is not the layer output."""
         sh = self.shape
         T = h.shape[0]
-        xn = rmsnorm(h, self.ln1[l])
+        norm = rmsnorm_native if self.glue == "native" else rmsnorm
+        xn = norm(h, self.ln1[l])
         q = self._lin(xn, l, views, "q", step, micro).view(T, sh.heads, sh.head_dim)
         k = self._lin(xn, l, views, "k", step, micro).view(T, sh.kv_heads, sh.head_dim)
         v = self._lin(xn, l, views, "v", step, micro).view(T, sh.kv_heads, sh.head_dim)
@@ -342,7 +369,7 @@ class Stack:
             q, k = rope(q, cos, sin), rope(k, cos, sin)
         att = causal_gqa_attention(q, k, v, self.mask_add[:T, :T])
         h1 = self._lin(att, l, views, "o", step, micro, residual=h)
-        xn2 = rmsnorm(h1, self.ln2[l])
+        xn2 = norm(h1, self.ln2[l])
         g = self._lin(xn2, l, views, "gate", step, micro)
         u = self._lin(xn2, l, views, "up", step, micro)
         a = _SwiGLU.apply(g, u) if self.glue == "native" else torch.nn.functional.silu(g) * u
@@ -380,7 +407,7 @@ class Stack:
                         self.window.prefetch(wins[wi + ahead])
         hf = h.detach().requires_grad_()
         with torch.enable_grad():
-            hn = rmsnorm(hf, self.lnf).to(torch.bfloat16)
+            hn = (rmsnorm_native if self.glue == "native" else rmsnorm)(hf, self.lnf).to(torch.bfloat16)
             logits = torch.matmul(hn, self.lm.t()).float()
             loss = torch.nn.functional.cross_entropy(logits[:-1], tokens[1:])
             loss.backward()

@@ -125,6 +125,12 @@ def test_glue_rejects_bad_arguments():
         assert fn(FAKE, FAKE, FAKE, 1 << 30, 1 << 10, 1 << 10, FAKE, None) == abi.MSQ_E_SHAPE
         assert fn(FAKE, None, FAKE, 4, 2, 64, FAKE, None) == abi.MSQ_E_INVAL
         assert fn(FAKE, FAKE, FAKE + 8, 4, 2, 64, FAKE, None) == abi.MSQ_E_INVAL
+    assert L.msq_rmsnorm_apply_fwd(None, None, None, 0, 64, None, None) == 0
+    assert L.msq_rmsnorm_apply_fwd(FAKE, FAKE, FAKE, 4, 6, FAKE, None) == abi.MSQ_E_SHAPE
+    assert L.msq_rmsnorm_apply_fwd(FAKE, FAKE, FAKE, -1, 64, FAKE, None) == abi.MSQ_E_SHAPE
+    assert L.msq_rmsnorm_apply_fwd(FAKE, FAKE + 2, FAKE, 4, 64, FAKE, None) == abi.MSQ_E_INVAL
+    assert L.msq_rmsnorm_apply_bwd(FAKE, FAKE, FAKE, FAKE, 4, 64, FAKE, None, None) == abi.MSQ_E_INVAL
+    assert L.msq_rmsnorm_apply_bwd(FAKE + 4, FAKE, FAKE, FAKE, 4, 64, FAKE, FAKE, None) == abi.MSQ_E_INVAL
 
 
 def test_workspace_size_depends_on_shape_only():

@@ -1,5 +1,5 @@
-"""Pointwise block glue in the library: SwiGLU, rotary embedding and the residual add
-fused into a projection's output pass.
+"""Pointwise block glue in the library: SwiGLU, rotary embedding, RMSNorm's pointwise
+tail and the residual add fused into a projection's output pass.
 
 The pages allow a fused kernel around the engine only when it is a pointwise chain that
 yields the unfused chain's values ("Poros" README, Roadmap, "The Poros kernel").  So each
@@ -94,6 +94,30 @@ def test_rope_bitwise_unfused_and_oracle(T, H, D):
         assert_parity(host_f64(got), want, tol=FP32_CHAIN_TOL, name=nm)
 
 
+@pytest.mark.parametrize("T,H", [(1, 4), (5, 64), (512, 896), (512, 5120), (77, 8192)])
+def test_rmsnorm_apply_bitwise_unfused_and_oracle(T, H):
+    """The whole RMSNorm with its pointwise tail fused equals the unfused chain, forward and
+    the input gradient through autograd (the mean and its gradient stay in PyTorch)."""
+    print(f"[rmsnorm] T={T} H={H}", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(T * 7 + H)
+    h = (torch.randn(T, H, generator=gen) * 2).cuda()
+    w = (1 + 0.02 * torch.randn(H, generator=gen)).cuda()
+    dy = torch.randn(T, H, generator=gen).cuda()
+    hn, hr = h.clone().requires_grad_(), h.clone().requires_grad_()
+    y = S.rmsnorm_native(hn, w)
+    ref = S.rmsnorm(hr, w)
+    y.backward(dy)
+    ref.backward(dy)
+    torch.cuda.synchronize()
+    assert _bits_equal(y.detach(), ref.detach()), "fused RMSNorm != the unfused chain"
+    assert _bits_equal(hn.grad, hr.grad), "fused RMSNorm backward != autograd of the unfused chain"
+    want_y, rinv = oblock.rmsnorm(host_f64(h), host_f64(w))
+    want_dx = oblock.rmsnorm_bwd(host_f64(h), host_f64(w), rinv, host_f64(dy))
+    for got, want, nm in ((y, want_y, "y"), (hn.grad, want_dx, "dx")):
+        assert_parity(host_f64(got), want, name=nm)
+        assert_parity(host_f64(got), want, tol=FP32_CHAIN_TOL, name=nm)
+
+
 def test_glue_rejects_bad_shapes():
     x = torch.zeros(4, 2, 6, device="cuda")
     cs = torch.zeros(4, 6, device="cuda")
@@ -105,6 +129,10 @@ def test_glue_rejects_bad_shapes():
     assert e.value.code == MSQ_E_SHAPE
     with pytest.raises(TypeError):
         msq.swiglu_fwd(torch.zeros(8, device="cuda", dtype=torch.bfloat16), torch.zeros(8, device="cuda"))
+    with pytest.raises(MsqError) as e:
+        msq.rmsnorm_apply_fwd(torch.zeros(3, 6, device="cuda"), torch.zeros(3, 1, device="cuda"),
+                              torch.zeros(6, device="cuda"))
+    assert e.value.code == MSQ_E_SHAPE
 
 
 # (t, k, n): the first shapes take a single-pass plan (4 k-steps admit no split), the
