@@ -72,6 +72,28 @@ def forward_backward(layers: List[Dict[str, object]], glob: Dict[str, np.ndarray
     return loss, grads
 
 
+def accumulated(layers: List[Dict[str, object]], glob: Dict[str, np.ndarray], toks_list,
+                shape, alpha: float, p: float, seed: int, step: int):
+    """Gradient accumulation over M micro-batches ("Poros" research post and "Current
+    limitations", "What 0.00e+00 means": accumulation at 2 and 4 micro-batches is part of
+    the parity surface).  Reading: one optimizer step sees the mean of the micro-batch
+    losses and its gradient, the mean of the micro-batch gradients; micro-batch m keys its
+    dropout masks with micro = m.  The order in which the micro-batches and blocks are
+    visited is not part of the definition.  Returns (mean loss, grads)."""
+    M = len(toks_list)
+    total, acc = 0.0, None
+    for m, toks in enumerate(toks_list):
+        loss, g = forward_backward(layers, glob, toks, shape, alpha, p, seed, step, micro=m)
+        total += loss
+        if acc is None:
+            acc = [{proj: (dA.astype(np.float64), dB.astype(np.float64)) for proj, (dA, dB) in gl.items()}
+                   for gl in g]
+        else:
+            acc = [{proj: (a[proj][0] + gl[proj][0], a[proj][1] + gl[proj][1]) for proj in a}
+                   for a, gl in zip(acc, g)]
+    return total / M, [{proj: (dA / M, dB / M) for proj, (dA, dB) in a.items()} for a in acc]
+
+
 def grad_norm(grads) -> float:
     s = 0.0
     for g in grads:

@@ -74,3 +74,63 @@ def test_grad_norm_is_l2_of_everything():
     flat = np.concatenate([np.concatenate([g[p][0].ravel(), g[p][1].ravel()])
                            for g in grads for p in block.PROJS])
     assert np.isclose(step.grad_norm(grads), np.linalg.norm(flat), rtol=1e-14)
+
+
+def _fd_stack(p_drop=0.1):
+    sh = mi.TINY
+    alpha = 8.0
+    layers = []
+    for li in range(sh.layers):
+        prm = mi.block_params(0, 89, li, sh, mi.LoraSpec(4, alpha, p_drop), w_std=0.2)
+        for proj in block.PROJS:
+            prm[proj]["B"] = (prm[proj]["B"] * 30).astype(np.float32)
+        layers.append(block.quantize_params(prm))
+    glob = mi.stack_globals(0, 89, sh, 8)
+    glob = {k: (v * 10 if k in ("emb", "lm") else v) for k, v in glob.items()}
+    return sh, alpha, layers, glob
+
+
+def test_accumulated_gradient_is_gradient_of_mean_loss():
+    """Finite differences of the mean loss over 2 micro-batches with dropout (each
+    micro-batch its own masks) against the accumulated gradient."""
+    sh, alpha, layers, glob = _fd_stack(0.1)
+    toks = [mi.tokens(0, 89, m, 8, sh.vocab) for m in range(2)]
+    loss, grads = step.accumulated(layers, glob, toks, sh, alpha, 0.1, 5, 2)
+    h = 1e-6
+    rng = np.random.default_rng(4)
+    for li, proj, name in [(0, "k", "A"), (1, "up", "B"), (1, "o", "A")]:
+        g = grads[li][proj][0 if name == "A" else 1]
+        idx = tuple(int(rng.integers(0, s)) for s in g.shape)
+
+        def with_delta(dlt):
+            ls = [dict(l) for l in layers]
+            ls[li] = {k: (dict(v) if isinstance(v, dict) else v) for k, v in layers[li].items()}
+            arr = layers[li][proj][name].astype(np.float64).copy()
+            arr[idx] += dlt
+            ls[li][proj][name] = arr
+            return step.accumulated(ls, glob, toks, sh, alpha, 0.1, 5, 2)[0]
+
+        fd = (with_delta(h) - with_delta(-h)) / (2 * h)
+        assert abs(fd - g[idx]) <= 1e-6 * max(1e-3, abs(fd)) + 1e-9, (li, proj, name, fd, g[idx])
+
+
+def test_accumulation_special_cases():
+    """Without dropout, M copies of one micro-batch give that micro-batch's loss and
+    gradient; with dropout the copies differ (micro keys the masks), and the result is the
+    mean of the separately computed micro-batch results."""
+    sh, alpha, layers, glob = _fd_stack(0.0)
+    t0 = mi.tokens(0, 89, 0, 8, sh.vocab)
+    l1, g1 = step.forward_backward(layers, glob, t0, sh, alpha, 0.0, 5, 0)
+    l4, g4 = step.accumulated(layers, glob, [t0] * 4, sh, alpha, 0.0, 5, 0)
+    assert abs(l4 - l1) <= 1e-14 * abs(l1)
+    for a, b in zip(g1, g4):
+        for proj in block.PROJS:
+            for i in range(2):
+                assert np.allclose(a[proj][i], b[proj][i], rtol=1e-13, atol=1e-18)
+    sh, alpha, layers, glob = _fd_stack(0.1)
+    la, ga = step.forward_backward(layers, glob, t0, sh, alpha, 0.1, 5, 0, micro=0)
+    lb, gb = step.forward_backward(layers, glob, t0, sh, alpha, 0.1, 5, 0, micro=1)
+    assert la != lb
+    l2, g2 = step.accumulated(layers, glob, [t0, t0], sh, alpha, 0.1, 5, 0)
+    assert abs(l2 - (la + lb) / 2) <= 1e-14 * abs(l2)
+    assert np.allclose(g2[1]["gate"][0], (ga[1]["gate"][0] + gb[1]["gate"][0]) / 2, rtol=1e-13, atol=1e-18)
