@@ -12,6 +12,9 @@ package README, "How it works"):
             the adapters and the block input only
   update    one AdamW step on the fp32 adapters, identical to the resident run's.
 Resident mode runs the same code with every layer's blob already in device memory.
+Gradient accumulation over M micro-batches runs micro-batch by micro-batch or
+block-major (every micro-batch through a window before the next window), with the
+same bits either way; dropout masks are keyed by the micro-batch index.
 
 Every projection goes through the library (nf4_lora_fwd / nf4_lora_bwd) with fp32
 activations in and out; the library rounds them to bf16 only as the MFMA operand of
@@ -386,50 +389,73 @@ class Stack:
 
     # -- the step ----------------------------------------------------------------------
     def forward_backward(self, tokens: torch.Tensor, step: int, micro: int = 0) -> torch.Tensor:
-        """Accumulates adapter gradients into .grad; returns the loss (device scalar)."""
+        """One micro-batch: accumulates adapter gradients into .grad; returns the loss
+        (device scalar)."""
+        return self._forward_backward([tokens], step, [micro], 1.0)[0]
+
+    def _forward_backward(self, toks: List[torch.Tensor], step: int, micros: List[int],
+                          scale: float) -> List[torch.Tensor]:
+        """Block-major pass over the micro-batches toks (dropout keys micros): each window is
+        fetched once and runs every micro-batch before the next window, forward and
+        backward.  Each micro-batch's loss is scaled by `scale` before its backward (1.0:
+        no scaling op); gradients accumulate into .grad, for every adapter in micro-batch
+        order.  Returns the unscaled losses."""
         L = self.shape.layers
+        M = len(toks)
         wins = self._windows()
         streamed = self.mode == "streamed"
-        h = self.emb[tokens].float()
-        bounds: List[torch.Tensor] = []
+        hs = [self.emb[t].float() for t in toks]
+        bounds: List[List[torch.Tensor]] = [[] for _ in range(M)]
         ahead = self.n_slots
         if streamed:
             for w in wins[:ahead]:
                 self.window.prefetch(w)
         with torch.no_grad():
             for wi, w in enumerate(wins):
-                for l in range(w, min(w + self.window_blocks, L)):
-                    bounds.append(h)
-                    h = self.layer_forward(h, l, self._views(l), step, micro)
+                layers = range(w, min(w + self.window_blocks, L))
+                views = {l: self._views(l) for l in layers}
+                for m in range(M):
+                    for l in layers:
+                        bounds[m].append(hs[m])
+                        hs[m] = self.layer_forward(hs[m], l, views[l], step, micros[m])
                 if streamed:
                     self.window.release(w)
                     if wi + ahead < len(wins):
                         self.window.prefetch(wins[wi + ahead])
-        hf = h.detach().requires_grad_()
-        with torch.enable_grad():
-            hn = (rmsnorm_native if self.glue == "native" else rmsnorm)(hf, self.lnf).to(torch.bfloat16)
-            logits = torch.matmul(hn, self.lm.t()).float()
-            loss = torch.nn.functional.cross_entropy(logits[:-1], tokens[1:])
-            loss.backward()
-        dh = hf.grad
-        del logits
+        dhs: List[torch.Tensor] = []
+        losses: List[torch.Tensor] = []
+        for m in range(M):
+            hf = hs[m].detach().requires_grad_()
+            with torch.enable_grad():
+                norm = rmsnorm_native if self.glue == "native" else rmsnorm
+                hn = norm(hf, self.lnf).to(torch.bfloat16)
+                logits = torch.matmul(hn, self.lm.t()).float()
+                loss = torch.nn.functional.cross_entropy(logits[:-1], toks[m][1:])
+                (loss if scale == 1.0 else loss * scale).backward()
+            dhs.append(hf.grad)
+            losses.append(loss.detach())
+            del logits
+        hs = None
         rw = wins[::-1]
         if streamed:
             for w in rw[:ahead]:
                 self.window.prefetch(w)
         for wi, w in enumerate(rw):
-            for l in reversed(range(w, min(w + self.window_blocks, L))):
-                x_in = bounds[l].detach().requires_grad_()
-                with torch.enable_grad():
-                    out = self.layer_forward(x_in, l, self._views(l), step, micro, recompute=True)
-                out.backward(dh)
-                dh = x_in.grad
-                bounds[l] = None
+            layers = range(w, min(w + self.window_blocks, L))
+            views = {l: self._views(l) for l in layers}
+            for m in range(M):
+                for l in reversed(layers):
+                    x_in = bounds[m][l].detach().requires_grad_()
+                    with torch.enable_grad():
+                        out = self.layer_forward(x_in, l, views[l], step, micros[m], recompute=True)
+                    out.backward(dhs[m])
+                    dhs[m] = x_in.grad
+                    bounds[m][l] = None
             if streamed:
                 self.window.release(w)
                 if wi + ahead < len(rw):
                     self.window.prefetch(rw[wi + ahead])
-        return loss.detach()
+        return losses
 
     def params(self) -> List[torch.nn.Parameter]:
         return [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
@@ -438,10 +464,32 @@ class Stack:
         grads = [p.grad for p in self.params() if p.grad is not None]
         return torch.linalg.vector_norm(torch.stack(torch._foreach_norm(grads)))
 
-    def train_step(self, tokens: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
-        """One optimizer step on one micro-batch; returns (loss, grad_norm) device scalars."""
+    def train_step(self, tokens: torch.Tensor, order: str = "block") -> Tuple[torch.Tensor, torch.Tensor]:
+        """One optimizer step; returns (loss, grad_norm) device scalars.
+
+        tokens [T]: one micro-batch.  tokens [M, T]: gradient accumulation over M
+        micro-batches (micro-batch m keys its dropout masks with micro = m), loss = the mean
+        of the micro-batch losses.  order "micro" runs the micro-batches one after another,
+        each streaming the whole base; "block" (block-major) runs all of them through each
+        window while it is resident, streaming the base once per optimizer step.  Both
+        orders give the same bits: every micro-batch computes the same values either way
+        and every adapter gradient is summed in micro-batch order."""
+        if order not in ("micro", "block"):
+            raise ValueError(f"order must be 'micro' or 'block', got {order!r}")
         self.opt.zero_grad(set_to_none=True)
-        loss = self.forward_backward(tokens, self.step_index)
+        if tokens.dim() == 1:
+            loss = self.forward_backward(tokens, self.step_index)
+        else:
+            M = tokens.shape[0]
+            scale = 1.0 / M
+            if order == "micro":
+                losses = [self._forward_backward([tokens[m]], self.step_index, [m], scale)[0] for m in range(M)]
+            else:
+                losses = self._forward_backward([tokens[m] for m in range(M)], self.step_index, list(range(M)),
+                                                scale)
+            loss = losses[0] * scale
+            for lm in losses[1:]:
+                loss = loss + lm * scale
         gn = self.grad_norm()
         self.opt.step()
         self.step_index += 1
