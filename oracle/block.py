@@ -15,8 +15,10 @@ the Poros kernel).  Block math is a reading of the Qwen2 architecture:
   xn2 = RMSNorm(x1; w2)
   out = x1 + down(SiLU(gate(xn2)) * up(xn2))
 
-Each projection draws its dropout mask from the key (seed, step, micro, layer,
-proj), so the recompute in the backward replays it ("Poros" research post, RNG
+The frozen base of each projection is NF4 (quantize_params) or kept in bf16
+(bf16_params, the pages' bf16 streaming variant).  Each projection draws its dropout
+mask from the key (seed, step, micro, layer, proj), so the recompute in the backward
+replays it ("Poros" research post, RNG
 state capture).  The backward is derived by hand and differentiates only the
 adapters and the block input (frozen norms, frozen base).
 """
@@ -41,6 +43,14 @@ def quantize_params(params: Dict[str, object]) -> Dict[str, object]:
         pp = params[proj]
         codes, a = nf4.quantize(pp["W"])
         q[proj] = {"codes": codes, "absmax": a, "bias": pp["bias"], "A": pp["A"], "B": pp["B"]}
+    q["ln1"] = params["ln1"]
+    q["ln2"] = params["ln2"]
+    return q
+
+
+def bf16_params(params: Dict[str, object]) -> Dict[str, object]:
+    """Keep each projection's bf16 W as the frozen base (no quantization)."""
+    q = {proj: {k: params[proj][k] for k in ("W", "bias", "A", "B")} for proj in PROJS}
     q["ln1"] = params["ln1"]
     q["ln2"] = params["ln2"]
     return q
@@ -130,6 +140,13 @@ def silu_grad(g):
     return sg * (1.0 + g * (1.0 - sg))
 
 
+def base_weight(pp: Dict[str, object]) -> np.ndarray:
+    """A projection's frozen base as values: the bf16 W, or the dequantized NF4 codes."""
+    if "W" in pp:
+        return pp["W"]
+    return nf4.dequantize(pp["codes"], pp["absmax"])
+
+
 def _key(rk: lora.RngKey, layer: int, proj: str) -> lora.RngKey:
     return lora.RngKey(seed=rk.seed, step=rk.step, micro=rk.micro, layer=layer,
                        proj=PROJ_ID[proj])
@@ -146,8 +163,8 @@ def forward(x, qp, shape, layer: int, alpha: float, p: float, rk: lora.RngKey):
 
     def lin(inp, proj):
         pp = qp[proj]
-        y, _ = lora.fwd(inp, pp["codes"], pp["absmax"], pp["bias"], pp["A"], pp["B"], alpha, p,
-                        _key(rk, layer, proj))
+        y, _ = lora.fwd_dense(inp, base_weight(pp), pp["bias"], pp["A"], pp["B"], alpha, p,
+                              _key(rk, layer, proj))
         return y
 
     q = lin(xn, "q").reshape(T, H, D)
@@ -181,8 +198,8 @@ def backward(dout, c, qp, shape, layer: int, alpha: float, p: float, rk: lora.Rn
 
     def lin_bwd(dy, inp, proj):
         pp = qp[proj]
-        dx, dA, dB = lora.bwd(dy, inp, pp["codes"], pp["absmax"], pp["A"], pp["B"], alpha, p,
-                              _key(rk, layer, proj))
+        dx, dA, dB = lora.bwd_dense(dy, inp, base_weight(pp), pp["A"], pp["B"], alpha, p,
+                                    _key(rk, layer, proj))
         grads[proj] = (dA, dB)
         return dx
 

@@ -16,8 +16,10 @@ Readings (the pages give only r and alpha -- rank 16, alpha 32 in the README
   * dA = du^T drop(x)
   * dx = dy W + sigma * keep (.) (du A)
   * no gradient for W, its absmax, or the bias (frozen).
-W here is the dequantized NF4 matrix.  All contractions run in float64 on
-exactly-represented inputs (bf16 x, fp32 A and B, bf16 dequantized W).
+W here is the dequantized NF4 matrix, or for a bf16 base ("Current limitations",
+"bf16 LoRA": the same streaming with the frozen base kept in bf16) the bf16 matrix
+itself.  All contractions run in float64 on exactly-represented inputs (bf16 x, fp32 A
+and B, bf16 W).
 """
 from __future__ import annotations
 
@@ -46,10 +48,11 @@ def lora_input(x: np.ndarray, p: float, key: RngKey) -> np.ndarray:
     return np.where(keep, x.astype(np.float64) * sigma, 0.0), keep, sigma
 
 
-def fwd(x: np.ndarray, codes: np.ndarray, absmax: np.ndarray, bias: Optional[np.ndarray],
-        A: np.ndarray, B: np.ndarray, alpha: float, p: float, key: RngKey):
-    """Returns (y, u) in float64.  r = A.shape[0]; r = 0 means base only."""
-    W = nf4.dequantize(codes, absmax).astype(np.float64)
+def fwd_dense(x: np.ndarray, W: np.ndarray, bias: Optional[np.ndarray], A: np.ndarray, B: np.ndarray,
+              alpha: float, p: float, key: RngKey):
+    """The layer with its frozen base given as values (bf16 W [N, K], or the dequantized
+    NF4 matrix).  Returns (y, u) in float64.  r = A.shape[0]; r = 0 means base only."""
+    W = W.astype(np.float64)
     y = x.astype(np.float64) @ W.T
     if bias is not None:
         y = y + bias.astype(np.float64)[None, :]
@@ -63,10 +66,10 @@ def fwd(x: np.ndarray, codes: np.ndarray, absmax: np.ndarray, bias: Optional[np.
     return y, u
 
 
-def bwd(dy: np.ndarray, x: np.ndarray, codes: np.ndarray, absmax: np.ndarray,
-        A: np.ndarray, B: np.ndarray, alpha: float, p: float, key: RngKey):
+def bwd_dense(dy: np.ndarray, x: np.ndarray, W: np.ndarray, A: np.ndarray, B: np.ndarray,
+              alpha: float, p: float, key: RngKey):
     """Returns (dx, dA, dB) in float64, replaying the forward's mask from the key."""
-    W = nf4.dequantize(codes, absmax).astype(np.float64)
+    W = W.astype(np.float64)
     dy64 = dy.astype(np.float64)
     dx = dy64 @ W
     r = A.shape[0]
@@ -80,3 +83,14 @@ def bwd(dy: np.ndarray, x: np.ndarray, codes: np.ndarray, absmax: np.ndarray,
     dA = du.T @ h
     dx = dx + sigma * np.where(keep, du @ A.astype(np.float64), 0.0)
     return dx, dA, dB
+
+
+def fwd(x: np.ndarray, codes: np.ndarray, absmax: np.ndarray, bias: Optional[np.ndarray],
+        A: np.ndarray, B: np.ndarray, alpha: float, p: float, key: RngKey):
+    """The NF4 layer: W is the dequantized matrix."""
+    return fwd_dense(x, nf4.dequantize(codes, absmax), bias, A, B, alpha, p, key)
+
+
+def bwd(dy: np.ndarray, x: np.ndarray, codes: np.ndarray, absmax: np.ndarray,
+        A: np.ndarray, B: np.ndarray, alpha: float, p: float, key: RngKey):
+    return bwd_dense(dy, x, nf4.dequantize(codes, absmax), A, B, alpha, p, key)

@@ -20,16 +20,16 @@ def _r16(x):
     return nf4.bf16_round(np.asarray(x, np.float32)).astype(np.float64)
 
 
-def _fwd(x, codes, a, bias, A, B, alpha, p, key):
-    W = nf4.dequantize(codes, a).astype(np.float64)
+def _fwd(x, W, bias, A, B, alpha, p, key):
+    W = W.astype(np.float64)
     y = _r16(x) @ W.T + (bias.astype(np.float64) if bias is not None else 0.0)
     h, _, _ = OL.lora_input(x, p, key)
     u = h @ A.astype(np.float64).T
     return y + alpha / A.shape[0] * (u @ B.astype(np.float64).T), u
 
 
-def _bwd(dy, x, codes, a, A, B, alpha, p, key):
-    W = nf4.dequantize(codes, a).astype(np.float64)
+def _bwd(dy, x, W, A, B, alpha, p, key):
+    W = W.astype(np.float64)
     s = alpha / A.shape[0]
     h, keep, sig = OL.lora_input(x, p, key)
     A64, B64 = A.astype(np.float64), B.astype(np.float64)
@@ -44,8 +44,8 @@ def test_bf16_operand_rounding_envelope(monkeypatch):
     glob = mi.stack_globals(seed, 3, TINY, T)
     toks = mi.tokens(seed, 3, 0, T, TINY.vocab)
     ref_loss, ref = step.forward_backward(layers, glob, toks, TINY, lo.alpha, lo.p_drop, seed, 0)
-    monkeypatch.setattr(block.lora, "fwd", _fwd)
-    monkeypatch.setattr(block.lora, "bwd", _bwd)
+    monkeypatch.setattr(block.lora, "fwd_dense", _fwd)
+    monkeypatch.setattr(block.lora, "bwd_dense", _bwd)
     loss, got = step.forward_backward(layers, glob, toks, TINY, lo.alpha, lo.p_drop, seed, 0)
     worst = max(np.max(np.abs(got[l][p][w] - ref[l][p][w])) / np.sqrt(np.mean(ref[l][p][w] ** 2))
                 for l in range(3) for p in block.PROJS for w in (0, 1))

@@ -134,3 +134,42 @@ def test_accumulation_special_cases():
     l2, g2 = step.accumulated(layers, glob, [t0, t0], sh, alpha, 0.1, 5, 0)
     assert abs(l2 - (la + lb) / 2) <= 1e-14 * abs(l2)
     assert np.allclose(g2[1]["gate"][0], (ga[1]["gate"][0] + gb[1]["gate"][0]) / 2, rtol=1e-13, atol=1e-18)
+
+
+def test_bf16_base_step():
+    """The bf16-base stack (frozen base kept in bf16): with W set to the dequantized NF4
+    matrices it reproduces the NF4 stack exactly, and with its own bf16 W its gradient
+    matches central differences of its loss."""
+    from oracle import nf4
+    sh, alpha, layers, glob = _fd_stack(0.1)
+    toks = mi.tokens(0, 89, 0, 8, sh.vocab)
+    as_bf16 = []
+    for qp in layers:
+        d = {proj: {"W": nf4.dequantize(qp[proj]["codes"], qp[proj]["absmax"]), "bias": qp[proj]["bias"],
+                    "A": qp[proj]["A"], "B": qp[proj]["B"]} for proj in block.PROJS}
+        d["ln1"], d["ln2"] = qp["ln1"], qp["ln2"]
+        as_bf16.append(d)
+    la, ga = step.forward_backward(layers, glob, toks, sh, alpha, 0.1, 5, 0)
+    lb, gb = step.forward_backward(as_bf16, glob, toks, sh, alpha, 0.1, 5, 0)
+    assert la == lb
+    for x, y in zip(ga, gb):
+        for proj in block.PROJS:
+            assert np.array_equal(x[proj][0], y[proj][0]) and np.array_equal(x[proj][1], y[proj][1])
+
+    bl = [block.bf16_params(mi.block_params(0, 90, li, sh, mi.LoraSpec(4, alpha, 0.1), w_std=0.2))
+          for li in range(sh.layers)]
+    for d in bl:
+        for proj in block.PROJS:
+            d[proj]["B"] = (d[proj]["B"] * 30).astype(np.float32)
+    loss, grads = step.forward_backward(bl, glob, toks, sh, alpha, 0.1, 5, 0)
+    h = 1e-6
+    for li, proj, name, idx in [(0, "v", "A", (1, 3)), (1, "down", "B", (5, 2))]:
+        def with_delta(dlt):
+            ls = [{k: (dict(v) if isinstance(v, dict) else v) for k, v in d.items()} for d in bl]
+            arr = bl[li][proj][name].astype(np.float64).copy()
+            arr[idx] += dlt
+            ls[li][proj][name] = arr
+            return step.forward_backward(ls, glob, toks, sh, alpha, 0.1, 5, 0)[0]
+        g = grads[li][proj][0 if name == "A" else 1][idx]
+        fd = (with_delta(h) - with_delta(-h)) / (2 * h)
+        assert abs(fd - g) <= 1e-6 * max(1e-3, abs(fd)) + 1e-9, (li, proj, name, fd, g)
