@@ -233,6 +233,8 @@ def main() -> int:
                     help="micro-batches of 512 tokens per optimizer step (gradient accumulation)")
     ap.add_argument("--order", choices=("block", "micro"), default="block",
                     help="accumulation loop order: block-major (one base stream per step) or micro-batch-major")
+    ap.add_argument("--base", choices=("nf4", "bf16"), default="nf4",
+                    help="frozen base format: NF4, or bf16 (the pages' bf16 streaming variant, 4x the bytes)")
     ap.add_argument("--glue", choices=("native", "torch"), default="native",
                     help="pointwise block glue: the library's fused kernels, or the unfused PyTorch chain")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -261,7 +263,8 @@ def main() -> int:
     def run(mode: str):
         t_build = time.time()
         st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=0.0,
-                            window_blocks=args.window_blocks, n_slots=args.slots, mode=mode, glue=args.glue)
+                            window_blocks=args.window_blocks, n_slots=args.slots, mode=mode, glue=args.glue,
+                            base=args.base)
         torch.cuda.synchronize()
         log(f"{mode}: built {args.layers} layers in {time.time() - t_build:.1f}s "
             f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
@@ -328,7 +331,8 @@ def main() -> int:
         "ms_per_step": round(ms, 2),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / (T / PAGES_A100_S_PER_STEP), 3) if args.layers == 64 and args.ga == 1 else None,
+        "vs_baseline": (round(value / (T / PAGES_A100_S_PER_STEP), 3)
+                        if args.layers == 64 and args.ga == 1 and args.base == "nf4" else None),
         "dtype": "bf16",
         "data": "synthetic (random N(0,0.02) NF4 base, random adapters, random tokens)",
         "config": {"workload": "Qwen2.5-32B-shaped streamed NF4+LoRA train step", "layers": args.layers,
@@ -338,7 +342,7 @@ def main() -> int:
                    "window": {"layers_resident": args.window_blocks * args.slots,
                               "slots": args.slots, "layers_per_slot": args.window_blocks},
                    "lora_r": 16, "lora_alpha": 32,
-                   "dropout": 0.0, "optimizer": "AdamW", "glue": args.glue, "parallelism": "single GPU"},
+                   "dropout": 0.0, "optimizer": "AdamW", "base": args.base, "glue": args.glue, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma" if avg_flops > 0 else "hbm", "kernel": name, "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(name), "avg_launch_ms": round(avg_ms, 4),

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 3
+#define MSQ_ABI_VERSION 4
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -177,6 +177,21 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
                  msq_lora_cfg cfg, msq_rng_key key, const float* u, void* dx,
                  int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
                  size_t workspace_bytes, msq_stream_t stream);
+
+/* The same layer over a frozen base kept in bf16 instead of NF4: the pages' bf16
+ * streaming variant, which streams the base blockwise like NF4 at 4x the bytes and is
+ * held to the same bitwise parity ("Current limitations", "bf16 LoRA").
+ *   w  [n, k] bf16, row-major, 16-byte aligned (replaces codes and absmax)
+ * Every other argument, the workspace (nf4_lora_workspace_size), the outputs, the
+ * dropout keys and the error behaviour are those of nf4_lora_fwd / nf4_lora_bwd. */
+int bf16_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint16_t* w,
+                  const uint16_t* bias, const void* residual, const float* A, const float* B,
+                  msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out, void* workspace,
+                  size_t workspace_bytes, msq_stream_t stream);
+int bf16_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n, const uint16_t* w,
+                  const float* A, const float* B, msq_lora_cfg cfg, msq_rng_key key, const float* u,
+                  void* dx, int dx_accumulate, float* dA, float* dB, int dAB_accumulate,
+                  void* workspace, size_t workspace_bytes, msq_stream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Pointwise block glue of a Qwen2.5-style decoder block, fp32.

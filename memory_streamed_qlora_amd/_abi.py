@@ -77,6 +77,11 @@ _SIG = {
     "msq_rope_bwd": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "msq_rmsnorm_apply_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P]),
     "msq_rmsnorm_apply_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P, _P, _P]),
+    "bf16_lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, LoraCfg, RngKey,
+                                     _P, _P, _P, ctypes.c_size_t, _P]),
+    "bf16_lora_bwd": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P, LoraCfg, RngKey, _P,
+                                     _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
+                                     _P]),
     "block_stream_arena_bytes": (ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "block_stream_create": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
                                            ctypes.c_size_t, _P]),
@@ -90,7 +95,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 3  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 4  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

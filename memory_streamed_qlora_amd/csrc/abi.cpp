@@ -167,25 +167,44 @@ size_t nf4_lora_workspace_size(int64_t t, int64_t k, int64_t n, int32_t r) {
   return std::max<size_t>(256, std::max(p.fwd_bytes, p.bwd_bytes));  // 0 is reserved for "invalid"
 }
 
-int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
-                 const float* absmax, const uint16_t* bias, const void* residual, const float* A,
-                 const float* B, msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out,
-                 void* workspace, size_t workspace_bytes, msq_stream_t stream) {
-  int rc = check_linear("nf4_lora_fwd", t, k, n, cfg, key);
+}  // extern "C"
+
+namespace {
+
+// The frozen base of one linear: NF4 (codes + absmax) or bf16 values; exactly one is set.
+struct Base {
+  const uint8_t* codes;
+  const float* absmax;
+  const uint16_t* wbf;
+};
+
+int check_base(const char* fn, const Base& b) {
+  if (b.wbf ? (b.codes || b.absmax) : (!b.codes || !b.absmax)) return set_error(MSQ_E_INVAL, "%s: null pointer (base)", fn);
+  if (!aligned(b.codes, 16) || !aligned(b.absmax, 4) || !aligned(b.wbf, 16))
+    return set_error(MSQ_E_INVAL, "%s: misaligned base (codes, bf16 W: 16 bytes; absmax 4)", fn);
+  return MSQ_OK;
+}
+
+int lora_fwd(const char* fn, const void* x, int64_t t, int64_t k, int64_t n, const Base& base,
+             const uint16_t* bias, const void* residual, const float* A, const float* B, msq_lora_cfg cfg,
+             msq_rng_key key, void* y, float* u_out, void* workspace, size_t workspace_bytes, msq_stream_t stream) {
+  int rc = check_linear(fn, t, k, n, cfg, key);
+  if (rc) return rc;
+  rc = check_base(fn, base);
   if (rc) return rc;
   const bool u_only = cfg.flags & MSQ_U_ONLY;
-  if (!codes || !absmax || !workspace || (t > 0 && (!x || (!y && !u_only))))
-    return set_error(MSQ_E_INVAL, "nf4_lora_fwd: null pointer");
+  if (!workspace || (t > 0 && (!x || (!y && !u_only))))
+    return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
   if (u_only && (cfg.r == 0 || !u_out))
-    return set_error(MSQ_E_INVAL, "nf4_lora_fwd: MSQ_U_ONLY needs r > 0 and u_out");
-  if (cfg.r > 0 && (!A || !B)) return set_error(MSQ_E_INVAL, "nf4_lora_fwd: r > 0 needs A and B");
-  if (u_only && residual) return set_error(MSQ_E_INVAL, "nf4_lora_fwd: MSQ_U_ONLY writes no y to add a residual to");
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(codes, 16) || !aligned(absmax, 4) || !aligned(bias, 8) ||
-      !aligned(residual, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(u_out, 4) || !aligned(workspace, 256))
-    return set_error(MSQ_E_INVAL, "nf4_lora_fwd: misaligned pointer (x, y, residual, codes, A, B: 16 bytes; bias 8; workspace 256)");
+    return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY needs r > 0 and u_out", fn);
+  if (cfg.r > 0 && (!A || !B)) return set_error(MSQ_E_INVAL, "%s: r > 0 needs A and B", fn);
+  if (u_only && residual) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY writes no y to add a residual to", fn);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(bias, 8) || !aligned(residual, 16) || !aligned(A, 16) ||
+      !aligned(B, 16) || !aligned(u_out, 4) || !aligned(workspace, 256))
+    return set_error(MSQ_E_INVAL, "%s: misaligned pointer (x, y, residual, A, B: 16 bytes; bias 8; workspace 256)", fn);
   const LoraPlan p = lora_plan(t, k, n, cfg.r);
   if (workspace_bytes < std::max(p.fwd_bytes, p.bwd_bytes))
-    return set_error(MSQ_E_WORKSPACE, "nf4_lora_fwd: workspace %zu < %zu bytes", workspace_bytes, std::max(p.fwd_bytes, p.bwd_bytes));
+    return set_error(MSQ_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, std::max(p.fwd_bytes, p.bwd_bytes));
   if (t == 0) return MSQ_OK;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -198,14 +217,15 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
   hipError_t e = hipSuccess;
   uint16_t* xb = u_only ? nullptr : (uint16_t*)(ws + p.off_act_fwd);
   e = launch_pack_lora(x, act_f32, t, k, A, 0, r, 1.0f, d, xb, (float*)(ws + p.off_sk_fwd), u, s);
-  if (u_only) return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
+  if (u_only) return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
 
   if (e == hipSuccess) {
     GemmLaunch L;
     L.mode = 0;
     L.act = xb;
-    L.codes = codes;
-    L.absmax = absmax;
+    L.codes = base.codes;
+    L.absmax = base.absmax;
+    L.wbf = base.wbf;
     L.M = t;
     L.N = n;
     L.K = k;
@@ -223,29 +243,29 @@ int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* 
   }
   if (e == hipSuccess && p.fwd.splits > 1)
     e = launch_split_reduce(part, p.fwd.splits, t, n, bias, residual, true, y, out_f32, s);
-  return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_fwd launch");
+  return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
 }
 
-int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
-                 const uint8_t* codes, const float* absmax, const float* A, const float* B,
-                 msq_lora_cfg cfg, msq_rng_key key, const float* u, void* dx,
-                 int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
-                 size_t workspace_bytes, msq_stream_t stream) {
-  int rc = check_linear("nf4_lora_bwd", t, k, n, cfg, key);
+int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k, int64_t n, const Base& base,
+             const float* A, const float* B, msq_lora_cfg cfg, msq_rng_key key, const float* u, void* dx,
+             int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace, size_t workspace_bytes,
+             msq_stream_t stream) {
+  int rc = check_linear(fn, t, k, n, cfg, key);
   if (rc) return rc;
-  if (!codes || !absmax || !workspace || (t > 0 && (!dy || !x || !dx)))
-    return set_error(MSQ_E_INVAL, "nf4_lora_bwd: null pointer");
-  if (cfg.r > 0 && (!A || !B || !dA || !dB)) return set_error(MSQ_E_INVAL, "nf4_lora_bwd: r > 0 needs A, B, dA, dB");
-  if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "nf4_lora_bwd: MSQ_U_ONLY is a forward flag");
+  rc = check_base(fn, base);
+  if (rc) return rc;
+  if (!workspace || (t > 0 && (!dy || !x || !dx)))
+    return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
+  if (cfg.r > 0 && (!A || !B || !dA || !dB)) return set_error(MSQ_E_INVAL, "%s: r > 0 needs A, B, dA, dB", fn);
+  if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY is a forward flag", fn);
   if ((dx_accumulate != 0 && dx_accumulate != 1) || (dAB_accumulate != 0 && dAB_accumulate != 1))
-    return set_error(MSQ_E_INVAL, "nf4_lora_bwd: accumulate flags must be 0 or 1");
-  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16) || !aligned(codes, 16) || !aligned(absmax, 4) ||
-      !aligned(A, 16) || !aligned(B, 16) || !aligned(u, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
-      !aligned(workspace, 256))
-    return set_error(MSQ_E_INVAL, "nf4_lora_bwd: misaligned pointer (dy, x, dx, codes, A, B: 16 bytes; workspace 256)");
+    return set_error(MSQ_E_INVAL, "%s: accumulate flags must be 0 or 1", fn);
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16) || !aligned(A, 16) || !aligned(B, 16) ||
+      !aligned(u, 4) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(workspace, 256))
+    return set_error(MSQ_E_INVAL, "%s: misaligned pointer (dy, x, dx, A, B: 16 bytes; workspace 256)", fn);
   const LoraPlan p = lora_plan(t, k, n, cfg.r);
   if (workspace_bytes < std::max(p.fwd_bytes, p.bwd_bytes))
-    return set_error(MSQ_E_WORKSPACE, "nf4_lora_bwd: workspace %zu < %zu bytes", workspace_bytes, std::max(p.fwd_bytes, p.bwd_bytes));
+    return set_error(MSQ_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, std::max(p.fwd_bytes, p.bwd_bytes));
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int r = cfg.r;
@@ -269,8 +289,9 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
       GemmLaunch L;
       L.mode = 1;
       L.act = dyb;
-      L.codes = codes;
-      L.absmax = absmax;
+      L.codes = base.codes;
+      L.absmax = base.absmax;
+      L.wbf = base.wbf;
       L.M = t;
       L.N = n;
       L.K = k;
@@ -298,7 +319,48 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
     e = launch_colgrad_reduce((float*)(ws + p.off_pa), p.nch, r, k, 1.0f, false, dA, dAB_accumulate, s);
   if (e == hipSuccess && r > 0)
     e = launch_colgrad_reduce((float*)(ws + p.off_pb), p.nch, r, n, lscale, true, dB, dAB_accumulate, s);
-  return e == hipSuccess ? MSQ_OK : hip_error(e, "nf4_lora_bwd launch");
+  return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int nf4_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
+                 const float* absmax, const uint16_t* bias, const void* residual, const float* A,
+                 const float* B, msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out,
+                 void* workspace, size_t workspace_bytes, msq_stream_t stream) {
+  if (!codes || !absmax) return set_error(MSQ_E_INVAL, "nf4_lora_fwd: null pointer (codes, absmax)");
+  return lora_fwd("nf4_lora_fwd", x, t, k, n, Base{codes, absmax, nullptr}, bias, residual, A, B, cfg, key, y,
+                  u_out, workspace, workspace_bytes, stream);
+}
+
+int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
+                 const uint8_t* codes, const float* absmax, const float* A, const float* B,
+                 msq_lora_cfg cfg, msq_rng_key key, const float* u, void* dx,
+                 int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
+                 size_t workspace_bytes, msq_stream_t stream) {
+  if (!codes || !absmax) return set_error(MSQ_E_INVAL, "nf4_lora_bwd: null pointer (codes, absmax)");
+  return lora_bwd("nf4_lora_bwd", dy, x, t, k, n, Base{codes, absmax, nullptr}, A, B, cfg, key, u, dx,
+                  dx_accumulate, dA, dB, dAB_accumulate, workspace, workspace_bytes, stream);
+}
+
+int bf16_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint16_t* w,
+                  const uint16_t* bias, const void* residual, const float* A, const float* B,
+                  msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out, void* workspace,
+                  size_t workspace_bytes, msq_stream_t stream) {
+  if (!w) return set_error(MSQ_E_INVAL, "bf16_lora_fwd: null pointer (w)");
+  return lora_fwd("bf16_lora_fwd", x, t, k, n, Base{nullptr, nullptr, w}, bias, residual, A, B, cfg, key, y,
+                  u_out, workspace, workspace_bytes, stream);
+}
+
+int bf16_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n, const uint16_t* w,
+                  const float* A, const float* B, msq_lora_cfg cfg, msq_rng_key key, const float* u,
+                  void* dx, int dx_accumulate, float* dA, float* dB, int dAB_accumulate,
+                  void* workspace, size_t workspace_bytes, msq_stream_t stream) {
+  if (!w) return set_error(MSQ_E_INVAL, "bf16_lora_bwd: null pointer (w)");
+  return lora_bwd("bf16_lora_bwd", dy, x, t, k, n, Base{nullptr, nullptr, w}, A, B, cfg, key, u, dx,
+                  dx_accumulate, dA, dB, dAB_accumulate, workspace, workspace_bytes, stream);
 }
 
 int msq_swiglu_fwd(const float* g, const float* u, int64_t n, float* a, msq_stream_t stream) {

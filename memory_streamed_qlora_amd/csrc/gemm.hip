@@ -7,7 +7,10 @@
 // up four at a time with v_perm, and writes the bf16 tile into LDS in the layout the
 // MFMA operand reads want; the contraction runs on v_mfma_f32_32x32x16_bf16 with fp32
 // accumulation.  The pages' base is frozen (never differentiated: "Poros" research
-// post, training-step paragraph), so there is no dW kernel.
+// post, training-step paragraph), so there is no dW kernel.  The bf16_* kernels are the
+// same GEMMs over a base kept in bf16 (the pages' bf16 streaming variant, "Current
+// limitations", "bf16 LoRA"): each thread loads its 16 bf16 values of the tile and
+// stores them into the same LDS layout, with no dequantization.
 //
 // Tile: BM=512 rows of t x BN=128 output columns x BK=64 reduction, 512 threads = 8
 // waves; wave w owns rows 64w..64w+63 and all 128 columns (2x4 MFMA 32x32 blocks).
@@ -36,7 +39,7 @@ constexpr int THREADS = 512;  // 8 waves, one per 64 rows
 
 struct GemmArgs {
   const uint16_t* act;   // [M][R] bf16
-  const uint8_t* codes;  // [N][K/2]
+  const uint8_t* codes;  // [N][K/2]   NF4 base
   const float* absmax;   // [N][K/64]
   int64_t M, N, K;       // W is [N][K]
   int64_t R, Nc;         // reduction length and output columns
@@ -58,6 +61,7 @@ struct GemmArgs {
   const void* addend;  // [M][Nc] in the output's type, may equal out
   void* out;
   int out_f32;
+  const uint16_t* wbf;  // [N][K] bf16 base (the bf16 kernels; NULL for NF4)
 };
 
 // Eight fp32 values -> hi and lo bf16 MFMA operands, hi = rne(v), lo = rne(v - hi), so
@@ -120,7 +124,19 @@ __device__ __forceinline__ uint32_t keep_rows16(const Dropout& d, int64_t mrow0,
   return bits;
 }
 
-template <int MODE, bool DROP>
+// One k-step's share of the W tile held in registers by one thread: 16 NF4 codes and
+// their block's absmax, or 16 bf16 values.
+template <bool BF16W>
+struct WShare {
+  uint2 q;
+  float s;
+};
+template <>
+struct WShare<true> {
+  uint4 q[2];
+};
+
+template <int MODE, bool DROP, bool BF16W>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[3][BN * LDW];
 
@@ -160,43 +176,59 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const uint16_t* ap0 = g.act + min(mw / 32, ngrp - 1) * g.steps * 2048 + lane * 8;
     const uint16_t* ap1 = g.act + min(mw / 32 + 1, ngrp - 1) * g.steps * 2048 + lane * 8;
 
-    // NF4 source of this thread's share of the W tile (clamped like the rows above):
-    // 16 codes, one 8-byte load per k-step.
-    //   forward:  W row n0 + (tid >> 2), codes 16*(tid & 3) .. +15 of the step's block
+    // Source of this thread's share of the W tile (clamped like the rows above): 16
+    // elements per k-step, as NF4 codes (one 8-byte load + the block's absmax) or bf16
+    // values (two 16-byte loads).
+    //   forward:  W row n0 + (tid >> 2), elements 16*(tid & 3) .. +15 of the step's block
     //   backward: reduction row `lane` of the step, output columns n0 + 16*wave .. +15
-    const uint8_t* cbase;
-    const float* sbase;
-    int64_t cstride, sstride;
+    const uint8_t* cbase = nullptr;
+    const float* sbase = nullptr;
+    const uint16_t* wbase = nullptr;
+    int64_t cstride = 0, sstride = 0, wstride = 0;
     if (MODE == 0) {
       const int64_t wn = min(n0 + (tid >> 2), g.Nc - 1);
-      cbase = g.codes + wn * (g.K / 2) + 8 * (tid & 3);
-      sbase = g.absmax + wn * (g.K / 64);
-      cstride = BK / 2;
-      sstride = 1;
+      if constexpr (BF16W) {
+        wbase = g.wbf + wn * g.K + 16 * (tid & 3);
+        wstride = BK;
+      } else {
+        cbase = g.codes + wn * (g.K / 2) + 8 * (tid & 3);
+        sbase = g.absmax + wn * (g.K / 64);
+        cstride = BK / 2;
+        sstride = 1;
+      }
     } else {
       const int64_t col = n0 + 16 * wave < g.Nc ? n0 + 16 * wave : 0;
-      cbase = g.codes + (int64_t)lane * (g.K / 2) + col / 2;
-      sbase = g.absmax + (int64_t)lane * (g.K / 64) + col / 64;
-      cstride = (int64_t)BK * (g.K / 2);
-      sstride = (int64_t)BK * (g.K / 64);
+      if constexpr (BF16W) {
+        wbase = g.wbf + (int64_t)lane * g.K + col;
+        wstride = (int64_t)BK * g.K;
+      } else {
+        cbase = g.codes + (int64_t)lane * (g.K / 2) + col / 2;
+        sbase = g.absmax + (int64_t)lane * (g.K / 64) + col / 64;
+        cstride = (int64_t)BK * (g.K / 2);
+        sstride = (int64_t)BK * (g.K / 64);
+      }
     }
 
-    uint4 a[2][4];     // activation operand of the current k-step, refilled per sub-step
-    uint2 qa, qb;      // NF4 codes of this thread's share, alternating between k-steps ...
-    float sa, sb;      // ... and their block's absmax
+    uint4 a[2][4];            // activation operand of the current k-step, refilled per sub-step
+    WShare<BF16W> qa, qb;     // this thread's W share, alternating between k-steps
     auto load_a = [&](int step, int c) {
       const int64_t o = ((int64_t)step * 4 + c) * 512;
       a[0][c] = *reinterpret_cast<const uint4*>(ap0 + o);
       a[1][c] = *reinterpret_cast<const uint4*>(ap1 + o);
     };
-    auto load_w = [&](uint2& q, float& qs, int step) {
-      q = *reinterpret_cast<const uint2*>(cbase + (int64_t)step * cstride);
-      qs = sbase[(int64_t)step * sstride];
+    auto load_w = [&](WShare<BF16W>& w, int step) {
+      if constexpr (BF16W) {
+        const uint16_t* p = wbase + (int64_t)step * wstride;
+        w.q[0] = *reinterpret_cast<const uint4*>(p);
+        w.q[1] = *reinterpret_cast<const uint4*>(p + 8);
+      } else {
+        w.q = *reinterpret_cast<const uint2*>(cbase + (int64_t)step * cstride);
+        w.s = sbase[(int64_t)step * sstride];
+      }
     };
-    // Eight codes (dword h of this thread's share) -> bf16 into LDS buffer `buf`.
-    auto dequant_store = [&](const Nf4Planes& P, uint32_t w, int h, int buf) {
-      uint32_t out[4];
-      nf4_dequant8(P, w, out);
+    // Eight bf16 values (elements 8h .. 8h+7 of this thread's share, packed in pairs)
+    // into LDS buffer `buf`.
+    auto store8 = [&](const uint32_t (&out)[4], int h, int buf) {
       if (MODE == 0) {
         *reinterpret_cast<uint4*>(&sB[buf][(tid >> 2) * LDW + 16 * (tid & 3) + 8 * h]) =
             make_uint4(out[0], out[1], out[2], out[3]);
@@ -206,6 +238,26 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) dst[e * LDW] = (uint16_t)((e & 1) ? (out[e >> 1] >> 16) : out[e >> 1]);
       }
+    };
+    // Half h of a share -> bf16 in LDS: eight codes dequantized through the block's
+    // planes, or eight bf16 values stored as they are.
+    auto fill = [&](const Nf4Planes& P, const WShare<BF16W>& w, int h, int buf) {
+      uint32_t out[4];
+      if constexpr (BF16W) {
+        const uint4 v = w.q[h];
+        out[0] = v.x;
+        out[1] = v.y;
+        out[2] = v.z;
+        out[3] = v.w;
+      } else {
+        nf4_dequant8(P, h ? w.q.y : w.q.x, out);
+      }
+      store8(out, h, buf);
+    };
+    auto planes = [&](const WShare<BF16W>& w) {
+      Nf4Planes P;
+      if constexpr (!BF16W) P = nf4_planes(g.lut, w.s);
+      return P;
     };
     auto read_b = [&](bf16x8_t(&b)[4], int c, int buf) {
 #pragma unroll
@@ -235,24 +287,24 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     // fetches are clamped onto the last step and never read).
     bf16x8_t b0[4];
     int cur = 0;  // LDS buffer of the current tile
-    auto kstep = [&](int step, const uint2& qc, float qsc, uint2& qn, float& qsn) {
+    auto kstep = [&](int step, const WShare<BF16W>& qc, WShare<BF16W>& qn) {
       const int nxt = min(step + 1, s_end - 1);
       const int b_next = cur == 2 ? 0 : cur + 1, b_fill = b_next == 2 ? 0 : b_next + 1;
-      load_w(qn, qsn, min(step + 3, s_end - 1));
+      load_w(qn, min(step + 3, s_end - 1));
       Nf4Planes P;
       bf16x8_t b1[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         __builtin_amdgcn_sched_barrier(0);
-        if (c == 0) P = nf4_planes(g.lut, qsc);
+        if (c == 0) P = planes(qc);
         if (c < 3)
           read_b((c & 1) ? b0 : b1, c + 1, cur);
         else
           read_b(b0, 0, b_next);  // tile s+1 is complete: its first operands load under these MFMAs
         mfma_sub((c & 1) ? b1 : b0, c);
         load_a(nxt, c);
-        if (c == 1) dequant_store(P, qc.x, 0, b_fill);
-        if (c == 2) dequant_store(P, qc.y, 1, b_fill);
+        if (c == 1) fill(P, qc, 0, b_fill);
+        if (c == 2) fill(P, qc, 1, b_fill);
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
@@ -264,28 +316,27 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     // flight, so the wait counts the compiler derives at the loop head hold on entry
     // as well as on the back edge.
     {
-      uint2 t0, t1;
-      float ts0, ts1;
-      load_w(t0, ts0, s_begin);
-      load_w(t1, ts1, min(s_begin + 1, s_end - 1));
-      load_w(qa, sa, min(s_begin + 2, s_end - 1));
+      WShare<BF16W> t0, t1;
+      load_w(t0, s_begin);
+      load_w(t1, min(s_begin + 1, s_end - 1));
+      load_w(qa, min(s_begin + 2, s_end - 1));
 #pragma unroll
       for (int c = 0; c < 4; ++c) load_a(s_begin, c);
-      const Nf4Planes P0 = nf4_planes(g.lut, ts0);
-      dequant_store(P0, t0.x, 0, 0);
-      dequant_store(P0, t0.y, 1, 0);
-      const Nf4Planes P1 = nf4_planes(g.lut, ts1);
-      dequant_store(P1, t1.x, 0, 1);
-      dequant_store(P1, t1.y, 1, 1);
+      const Nf4Planes P0 = planes(t0);
+      fill(P0, t0, 0, 0);
+      fill(P0, t0, 1, 0);
+      const Nf4Planes P1 = planes(t1);
+      fill(P1, t1, 0, 1);
+      fill(P1, t1, 1, 1);
     }
     __syncthreads();
     read_b(b0, 0, 0);
     int step = s_begin;
     for (; step + 1 < s_end; step += 2) {
-      kstep(step, qa, sa, qb, sb);
-      kstep(step + 1, qb, sb, qa, sa);
+      kstep(step, qa, qb);
+      kstep(step + 1, qb, qa);
     }
-    if (step < s_end) kstep(step, qa, sa, qb, sb);
+    if (step < s_end) kstep(step, qa, qb);
   }
 
   // ---- LoRA term: one extra MFMA k-step per 16 ranks, operands split hi/lo ---------------
@@ -399,9 +450,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
 }
 
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nf4_fwd_gemm(GemmArgs g) { gemm_body<0, false>(g); }
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nf4_bwd_gemm(GemmArgs g) { gemm_body<1, false>(g); }
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void nf4_bwd_gemm_dropout(GemmArgs g) { gemm_body<1, true>(g); }
+#define MSQ_GEMM_KERNEL(name, MODE, DROP, BF16W) \
+  __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2))) void name(GemmArgs g) { \
+    gemm_body<MODE, DROP, BF16W>(g);                                                                       \
+  }
+MSQ_GEMM_KERNEL(nf4_fwd_gemm, 0, false, false)
+MSQ_GEMM_KERNEL(nf4_bwd_gemm, 1, false, false)
+MSQ_GEMM_KERNEL(nf4_bwd_gemm_dropout, 1, true, false)
+MSQ_GEMM_KERNEL(bf16_fwd_gemm, 0, false, true)
+MSQ_GEMM_KERNEL(bf16_bwd_gemm, 1, false, true)
+MSQ_GEMM_KERNEL(bf16_bwd_gemm_dropout, 1, true, true)
+#undef MSQ_GEMM_KERNEL
 
 }  // namespace
 
@@ -435,6 +494,7 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   g.act = L.act;
   g.codes = L.codes;
   g.absmax = L.absmax;
+  g.wbf = L.wbf;
   g.M = L.M;
   g.N = L.N;
   g.K = L.K;
@@ -457,20 +517,23 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   if (g.M < 1 || g.Nc < 1 || g.R % BK || g.K % 64 || g.steps != (int)(g.R / BK)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)g.splits);
   const double flops = 2.0 * (double)g.M * (double)g.N * (double)g.K;
+  const bool bf = L.wbf != nullptr;
+  if (bf == (L.codes != nullptr)) return hipErrorInvalidValue;  // exactly one base format
   void (*kern)(GemmArgs);
   const char* name;
   if (L.mode == 0) {
-    kern = nf4_fwd_gemm;
-    name = "nf4_fwd_gemm";
+    kern = bf ? bf16_fwd_gemm : nf4_fwd_gemm;
+    name = bf ? "bf16_fwd_gemm" : "nf4_fwd_gemm";
   } else if (L.r > 0 && L.drop.threshold != 0u) {
-    kern = nf4_bwd_gemm_dropout;
-    name = "nf4_bwd_gemm";
+    kern = bf ? bf16_bwd_gemm_dropout : nf4_bwd_gemm_dropout;
+    name = bf ? "bf16_bwd_gemm" : "nf4_bwd_gemm";
   } else {
-    kern = nf4_bwd_gemm;
-    name = "nf4_bwd_gemm";
+    kern = bf ? bf16_bwd_gemm : nf4_bwd_gemm;
+    name = bf ? "bf16_bwd_gemm" : "nf4_bwd_gemm";
   }
-  // algorithmic bytes: NF4 codes + scales, the packed activation, the output (or split partials)
-  const double bytes = (double)g.N * g.K * 0.5625 + (double)frag_rows(g.M) * g.R * 2 +
+  // algorithmic bytes: the base (NF4 codes + scales, or bf16), the packed activation, the
+  // output (or split partials)
+  const double bytes = (double)g.N * g.K * (bf ? 2.0 : 0.5625) + (double)frag_rows(g.M) * g.R * 2 +
                        (double)g.M * g.Nc * (g.splits > 1 ? 4.0 * g.splits : (g.out_f32 ? 4.0 : 2.0) * (g.addend ? 2 : 1));
   char shape[32];
   snprintf(shape, sizeof(shape), "%lldx%lldx%lld", (long long)L.M, (long long)L.N, (long long)L.K);

@@ -56,8 +56,9 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 struct GemmLaunch {
   int mode;
   const uint16_t* act;  // packed by launch_pack_lora
-  const uint8_t* codes;
+  const uint8_t* codes;  // NF4 base (codes + absmax), or
   const float* absmax;
+  const uint16_t* wbf = nullptr;  // bf16 base [N][K]: exactly one of codes / wbf is set
   int64_t M, N, K;
   GemmPlan plan;
   const float* lu;

@@ -137,26 +137,26 @@ def rng_key(seed: int = 0, step: int = 0, micro: int = 0, layer: int = 0, proj: 
     return RngKey(seed, step, micro, layer, proj)
 
 
-def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
-                 bias: Optional[torch.Tensor], A: Optional[torch.Tensor], B: Optional[torch.Tensor],
-                 cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
-                 u_out: Optional[torch.Tensor] = None, want_u: bool = True,
-                 workspace: Optional[Workspace] = None, stream=None,
-                 out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
-                 residual: Optional[torch.Tensor] = None):
-    """y = [residual +] (x W^T + bias + (alpha/r) drop(x) A^T B^T).  Returns (y, u) (u None
-    if not wanted).
+def _base_args(base: Tuple[torch.Tensor, ...], k: int) -> Tuple[str, int, list]:
+    """(entry-point prefix, n, pointer arguments) for an NF4 (codes, absmax) or bf16 (w,) base."""
+    if len(base) == 2:
+        codes, absmax = base
+        n = codes.shape[0]
+        _req(codes, "codes", torch.uint8, (n, k // 2))
+        _req(absmax, "absmax", torch.float32, (n, k // 64))
+        return "nf4", n, [_ptr(codes), _ptr(absmax)]
+    (w,) = base
+    n = w.shape[0]
+    _req(w, "w", torch.bfloat16, (n, k))
+    return "bf16", n, [_ptr(w)]
 
-    x may be bf16 or fp32; y is out_dtype (default: x's dtype, or y's if given).
-    residual ([t, n], y's dtype) is added in the output pass, rounded as a separate add.
-    u_only: compute only u (y is None)."""
+
+def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype, u_only, residual):
     t, k = x.shape
-    n = codes.shape[0]
     _req(x, "x", x.dtype, (t, k))
+    fmt, n, bptr = _base_args(base, k)
     out_dtype = out_dtype or (y.dtype if y is not None else x.dtype)
     flags = _flags(x.dtype, out_dtype)
-    _req(codes, "codes", torch.uint8, (n, k // 2))
-    _req(absmax, "absmax", torch.float32, (n, k // 64))
     if bias is not None:
         _req(bias, "bias", torch.bfloat16, (n,))
     r = cfg.r
@@ -183,31 +183,22 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
         _req(u_out, "u_out", torch.float32, (t, r))
     need = nf4_lora_workspace_size(t, k, n, r)
     ws = _workspace(x.device, need, workspace)
-    check("nf4_lora_fwd", lib().nf4_lora_fwd(
-        _ptr(x), t, k, n, _ptr(codes), _ptr(absmax), _ptr(bias), _ptr(residual),
-        _ptr(A) if r > 0 else None,
+    fn = f"{fmt}_lora_fwd"
+    check(fn, getattr(lib(), fn)(
+        _ptr(x), t, k, n, *bptr, _ptr(bias), _ptr(residual), _ptr(A) if r > 0 else None,
         _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(),
         _stream(stream)))
     return y, u_out
 
 
-def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
-                 A: Optional[torch.Tensor], B: Optional[torch.Tensor], cfg: Lora, key: RngKey,
-                 u: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
-                 dx_accumulate: bool = False, dA: Optional[torch.Tensor] = None,
-                 dB: Optional[torch.Tensor] = None, dAB_accumulate: bool = False,
-                 workspace: Optional[Workspace] = None, stream=None,
-                 out_dtype: Optional[torch.dtype] = None):
-    """Returns (dx, dA, dB); dA/dB are None when r == 0.  dy and x share one dtype (bf16
-    or fp32); dx is out_dtype (default: dx's dtype if given, else the activations')."""
+def _lora_bwd(base, dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_accumulate, workspace, stream,
+              out_dtype):
     t, k = x.shape
-    n = codes.shape[0]
     _req(x, "x", x.dtype, (t, k))
+    fmt, n, bptr = _base_args(base, k)
     _req(dy, "dy", x.dtype, (t, n))
     out_dtype = out_dtype or (dx.dtype if dx is not None else x.dtype)
     flags = _flags(x.dtype, out_dtype)
-    _req(codes, "codes", torch.uint8, (n, k // 2))
-    _req(absmax, "absmax", torch.float32, (n, k // 64))
     r = cfg.r
     if r > 0:
         _req(A, "A", torch.float32, (r, k))
@@ -225,12 +216,66 @@ def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax:
     _req(dx, "dx", out_dtype, (t, k))
     need = nf4_lora_workspace_size(t, k, n, r)
     ws = _workspace(x.device, need, workspace)
-    check("nf4_lora_bwd", lib().nf4_lora_bwd(
-        _ptr(dy), _ptr(x), t, k, n, _ptr(codes), _ptr(absmax), _ptr(A) if r > 0 else None,
+    fn = f"{fmt}_lora_bwd"
+    check(fn, getattr(lib(), fn)(
+        _ptr(dy), _ptr(x), t, k, n, *bptr, _ptr(A) if r > 0 else None,
         _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(u) if r > 0 else None, _ptr(dx),
         int(dx_accumulate), _ptr(dA) if r > 0 else None, _ptr(dB) if r > 0 else None,
         int(dAB_accumulate), _ptr(ws), ws.numel(), _stream(stream)))
     return dx, (dA if r > 0 else None), (dB if r > 0 else None)
+
+
+def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
+                 bias: Optional[torch.Tensor], A: Optional[torch.Tensor], B: Optional[torch.Tensor],
+                 cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
+                 u_out: Optional[torch.Tensor] = None, want_u: bool = True,
+                 workspace: Optional[Workspace] = None, stream=None,
+                 out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
+                 residual: Optional[torch.Tensor] = None):
+    """y = [residual +] (x W^T + bias + (alpha/r) drop(x) A^T B^T), W the NF4 base.  Returns
+    (y, u) (u None if not wanted).
+
+    x may be bf16 or fp32; y is out_dtype (default: x's dtype, or y's if given).
+    residual ([t, n], y's dtype) is added in the output pass, rounded as a separate add.
+    u_only: compute only u (y is None)."""
+    return _lora_fwd((codes, absmax), x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype,
+                     u_only, residual)
+
+
+def bf16_lora_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], A: Optional[torch.Tensor],
+                  B: Optional[torch.Tensor], cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
+                  u_out: Optional[torch.Tensor] = None, want_u: bool = True,
+                  workspace: Optional[Workspace] = None, stream=None,
+                  out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
+                  residual: Optional[torch.Tensor] = None):
+    """nf4_lora_fwd over a frozen base kept in bf16, w [n, k]."""
+    return _lora_fwd((w,), x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype, u_only,
+                     residual)
+
+
+def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
+                 A: Optional[torch.Tensor], B: Optional[torch.Tensor], cfg: Lora, key: RngKey,
+                 u: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
+                 dx_accumulate: bool = False, dA: Optional[torch.Tensor] = None,
+                 dB: Optional[torch.Tensor] = None, dAB_accumulate: bool = False,
+                 workspace: Optional[Workspace] = None, stream=None,
+                 out_dtype: Optional[torch.dtype] = None):
+    """Returns (dx, dA, dB); dA/dB are None when r == 0.  dy and x share one dtype (bf16
+    or fp32); dx is out_dtype (default: dx's dtype if given, else the activations')."""
+    return _lora_bwd((codes, absmax), dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_accumulate,
+                     workspace, stream, out_dtype)
+
+
+def bf16_lora_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, A: Optional[torch.Tensor],
+                  B: Optional[torch.Tensor], cfg: Lora, key: RngKey, u: Optional[torch.Tensor] = None,
+                  dx: Optional[torch.Tensor] = None, dx_accumulate: bool = False,
+                  dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+                  dAB_accumulate: bool = False, workspace: Optional[Workspace] = None, stream=None,
+                  out_dtype: Optional[torch.dtype] = None):
+    """nf4_lora_bwd over a frozen base kept in bf16, w [n, k]."""
+    return _lora_bwd((w,), dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_accumulate, workspace,
+                     stream, out_dtype)
+
 
 # ---------------------------------------------------------------------------------
 # pointwise block glue (fp32, contiguous)
@@ -360,6 +405,8 @@ class BlockStreamWindow:
         if getattr(self, "_h", None):
             h, self._h = self._h, None
             check("block_stream_destroy", lib().block_stream_destroy(h))
+            self.host_blobs = []
+            self.arena = None
 
     def __del__(self):
         try:

@@ -80,14 +80,20 @@ def _align(x: int, a: int = 256) -> int:
 class LayerLayout:
     """One layer's frozen base as a single contiguous blob (the unit the window
     streams): for q, k, v, o, gate, up, down in order, packed NF4 codes [N, K/2] then
-    fp32 absmax [N, K/64]; then the bf16 q/k/v biases.  Every segment starts on a
-    256-byte boundary."""
+    fp32 absmax [N, K/64] (base "nf4"), or the bf16 matrix [N, K] (base "bf16"); then the
+    bf16 q/k/v biases.  Every segment starts on a 256-byte boundary."""
 
-    def __init__(self, shape: Shape):
+    def __init__(self, shape: Shape, base: str = "nf4"):
+        assert base in ("nf4", "bf16")
+        self.base = base
         self.segs: Dict[Tuple[str, str], Tuple[int, int, torch.dtype, Tuple[int, ...]]] = {}
         off = 0
         for proj in PROJS:
             K, N = shape.proj_shape(proj)
+            if base == "bf16":
+                self.segs[(proj, "w")] = (off, 2 * N * K, torch.bfloat16, (N, K))
+                off = _align(off + 2 * N * K)
+                continue
             self.segs[(proj, "codes")] = (off, N * K // 2, torch.uint8, (N, K // 2))
             off = _align(off + N * K // 2)
             self.segs[(proj, "absmax")] = (off, N * K // 16, torch.float32, (N, K // 64))
@@ -108,40 +114,51 @@ class LayerLayout:
 # ---------------------------------------------------------------------------------
 # autograd bridge to the library
 
-class _NF4LoraLinear(torch.autograd.Function):
+def _fwd(base, x, bias, A, B, cfg, key, **kw):
+    """The library's forward for an NF4 (codes, absmax) or bf16 (w,) base."""
+    if len(base) == 2:
+        return ops.nf4_lora_fwd(x, base[0], base[1], bias, A, B, cfg, key, **kw)
+    return ops.bf16_lora_fwd(x, base[0], bias, A, B, cfg, key, **kw)
+
+
+def _bwd(base, dy, x, A, B, cfg, key, **kw):
+    if len(base) == 2:
+        return ops.nf4_lora_bwd(dy, x, base[0], base[1], A, B, cfg, key, **kw)
+    return ops.bf16_lora_bwd(dy, x, base[0], A, B, cfg, key, **kw)
+
+
+class _LoraLinear(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, A, B, codes, absmax, bias, residual, cfg, key, value_unused):
+    def forward(ctx, x, A, B, base, bias, residual, cfg, key, value_unused):
         if value_unused:
             # selective recompute: the backward reads only x and u, never y, so the
             # frozen-base product is skipped and y is a zero placeholder
-            _, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, u_only=True)
-            y = x.new_zeros(()).expand(x.shape[0], codes.shape[0])
+            _, u = _fwd(base, x, bias, A, B, cfg, key, u_only=True)
+            y = x.new_zeros(()).expand(x.shape[0], base[0].shape[0])
         else:
-            y, u = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=True,
-                                    residual=residual)
+            y, u = _fwd(base, x, bias, A, B, cfg, key, want_u=True, residual=residual)
         ctx.save_for_backward(x, A, B, u)
-        ctx.codes, ctx.absmax, ctx.cfg, ctx.key = codes, absmax, cfg, key
+        ctx.base, ctx.cfg, ctx.key = base, cfg, key
         return y
 
     @staticmethod
     def backward(ctx, dy):
         x, A, B, u = ctx.saved_tensors
         dy = dy.contiguous()
-        dx, dA, dB = ops.nf4_lora_bwd(dy, x, ctx.codes, ctx.absmax, A, B, ctx.cfg, ctx.key, u=u)
+        dx, dA, dB = _bwd(ctx.base, dy, x, A, B, ctx.cfg, ctx.key, u=u)
         # y = residual + (...): the residual's gradient is dy itself
-        dres = dy if ctx.needs_input_grad[6] else None
-        return dx, dA, dB, None, None, None, dres, None, None, None
+        dres = dy if ctx.needs_input_grad[5] else None
+        return dx, dA, dB, None, None, dres, None, None, None
 
 
-def nf4_lora_linear(x, A, B, codes, absmax, bias, cfg: ops.Lora, key,
-                    value_unused: bool = False, residual: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """[residual +] the projection; with a residual the add happens in the library's
-    output pass."""
+def lora_linear(x, A, B, base: Tuple[torch.Tensor, ...], bias, cfg: ops.Lora, key,
+                value_unused: bool = False, residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[residual +] the projection over an NF4 (codes, absmax) or bf16 (w,) frozen base;
+    with a residual the add happens in the library's output pass."""
     if torch.is_grad_enabled() and (x.requires_grad or A.requires_grad or B.requires_grad or
                                     (residual is not None and residual.requires_grad)):
-        return _NF4LoraLinear.apply(x, A, B, codes, absmax, bias, residual, cfg, key,
-                                    value_unused and cfg.r > 0)
-    y, _ = ops.nf4_lora_fwd(x, codes, absmax, bias, A, B, cfg, key, want_u=False, residual=residual)
+        return _LoraLinear.apply(x, A, B, base, bias, residual, cfg, key, value_unused and cfg.r > 0)
+    y, _ = _fwd(base, x, bias, A, B, cfg, key, want_u=False, residual=residual)
     return y
 
 
@@ -245,7 +262,7 @@ class Stack:
 
     def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
                  window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
-                 n_slots: int = 2, glue: str = "native"):
+                 n_slots: int = 2, glue: str = "native", base: str = "nf4"):
         assert mode in ("streamed", "resident")
         assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
@@ -254,7 +271,7 @@ class Stack:
         self.window_blocks = window_blocks
         self.n_slots = n_slots
         self.dev = torch.device(device or "cuda")
-        self.layout = LayerLayout(shape)
+        self.layout = LayerLayout(shape, base)
         self.host_blobs: List[torch.Tensor] = []
         self.dev_blobs: List[torch.Tensor] = []
         self.window: Optional[ops.BlockStreamWindow] = None
@@ -278,11 +295,15 @@ class Stack:
             self.host_blobs.append(host)
 
     def add_layer(self, W: Dict[str, torch.Tensor], bias: Dict[str, torch.Tensor], A, B, ln1, ln2):
-        """W[proj] bf16 [N, K] on the device -> NF4 into a fresh blob (nf4_quantize)."""
+        """W[proj] bf16 [N, K] on the device -> NF4 into a fresh blob (nf4_quantize), or
+        copied as it is for a bf16 base."""
         blob = torch.zeros(self.layout.nbytes, dtype=torch.uint8, device=self.dev)
         v = self.layout.views(blob)
         for proj in PROJS:
-            ops.nf4_quantize(W[proj], v[(proj, "codes")], v[(proj, "absmax")])
+            if self.layout.base == "bf16":
+                v[(proj, "w")].copy_(W[proj])
+            else:
+                ops.nf4_quantize(W[proj], v[(proj, "codes")], v[(proj, "absmax")])
         for proj in ("q", "k", "v"):
             v[(proj, "bias")].copy_(bias[proj])
         self._store_layer(blob)
@@ -309,8 +330,9 @@ class Stack:
     def random(cls, shape: Shape, seq: int, seed: int = 0, cfg_id: int = 0, w_std: float = 0.02,
                **kw) -> "Stack":
         """Random-weight stack generated layer by layer on the device (the base is
-        drawn, quantized with nf4_quantize and, when streamed, moved to pinned host
-        memory one layer at a time, so the device never holds more than one layer)."""
+        drawn, quantized with nf4_quantize (or kept in bf16) and, when streamed, moved to
+        pinned host memory one layer at a time, so the device never holds more than one
+        layer)."""
         st = cls(shape, seq, seed=seed, **kw)
         dev = st.dev
         r = st.cfg.r
@@ -345,11 +367,12 @@ class Stack:
     def _lin(self, x, l, views, proj, step, micro, value_unused=False, residual=None):
         key = ops.rng_key(self.seed, step, micro, l, PROJ_ID[proj])
         bias = views.get((proj, "bias"))
+        base = ((views[(proj, "w")],) if self.layout.base == "bf16" else
+                (views[(proj, "codes")], views[(proj, "absmax")]))
         if residual is not None and self.glue == "torch":
-            return residual + nf4_lora_linear(x, self.A[l][proj], self.B[l][proj], views[(proj, "codes")],
-                                              views[(proj, "absmax")], bias, self.cfg, key, value_unused)
-        return nf4_lora_linear(x, self.A[l][proj], self.B[l][proj], views[(proj, "codes")],
-                               views[(proj, "absmax")], bias, self.cfg, key, value_unused, residual)
+            return residual + lora_linear(x, self.A[l][proj], self.B[l][proj], base, bias, self.cfg, key,
+                                          value_unused)
+        return lora_linear(x, self.A[l][proj], self.B[l][proj], base, bias, self.cfg, key, value_unused, residual)
 
     def layer_forward(self, h: torch.Tensor, l: int, views, step: int, micro: int = 0,
                       recompute: bool = False) -> torch.Tensor:
@@ -512,9 +535,18 @@ class Stack:
         return out
 
     def close(self) -> None:
+        """Destroys the window (waiting for its copies) and gives the pinned host base and
+        the device blobs back; pinned memory goes back to the system, not to PyTorch's
+        pinned-block cache, so a following stack of other layer sizes can pin its own."""
         if self.window is not None:
             self.window.close()
             self.window = None
+        torch.cuda.synchronize(self.dev)
+        had_host = bool(self.host_blobs)
+        self.host_blobs = []
+        self.dev_blobs = []
+        if had_host:
+            torch._C._host_emptyCache()
 
 
 def random_tokens(seed: int, step: int, T: int, vocab: int, device) -> torch.Tensor:
