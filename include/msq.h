@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 4
+#define MSQ_ABI_VERSION 5
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -238,6 +238,39 @@ int msq_rmsnorm_apply_fwd(const float* h, const float* r, const float* w, int64_
                           float* y, msq_stream_t stream);
 int msq_rmsnorm_apply_bwd(const float* dy, const float* h, const float* r, const float* w, int64_t t,
                           int64_t d, float* dh, float* hdot, msq_stream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Streamed quantizing load.
+ * The pages' default loader stages one tensor at a time, quantizes it and evicts it
+ * before the next, keeping the load-time device peak far below a standard load, with
+ * output byte-identical to the standard load ("Poros" research post, streamed-loader
+ * paragraph).  nf4_stream_load turns bf16 host tensors into NF4 codes + absmax in host
+ * memory, one row chunk at a time: chunk c is copied into pinned bounce buffer c % 2
+ * (host_threads threads), sent to device slot c % 2, quantized by the nf4_quantize
+ * kernel and copied back into the job's destinations, the host copy of the next chunk
+ * overlapping the device work.  A chunk holds up to chunk_rows * max_cols elements
+ * (max_cols = the widest job): more rows for narrower tensors, whole rows always, so
+ * the output is nf4_quantize's on the whole tensor, byte for byte.
+ *   jobs        n_jobs tensors: src host bf16 [rows][cols] (any host memory, e.g. a
+ *               memory-mapped file), cols % 64 == 0; codes [rows][cols/2] and absmax
+ *               [rows][cols/64] host destinations (pinned for asynchronous copies)
+ *   dev_staging device memory, 256-byte aligned, >= nf4_stream_load_device_bytes
+ *   host_bounce pinned host memory, 256-byte aligned, >= nf4_stream_load_host_bytes
+ * The call returns when every destination byte is written (it synchronizes `stream`).
+ * Errors: MSQ_E_SHAPE for cols % 64, MSQ_E_WORKSPACE for short staging, MSQ_E_INVAL for
+ * null or misaligned pointers and bad counts, MSQ_E_HIP for a failed HIP call. */
+typedef struct {
+  const void* src;
+  int64_t rows, cols;
+  uint8_t* codes;
+  float* absmax;
+} msq_quant_job;
+
+size_t nf4_stream_load_device_bytes(int64_t max_cols, int64_t chunk_rows);
+size_t nf4_stream_load_host_bytes(int64_t max_cols, int64_t chunk_rows);
+int nf4_stream_load(const msq_quant_job* jobs, int n_jobs, int64_t chunk_rows, void* dev_staging,
+                    size_t dev_bytes, void* host_bounce, size_t host_bytes, int host_threads,
+                    msq_stream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Host-to-device block-prefetch window.

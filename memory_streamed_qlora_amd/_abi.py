@@ -43,6 +43,11 @@ class WindowStats(ctypes.Structure):
                 ("windows_reused", ctypes.c_uint64)]
 
 
+class QuantJob(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
+
+
 class KernelTiming(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_uint64),
                 ("total_ms", ctypes.c_double), ("total_flops", ctypes.c_double),
@@ -82,6 +87,10 @@ _SIG = {
     "bf16_lora_bwd": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P, LoraCfg, RngKey, _P,
                                      _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
                                      _P]),
+    "nf4_stream_load_device_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "nf4_stream_load_host_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "nf4_stream_load": (ctypes.c_int, [_P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
+                                       ctypes.c_int, _P]),
     "block_stream_arena_bytes": (ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "block_stream_create": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
                                            ctypes.c_size_t, _P]),
@@ -95,7 +104,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 4  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 5  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

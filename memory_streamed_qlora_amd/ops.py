@@ -347,6 +347,40 @@ def rmsnorm_apply_bwd(dy: torch.Tensor, h: torch.Tensor, r: torch.Tensor, w: tor
                                                                _ptr(dh), _ptr(hdot), _stream(stream)))
     return dh, hdot
 
+
+def nf4_stream_load(jobs: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], chunk_bytes: int = 32 << 20,
+                    host_threads: int = 8, stream=None, device=None) -> dict:
+    """Streamed quantizing load: jobs of (w bf16 host [rows, cols], codes uint8 host
+    [rows, cols/2], absmax fp32 host [rows, cols/64]); each w is quantized on the device
+    chunk by chunk into its codes and absmax.  chunk_bytes bounds the bf16 bytes of one
+    chunk (two chunks are staged at a time).  Returns the staging sizes used."""
+    if not jobs:
+        return {"device_bytes": 0, "host_bytes": 0, "chunk_rows": 0}
+    arr = (_abi.QuantJob * len(jobs))()
+    max_cols = 0
+    for i, (w, codes, absmax) in enumerate(jobs):
+        if w.dim() != 2:
+            raise ValueError(f"job {i}: w must be 2-D")
+        rows, cols = w.shape
+        for nm, t, dt, shp in (("w", w, torch.bfloat16, (rows, cols)), ("codes", codes, torch.uint8, (rows, cols // 2)),
+                               ("absmax", absmax, torch.float32, (rows, cols // 64))):
+            if t.device.type != "cpu" or t.dtype != dt or tuple(t.shape) != shp or not t.is_contiguous():
+                raise ValueError(f"job {i}: {nm} must be a contiguous host {dt} tensor of shape {shp}")
+        arr[i] = _abi.QuantJob(w.data_ptr(), rows, cols, codes.data_ptr(), absmax.data_ptr())
+        max_cols = max(max_cols, cols)
+    chunk_rows = max(1, chunk_bytes // (2 * max_cols))
+    dev_need = int(lib().nf4_stream_load_device_bytes(max_cols, chunk_rows))
+    host_need = int(lib().nf4_stream_load_host_bytes(max_cols, chunk_rows))
+    if dev_need == 0:
+        raise ValueError(f"cols must be a multiple of 64 (widest job has {max_cols})")
+    dev = torch.device(device or "cuda")
+    staging = torch.empty(dev_need, dtype=torch.uint8, device=dev)
+    bounce = torch.empty(host_need, dtype=torch.uint8, pin_memory=True)
+    check("nf4_stream_load", lib().nf4_stream_load(arr, len(jobs), chunk_rows, _ptr(staging), dev_need,
+                                                   _ptr(bounce), host_need, host_threads, _stream(stream)))
+    del staging, bounce
+    return {"device_bytes": dev_need, "host_bytes": host_need, "chunk_rows": chunk_rows}
+
 class BlockStreamWindow:
     """block_stream_* over pinned host blobs and a caller-owned device arena."""
 

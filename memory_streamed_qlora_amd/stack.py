@@ -335,20 +335,14 @@ class Stack:
         layer)."""
         st = cls(shape, seq, seed=seed, **kw)
         dev = st.dev
-        r = st.cfg.r
-
-        def gen(layer, tid):
-            g = torch.Generator(device=dev)
-            g.manual_seed((seed * 1000003 + cfg_id * 10007 + layer * 101 + tid) & 0x7FFFFFFFFFFFFFFF)
-            return g
+        gen = st._generators(cfg_id)
 
         for l in range(shape.layers):
-            W, bias, A, B = {}, {}, {}, {}
+            W, bias = {}, {}
+            A, B = st._draw_adapters(l, gen)
             for i, proj in enumerate(PROJS):
                 K, N = shape.proj_shape(proj)
                 W[proj] = (torch.randn(N, K, generator=gen(l, 16 * i), device=dev) * w_std).to(torch.bfloat16)
-                A[proj] = (torch.rand(r, K, generator=gen(l, 16 * i + 2), device=dev) * 2 - 1) / math.sqrt(K)
-                B[proj] = torch.randn(N, r, generator=gen(l, 16 * i + 3), device=dev) * 0.01
                 if proj in ("q", "k", "v"):
                     bias[proj] = (torch.randn(N, generator=gen(l, 16 * i + 1), device=dev) * 0.02).to(torch.bfloat16)
             ln1 = 1 + 0.02 * torch.randn(shape.hidden, generator=gen(l, 200), device=dev)
@@ -360,6 +354,101 @@ class Stack:
         lm = (torch.randn(shape.vocab, shape.hidden, generator=gen(10000, 1), device=dev) * 0.02).to(torch.bfloat16)
         lnf = 1 + 0.02 * torch.randn(shape.hidden, generator=gen(10000, 2), device=dev)
         st.set_globals(emb, lm, lnf)
+        st.finalize()
+        return st
+
+    def _generators(self, cfg_id: int):
+        """gen(layer, tensor_id): the device generator every drawn tensor comes from."""
+        def gen(layer, tid):
+            g = torch.Generator(device=self.dev)
+            g.manual_seed((self.seed * 1000003 + cfg_id * 10007 + layer * 101 + tid) & 0x7FFFFFFFFFFFFFFF)
+            return g
+        return gen
+
+    def _draw_adapters(self, l: int, gen):
+        """Layer l's LoRA adapters: A ~ U(+-1/sqrt(K)), B ~ N(0, 0.01)."""
+        r = self.cfg.r
+        A, B = {}, {}
+        for i, proj in enumerate(PROJS):
+            K, N = self.shape.proj_shape(proj)
+            A[proj] = (torch.rand(r, K, generator=gen(l, 16 * i + 2), device=self.dev) * 2 - 1) / math.sqrt(K)
+            B[proj] = torch.randn(N, r, generator=gen(l, 16 * i + 3), device=self.dev) * 0.01
+        return A, B
+
+    @staticmethod
+    def tensor_name(layer: int, proj: str, kind: str = "weight") -> str:
+        """A projection's name in a Qwen2-style checkpoint (the loader's source naming)."""
+        mod = "mlp" if proj in ("gate", "up", "down") else "self_attn"
+        return f"model.layers.{layer}.{mod}.{proj}_proj.{kind}"
+
+    @classmethod
+    def load_base(cls, shape: Shape, source, loader: str = "streamed", device=None, chunk_bytes: int = 32 << 20,
+                  host_threads: int = 8) -> List[torch.Tensor]:
+        """Every layer's NF4 base (LayerLayout, with the q/k/v biases) as a pinned host
+        blob, quantized from a host bf16 source: source(name) returns a contiguous host
+        tensor under the Qwen2 checkpoint names (tensor_name).
+
+        loader "streamed" (the pages' default): nf4_stream_load quantizes each layer's
+        projections chunk by chunk straight into the layer's pinned blob; the device holds
+        only the two staging slots.  "standard": every base matrix is first moved to the
+        device (the whole bf16 base materialised there), then quantized with nf4_quantize
+        and the blobs copied back.  Both give the same bytes."""
+        if loader not in ("streamed", "standard"):
+            raise ValueError(f"loader must be 'streamed' or 'standard', got {loader!r}")
+        dev = torch.device(device or "cuda")
+        layout = LayerLayout(shape)
+        L = shape.layers
+        W_dev = None
+        if loader == "standard":
+            W_dev = {(l, p): source(cls.tensor_name(l, p)).to(dev) for l in range(L) for p in PROJS}
+        blobs = []
+        for l in range(L):
+            if loader == "streamed":
+                blob = torch.zeros(layout.nbytes, dtype=torch.uint8, pin_memory=True)
+                v = layout.views(blob)
+                ops.nf4_stream_load([(source(cls.tensor_name(l, p)), v[(p, "codes")], v[(p, "absmax")])
+                                     for p in PROJS], chunk_bytes=chunk_bytes, host_threads=host_threads,
+                                    device=dev)
+            else:
+                blob_dev = torch.zeros(layout.nbytes, dtype=torch.uint8, device=dev)
+                vd = layout.views(blob_dev)
+                for p in PROJS:
+                    ops.nf4_quantize(W_dev.pop((l, p)), vd[(p, "codes")], vd[(p, "absmax")])
+                blob = torch.zeros(layout.nbytes, dtype=torch.uint8, pin_memory=True)
+                blob.copy_(blob_dev)
+                del blob_dev
+                v = layout.views(blob)
+            for p in ("q", "k", "v"):
+                v[(p, "bias")].copy_(source(cls.tensor_name(l, p, "bias")))
+            blobs.append(blob)
+        return blobs
+
+    @classmethod
+    def load(cls, shape: Shape, seq: int, source, loader: str = "streamed", seed: int = 0, cfg_id: int = 0,
+             chunk_bytes: int = 32 << 20, host_threads: int = 8, **kw) -> "Stack":
+        """A stack whose frozen NF4 base comes from load_base (same source and loaders);
+        the norms and the frozen embedding / lm_head come from the source
+        (model.layers.{l}.input_layernorm.weight / post_attention_layernorm.weight,
+        model.embed_tokens.weight, lm_head.weight, model.norm.weight), the adapters are
+        drawn as in random()."""
+        st = cls(shape, seq, seed=seed, **kw)
+        if st.layout.base != "nf4":
+            raise ValueError("the quantizing loader builds an NF4 base")
+        dev = st.dev
+        blobs = cls.load_base(shape, source, loader, dev, chunk_bytes, host_threads)
+        gen = st._generators(cfg_id)
+        for l, blob in enumerate(blobs):
+            if st.mode == "resident":
+                st.dev_blobs.append(blob.to(dev))
+            else:
+                st.host_blobs.append(blob)
+            A, B = st._draw_adapters(l, gen)
+            st.A.append({p: torch.nn.Parameter(A[p].contiguous()) for p in PROJS})
+            st.B.append({p: torch.nn.Parameter(B[p].contiguous()) for p in PROJS})
+            st.ln1.append(source(f"model.layers.{l}.input_layernorm.weight").to(dev, torch.float32))
+            st.ln2.append(source(f"model.layers.{l}.post_attention_layernorm.weight").to(dev, torch.float32))
+        del blobs
+        st.set_globals(source("model.embed_tokens.weight"), source("lm_head.weight"), source("model.norm.weight"))
         st.finalize()
         return st
 

@@ -133,6 +133,28 @@ def test_glue_rejects_bad_arguments():
     assert L.msq_rmsnorm_apply_bwd(FAKE + 4, FAKE, FAKE, FAKE, 4, 64, FAKE, FAKE, None) == abi.MSQ_E_INVAL
 
 
+def test_stream_load_rejects_bad_arguments():
+    """The loader validates jobs and staging on the host before any HIP call."""
+    L = abi.lib()
+    assert L.nf4_stream_load_device_bytes(96, 4) == 0
+    assert L.nf4_stream_load_device_bytes(128, 0) == 0
+    dev_need = L.nf4_stream_load_device_bytes(128, 8)
+    host_need = L.nf4_stream_load_host_bytes(128, 8)
+    assert dev_need >= 2 * (8 * 128 * 2 + 8 * 64 + 8 * 2) and host_need >= 2 * 8 * 128 * 2
+    jobs = (abi.QuantJob * 2)(abi.QuantJob(FAKE, 4, 128, FAKE, FAKE), abi.QuantJob(FAKE, 4, 96, FAKE, FAKE))
+    assert L.nf4_stream_load(jobs, 2, 8, FAKE, dev_need, FAKE, host_need, 4, None) == abi.MSQ_E_SHAPE
+    jobs[1] = abi.QuantJob(None, 4, 64, FAKE, FAKE)
+    assert L.nf4_stream_load(jobs, 2, 8, FAKE, dev_need, FAKE, host_need, 4, None) == abi.MSQ_E_INVAL
+    jobs[1] = abi.QuantJob(FAKE, 4, 64, FAKE, FAKE)
+    assert L.nf4_stream_load(jobs, 2, 8, FAKE, dev_need - 1, FAKE, host_need, 4, None) == abi.MSQ_E_WORKSPACE
+    assert L.nf4_stream_load(jobs, 2, 8, FAKE + 16, dev_need, FAKE, host_need, 4, None) == abi.MSQ_E_INVAL
+    assert L.nf4_stream_load(jobs, 2, 8, FAKE, dev_need, FAKE, host_need, 0, None) == abi.MSQ_E_INVAL
+    assert L.nf4_stream_load(jobs, 2, 0, FAKE, dev_need, FAKE, host_need, 4, None) == abi.MSQ_E_INVAL
+    empty = (abi.QuantJob * 1)(abi.QuantJob(None, 0, 64, None, None))
+    assert L.nf4_stream_load(empty, 1, 8, None, 0, None, 0, 4, None) == abi.MSQ_E_INVAL
+    assert L.nf4_stream_load(None, 0, 8, None, 0, None, 0, 4, None) == 0
+
+
 def test_workspace_size_depends_on_shape_only():
     L = abi.lib()
     a = L.nf4_lora_workspace_size(512, 5120, 27648, 16)
