@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 5
+#define MSQ_ABI_VERSION 6
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -192,6 +192,38 @@ int bf16_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n
                   const float* A, const float* B, msq_lora_cfg cfg, msq_rng_key key, const float* u,
                   void* dx, int dx_accumulate, float* dA, float* dB, int dAB_accumulate,
                   void* workspace, size_t workspace_bytes, msq_stream_t stream);
+
+/* Grouped forward: up to 3 projections of the same input x [t, k] (a decoder block's
+ * q/k/v, or gate/up) in one pass.  x is packed for the MFMA once, each projection's
+ * rank-r product is formed with its own key and A, and one GEMM launch covers the column
+ * tiles of all of them with one split plan, so the narrow projections no longer leave
+ * most of the chip idle.  Each projection's outputs are those of nf4_lora_fwd (or
+ * bf16_lora_fwd) with the same arguments, up to the fp32 summation order of the split
+ * reduction, which the group's plan fixes.
+ *   projs   n_proj (1..3) descriptors: n, the base (codes + absmax, or w; one format per
+ *           group), bias, residual, A, B, the projection's rng key, y and u_out (or NULL),
+ *           with the alignment and shapes of nf4_lora_fwd
+ *   cfg     r, alpha, p_drop and the activation / output flags shared by the group
+ *           (MSQ_U_ONLY is rejected)
+ *   workspace  >= lora_group_workspace_size(t, k, projs, n_proj, r) bytes (0 for invalid
+ *           descriptors), 256-byte aligned. */
+typedef struct {
+  int64_t n;
+  const uint8_t* codes;
+  const float* absmax;
+  const uint16_t* w;
+  const uint16_t* bias;
+  const void* residual;
+  const float* A;
+  const float* B;
+  msq_rng_key key;
+  void* y;
+  float* u_out;
+} msq_lora_proj;
+
+size_t lora_group_workspace_size(int64_t t, int64_t k, const msq_lora_proj* projs, int n_proj, int32_t r);
+int lora_fwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj* projs, int n_proj,
+                   msq_lora_cfg cfg, void* workspace, size_t workspace_bytes, msq_stream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Pointwise block glue of a Qwen2.5-style decoder block, fp32.

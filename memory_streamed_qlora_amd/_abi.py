@@ -48,6 +48,13 @@ class QuantJob(ctypes.Structure):
                 ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
 
 
+class LoraProj(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+                ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("key", RngKey), ("y", ctypes.c_void_p),
+                ("u_out", ctypes.c_void_p)]
+
+
 class KernelTiming(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_uint64),
                 ("total_ms", ctypes.c_double), ("total_flops", ctypes.c_double),
@@ -87,6 +94,8 @@ _SIG = {
     "bf16_lora_bwd": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P, LoraCfg, RngKey, _P,
                                      _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
                                      _P]),
+    "lora_group_workspace_size": (ctypes.c_size_t, [_I64, _I64, _P, ctypes.c_int, ctypes.c_int32]),
+    "lora_fwd_group": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, LoraCfg, _P, ctypes.c_size_t, _P]),
     "nf4_stream_load_device_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "nf4_stream_load_host_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "nf4_stream_load": (ctypes.c_int, [_P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
@@ -104,7 +113,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 5  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 6  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

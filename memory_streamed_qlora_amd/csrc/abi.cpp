@@ -223,27 +223,81 @@ int lora_fwd(const char* fn, const void* x, int64_t t, int64_t k, int64_t n, con
     GemmLaunch L;
     L.mode = 0;
     L.act = xb;
-    L.codes = base.codes;
-    L.absmax = base.absmax;
-    L.wbf = base.wbf;
     L.M = t;
-    L.N = n;
     L.K = k;
     L.plan = p.fwd;
-    L.lu = u;
-    L.lw = B;
     L.r = r;
     L.lscale = lscale;
     L.drop = no_dropout();
-    L.bias = bias;
-    L.addend = p.fwd.splits == 1 ? residual : nullptr;
-    L.out = p.fwd.splits == 1 ? y : (void*)part;
     L.out_f32 = out_f32;
+    GemmSegment& S = L.seg[0];
+    S.codes = base.codes;
+    S.absmax = base.absmax;
+    S.wbf = base.wbf;
+    S.N = n;
+    S.lu = u;
+    S.lw = B;
+    S.bias = bias;
+    S.addend = p.fwd.splits == 1 ? residual : nullptr;
+    S.out = p.fwd.splits == 1 ? y : (void*)part;
     e = launch_gemm(L, s);
   }
   if (e == hipSuccess && p.fwd.splits > 1)
     e = launch_split_reduce(part, p.fwd.splits, t, n, bias, residual, true, y, out_f32, s);
   return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
+}
+
+// Workspace of a grouped forward: fp32 split partials of every projection (consecutive
+// [splits][t][n_i] blocks), u of each projection, the packed activation and the chunk
+// partials of the rank-r products (shared: the products run one after another).
+struct GroupPlan {
+  GemmPlan fwd;
+  size_t off_part, off_u[GEMM_MAX_SEGS], off_act, off_sk, bytes;
+};
+
+GroupPlan group_plan(int64_t t, int64_t k, const int64_t* ns, int np, int32_t r) {
+  GroupPlan p;
+  p.fwd = gemm_plan_group(t, ns, np, k);
+  int64_t ntot = 0;
+  for (int i = 0; i < np; ++i) ntot += ns[i];
+  size_t o = 0;
+  p.off_part = o;
+  o = align256(o + (p.fwd.splits > 1 ? (size_t)p.fwd.splits * t * ntot * sizeof(float) : 0));
+  for (int i = 0; i < GEMM_MAX_SEGS; ++i) {
+    p.off_u[i] = o;
+    if (i < np) o = align256(o + (size_t)t * r * sizeof(float));
+  }
+  p.off_act = o;
+  o = align256(o + (size_t)frag_rows(t) * k * sizeof(uint16_t));
+  p.off_sk = o;
+  o = align256(o + (size_t)((k + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
+  p.bytes = o;
+  return p;
+}
+
+int group_check(const char* fn, int64_t t, int64_t k, const msq_lora_proj* projs, int n_proj, const msq_lora_cfg& cfg,
+                int64_t* ns) {
+  if (n_proj < 1 || n_proj > GEMM_MAX_SEGS || !projs)
+    return set_error(MSQ_E_INVAL, "%s: n_proj=%d outside [1, %d]", fn, n_proj, GEMM_MAX_SEGS);
+  if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY is not available for groups", fn);
+  int64_t ntot = 0;
+  for (int i = 0; i < n_proj; ++i) {
+    const msq_lora_proj& q = projs[i];
+    int rc = check_linear(fn, t, k, q.n, cfg, q.key);
+    if (rc) return rc;
+    rc = check_base(fn, Base{q.codes, q.absmax, q.w});
+    if (rc) return rc;
+    if ((q.w != nullptr) != (projs[0].w != nullptr)) return set_error(MSQ_E_INVAL, "%s: mixed base formats in one group", fn);
+    if (t > 0 && !q.y) return set_error(MSQ_E_INVAL, "%s: projection %d: null y", fn, i);
+    if (cfg.r > 0 && (!q.A || !q.B)) return set_error(MSQ_E_INVAL, "%s: projection %d: r > 0 needs A and B", fn, i);
+    if (!aligned(q.y, 16) || !aligned(q.bias, 8) || !aligned(q.residual, 16) || !aligned(q.A, 16) || !aligned(q.B, 16) ||
+        !aligned(q.u_out, 4))
+      return set_error(MSQ_E_INVAL, "%s: projection %d: misaligned pointer (y, residual, A, B: 16 bytes; bias 8)", fn, i);
+    ns[i] = q.n;
+    ntot += q.n;
+  }
+  if (t * ntot >= MAX_ELEMS) return set_error(MSQ_E_SHAPE, "%s: t * (sum of n) reaches 2^34", fn);
+  return MSQ_OK;
 }
 
 int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k, int64_t n, const Base& base,
@@ -289,22 +343,22 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
       GemmLaunch L;
       L.mode = 1;
       L.act = dyb;
-      L.codes = base.codes;
-      L.absmax = base.absmax;
-      L.wbf = base.wbf;
       L.M = t;
-      L.N = n;
       L.K = k;
       L.plan = p.bwd;
-      L.lu = du;
-      L.lw = A;
       L.r = r;
       L.lscale = 1.0f;
       L.drop = d;
-      L.bias = nullptr;
-      L.addend = dx_accumulate && p.bwd.splits == 1 ? dx : nullptr;
-      L.out = p.bwd.splits == 1 ? dx : (void*)part;
       L.out_f32 = out_f32;
+      GemmSegment& S = L.seg[0];
+      S.codes = base.codes;
+      S.absmax = base.absmax;
+      S.wbf = base.wbf;
+      S.N = n;
+      S.lu = du;
+      S.lw = A;
+      S.addend = dx_accumulate && p.bwd.splits == 1 ? dx : nullptr;
+      S.out = p.bwd.splits == 1 ? dx : (void*)part;
       e = launch_gemm(L, s);
     }
     if (e == hipSuccess && p.bwd.splits > 1)
@@ -343,6 +397,82 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
   if (!codes || !absmax) return set_error(MSQ_E_INVAL, "nf4_lora_bwd: null pointer (codes, absmax)");
   return lora_bwd("nf4_lora_bwd", dy, x, t, k, n, Base{codes, absmax, nullptr}, A, B, cfg, key, u, dx,
                   dx_accumulate, dA, dB, dAB_accumulate, workspace, workspace_bytes, stream);
+}
+
+size_t lora_group_workspace_size(int64_t t, int64_t k, const msq_lora_proj* projs, int n_proj, int32_t r) {
+  int64_t ns[GEMM_MAX_SEGS];
+  msq_lora_cfg cfg;
+  memset(&cfg, 0, sizeof(cfg));
+  cfg.r = r;
+  cfg.alpha = 1.0f;
+  if (group_check("lora_group_workspace_size", t, k, projs, n_proj, cfg, ns) != MSQ_OK) return 0;
+  return group_plan(t, k, ns, n_proj, r).bytes;
+}
+
+int lora_fwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj* projs, int n_proj, msq_lora_cfg cfg,
+                   void* workspace, size_t workspace_bytes, msq_stream_t stream) {
+  const char* fn = "lora_fwd_group";
+  int64_t ns[GEMM_MAX_SEGS];
+  int rc = group_check(fn, t, k, projs, n_proj, cfg, ns);
+  if (rc) return rc;
+  if (!workspace || (t > 0 && !x)) return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(workspace, 256))
+    return set_error(MSQ_E_INVAL, "%s: misaligned pointer (x 16 bytes; workspace 256)", fn);
+  const GroupPlan p = group_plan(t, k, ns, n_proj, cfg.r);
+  if (workspace_bytes < p.bytes) return set_error(MSQ_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, p.bytes);
+  if (t == 0) return MSQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int r = cfg.r;
+  const bool act_f32 = cfg.flags & MSQ_ACT_F32, out_f32 = cfg.flags & MSQ_OUT_F32;
+  const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
+  uint16_t* xb = (uint16_t*)(ws + p.off_act);
+  float* u[GEMM_MAX_SEGS];
+  hipError_t e = hipSuccess;
+  // the activation is packed once (with the first projection's rank-r product); the other
+  // products read x again with their own dropout masks
+  for (int i = 0; i < n_proj && e == hipSuccess; ++i) {
+    const msq_lora_proj& q = projs[i];
+    u[i] = q.u_out ? q.u_out : (float*)(ws + p.off_u[i]);
+    e = launch_pack_lora(x, act_f32, t, k, q.A, 0, r, 1.0f, make_dropout(q.key, cfg.p_drop), i == 0 ? xb : nullptr,
+                         (float*)(ws + p.off_sk), u[i], s);
+  }
+  float* part = (float*)(ws + p.off_part);
+  size_t part_off[GEMM_MAX_SEGS];
+  if (e == hipSuccess) {
+    GemmLaunch L;
+    L.mode = 0;
+    L.act = xb;
+    L.M = t;
+    L.K = k;
+    L.plan = p.fwd;
+    L.r = r;
+    L.lscale = lscale;
+    L.drop = no_dropout();
+    L.out_f32 = out_f32;
+    L.nseg = n_proj;
+    size_t o = 0;
+    for (int i = 0; i < n_proj; ++i) {
+      const msq_lora_proj& q = projs[i];
+      GemmSegment& S = L.seg[i];
+      S.codes = q.codes;
+      S.absmax = q.absmax;
+      S.wbf = q.w;
+      S.N = q.n;
+      S.lu = u[i];
+      S.lw = q.B;
+      S.bias = q.bias;
+      part_off[i] = o;
+      S.addend = p.fwd.splits == 1 ? q.residual : nullptr;
+      S.out = p.fwd.splits == 1 ? q.y : (void*)(part + o);
+      o += (size_t)p.fwd.splits * t * q.n;
+    }
+    e = launch_gemm(L, s);
+  }
+  for (int i = 0; i < n_proj && e == hipSuccess && p.fwd.splits > 1; ++i)
+    e = launch_split_reduce(part + part_off[i], p.fwd.splits, t, projs[i].n, projs[i].bias, projs[i].residual, true,
+                            projs[i].y, out_f32, s);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
 }
 
 int bf16_lora_fwd(const void* x, int64_t t, int64_t k, int64_t n, const uint16_t* w,

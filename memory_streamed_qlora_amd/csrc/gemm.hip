@@ -26,6 +26,8 @@
 // can instead be split over gridDim.z, in which case split 0 carries the LoRA term and
 // fp32 partial tiles go to a workspace summed in split order by a separate kernel, so
 // results never depend on timing.
+#include <string.h>
+
 #include "internal.hpp"
 
 namespace msq {
@@ -37,22 +39,18 @@ constexpr int LDW = BK + PAD;       // LDS row pitch in bf16 elements (144 bytes
 static_assert(BM == 512 && BN == 128 && BK == 64, "the thread mappings below assume this tile");
 constexpr int THREADS = 512;  // 8 waves, one per 64 rows
 
-struct GemmArgs {
-  const uint16_t* act;   // [M][R] bf16
-  const uint8_t* codes;  // [N][K/2]   NF4 base
+// One projection of a launch.  A forward launch may group up to GEMM_MAX_SEGS projections
+// that share the activation (same K): their column tiles are concatenated in the grid and
+// each workgroup finds its projection from its tile.
+struct GemmSeg {
+  const uint8_t* codes;  // [N][K/2] NF4 base, or
   const float* absmax;   // [N][K/64]
-  int64_t M, N, K;       // W is [N][K]
-  int64_t R, Nc;         // reduction length and output columns
-  int steps, steps_per_split, splits;
-  Nf4Lut lut;
+  const uint16_t* wbf;   // [N][K] bf16 base (the bf16 kernels)
   // LoRA term, added once (by split 0):
   //   forward  lscale * lu[m][:] . lw[n][:]          lu = u [M][r], lw = B [N][r]
   //   backward keep(m,k) * sigma * lu[m][:] . lw[:][k]  lu = du [M][r], lw = A [r][K]
   const float* lu;
   const float* lw;
-  int r;
-  float lscale;
-  Dropout drop;
   // output: splits == 1 -> y / dx directly (bf16 or fp32): acc + bias, then addend + that
   //         when addend is set (forward: a residual input, added to y after y's own
   //         rounding; backward: the old dx, one rounding of the sum);
@@ -60,8 +58,41 @@ struct GemmArgs {
   const uint16_t* bias;
   const void* addend;  // [M][Nc] in the output's type, may equal out
   void* out;
+  int64_t Nc;          // output columns
+  int tile0;           // first column tile of this projection in the grid
+};
+
+struct GemmArgs {
+  const uint16_t* act;   // [M][R] bf16, packed
+  int64_t M, K;          // every W is [N][K]
+  int64_t R;             // reduction length
+  int steps, steps_per_split, splits;
+  Nf4Lut lut;
+  int r;
+  float lscale;
+  Dropout drop;
   int out_f32;
-  const uint16_t* wbf;  // [N][K] bf16 base (the bf16 kernels; NULL for NF4)
+  int nseg;
+  GemmSeg seg[GEMM_MAX_SEGS];
+};
+
+// The launch as the workgroup's projection sees it.
+struct GemmView {
+  const uint16_t* act;
+  const uint8_t* codes;
+  const float* absmax;
+  const uint16_t* wbf;
+  int64_t M, K, Nc;
+  int steps;
+  const float* lu;
+  const float* lw;
+  int r;
+  float lscale;
+  Dropout drop;
+  const uint16_t* bias;
+  const void* addend;
+  void* out;
+  int out_f32;
 };
 
 // Eight fp32 values -> hi and lo bf16 MFMA operands, hi = rne(v), lo = rne(v - hi), so
@@ -137,7 +168,7 @@ struct WShare<true> {
 };
 
 template <int MODE, bool DROP, bool BF16W>
-__device__ __forceinline__ void gemm_body(const GemmArgs& g) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[3][BN * LDW];
 
   const int tid = threadIdx.x;
@@ -147,8 +178,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   int64_t n0, m0;
   int split;
   tile_of(n0, m0, split);
-  const int s_begin = split * g.steps_per_split;
-  const int s_end = min(g.steps, s_begin + g.steps_per_split);
+  // this workgroup's projection (uniform): the last segment whose tiles start at or
+  // before the tile; n0 becomes the column within it
+  int sgi = 0;
+  if (ga.nseg > 1 && n0 >= (int64_t)ga.seg[1].tile0 * BN) sgi = 1;
+  if (ga.nseg > 2 && n0 >= (int64_t)ga.seg[2].tile0 * BN) sgi = 2;
+  const GemmSeg& sg = ga.seg[sgi];
+  n0 -= (int64_t)sg.tile0 * BN;
+  const GemmView g{ga.act, sg.codes, sg.absmax, sg.wbf, ga.M, ga.K, sg.Nc, ga.steps, sg.lu, sg.lw, ga.r,
+                   ga.lscale, ga.drop, sg.bias, sg.addend, sg.out, ga.out_f32};
+  const int s_begin = split * ga.steps_per_split;
+  const int s_end = min(ga.steps, s_begin + ga.steps_per_split);
   const int64_t mw = m0 + 64 * wave;  // first row of this wave
 
   // An asm operand in an AGPR lets the compiler place the MFMA accumulators in AGPRs
@@ -256,7 +296,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     };
     auto planes = [&](const WShare<BF16W>& w) {
       Nf4Planes P;
-      if constexpr (!BF16W) P = nf4_planes(g.lut, w.s);
+      if constexpr (!BF16W) P = nf4_planes(ga.lut, w.s);
       return P;
     };
     auto read_b = [&](bf16x8_t(&b)[4], int c, int buf) {
@@ -410,7 +450,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       const bool all_in = rows_in && n0 + 32 * jn + 32 <= g.Nc;
       if (!all_in && n >= g.Nc) continue;
       const int64_t mb = mw + 32 * i + 4 * hk;
-      if (g.splits > 1) {
+      if (ga.splits > 1) {
         float* po = reinterpret_cast<float*>(g.out) + ((int64_t)split * g.M) * g.Nc + n;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -468,10 +508,10 @@ MSQ_GEMM_KERNEL(bf16_bwd_gemm_dropout, 1, true, true)
 // workgroup keeps its CU's matrix cores busy for ~1 us (64 MFMAs per SIMD), the
 // workgroups spread evenly over the 256 CUs, and every extra split writes and re-reads
 // an fp32 partial tile (~4 TB/s).  The cheapest S wins; S = 1 on ties.
-GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red) {
+GemmPlan gemm_plan_tiles(int64_t m, int64_t n_tiles, int64_t nc, int64_t red) {
   GemmPlan p;
   p.steps = (int)(red / BK);
-  const int64_t tiles = ((m + BM - 1) / BM) * ((nc + BN - 1) / BN);
+  const int64_t tiles = ((m + BM - 1) / BM) * n_tiles;
   double best = 0.0;
   int best_s = 1;
   for (int s = 1; s <= 32 && s <= p.steps; ++s) {
@@ -489,36 +529,60 @@ GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red) {
   return p;
 }
 
+GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red) { return gemm_plan_tiles(m, (nc + BN - 1) / BN, nc, red); }
+
+GemmPlan gemm_plan_group(int64_t m, const int64_t* ns, int nseg, int64_t red) {
+  int64_t tiles = 0, nc = 0;
+  for (int i = 0; i < nseg; ++i) {
+    tiles += (ns[i] + BN - 1) / BN;
+    nc += ns[i];
+  }
+  return gemm_plan_tiles(m, tiles, nc, red);
+}
+
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  if (L.nseg < 1 || L.nseg > GEMM_MAX_SEGS || (L.mode == 1 && L.nseg != 1)) return hipErrorInvalidValue;
+  const bool bf = L.seg[0].wbf != nullptr;
   g.act = L.act;
-  g.codes = L.codes;
-  g.absmax = L.absmax;
-  g.wbf = L.wbf;
   g.M = L.M;
-  g.N = L.N;
   g.K = L.K;
-  g.R = L.mode == 0 ? L.K : L.N;
-  g.Nc = L.mode == 0 ? L.N : L.K;
+  g.R = L.mode == 0 ? L.K : L.seg[0].N;
   g.steps = L.plan.steps;
   g.steps_per_split = L.plan.steps_per_split;
   g.splits = L.plan.splits;
   g.lut = nf4_lut();
-  g.lu = L.lu;
-  g.lw = L.lw;
   g.r = L.r;
   g.lscale = L.lscale;
   g.drop = L.drop;
-  g.bias = L.bias;
-  g.addend = L.addend;
-  g.out = L.out;
   g.out_f32 = L.out_f32;
+  g.nseg = L.nseg;
+  int tiles = 0;
+  int64_t n_total = 0, nc_total = 0;
+  for (int i = 0; i < L.nseg; ++i) {
+    const GemmSegment& S = L.seg[i];
+    if ((S.wbf != nullptr) != bf || (S.codes != nullptr) == bf) return hipErrorInvalidValue;  // one base format
+    GemmSeg& d = g.seg[i];
+    d.codes = S.codes;
+    d.absmax = S.absmax;
+    d.wbf = S.wbf;
+    d.lu = S.lu;
+    d.lw = S.lw;
+    d.bias = S.bias;
+    d.addend = S.addend;
+    d.out = S.out;
+    d.Nc = L.mode == 0 ? S.N : L.K;
+    d.tile0 = tiles;
+    if (d.Nc < 1) return hipErrorInvalidValue;
+    tiles += (int)((d.Nc + BN - 1) / BN);
+    n_total += S.N;
+    nc_total += d.Nc;
+  }
   // The kernel clamps rows and columns onto [0, M) x [0, Nc) and reads whole k-steps.
-  if (g.M < 1 || g.Nc < 1 || g.R % BK || g.K % 64 || g.steps != (int)(g.R / BK)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)g.splits);
-  const double flops = 2.0 * (double)g.M * (double)g.N * (double)g.K;
-  const bool bf = L.wbf != nullptr;
-  if (bf == (L.codes != nullptr)) return hipErrorInvalidValue;  // exactly one base format
+  if (g.M < 1 || g.R % BK || g.K % 64 || g.steps != (int)(g.R / BK)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles, (unsigned)((g.M + BM - 1) / BM), (unsigned)g.splits);
+  const double flops = 2.0 * (double)g.M * (double)n_total * (double)g.K;
   void (*kern)(GemmArgs);
   const char* name;
   if (L.mode == 0) {
@@ -533,10 +597,13 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   }
   // algorithmic bytes: the base (NF4 codes + scales, or bf16), the packed activation, the
   // output (or split partials)
-  const double bytes = (double)g.N * g.K * (bf ? 2.0 : 0.5625) + (double)frag_rows(g.M) * g.R * 2 +
-                       (double)g.M * g.Nc * (g.splits > 1 ? 4.0 * g.splits : (g.out_f32 ? 4.0 : 2.0) * (g.addend ? 2 : 1));
-  char shape[32];
-  snprintf(shape, sizeof(shape), "%lldx%lldx%lld", (long long)L.M, (long long)L.N, (long long)L.K);
+  double out_bytes = 0.0;
+  for (int i = 0; i < L.nseg; ++i)
+    out_bytes += (double)g.M * g.seg[i].Nc *
+                 (g.splits > 1 ? 4.0 * g.splits : (g.out_f32 ? 4.0 : 2.0) * (g.seg[i].addend ? 2 : 1));
+  const double bytes = (double)n_total * g.K * (bf ? 2.0 : 0.5625) + (double)frag_rows(g.M) * g.R * 2 + out_bytes;
+  char shape[40];
+  snprintf(shape, sizeof(shape), "%lldx%lldx%lld", (long long)L.M, (long long)n_total, (long long)L.K);
   return timed_launch(name, shape, flops, bytes, kern, grid, dim3(THREADS), s, g);
 }
 

@@ -31,6 +31,7 @@ struct GemmPlan {
   int steps_per_split;
 };
 GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red);
+GemmPlan gemm_plan_group(int64_t m, const int64_t* ns, int nseg, int64_t red);
 
 struct LoraPlan {
   GemmPlan fwd, bwd;
@@ -53,23 +54,32 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 // addend ([M][Nc] in the output's type, NULL for none) may be `out` itself.
 // With plan.splits > 1, `out` receives fp32 partials [splits][M][Nc] instead (split 0
 // carrying the LoRA term) and launch_split_reduce finishes the output.
+// A forward launch may group up to GEMM_MAX_SEGS projections of the same activation (same
+// K, each with its own base, LoRA factors, bias, addend and output): one grid over all
+// their column tiles, one split plan (gemm_plan_group).  The backward takes one.
+constexpr int GEMM_MAX_SEGS = 3;
+struct GemmSegment {
+  const uint8_t* codes = nullptr;  // NF4 base (codes + absmax), or
+  const float* absmax = nullptr;
+  const uint16_t* wbf = nullptr;   // bf16 base [N][K]: exactly one of codes / wbf is set
+  int64_t N = 0;                   // W rows (forward: output columns; backward: reduction)
+  const float* lu = nullptr;
+  const float* lw = nullptr;
+  const uint16_t* bias = nullptr;
+  const void* addend = nullptr;
+  void* out = nullptr;
+};
 struct GemmLaunch {
   int mode;
   const uint16_t* act;  // packed by launch_pack_lora
-  const uint8_t* codes;  // NF4 base (codes + absmax), or
-  const float* absmax;
-  const uint16_t* wbf = nullptr;  // bf16 base [N][K]: exactly one of codes / wbf is set
-  int64_t M, N, K;
+  int64_t M, K;
   GemmPlan plan;
-  const float* lu;
-  const float* lw;
   int r;
   float lscale;
   Dropout drop;
-  const uint16_t* bias;
-  const void* addend;
-  void* out;
   int out_f32;
+  int nseg = 1;
+  GemmSegment seg[GEMM_MAX_SEGS];
 };
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s);
 

@@ -225,6 +225,46 @@ def _lora_bwd(base, dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_acc
     return dx, (dA if r > 0 else None), (dB if r > 0 else None)
 
 
+def lora_fwd_group(x: torch.Tensor, projs: Sequence[dict], cfg: Lora, want_u: bool = True,
+                   workspace: Optional[Workspace] = None, stream=None,
+                   out_dtype: Optional[torch.dtype] = None):
+    """Up to three projections of the same x in one pass (lora_fwd_group): each dict has
+    base ((codes, absmax) or (w,)), bias, A, B, key and optionally residual.  Returns a
+    list of (y, u)."""
+    t, k = x.shape
+    _req(x, "x", x.dtype, (t, k))
+    out_dtype = out_dtype or x.dtype
+    flags = _flags(x.dtype, out_dtype)
+    if not 1 <= len(projs) <= 3:
+        raise ValueError("a group has 1 to 3 projections")
+    arr = (_abi.LoraProj * len(projs))()
+    outs = []
+    r = cfg.r
+    for i, pr in enumerate(projs):
+        fmt, n, bptr = _base_args(pr["base"], k)
+        bias, res = pr.get("bias"), pr.get("residual")
+        if bias is not None:
+            _req(bias, "bias", torch.bfloat16, (n,))
+        if res is not None:
+            _req(res, "residual", out_dtype, (t, n))
+        if r > 0:
+            _req(pr["A"], "A", torch.float32, (r, k))
+            _req(pr["B"], "B", torch.float32, (n, r))
+        y = torch.empty((t, n), dtype=out_dtype, device=x.device)
+        u = torch.empty((t, r), dtype=torch.float32, device=x.device) if (want_u and r > 0) else None
+        codes, absmax, w = (bptr + [None])[:3] if fmt == "nf4" else (None, None, bptr[0])
+        arr[i] = _abi.LoraProj(n, codes, absmax, w, _ptr(bias), _ptr(res), _ptr(pr["A"]) if r > 0 else None,
+                               _ptr(pr["B"]) if r > 0 else None, pr["key"], _ptr(y), _ptr(u))
+        outs.append((y, u))
+    need = int(lib().lora_group_workspace_size(t, k, arr, len(projs), r))
+    if need == 0:
+        raise ValueError(f"invalid group: {lib().msq_last_error().decode(errors='replace')}")
+    ws = _workspace(x.device, need, workspace)
+    check("lora_fwd_group", lib().lora_fwd_group(_ptr(x), t, k, arr, len(projs), cfg.c(flags), _ptr(ws), ws.numel(),
+                                                 _stream(stream)))
+    return outs
+
+
 def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
                  bias: Optional[torch.Tensor], A: Optional[torch.Tensor], B: Optional[torch.Tensor],
                  cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,

@@ -162,6 +162,53 @@ def lora_linear(x, A, B, base: Tuple[torch.Tensor, ...], bias, cfg: ops.Lora, ke
     return y
 
 
+class _Spec:
+    """One projection of a group: its base, bias and dropout key."""
+
+    __slots__ = ("base", "bias", "key")
+
+    def __init__(self, base, bias, key):
+        self.base, self.bias, self.key = base, bias, key
+
+
+class _LoraLinearGroup(torch.autograd.Function):
+    """Projections of one input (q/k/v, gate/up): the forward is one grouped library pass;
+    the backward runs each projection's library backward and sums their dx in projection
+    order (separate adds: an unsplit GEMM epilogue that reads the old dx waits on those
+    loads block by block)."""
+
+    @staticmethod
+    def forward(ctx, x, specs, cfg, *AB):
+        projs = [{"base": sp.base, "bias": sp.bias, "key": sp.key, "A": AB[2 * i], "B": AB[2 * i + 1]}
+                 for i, sp in enumerate(specs)]
+        outs = ops.lora_fwd_group(x, projs, cfg, want_u=True)
+        ctx.save_for_backward(x, *AB, *[u for _, u in outs])
+        ctx.specs, ctx.cfg = specs, cfg
+        return tuple(y for y, _ in outs)
+
+    @staticmethod
+    def backward(ctx, *dys):
+        P = len(ctx.specs)
+        saved = ctx.saved_tensors
+        x, AB, us = saved[0], saved[1:1 + 2 * P], saved[1 + 2 * P:]
+        dx, grads = None, []
+        for i, sp in enumerate(ctx.specs):
+            dxi, dA, dB = _bwd(sp.base, dys[i].contiguous(), x, AB[2 * i], AB[2 * i + 1], ctx.cfg, sp.key, u=us[i])
+            dx = dxi if dx is None else dx.add_(dxi)
+            grads += [dA, dB]
+        return (dx, None, None, *grads)
+
+
+def lora_linear_group(x, specs, As, Bs, cfg: ops.Lora):
+    """The projections of one input x, grouped: a tuple of outputs."""
+    if torch.is_grad_enabled() and (x.requires_grad or any(a.requires_grad or b.requires_grad
+                                                           for a, b in zip(As, Bs))):
+        AB = [t for pair in zip(As, Bs) for t in pair]
+        return _LoraLinearGroup.apply(x, specs, cfg, *AB)
+    projs = [{"base": sp.base, "bias": sp.bias, "key": sp.key, "A": a, "B": b} for sp, a, b in zip(specs, As, Bs)]
+    return tuple(y for y, _ in ops.lora_fwd_group(x, projs, cfg, want_u=False))
+
+
 class _SwiGLU(torch.autograd.Function):
     @staticmethod
     def forward(ctx, g, u):
@@ -262,11 +309,12 @@ class Stack:
 
     def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
                  window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
-                 n_slots: int = 2, glue: str = "native", base: str = "nf4"):
+                 n_slots: int = 2, glue: str = "native", base: str = "nf4", group: bool = True):
         assert mode in ("streamed", "resident")
         assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
         self.glue = glue
+        self.group = group
         self.cfg = ops.Lora(r, alpha, p_drop)
         self.window_blocks = window_blocks
         self.n_slots = n_slots
@@ -453,11 +501,22 @@ class Stack:
         return st
 
     # -- one layer -----------------------------------------------------------------
+    def _base(self, views, proj):
+        return ((views[(proj, "w")],) if self.layout.base == "bf16" else
+                (views[(proj, "codes")], views[(proj, "absmax")]))
+
+    def _lin_group(self, x, l, views, projs, step, micro):
+        """Projections of one input: one grouped pass (group=True) or one call each."""
+        if not self.group:
+            return tuple(self._lin(x, l, views, p, step, micro) for p in projs)
+        specs = [_Spec(self._base(views, p), views.get((p, "bias")), ops.rng_key(self.seed, step, micro, l, PROJ_ID[p]))
+                 for p in projs]
+        return lora_linear_group(x, specs, [self.A[l][p] for p in projs], [self.B[l][p] for p in projs], self.cfg)
+
     def _lin(self, x, l, views, proj, step, micro, value_unused=False, residual=None):
         key = ops.rng_key(self.seed, step, micro, l, PROJ_ID[proj])
         bias = views.get((proj, "bias"))
-        base = ((views[(proj, "w")],) if self.layout.base == "bf16" else
-                (views[(proj, "codes")], views[(proj, "absmax")]))
+        base = self._base(views, proj)
         if residual is not None and self.glue == "torch":
             return residual + lora_linear(x, self.A[l][proj], self.B[l][proj], base, bias, self.cfg, key,
                                           value_unused)
@@ -474,9 +533,10 @@ class Stack:
         T = h.shape[0]
         norm = rmsnorm_native if self.glue == "native" else rmsnorm
         xn = norm(h, self.ln1[l])
-        q = self._lin(xn, l, views, "q", step, micro).view(T, sh.heads, sh.head_dim)
-        k = self._lin(xn, l, views, "k", step, micro).view(T, sh.kv_heads, sh.head_dim)
-        v = self._lin(xn, l, views, "v", step, micro).view(T, sh.kv_heads, sh.head_dim)
+        q, k, v = self._lin_group(xn, l, views, ("q", "k", "v"), step, micro)
+        q = q.view(T, sh.heads, sh.head_dim)
+        k = k.view(T, sh.kv_heads, sh.head_dim)
+        v = v.view(T, sh.kv_heads, sh.head_dim)
         cos, sin = self.cos[:T], self.sin[:T]
         if self.glue == "native":
             q, k = _RoPE.apply(q, cos, sin), _RoPE.apply(k, cos, sin)
@@ -485,8 +545,7 @@ class Stack:
         att = causal_gqa_attention(q, k, v, self.mask_add[:T, :T])
         h1 = self._lin(att, l, views, "o", step, micro, residual=h)
         xn2 = norm(h1, self.ln2[l])
-        g = self._lin(xn2, l, views, "gate", step, micro)
-        u = self._lin(xn2, l, views, "up", step, micro)
+        g, u = self._lin_group(xn2, l, views, ("gate", "up"), step, micro)
         a = _SwiGLU.apply(g, u) if self.glue == "native" else torch.nn.functional.silu(g) * u
         return self._lin(a, l, views, "down", step, micro, value_unused=recompute, residual=h1)
 

@@ -155,6 +155,32 @@ def test_stream_load_rejects_bad_arguments():
     assert L.nf4_stream_load(None, 0, 8, None, 0, None, 0, 4, None) == 0
 
 
+def test_group_rejects_bad_arguments():
+    L = abi.lib()
+    key = abi.RngKey(0, 0, 0, 0, 0)
+
+    def proj(n=128, w=None, codes=FAKE, y=FAKE):
+        return abi.LoraProj(n, codes, FAKE if codes else None, w, None, None, FAKE, FAKE, key, y, None)
+
+    two = (abi.LoraProj * 2)(proj(), proj(n=64))
+    need = L.lora_group_workspace_size(8, 128, two, 2, 16)
+    assert need > 0
+    cfg = abi.LoraCfg(16, 32.0, 0.0)
+    assert L.lora_fwd_group(FAKE, 8, 128, two, 0, cfg, FAKE, need, None) == abi.MSQ_E_INVAL
+    assert L.lora_fwd_group(FAKE, 8, 128, two, 4, cfg, FAKE, need, None) == abi.MSQ_E_INVAL
+    assert L.lora_fwd_group(FAKE, 8, 128, two, 2, cfg, FAKE, need - 1, None) == abi.MSQ_E_WORKSPACE
+    assert L.lora_fwd_group(FAKE, 8, 128, two, 2, abi.LoraCfg(16, 32.0, 0.0, abi.MSQ_U_ONLY), FAKE, need,
+                            None) == abi.MSQ_E_INVAL
+    mixed = (abi.LoraProj * 2)(proj(), proj(codes=None, w=FAKE))
+    assert L.lora_fwd_group(FAKE, 8, 128, mixed, 2, cfg, FAKE, need, None) == abi.MSQ_E_INVAL
+    assert "mixed" in _err()
+    bad_n = (abi.LoraProj * 2)(proj(), proj(n=100))
+    assert L.lora_group_workspace_size(8, 128, bad_n, 2, 16) == 0
+    assert L.lora_fwd_group(FAKE, 8, 128, bad_n, 2, cfg, FAKE, need, None) == abi.MSQ_E_SHAPE
+    no_y = (abi.LoraProj * 1)(proj(y=None))
+    assert L.lora_fwd_group(FAKE, 8, 128, no_y, 1, cfg, FAKE, need, None) == abi.MSQ_E_INVAL
+
+
 def test_workspace_size_depends_on_shape_only():
     L = abi.lib()
     a = L.nf4_lora_workspace_size(512, 5120, 27648, 16)
