@@ -185,6 +185,17 @@ def cpu_baseline(seconds_hint=True) -> dict:
             "s_per_step_extrapolated": step_s}
 
 
+def h2d_busy(window, ms_per_step: float, ceiling: float) -> dict:
+    """Copy-stream busy time per step (the window's own events around each window copy)
+    and the H2D rate while copying, against the measured ceiling."""
+    if not window or not window.get("copies_timed"):
+        return {}
+    busy = window["copy_ms"]
+    rate = window["bytes_copied"] / (busy * 1e-3) / 1e9 if busy > 0 else 0.0
+    return {"copy_busy_ms_per_step": round(busy, 1), "copy_busy_frac": round(busy / ms_per_step, 3),
+            "GBps_while_copying": round(rate, 1), "frac_while_copying": round(rate / ceiling, 3)}
+
+
 def rocprof_summary(d: str) -> int:
     """Summarise rocprofv3 CSV output found under directory d (kernel stats and/or
     per-dispatch counter collections) as markdown on stdout."""
@@ -258,6 +269,8 @@ def main() -> int:
                     help="frozen base format: NF4, or bf16 (the pages' bf16 streaming variant, 4x the bytes)")
     ap.add_argument("--glue", choices=("native", "torch"), default="native",
                     help="pointwise block glue: the library's fused kernels, or the unfused PyTorch chain")
+    ap.add_argument("--window-release", action="store_true",
+                    help="release whole windows instead of layer by layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the streamed steps without per-launch events (no roofline figures)")
@@ -287,7 +300,7 @@ def main() -> int:
         t_build = time.time()
         st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=0.0,
                             window_blocks=args.window_blocks, n_slots=args.slots, mode=mode, glue=args.glue,
-                            base=args.base)
+                            base=args.base, layer_release=not args.window_release)
         torch.cuda.synchronize()
         log(f"{mode}: built {args.layers} layers in {time.time() - t_build:.1f}s "
             f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
@@ -379,7 +392,8 @@ def main() -> int:
         "h2d": {"bytes_per_step": int(h2d_bytes), "achieved_GBps": round(h2d_rate, 1),
                 "ceiling_GBps": round(ceiling, 1), "frac": round(h2d_rate / ceiling, 3),
                 "windows_copied_per_step": streamed["window"]["windows_copied"] if streamed["window"] else 0,
-                "windows_reused_per_step": streamed["window"]["windows_reused"] if streamed["window"] else 0},
+                "windows_reused_per_step": streamed["window"]["windows_reused"] if streamed["window"] else 0,
+                **h2d_busy(streamed["window"], ms, ceiling)},
         "kernels": kernels,
         "gemm_shapes": shapes,
         "hbm_kernels": hbm,

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 6
+#define MSQ_ABI_VERSION 8
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -334,6 +334,9 @@ typedef struct {
   uint64_t bytes_copied;    /* host-to-device bytes issued */
   uint64_t windows_copied;  /* window loads that issued copies */
   uint64_t windows_reused;  /* prefetches satisfied by a slot that still held the window */
+  double copy_ms;           /* time the copy stream spent in window copies (events around
+                               each window's copies, after its wait for the slot) */
+  uint64_t copies_timed;    /* window copies included in copy_ms */
 } msq_window_stats;
 
 size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks,
@@ -347,13 +350,23 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
  * then marks it ready.  If a free slot still holds this window's bytes, no copy is
  * issued.  No free slot: MSQ_E_ORDER. */
 int block_stream_prefetch(msq_window* w, int first_layer);
-/* Make `compute` wait until the window holding `layer` has arrived, and return
+/* Make `compute` wait until `layer` (of a prefetched window) has arrived, and return
  * the layer's device address.  Window not prefetched: MSQ_E_ORDER. */
 int block_stream_acquire(msq_window* w, int layer, msq_stream_t compute, const void** dev_blob);
 /* Mark the window beginning at first_layer as no longer read by work queued so
- * far on `compute`; its slot may then be refilled.  Not held: MSQ_E_ORDER. */
+ * far on `compute` (its layers not yet released, in ascending order); its slot may then
+ * be refilled.  Not held: MSQ_E_ORDER. */
 int block_stream_release(msq_window* w, int first_layer, msq_stream_t compute);
-int block_stream_stats(const msq_window* w, msq_window_stats* out);
+/* Release one layer of a held window as soon as the work queued so far on `compute` no
+ * longer reads it.  Once every layer of the window is released the slot may be refilled;
+ * the next window's layers are then copied in the order these layers were released, each
+ * copy waiting only for the layer it overwrites, and block_stream_acquire waits only for
+ * the acquired layer's own copy.  Window not held: MSQ_E_ORDER; released twice:
+ * MSQ_E_ORDER. */
+int block_stream_release_layer(msq_window* w, int layer, msq_stream_t compute);
+/* Statistics since creation.  Waits for the issued copies to finish so that their
+ * durations are included (call it outside timed regions). */
+int block_stream_stats(msq_window* w, msq_window_stats* out);
 /* Waits for the window's outstanding copies, then frees its events. */
 int block_stream_destroy(msq_window* w);
 

@@ -40,7 +40,8 @@ class LoraCfg(ctypes.Structure):
 
 class WindowStats(ctypes.Structure):
     _fields_ = [("bytes_copied", ctypes.c_uint64), ("windows_copied", ctypes.c_uint64),
-                ("windows_reused", ctypes.c_uint64)]
+                ("windows_reused", ctypes.c_uint64), ("copy_ms", ctypes.c_double),
+                ("copies_timed", ctypes.c_uint64)]
 
 
 class QuantJob(ctypes.Structure):
@@ -106,6 +107,7 @@ _SIG = {
     "block_stream_prefetch": (ctypes.c_int, [_P, ctypes.c_int]),
     "block_stream_acquire": (ctypes.c_int, [_P, ctypes.c_int, _P, _P]),
     "block_stream_release": (ctypes.c_int, [_P, ctypes.c_int, _P]),
+    "block_stream_release_layer": (ctypes.c_int, [_P, ctypes.c_int, _P]),
     "block_stream_stats": (ctypes.c_int, [_P, _P]),
     "block_stream_destroy": (ctypes.c_int, [_P]),
     "msq_timing_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -113,7 +115,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 6  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 8  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

@@ -10,12 +10,17 @@
 // one loads: the default is two slots.  More slots let the copies run further ahead,
 // and single-layer slots let a slot be refilled as soon as its one layer is done.
 //
-// Ordering: the copy stream waits on a slot's "freed" event (recorded on the
-// compute stream by release) before overwriting it, and records the slot's "ready"
-// event after its copies; acquire makes the compute stream wait on "ready".  The host
-// never blocks.  A prefetch of a window that a free slot still holds issues no copy
-// (the two windows in the slots at the end of the forward are the first two the
-// backward needs).
+// Ordering is kept per layer position inside a slot: the copy stream waits on the
+// position's "freed" event (recorded on the compute stream when the layer that held it
+// was released) before overwriting it, and records the position's "ready" event after
+// its copy; acquire makes the compute stream wait on the layer's own "ready".  A window
+// is still claimed and copied as one unit, but its layers are copied in the order the
+// slot's previous layers were released (ascending after a forward, descending after a
+// backward), so the first layer of the next window lands as soon as the first layer of
+// the last one is done, and compute on a layer starts as soon as that layer has landed.
+// The host never blocks.  A prefetch of a window that a free slot still holds issues no
+// copy (the windows in the slots at the end of the forward are the first the backward
+// needs).
 #include <string.h>
 
 #include <algorithm>
@@ -40,13 +45,23 @@ struct msq_window {
   size_t slot_bytes = 0;
   std::vector<char*> slot_base;
   hipStream_t copy = nullptr;
+  // per (slot, position) events, index slot * window_blocks + position
   std::vector<hipEvent_t> ready, freed;
   std::vector<char> freed_recorded;
+  std::vector<std::vector<int>> release_order;  // positions in the order they were released
+  std::vector<std::vector<char>> released;      // per slot and position: released since claimed
   std::vector<int> slot_window;  // window whose bytes the slot holds (or will hold)
   std::vector<int> state;
   std::vector<uint64_t> release_tick;
   uint64_t tick = 0;
-  msq_window_stats stats = {0, 0, 0};
+  msq_window_stats stats = {0, 0, 0, 0.0, 0};
+  // copy timing: one (start, end) event pair per issued layer copy, from a ring; a pair is
+  // read (and its duration added to stats.copy_ms) when the ring comes round to it or when
+  // the statistics are asked for
+  static constexpr int TIMING_RING = 64;
+  hipEvent_t t_start[TIMING_RING] = {}, t_end[TIMING_RING] = {};
+  bool t_pending[TIMING_RING] = {};
+  int t_next = 0;
 };
 
 namespace {
@@ -61,6 +76,19 @@ size_t max_window_bytes(const size_t* blob_bytes, int n_layers, int wb) {
   size_t m = 0;
   for (int f = 0; f < n_layers; f += wb) m = std::max(m, window_bytes(blob_bytes, n_layers, f, wb));
   return m;
+}
+
+// Adds the duration of timing pair i to the statistics once its copies are done.
+hipError_t collect_timing(msq_window* w, int i) {
+  if (!w->t_pending[i]) return hipSuccess;
+  hipError_t e = hipEventSynchronize(w->t_end[i]);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, w->t_start[i], w->t_end[i]);
+  if (e != hipSuccess) return e;
+  w->stats.copy_ms += ms;
+  w->stats.copies_timed++;
+  w->t_pending[i] = false;
+  return hipSuccess;
 }
 
 int find_slot(const msq_window* w, int win, int state) {
@@ -125,24 +153,36 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
   w->slot_bytes = need / n_slots;
   w->slot_base.resize(n_slots);
   for (int i = 0; i < n_slots; ++i) w->slot_base[i] = (char*)dev_arena + (size_t)i * w->slot_bytes;
-  w->ready.assign(n_slots, nullptr);
-  w->freed.assign(n_slots, nullptr);
-  w->freed_recorded.assign(n_slots, 0);
+  const int ne = n_slots * window_blocks;
+  w->ready.assign(ne, nullptr);
+  w->freed.assign(ne, nullptr);
+  w->freed_recorded.assign(ne, 0);
+  w->release_order.assign(n_slots, std::vector<int>());
+  w->released.assign(n_slots, std::vector<char>(window_blocks, 0));
   w->slot_window.assign(n_slots, -1);
   w->state.assign(n_slots, SLOT_FREE);
   w->release_tick.assign(n_slots, 0);
   w->copy = (hipStream_t)copy_stream;
-  for (int i = 0; i < n_slots; ++i) {
-    hipError_t e = hipEventCreateWithFlags(&w->ready[i], hipEventDisableTiming);
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < ne && e == hipSuccess; ++i) {
+    e = hipEventCreateWithFlags(&w->ready[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&w->freed[i], hipEventDisableTiming);
-    if (e != hipSuccess) {
-      for (int j = 0; j < n_slots; ++j) {
-        if (w->ready[j]) (void)hipEventDestroy(w->ready[j]);
-        if (w->freed[j]) (void)hipEventDestroy(w->freed[j]);
-      }
-      delete w;
-      return hip_error(e, "block_stream_create: hipEventCreate");
+  }
+  for (int i = 0; i < msq_window::TIMING_RING && e == hipSuccess; ++i) {
+    e = hipEventCreate(&w->t_start[i]);
+    if (e == hipSuccess) e = hipEventCreate(&w->t_end[i]);
+  }
+  if (e != hipSuccess) {
+    for (int j = 0; j < ne; ++j) {
+      if (w->ready[j]) (void)hipEventDestroy(w->ready[j]);
+      if (w->freed[j]) (void)hipEventDestroy(w->freed[j]);
     }
+    for (int j = 0; j < msq_window::TIMING_RING; ++j) {
+      if (w->t_start[j]) (void)hipEventDestroy(w->t_start[j]);
+      if (w->t_end[j]) (void)hipEventDestroy(w->t_end[j]);
+    }
+    delete w;
+    return hip_error(e, "block_stream_create: hipEventCreate");
   }
   *out = w;
   return MSQ_OK;
@@ -157,6 +197,8 @@ int block_stream_prefetch(msq_window* w, int first_layer) {
   int slot = find_slot(w, win, SLOT_FREE);
   if (slot >= 0) {  // the free slot still holds this window's bytes
     w->state[slot] = SLOT_HELD;
+    w->release_order[slot].clear();
+    std::fill(w->released[slot].begin(), w->released[slot].end(), 0);
     w->stats.windows_reused++;
     return MSQ_OK;
   }
@@ -167,18 +209,37 @@ int block_stream_prefetch(msq_window* w, int first_layer) {
   if (slot < 0)
     return set_error(MSQ_E_ORDER, "block_stream_prefetch: no free slot for window %d (release a window first)", win);
   hipError_t e = hipSuccess;
-  if (w->freed_recorded[slot]) e = hipStreamWaitEvent(w->copy, w->freed[slot], 0);
   // the slot's old contents are about to be overwritten
   w->slot_window[slot] = -1;
+  const int wb = w->window_blocks;
+  const int count = std::min(wb, w->n_layers - first_layer);
+  // copy order: the positions in the order the slot's last layers were released, then
+  // any position not released before (a fresh slot, or a shorter last window)
+  std::vector<int> order = w->release_order[slot];
+  for (int q = 0; q < wb; ++q)
+    if (std::find(order.begin(), order.end(), q) == order.end()) order.push_back(q);
   size_t total = 0;
-  for (int l = first_layer; e == hipSuccess && l < first_layer + w->window_blocks && l < w->n_layers; ++l) {
-    e = hipMemcpyAsync(w->slot_base[slot] + w->offset[l], w->host[l], w->bytes[l], hipMemcpyHostToDevice, w->copy);
+  for (int q : order) {
+    if (q >= count || e != hipSuccess) continue;
+    const int l = first_layer + q;
+    const int ev = slot * wb + q;
+    if (w->freed_recorded[ev]) e = hipStreamWaitEvent(w->copy, w->freed[ev], 0);
+    const int ti = w->t_next;
+    w->t_next = (w->t_next + 1) % msq_window::TIMING_RING;
+    if (e == hipSuccess) e = collect_timing(w, ti);  // the ring's oldest pair, long complete
+    if (e == hipSuccess) e = hipEventRecord(w->t_start[ti], w->copy);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(w->slot_base[slot] + w->offset[l], w->host[l], w->bytes[l], hipMemcpyHostToDevice, w->copy);
+    if (e == hipSuccess) e = hipEventRecord(w->t_end[ti], w->copy);
+    if (e == hipSuccess) w->t_pending[ti] = true;
+    if (e == hipSuccess) e = hipEventRecord(w->ready[ev], w->copy);
     total += w->bytes[l];
   }
-  if (e == hipSuccess) e = hipEventRecord(w->ready[slot], w->copy);
   if (e != hipSuccess) return hip_error(e, "block_stream_prefetch: copy");
   w->slot_window[slot] = win;
   w->state[slot] = SLOT_HELD;
+  w->release_order[slot].clear();
+  std::fill(w->released[slot].begin(), w->released[slot].end(), 0);
   w->stats.bytes_copied += total;
   w->stats.windows_copied++;
   return MSQ_OK;
@@ -190,11 +251,38 @@ int block_stream_acquire(msq_window* w, int layer, msq_stream_t compute, const v
   const int win = layer / w->window_blocks;
   const int slot = find_slot(w, win, SLOT_HELD);
   if (slot < 0) return set_error(MSQ_E_ORDER, "block_stream_acquire: window %d (layer %d) was not prefetched", win, layer);
-  const hipError_t e = hipStreamWaitEvent((hipStream_t)compute, w->ready[slot], 0);
+  const hipError_t e =
+      hipStreamWaitEvent((hipStream_t)compute, w->ready[slot * w->window_blocks + layer % w->window_blocks], 0);
   if (e != hipSuccess) return hip_error(e, "block_stream_acquire: hipStreamWaitEvent");
   *dev_blob = w->slot_base[slot] + w->offset[layer];
   return MSQ_OK;
 }
+
+}  // extern "C"
+
+namespace {
+
+// Records that position q of `slot` is no longer read by work queued on `compute`; the slot
+// becomes free once every position of its window is released.
+int release_position(msq_window* w, int slot, int q, hipStream_t compute, const char* fn) {
+  const int wb = w->window_blocks;
+  const int count = std::min(wb, w->n_layers - w->slot_window[slot] * wb);
+  if (w->released[slot][q]) return set_error(MSQ_E_ORDER, "%s: layer %d was already released", fn, w->slot_window[slot] * wb + q);
+  const hipError_t e = hipEventRecord(w->freed[slot * wb + q], compute);
+  if (e != hipSuccess) return hip_error(e, fn);
+  w->freed_recorded[slot * wb + q] = 1;
+  w->released[slot][q] = 1;
+  w->release_order[slot].push_back(q);
+  if ((int)w->release_order[slot].size() == count) {
+    w->state[slot] = SLOT_FREE;
+    w->release_tick[slot] = ++w->tick;
+  }
+  return MSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
 
 int block_stream_release(msq_window* w, int first_layer, msq_stream_t compute) {
   if (!w) return set_error(MSQ_E_INVAL, "block_stream_release: null window");
@@ -203,16 +291,30 @@ int block_stream_release(msq_window* w, int first_layer, msq_stream_t compute) {
   const int win = first_layer / w->window_blocks;
   const int slot = find_slot(w, win, SLOT_HELD);
   if (slot < 0) return set_error(MSQ_E_ORDER, "block_stream_release: window %d is not held", win);
-  const hipError_t e = hipEventRecord(w->freed[slot], (hipStream_t)compute);
-  if (e != hipSuccess) return hip_error(e, "block_stream_release: hipEventRecord");
-  w->freed_recorded[slot] = 1;
-  w->state[slot] = SLOT_FREE;
-  w->release_tick[slot] = ++w->tick;
+  const int count = std::min(w->window_blocks, w->n_layers - first_layer);
+  for (int q = 0; q < count; ++q) {
+    if (w->released[slot][q]) continue;
+    const int rc = release_position(w, slot, q, (hipStream_t)compute, "block_stream_release");
+    if (rc) return rc;
+  }
   return MSQ_OK;
 }
 
-int block_stream_stats(const msq_window* w, msq_window_stats* out) {
+int block_stream_release_layer(msq_window* w, int layer, msq_stream_t compute) {
+  if (!w) return set_error(MSQ_E_INVAL, "block_stream_release_layer: null window");
+  if (layer < 0 || layer >= w->n_layers) return set_error(MSQ_E_INVAL, "block_stream_release_layer: layer %d out of range", layer);
+  const int win = layer / w->window_blocks;
+  const int slot = find_slot(w, win, SLOT_HELD);
+  if (slot < 0) return set_error(MSQ_E_ORDER, "block_stream_release_layer: window %d (layer %d) is not held", win, layer);
+  return release_position(w, slot, layer % w->window_blocks, (hipStream_t)compute, "block_stream_release_layer");
+}
+
+int block_stream_stats(msq_window* w, msq_window_stats* out) {
   if (!w || !out) return set_error(MSQ_E_INVAL, "block_stream_stats: null pointer");
+  for (int i = 0; i < msq_window::TIMING_RING; ++i) {
+    const hipError_t e = collect_timing(w, i);
+    if (e != hipSuccess) return hip_error(e, "block_stream_stats: copy timing");
+  }
   *out = w->stats;
   return MSQ_OK;
 }
@@ -220,13 +322,17 @@ int block_stream_stats(const msq_window* w, msq_window_stats* out) {
 int block_stream_destroy(msq_window* w) {
   if (!w) return MSQ_OK;
   hipError_t e = hipSuccess;
-  for (int i = 0; i < w->n_slots; ++i) {
+  for (size_t i = 0; i < w->ready.size(); ++i) {
     if (w->ready[i]) {
       const hipError_t e1 = hipEventSynchronize(w->ready[i]);
       if (e == hipSuccess) e = e1;
       (void)hipEventDestroy(w->ready[i]);
     }
     if (w->freed[i]) (void)hipEventDestroy(w->freed[i]);
+  }
+  for (int i = 0; i < msq_window::TIMING_RING; ++i) {
+    if (w->t_start[i]) (void)hipEventDestroy(w->t_start[i]);
+    if (w->t_end[i]) (void)hipEventDestroy(w->t_end[i]);
   }
   delete w;
   return e == hipSuccess ? MSQ_OK : hip_error(e, "block_stream_destroy");

@@ -469,11 +469,14 @@ class BlockStreamWindow:
     def release(self, first_layer: int, stream=None) -> None:
         check("block_stream_release", lib().block_stream_release(self._h, first_layer, _stream(stream)))
 
+    def release_layer(self, layer: int, stream=None) -> None:
+        check("block_stream_release_layer", lib().block_stream_release_layer(self._h, layer, _stream(stream)))
+
     def stats(self) -> dict:
         s = _abi.WindowStats()
         check("block_stream_stats", lib().block_stream_stats(self._h, ctypes.byref(s)))
         return {"bytes_copied": s.bytes_copied, "windows_copied": s.windows_copied,
-                "windows_reused": s.windows_reused}
+                "windows_reused": s.windows_reused, "copy_ms": s.copy_ms, "copies_timed": s.copies_timed}
 
     def close(self) -> None:
         if getattr(self, "_h", None):

@@ -309,12 +309,14 @@ class Stack:
 
     def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
                  window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
-                 n_slots: int = 2, glue: str = "native", base: str = "nf4", group: bool = True):
+                 n_slots: int = 2, glue: str = "native", base: str = "nf4", group: bool = True,
+                 layer_release: bool = True):
         assert mode in ("streamed", "resident")
         assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
         self.glue = glue
         self.group = group
+        self.layer_release = layer_release
         self.cfg = ops.Lora(r, alpha, p_drop)
         self.window_blocks = window_blocks
         self.n_slots = n_slots
@@ -568,7 +570,8 @@ class Stack:
                           scale: float) -> List[torch.Tensor]:
         """Block-major pass over the micro-batches toks (dropout keys micros): each window is
         fetched once and runs every micro-batch before the next window, forward and
-        backward.  Each micro-batch's loss is scaled by `scale` before its backward (1.0:
+        backward.  Streamed, each layer is acquired just before its first use and released
+        right after its last, so a window's slot refills layer by layer.  Each micro-batch's loss is scaled by `scale` before its backward (1.0:
         no scaling op); gradients accumulate into .grad, for every adapter in micro-batch
         order.  Returns the unscaled losses."""
         L = self.shape.layers
@@ -584,15 +587,19 @@ class Stack:
         with torch.no_grad():
             for wi, w in enumerate(wins):
                 layers = range(w, min(w + self.window_blocks, L))
-                views = {l: self._views(l) for l in layers}
+                views = {}
                 for m in range(M):
                     for l in layers:
+                        if l not in views:  # acquired just before first use: waits for this layer only
+                            views[l] = self._views(l)
                         bounds[m].append(hs[m])
                         hs[m] = self.layer_forward(hs[m], l, views[l], step, micros[m])
-                if streamed:
+                        if streamed and m == M - 1 and self.layer_release:
+                            self.window.release_layer(l)
+                if streamed and not self.layer_release:
                     self.window.release(w)
-                    if wi + ahead < len(wins):
-                        self.window.prefetch(wins[wi + ahead])
+                if streamed and wi + ahead < len(wins):
+                    self.window.prefetch(wins[wi + ahead])
         dhs: List[torch.Tensor] = []
         losses: List[torch.Tensor] = []
         for m in range(M):
@@ -613,19 +620,23 @@ class Stack:
                 self.window.prefetch(w)
         for wi, w in enumerate(rw):
             layers = range(w, min(w + self.window_blocks, L))
-            views = {l: self._views(l) for l in layers}
+            views = {}
             for m in range(M):
                 for l in reversed(layers):
+                    if l not in views:
+                        views[l] = self._views(l)
                     x_in = bounds[m][l].detach().requires_grad_()
                     with torch.enable_grad():
                         out = self.layer_forward(x_in, l, views[l], step, micros[m], recompute=True)
                     out.backward(dhs[m])
                     dhs[m] = x_in.grad
                     bounds[m][l] = None
-            if streamed:
+                    if streamed and m == M - 1 and self.layer_release:
+                        self.window.release_layer(l)
+            if streamed and not self.layer_release:
                 self.window.release(w)
-                if wi + ahead < len(rw):
-                    self.window.prefetch(rw[wi + ahead])
+            if streamed and wi + ahead < len(rw):
+                self.window.prefetch(rw[wi + ahead])
         return losses
 
     def params(self) -> List[torch.nn.Parameter]:

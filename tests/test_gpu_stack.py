@@ -225,6 +225,47 @@ def test_window_protocol():
     w.close()
 
 
+def test_window_per_layer_release():
+    """Layers released one by one (in any order) free the slot only when all are released;
+    the next window's bytes arrive whole whatever the release order; a layer cannot be
+    released twice or from a window that is not held."""
+    blobs = []
+    for i in range(9):
+        b = torch.empty(4096 + 256 * i, dtype=torch.uint8, pin_memory=True)
+        b.copy_(torch.arange(b.numel(), dtype=torch.int64).mul_(7).add_(11 * i).remainder_(253).to(torch.uint8))
+        blobs.append(b)
+    w = msq.BlockStreamWindow(blobs, 3, n_slots=2)
+    w.prefetch(0)
+    w.prefetch(3)
+    for l in range(6):
+        assert torch.equal(w.acquire_view(l).cpu(), blobs[l])
+    w.release_layer(2)
+    w.release_layer(0)
+    with pytest.raises(MsqError) as e:
+        w.prefetch(6)                               # window 0 still has layer 1 held
+    assert e.value.code == MSQ_E_ORDER
+    with pytest.raises(MsqError) as e:
+        w.release_layer(2)
+    assert e.value.code == MSQ_E_ORDER
+    w.release_layer(1)
+    w.prefetch(6)                                   # copied in release order 2, 0, 1
+    for l in (8, 6, 7):
+        assert torch.equal(w.acquire_view(l).cpu(), blobs[l])
+    for l in (5, 4, 3):
+        w.release_layer(l)
+    w.prefetch(3)                                   # the slot still holds window 1: reused
+    assert torch.equal(w.acquire_view(4).cpu(), blobs[4])
+    with pytest.raises(MsqError) as e:
+        w.release_layer(0)                          # window 0 is no longer held
+    assert e.value.code == MSQ_E_ORDER
+    s = w.stats()
+    assert s["windows_copied"] == 3 and s["windows_reused"] == 1 and s["copies_timed"] == 9
+    assert s["copy_ms"] > 0
+    w.release(3)
+    w.release(6)
+    w.close()
+
+
 def test_selective_recompute_gives_identical_gradients():
     """The backward's rerun skips the last projection's frozen-base product (its output
     is never read); gradients must be bit-identical to a full recompute."""
