@@ -258,7 +258,9 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=64, help="stack depth (64 = the 32B shape)")
     ap.add_argument("--window-blocks", type=int, default=4,
                     help="layers per window slot (blocks per streamed window)")
-    ap.add_argument("--slots", type=int, default=3, help="window slots in the device arena (prefetch depth + 1)")
+    ap.add_argument("--slots", type=int, default=5,
+                    help="window slots in the device arena: the deepest prefetch whose peak device memory "
+                         "stays under the pages' 10.95 GB streamed peak for this configuration")
     ap.add_argument("--resident", action="store_true",
                     help="also time the same step with the whole base resident in device memory")
     ap.add_argument("--ga", type=int, default=1,
@@ -293,8 +295,8 @@ def main() -> int:
     def batch(st, s: int):
         """One optimizer step's tokens: [T], or [ga, T] micro-batches."""
         if args.ga == 1:
-            return S.random_tokens(0, s, T, shape.vocab, st.dev)
-        return torch.stack([S.random_tokens(0, s * args.ga + m, T, shape.vocab, st.dev) for m in range(args.ga)])
+            return S.random_tokens(0, s, T, shape.vocab, "cpu")
+        return torch.stack([S.random_tokens(0, s * args.ga + m, T, shape.vocab, "cpu") for m in range(args.ga)])
 
     def run(mode: str, kernel_timing: bool):
         t_build = time.time()

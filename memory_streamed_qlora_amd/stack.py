@@ -363,9 +363,17 @@ class Stack:
         self.ln2.append(ln2.to(self.dev, torch.float32))
 
     def set_globals(self, emb: torch.Tensor, lm: torch.Tensor, lnf: torch.Tensor) -> None:
-        self.emb = emb.to(self.dev, torch.bfloat16).contiguous()
+        """The frozen token embedding stays in host memory (a step gathers only its T rows
+        and copies them over); the frozen lm_head and final norm live on the device."""
+        self.emb = emb.detach().to("cpu", torch.bfloat16).contiguous()
         self.lm = lm.to(self.dev, torch.bfloat16).contiguous()
         self.lnf = lnf.to(self.dev, torch.float32)
+
+    def _embed(self, tokens: torch.Tensor) -> torch.Tensor:
+        """Rows of the host embedding for `tokens` (host or device), as fp32 on the device."""
+        idx = tokens if tokens.device.type == "cpu" else tokens.cpu()
+        rows = self.emb.index_select(0, idx).pin_memory()
+        return rows.to(self.dev, non_blocking=True).float()
 
     def finalize(self) -> None:
         params = [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
@@ -578,7 +586,7 @@ class Stack:
         M = len(toks)
         wins = self._windows()
         streamed = self.mode == "streamed"
-        hs = [self.emb[t].float() for t in toks]
+        hs = [self._embed(t) for t in toks]
         bounds: List[List[torch.Tensor]] = [[] for _ in range(M)]
         ahead = self.n_slots
         if streamed:
@@ -607,12 +615,9 @@ class Stack:
             with torch.enable_grad():
                 norm = rmsnorm_native if self.glue == "native" else rmsnorm
                 hn = norm(hf, self.lnf).to(torch.bfloat16)
-                logits = torch.matmul(hn, self.lm.t()).float()
-                loss = torch.nn.functional.cross_entropy(logits[:-1], toks[m][1:])
-                (loss if scale == 1.0 else loss * scale).backward()
+            loss = self._lm_loss_backward(hn, toks[m], scale)
             dhs.append(hf.grad)
-            losses.append(loss.detach())
-            del logits
+            losses.append(loss)
         hs = None
         rw = wins[::-1]
         if streamed:
@@ -638,6 +643,29 @@ class Stack:
             if streamed and wi + ahead < len(rw):
                 self.window.prefetch(rw[wi + ahead])
         return losses
+
+    CE_CHUNK = 128  # tokens per lm_head / cross-entropy chunk
+
+    def _lm_loss_backward(self, hn: torch.Tensor, tokens: torch.Tensor, scale: float) -> torch.Tensor:
+        """Mean next-token cross-entropy of the frozen lm_head over hn [T, hidden] (bf16),
+        back-propagated into hn's graph (each chunk's loss scaled by `scale`).  The logits
+        are formed CE_CHUNK tokens at a time, so their fp32 working set stays ~0.3 GB at a
+        152064-entry vocabulary instead of ~1.2 GB.  Returns the (unscaled) loss."""
+        T = hn.shape[0]
+        n = T - 1
+        tgt = tokens[1:].to(self.dev, non_blocking=True)
+        hd = hn.detach().requires_grad_()
+        total = None
+        for c0 in range(0, n, self.CE_CHUNK):
+            c1 = min(n, c0 + self.CE_CHUNK)
+            with torch.enable_grad():
+                logits = torch.matmul(hd[c0:c1], self.lm.t()).float()
+                lc = torch.nn.functional.cross_entropy(logits, tgt[c0:c1], reduction="sum") / n
+                (lc if scale == 1.0 else lc * scale).backward()
+            total = lc.detach() if total is None else total + lc.detach()
+            del logits
+        hn.backward(hd.grad)
+        return total
 
     def params(self) -> List[torch.nn.Parameter]:
         return [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
