@@ -24,7 +24,7 @@ def _run(sh, mode, steps, window_blocks, n_slots, p_drop, cfg_id, every):
     losses, norms = [], []
     t0 = time.perf_counter()
     for s in range(steps):
-        loss, gn = st.train_step(S.random_tokens(0, s, 512, sh.vocab, st.dev))
+        loss, gn = st.train_step(S.random_tokens(0, s, 512, sh.vocab, "cpu"))
         losses.append(loss)
         norms.append(gn)
         if (s + 1) % every == 0:
@@ -33,11 +33,12 @@ def _run(sh, mode, steps, window_blocks, n_slots, p_drop, cfg_id, every):
                   f"{(time.perf_counter() - t0) / (s + 1) * 1e3:.0f} ms/step", flush=True)
     torch.cuda.synchronize()
     secs = time.perf_counter() - t0
+    peak = torch.cuda.max_memory_allocated() / 1e9  # before the state copies below
     out = {"losses": [l.item() for l in losses], "norms": [g.item() for g in norms],
            "state": {k: v.clone() for k, v in st.state_tensors().items()},
            "stats": st.window.stats() if st.window else None,
            "ms_per_step": secs / steps * 1e3,
-           "peak_gb": torch.cuda.max_memory_allocated() / 1e9}
+           "peak_gb": peak}
     st.close()
     del st
     torch.cuda.empty_cache()
@@ -63,6 +64,19 @@ def test_qwen7b_200_steps_streamed_equals_resident():
     n_win = 28 // 4
     assert stm["stats"]["windows_copied"] + stm["stats"]["windows_reused"] == steps * 2 * n_win
     print(f"7B: streamed {stm['ms_per_step']:.1f} ms/step, peak {stm['peak_gb']:.2f} GB; "
+          f"resident {res['ms_per_step']:.1f} ms/step, peak {res['peak_gb']:.2f} GB", flush=True)
+
+
+def test_qwen32b_200_steps_streamed_equals_resident():
+    """Qwen2.5-32B-shaped stack, 64 layers streamed in windows of 4 blocks through five
+    slots (the benchmark's window), LoRA r16 alpha32 dropout 0.0, 512 tokens, 200 AdamW
+    steps: every loss, grad norm, adapter, gradient and AdamW moment equal."""
+    sh, steps = S.QWEN25_32B, 200
+    stm = _run(sh, "streamed", steps, 4, 5, 0.0, 4, every=20)
+    res = _run(sh, "resident", steps, 4, 5, 0.0, 4, every=20)
+    _assert_bitwise(res, stm)
+    assert res["losses"][0] != res["losses"][-1]
+    print(f"32B: streamed {stm['ms_per_step']:.1f} ms/step, peak {stm['peak_gb']:.2f} GB; "
           f"resident {res['ms_per_step']:.1f} ms/step, peak {res['peak_gb']:.2f} GB", flush=True)
 
 
