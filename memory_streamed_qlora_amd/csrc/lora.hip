@@ -91,27 +91,8 @@ __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int
   const int j0 = blockIdx.z * 16;
   const int64_t m = (int64_t)grp * 32 + row;
   const int64_t c0 = (int64_t)s0 * 64;
-  if (r > 0) {
-    const int ncol = nst * 64;
-    if (MAT_KIND == 0) {  // mat [r][C]
-      for (int idx = tid; idx < 16 * LORA_CHUNK / 4; idx += 256) {
-        const int j = idx / (LORA_CHUNK / 4), c4 = 4 * (idx % (LORA_CHUNK / 4));
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j0 + j < r && c4 < ncol) v = *reinterpret_cast<const float4*>(mat + (int64_t)(j0 + j) * C + c0 + c4);
-        *reinterpret_cast<float4*>(&ms[j][c4]) = v;
-      }
-    } else {  // mat [C][r]
-      for (int idx = tid; idx < 16 * LORA_CHUNK; idx += 256) {
-        const int c = idx / 16, j = idx % 16;
-        ms[j][c] = (j0 + j < r && c < ncol) ? mat[(c0 + c) * (int64_t)r + j0 + j] : 0.0f;
-      }
-    }
-    __syncthreads();
-  }
-  float acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-  // all of this thread's loads first (PK_STEPS x 8 elements in flight), then the work
+  // this thread's activation loads first (PK_STEPS x 8 elements in flight), so that their
+  // latency overlaps the staging of the adapter chunk below
   float fa[PK_STEPS][8];
 #pragma unroll
   for (int b = 0; b < PK_STEPS; ++b) {
@@ -119,6 +100,42 @@ __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int
     for (int e = 0; e < 8; ++e) fa[b][e] = 0.0f;
     if (b < nst && m < T) load8(in + m * C + (int64_t)(s0 + b) * 64 + ch * 8, fa[b]);
   }
+  if (r > 0) {
+    // the chunk of the adapter, staged rank-major: every load issued before any LDS store
+    const int ncol = nst * 64;
+    if (MAT_KIND == 0) {  // mat [r][C]: 4 float4 per thread
+      constexpr int NV = 16 * LORA_CHUNK / 4 / 256;
+      float4 v[NV];
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int idx = tid + 256 * q, j = idx / (LORA_CHUNK / 4), c4 = 4 * (idx % (LORA_CHUNK / 4));
+        v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j0 + j < r && c4 < ncol) v[q] = *reinterpret_cast<const float4*>(mat + (int64_t)(j0 + j) * C + c0 + c4);
+      }
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int idx = tid + 256 * q, j = idx / (LORA_CHUNK / 4), c4 = 4 * (idx % (LORA_CHUNK / 4));
+        *reinterpret_cast<float4*>(&ms[j][c4]) = v[q];
+      }
+    } else {  // mat [C][r]: 16 values per thread
+      constexpr int NV = 16 * LORA_CHUNK / 256;
+      float v[NV];
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int idx = tid + 256 * q, c = idx / 16, j = idx % 16;
+        v[q] = (j0 + j < r && c < ncol) ? mat[(c0 + c) * (int64_t)r + j0 + j] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int idx = tid + 256 * q, c = idx / 16, j = idx % 16;
+        ms[j][c] = v[q];
+      }
+    }
+    __syncthreads();
+  }
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
 #pragma unroll
   for (int b = 0; b < PK_STEPS; ++b) {
     if (b >= nst) break;
