@@ -2,14 +2,16 @@
 
 Workload: 64 decoder layers (hidden 5120, 40/8 heads, SwiGLU 27648), random N(0, 0.02)
 base quantized to NF4 and held in pinned host memory, streamed in windows of 4 blocks
-through a device arena of 3 window slots (one computing, two prefetching); LoRA r16
+through a device arena of 5 window slots (one computing, the others prefetching); LoRA r16
 alpha32 dropout 0.0 on all seven projections;
 batch 1 x 512 random tokens over a 152064-entry vocabulary; one AdamW step per
 training step.  A step is the whole hot path: forward with streaming, loss, backward
 with reload + recompute, AdamW.  tokens/s = 512 * steps / timed seconds.
 
 Prints one JSON line (see the fields below); --gpus N > 1 exits: this build runs on
-one GPU.
+one GPU.  --vendor-gemm instead compares the library's NF4 GEMMs at the step's projection
+shapes with the vendor library's plain bf16 GEMM (torch.matmul -> hipBLASLt) of the same
+dimensions.
 """
 from __future__ import annotations
 
@@ -248,6 +250,98 @@ def rocprof_summary(d: str) -> int:
     return 0
 
 
+def vendor_gemm(reps: int = 20) -> int:
+    """The step's GEMM launches at T = 512 (Qwen2.5-32B shapes, projections grouped as the
+    stack groups them) against torch.matmul in bf16 of the same M x N x K: the vendor's own
+    dense GEMM with the weight already in bf16 (no dequantization, no LoRA term).  Ours:
+    the NF4 GEMM kernel's average launch time (HIP events on its launches) and the whole
+    library call (pack + products + GEMM + split reduction, torch events).  Prints one
+    JSON line."""
+    import torch
+
+    from memory_streamed_qlora_amd import ops
+
+    torch.cuda.set_device(0)
+    T, H, I = 512, 5120, 27648
+    g = torch.Generator(device="cuda").manual_seed(0)
+    cfg = ops.Lora(16, 32.0, 0.0)
+
+    def proj(n, k, i):
+        W = (torch.randn(n, k, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        c, a = ops.nf4_quantize(W)
+        return {"base": (c, a), "W": W, "A": torch.randn(16, k, generator=g, device="cuda") * 0.01,
+                "B": torch.randn(n, 16, generator=g, device="cuda") * 0.01, "key": ops.rng_key(0, 0, 0, 0, i),
+                "bias": None}
+
+    x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
+    a = torch.randn(T, I, generator=g, device="cuda").to(torch.bfloat16)
+    qkv = [proj(H, H, 0), proj(1024, H, 1), proj(1024, H, 2)]
+    o, gu, down = proj(H, H, 3), [proj(I, H, 4), proj(I, H, 5)], proj(H, I, 6)
+
+    def dys(ps):
+        return [dict(p, dy=torch.randn(T, p["W"].shape[0], generator=g, device="cuda").to(torch.bfloat16))
+                for p in ps]
+
+    def wcat(ps):
+        return torch.cat([p["W"] for p in ps]).contiguous()
+
+    cases = [  # (name, our call, vendor call)
+        ("q+k+v fwd", lambda: ops.lora_fwd_group(x, qkv, cfg, want_u=False), (x, wcat(qkv).t())),
+        ("o fwd", lambda: ops.nf4_lora_fwd(x, *o["base"], None, o["A"], o["B"], cfg, o["key"], want_u=False),
+         (x, o["W"].t())),
+        ("gate+up fwd", lambda: ops.lora_fwd_group(x, gu, cfg, want_u=False), (x, wcat(gu).t())),
+        ("down fwd", lambda: ops.nf4_lora_fwd(a, *down["base"], None, down["A"], down["B"], cfg, down["key"],
+                                              want_u=False), (a, down["W"].t())),
+    ]
+    qkv_b, gu_b = dys(qkv), dys(gu)
+    dy_o, dy_d = dys([o])[0]["dy"], dys([down])[0]["dy"]
+    cases += [
+        ("q+k+v bwd", lambda: ops.lora_bwd_group(x, qkv_b, cfg), (torch.cat([p["dy"] for p in qkv_b], 1), wcat(qkv))),
+        ("o bwd", lambda: ops.nf4_lora_bwd(dy_o, x, *o["base"], o["A"], o["B"], cfg, o["key"]), (dy_o, o["W"])),
+        ("gate+up bwd", lambda: ops.lora_bwd_group(x, gu_b, cfg), (torch.cat([p["dy"] for p in gu_b], 1), wcat(gu))),
+        ("down bwd", lambda: ops.nf4_lora_bwd(dy_d, a, *down["base"], down["A"], down["B"], cfg, down["key"]),
+         (dy_d, down["W"])),
+    ]
+
+    def timed(fn) -> float:
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e3  # us
+
+    rows = []
+    for name, ours, (lhs, rhs) in cases:
+        m, kk = lhs.shape
+        n = rhs.shape[1]
+        flop = 2.0 * m * n * kk
+        call_us = timed(ours)
+        ops.timing_enable(True)
+        ops.timing_collect()
+        for _ in range(reps):
+            ours()
+        torch.cuda.synchronize()
+        kt = by_kernel(ops.timing_collect())
+        ops.timing_enable(False)
+        gk = kt.get("nf4_fwd_gemm" if "fwd" in name else "nf4_bwd_gemm")
+        gemm_us = gk["total_ms"] / gk["launches"] * 1e3
+        vend_us = timed(lambda: torch.matmul(lhs, rhs))
+        rows.append({"gemm": name, "m": m, "n": n, "k": kk, "nf4_gemm_us": round(gemm_us, 1),
+                     "nf4_gemm_tflops": round(flop / gemm_us / 1e6, 1), "nf4_call_us": round(call_us, 1),
+                     "hipblaslt_bf16_us": round(vend_us, 1), "hipblaslt_bf16_tflops": round(flop / vend_us / 1e6, 1)})
+        log(json.dumps(rows[-1]))
+    tot = {k: sum(r[k] for r in rows) for k in ("nf4_gemm_us", "nf4_call_us", "hipblaslt_bf16_us")}
+    print(json.dumps({"vendor_gemm": rows, "per_layer_us": {k: round(v, 1) for k, v in tot.items()},
+                      "note": "forward and backward launches of one 32B layer at T 512; hipBLASLt multiplies "
+                              "bf16 weights (no dequantization, no LoRA term)"}))
+    return 0
+
+
 def main() -> int:
     if len(sys.argv) == 3 and sys.argv[1] == "--rocprof-summary":
         return rocprof_summary(sys.argv[2])
@@ -276,10 +370,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the streamed steps without per-launch events (no roofline figures)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only compare the NF4 GEMMs with hipBLASLt's bf16 GEMM at the step's shapes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs the hot path on one GPU only; --gpus must be 1", file=sys.stderr)
         return 2
+    if args.vendor_gemm:
+        return vendor_gemm()
 
     import torch
 

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 8
+#define MSQ_ABI_VERSION 9
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -224,6 +224,50 @@ typedef struct {
 size_t lora_group_workspace_size(int64_t t, int64_t k, const msq_lora_proj* projs, int n_proj, int32_t r);
 int lora_fwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj* projs, int n_proj,
                    msq_lora_cfg cfg, void* workspace, size_t workspace_bytes, msq_stream_t stream);
+
+/* Grouped backward of up to 3 projections of the same input x [t, k] (q/k/v, or
+ * gate/up): the gradients of nf4_lora_bwd (or bf16_lora_bwd) for each projection, with
+ * their input gradients summed into one dx,
+ *   dx = sum_i ( dy_i W_i + sigma * keep_i (.) (du_i A_i) ),   du_i = s dy_i B_i,
+ * which is the backward of the block's use of x in the pages' training step ("Poros"
+ * research post, the training-step paragraph: gradients reach only the adapters and the
+ * activations).  The sum over i is one reduction over the projections' concatenated W rows
+ * (a single GEMM launch with one split plan, each projection's LoRA term added with its
+ * own key and keep mask), so a narrow k/v backward no longer runs as a launch of its own;
+ * dx therefore equals the sum of the single calls' dx up to fp32 summation order.  dA_i
+ * and dB_i are those of the single call with the same arguments.
+ *   projs   n_proj (1..3) descriptors: n (% 64 == 0), the base (codes + absmax, or w; one
+ *           format per group), A, B, the projection's rng key, dy [t, n] (x's type), u
+ *           [t, r] fp32 from the forward or NULL to recompute, and the outputs dA [r, k],
+ *           dB [n, r] fp32 (NULL only when r == 0); alignment as in nf4_lora_bwd
+ *   dx      [t, k] output (bf16, or fp32 with MSQ_OUT_F32); dx_accumulate = 1 adds the sum
+ *           into the existing dx (one rounding), 0 overwrites
+ *   dAB_accumulate = 1 adds into every dA_i, dB_i
+ *   cfg     r, alpha, p_drop and the activation / output flags shared by the group
+ *           (MSQ_U_ONLY is rejected)
+ *   workspace  >= lora_group_bwd_workspace_size(t, k, projs, n_proj, r) bytes (0 for
+ *           invalid descriptors), 256-byte aligned.
+ * t == 0: dA_i, dB_i are set to zero (or left unchanged when accumulating); x, dx and dy
+ * may be NULL.  t * (sum of n) must stay below 2^34. */
+typedef struct {
+  int64_t n;
+  const uint8_t* codes;
+  const float* absmax;
+  const uint16_t* w;
+  const float* A;
+  const float* B;
+  msq_rng_key key;
+  const void* dy;
+  const float* u;
+  float* dA;
+  float* dB;
+} msq_lora_proj_grad;
+
+size_t lora_group_bwd_workspace_size(int64_t t, int64_t k, const msq_lora_proj_grad* projs, int n_proj,
+                                     int32_t r);
+int lora_bwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj_grad* projs, int n_proj,
+                   msq_lora_cfg cfg, void* dx, int dx_accumulate, int dAB_accumulate, void* workspace,
+                   size_t workspace_bytes, msq_stream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Pointwise block glue of a Qwen2.5-style decoder block, fp32.

@@ -56,6 +56,12 @@ class LoraProj(ctypes.Structure):
                 ("u_out", ctypes.c_void_p)]
 
 
+class LoraProjGrad(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+                ("w", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("key", RngKey),
+                ("dy", ctypes.c_void_p), ("u", ctypes.c_void_p), ("dA", ctypes.c_void_p), ("dB", ctypes.c_void_p)]
+
+
 class KernelTiming(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_uint64),
                 ("total_ms", ctypes.c_double), ("total_flops", ctypes.c_double),
@@ -97,6 +103,9 @@ _SIG = {
                                      _P]),
     "lora_group_workspace_size": (ctypes.c_size_t, [_I64, _I64, _P, ctypes.c_int, ctypes.c_int32]),
     "lora_fwd_group": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, LoraCfg, _P, ctypes.c_size_t, _P]),
+    "lora_group_bwd_workspace_size": (ctypes.c_size_t, [_I64, _I64, _P, ctypes.c_int, ctypes.c_int32]),
+    "lora_bwd_group": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, LoraCfg, _P, ctypes.c_int, ctypes.c_int, _P,
+                                      ctypes.c_size_t, _P]),
     "nf4_stream_load_device_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "nf4_stream_load_host_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "nf4_stream_load": (ctypes.c_int, [_P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
@@ -115,7 +124,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 8  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 9  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

@@ -228,7 +228,6 @@ int lora_fwd(const char* fn, const void* x, int64_t t, int64_t k, int64_t n, con
     L.plan = p.fwd;
     L.r = r;
     L.lscale = lscale;
-    L.drop = no_dropout();
     L.out_f32 = out_f32;
     GemmSegment& S = L.seg[0];
     S.codes = base.codes;
@@ -348,7 +347,6 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
       L.plan = p.bwd;
       L.r = r;
       L.lscale = 1.0f;
-      L.drop = d;
       L.out_f32 = out_f32;
       GemmSegment& S = L.seg[0];
       S.codes = base.codes;
@@ -357,6 +355,7 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
       S.N = n;
       S.lu = du;
       S.lw = A;
+      S.drop = d;
       S.addend = dx_accumulate && p.bwd.splits == 1 ? dx : nullptr;
       S.out = p.bwd.splits == 1 ? dx : (void*)part;
       e = launch_gemm(L, s);
@@ -374,6 +373,75 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
   if (e == hipSuccess && r > 0)
     e = launch_colgrad_reduce((float*)(ws + p.off_pb), p.nch, r, n, lscale, true, dB, dAB_accumulate, s);
   return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
+}
+
+// Workspace of a grouped backward: fp32 split partials of dx, u (when recomputed) and du
+// of every projection, the projections' dy packed side by side along the reduction, and
+// the chunk partials of the rank-r products and of dA / dB (shared: the projections'
+// passes run one after another on the stream).
+struct GroupBwdPlan {
+  GemmPlan bwd;
+  int64_t red;  // concatenated reduction: the sum of the projections' n
+  int nch;
+  size_t off_part, off_u[GEMM_MAX_SEGS], off_du[GEMM_MAX_SEGS], off_act, off_sk, off_pa, off_pb, bytes;
+};
+
+GroupBwdPlan group_bwd_plan(int64_t t, int64_t k, const int64_t* ns, int np, int32_t r) {
+  GroupBwdPlan p;
+  p.red = 0;
+  int64_t nmax = 0;
+  for (int i = 0; i < np; ++i) {
+    p.red += ns[i];
+    nmax = std::max(nmax, ns[i]);
+  }
+  p.bwd = gemm_plan(t, k, p.red, np);  // split i adds projection i's LoRA term
+  p.nch = (int)((t + COLGRAD_TCHUNK - 1) / COLGRAD_TCHUNK);
+  const size_t tr = (size_t)t * (size_t)r * sizeof(float);
+  size_t o = 0;
+  p.off_part = o;
+  o = align256(o + (p.bwd.splits > 1 ? (size_t)p.bwd.splits * t * k * sizeof(float) : 0));
+  for (int i = 0; i < GEMM_MAX_SEGS; ++i) {
+    p.off_u[i] = o;
+    if (i < np) o = align256(o + tr);
+    p.off_du[i] = o;
+    if (i < np) o = align256(o + tr);
+  }
+  p.off_act = o;
+  o = align256(o + (size_t)frag_rows(t) * p.red * sizeof(uint16_t));
+  p.off_sk = o;
+  o = align256(o + (size_t)((std::max(k, nmax) + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
+  p.off_pa = o;
+  o = align256(o + (size_t)p.nch * r * k * sizeof(float));
+  p.off_pb = o;
+  o = align256(o + (size_t)p.nch * r * nmax * sizeof(float));
+  p.bytes = o;
+  return p;
+}
+
+int group_bwd_check(const char* fn, int64_t t, int64_t k, const msq_lora_proj_grad* projs, int n_proj,
+                    const msq_lora_cfg& cfg, int64_t* ns) {
+  if (n_proj < 1 || n_proj > GEMM_MAX_SEGS || !projs)
+    return set_error(MSQ_E_INVAL, "%s: n_proj=%d outside [1, %d]", fn, n_proj, GEMM_MAX_SEGS);
+  if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY is a forward flag", fn);
+  int64_t red = 0;
+  for (int i = 0; i < n_proj; ++i) {
+    const msq_lora_proj_grad& q = projs[i];
+    int rc = check_linear(fn, t, k, q.n, cfg, q.key);
+    if (rc) return rc;
+    rc = check_base(fn, Base{q.codes, q.absmax, q.w});
+    if (rc) return rc;
+    if ((q.w != nullptr) != (projs[0].w != nullptr)) return set_error(MSQ_E_INVAL, "%s: mixed base formats in one group", fn);
+    if (t > 0 && !q.dy) return set_error(MSQ_E_INVAL, "%s: projection %d: null dy", fn, i);
+    if (cfg.r > 0 && (!q.A || !q.B || !q.dA || !q.dB))
+      return set_error(MSQ_E_INVAL, "%s: projection %d: r > 0 needs A, B, dA, dB", fn, i);
+    if (!aligned(q.dy, 16) || !aligned(q.A, 16) || !aligned(q.B, 16) || !aligned(q.u, 4) || !aligned(q.dA, 4) ||
+        !aligned(q.dB, 4))
+      return set_error(MSQ_E_INVAL, "%s: projection %d: misaligned pointer (dy, A, B: 16 bytes; u, dA, dB: 4)", fn, i);
+    ns[i] = q.n;
+    red += q.n;
+  }
+  if (t * red >= MAX_ELEMS) return set_error(MSQ_E_SHAPE, "%s: t * (sum of n) reaches 2^34", fn);
+  return MSQ_OK;
 }
 
 }  // namespace
@@ -448,7 +516,6 @@ int lora_fwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj* pro
     L.plan = p.fwd;
     L.r = r;
     L.lscale = lscale;
-    L.drop = no_dropout();
     L.out_f32 = out_f32;
     L.nseg = n_proj;
     size_t o = 0;
@@ -472,6 +539,104 @@ int lora_fwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj* pro
   for (int i = 0; i < n_proj && e == hipSuccess && p.fwd.splits > 1; ++i)
     e = launch_split_reduce(part + part_off[i], p.fwd.splits, t, projs[i].n, projs[i].bias, projs[i].residual, true,
                             projs[i].y, out_f32, s);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
+}
+
+size_t lora_group_bwd_workspace_size(int64_t t, int64_t k, const msq_lora_proj_grad* projs, int n_proj, int32_t r) {
+  int64_t ns[GEMM_MAX_SEGS];
+  msq_lora_cfg cfg;
+  memset(&cfg, 0, sizeof(cfg));
+  cfg.r = r;
+  cfg.alpha = 1.0f;
+  if (group_bwd_check("lora_group_bwd_workspace_size", t, k, projs, n_proj, cfg, ns) != MSQ_OK) return 0;
+  return group_bwd_plan(t, k, ns, n_proj, r).bytes;
+}
+
+int lora_bwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj_grad* projs, int n_proj,
+                   msq_lora_cfg cfg, void* dx, int dx_accumulate, int dAB_accumulate, void* workspace,
+                   size_t workspace_bytes, msq_stream_t stream) {
+  const char* fn = "lora_bwd_group";
+  int64_t ns[GEMM_MAX_SEGS];
+  int rc = group_bwd_check(fn, t, k, projs, n_proj, cfg, ns);
+  if (rc) return rc;
+  if (!workspace || (t > 0 && (!x || !dx))) return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
+  if ((dx_accumulate != 0 && dx_accumulate != 1) || (dAB_accumulate != 0 && dAB_accumulate != 1))
+    return set_error(MSQ_E_INVAL, "%s: accumulate flags must be 0 or 1", fn);
+  if (!aligned(x, 16) || !aligned(dx, 16) || !aligned(workspace, 256))
+    return set_error(MSQ_E_INVAL, "%s: misaligned pointer (x, dx: 16 bytes; workspace 256)", fn);
+  const GroupBwdPlan p = group_bwd_plan(t, k, ns, n_proj, cfg.r);
+  if (workspace_bytes < p.bytes) return set_error(MSQ_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, p.bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int r = cfg.r;
+  const bool act_f32 = cfg.flags & MSQ_ACT_F32, out_f32 = cfg.flags & MSQ_OUT_F32;
+  const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
+  hipError_t e = hipSuccess;
+  const float* u[GEMM_MAX_SEGS];
+  float* du[GEMM_MAX_SEGS];
+  Dropout d[GEMM_MAX_SEGS];
+  for (int i = 0; i < n_proj; ++i) {
+    d[i] = make_dropout(projs[i].key, cfg.p_drop);
+    du[i] = (float*)(ws + p.off_du[i]);
+    u[i] = projs[i].u;
+  }
+  if (t > 0) {
+    float* sk = (float*)(ws + p.off_sk);
+    uint16_t* act = (uint16_t*)(ws + p.off_act);
+    const int steps = (int)(p.red / 64);
+    int step0 = 0;
+    for (int i = 0; i < n_proj && e == hipSuccess; ++i) {
+      const msq_lora_proj_grad& q = projs[i];
+      if (r > 0 && !u[i]) {
+        float* ut = (float*)(ws + p.off_u[i]);
+        e = launch_pack_lora(x, act_f32, t, k, q.A, 0, r, 1.0f, d[i], nullptr, sk, ut, s);
+        u[i] = ut;
+      }
+      // dy_i into k-steps step0 .. of the shared operand, with du_i = s dy_i B_i
+      if (e == hipSuccess)
+        e = launch_pack_lora(q.dy, act_f32, t, q.n, q.B, 1, r, lscale, no_dropout(), act, sk, du[i], s, steps, step0);
+      step0 += (int)(q.n / 64);
+    }
+    float* part = (float*)(ws + p.off_part);
+    if (e == hipSuccess) {
+      GemmLaunch L;
+      L.mode = 1;
+      L.act = act;
+      L.M = t;
+      L.K = k;
+      L.plan = p.bwd;
+      L.r = r;
+      L.lscale = 1.0f;
+      L.out_f32 = out_f32;
+      L.nseg = n_proj;
+      for (int i = 0; i < n_proj; ++i) {
+        const msq_lora_proj_grad& q = projs[i];
+        GemmSegment& S = L.seg[i];
+        S.codes = q.codes;
+        S.absmax = q.absmax;
+        S.wbf = q.w;
+        S.N = q.n;
+        S.lu = du[i];
+        S.lw = q.A;
+        S.drop = d[i];
+      }
+      L.seg[0].addend = dx_accumulate && p.bwd.splits == 1 ? dx : nullptr;
+      L.seg[0].out = p.bwd.splits == 1 ? dx : (void*)part;
+      e = launch_gemm(L, s);
+    }
+    if (e == hipSuccess && p.bwd.splits > 1)
+      e = launch_split_reduce(part, p.bwd.splits, t, k, nullptr, dx_accumulate ? dx : nullptr, false, dx, out_f32, s);
+  }
+  // dA_i and dB_i, one projection after another through the shared chunk partials
+  for (int i = 0; i < n_proj && e == hipSuccess && r > 0; ++i) {
+    const msq_lora_proj_grad& q = projs[i];
+    float* pa = (float*)(ws + p.off_pa);
+    float* pb = (float*)(ws + p.off_pb);
+    if (t > 0) e = launch_colgrad(x, act_f32, t, k, du[i], r, d[i], p.nch, false, pa, s);
+    if (e == hipSuccess && t > 0) e = launch_colgrad(q.dy, act_f32, t, q.n, u[i], r, no_dropout(), p.nch, true, pb, s);
+    if (e == hipSuccess) e = launch_colgrad_reduce(pa, p.nch, r, k, 1.0f, false, q.dA, dAB_accumulate, s);
+    if (e == hipSuccess) e = launch_colgrad_reduce(pb, p.nch, r, q.n, lscale, true, q.dB, dAB_accumulate, s);
+  }
   return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
 }
 

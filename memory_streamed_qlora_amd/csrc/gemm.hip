@@ -28,6 +28,8 @@
 // results never depend on timing.
 #include <string.h>
 
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace msq {
@@ -41,7 +43,10 @@ constexpr int THREADS = 512;  // 8 waves, one per 64 rows
 
 // One projection of a launch.  A forward launch may group up to GEMM_MAX_SEGS projections
 // that share the activation (same K): their column tiles are concatenated in the grid and
-// each workgroup finds its projection from its tile.
+// each workgroup finds its projection from its tile.  A backward launch may group the
+// projections whose dx add up: their W rows are concatenated along the reduction, k-steps
+// step0 .. of the packed dy belong to projection i, and every workgroup runs through all
+// of them; the output fields of segment 0 describe dx.
 struct GemmSeg {
   const uint8_t* codes;  // [N][K/2] NF4 base, or
   const float* absmax;   // [N][K/64]
@@ -51,6 +56,8 @@ struct GemmSeg {
   //   backward keep(m,k) * sigma * lu[m][:] . lw[:][k]  lu = du [M][r], lw = A [r][K]
   const float* lu;
   const float* lw;
+  Dropout drop;  // backward: keep mask of this projection's LoRA input gradient
+  int step0;     // backward: first k-step of this projection's rows in the reduction
   // output: splits == 1 -> y / dx directly (bf16 or fp32): acc + bias, then addend + that
   //         when addend is set (forward: a residual input, added to y after y's own
   //         rounding; backward: the old dx, one rounding of the sum);
@@ -70,7 +77,6 @@ struct GemmArgs {
   Nf4Lut lut;
   int r;
   float lscale;
-  Dropout drop;
   int out_f32;
   int nseg;
   GemmSeg seg[GEMM_MAX_SEGS];
@@ -84,11 +90,8 @@ struct GemmView {
   const uint16_t* wbf;
   int64_t M, K, Nc;
   int steps;
-  const float* lu;
-  const float* lw;
   int r;
   float lscale;
-  Dropout drop;
   const uint16_t* bias;
   const void* addend;
   void* out;
@@ -178,15 +181,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
   int64_t n0, m0;
   int split;
   tile_of(n0, m0, split);
-  // this workgroup's projection (uniform): the last segment whose tiles start at or
-  // before the tile; n0 becomes the column within it
+  // forward: this workgroup's projection (uniform), the last segment whose tiles start at
+  // or before the tile; n0 becomes the column within it.  Backward: segment 0 holds dx.
   int sgi = 0;
-  if (ga.nseg > 1 && n0 >= (int64_t)ga.seg[1].tile0 * BN) sgi = 1;
-  if (ga.nseg > 2 && n0 >= (int64_t)ga.seg[2].tile0 * BN) sgi = 2;
+  if (MODE == 0 && ga.nseg > 1 && n0 >= (int64_t)ga.seg[1].tile0 * BN) sgi = 1;
+  if (MODE == 0 && ga.nseg > 2 && n0 >= (int64_t)ga.seg[2].tile0 * BN) sgi = 2;
   const GemmSeg& sg = ga.seg[sgi];
   n0 -= (int64_t)sg.tile0 * BN;
-  const GemmView g{ga.act, sg.codes, sg.absmax, sg.wbf, ga.M, ga.K, sg.Nc, ga.steps, sg.lu, sg.lw, ga.r,
-                   ga.lscale, ga.drop, sg.bias, sg.addend, sg.out, ga.out_f32};
+  const GemmView g{ga.act, sg.codes, sg.absmax, sg.wbf, ga.M, ga.K, sg.Nc, ga.steps, ga.r,
+                   ga.lscale, sg.bias, sg.addend, sg.out, ga.out_f32};
   const int s_begin = split * ga.steps_per_split;
   const int s_end = min(ga.steps, s_begin + ga.steps_per_split);
   const int64_t mw = m0 + 64 * wave;  // first row of this wave
@@ -225,6 +228,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
     const float* sbase = nullptr;
     const uint16_t* wbase = nullptr;
     int64_t cstride = 0, sstride = 0, wstride = 0;
+    int64_t coff = 0, soff = 0, woff = 0;  // backward: the thread's offsets within a projection's W
     if (MODE == 0) {
       const int64_t wn = min(n0 + (tid >> 2), g.Nc - 1);
       if constexpr (BF16W) {
@@ -237,13 +241,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
         sstride = 1;
       }
     } else {
+      // offsets within a projection's W; the projection and its row base follow the step
       const int64_t col = n0 + 16 * wave < g.Nc ? n0 + 16 * wave : 0;
       if constexpr (BF16W) {
-        wbase = g.wbf + (int64_t)lane * g.K + col;
+        woff = (int64_t)lane * g.K + col;
         wstride = (int64_t)BK * g.K;
       } else {
-        cbase = g.codes + (int64_t)lane * (g.K / 2) + col / 2;
-        sbase = g.absmax + (int64_t)lane * (g.K / 64) + col / 64;
+        coff = (int64_t)lane * (g.K / 2) + col / 2;
+        soff = (int64_t)lane * (g.K / 64) + col / 64;
         cstride = (int64_t)BK * (g.K / 2);
         sstride = (int64_t)BK * (g.K / 64);
       }
@@ -257,6 +262,24 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
       a[1][c] = *reinterpret_cast<const uint4*>(ap1 + o);
     };
     auto load_w = [&](WShare<BF16W>& w, int step) {
+      if (MODE == 1) {
+        // the projection whose rows the step covers (uniform): base + lane offset + rows
+        const bool in2 = ga.nseg > 2 && step >= ga.seg[2].step0;
+        const bool in1 = !in2 && ga.nseg > 1 && step >= ga.seg[1].step0;
+        const int64_t ls = step - (in2 ? ga.seg[2].step0 : in1 ? ga.seg[1].step0 : 0);
+        if constexpr (BF16W) {
+          const uint16_t* wb = in2 ? ga.seg[2].wbf : in1 ? ga.seg[1].wbf : ga.seg[0].wbf;
+          const uint16_t* p = wb + (woff + ls * wstride);
+          w.q[0] = *reinterpret_cast<const uint4*>(p);
+          w.q[1] = *reinterpret_cast<const uint4*>(p + 8);
+        } else {
+          const uint8_t* cb = in2 ? ga.seg[2].codes : in1 ? ga.seg[1].codes : ga.seg[0].codes;
+          const float* sb = in2 ? ga.seg[2].absmax : in1 ? ga.seg[1].absmax : ga.seg[0].absmax;
+          w.q = *reinterpret_cast<const uint2*>(cb + (coff + ls * cstride));
+          w.s = sb[soff + ls * sstride];
+        }
+        return;
+      }
       if constexpr (BF16W) {
         const uint16_t* p = wbase + (int64_t)step * wstride;
         w.q[0] = *reinterpret_cast<const uint4*>(p);
@@ -382,58 +405,82 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
   // ---- LoRA term: one extra MFMA k-step per 16 ranks, operands split hi/lo ---------------
   // Operands come straight from global memory in the MFMA lane layout: lane half hk
   // holds ranks rc + 8*hk .. +7 of its row (u side) or column (B / A side).
-  if (split == 0 && g.r > 0) {
-    for (int rc = 0; rc < g.r; rc += 16) {
-      bf16x8_t ah[2], al[2], bh[4], bl[4];
+  // One projection's term, added by split 0; in a backward group split p adds projection
+  // p's with its own factors and keep mask (a group's plan has a split per projection), so
+  // no workgroup adds more than one (several terms in one workgroup keep enough values
+  // live that the dropout variant spills).
+  auto lora_term = [&](const float* lu, const float* lw, const Dropout& dr) {
+      for (int rc = 0; rc < g.r; rc += 16) {
+        bf16x8_t ah[2], al[2], bh[4], bl[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t m = min(mw + 32 * i + r32, g.M - 1);
-        float v[8];
+        for (int i = 0; i < 2; ++i) {
+          const int64_t m = min(mw + 32 * i + r32, g.M - 1);
+          float v[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int j = rc + 8 * hk + jj;
-          const float x = g.lu[m * g.r + min(j, g.r - 1)];
-          v[jj] = j < g.r ? g.lscale * x : 0.0f;
+          for (int jj = 0; jj < 8; ++jj) {
+            const int j = rc + 8 * hk + jj;
+            const float x = lu[m * g.r + min(j, g.r - 1)];
+            v[jj] = j < g.r ? g.lscale * x : 0.0f;
+          }
+          split8(v, ah[i], al[i]);
         }
-        split8(v, ah[i], al[i]);
-      }
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) {
-        const int64_t n = min(n0 + 32 * jn + r32, g.Nc - 1);
-        float v[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int j = rc + 8 * hk + jj;
-          const int jc = min(j, g.r - 1);
-          const float x = (MODE == 0) ? g.lw[n * g.r + jc] : g.lw[(int64_t)jc * g.K + n];
-          v[jj] = j < g.r ? x : 0.0f;
-        }
-        split8(v, bh[jn], bl[jn]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn) {
-          if (!DROP) {
-            f32x16_t t = acc[i][jn];
-            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[jn], t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[jn], t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[jn], t, 0, 0, 0);
-            acc[i][jn] = t;
-          } else {
-            // masked LoRA input gradient: acc += keep * sigma * (du . A)
-            f32x16_t t;
+          const int64_t n = min(n0 + 32 * jn + r32, g.Nc - 1);
+          float v[8];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) t[v] = 0.0f;
-            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[jn], t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[jn], t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[jn], t, 0, 0, 0);
-            const uint32_t keep = keep_rows16(g.drop, mw + 32 * i, hk, n0 + 32 * jn + r32, g.Nc, lane);
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if ((keep >> v) & 1u) acc[i][jn][v] += g.drop.sigma * t[v];
+          for (int jj = 0; jj < 8; ++jj) {
+            const int j = rc + 8 * hk + jj;
+            const int jc = min(j, g.r - 1);
+            const float x = (MODE == 0) ? lw[n * g.r + jc] : lw[(int64_t)jc * g.K + n];
+            v[jj] = j < g.r ? x : 0.0f;
           }
+          split8(v, bh[jn], bl[jn]);
         }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jn = 0; jn < 4; ++jn) {
+            if (!DROP) {
+              f32x16_t t = acc[i][jn];
+              t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[jn], t, 0, 0, 0);
+              t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[jn], t, 0, 0, 0);
+              t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[jn], t, 0, 0, 0);
+              acc[i][jn] = t;
+            } else {
+              // masked LoRA input gradient: acc += keep * sigma * (du . A)
+              f32x16_t t;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) t[v] = 0.0f;
+              t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[jn], t, 0, 0, 0);
+              t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[jn], t, 0, 0, 0);
+              t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[jn], t, 0, 0, 0);
+              const uint32_t keep = keep_rows16(dr, mw + 32 * i, hk, n0 + 32 * jn + r32, g.Nc, lane);
+#pragma unroll
+              for (int v = 0; v < 16; ++v)
+                if ((keep >> v) & 1u) acc[i][jn][v] += dr.sigma * t[v];
+              __builtin_amdgcn_sched_barrier(0);  // one block's term live at a time
+            }
+          }
+      }
+  };
+  if (g.r > 0) {
+    if (MODE == 0) {
+      if (split == 0) lora_term(sg.lu, sg.lw, sg.drop);
+    } else {
+      if (split < ga.nseg) {
+        const bool s1 = split == 1, s2 = split == 2;  // uniform picks, no indexed segment
+        Dropout dr;
+        dr.k0 = s2 ? ga.seg[2].drop.k0 : s1 ? ga.seg[1].drop.k0 : ga.seg[0].drop.k0;
+        dr.k1 = s2 ? ga.seg[2].drop.k1 : s1 ? ga.seg[1].drop.k1 : ga.seg[0].drop.k1;
+        dr.c1 = s2 ? ga.seg[2].drop.c1 : s1 ? ga.seg[1].drop.c1 : ga.seg[0].drop.c1;
+        dr.c2 = s2 ? ga.seg[2].drop.c2 : s1 ? ga.seg[1].drop.c2 : ga.seg[0].drop.c2;
+        dr.c3 = s2 ? ga.seg[2].drop.c3 : s1 ? ga.seg[1].drop.c3 : ga.seg[0].drop.c3;
+        dr.threshold = s2 ? ga.seg[2].drop.threshold : s1 ? ga.seg[1].drop.threshold : ga.seg[0].drop.threshold;
+        dr.sigma = s2 ? ga.seg[2].drop.sigma : s1 ? ga.seg[1].drop.sigma : ga.seg[0].drop.sigma;
+        lora_term(s2 ? ga.seg[2].lu : s1 ? ga.seg[1].lu : ga.seg[0].lu,
+                  s2 ? ga.seg[2].lw : s1 ? ga.seg[1].lw : ga.seg[0].lw, dr);
+      }
     }
   }
 
@@ -507,19 +554,22 @@ MSQ_GEMM_KERNEL(bf16_bwd_gemm_dropout, 1, true, true)
 // Split of the reduction dimension.  Cost model per candidate split S: a k-step of one
 // workgroup keeps its CU's matrix cores busy for ~1 us (64 MFMAs per SIMD), the
 // workgroups spread evenly over the 256 CUs, and every extra split writes and re-reads
-// an fp32 partial tile (~4 TB/s).  The cheapest S wins; S = 1 on ties.
-GemmPlan gemm_plan_tiles(int64_t m, int64_t n_tiles, int64_t nc, int64_t red) {
+// an fp32 partial tile at ~8 TB/s (the partials are re-read while still in the L2 and
+// last-level caches; measured at the 32B shapes, this rate picks the fastest S of every
+// one of them).  The cheapest S wins; the smallest on ties.
+GemmPlan gemm_plan_tiles(int64_t m, int64_t n_tiles, int64_t nc, int64_t red, int min_splits) {
   GemmPlan p;
   p.steps = (int)(red / BK);
   const int64_t tiles = ((m + BM - 1) / BM) * n_tiles;
+  const int s0 = std::max(1, std::min(min_splits, p.steps));
   double best = 0.0;
-  int best_s = 1;
-  for (int s = 1; s <= 32 && s <= p.steps; ++s) {
+  int best_s = s0;
+  for (int s = s0; s <= 32 && s <= p.steps; ++s) {
     const int64_t per = (p.steps + s - 1) / s;
-    if (s > 1 && (per < 4 || (int64_t)(s - 1) * per >= p.steps)) continue;  // no empty or tiny splits
+    if (s > s0 && (per < 4 || (int64_t)(s - 1) * per >= p.steps)) continue;  // no empty or tiny splits
     const double per_cu = (double)((tiles * s + 255) / 256);
-    const double t = per_cu * (double)per * 1.0 + (s > 1 ? (double)s * (double)m * (double)nc * 8.0 / 4e6 : 0.0);
-    if (s == 1 || t < best) {
+    const double t = per_cu * (double)per * 1.0 + (s > 1 ? (double)s * (double)m * (double)nc * 8.0 / 8e6 : 0.0);
+    if (s == s0 || t < best) {
       best = t;
       best_s = s;
     }
@@ -529,7 +579,9 @@ GemmPlan gemm_plan_tiles(int64_t m, int64_t n_tiles, int64_t nc, int64_t red) {
   return p;
 }
 
-GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red) { return gemm_plan_tiles(m, (nc + BN - 1) / BN, nc, red); }
+GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red, int min_splits) {
+  return gemm_plan_tiles(m, (nc + BN - 1) / BN, nc, red, min_splits);
+}
 
 GemmPlan gemm_plan_group(int64_t m, const int64_t* ns, int nseg, int64_t red) {
   int64_t tiles = 0, nc = 0;
@@ -537,29 +589,35 @@ GemmPlan gemm_plan_group(int64_t m, const int64_t* ns, int nseg, int64_t red) {
     tiles += (ns[i] + BN - 1) / BN;
     nc += ns[i];
   }
-  return gemm_plan_tiles(m, tiles, nc, red);
+  return gemm_plan_tiles(m, tiles, nc, red, 1);
 }
 
 hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
-  if (L.nseg < 1 || L.nseg > GEMM_MAX_SEGS || (L.mode == 1 && L.nseg != 1)) return hipErrorInvalidValue;
+  if (L.nseg < 1 || L.nseg > GEMM_MAX_SEGS) return hipErrorInvalidValue;
   const bool bf = L.seg[0].wbf != nullptr;
   g.act = L.act;
   g.M = L.M;
   g.K = L.K;
-  g.R = L.mode == 0 ? L.K : L.seg[0].N;
+  g.R = 0;
+  for (int i = 0; i < L.nseg && L.mode == 1; ++i) {
+    if (L.seg[i].N % BK) return hipErrorInvalidValue;  // a k-step never straddles two projections
+    g.seg[i].step0 = (int)(g.R / BK);
+    g.R += L.seg[i].N;
+  }
+  if (L.mode == 0) g.R = L.K;
   g.steps = L.plan.steps;
   g.steps_per_split = L.plan.steps_per_split;
   g.splits = L.plan.splits;
   g.lut = nf4_lut();
   g.r = L.r;
   g.lscale = L.lscale;
-  g.drop = L.drop;
   g.out_f32 = L.out_f32;
   g.nseg = L.nseg;
   int tiles = 0;
-  int64_t n_total = 0, nc_total = 0;
+  int64_t n_total = 0;
+  bool drop_any = false;
   for (int i = 0; i < L.nseg; ++i) {
     const GemmSegment& S = L.seg[i];
     if ((S.wbf != nullptr) != bf || (S.codes != nullptr) == bf) return hipErrorInvalidValue;  // one base format
@@ -569,18 +627,21 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
     d.wbf = S.wbf;
     d.lu = S.lu;
     d.lw = S.lw;
+    d.drop = S.drop;
     d.bias = S.bias;
     d.addend = S.addend;
     d.out = S.out;
     d.Nc = L.mode == 0 ? S.N : L.K;
-    d.tile0 = tiles;
+    d.tile0 = L.mode == 0 ? tiles : 0;
     if (d.Nc < 1) return hipErrorInvalidValue;
-    tiles += (int)((d.Nc + BN - 1) / BN);
+    if (L.mode == 0 || i == 0) tiles += (int)((d.Nc + BN - 1) / BN);
+    if (S.drop.threshold != 0u) drop_any = true;
     n_total += S.N;
-    nc_total += d.Nc;
   }
-  // The kernel clamps rows and columns onto [0, M) x [0, Nc) and reads whole k-steps.
+  // The kernel clamps rows and columns onto [0, M) x [0, Nc) and reads whole k-steps; a
+  // backward group's split p adds projection p's LoRA term.
   if (g.M < 1 || g.R % BK || g.K % 64 || g.steps != (int)(g.R / BK)) return hipErrorInvalidValue;
+  if (L.mode == 1 && g.splits < g.nseg) return hipErrorInvalidValue;
   const dim3 grid((unsigned)tiles, (unsigned)((g.M + BM - 1) / BM), (unsigned)g.splits);
   const double flops = 2.0 * (double)g.M * (double)n_total * (double)g.K;
   void (*kern)(GemmArgs);
@@ -588,7 +649,7 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   if (L.mode == 0) {
     kern = bf ? bf16_fwd_gemm : nf4_fwd_gemm;
     name = bf ? "bf16_fwd_gemm" : "nf4_fwd_gemm";
-  } else if (L.r > 0 && L.drop.threshold != 0u) {
+  } else if (L.r > 0 && drop_any) {
     kern = bf ? bf16_bwd_gemm_dropout : nf4_bwd_gemm_dropout;
     name = bf ? "bf16_bwd_gemm" : "nf4_bwd_gemm";
   } else {
@@ -598,7 +659,7 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s) {
   // algorithmic bytes: the base (NF4 codes + scales, or bf16), the packed activation, the
   // output (or split partials)
   double out_bytes = 0.0;
-  for (int i = 0; i < L.nseg; ++i)
+  for (int i = 0; i < (L.mode == 0 ? L.nseg : 1); ++i)
     out_bytes += (double)g.M * g.seg[i].Nc *
                  (g.splits > 1 ? 4.0 * g.splits : (g.out_f32 ? 4.0 : 2.0) * (g.seg[i].addend ? 2 : 1));
   const double bytes = (double)n_total * g.K * (bf ? 2.0 : 0.5625) + (double)frag_rows(g.M) * g.R * 2 + out_bytes;

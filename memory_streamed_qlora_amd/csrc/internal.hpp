@@ -30,7 +30,9 @@ struct GemmPlan {
   int steps;           // reduction steps of GEMM_BK
   int steps_per_split;
 };
-GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red);
+// Split plan of an m x nc output over a reduction of red; min_splits (at most the k-step
+// count) is the fewest splits allowed: a backward group needs one per projection.
+GemmPlan gemm_plan(int64_t m, int64_t nc, int64_t red, int min_splits = 1);
 GemmPlan gemm_plan_group(int64_t m, const int64_t* ns, int nseg, int64_t red);
 
 struct LoraPlan {
@@ -54,9 +56,13 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 // addend ([M][Nc] in the output's type, NULL for none) may be `out` itself.
 // With plan.splits > 1, `out` receives fp32 partials [splits][M][Nc] instead (split 0
 // carrying the LoRA term) and launch_split_reduce finishes the output.
-// A forward launch may group up to GEMM_MAX_SEGS projections of the same activation (same
-// K, each with its own base, LoRA factors, bias, addend and output): one grid over all
-// their column tiles, one split plan (gemm_plan_group).  The backward takes one.
+// A launch may group up to GEMM_MAX_SEGS projections of the same input (same K):
+//   forward:  each with its own base, LoRA factors, bias, addend and output; one grid over
+//             all their column tiles, one split plan (gemm_plan_group);
+//   backward: their contributions to the one dx: the reduction runs over the projections'
+//             rows in segment order (act holds each projection's dy in its k-steps, see
+//             launch_pack_lora's step offset) and each adds its own LoRA term with its own
+//             dropout key; out and addend are segment 0's.
 constexpr int GEMM_MAX_SEGS = 3;
 struct GemmSegment {
   const uint8_t* codes = nullptr;  // NF4 base (codes + absmax), or
@@ -65,6 +71,7 @@ struct GemmSegment {
   int64_t N = 0;                   // W rows (forward: output columns; backward: reduction)
   const float* lu = nullptr;
   const float* lw = nullptr;
+  Dropout drop{0, 0, 0, 0, 0, 0, 1.0f};  // backward LoRA term's keep mask (threshold 0: none)
   const uint16_t* bias = nullptr;
   const void* addend = nullptr;
   void* out = nullptr;
@@ -76,7 +83,6 @@ struct GemmLaunch {
   GemmPlan plan;
   int r;
   float lscale;
-  Dropout drop;
   int out_f32;
   int nseg = 1;
   GemmSegment seg[GEMM_MAX_SEGS];
@@ -95,9 +101,12 @@ hipError_t launch_gemm(const GemmLaunch& L, hipStream_t s);
 //    floats) and are summed in chunk order.
 constexpr int LORA_CHUNK = 256;
 inline int64_t frag_rows(int64_t M) { return (M + 31) / 32 * 32; }
+//  - pack_steps / pack_step0: the packed buffer holds pack_steps k-steps per 32-row group
+//    and this activation fills k-steps pack_step0 .. pack_step0 + C/64 - 1 of each group (a
+//    grouped backward packs its projections' dy side by side); 0 / 0: C/64 and 0.
 hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat, int mat_kind,
                             int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
-                            hipStream_t s);
+                            hipStream_t s, int pack_steps = 0, int pack_step0 = 0);
 
 // Column gradients in two passes, reduced over tokens in fixed-size chunks:
 // partials P(ch, j, c) = sum_{t in chunk ch} coef[t][j] * h[t][c], h = drop(in), laid out

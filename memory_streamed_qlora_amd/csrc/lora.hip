@@ -83,7 +83,8 @@ constexpr int PK_STEPS = LORA_CHUNK / 64;
 template <typename TIN, int MAT_KIND>
 __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int64_t T, int64_t C, int steps,
                                                  const float* __restrict__ mat, int r, Dropout d,
-                                                 uint16_t* __restrict__ packed, float* __restrict__ part) {
+                                                 uint16_t* __restrict__ packed, int pstride, int pstep0,
+                                                 float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) float ms[16][LORA_CHUNK + 4];
   const int tid = threadIdx.x, row = tid >> 3, ch = tid & 7;
   const int grp = blockIdx.y, s0 = blockIdx.x * PK_STEPS;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int
       const uint4 v = make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
                                  bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
       const int lane = row + 32 * (ch >> 2), sub = ch & 3;
-      *reinterpret_cast<uint4*>(packed + (((int64_t)grp * steps + step) * 4 + sub) * 512 + lane * 8) = v;
+      *reinterpret_cast<uint4*>(packed + (((int64_t)grp * pstride + pstep0 + step) * 4 + sub) * 512 + lane * 8) = v;
     }
     if (r > 0) {
       if (d.threshold != 0u && m < T) {
@@ -382,8 +383,10 @@ __global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ pa
 
 template <typename TIN, int MAT_KIND>
 hipError_t pack_lora_dispatch(const TIN* in, int64_t T, int64_t C, const float* mat, int r, const Dropout& d,
-                              uint16_t* packed, float* part, hipStream_t s) {
+                              uint16_t* packed, int pstride, int pstep0, float* part, hipStream_t s) {
   const int steps = (int)(C / 64);
+  if (pstride == 0) pstride = steps;
+  if (pstep0 < 0 || pstep0 + steps > pstride) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((steps + PK_STEPS - 1) / PK_STEPS), (unsigned)((T + 31) / 32),
                   (unsigned)(r > 0 ? (r + 15) / 16 : 1));
   const double nck = (double)((C + LORA_CHUNK - 1) / LORA_CHUNK);
@@ -392,22 +395,23 @@ hipError_t pack_lora_dispatch(const TIN* in, int64_t T, int64_t C, const float* 
   char shape[32];
   snprintf(shape, sizeof(shape), "%lldx%lld r%d", (long long)T, (long long)C, r);
   return timed_launch(packed ? "pack_lora" : "lora_product", shape, 0.0, bytes, pack_lora<TIN, MAT_KIND>, grid,
-                      dim3(256), s, in, T, C, steps, mat, r, d, packed, part);
+                      dim3(256), s, in, T, C, steps, mat, r, d, packed, pstride, pstep0, part);
 }
 
 }  // namespace
 
 hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat, int mat_kind,
                             int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
-                            hipStream_t s) {
+                            hipStream_t s, int pack_steps, int pack_step0) {
   if (T == 0 || (r == 0 && !packed)) return hipSuccess;
   hipError_t e;
+  const int ps = pack_steps, p0 = pack_step0;
   if (in_f32)
-    e = mat_kind == 0 ? pack_lora_dispatch<float, 0>((const float*)in, T, C, mat, r, d, packed, part, s)
-                      : pack_lora_dispatch<float, 1>((const float*)in, T, C, mat, r, d, packed, part, s);
+    e = mat_kind == 0 ? pack_lora_dispatch<float, 0>((const float*)in, T, C, mat, r, d, packed, ps, p0, part, s)
+                      : pack_lora_dispatch<float, 1>((const float*)in, T, C, mat, r, d, packed, ps, p0, part, s);
   else
-    e = mat_kind == 0 ? pack_lora_dispatch<uint16_t, 0>((const uint16_t*)in, T, C, mat, r, d, packed, part, s)
-                      : pack_lora_dispatch<uint16_t, 1>((const uint16_t*)in, T, C, mat, r, d, packed, part, s);
+    e = mat_kind == 0 ? pack_lora_dispatch<uint16_t, 0>((const uint16_t*)in, T, C, mat, r, d, packed, ps, p0, part, s)
+                      : pack_lora_dispatch<uint16_t, 1>((const uint16_t*)in, T, C, mat, r, d, packed, ps, p0, part, s);
   if (e != hipSuccess || r == 0) return e;
   const int nck = (int)((C + LORA_CHUNK - 1) / LORA_CHUNK);
   const int64_t n = T * r;

@@ -265,6 +265,58 @@ def lora_fwd_group(x: torch.Tensor, projs: Sequence[dict], cfg: Lora, want_u: bo
     return outs
 
 
+def lora_bwd_group(x: torch.Tensor, projs: Sequence[dict], cfg: Lora, dx: Optional[torch.Tensor] = None,
+                   dx_accumulate: bool = False, dAB_accumulate: bool = False,
+                   workspace: Optional[Workspace] = None, stream=None,
+                   out_dtype: Optional[torch.dtype] = None):
+    """Backward of up to three projections of the same x (lora_bwd_group): each dict has
+    base ((codes, absmax) or (w,)), A, B, key, dy, and optionally u (the forward's) and dA,
+    dB outputs.  Returns (dx, [(dA, dB), ...]) with dx the sum of the projections' input
+    gradients."""
+    t, k = x.shape
+    _req(x, "x", x.dtype, (t, k))
+    out_dtype = out_dtype or (dx.dtype if dx is not None else x.dtype)
+    flags = _flags(x.dtype, out_dtype)
+    if not 1 <= len(projs) <= 3:
+        raise ValueError("a group has 1 to 3 projections")
+    arr = (_abi.LoraProjGrad * len(projs))()
+    grads = []
+    r = cfg.r
+    for i, pr in enumerate(projs):
+        fmt, n, bptr = _base_args(pr["base"], k)
+        dy = pr["dy"]
+        _req(dy, "dy", x.dtype, (t, n))
+        dA = dB = None
+        u = pr.get("u")
+        if r > 0:
+            _req(pr["A"], "A", torch.float32, (r, k))
+            _req(pr["B"], "B", torch.float32, (n, r))
+            dA = pr.get("dA")
+            dB = pr.get("dB")
+            dA = torch.empty((r, k), dtype=torch.float32, device=x.device) if dA is None else dA
+            dB = torch.empty((n, r), dtype=torch.float32, device=x.device) if dB is None else dB
+            _req(dA, "dA", torch.float32, (r, k))
+            _req(dB, "dB", torch.float32, (n, r))
+            if u is not None:
+                _req(u, "u", torch.float32, (t, r))
+        codes, absmax, w = (bptr + [None])[:3] if fmt == "nf4" else (None, None, bptr[0])
+        arr[i] = _abi.LoraProjGrad(n, codes, absmax, w, _ptr(pr["A"]) if r > 0 else None,
+                                   _ptr(pr["B"]) if r > 0 else None, pr["key"], _ptr(dy),
+                                   _ptr(u) if r > 0 else None, _ptr(dA), _ptr(dB))
+        grads.append((dA, dB))
+    if dx is None:
+        dx = torch.empty((t, k), dtype=out_dtype, device=x.device)
+    _req(dx, "dx", out_dtype, (t, k))
+    need = int(lib().lora_group_bwd_workspace_size(t, k, arr, len(projs), r))
+    if need == 0:
+        raise ValueError(f"invalid group: {lib().msq_last_error().decode(errors='replace')}")
+    ws = _workspace(x.device, need, workspace)
+    check("lora_bwd_group", lib().lora_bwd_group(_ptr(x), t, k, arr, len(projs), cfg.c(flags), _ptr(dx),
+                                                 int(dx_accumulate), int(dAB_accumulate), _ptr(ws), ws.numel(),
+                                                 _stream(stream)))
+    return dx, grads
+
+
 def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
                  bias: Optional[torch.Tensor], A: Optional[torch.Tensor], B: Optional[torch.Tensor],
                  cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,

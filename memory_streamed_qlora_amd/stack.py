@@ -172,10 +172,9 @@ class _Spec:
 
 
 class _LoraLinearGroup(torch.autograd.Function):
-    """Projections of one input (q/k/v, gate/up): the forward is one grouped library pass;
-    the backward runs each projection's library backward and sums their dx in projection
-    order (separate adds: an unsplit GEMM epilogue that reads the old dx waits on those
-    loads block by block)."""
+    """Projections of one input (q/k/v, gate/up): the forward is one grouped library pass,
+    and so is the backward (lora_bwd_group: the projections' input gradients summed by one
+    GEMM over their concatenated rows, each projection's dA / dB as in a single call)."""
 
     @staticmethod
     def forward(ctx, x, specs, cfg, *AB):
@@ -191,12 +190,10 @@ class _LoraLinearGroup(torch.autograd.Function):
         P = len(ctx.specs)
         saved = ctx.saved_tensors
         x, AB, us = saved[0], saved[1:1 + 2 * P], saved[1 + 2 * P:]
-        dx, grads = None, []
-        for i, sp in enumerate(ctx.specs):
-            dxi, dA, dB = _bwd(sp.base, dys[i].contiguous(), x, AB[2 * i], AB[2 * i + 1], ctx.cfg, sp.key, u=us[i])
-            dx = dxi if dx is None else dx.add_(dxi)
-            grads += [dA, dB]
-        return (dx, None, None, *grads)
+        projs = [{"base": sp.base, "A": AB[2 * i], "B": AB[2 * i + 1], "key": sp.key, "dy": dys[i].contiguous(),
+                  "u": us[i]} for i, sp in enumerate(ctx.specs)]
+        dx, dAB = ops.lora_bwd_group(x, projs, ctx.cfg)
+        return (dx, None, None, *[g for pair in dAB for g in pair])
 
 
 def lora_linear_group(x, specs, As, Bs, cfg: ops.Lora):

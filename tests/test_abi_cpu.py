@@ -181,6 +181,54 @@ def test_group_rejects_bad_arguments():
     assert L.lora_fwd_group(FAKE, 8, 128, no_y, 1, cfg, FAKE, need, None) == abi.MSQ_E_INVAL
 
 
+def test_group_bwd_rejects_bad_arguments():
+    L = abi.lib()
+    key = abi.RngKey(0, 0, 0, 0, 0)
+
+    def proj(n=128, w=None, codes=FAKE, dy=FAKE, dA=FAKE):
+        return abi.LoraProjGrad(n, codes, FAKE if codes else None, w, FAKE, FAKE, key, dy, None, dA, FAKE)
+
+    two = (abi.LoraProjGrad * 2)(proj(), proj(n=64))
+    need = L.lora_group_bwd_workspace_size(8, 128, two, 2, 16)
+    assert need > 0
+    cfg = abi.LoraCfg(16, 32.0, 0.0)
+
+    def call(arr, n, c=cfg, ws=need, dx=FAKE, acc=0):
+        return L.lora_bwd_group(FAKE, 8, 128, arr, n, c, dx, acc, 0, FAKE, ws, None)
+
+    assert call(two, 0) == abi.MSQ_E_INVAL
+    assert call(two, 4) == abi.MSQ_E_INVAL
+    assert call(two, 2, ws=need - 1) == abi.MSQ_E_WORKSPACE
+    assert call(two, 2, c=abi.LoraCfg(16, 32.0, 0.0, abi.MSQ_U_ONLY)) == abi.MSQ_E_INVAL
+    assert call(two, 2, acc=2) == abi.MSQ_E_INVAL
+    assert call(two, 2, dx=None) == abi.MSQ_E_INVAL
+    assert call(two, 2, dx=FAKE + 8) == abi.MSQ_E_INVAL
+    mixed = (abi.LoraProjGrad * 2)(proj(), proj(codes=None, w=FAKE))
+    assert call(mixed, 2) == abi.MSQ_E_INVAL
+    assert "mixed" in _err()
+    bad_n = (abi.LoraProjGrad * 2)(proj(), proj(n=100))
+    assert L.lora_group_bwd_workspace_size(8, 128, bad_n, 2, 16) == 0
+    assert call(bad_n, 2) == abi.MSQ_E_SHAPE
+    assert call((abi.LoraProjGrad * 1)(proj(dy=None)), 1) == abi.MSQ_E_INVAL
+    assert call((abi.LoraProjGrad * 1)(proj(dA=None)), 1) == abi.MSQ_E_INVAL
+    assert "dA" in _err()
+    # r == 0 needs no adapters or gradient outputs
+    bare = (abi.LoraProjGrad * 1)(abi.LoraProjGrad(128, FAKE, FAKE, None, None, None, key, FAKE, None, None, None))
+    assert L.lora_group_bwd_workspace_size(8, 128, bare, 1, 0) > 0
+
+
+def test_group_bwd_plan_has_a_split_per_projection():
+    """Split i of a backward group adds projection i's LoRA term, so even a reduction of
+    three k-steps (which a single projection would not split) is cut in three: the
+    workspace holds three fp32 partial copies of dx."""
+    L = abi.lib()
+    key = abi.RngKey(0, 0, 0, 0, 0)
+    t, k = 8, 128
+    arr = (abi.LoraProjGrad * 3)(*[abi.LoraProjGrad(64, FAKE, FAKE, None, FAKE, FAKE, key, FAKE, None, FAKE, FAKE)
+                                   for _ in range(3)])
+    assert L.lora_group_bwd_workspace_size(t, k, arr, 3, 16) >= 3 * t * k * 4
+
+
 def test_workspace_size_depends_on_shape_only():
     L = abi.lib()
     a = L.nf4_lora_workspace_size(512, 5120, 27648, 16)
