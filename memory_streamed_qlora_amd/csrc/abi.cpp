@@ -85,7 +85,6 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   p.off_sk_fwd = o;   // chunk partials of the rank-r skinny products
   o = align256(o + (size_t)((k + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
   p.fwd_bytes = o;
-  p.nch = (int)((t + COLGRAD_TCHUNK - 1) / COLGRAD_TCHUNK);
   o = 0;
   p.off_part_bwd = o;
   o = align256(o + (size_t)p.bwd.splits * t * k * sizeof(float));
@@ -93,10 +92,6 @@ LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r) {
   o = align256(o + tr);
   p.off_du = o;
   o = align256(o + tr);
-  p.off_pa = o;
-  o = align256(o + (size_t)p.nch * r * k * sizeof(float));
-  p.off_pb = o;
-  o = align256(o + (size_t)p.nch * r * n * sizeof(float));
   p.off_act_bwd = o;  // dy packed into MFMA-fragment order (bf16)
   o = align256(o + (size_t)frag_rows(t) * n * sizeof(uint16_t));
   p.off_sk_bwd = o;
@@ -363,27 +358,27 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
     if (e == hipSuccess && p.bwd.splits > 1)
       e = launch_split_reduce(part, p.bwd.splits, t, k, nullptr, dx_accumulate ? dx : nullptr, false, dx, out_f32,
                               s);
-    if (e == hipSuccess && r > 0)
-      e = launch_colgrad(x, act_f32, t, k, du, r, d, p.nch, false, (float*)(ws + p.off_pa), s);
-    if (e == hipSuccess && r > 0)
-      e = launch_colgrad(dy, act_f32, t, n, uu, r, no_dropout(), p.nch, true, (float*)(ws + p.off_pb), s);
+    if (e == hipSuccess && r > 0) {
+      const ColgradTask tasks[2] = {{x, du, dA, k, 1.0f, 0, d}, {dy, uu, dB, n, lscale, 1, no_dropout()}};
+      e = launch_colgrad(tasks, 2, act_f32, t, r, dAB_accumulate, s);
+    }
+  } else if (r > 0) {
+    // no tokens: the gradients are zero (or stay as they are when accumulating)
+    const ColgradTask tasks[2] = {{nullptr, nullptr, dA, k, 1.0f, 0, no_dropout()},
+                                  {nullptr, nullptr, dB, n, lscale, 1, no_dropout()}};
+    e = launch_colgrad(tasks, 2, false, 0, r, dAB_accumulate, s);
   }
-  if (e == hipSuccess && r > 0)
-    e = launch_colgrad_reduce((float*)(ws + p.off_pa), p.nch, r, k, 1.0f, false, dA, dAB_accumulate, s);
-  if (e == hipSuccess && r > 0)
-    e = launch_colgrad_reduce((float*)(ws + p.off_pb), p.nch, r, n, lscale, true, dB, dAB_accumulate, s);
   return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
 }
 
 // Workspace of a grouped backward: fp32 split partials of dx, u (when recomputed) and du
 // of every projection, the projections' dy packed side by side along the reduction, and
-// the chunk partials of the rank-r products and of dA / dB (shared: the projections'
-// passes run one after another on the stream).
+// the chunk partials of the rank-r products (shared: the products run one after another
+// on the stream).
 struct GroupBwdPlan {
   GemmPlan bwd;
   int64_t red;  // concatenated reduction: the sum of the projections' n
-  int nch;
-  size_t off_part, off_u[GEMM_MAX_SEGS], off_du[GEMM_MAX_SEGS], off_act, off_sk, off_pa, off_pb, bytes;
+  size_t off_part, off_u[GEMM_MAX_SEGS], off_du[GEMM_MAX_SEGS], off_act, off_sk, bytes;
 };
 
 GroupBwdPlan group_bwd_plan(int64_t t, int64_t k, const int64_t* ns, int np, int32_t r) {
@@ -395,7 +390,6 @@ GroupBwdPlan group_bwd_plan(int64_t t, int64_t k, const int64_t* ns, int np, int
     nmax = std::max(nmax, ns[i]);
   }
   p.bwd = gemm_plan(t, k, p.red, np);  // split i adds projection i's LoRA term
-  p.nch = (int)((t + COLGRAD_TCHUNK - 1) / COLGRAD_TCHUNK);
   const size_t tr = (size_t)t * (size_t)r * sizeof(float);
   size_t o = 0;
   p.off_part = o;
@@ -410,10 +404,6 @@ GroupBwdPlan group_bwd_plan(int64_t t, int64_t k, const int64_t* ns, int np, int
   o = align256(o + (size_t)frag_rows(t) * p.red * sizeof(uint16_t));
   p.off_sk = o;
   o = align256(o + (size_t)((std::max(k, nmax) + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
-  p.off_pa = o;
-  o = align256(o + (size_t)p.nch * r * k * sizeof(float));
-  p.off_pb = o;
-  o = align256(o + (size_t)p.nch * r * nmax * sizeof(float));
   p.bytes = o;
   return p;
 }
@@ -627,15 +617,15 @@ int lora_bwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj_grad
     if (e == hipSuccess && p.bwd.splits > 1)
       e = launch_split_reduce(part, p.bwd.splits, t, k, nullptr, dx_accumulate ? dx : nullptr, false, dx, out_f32, s);
   }
-  // dA_i and dB_i, one projection after another through the shared chunk partials
-  for (int i = 0; i < n_proj && e == hipSuccess && r > 0; ++i) {
-    const msq_lora_proj_grad& q = projs[i];
-    float* pa = (float*)(ws + p.off_pa);
-    float* pb = (float*)(ws + p.off_pb);
-    if (t > 0) e = launch_colgrad(x, act_f32, t, k, du[i], r, d[i], p.nch, false, pa, s);
-    if (e == hipSuccess && t > 0) e = launch_colgrad(q.dy, act_f32, t, q.n, u[i], r, no_dropout(), p.nch, true, pb, s);
-    if (e == hipSuccess) e = launch_colgrad_reduce(pa, p.nch, r, k, 1.0f, false, q.dA, dAB_accumulate, s);
-    if (e == hipSuccess) e = launch_colgrad_reduce(pb, p.nch, r, q.n, lscale, true, q.dB, dAB_accumulate, s);
+  // every dA_i and dB_i in one launch (zero, or unchanged when accumulating, at t == 0)
+  if (e == hipSuccess && r > 0) {
+    ColgradTask tasks[COLGRAD_MAX_TASKS];
+    for (int i = 0; i < n_proj; ++i) {
+      const msq_lora_proj_grad& q = projs[i];
+      tasks[2 * i] = {t > 0 ? x : nullptr, du[i], q.dA, k, 1.0f, 0, d[i]};
+      tasks[2 * i + 1] = {t > 0 ? q.dy : nullptr, u[i], q.dB, q.n, lscale, 1, no_dropout()};
+    }
+    e = launch_colgrad(tasks, 2 * n_proj, act_f32, t, r, dAB_accumulate, s);
   }
   return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
 }

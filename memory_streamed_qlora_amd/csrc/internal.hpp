@@ -23,7 +23,6 @@ const Nf4Mid& nf4_mid();
 constexpr int GEMM_BM = 512;
 constexpr int GEMM_BN = 128;
 constexpr int GEMM_BK = 64;
-constexpr int COLGRAD_TCHUNK = 64;
 
 struct GemmPlan {
   int splits;          // split of the reduction dimension
@@ -38,8 +37,7 @@ GemmPlan gemm_plan_group(int64_t m, const int64_t* ns, int nseg, int64_t red);
 struct LoraPlan {
   GemmPlan fwd, bwd;
   size_t off_part_fwd, off_u_fwd, off_act_fwd, off_sk_fwd;                   // fwd layout
-  size_t off_part_bwd, off_u_bwd, off_du, off_pa, off_pb, off_act_bwd, off_sk_bwd;  // bwd layout
-  int nch;                                   // T-chunks of the dA/dB reductions
+  size_t off_part_bwd, off_u_bwd, off_du, off_act_bwd, off_sk_bwd;  // bwd layout
   size_t fwd_bytes, bwd_bytes;
 };
 LoraPlan lora_plan(int64_t t, int64_t k, int64_t n, int32_t r);
@@ -108,14 +106,23 @@ hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, c
                             int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
                             hipStream_t s, int pack_steps = 0, int pack_step0 = 0);
 
-// Column gradients in two passes, reduced over tokens in fixed-size chunks:
-// partials P(ch, j, c) = sum_{t in chunk ch} coef[t][j] * h[t][c], h = drop(in), laid out
-// [nch][r][C] (out_cr false: the output is [r][C], LoRA dA) or [nch][C][r] (out_cr true:
-// output [C][r], LoRA dB), then out = [out +] scale * sum_ch P in chunk order.
-hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
-                          const Dropout& d, int nch, bool out_cr, float* part, hipStream_t s);
-hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale, bool out_cr,
-                                 float* out, int accumulate, hipStream_t s);
+// Column gradients of the LoRA factors, up to COLGRAD_MAX_TASKS in one launch, each
+//   out[j][c] (out_cr 0: [r][C], LoRA dA) or out[c][j] (out_cr 1: [C][r], LoRA dB)
+//     = [out +] scale * sum_t coef[t][j] * h[t][c],   h = drop(in) [T][C],  coef [T][r]
+// summed over tokens in a fixed order in one pass (no workspace).  in is bf16, or fp32
+// with in_f32, for every task; accumulate applies to every task.
+constexpr int COLGRAD_MAX_TASKS = 2 * GEMM_MAX_SEGS;
+struct ColgradTask {
+  const void* in;
+  const float* coef;
+  float* out;
+  int64_t C;
+  float scale;
+  int out_cr;
+  Dropout drop;
+};
+hipError_t launch_colgrad(const ColgradTask* tasks, int ntask, bool in_f32, int64_t T, int r, int accumulate,
+                          hipStream_t s);
 
 // Sum of split partials [splits][T][N] in split order, then + bias[n] (bias may be NULL),
 // then addend + that (addend [T][N] in the output's type, may be `out`, NULL for none),

@@ -19,6 +19,8 @@
 // bitwise reproducible.  Dropout masks are regenerated from the Philox key wherever
 // they are needed; the same key gives the same mask in the forward, the recompute and
 // the backward (the pages' RNG replay requirement, "Poros" research post).
+#include <string.h>
+
 #include "internal.hpp"
 
 namespace msq {
@@ -226,123 +228,124 @@ __global__ __launch_bounds__(256) void lora_skinny_reduce(const float* __restric
   if (g == 0 && i < n) out[i] = scale * (((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x]);
 }
 
-// Partial column gradients over one chunk of COLGRAD_TCHUNK tokens:
-//   P(ch, j, c) = sum_{t in chunk} coef[t][j] * h[t][c],  j in [j0, j0 + 16), h = drop(in),
-// stored part[ch][j][c] (OUT_CR = 0, for an output laid out [r][C]) or part[ch][c][j]
-// (OUT_CR = 1, output [C][r]) so that both the stores here and the reduction read and
-// write contiguously.  Workgroup: CG_COLS columns x the chunk; thread = (4 columns, token
-// quarter = wave); each wave runs over its quarter of the tokens in order with CG_UNROLL
-// rows loaded ahead of their use, then the quarter sums are added in quarter order
-// through LDS (quarter 0 stores, 1 and 2 add, 3 adds and writes the partial).
-constexpr int CG_THREADS = 256;
-constexpr int CG_COLS = 256;
+// Column gradients of the LoRA factors, several in one launch:
+//   task i: out_i[j][c] (or out_i[c][j]) = [out_i +] scale_i * sum_t coef_i[t][j] * h_i[t][c],
+//   h_i = drop_i(in_i), j < r, c < C_i
+// (dA = du^T drop(x) with out [r][K]; dB = s dy^T u with out [N][r]).  A workgroup owns 64
+// columns of one task and CG_J ranks over all T tokens, so nothing is written twice and no
+// second pass sums partials.  Thread = (column quad cq, token slice sl): slice sl runs over
+// tokens [sl*Ts, (sl+1)*Ts) in order (Ts = ceil(T / 16)), CG_UNROLL rows in flight, with
+// the rank coefficients of its tokens loaded straight from global memory (the 16 threads of
+// a slice share each row); the 16 slice sums are then added in slice order through LDS.
 constexpr int CG_J = 16;
+constexpr int CG_COLS = 64;
+constexpr int CG_SLICES = 16;
 constexpr int CG_UNROLL = 4;
-constexpr int CG_TQ = COLGRAD_TCHUNK / 4;  // tokens per quarter
-static_assert(CG_TQ % CG_UNROLL == 0, "token quarters are whole unroll groups");
+constexpr int CG_PITCH = CG_COLS + 4;  // LDS row pitch in floats (keeps float4 alignment)
 
-template <typename TIN, int OUT_CR>
-__global__ __launch_bounds__(CG_THREADS) void lora_colgrad(const TIN* __restrict__ in, int64_t T,
-                                                           int64_t C, const float* __restrict__ coef,
-                                                           int r, Dropout d, float* __restrict__ part) {
-  __shared__ float sc[COLGRAD_TCHUNK][CG_J];
-  __shared__ __attribute__((aligned(16))) float red[CG_J][CG_COLS];
-  const int quad = threadIdx.x & 63, quarter = threadIdx.x >> 6;
-  const int64_t c = (int64_t)blockIdx.x * CG_COLS + 4 * quad;
-  const int ch = blockIdx.y;
-  const int j0 = blockIdx.z * CG_J;
-  const int64_t t0 = (int64_t)ch * COLGRAD_TCHUNK;
-  const int64_t t1 = min(T, t0 + COLGRAD_TCHUNK);
-  for (int i = threadIdx.x; i < COLGRAD_TCHUNK * CG_J; i += CG_THREADS) {
-    const int tt = i / CG_J, jj = i % CG_J;
-    const int64_t t = t0 + tt;
-    sc[tt][jj] = (t < t1 && j0 + jj < r) ? coef[t * r + j0 + jj] : 0.0f;
-  }
-  __syncthreads();
+struct CgTaskDev {
+  const void* in;
+  const float* coef;
+  float* out;
+  int64_t C;
+  float scale;
+  int out_cr;
+  int block0;  // first workgroup of the task (blockIdx.x)
+  Dropout d;
+};
+struct CgArgs {
+  CgTaskDev t[COLGRAD_MAX_TASKS];
+  int ntask;
+  int64_t T;
+  int r;
+  int accumulate;
+};
+
+template <typename TIN>
+__global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
+  __shared__ __attribute__((aligned(16))) float red[CG_SLICES][CG_J][CG_PITCH];
+  // this workgroup's task (uniform): the last one whose first block is at or before it,
+  // its fields picked at constant indices
+  CgTaskDev tk = a.t[0];
+#pragma unroll
+  for (int i = 1; i < COLGRAD_MAX_TASKS; ++i)
+    if (i < a.ntask && (int)blockIdx.x >= a.t[i].block0) tk = a.t[i];
+  const TIN* in = (const TIN*)tk.in;
+  const int tid = threadIdx.x, cq = tid & 15, sl = tid >> 4;
+  const int64_t c = (int64_t)((int)blockIdx.x - tk.block0) * CG_COLS + 4 * cq;
+  const int j0 = blockIdx.y * CG_J;
+  const int r = a.r;
+  const int64_t T = a.T, C = tk.C;
+  const bool live = c < C;
+  // rank rows as float4 when whole vectors of them stay in the row and are aligned
+  const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tk.coef) & 15) == 0;
+  const int64_t ts = (T + CG_SLICES - 1) / CG_SLICES;
+  const int64_t t0 = min(T, (int64_t)sl * ts), t1 = min(T, t0 + ts);
   float acc[CG_J][4];
 #pragma unroll
   for (int j = 0; j < CG_J; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
-  const bool live = c < C;
-  const int64_t tq0 = t0 + (int64_t)quarter * CG_TQ;
   if (live) {
-    for (int64_t tb = tq0; tb < tq0 + CG_TQ; tb += CG_UNROLL) {
+    for (int64_t tb = t0; tb < t1; tb += CG_UNROLL) {
       float h[CG_UNROLL][4];
+      float cf[CG_UNROLL][CG_J];
 #pragma unroll
       for (int u = 0; u < CG_UNROLL; ++u) {
-        const int64_t t = min(tb + u, t1 - 1);  // rows past the chunk are loaded but weighted 0
+        const int64_t t = min(tb + u, t1 - 1);  // rows past the slice: loaded, weighted 0
         load4(in + t * C + c, h[u]);
+        if (vec) {
+#pragma unroll
+          for (int j4 = 0; j4 < CG_J; j4 += 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j0 + j4 < r) v = *reinterpret_cast<const float4*>(tk.coef + t * r + j0 + j4);
+            cf[u][j4] = v.x;
+            cf[u][j4 + 1] = v.y;
+            cf[u][j4 + 2] = v.z;
+            cf[u][j4 + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < CG_J; ++j) cf[u][j] = j0 + j < r ? tk.coef[t * r + j0 + j] : 0.0f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < CG_UNROLL; ++u) {
         const int64_t t = tb + u;
-        if (d.threshold != 0u) {
-          const uint32_t keep = keep4(d, (uint64_t)min(t, t1 - 1) * (uint64_t)C + (uint64_t)c);
+        if (t >= t1) break;
+        if (tk.d.threshold != 0u) {
+          const uint32_t keep = keep4(tk.d, (uint64_t)t * (uint64_t)C + (uint64_t)c);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) h[u][q] = ((keep >> q) & 1u) ? h[u][q] * d.sigma : 0.0f;
+          for (int q = 0; q < 4; ++q) h[u][q] = ((keep >> q) & 1u) ? h[u][q] * tk.d.sigma : 0.0f;
         }
-        const int tt = (int)(t - t0);  // < COLGRAD_TCHUNK; coefficients are 0 past the chunk
 #pragma unroll
-        for (int j = 0; j < CG_J; ++j) {
-          const float cj = sc[tt][j];
+        for (int j = 0; j < CG_J; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(cj, h[u][q], acc[j][q]);
-        }
+          for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(cf[u][j], h[u][q], acc[j][q]);
       }
     }
   }
-  for (int g = 0; g < 4; ++g) {
-    if (quarter == g) {
 #pragma unroll
-      for (int j = 0; j < CG_J; ++j) {
-        float4* rp = reinterpret_cast<float4*>(&red[j][4 * quad]);
-        float4 v = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-        if (g > 0) {
-          const float4 w = *rp;
-          v = make_float4(w.x + v.x, w.y + v.y, w.z + v.z, w.w + v.w);
-        }
-        if (g < 3) {
-          *rp = v;
-        } else if (live) {
-          acc[j][0] = v.x;
-          acc[j][1] = v.y;
-          acc[j][2] = v.z;
-          acc[j][3] = v.w;
-        }
-      }
-    }
-    __syncthreads();
+  for (int j = 0; j < CG_J; ++j)
+    *reinterpret_cast<float4*>(&red[sl][j][4 * cq]) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  __syncthreads();
+  // 16 ranks x 64 columns of sums, 4 per thread; slices added in order
+  const int64_t cbase = (int64_t)((int)blockIdx.x - tk.block0) * CG_COLS;
+#pragma unroll
+  for (int k = 0; k < CG_J * CG_COLS / 256; ++k) {
+    const int o = tid + 256 * k;
+    // [r][C] output: consecutive threads take consecutive columns; [C][r]: consecutive ranks
+    const int j = tk.out_cr ? (o & (CG_J - 1)) : (o / CG_COLS);
+    const int cc = tk.out_cr ? (o / CG_J) : (o & (CG_COLS - 1));
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CG_SLICES; ++q) v += red[q][j][cc];
+    v *= tk.scale;
+    const int64_t col = cbase + cc;
+    if (j0 + j >= r || col >= C) continue;
+    float* po = tk.out_cr ? tk.out + col * r + j0 + j : tk.out + (int64_t)(j0 + j) * C + col;
+    *po = a.accumulate ? *po + v : v;
   }
-  if (quarter != 3 || !live) return;
-  if (OUT_CR == 0) {
-#pragma unroll
-    for (int j = 0; j < CG_J; ++j)
-      if (j0 + j < r)
-        *reinterpret_cast<float4*>(part + ((int64_t)ch * r + j0 + j) * C + c) =
-            make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float* p = part + ((int64_t)ch * C + c + q) * r + j0;
-#pragma unroll
-      for (int j = 0; j < CG_J; ++j)
-        if (j0 + j < r) p[j] = acc[j][q];
-    }
-  }
-}
-
-// out[i] = [out[i] +] scale * sum_ch part[ch][i], chunks in order.  The partials share the
-// output's layout ([r][C] or [C][r]), so reads and writes are contiguous either way.
-__global__ __launch_bounds__(256) void lora_colgrad_reduce(const float* __restrict__ part, int nch,
-                                                           int64_t n, float scale,
-                                                           float* __restrict__ out, int accumulate) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.0f;
-  for (int ch = 0; ch < nch; ++ch) s += part[(int64_t)ch * n + i];
-  s *= scale;
-  out[i] = accumulate ? (out[i] + s) : s;
 }
 
 // out[t][n..n+3] = sum_s P[s][t][n..n+3] (+ bias[n..n+3]) (+ old out), one rounding.
@@ -421,39 +424,39 @@ hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, c
                       dim3((unsigned)((n + 63) / 64)), dim3(256), s, (const float*)part, nck, n, scale, out);
 }
 
-hipError_t launch_colgrad(const void* in, bool in_f32, int64_t T, int64_t C, const float* coef, int r,
-                          const Dropout& d, int nch, bool out_cr, float* part, hipStream_t s) {
-  if (T == 0 || r == 0) return hipSuccess;
-  const dim3 grid((unsigned)((C + CG_COLS - 1) / CG_COLS), (unsigned)nch, (unsigned)((r + CG_J - 1) / CG_J));
-  const double bytes = (double)T * C * (in_f32 ? 4 : 2) + (double)T * r * 4 + (double)nch * r * C * 4;
-  char shape[32];
-  snprintf(shape, sizeof(shape), "%lldx%lld r%d", (long long)T, (long long)C, r);
-  const dim3 blk(CG_THREADS);
-  if (in_f32) {
-    const float* x = (const float*)in;
-    return out_cr ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float, 1>, grid, blk, s, x, T, C,
-                                 coef, r, d, part)
-                  : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float, 0>, grid, blk, s, x, T, C,
-                                 coef, r, d, part);
+hipError_t launch_colgrad(const ColgradTask* tasks, int ntask, bool in_f32, int64_t T, int r, int accumulate,
+                          hipStream_t s) {
+  if (ntask < 1 || ntask > COLGRAD_MAX_TASKS || r < 1) return hipErrorInvalidValue;
+  CgArgs a;
+  memset(&a, 0, sizeof(a));
+  a.ntask = ntask;
+  a.T = T;
+  a.r = r;
+  a.accumulate = accumulate;
+  int blocks = 0;
+  double bytes = 0.0;
+  int64_t ctot = 0;
+  for (int i = 0; i < ntask; ++i) {
+    const ColgradTask& q = tasks[i];
+    if (q.C < 1) return hipErrorInvalidValue;
+    CgTaskDev& d = a.t[i];
+    d.in = q.in;
+    d.coef = q.coef;
+    d.out = q.out;
+    d.C = q.C;
+    d.scale = q.scale;
+    d.out_cr = q.out_cr;
+    d.d = q.drop;
+    d.block0 = blocks;
+    blocks += (int)((q.C + CG_COLS - 1) / CG_COLS);
+    bytes += (double)T * q.C * (in_f32 ? 4 : 2) + (double)T * r * 4 + (double)r * q.C * 4 * (accumulate ? 2 : 1);
+    ctot += q.C;
   }
-  const uint16_t* x = (const uint16_t*)in;
-  return out_cr ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t, 1>, grid, blk, s, x, T, C,
-                               coef, r, d, part)
-                : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t, 0>, grid, blk, s, x, T, C,
-                               coef, r, d, part);
-}
-
-hipError_t launch_colgrad_reduce(const float* part, int nch, int r, int64_t C, float scale, bool out_cr,
-                                 float* out, int accumulate, hipStream_t s) {
-  const int64_t n = (int64_t)r * C;
-  if (n == 0) return hipSuccess;
-  char shape[32];
-  snprintf(shape, sizeof(shape), "%dx%lld c%d", r, (long long)C, nch);
-  const dim3 grid((unsigned)((n + 255) / 256));
-  const double bytes = (double)(nch + 1 + (accumulate ? 1 : 0)) * n * 4;
-  (void)out_cr;  // the partials already carry the output's layout
-  return timed_launch("lora_colgrad_reduce", shape, 0.0, bytes, lora_colgrad_reduce, grid, dim3(256), s, part, nch, n,
-                      scale, out, accumulate);
+  const dim3 grid((unsigned)blocks, (unsigned)((r + CG_J - 1) / CG_J));
+  char shape[40];
+  snprintf(shape, sizeof(shape), "%lldx%lld r%d n%d", (long long)T, (long long)ctot, r, ntask);
+  return in_f32 ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float>, grid, dim3(256), s, a)
+                : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t>, grid, dim3(256), s, a);
 }
 
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,
