@@ -198,9 +198,12 @@ def h2d_busy(window, ms_per_step: float, ceiling: float) -> dict:
             "GBps_while_copying": round(rate, 1), "frac_while_copying": round(rate / ceiling, 3)}
 
 
-def rocprof_summary(d: str) -> int:
-    """Summarise rocprofv3 CSV output found under directory d (kernel stats and/or
-    per-dispatch counter collections) as markdown on stdout."""
+def rocprof_summary(d: str, timed: int = 5, total: int = 7) -> int:
+    """Summarise rocprofv3 CSV output found under directory d (kernel stats, per-dispatch
+    kernel traces, counter collections, memory-copy traces) as markdown on stdout.  For a
+    kernel trace of the bench, the GEMM kernels' average is also given over the last
+    timed/total of their dispatches: the timed steps of a run with `total` streamed steps
+    of which the last `timed` are timed (no resident leg)."""
     import csv
     import glob
 
@@ -213,6 +216,21 @@ def rocprof_summary(d: str) -> int:
         for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:25]:
             print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                   f"{float(r['TotalDurationNs']) / 1e6:.1f} | {100 * float(r['TotalDurationNs']) / tot:.1f} |")
+        print()
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        durs = {}
+        for r in csv.DictReader(open(path)):
+            for k in ("nf4_fwd_gemm", "nf4_bwd_gemm"):
+                if f"::{k}(" in r["Kernel_Name"]:
+                    durs.setdefault(k, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        print(f"### GEMM dispatches ({os.path.relpath(path, d)})\n")
+        print(f"| kernel | dispatches | avg us (all) | dispatches in the last {timed}/{total} | avg us (those) |")
+        print("|---|---|---|---|---|")
+        for k, v in sorted(durs.items()):
+            v.sort()
+            us = [(b - a) / 1e3 for a, b in v]
+            last = us[len(us) - len(us) // total * timed:]
+            print(f"| {k} | {len(us)} | {sum(us) / len(us):.1f} | {len(last)} | {sum(last) / max(1, len(last)):.1f} |")
         print()
     for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         agg = {}
@@ -343,8 +361,8 @@ def vendor_gemm(reps: int = 20) -> int:
 
 
 def main() -> int:
-    if len(sys.argv) == 3 and sys.argv[1] == "--rocprof-summary":
-        return rocprof_summary(sys.argv[2])
+    if len(sys.argv) in (3, 5) and sys.argv[1] == "--rocprof-summary":
+        return rocprof_summary(sys.argv[2], *[int(a) for a in sys.argv[3:]])
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
