@@ -243,10 +243,10 @@ int lora_fwd(const char* fn, const void* x, int64_t t, int64_t k, int64_t n, con
 
 // Workspace of a grouped forward: fp32 split partials of every projection (consecutive
 // [splits][t][n_i] blocks), u of each projection, the packed activation and the chunk
-// partials of the rank-r products (shared: the products run one after another).
+// partials of each projection's rank-r product (one packing pass forms them all).
 struct GroupPlan {
   GemmPlan fwd;
-  size_t off_part, off_u[GEMM_MAX_SEGS], off_act, off_sk, bytes;
+  size_t off_part, off_u[GEMM_MAX_SEGS], off_act, off_sk[GEMM_MAX_SEGS], bytes;
 };
 
 GroupPlan group_plan(int64_t t, int64_t k, const int64_t* ns, int np, int32_t r) {
@@ -263,8 +263,10 @@ GroupPlan group_plan(int64_t t, int64_t k, const int64_t* ns, int np, int32_t r)
   }
   p.off_act = o;
   o = align256(o + (size_t)frag_rows(t) * k * sizeof(uint16_t));
-  p.off_sk = o;
-  o = align256(o + (size_t)((k + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
+  for (int i = 0; i < GEMM_MAX_SEGS; ++i) {
+    p.off_sk[i] = o;
+    if (i < np) o = align256(o + (size_t)((k + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
+  }
   p.bytes = o;
   return p;
 }
@@ -373,12 +375,12 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
 
 // Workspace of a grouped backward: fp32 split partials of dx, u (when recomputed) and du
 // of every projection, the projections' dy packed side by side along the reduction, and
-// the chunk partials of the rank-r products (shared: the products run one after another
-// on the stream).
+// each projection's chunk partials of its rank-r products (the u pass is summed before
+// the du pass reuses them).
 struct GroupBwdPlan {
   GemmPlan bwd;
   int64_t red;  // concatenated reduction: the sum of the projections' n
-  size_t off_part, off_u[GEMM_MAX_SEGS], off_du[GEMM_MAX_SEGS], off_act, off_sk, bytes;
+  size_t off_part, off_u[GEMM_MAX_SEGS], off_du[GEMM_MAX_SEGS], off_act, off_sk[GEMM_MAX_SEGS], bytes;
 };
 
 GroupBwdPlan group_bwd_plan(int64_t t, int64_t k, const int64_t* ns, int np, int32_t r) {
@@ -402,8 +404,10 @@ GroupBwdPlan group_bwd_plan(int64_t t, int64_t k, const int64_t* ns, int np, int
   }
   p.off_act = o;
   o = align256(o + (size_t)frag_rows(t) * p.red * sizeof(uint16_t));
-  p.off_sk = o;
-  o = align256(o + (size_t)((std::max(k, nmax) + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
+  for (int i = 0; i < GEMM_MAX_SEGS; ++i) {
+    p.off_sk[i] = o;
+    if (i < np) o = align256(o + (size_t)((std::max(k, ns[i]) + LORA_CHUNK - 1) / LORA_CHUNK) * t * r * sizeof(float));
+  }
   p.bytes = o;
   return p;
 }
@@ -487,14 +491,16 @@ int lora_fwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj* pro
   uint16_t* xb = (uint16_t*)(ws + p.off_act);
   float* u[GEMM_MAX_SEGS];
   hipError_t e = hipSuccess;
-  // the activation is packed once (with the first projection's rank-r product); the other
-  // products read x again with their own dropout masks
-  for (int i = 0; i < n_proj && e == hipSuccess; ++i) {
+  // one pass over x packs it and forms every projection's rank-r product (each with its
+  // own A and dropout mask), one launch sums their chunk partials
+  LoraProduct prods[GEMM_MAX_SEGS];
+  for (int i = 0; i < n_proj; ++i) {
     const msq_lora_proj& q = projs[i];
     u[i] = q.u_out ? q.u_out : (float*)(ws + p.off_u[i]);
-    e = launch_pack_lora(x, act_f32, t, k, q.A, 0, r, 1.0f, make_dropout(q.key, cfg.p_drop), i == 0 ? xb : nullptr,
-                         (float*)(ws + p.off_sk), u[i], s);
+    prods[i] = {q.A, make_dropout(q.key, cfg.p_drop), 1.0f, (float*)(ws + p.off_sk[i]), u[i], 0};
   }
+  e = launch_pack_products(x, act_f32, t, k, 0, r, prods, n_proj, xb, s);
+  if (e == hipSuccess) e = launch_product_reduce(prods, n_proj, t, r, s);
   float* part = (float*)(ws + p.off_part);
   size_t part_off[GEMM_MAX_SEGS];
   if (e == hipSuccess) {
@@ -571,22 +577,32 @@ int lora_bwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj_grad
     u[i] = projs[i].u;
   }
   if (t > 0) {
-    float* sk = (float*)(ws + p.off_sk);
     uint16_t* act = (uint16_t*)(ws + p.off_act);
     const int steps = (int)(p.red / 64);
+    // u of the projections whose forward u was not passed in: one pass over x for all
+    LoraProduct up[GEMM_MAX_SEGS];
+    int nu = 0;
+    for (int i = 0; i < n_proj && r > 0; ++i)
+      if (!u[i]) {
+        float* ut = (float*)(ws + p.off_u[i]);
+        up[nu++] = {projs[i].A, d[i], 1.0f, (float*)(ws + p.off_sk[i]), ut, 0};
+        u[i] = ut;
+      }
+    if (nu > 0) {
+      e = launch_pack_products(x, act_f32, t, k, 0, r, up, nu, nullptr, s);
+      if (e == hipSuccess) e = launch_product_reduce(up, nu, t, r, s);
+    }
+    // dy_i into k-steps step0 .. of the shared operand, with the partials of du_i = s dy_i B_i;
+    // one launch then sums every du
+    LoraProduct dp[GEMM_MAX_SEGS];
     int step0 = 0;
     for (int i = 0; i < n_proj && e == hipSuccess; ++i) {
       const msq_lora_proj_grad& q = projs[i];
-      if (r > 0 && !u[i]) {
-        float* ut = (float*)(ws + p.off_u[i]);
-        e = launch_pack_lora(x, act_f32, t, k, q.A, 0, r, 1.0f, d[i], nullptr, sk, ut, s);
-        u[i] = ut;
-      }
-      // dy_i into k-steps step0 .. of the shared operand, with du_i = s dy_i B_i
-      if (e == hipSuccess)
-        e = launch_pack_lora(q.dy, act_f32, t, q.n, q.B, 1, r, lscale, no_dropout(), act, sk, du[i], s, steps, step0);
+      dp[i] = {q.B, no_dropout(), lscale, (float*)(ws + p.off_sk[i]), du[i], 0};
+      e = launch_pack_products(q.dy, act_f32, t, q.n, 1, r, &dp[i], 1, act, s, steps, step0);
       step0 += (int)(q.n / 64);
     }
+    if (e == hipSuccess) e = launch_product_reduce(dp, n_proj, t, r, s);
     float* part = (float*)(ws + p.off_part);
     if (e == hipSuccess) {
       GemmLaunch L;

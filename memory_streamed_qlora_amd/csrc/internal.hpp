@@ -106,6 +106,24 @@ hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, c
                             int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
                             hipStream_t s, int pack_steps = 0, int pack_step0 = 0);
 
+// The same pass with the rank-r products of up to GEMM_MAX_SEGS projections that read one
+// activation (each its own matrix, dropout mask, partial buffer and output), in two
+// launches: launch_pack_products (the packing and every product's chunk partials; sets
+// each nck) and launch_product_reduce (every product's chunks summed in order, scaled).
+// The reduction may also take products of different packing passes (their own nck).
+struct LoraProduct {
+  const float* mat;  // [r][C] (mat_kind 0) or [C][r] (mat_kind 1)
+  Dropout drop;
+  float scale;
+  float* part;       // [ceil(C / LORA_CHUNK)][T][r] floats of its own
+  float* out;        // [T][r]
+  int nck;
+};
+hipError_t launch_pack_products(const void* in, bool in_f32, int64_t T, int64_t C, int mat_kind, int r,
+                                LoraProduct* prods, int nprod, uint16_t* packed, hipStream_t s,
+                                int pack_steps = 0, int pack_step0 = 0);
+hipError_t launch_product_reduce(const LoraProduct* prods, int nprod, int64_t T, int r, hipStream_t s);
+
 // Column gradients of the LoRA factors, up to COLGRAD_MAX_TASKS in one launch, each
 //   out[j][c] (out_cr 0: [r][C], LoRA dA) or out[c][j] (out_cr 1: [C][r], LoRA dB)
 //     = [out +] scale * sum_t coef[t][j] * h[t][c],   h = drop(in) [T][C],  coef [T][r]

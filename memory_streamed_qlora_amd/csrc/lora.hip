@@ -21,6 +21,8 @@
 // the backward (the pages' RNG replay requirement, "Poros" research post).
 #include <string.h>
 
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace msq {
@@ -70,28 +72,51 @@ __device__ __forceinline__ void round4(const uint16_t*, float a[4]) {
 }
 __device__ __forceinline__ void round4(const float*, float[4]) {}
 
-// Packing pass over an activation [T][C] (bf16 or fp32), fused with its rank-r product.
-// One workgroup covers 32 rows x LORA_CHUNK columns (4 k-steps of 64) and ranks
-// j0..j0+15 (grid z over rank groups).  Thread t handles row t >> 3 and 8 consecutive
-// columns (t & 7) of every k-step, loaded coalesced, and
-//   - writes them as bf16 in MFMA-fragment order (rank group 0 only, if `packed`):
+// Packing pass over an activation [T][C] (bf16 or fp32), fused with the rank-r products
+// of up to GEMM_MAX_SEGS projections that read it (each its own adapter and dropout mask).
+// One workgroup covers 32 rows x LORA_CHUNK columns (4 k-steps of 64), one projection and
+// its ranks j0..j0+15 (grid z over projection x rank group).  Thread t handles row t >> 3
+// and 8 consecutive columns (t & 7) of every k-step, loaded coalesced, and
+//   - writes them as bf16 in MFMA-fragment order (grid z 0 only, if `packed`):
 //     lane (row + 32 * (chunk >> 2)) of sub-step (chunk & 3), see launch_pack_frag;
-//   - accumulates h[t][c] * M(c, j) for its 16 ranks, h = drop(in) (dropout applied to
-//     the rank-r copy only), the adapter chunk staged in LDS rank-major;
+//   - accumulates h[t][c] * M(c, j) for its 16 ranks, h = drop(in) (the projection's
+//     dropout applied to the rank-r copy only), the adapter chunk staged in LDS rank-major;
 // then the 8 threads of a row combine their partials with a fixed butterfly and the
-// chunk partial goes to part[chunk][t][j]; skinny_reduce sums the chunks in order.
+// chunk partial goes to the projection's part[chunk][t][j]; lora_skinny_reduce sums the
+// chunks in order.
 constexpr int PK_STEPS = LORA_CHUNK / 64;
 
+struct PackProj {
+  const float* mat;
+  float* part;
+  Dropout d;
+};
+struct PackArgs {
+  int64_t T, C;
+  int steps, r, rgroups;
+  uint16_t* packed;
+  int pstride, pstep0;
+  PackProj p[GEMM_MAX_SEGS];
+};
+
 template <typename TIN, int MAT_KIND>
-__global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int64_t T, int64_t C, int steps,
-                                                 const float* __restrict__ mat, int r, Dropout d,
-                                                 uint16_t* __restrict__ packed, int pstride, int pstep0,
-                                                 float* __restrict__ part) {
+__global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, PackArgs a) {
   __shared__ __attribute__((aligned(16))) float ms[16][LORA_CHUNK + 4];
+  const int64_t T = a.T, C = a.C;
+  const int steps = a.steps, r = a.r;
+  // projection and rank group of this workgroup (uniform); fields picked at constant indices
+  const int pi = (int)blockIdx.z / a.rgroups, rg = (int)blockIdx.z % a.rgroups;
+  const float* __restrict__ mat = pi == 0 ? a.p[0].mat : pi == 1 ? a.p[1].mat : a.p[2].mat;
+  float* __restrict__ part = pi == 0 ? a.p[0].part : pi == 1 ? a.p[1].part : a.p[2].part;
+  Dropout d = a.p[0].d;
+  if (pi == 1) d = a.p[1].d;
+  if (pi == 2) d = a.p[2].d;
+  uint16_t* __restrict__ packed = blockIdx.z == 0 ? a.packed : nullptr;
+  const int pstride = a.pstride, pstep0 = a.pstep0;
   const int tid = threadIdx.x, row = tid >> 3, ch = tid & 7;
   const int grp = blockIdx.y, s0 = blockIdx.x * PK_STEPS;
   const int nst = min(PK_STEPS, steps - s0);
-  const int j0 = blockIdx.z * 16;
+  const int j0 = rg * 16;
   const int64_t m = (int64_t)grp * 32 + row;
   const int64_t c0 = (int64_t)s0 * 64;
   // this thread's activation loads first (PK_STEPS x 8 elements in flight), so that their
@@ -145,7 +170,7 @@ __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int
     const int step = s0 + b;
     const int64_t c = (int64_t)step * 64 + ch * 8;
     float* f = fa[b];
-    if (packed && blockIdx.z == 0) {
+    if (packed) {
       const uint4 v = make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
                                  bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
       const int lane = row + 32 * (ch >> 2), sub = ch & 3;
@@ -200,13 +225,29 @@ __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, int
   }
 }
 
-// out[i] = scale * sum_c part[c][i] for i < n.  A workgroup owns 64 outputs; its four
-// waves sum four contiguous ranges of chunks in order (loads issued ahead of the adds)
-// and the four range sums are added in range order, so the result is fixed.
-__global__ __launch_bounds__(256) void lora_skinny_reduce(const float* __restrict__ part, int nck,
-                                                          int64_t n, float scale,
-                                                          float* __restrict__ out) {
+// out[i] = scale * sum_c part[c][i] for i < n, for up to GEMM_MAX_SEGS products (grid y).
+// A workgroup owns 64 outputs; its four waves sum four contiguous ranges of chunks in order
+// (loads issued ahead of the adds) and the four range sums are added in range order, so
+// the result is fixed.
+struct ReduceTask {
+  const float* part;
+  float* out;
+  float scale;
+  int nck;
+};
+struct ReduceArgs {
+  ReduceTask t[GEMM_MAX_SEGS];
+  int64_t n;
+};
+
+__global__ __launch_bounds__(256) void lora_skinny_reduce(ReduceArgs ra) {
   __shared__ float red[4][64];
+  const int ti = blockIdx.y;
+  const float* __restrict__ part = ti == 0 ? ra.t[0].part : ti == 1 ? ra.t[1].part : ra.t[2].part;
+  float* __restrict__ out = ti == 0 ? ra.t[0].out : ti == 1 ? ra.t[1].out : ra.t[2].out;
+  const float scale = ti == 0 ? ra.t[0].scale : ti == 1 ? ra.t[1].scale : ra.t[2].scale;
+  const int nck = ti == 0 ? ra.t[0].nck : ti == 1 ? ra.t[1].nck : ra.t[2].nck;
+  const int64_t n = ra.n;
   const int g = threadIdx.x >> 6;
   const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
   const int q = (nck + 3) / 4, c0 = g * q, c1 = min(nck, c0 + q);
@@ -385,43 +426,77 @@ __global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ pa
 }
 
 template <typename TIN, int MAT_KIND>
-hipError_t pack_lora_dispatch(const TIN* in, int64_t T, int64_t C, const float* mat, int r, const Dropout& d,
-                              uint16_t* packed, int pstride, int pstep0, float* part, hipStream_t s) {
-  const int steps = (int)(C / 64);
-  if (pstride == 0) pstride = steps;
-  if (pstep0 < 0 || pstep0 + steps > pstride) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((steps + PK_STEPS - 1) / PK_STEPS), (unsigned)((T + 31) / 32),
-                  (unsigned)(r > 0 ? (r + 15) / 16 : 1));
-  const double nck = (double)((C + LORA_CHUNK - 1) / LORA_CHUNK);
-  const double bytes = (double)T * C * sizeof(TIN) + (packed ? (double)frag_rows(T) * C * 2 : 0.0) +
-                       (r > 0 ? (double)r * C * 4 + nck * T * r * 4 : 0.0);
-  char shape[32];
-  snprintf(shape, sizeof(shape), "%lldx%lld r%d", (long long)T, (long long)C, r);
-  return timed_launch(packed ? "pack_lora" : "lora_product", shape, 0.0, bytes, pack_lora<TIN, MAT_KIND>, grid,
-                      dim3(256), s, in, T, C, steps, mat, r, d, packed, pstride, pstep0, part);
+hipError_t pack_lora_dispatch(const TIN* in, const PackArgs& a, int nprod, bool packs, hipStream_t s) {
+  const dim3 grid((unsigned)((a.steps + PK_STEPS - 1) / PK_STEPS), (unsigned)((a.T + 31) / 32),
+                  (unsigned)(nprod * a.rgroups));
+  const double nck = (double)((a.C + LORA_CHUNK - 1) / LORA_CHUNK);
+  const double bytes = (double)a.T * a.C * sizeof(TIN) + (packs ? (double)frag_rows(a.T) * a.C * 2 : 0.0) +
+                       (a.r > 0 ? nprod * ((double)a.r * a.C * 4 + nck * a.T * a.r * 4) : 0.0);
+  char shape[40];
+  snprintf(shape, sizeof(shape), "%lldx%lld r%d p%d", (long long)a.T, (long long)a.C, a.r, nprod);
+  return timed_launch(packs ? "pack_lora" : "lora_product", shape, 0.0, bytes, pack_lora<TIN, MAT_KIND>, grid,
+                      dim3(256), s, in, a);
 }
 
 }  // namespace
 
+hipError_t launch_pack_products(const void* in, bool in_f32, int64_t T, int64_t C, int mat_kind, int r,
+                                LoraProduct* prods, int nprod, uint16_t* packed, hipStream_t s, int pack_steps,
+                                int pack_step0) {
+  if (nprod < 0 || nprod > GEMM_MAX_SEGS || (r > 0 && nprod < 1)) return hipErrorInvalidValue;
+  const int nck = (int)((C + LORA_CHUNK - 1) / LORA_CHUNK);
+  for (int i = 0; i < nprod; ++i) prods[i].nck = nck;
+  if (T == 0 || (r == 0 && !packed)) return hipSuccess;
+  PackArgs a;
+  memset(&a, 0, sizeof(a));
+  a.T = T;
+  a.C = C;
+  a.steps = (int)(C / 64);
+  a.r = r;
+  a.rgroups = r > 0 ? (r + 15) / 16 : 1;
+  a.packed = packed;
+  a.pstride = pack_steps == 0 ? a.steps : pack_steps;
+  a.pstep0 = pack_step0;
+  if (a.pstep0 < 0 || a.pstep0 + a.steps > a.pstride) return hipErrorInvalidValue;
+  const int np = r > 0 ? nprod : 1;  // r == 0: a packing pass only
+  for (int i = 0; i < np && r > 0; ++i) {
+    a.p[i].mat = prods[i].mat;
+    a.p[i].part = prods[i].part;
+    a.p[i].d = prods[i].drop;
+  }
+  if (in_f32)
+    return mat_kind == 0 ? pack_lora_dispatch<float, 0>((const float*)in, a, np, packed != nullptr, s)
+                         : pack_lora_dispatch<float, 1>((const float*)in, a, np, packed != nullptr, s);
+  return mat_kind == 0 ? pack_lora_dispatch<uint16_t, 0>((const uint16_t*)in, a, np, packed != nullptr, s)
+                       : pack_lora_dispatch<uint16_t, 1>((const uint16_t*)in, a, np, packed != nullptr, s);
+}
+
+hipError_t launch_product_reduce(const LoraProduct* prods, int nprod, int64_t T, int r, hipStream_t s) {
+  if (T == 0 || r == 0 || nprod == 0) return hipSuccess;
+  if (nprod < 0 || nprod > GEMM_MAX_SEGS) return hipErrorInvalidValue;
+  ReduceArgs ra;
+  memset(&ra, 0, sizeof(ra));
+  ra.n = T * r;
+  double bytes = 0.0;
+  int nck_max = 0;
+  for (int i = 0; i < nprod; ++i) {
+    ra.t[i] = {prods[i].part, prods[i].out, prods[i].scale, prods[i].nck};
+    bytes += (double)(prods[i].nck + 1) * ra.n * 4;
+    nck_max = std::max(nck_max, prods[i].nck);
+  }
+  char shape[40];
+  snprintf(shape, sizeof(shape), "%lldx%d c%d p%d", (long long)T, r, nck_max, nprod);
+  return timed_launch("lora_product_reduce", shape, 0.0, bytes, lora_skinny_reduce,
+                      dim3((unsigned)((ra.n + 63) / 64), (unsigned)nprod), dim3(256), s, ra);
+}
+
 hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, const float* mat, int mat_kind,
                             int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
                             hipStream_t s, int pack_steps, int pack_step0) {
-  if (T == 0 || (r == 0 && !packed)) return hipSuccess;
-  hipError_t e;
-  const int ps = pack_steps, p0 = pack_step0;
-  if (in_f32)
-    e = mat_kind == 0 ? pack_lora_dispatch<float, 0>((const float*)in, T, C, mat, r, d, packed, ps, p0, part, s)
-                      : pack_lora_dispatch<float, 1>((const float*)in, T, C, mat, r, d, packed, ps, p0, part, s);
-  else
-    e = mat_kind == 0 ? pack_lora_dispatch<uint16_t, 0>((const uint16_t*)in, T, C, mat, r, d, packed, ps, p0, part, s)
-                      : pack_lora_dispatch<uint16_t, 1>((const uint16_t*)in, T, C, mat, r, d, packed, ps, p0, part, s);
-  if (e != hipSuccess || r == 0) return e;
-  const int nck = (int)((C + LORA_CHUNK - 1) / LORA_CHUNK);
-  const int64_t n = T * r;
-  char shape[32];
-  snprintf(shape, sizeof(shape), "%lldx%d c%d", (long long)T, r, nck);
-  return timed_launch("lora_product_reduce", shape, 0.0, (double)(nck + 1) * n * 4, lora_skinny_reduce,
-                      dim3((unsigned)((n + 63) / 64)), dim3(256), s, (const float*)part, nck, n, scale, out);
+  LoraProduct pr{mat, d, scale, part, out, 0};
+  hipError_t e = launch_pack_products(in, in_f32, T, C, mat_kind, r, &pr, 1, packed, s, pack_steps, pack_step0);
+  if (e == hipSuccess) e = launch_product_reduce(&pr, 1, T, r, s);
+  return e;
 }
 
 hipError_t launch_colgrad(const ColgradTask* tasks, int ntask, bool in_f32, int64_t T, int r, int accumulate,
