@@ -277,20 +277,23 @@ def rope(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor) -> torch.Tensor:
     return x * cos[:, None, :] + rot * sin[:, None, :]
 
 
-def causal_gqa_attention(q, k, v, mask_add):
-    """q [T,H,D], k/v [T,KV,D] fp32 -> [T, H*D] fp32."""
+def causal_gqa_attention(q, k, v, mask_rep):
+    """q [T,H,D], k/v [T,KV,D] fp32 -> [T, H*D] fp32; key/value head j serves query heads
+    j*g .. j*g+g-1 (g = H/KV).  The g query heads that share a key/value head are stacked
+    along the rows of one operand, so each product is a batch of KV GEMMs over g*T rows
+    (no expanded copies of k and v), and the scale and the causal mask (mask_rep: the
+    additive [T, T] mask repeated for the g heads, [g*T, T]) are applied by the score
+    product itself (baddbmm)."""
     T, H, D = q.shape
     KV = k.shape[1]
     g = H // KV
-    k = k[:, :, None, :].expand(T, KV, g, D).reshape(T, H, D)
-    v = v[:, :, None, :].expand(T, KV, g, D).reshape(T, H, D)
-    qh = q.permute(1, 0, 2).contiguous()
+    qh = q.permute(1, 0, 2).reshape(KV, g * T, D)
     kt = k.permute(1, 2, 0).contiguous()
     vh = v.permute(1, 0, 2).contiguous()
-    s = torch.matmul(qh, kt) * (1.0 / math.sqrt(D)) + mask_add
+    s = torch.baddbmm(mask_rep, qh, kt, alpha=1.0 / math.sqrt(D))
     p = torch.softmax(s, dim=-1)
-    o = torch.matmul(p, vh)
-    return o.permute(1, 0, 2).reshape(T, H * D)
+    o = torch.bmm(p, vh)
+    return o.view(H, T, D).permute(1, 0, 2).reshape(T, H * D)
 
 
 @dataclass
@@ -329,6 +332,7 @@ class Stack:
         self.emb = self.lm = self.lnf = None
         self.cos, self.sin = rope_tables(seq, shape.head_dim, self.dev)
         self.mask_add = torch.triu(torch.full((seq, seq), float("-inf"), device=self.dev), 1)
+        self._mask_reps: Dict[int, torch.Tensor] = {}
         self.opt: Optional[torch.optim.Optimizer] = None
         self.step_index = 0
 
@@ -365,6 +369,13 @@ class Stack:
         self.emb = emb.detach().to("cpu", torch.bfloat16).contiguous()
         self.lm = lm.to(self.dev, torch.bfloat16).contiguous()
         self.lnf = lnf.to(self.dev, torch.float32)
+
+    def _mask_rep(self, T: int) -> torch.Tensor:
+        """The causal mask of T tokens repeated for the query heads of one key/value head."""
+        if T not in self._mask_reps:
+            g = self.shape.heads // self.shape.kv_heads
+            self._mask_reps[T] = self.mask_add[:T, :T].repeat(g, 1).contiguous()
+        return self._mask_reps[T]
 
     def _embed(self, tokens: torch.Tensor) -> torch.Tensor:
         """Rows of the host embedding for `tokens` (host or device), as fp32 on the device."""
@@ -549,7 +560,7 @@ class Stack:
             q, k = _RoPE.apply(q, cos, sin), _RoPE.apply(k, cos, sin)
         else:
             q, k = rope(q, cos, sin), rope(k, cos, sin)
-        att = causal_gqa_attention(q, k, v, self.mask_add[:T, :T])
+        att = causal_gqa_attention(q, k, v, self._mask_rep(T))
         h1 = self._lin(att, l, views, "o", step, micro, residual=h)
         xn2 = norm(h1, self.ln2[l])
         g, u = self._lin_group(xn2, l, views, ("gate", "up"), step, micro)
