@@ -330,6 +330,11 @@ class Stack:
         self.A: List[Dict[str, torch.nn.Parameter]] = []
         self.B: List[Dict[str, torch.nn.Parameter]] = []
         self.emb = self.lm = self.lnf = None
+        self.lm_host: Optional[torch.Tensor] = None
+        self._lm_ring: List[torch.Tensor] = []
+        self._lm_read: List[Optional[torch.cuda.Event]] = [None, None]
+        self.lm_copy_timing = False  # time each lm_head chunk copy (events on the copy stream)
+        self._lm_copy_log: List[Tuple[torch.cuda.Event, torch.cuda.Event, int]] = []
         self.cos, self.sin = rope_tables(seq, shape.head_dim, self.dev)
         self.mask_add = torch.triu(torch.full((seq, seq), float("-inf"), device=self.dev), 1)
         self._mask_reps: Dict[int, torch.Tensor] = {}
@@ -365,9 +370,18 @@ class Stack:
 
     def set_globals(self, emb: torch.Tensor, lm: torch.Tensor, lnf: torch.Tensor) -> None:
         """The frozen token embedding stays in host memory (a step gathers only its T rows
-        and copies them over); the frozen lm_head and final norm live on the device."""
+        and copies them over).  The frozen lm_head lives on the device in resident mode; in
+        streamed mode it stays in pinned host memory and the loss streams it chunk by chunk
+        through a two-chunk device ring, like the base.  The final norm is on the device."""
         self.emb = emb.detach().to("cpu", torch.bfloat16).contiguous()
-        self.lm = lm.to(self.dev, torch.bfloat16).contiguous()
+        if self.mode == "streamed":
+            self.lm_host = torch.empty(lm.shape, dtype=torch.bfloat16, pin_memory=True)
+            self.lm_host.copy_(lm)
+            self.lm = None
+            rows = min(self.LM_CHUNK, lm.shape[0])
+            self._lm_ring = [torch.empty(rows, lm.shape[1], dtype=torch.bfloat16, device=self.dev) for _ in range(2)]
+        else:
+            self.lm = lm.to(self.dev, torch.bfloat16).contiguous()
         self.lnf = lnf.to(self.dev, torch.float32)
 
     def _mask_rep(self, T: int) -> torch.Tensor:
@@ -384,9 +398,11 @@ class Stack:
         return rows.to(self.dev, non_blocking=True).float()
 
     def finalize(self) -> None:
-        params = [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
-        self.opt = torch.optim.AdamW(params, lr=LR, betas=BETAS, eps=ADAM_EPS, weight_decay=WD,
-                                     foreach=True)
+        # one parameter group per layer: the foreach update then allocates its temporaries
+        # one layer at a time instead of for all adapters at once (the per-element arithmetic
+        # is the same either way)
+        groups = [{"params": list(self.A[l].values()) + list(self.B[l].values())} for l in range(len(self.A))]
+        self.opt = torch.optim.AdamW(groups, lr=LR, betas=BETAS, eps=ADAM_EPS, weight_decay=WD, foreach=True)
         if self.mode == "streamed":
             self.copy_stream = torch.cuda.Stream(device=self.dev)
             self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks, self.n_slots,
@@ -652,28 +668,114 @@ class Stack:
                 self.window.prefetch(rw[wi + ahead])
         return losses
 
-    CE_CHUNK = 128  # tokens per lm_head / cross-entropy chunk
+    LM_CHUNK = 4224  # vocabulary rows per lm_head chunk (152064 = 36 x 4224)
+
+    def _lm_chunks(self):
+        """(first row, lm_head rows) over the vocabulary in order: views of the device
+        lm_head, or, with the lm_head in pinned host memory, chunks copied through a
+        two-buffer device ring on the copy stream (a buffer is refilled only after the
+        work that read its previous chunk)."""
+        V = self.shape.vocab
+        starts = list(range(0, V, self.LM_CHUNK))
+        if self.lm_host is None:
+            for c0 in starts:
+                yield c0, self.lm[c0:c0 + self.LM_CHUNK]
+            return
+        cur = torch.cuda.current_stream(self.dev)
+        copied = {}
+
+        def issue(i: int) -> None:
+            b, c0 = i % 2, starts[i]
+            rows = min(self.LM_CHUNK, V - c0)
+            with torch.cuda.stream(self.copy_stream):
+                if self._lm_read[b] is not None:
+                    self.copy_stream.wait_event(self._lm_read[b])
+                t0 = None
+                if self.lm_copy_timing:
+                    t0 = torch.cuda.Event(enable_timing=True)
+                    t0.record(self.copy_stream)
+                self._lm_ring[b][:rows].copy_(self.lm_host[c0:c0 + rows], non_blocking=True)
+                ev = torch.cuda.Event(enable_timing=self.lm_copy_timing)
+                ev.record(self.copy_stream)
+                if t0 is not None:
+                    self._lm_copy_log.append((t0, ev, self._lm_ring[b][:rows].nbytes))
+            copied[i] = ev
+
+        for i in range(min(2, len(starts))):
+            issue(i)
+        for i, c0 in enumerate(starts):
+            rows = min(self.LM_CHUNK, V - c0)
+            cur.wait_event(copied.pop(i))
+            yield c0, self._lm_ring[i % 2][:rows]
+            ev = torch.cuda.Event()
+            ev.record(cur)
+            self._lm_read[i % 2] = ev
+            if i + 2 < len(starts):
+                issue(i + 2)
+
+    def lm_copy_stats(self) -> Dict[str, float]:
+        """Bytes, copies and copy-stream milliseconds of the lm_head chunk copies timed since
+        the last call (lm_copy_timing on; call after the device has synchronised)."""
+        ms = sum(a.elapsed_time(b) for a, b, _ in self._lm_copy_log)
+        out = {"bytes": float(sum(n for _, _, n in self._lm_copy_log)), "copies": len(self._lm_copy_log), "ms": ms}
+        self._lm_copy_log = []
+        return out
+
+    def _lm_rows(self, idx_cpu: torch.Tensor) -> torch.Tensor:
+        """lm_head rows idx (bf16 [len(idx), hidden]) on the device."""
+        if self.lm_host is None:
+            return self.lm.index_select(0, idx_cpu.to(self.dev, non_blocking=True))
+        return self.lm_host.index_select(0, idx_cpu).pin_memory().to(self.dev, non_blocking=True)
 
     def _lm_loss_backward(self, hn: torch.Tensor, tokens: torch.Tensor, scale: float) -> torch.Tensor:
         """Mean next-token cross-entropy of the frozen lm_head over hn [T, hidden] (bf16),
-        back-propagated into hn's graph (each chunk's loss scaled by `scale`).  The logits
-        are formed CE_CHUNK tokens at a time, so their fp32 working set stays ~0.3 GB at a
-        152064-entry vocabulary instead of ~1.2 GB.  Returns the (unscaled) loss."""
-        T = hn.shape[0]
+        back-propagated into hn's graph (its gradient scaled by `scale`).  Returns the
+        (unscaled) loss.
+
+        One pass over the lm_head, LM_CHUNK vocabulary rows at a time, with a running
+        (online) softmax per token: the logits of a chunk (the bf16 product of a plain
+        lm_head, in fp32) update the running maximum m, the normaliser Z and
+        U = sum over non-target rows of exp(logit - m) * lm_row, each rescaled by
+        exp(m_old - m_new) as the maximum grows.  At the end lse = m + log Z and
+            d loss / d h_t = (U_t / Z_t + expm1(l_target - lse) * lm_target) / n,
+        the target's softmax-minus-one formed by expm1, so a confident prediction loses
+        nothing to cancellation.  U takes the probabilities as a bf16 hi/lo pair (two bf16
+        products with fp32 output), ~2^-16 relative.  The lm_head is thus read once per
+        step and never needs to be resident: streamed, it comes from pinned host memory
+        (see _lm_chunks)."""
+        T, H = hn.shape
         n = T - 1
-        tgt = tokens[1:].to(self.dev, non_blocking=True)
-        hd = hn.detach().requires_grad_()
-        total = None
-        for c0 in range(0, n, self.CE_CHUNK):
-            c1 = min(n, c0 + self.CE_CHUNK)
-            with torch.enable_grad():
-                logits = torch.matmul(hd[c0:c1], self.lm.t()).float()
-                lc = torch.nn.functional.cross_entropy(logits, tgt[c0:c1], reduction="sum") / n
-                (lc if scale == 1.0 else lc * scale).backward()
-            total = lc.detach() if total is None else total + lc.detach()
-            del logits
-        hn.backward(hd.grad)
-        return total
+        tg_cpu = tokens[1:].cpu()
+        tgt = tg_cpu.to(self.dev, non_blocking=True)
+        h = hn.detach()[:n]
+        m = torch.full((n,), float("-inf"), device=self.dev)
+        Z = torch.zeros(n, device=self.dev)
+        U = torch.zeros(n, H, device=self.dev)
+        lt = torch.zeros(n, device=self.dev)
+        for c0, lm_c in self._lm_chunks():
+            rows = lm_c.shape[0]
+            logits = torch.matmul(h, lm_c.t()).float()
+            rel = tgt - c0
+            hit = (rel >= 0) & (rel < rows)
+            idx = rel.clamp(0, rows - 1)[:, None]
+            lt = torch.where(hit, logits.gather(1, idx)[:, 0], lt)
+            m_new = torch.maximum(m, logits.amax(1))
+            a = torch.exp(m - m_new)
+            p = torch.exp(logits - m_new[:, None])
+            Z = Z * a + p.sum(1)
+            p.scatter_(1, idx, p.gather(1, idx) * (~hit)[:, None].float())  # the target's own term apart
+            p_hi = p.to(torch.bfloat16)
+            p_lo = (p - p_hi.float()).to(torch.bfloat16)
+            U = U * a[:, None] + torch.mm(p_hi, lm_c, out_dtype=torch.float32) + \
+                torch.mm(p_lo, lm_c, out_dtype=torch.float32)
+            m = m_new
+        lse = m + torch.log(Z)
+        loss = (lse - lt).sum() / n
+        dh = (U / Z[:, None] + torch.expm1(lt - lse)[:, None] * self._lm_rows(tg_cpu).float()) * (scale / n)
+        g = torch.zeros_like(hn)
+        g[:n] = dh.to(hn.dtype)
+        hn.backward(g)
+        return loss
 
     def params(self) -> List[torch.nn.Parameter]:
         return [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
@@ -737,9 +839,11 @@ class Stack:
             self.window.close()
             self.window = None
         torch.cuda.synchronize(self.dev)
-        had_host = bool(self.host_blobs)
+        had_host = bool(self.host_blobs) or self.lm_host is not None
         self.host_blobs = []
         self.dev_blobs = []
+        self.lm_host = None
+        self._lm_ring = []
         if had_host:
             torch._C._host_emptyCache()
 
