@@ -310,13 +310,16 @@ class Stack:
     def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
                  window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
                  n_slots: int = 2, glue: str = "native", base: str = "nf4", group: bool = True,
-                 layer_release: bool = True):
+                 layer_release: bool = True, lm_stream: Optional[bool] = None):
         assert mode in ("streamed", "resident")
         assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
         self.glue = glue
         self.group = group
         self.layer_release = layer_release
+        # the frozen lm_head in pinned host memory, streamed by the loss (streamed stacks by
+        # default); False keeps it on the device
+        self.lm_stream = (mode == "streamed") if lm_stream is None else lm_stream
         self.cfg = ops.Lora(r, alpha, p_drop)
         self.window_blocks = window_blocks
         self.n_slots = n_slots
@@ -372,9 +375,10 @@ class Stack:
         """The frozen token embedding stays in host memory (a step gathers only its T rows
         and copies them over).  The frozen lm_head lives on the device in resident mode; in
         streamed mode it stays in pinned host memory and the loss streams it chunk by chunk
-        through a two-chunk device ring, like the base.  The final norm is on the device."""
+        through a two-chunk device ring, like the base (lm_stream).  The final norm is on the
+        device."""
         self.emb = emb.detach().to("cpu", torch.bfloat16).contiguous()
-        if self.mode == "streamed":
+        if self.lm_stream:
             self.lm_host = torch.empty(lm.shape, dtype=torch.bfloat16, pin_memory=True)
             self.lm_host.copy_(lm)
             self.lm = None
@@ -403,8 +407,9 @@ class Stack:
         # is the same either way)
         groups = [{"params": list(self.A[l].values()) + list(self.B[l].values())} for l in range(len(self.A))]
         self.opt = torch.optim.AdamW(groups, lr=LR, betas=BETAS, eps=ADAM_EPS, weight_decay=WD, foreach=True)
-        if self.mode == "streamed":
+        if self.mode == "streamed" or self.lm_stream:
             self.copy_stream = torch.cuda.Stream(device=self.dev)
+        if self.mode == "streamed":
             self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks, self.n_slots,
                                                 copy_stream=self.copy_stream, device=self.dev)
 
