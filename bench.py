@@ -363,6 +363,71 @@ def vendor_gemm(reps: int = 20) -> int:
     return 0
 
 
+def skinny(reps: int = 50) -> int:
+    """The small shapes of the path, whose roofline is HBM bandwidth, not the matrix cores:
+    the single 896 x 896 NF4 + LoRA linear (r 16, alpha 32, dropout 0.0) and the seven
+    projections of a Qwen2.5-0.5B-shaped block (q/o 896x896, k/v 128x896, gate/up 4864x896,
+    down 896x4864, dropout 0.1), all at T = 512, forward and backward through the library
+    entry points.  Per kernel: average launch time (HIP events on its launches), algorithmic
+    bytes per launch (as the library records them) and the GB/s and TFLOP/s they give.
+    Prints one JSON line."""
+    import torch
+
+    from memory_streamed_qlora_amd import ops
+
+    torch.cuda.set_device(0)
+    T = 512
+    g = torch.Generator(device="cuda").manual_seed(0)
+    cases = [("cfg1 896x896", 896, 896, 0.0)] + [
+        (f"0.5B {name}", k, n, 0.1) for name, k, n in
+        (("q/o", 896, 896), ("k/v", 896, 128), ("gate/up", 896, 4864), ("down", 4864, 896))]
+    rows = []
+    for name, K, N, p in cases:
+        cfg = ops.Lora(16, 32.0, p)
+        W = (torch.randn(N, K, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        codes, absmax = ops.nf4_quantize(W)
+        A = (torch.rand(16, K, generator=g, device="cuda") * 2 - 1) / K ** 0.5
+        B = torch.randn(N, 16, generator=g, device="cuda") * 0.01
+        x = torch.randn(T, K, generator=g, device="cuda").to(torch.bfloat16)
+        dy = torch.randn(T, N, generator=g, device="cuda").to(torch.bfloat16)
+        key = ops.rng_key(0, 0, 0, 0, 0)
+
+        def step():
+            y, u = ops.nf4_lora_fwd(x, codes, absmax, None, A, B, cfg, key)
+            ops.nf4_lora_bwd(dy, x, codes, absmax, A, B, cfg, key, u=u)
+
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        for _ in range(reps):
+            step()
+        e_ev.record()
+        torch.cuda.synchronize()
+        call_us = s_ev.elapsed_time(e_ev) / reps * 1e3
+        ops.timing_enable(True)
+        ops.timing_collect()
+        for _ in range(reps):
+            step()
+        torch.cuda.synchronize()
+        kt = by_kernel(ops.timing_collect())
+        ops.timing_enable(False)
+        kern = {}
+        for kname, v in sorted(kt.items()):
+            us = v["total_ms"] / v["launches"] * 1e3
+            kern[kname] = {"launches_per_step": v["launches"] / reps, "avg_us": round(us, 2),
+                           "algorithmic_MB_per_launch": round(v["total_bytes"] / v["launches"] / 1e6, 3),
+                           "GBps": round(v["total_bytes"] / v["total_ms"] / 1e6, 1),
+                           "hbm_frac": round(v["total_bytes"] / v["total_ms"] / 1e6 / PEAK_HBM_GBPS, 4),
+                           **({"tflops": round(v["total_flops"] / v["total_ms"] / 1e9, 1)} if v["total_flops"] else {})}
+        rows.append({"shape": name, "t": T, "k": K, "n": N, "p_drop": p, "fwd_bwd_us": round(call_us, 1),
+                     "kernels": kern})
+        log(f"{name}: fwd+bwd {call_us:.1f} us")
+    print(json.dumps({"skinny": rows, "peak_hbm_GBps": PEAK_HBM_GBPS}))
+    return 0
+
+
 def main() -> int:
     if len(sys.argv) in (3, 5) and sys.argv[1] == "--rocprof-summary":
         return rocprof_summary(sys.argv[2], *[int(a) for a in sys.argv[3:]])
@@ -391,6 +456,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the streamed steps without per-launch events (no roofline figures)")
+    ap.add_argument("--skinny", action="store_true",
+                    help="only time the small (HBM-bound) shapes: the 896x896 linear and the 0.5B block's projections")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only compare the NF4 GEMMs with hipBLASLt's bf16 GEMM at the step's shapes")
     args = ap.parse_args()
@@ -399,6 +466,8 @@ def main() -> int:
         return 2
     if args.vendor_gemm:
         return vendor_gemm()
+    if args.skinny:
+        return skinny()
 
     import torch
 
