@@ -456,6 +456,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the streamed steps without per-launch events (no roofline figures)")
+    ap.add_argument("--lm-resident", action="store_true",
+                    help="keep the frozen lm_head on the device in the streamed step (instead of streaming it)")
     ap.add_argument("--skinny", action="store_true",
                     help="only time the small (HBM-bound) shapes: the 896x896 linear and the 0.5B block's projections")
     ap.add_argument("--vendor-gemm", action="store_true",
@@ -490,7 +492,8 @@ def main() -> int:
         t_build = time.time()
         st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=0.0,
                             window_blocks=args.window_blocks, n_slots=args.slots, mode=mode, glue=args.glue,
-                            base=args.base, layer_release=not args.window_release)
+                            base=args.base, layer_release=not args.window_release,
+                            lm_stream=mode == "streamed" and not args.lm_resident)
         torch.cuda.synchronize()
         log(f"{mode}: built {args.layers} layers in {time.time() - t_build:.1f}s "
             f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
