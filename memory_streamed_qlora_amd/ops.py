@@ -490,6 +490,9 @@ class BlockStreamWindow:
         self._sizes = (ctypes.c_size_t * self.n_layers)(*[b.numel() for b in host_blobs])
         self.arena_bytes_needed = int(lib().block_stream_arena_bytes(self._sizes, self.n_layers,
                                                                      self.window_blocks, self.n_slots))
+        if self.arena_bytes_needed == 0:
+            raise ValueError(f"invalid window: {self.n_layers} layers, {self.window_blocks} per window, "
+                             f"{self.n_slots} slots (at least 2 slots, 1 <= window_blocks <= layers)")
         dev = torch.device(device or "cuda")
         if arena is None:
             arena = torch.empty(self.arena_bytes_needed, dtype=torch.uint8, device=dev)

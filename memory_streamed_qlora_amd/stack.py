@@ -739,22 +739,25 @@ class Stack:
 
         One pass over the lm_head, LM_CHUNK vocabulary rows at a time, with a running
         (online) softmax per token: the logits of a chunk (the bf16 product of a plain
-        lm_head, in fp32) update the running maximum m, the normaliser Z and
-        U = sum over non-target rows of exp(logit - m) * lm_row, each rescaled by
-        exp(m_old - m_new) as the maximum grows.  At the end lse = m + log Z and
-            d loss / d h_t = (U_t / Z_t + expm1(l_target - lse) * lm_target) / n,
-        the target's softmax-minus-one formed by expm1, so a confident prediction loses
-        nothing to cancellation.  U takes the probabilities as a bf16 hi/lo pair (two bf16
-        products with fp32 output), ~2^-16 relative.  The lm_head is thus read once per
-        step and never needs to be resident: streamed, it comes from pinned host memory
-        (see _lm_chunks)."""
+        lm_head, in fp32) update the running maximum m and, rescaled by exp(m_old - m_new)
+        as the maximum grows, the sums over the non-target rows
+            Zo = sum exp(logit - m),   U = sum exp(logit - m) * lm_row,
+        and the target's own term Zt = exp(l_target - m).  With Z = Zo + Zt, the loss of a
+        token is m + log Z - l_target and
+            d loss / d h_t = (U_t - Zo_t * lm_target) / (Z_t * n),
+        i.e. sum_v softmax_v lm_v - lm_target with 1 - softmax_target = Zo / Z taken from the
+        non-target sum itself: a confident prediction loses nothing to cancellation.  U
+        takes the probabilities as a bf16 hi/lo pair (two bf16 products with fp32 output),
+        ~2^-16 relative.  The lm_head is thus read once per step and never needs to be
+        resident: streamed, it comes from pinned host memory (see _lm_chunks)."""
         T, H = hn.shape
         n = T - 1
         tg_cpu = tokens[1:].cpu()
         tgt = tg_cpu.to(self.dev, non_blocking=True)
         h = hn.detach()[:n]
         m = torch.full((n,), float("-inf"), device=self.dev)
-        Z = torch.zeros(n, device=self.dev)
+        Zo = torch.zeros(n, device=self.dev)
+        Zt = torch.zeros(n, device=self.dev)
         U = torch.zeros(n, H, device=self.dev)
         lt = torch.zeros(n, device=self.dev)
         for c0, lm_c in self._lm_chunks():
@@ -767,16 +770,17 @@ class Stack:
             m_new = torch.maximum(m, logits.amax(1))
             a = torch.exp(m - m_new)
             p = torch.exp(logits - m_new[:, None])
-            Z = Z * a + p.sum(1)
+            Zt = torch.where(hit, p.gather(1, idx)[:, 0], Zt * a)
             p.scatter_(1, idx, p.gather(1, idx) * (~hit)[:, None].float())  # the target's own term apart
+            Zo = Zo * a + p.sum(1)
             p_hi = p.to(torch.bfloat16)
             p_lo = (p - p_hi.float()).to(torch.bfloat16)
             U = U * a[:, None] + torch.mm(p_hi, lm_c, out_dtype=torch.float32) + \
                 torch.mm(p_lo, lm_c, out_dtype=torch.float32)
             m = m_new
-        lse = m + torch.log(Z)
-        loss = (lse - lt).sum() / n
-        dh = (U / Z[:, None] + torch.expm1(lt - lse)[:, None] * self._lm_rows(tg_cpu).float()) * (scale / n)
+        Z = Zo + Zt
+        loss = (m + torch.log(Z) - lt).sum() / n
+        dh = (U - Zo[:, None] * self._lm_rows(tg_cpu).float()) / Z[:, None] * (scale / n)
         g = torch.zeros_like(hn)
         g[:n] = dh.to(hn.dtype)
         hn.backward(g)
