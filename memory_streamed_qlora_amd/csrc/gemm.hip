@@ -368,6 +368,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
         load_a(nxt, c);
         if (c == 1) fill(P, qc, 0, b_fill);
         if (c == 2) fill(P, qc, 1, b_fill);
+        if (c < 3) {
+          // one MFMA, then up to four of the sub-step's other VALU instructions (the table
+          // build, the code lookups): both waves of a SIMD leave the barrier together, and a
+          // wave that ran its VALU block first would leave the matrix core idle meanwhile
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
