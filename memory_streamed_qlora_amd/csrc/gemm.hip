@@ -173,11 +173,19 @@ struct WShare<true> {
 template <int MODE, bool DROP, bool BF16W>
 __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[3][BN * LDW];
+  // forward NF4: the codebook, and each thread's quarter of its row's bf16 table planes
+  constexpr bool QUAD_TABLE = MODE == 0 && !BF16W;
+  __shared__ __attribute__((aligned(16))) float sLut[QUAD_TABLE ? 16 : 1];
+  __shared__ __attribute__((aligned(16))) uint2 sPl[QUAD_TABLE ? THREADS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hk = lane >> 5, r32 = lane & 31;
+  if constexpr (QUAD_TABLE) {
+    if (tid < 16) sLut[tid] = ga.lut.v[tid];
+    __syncthreads();
+  }
   int64_t n0, m0;
   int split;
   tile_of(n0, m0, split);
@@ -317,9 +325,30 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
       }
       store8(out, h, buf);
     };
+    // The forward's four threads of a W row (lanes 4r .. 4r+3 of one wave) share the row's
+    // block: each builds the table entries of codes 4q .. 4q+3 (q = tid & 3) and the quad
+    // exchanges them through LDS, in place of each building all 16.  A wave's LDS
+    // operations complete in order, so no barrier.  The backward's threads of one block
+    // sit in different waves and build the whole table.
     auto planes = [&](const WShare<BF16W>& w) {
       Nf4Planes P;
-      if constexpr (!BF16W) P = nf4_planes(ga.lut, w.s);
+      if constexpr (QUAD_TABLE) {
+        const float4 L = *reinterpret_cast<const float4*>(&sLut[4 * (tid & 3)]);
+        const uint32_t pk0 = pack_bf16x2(L.x * w.s, L.y * w.s), pk1 = pack_bf16x2(L.z * w.s, L.w * w.s);
+        sPl[tid] = make_uint2(__builtin_amdgcn_perm(pk1, pk0, 0x06040200u), __builtin_amdgcn_perm(pk1, pk0, 0x07050301u));
+        const uint4 r0 = *reinterpret_cast<const uint4*>(&sPl[tid & ~3]);
+        const uint4 r1 = *reinterpret_cast<const uint4*>(&sPl[(tid & ~3) + 2]);
+        P.lo[0] = r0.x;
+        P.hi[0] = r0.y;
+        P.lo[1] = r0.z;
+        P.hi[1] = r0.w;
+        P.lo[2] = r1.x;
+        P.hi[2] = r1.y;
+        P.lo[3] = r1.z;
+        P.hi[3] = r1.w;
+      } else if constexpr (!BF16W) {
+        P = nf4_planes(ga.lut, w.s);
+      }
       return P;
     };
     auto read_b = [&](bf16x8_t(&b)[4], int c, int buf) {
