@@ -410,8 +410,11 @@ class Stack:
         if self.mode == "streamed" or self.lm_stream:
             self.copy_stream = torch.cuda.Stream(device=self.dev)
         if self.mode == "streamed":
+            # the window alternates layers over two copy streams (the lm_head chunks use
+            # the first): a layer copy that waits for its slot does not hold up the next
             self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks, self.n_slots,
-                                                copy_stream=self.copy_stream, device=self.dev)
+                                                copy_streams=[self.copy_stream, torch.cuda.Stream(device=self.dev)],
+                                                device=self.dev)
 
     @classmethod
     def random(cls, shape: Shape, seq: int, seed: int = 0, cfg_id: int = 0, w_std: float = 0.02,
