@@ -101,6 +101,15 @@ double merge_spans(msq_window* w, size_t keep) {
   return total;
 }
 
+// Records the spans' reference event on the first copy stream; the other copy streams wait
+// for it, so that every later copy starts after it on any stream.
+hipError_t mark_reference(msq_window* w) {
+  hipError_t e = hipEventRecord(w->t_ref, w->copies[0]);
+  for (size_t i = 1; i < w->copies.size() && e == hipSuccess; ++i)
+    if (w->copies[i] != w->copies[0]) e = hipStreamWaitEvent(w->copies[i], w->t_ref, 0);
+  return e;
+}
+
 // Adds the duration and span of timing pair i to the statistics once its copies are done.
 hipError_t collect_timing(msq_window* w, int i) {
   if (!w->t_pending[i]) return hipSuccess;
@@ -203,7 +212,7 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
     if (e == hipSuccess) e = hipEventCreate(&w->t_end[i]);
   }
   if (e == hipSuccess) e = hipEventCreate(&w->t_ref);
-  if (e == hipSuccess) e = hipEventRecord(w->t_ref, w->copies[0]);
+  if (e == hipSuccess) e = mark_reference(w);
   if (e != hipSuccess) {
     if (w->t_ref) (void)hipEventDestroy(w->t_ref);
     for (int j = 0; j < ne; ++j) {
@@ -351,8 +360,8 @@ int block_stream_stats(msq_window* w, msq_window_stats* out) {
   }
   w->stats.busy_ms += merge_spans(w, 0);
   // every copy issued so far is done: later spans are measured from a fresh reference
-  const hipError_t e = hipEventRecord(w->t_ref, w->copies[0]);
-  if (e != hipSuccess) return hip_error(e, "block_stream_stats: hipEventRecord");
+  const hipError_t e = mark_reference(w);
+  if (e != hipSuccess) return hip_error(e, "block_stream_stats: reference event");
   *out = w->stats;
   return MSQ_OK;
 }
