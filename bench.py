@@ -189,23 +189,16 @@ def cpu_baseline(seconds_hint=True) -> dict:
 
 
 def h2d_busy(window, lm, ms_per_step: float, ceiling: float) -> dict:
-    """Time per step in which H2D copies ran (the window's: the union of its layer copies'
-    spans, events around each copy after its wait, which overlap across its two copy
-    streams; plus the lm_head chunk copies', which run while no window copy is pending)
-    and the H2D rate over that time, against the measured ceiling."""
+    """Copy-stream busy time per step (events around each window copy and each lm_head
+    chunk copy, taken after the copy's wait) and the H2D rate while copying, against the
+    measured ceiling."""
     if not window or not window.get("copies_timed"):
         return {}
-    busy = window["busy_ms"] + (lm["ms"] if lm else 0.0)
+    busy = window["copy_ms"] + (lm["ms"] if lm else 0.0)
     nbytes = window["bytes_copied"] + (lm["bytes"] if lm else 0.0)
     rate = nbytes / (busy * 1e-3) / 1e9 if busy > 0 else 0.0
-    out = {"copy_busy_ms_per_step": round(busy, 1), "copy_busy_frac": round(busy / ms_per_step, 3),
-           "GBps_while_copying": round(rate, 1), "frac_while_copying": round(rate / ceiling, 3)}
-    if window["busy_ms"] > 0:
-        out["window_GBps_while_copying"] = round(window["bytes_copied"] / (window["busy_ms"] * 1e-3) / 1e9, 1)
-        out["window_copy_overlap"] = round(window["copy_ms"] / window["busy_ms"], 2)
-    if lm and lm["ms"] > 0:
-        out["lm_head_GBps_while_copying"] = round(lm["bytes"] / (lm["ms"] * 1e-3) / 1e9, 1)
-    return out
+    return {"copy_busy_ms_per_step": round(busy, 1), "copy_busy_frac": round(busy / ms_per_step, 3),
+            "GBps_while_copying": round(rate, 1), "frac_while_copying": round(rate / ceiling, 3)}
 
 
 def rocprof_summary(d: str, timed: int = 5, total: int = 7) -> int:

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 10
+#define MSQ_ABI_VERSION 9
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -362,41 +362,32 @@ int nf4_stream_load(const msq_quant_job* jobs, int n_jobs, int64_t chunk_rows, v
  * window_blocks = 1 and n_slots = 2B the same arena as B-block windows double
  * buffered becomes a ring of single-layer slots, released and refilled layer by
  * layer.  Layer blobs live in pinned host memory (hipHostMalloc or equivalent) and
- * are copied with hipMemcpyAsync, layer l on copy_streams[l % n_copy_streams]: with
- * two or more caller-owned streams a copy that waits for its slot no longer holds up
- * the next layer's, and the copies may run on separate DMA engines.  Each layer's
- * device address is its offset in the slot (blob offsets rounded up to 256 bytes).
- * The window object owns only events and bookkeeping; it is not thread-safe.
+ * are copied with hipMemcpyAsync on copy_stream.  Each layer's device address is
+ * its offset in the slot (blob offsets rounded up to 256 bytes).  The window object
+ * owns only events and bookkeeping; it is not thread-safe.
  *
  *   host_blobs  host array of n_layers pointers to pinned host memory
  *   blob_bytes  host array of n_layers sizes
  *   dev_arena   caller-owned device memory, 256-byte aligned, arena_bytes long;
  *               needs at least block_stream_arena_bytes(...) bytes, else
  *               MSQ_E_WINDOW (the message names the largest window that fits).
- *   copy_streams  host array of n_copy_streams (1 .. MSQ_MAX_COPY_STREAMS) streams of
- *               the arena's device, owned by the caller (entries may repeat; NULL is
- *               the default stream); else MSQ_E_INVAL.
- * The arrays are copied; the blobs, the arena and the streams must outlive the window. */
-#define MSQ_MAX_COPY_STREAMS 4
+ * The arrays are copied; the blobs and the arena must outlive the window. */
 typedef struct msq_window msq_window;
 
 typedef struct {
   uint64_t bytes_copied;    /* host-to-device bytes issued */
   uint64_t windows_copied;  /* window loads that issued copies */
   uint64_t windows_reused;  /* prefetches satisfied by a slot that still held the window */
-  double copy_ms;           /* sum of the layer copies' durations (events around each
-                               copy, after its wait for the slot) */
-  uint64_t copies_timed;    /* layer copies included in copy_ms */
-  double busy_ms;           /* time at least one layer copy was running: the union of the
-                               copies' spans, which overlap when there are several copy
-                               streams (copy_ms counts the overlap twice) */
+  double copy_ms;           /* time the copy stream spent in window copies (events around
+                               each window's copies, after its wait for the slot) */
+  uint64_t copies_timed;    /* window copies included in copy_ms */
 } msq_window_stats;
 
 size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks,
                                 int n_slots);
 int block_stream_create(msq_window** out, const void* const* host_blobs, const size_t* blob_bytes,
                         int n_layers, int window_blocks, int n_slots, void* dev_arena,
-                        size_t arena_bytes, const msq_stream_t* copy_streams, int n_copy_streams);
+                        size_t arena_bytes, msq_stream_t copy_stream);
 /* Start loading the window that begins at first_layer (a multiple of
  * window_blocks) into a free slot (the least recently released one): the copy
  * stream first waits until the compute stream released that slot, then copies,
@@ -418,9 +409,7 @@ int block_stream_release(msq_window* w, int first_layer, msq_stream_t compute);
  * MSQ_E_ORDER. */
 int block_stream_release_layer(msq_window* w, int layer, msq_stream_t compute);
 /* Statistics since creation.  Waits for the issued copies to finish so that their
- * durations are included (call it outside timed regions).  The copies' spans are
- * measured from a reference event that each call re-records; busy_ms loses precision
- * only when calls are hours apart (float milliseconds). */
+ * durations are included (call it outside timed regions). */
 int block_stream_stats(msq_window* w, msq_window_stats* out);
 /* Waits for the window's outstanding copies, then frees its events. */
 int block_stream_destroy(msq_window* w);

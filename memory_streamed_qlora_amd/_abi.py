@@ -41,7 +41,7 @@ class LoraCfg(ctypes.Structure):
 class WindowStats(ctypes.Structure):
     _fields_ = [("bytes_copied", ctypes.c_uint64), ("windows_copied", ctypes.c_uint64),
                 ("windows_reused", ctypes.c_uint64), ("copy_ms", ctypes.c_double),
-                ("copies_timed", ctypes.c_uint64), ("busy_ms", ctypes.c_double)]
+                ("copies_timed", ctypes.c_uint64)]
 
 
 class QuantJob(ctypes.Structure):
@@ -112,7 +112,7 @@ _SIG = {
                                        ctypes.c_int, _P]),
     "block_stream_arena_bytes": (ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "block_stream_create": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
-                                           ctypes.c_size_t, _P, ctypes.c_int]),
+                                           ctypes.c_size_t, _P]),
     "block_stream_prefetch": (ctypes.c_int, [_P, ctypes.c_int]),
     "block_stream_acquire": (ctypes.c_int, [_P, ctypes.c_int, _P, _P]),
     "block_stream_release": (ctypes.c_int, [_P, ctypes.c_int, _P]),
@@ -124,7 +124,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 10  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 9  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

@@ -44,7 +44,7 @@ struct msq_window {
   std::vector<size_t> offset;  // offset of each layer inside its window's slot
   size_t slot_bytes = 0;
   std::vector<char*> slot_base;
-  std::vector<hipStream_t> copies;  // layer l is copied on copies[l % copies.size()]
+  hipStream_t copy = nullptr;
   // per (slot, position) events, index slot * window_blocks + position
   std::vector<hipEvent_t> ready, freed;
   std::vector<char> freed_recorded;
@@ -54,18 +54,14 @@ struct msq_window {
   std::vector<int> state;
   std::vector<uint64_t> release_tick;
   uint64_t tick = 0;
-  msq_window_stats stats = {0, 0, 0, 0.0, 0, 0.0};
+  msq_window_stats stats = {0, 0, 0, 0.0, 0};
   // copy timing: one (start, end) event pair per issued layer copy, from a ring; a pair is
-  // read (its duration added to stats.copy_ms, its span kept for stats.busy_ms) when the
-  // ring comes round to it or when the statistics are asked for.  Spans are measured from
-  // t_ref, an event recorded on the first copy stream at creation and again after each
-  // statistics call (which has waited for every copy), and merged at that call.
+  // read (and its duration added to stats.copy_ms) when the ring comes round to it or when
+  // the statistics are asked for
   static constexpr int TIMING_RING = 64;
   hipEvent_t t_start[TIMING_RING] = {}, t_end[TIMING_RING] = {};
   bool t_pending[TIMING_RING] = {};
   int t_next = 0;
-  hipEvent_t t_ref = nullptr;
-  std::vector<std::pair<double, double>> spans;
 };
 
 namespace {
@@ -82,47 +78,15 @@ size_t max_window_bytes(const size_t* blob_bytes, int n_layers, int wb) {
   return m;
 }
 
-// Length of the union of the kept spans, which are then dropped; with `keep` > 0 the last
-// `keep` merged spans stay (later copies may still overlap them).
-double merge_spans(msq_window* w, size_t keep) {
-  std::vector<std::pair<double, double>>& v = w->spans;
-  std::sort(v.begin(), v.end());
-  std::vector<std::pair<double, double>> m;
-  for (const auto& s : v) {
-    if (!m.empty() && s.first <= m.back().second)
-      m.back().second = std::max(m.back().second, s.second);
-    else
-      m.push_back(s);
-  }
-  const size_t done = m.size() > keep ? m.size() - keep : 0;
-  double total = 0.0;
-  for (size_t i = 0; i < done; ++i) total += m[i].second - m[i].first;
-  v.assign(m.begin() + done, m.end());
-  return total;
-}
-
-// Records the spans' reference event on the first copy stream; the other copy streams wait
-// for it, so that every later copy starts after it on any stream.
-hipError_t mark_reference(msq_window* w) {
-  hipError_t e = hipEventRecord(w->t_ref, w->copies[0]);
-  for (size_t i = 1; i < w->copies.size() && e == hipSuccess; ++i)
-    if (w->copies[i] != w->copies[0]) e = hipStreamWaitEvent(w->copies[i], w->t_ref, 0);
-  return e;
-}
-
-// Adds the duration and span of timing pair i to the statistics once its copies are done.
+// Adds the duration of timing pair i to the statistics once its copies are done.
 hipError_t collect_timing(msq_window* w, int i) {
   if (!w->t_pending[i]) return hipSuccess;
   hipError_t e = hipEventSynchronize(w->t_end[i]);
-  float ms = 0.0f, t0 = 0.0f, t1 = 0.0f;
+  float ms = 0.0f;
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, w->t_start[i], w->t_end[i]);
-  if (e == hipSuccess) e = hipEventElapsedTime(&t0, w->t_ref, w->t_start[i]);
-  if (e == hipSuccess) e = hipEventElapsedTime(&t1, w->t_ref, w->t_end[i]);
   if (e != hipSuccess) return e;
   w->stats.copy_ms += ms;
   w->stats.copies_timed++;
-  w->spans.emplace_back(t0, t1);
-  if (w->spans.size() > 4096) w->stats.busy_ms += merge_spans(w, 64);
   w->t_pending[i] = false;
   return hipSuccess;
 }
@@ -145,13 +109,10 @@ size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int wind
 
 int block_stream_create(msq_window** out, const void* const* host_blobs, const size_t* blob_bytes,
                         int n_layers, int window_blocks, int n_slots, void* dev_arena,
-                        size_t arena_bytes, const msq_stream_t* copy_streams, int n_copy_streams) {
-  if (!out || !host_blobs || !blob_bytes || !dev_arena || !copy_streams)
+                        size_t arena_bytes, msq_stream_t copy_stream) {
+  if (!out || !host_blobs || !blob_bytes || !dev_arena)
     return set_error(MSQ_E_INVAL, "block_stream_create: null pointer");
   *out = nullptr;
-  if (n_copy_streams < 1 || n_copy_streams > MSQ_MAX_COPY_STREAMS)
-    return set_error(MSQ_E_INVAL, "block_stream_create: n_copy_streams=%d outside [1, %d]", n_copy_streams,
-                     MSQ_MAX_COPY_STREAMS);
   if (n_layers <= 0 || window_blocks <= 0 || window_blocks > n_layers || n_slots < 2 || n_slots > 1024)
     return set_error(MSQ_E_INVAL, "block_stream_create: n_layers=%d window_blocks=%d n_slots=%d", n_layers,
                      window_blocks, n_slots);
@@ -201,7 +162,7 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
   w->slot_window.assign(n_slots, -1);
   w->state.assign(n_slots, SLOT_FREE);
   w->release_tick.assign(n_slots, 0);
-  for (int i = 0; i < n_copy_streams; ++i) w->copies.push_back((hipStream_t)copy_streams[i]);
+  w->copy = (hipStream_t)copy_stream;
   hipError_t e = hipSuccess;
   for (int i = 0; i < ne && e == hipSuccess; ++i) {
     e = hipEventCreateWithFlags(&w->ready[i], hipEventDisableTiming);
@@ -211,10 +172,7 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
     e = hipEventCreate(&w->t_start[i]);
     if (e == hipSuccess) e = hipEventCreate(&w->t_end[i]);
   }
-  if (e == hipSuccess) e = hipEventCreate(&w->t_ref);
-  if (e == hipSuccess) e = mark_reference(w);
   if (e != hipSuccess) {
-    if (w->t_ref) (void)hipEventDestroy(w->t_ref);
     for (int j = 0; j < ne; ++j) {
       if (w->ready[j]) (void)hipEventDestroy(w->ready[j]);
       if (w->freed[j]) (void)hipEventDestroy(w->freed[j]);
@@ -265,17 +223,16 @@ int block_stream_prefetch(msq_window* w, int first_layer) {
     if (q >= count || e != hipSuccess) continue;
     const int l = first_layer + q;
     const int ev = slot * wb + q;
-    hipStream_t cs = w->copies[l % w->copies.size()];
-    if (w->freed_recorded[ev]) e = hipStreamWaitEvent(cs, w->freed[ev], 0);
+    if (w->freed_recorded[ev]) e = hipStreamWaitEvent(w->copy, w->freed[ev], 0);
     const int ti = w->t_next;
     w->t_next = (w->t_next + 1) % msq_window::TIMING_RING;
     if (e == hipSuccess) e = collect_timing(w, ti);  // the ring's oldest pair, long complete
-    if (e == hipSuccess) e = hipEventRecord(w->t_start[ti], cs);
+    if (e == hipSuccess) e = hipEventRecord(w->t_start[ti], w->copy);
     if (e == hipSuccess)
-      e = hipMemcpyAsync(w->slot_base[slot] + w->offset[l], w->host[l], w->bytes[l], hipMemcpyHostToDevice, cs);
-    if (e == hipSuccess) e = hipEventRecord(w->t_end[ti], cs);
+      e = hipMemcpyAsync(w->slot_base[slot] + w->offset[l], w->host[l], w->bytes[l], hipMemcpyHostToDevice, w->copy);
+    if (e == hipSuccess) e = hipEventRecord(w->t_end[ti], w->copy);
     if (e == hipSuccess) w->t_pending[ti] = true;
-    if (e == hipSuccess) e = hipEventRecord(w->ready[ev], cs);
+    if (e == hipSuccess) e = hipEventRecord(w->ready[ev], w->copy);
     total += w->bytes[l];
   }
   if (e != hipSuccess) return hip_error(e, "block_stream_prefetch: copy");
@@ -358,10 +315,6 @@ int block_stream_stats(msq_window* w, msq_window_stats* out) {
     const hipError_t e = collect_timing(w, i);
     if (e != hipSuccess) return hip_error(e, "block_stream_stats: copy timing");
   }
-  w->stats.busy_ms += merge_spans(w, 0);
-  // every copy issued so far is done: later spans are measured from a fresh reference
-  const hipError_t e = mark_reference(w);
-  if (e != hipSuccess) return hip_error(e, "block_stream_stats: reference event");
   *out = w->stats;
   return MSQ_OK;
 }
@@ -381,7 +334,6 @@ int block_stream_destroy(msq_window* w) {
     if (w->t_start[i]) (void)hipEventDestroy(w->t_start[i]);
     if (w->t_end[i]) (void)hipEventDestroy(w->t_end[i]);
   }
-  if (w->t_ref) (void)hipEventDestroy(w->t_ref);
   delete w;
   return e == hipSuccess ? MSQ_OK : hip_error(e, "block_stream_destroy");
 }

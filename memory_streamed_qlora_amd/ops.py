@@ -474,13 +474,11 @@ def nf4_stream_load(jobs: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tenso
     return {"device_bytes": dev_need, "host_bytes": host_need, "chunk_rows": chunk_rows}
 
 class BlockStreamWindow:
-    """block_stream_* over pinned host blobs and a caller-owned device arena.  Layer l is
-    copied on copy_streams[l % len(copy_streams)] (by default two new streams of the
-    arena's device); copy_stream is the first of them."""
+    """block_stream_* over pinned host blobs and a caller-owned device arena."""
 
     def __init__(self, host_blobs: Sequence[torch.Tensor], window_blocks: int, n_slots: int = 2,
-                 arena: Optional[torch.Tensor] = None,
-                 copy_streams: Optional[Sequence[torch.cuda.Stream]] = None, device=None):
+                 arena: Optional[torch.Tensor] = None, copy_stream: Optional[torch.cuda.Stream] = None,
+                 device=None):
         self.n_layers = len(host_blobs)
         self.window_blocks = int(window_blocks)
         self.n_slots = int(n_slots)
@@ -501,15 +499,11 @@ class BlockStreamWindow:
         if arena.device.type != "cuda" or arena.dtype != torch.uint8:
             raise ValueError("arena must be a device uint8 tensor")
         self.arena = arena
-        if copy_streams is None:
-            copy_streams = [torch.cuda.Stream(device=arena.device) for _ in range(2)]
-        self.copy_streams = list(copy_streams)
-        self.copy_stream = self.copy_streams[0]
-        streams = (ctypes.c_void_p * len(self.copy_streams))(*[s.cuda_stream for s in self.copy_streams])
+        self.copy_stream = copy_stream or torch.cuda.Stream(device=arena.device)
         h = ctypes.c_void_p()
         check("block_stream_create", lib().block_stream_create(
             ctypes.byref(h), self._ptrs, self._sizes, self.n_layers, self.window_blocks, self.n_slots,
-            arena.data_ptr(), arena.numel(), streams, len(self.copy_streams)))
+            arena.data_ptr(), arena.numel(), self.copy_stream.cuda_stream))
         self._h = h
 
     def prefetch(self, first_layer: int) -> None:
@@ -537,8 +531,7 @@ class BlockStreamWindow:
         s = _abi.WindowStats()
         check("block_stream_stats", lib().block_stream_stats(self._h, ctypes.byref(s)))
         return {"bytes_copied": s.bytes_copied, "windows_copied": s.windows_copied,
-                "windows_reused": s.windows_reused, "copy_ms": s.copy_ms, "copies_timed": s.copies_timed,
-                "busy_ms": s.busy_ms}
+                "windows_reused": s.windows_reused, "copy_ms": s.copy_ms, "copies_timed": s.copies_timed}
 
     def close(self) -> None:
         if getattr(self, "_h", None):

@@ -304,23 +304,6 @@ class StepResult:
     window_stats: Optional[dict] = None
 
 
-_COPY_STREAMS: Dict[torch.device, List[torch.cuda.Stream]] = {}
-
-
-def copy_streams(dev: torch.device) -> List[torch.cuda.Stream]:
-    """The device's two copy streams, shared by every stack of the process.  HIP binds a
-    stream to one of a few hardware queues (4 by default) on its first use and keeps it;
-    streams made afresh by each new stack would, once earlier stacks' streams hold the other
-    queues, share the compute stream's queue, where a copy waiting for its slot holds up the
-    compute behind it (a 32B stack built after a 7B one ran 12% slower that way)."""
-    dev = torch.device(dev)
-    if dev.index is None:
-        dev = torch.device(dev.type, torch.cuda.current_device())
-    if dev not in _COPY_STREAMS:
-        _COPY_STREAMS[dev] = [torch.cuda.Stream(device=dev) for _ in range(2)]
-    return _COPY_STREAMS[dev]
-
-
 class Stack:
     """A Qwen2.5-shaped NF4 + LoRA stack with streamed or resident frozen base."""
 
@@ -425,14 +408,10 @@ class Stack:
         groups = [{"params": list(self.A[l].values()) + list(self.B[l].values())} for l in range(len(self.A))]
         self.opt = torch.optim.AdamW(groups, lr=LR, betas=BETAS, eps=ADAM_EPS, weight_decay=WD, foreach=True)
         if self.mode == "streamed" or self.lm_stream:
-            # two copy streams: the window alternates layers over them, so a layer copy that
-            # waits for its slot does not hold up the next one; the lm_head chunks use the
-            # first (spreading them too did not change the step)
-            self.copy_streams = copy_streams(self.dev)
-            self.copy_stream = self.copy_streams[0]
+            self.copy_stream = torch.cuda.Stream(device=self.dev)
         if self.mode == "streamed":
             self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks, self.n_slots,
-                                                copy_streams=self.copy_streams, device=self.dev)
+                                                copy_stream=self.copy_stream, device=self.dev)
 
     @classmethod
     def random(cls, shape: Shape, seq: int, seed: int = 0, cfg_id: int = 0, w_std: float = 0.02,
@@ -713,17 +692,16 @@ class Stack:
         def issue(i: int) -> None:
             b, c0 = i % 2, starts[i]
             rows = min(self.LM_CHUNK, V - c0)
-            cs = self.copy_stream
-            with torch.cuda.stream(cs):
+            with torch.cuda.stream(self.copy_stream):
                 if self._lm_read[b] is not None:
-                    cs.wait_event(self._lm_read[b])
+                    self.copy_stream.wait_event(self._lm_read[b])
                 t0 = None
                 if self.lm_copy_timing:
                     t0 = torch.cuda.Event(enable_timing=True)
-                    t0.record(cs)
+                    t0.record(self.copy_stream)
                 self._lm_ring[b][:rows].copy_(self.lm_host[c0:c0 + rows], non_blocking=True)
                 ev = torch.cuda.Event(enable_timing=self.lm_copy_timing)
-                ev.record(cs)
+                ev.record(self.copy_stream)
                 if t0 is not None:
                     self._lm_copy_log.append((t0, ev, self._lm_ring[b][:rows].nbytes))
             copied[i] = ev
@@ -741,18 +719,10 @@ class Stack:
                 issue(i + 2)
 
     def lm_copy_stats(self) -> Dict[str, float]:
-        """Bytes, copies and milliseconds of the lm_head chunk copies timed since the last
-        call (lm_copy_timing on; call after the device has synchronised): "ms" is the time
-        at least one chunk copy ran (the union of their spans, which overlap across the
-        two copy streams)."""
-        log = self._lm_copy_log
-        spans = sorted((log[0][0].elapsed_time(a), log[0][0].elapsed_time(b)) for a, b, _ in log) if log else []
-        ms, end = 0.0, float("-inf")
-        for a, b in spans:
-            if b > end:
-                ms += b - max(a, end)
-                end = b
-        out = {"bytes": float(sum(n for _, _, n in log)), "copies": len(log), "ms": ms}
+        """Bytes, copies and copy-stream milliseconds of the lm_head chunk copies timed since
+        the last call (lm_copy_timing on; call after the device has synchronised)."""
+        ms = sum(a.elapsed_time(b) for a, b, _ in self._lm_copy_log)
+        out = {"bytes": float(sum(n for _, _, n in self._lm_copy_log)), "copies": len(self._lm_copy_log), "ms": ms}
         self._lm_copy_log = []
         return out
 

@@ -249,20 +249,14 @@ def test_window_rejects_small_arena_and_names_what_fits():
     assert L.block_stream_arena_bytes(sizes, n, 2, 3) == 3 * 2 * 1000 * 256
     assert L.block_stream_arena_bytes(sizes, n, 4, 1) == 0
     h = ctypes.c_void_p()
-    cs = (ctypes.c_void_p * 2)(None, None)  # default streams: nothing here reaches a HIP call
-    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need - 1, cs, 2)
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need - 1, None)
     assert rc == abi.MSQ_E_WINDOW
     assert "window_blocks=3" in _err()
-    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, 1000, cs, 1)
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, 1000, None)
     assert rc == abi.MSQ_E_WINDOW and "not even one layer" in _err()
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 9, 2, FAKE, need, cs, 2) == abi.MSQ_E_INVAL
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 1, FAKE, need, cs, 2) == abi.MSQ_E_INVAL
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE + 16, need, cs, 2) == abi.MSQ_E_INVAL
-    # the copy streams: an array of 1 .. MSQ_MAX_COPY_STREAMS
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need, None, 1) == abi.MSQ_E_INVAL
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need, cs, 0) == abi.MSQ_E_INVAL
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need, cs, 5) == abi.MSQ_E_INVAL
-    assert "n_copy_streams=5" in _err()
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 9, 2, FAKE, need, None) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 1, FAKE, need, None) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE + 16, need, None) == abi.MSQ_E_INVAL
     assert L.block_stream_prefetch(None, 0) == abi.MSQ_E_INVAL
 
 
