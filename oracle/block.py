@@ -152,8 +152,9 @@ def _key(rk: lora.RngKey, layer: int, proj: str) -> lora.RngKey:
                        proj=PROJ_ID[proj])
 
 
-def forward(x, qp, shape, layer: int, alpha: float, p: float, rk: lora.RngKey):
-    """x: [T, hidden] (float values) -> (out float64 [T, hidden], cache)."""
+def forward(x, qp, shape, layer: int, alpha: float, p: float, rk: lora.RngKey, operand: str = "exact"):
+    """x: [T, hidden] (float values) -> (out float64 [T, hidden], cache).  operand: how the
+    activations enter the frozen-base products (lora.base_operand)."""
     H, KV, D = shape.heads, shape.kv_heads, shape.head_dim
     T = x.shape[0]
     x = x.astype(np.float64)
@@ -164,7 +165,7 @@ def forward(x, qp, shape, layer: int, alpha: float, p: float, rk: lora.RngKey):
     def lin(inp, proj):
         pp = qp[proj]
         y, _ = lora.fwd_dense(inp, base_weight(pp), pp["bias"], pp["A"], pp["B"], alpha, p,
-                              _key(rk, layer, proj))
+                              _key(rk, layer, proj), operand)
         return y
 
     q = lin(xn, "q").reshape(T, H, D)
@@ -189,8 +190,10 @@ def forward(x, qp, shape, layer: int, alpha: float, p: float, rk: lora.RngKey):
     return out, c
 
 
-def backward(dout, c, qp, shape, layer: int, alpha: float, p: float, rk: lora.RngKey):
-    """Returns (dx float64 [T, hidden], grads {proj: (dA, dB)})."""
+def backward(dout, c, qp, shape, layer: int, alpha: float, p: float, rk: lora.RngKey,
+             operand: str = "exact"):
+    """Returns (dx float64 [T, hidden], grads {proj: (dA, dB)}).  operand: how the incoming
+    gradients enter the frozen-base products (lora.base_operand)."""
     H, KV, D = shape.heads, shape.kv_heads, shape.head_dim
     T = dout.shape[0]
     dout = dout.astype(np.float64)
@@ -199,7 +202,7 @@ def backward(dout, c, qp, shape, layer: int, alpha: float, p: float, rk: lora.Rn
     def lin_bwd(dy, inp, proj):
         pp = qp[proj]
         dx, dA, dB = lora.bwd_dense(dy, inp, base_weight(pp), pp["A"], pp["B"], alpha, p,
-                                    _key(rk, layer, proj))
+                                    _key(rk, layer, proj), operand)
         grads[proj] = (dA, dB)
         return dx
 

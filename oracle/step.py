@@ -51,14 +51,16 @@ def loss_and_dlogits(logits: np.ndarray, tokens: np.ndarray):
 
 def forward_backward(layers: List[Dict[str, object]], glob: Dict[str, np.ndarray],
                      toks: np.ndarray, shape, alpha: float, p: float, seed: int, step: int,
-                     micro: int = 0):
-    """Returns (loss, grads[layer][proj] = (dA, dB)).  layers hold quantized params."""
+                     micro: int = 0, operand: str = "exact"):
+    """Returns (loss, grads[layer][proj] = (dA, dB)).  layers hold quantized params.
+    operand: how activations and gradients enter the frozen-base products
+    (lora.base_operand); "bf16" is the stack with fp32 activations on bf16 matrix cores."""
     rk = lora.RngKey(seed=seed, step=step, micro=micro)
     h = glob["emb"][toks].astype(np.float64)
     bounds = []
     for li, qp in enumerate(layers):
         bounds.append(h)
-        h, _ = block.forward(h, qp, shape, li, alpha, p, rk)
+        h, _ = block.forward(h, qp, shape, li, alpha, p, rk, operand)
     hn, rinv = block.rmsnorm(h, glob["lnf"].astype(np.float64))
     logits = hn @ glob["lm"].astype(np.float64).T
     loss, dlog = loss_and_dlogits(logits, toks)
@@ -67,13 +69,13 @@ def forward_backward(layers: List[Dict[str, object]], glob: Dict[str, np.ndarray
     grads: List[Dict[str, tuple]] = [None] * len(layers)
     for li in reversed(range(len(layers))):
         qp = layers[li]
-        _, cache = block.forward(bounds[li], qp, shape, li, alpha, p, rk)  # recompute
-        dh, grads[li] = block.backward(dh, cache, qp, shape, li, alpha, p, rk)
+        _, cache = block.forward(bounds[li], qp, shape, li, alpha, p, rk, operand)  # recompute
+        dh, grads[li] = block.backward(dh, cache, qp, shape, li, alpha, p, rk, operand)
     return loss, grads
 
 
 def accumulated(layers: List[Dict[str, object]], glob: Dict[str, np.ndarray], toks_list,
-                shape, alpha: float, p: float, seed: int, step: int):
+                shape, alpha: float, p: float, seed: int, step: int, operand: str = "exact"):
     """Gradient accumulation over M micro-batches ("Poros" research post and "Current
     limitations", "What 0.00e+00 means": accumulation at 2 and 4 micro-batches is part of
     the parity surface).  Reading: one optimizer step sees the mean of the micro-batch
@@ -83,7 +85,7 @@ def accumulated(layers: List[Dict[str, object]], glob: Dict[str, np.ndarray], to
     M = len(toks_list)
     total, acc = 0.0, None
     for m, toks in enumerate(toks_list):
-        loss, g = forward_backward(layers, glob, toks, shape, alpha, p, seed, step, micro=m)
+        loss, g = forward_backward(layers, glob, toks, shape, alpha, p, seed, step, micro=m, operand=operand)
         total += loss
         if acc is None:
             acc = [{proj: (dA.astype(np.float64), dB.astype(np.float64)) for proj, (dA, dB) in gl.items()}
