@@ -16,7 +16,9 @@
  *     compute call is asynchronous on the stream it is given and never
  *     synchronises the host.
  *   - The caller owns all device memory (inputs, outputs, workspaces, the
- *     window arena); the library allocates no device memory.
+ *     window arena); the library allocates no device memory.  The one exception
+ *     is nf4_lora_fwd_noalloc's scratch, a static array of the library's device
+ *     code, which the runtime provides when the code is loaded on a GPU.
  *   - Every function returns 0 on success or a negative MSQ_E_* code.  All
  *     arguments are validated on the host before any HIP call, so an invalid
  *     call launches nothing and leaves outputs untouched.  msq_last_error()
@@ -37,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 9
+#define MSQ_ABI_VERSION 10
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -177,6 +179,26 @@ int nf4_lora_bwd(const void* dy, const void* x, int64_t t, int64_t k, int64_t n,
                  msq_lora_cfg cfg, msq_rng_key key, const float* u, void* dx,
                  int dx_accumulate, float* dA, float* dB, int dAB_accumulate, void* workspace,
                  size_t workspace_bytes, msq_stream_t stream);
+
+/* nf4_lora_fwd for callers that cannot allocate device memory at the call: code under
+ * HIP stream capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments,
+ * outputs, dropout keys and results are nf4_lora_fwd's (the same kernels), except that
+ * there is no workspace argument: the scratch lives in a static device array of the
+ * library, MSQ_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held from the first call on that
+ * GPU until the process ends.  The call allocates and frees nothing.
+ *   - A shape whose nf4_lora_workspace_size() exceeds MSQ_NOALLOC_SCRATCH_BYTES returns
+ *     MSQ_E_WORKSPACE before any HIP call (at 512 tokens, r = 16, every projection of the
+ *     Qwen2.5 0.5B .. 72B shapes fits: the largest needs 96.6 MiB).
+ *   - The array is found on the stream's device (the current device for the NULL stream);
+ *     its address is looked up once per device.
+ *   - Every call on one GPU shares that GPU's array and nothing in it has to start at zero.
+ *     Calls that may run at the same time on one GPU (different streams, or threads) race
+ *     on it and give undefined results: serialise them on one stream. */
+#define MSQ_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int nf4_lora_fwd_noalloc(const void* x, int64_t t, int64_t k, int64_t n, const uint8_t* codes,
+                         const float* absmax, const uint16_t* bias, const void* residual, const float* A,
+                         const float* B, msq_lora_cfg cfg, msq_rng_key key, void* y, float* u_out,
+                         msq_stream_t stream);
 
 /* The same layer over a frozen base kept in bf16 instead of NF4: the pages' bf16
  * streaming variant, which streams the base blockwise like NF4 at 4x the bytes and is

@@ -87,6 +87,8 @@ _SIG = {
     "nf4_lora_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, ctypes.c_int32]),
     "nf4_lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, LoraCfg, RngKey,
                                     _P, _P, _P, ctypes.c_size_t, _P]),
+    "nf4_lora_fwd_noalloc": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, LoraCfg, RngKey,
+                                            _P, _P, _P]),
     "nf4_lora_bwd": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, LoraCfg, RngKey, _P,
                                     _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
                                     _P]),
@@ -124,7 +126,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 9  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 10  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

@@ -151,7 +151,8 @@ def _base_args(base: Tuple[torch.Tensor, ...], k: int) -> Tuple[str, int, list]:
     return "bf16", n, [_ptr(w)]
 
 
-def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype, u_only, residual):
+def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype, u_only, residual,
+              noalloc=False):
     t, k = x.shape
     _req(x, "x", x.dtype, (t, k))
     fmt, n, bptr = _base_args(base, k)
@@ -181,6 +182,11 @@ def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream
         u_out = torch.empty((t, r), dtype=torch.float32, device=x.device)
     if u_out is not None:
         _req(u_out, "u_out", torch.float32, (t, r))
+    args = (_ptr(x), t, k, n, *bptr, _ptr(bias), _ptr(residual), _ptr(A) if r > 0 else None,
+            _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(y), _ptr(u_out))
+    if noalloc:  # the library's static scratch, no workspace
+        check("nf4_lora_fwd_noalloc", lib().nf4_lora_fwd_noalloc(*args, _stream(stream)))
+        return y, u_out
     need = nf4_lora_workspace_size(t, k, n, r)
     ws = _workspace(x.device, need, workspace)
     fn = f"{fmt}_lora_fwd"
@@ -332,6 +338,19 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
     u_only: compute only u (y is None)."""
     return _lora_fwd((codes, absmax), x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype,
                      u_only, residual)
+
+
+def nf4_lora_fwd_noalloc(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
+                         bias: Optional[torch.Tensor], A: Optional[torch.Tensor], B: Optional[torch.Tensor],
+                         cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
+                         u_out: Optional[torch.Tensor] = None, want_u: bool = True, stream=None,
+                         out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
+                         residual: Optional[torch.Tensor] = None):
+    """nf4_lora_fwd with the library's static per-GPU scratch in place of a workspace (the
+    entry point for callers that cannot allocate).  Pass y (and u_out) to allocate nothing
+    here either."""
+    return _lora_fwd((codes, absmax), x, bias, A, B, cfg, key, y, u_out, want_u, None, stream, out_dtype,
+                     u_only, residual, noalloc=True)
 
 
 def bf16_lora_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], A: Optional[torch.Tensor],
