@@ -643,7 +643,7 @@ class Stack:
             hf = hs[m].detach().requires_grad_()
             with torch.enable_grad():
                 norm = rmsnorm_native if self.glue == "native" else rmsnorm
-                hn = norm(hf, self.lnf).to(torch.bfloat16)
+                hn = norm(hf, self.lnf)
             loss = self._lm_loss_backward(hn, toks[m], scale)
             dhs.append(hf.grad)
             losses.append(loss)
@@ -733,13 +733,14 @@ class Stack:
         return self.lm_host.index_select(0, idx_cpu).pin_memory().to(self.dev, non_blocking=True)
 
     def _lm_loss_backward(self, hn: torch.Tensor, tokens: torch.Tensor, scale: float) -> torch.Tensor:
-        """Mean next-token cross-entropy of the frozen lm_head over hn [T, hidden] (bf16),
-        back-propagated into hn's graph (its gradient scaled by `scale`).  Returns the
-        (unscaled) loss.
+        """Mean next-token cross-entropy of the frozen lm_head over hn [T, hidden] (fp32),
+        back-propagated into hn's graph (its gradient scaled by `scale`, in fp32).  Returns
+        the (unscaled) loss.
 
         One pass over the lm_head, LM_CHUNK vocabulary rows at a time, with a running
-        (online) softmax per token: the logits of a chunk (the bf16 product of a plain
-        lm_head, in fp32) update the running maximum m and, rescaled by exp(m_old - m_new)
+        (online) softmax per token: the logits of a chunk (fp32: hn enters the bf16 product
+        with the bf16 lm_head as a hi/lo pair of bf16 values, two products with fp32 output,
+        ~2^-16 relative) update the running maximum m and, rescaled by exp(m_old - m_new)
         as the maximum grows, the sums over the non-target rows
             Zo = sum exp(logit - m),   U = sum exp(logit - m) * lm_row,
         and the target's own term Zt = exp(l_target - m).  With Z = Zo + Zt, the loss of a
@@ -755,6 +756,8 @@ class Stack:
         tg_cpu = tokens[1:].cpu()
         tgt = tg_cpu.to(self.dev, non_blocking=True)
         h = hn.detach()[:n]
+        h_hi = h.to(torch.bfloat16)
+        h_lo = (h - h_hi.float()).to(torch.bfloat16)
         m = torch.full((n,), float("-inf"), device=self.dev)
         Zo = torch.zeros(n, device=self.dev)
         Zt = torch.zeros(n, device=self.dev)
@@ -762,7 +765,8 @@ class Stack:
         lt = torch.zeros(n, device=self.dev)
         for c0, lm_c in self._lm_chunks():
             rows = lm_c.shape[0]
-            logits = torch.matmul(h, lm_c.t()).float()
+            lm_t = lm_c.t()
+            logits = torch.mm(h_hi, lm_t, out_dtype=torch.float32) + torch.mm(h_lo, lm_t, out_dtype=torch.float32)
             rel = tgt - c0
             hit = (rel >= 0) & (rel < rows)
             idx = rel.clamp(0, rows - 1)[:, None]
@@ -782,7 +786,7 @@ class Stack:
         loss = (m + torch.log(Z) - lt).sum() / n
         dh = (U - Zo[:, None] * self._lm_rows(tg_cpu).float()) / Z[:, None] * (scale / n)
         g = torch.zeros_like(hn)
-        g[:n] = dh.to(hn.dtype)
+        g[:n] = dh
         hn.backward(g)
         return loss
 

@@ -2,10 +2,8 @@
 lm_head and its gradient into the final hidden state, computed in one chunked pass over the
 lm_head with a running softmax.
 
-Checked against the plain definition in float64, applied to the same bf16 logits (formed
-here by the same per-chunk bf16 products the loss issues: at logits in the hundreds one
-bf16 step is 2.0, so any other rounding of the product would change exp terms by e^2), at
-a vocabulary that is not a whole number of chunks:
+Checked against the plain definition in float64 (exact logits of the fp32 hidden state and
+the bf16 lm_head), at a vocabulary that is not a whole number of chunks:
   * loss within 1e-4 relative, gradient within the parity bar (2e-2 RMS);
   * rows whose target holds almost all the probability (1 - softmax of the target between
     1e-30 and 1e-6), where the gradient is the small remainder sum_v p_v lm_v - lm_target:
@@ -36,20 +34,16 @@ def _lm(st):
     return (st.lm_host if st.lm_host is not None else st.lm.cpu()).float().numpy().astype(np.float64)
 
 
-def _logits(hn_bf16, st):
-    """The bf16 logits of the first T-1 rows, chunk by chunk as the loss forms them."""
-    lm = st.lm if st.lm is not None else st.lm_host.cuda()
-    h = hn_bf16[:-1]
-    parts = [torch.matmul(h, lm[c0:c0 + S.Stack.LM_CHUNK].t()).float() for c0 in range(0, VOCAB, S.Stack.LM_CHUNK)]
-    torch.cuda.synchronize()
-    return torch.cat(parts, 1).cpu().numpy().astype(np.float64)
+def _logits(hn, lm64):
+    """float64 logits of the first T-1 rows (fp32 hidden state, bf16 lm_head: exact products)."""
+    return hn[:-1].cpu().numpy().astype(np.float64) @ lm64.T
 
 
-def _reference(hn_bf16, st, lm64, tokens):
+def _reference(hn, lm64, tokens):
     """float64 loss and d loss / d hn of the mean next-token cross-entropy over T-1 tokens."""
-    h = hn_bf16.float().cpu().numpy().astype(np.float64)
+    h = hn.cpu().numpy().astype(np.float64)
     n = h.shape[0] - 1
-    logits = _logits(hn_bf16, st)
+    logits = _logits(hn, lm64)
     tgt = tokens[1:].cpu().numpy()
     rows = np.arange(n)
     mx = logits.max(1, keepdims=True)
@@ -73,17 +67,18 @@ def _run(st, hn0, tokens, scale=1.0):
     hn = hn0.clone().requires_grad_()
     loss = st._lm_loss_backward(hn, tokens, scale)
     torch.cuda.synchronize()
-    return loss.item(), hn.grad.float().cpu().numpy().astype(np.float64), hn.grad.clone()
+    assert hn.grad.dtype == torch.float32
+    return loss.item(), hn.grad.cpu().numpy().astype(np.float64), hn.grad.clone()
 
 
 def test_loss_and_gradient_against_the_definition():
     st = _stack("streamed")
     lm64 = _lm(st)
     g = torch.Generator(device="cpu").manual_seed(1)
-    hn = (torch.randn(T, SHAPE.hidden, generator=g) * 2).to(torch.bfloat16).cuda()
+    hn = (torch.randn(T, SHAPE.hidden, generator=g) * 2).cuda()
     tokens = torch.randint(0, VOCAB, (T,), generator=g)
     loss, dh, _ = _run(st, hn, tokens)
-    rloss, rdh, _ = _reference(hn, st, lm64, tokens)
+    rloss, rdh, _ = _reference(hn, lm64, tokens)
     print(f"[loss] {loss:.6f} vs {rloss:.6f}", flush=True)
     assert abs(loss - rloss) <= 1e-4 * abs(rloss)
     assert_parity(dh, rdh, name="d hn")
@@ -102,14 +97,14 @@ def test_confident_rows():
     g = torch.Generator(device="cpu").manual_seed(2)
     h = torch.randn(T, SHAPE.hidden, generator=g)
     h = h / h.norm(dim=1, keepdim=True) * 5e3  # logits with a standard deviation ~100
-    hn = h.to(torch.bfloat16).cuda()
+    hn = h.cuda()
     n = T - 1
-    logits = _logits(hn, st)
+    logits = _logits(hn, lm64)
     tokens = torch.randint(0, VOCAB, (T,), generator=g)
     conf = np.arange(n) % 2 == 0
     tokens[1:][torch.from_numpy(conf)] = torch.from_numpy(logits.argmax(1)[conf])
     loss, dh, _ = _run(st, hn, tokens)
-    rloss, rdh, rest = _reference(hn, st, lm64, tokens)
+    rloss, rdh, rest = _reference(hn, lm64, tokens)
     assert abs(loss - rloss) <= 1e-4 * abs(rloss) + 1e-6
     sharp = conf & (rest < 1e-6) & (rest > 1e-30)
     print(f"[loss] confident rows with 1e-30 < 1 - p_target < 1e-6: {int(sharp.sum())}", flush=True)
@@ -123,7 +118,7 @@ def test_confident_rows():
 
 def test_streamed_lm_head_equals_resident_bitwise():
     g = torch.Generator(device="cpu").manual_seed(3)
-    hn = (torch.randn(T, SHAPE.hidden, generator=g) * 2).to(torch.bfloat16).cuda()
+    hn = (torch.randn(T, SHAPE.hidden, generator=g) * 2).cuda()
     tokens = torch.randint(0, VOCAB, (T,), generator=g)
     outs = []
     for mode in ("resident", "streamed"):
