@@ -168,3 +168,15 @@ def tokens(seed: int, cfg_id: int, step: int, T: int, vocab: int) -> np.ndarray:
 def seed_int(seed: int, cfg_id: int, layer: int, tensor_id: int) -> int:
     """A 63-bit integer seed for device-side generators, derived from the same tuple."""
     return int(rng_for(seed, cfg_id, layer, tensor_id).integers(0, 2**63 - 1))
+
+
+def device_normal_bf16(seed: int, cfg_id: int, layer: int, tensor_id: int, shape, std: float, device):
+    """A large bf16 ~N(0, std) tensor drawn on the device by a torch generator seeded from
+    the same tuple (for matrices too large to draw on the host quickly, such as the 72B
+    projections).  The values are plain torch draws rounded to bf16; a test copies back the
+    rows or columns it needs."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_int(seed, cfg_id, layer, tensor_id))
+    return (torch.randn(*shape, generator=g, device=device) * std).to(torch.bfloat16)

@@ -51,26 +51,36 @@ def loss_and_dlogits(logits: np.ndarray, tokens: np.ndarray):
 
 def forward_backward(layers: List[Dict[str, object]], glob: Dict[str, np.ndarray],
                      toks: np.ndarray, shape, alpha: float, p: float, seed: int, step: int,
-                     micro: int = 0, operand: str = "exact"):
+                     micro: int = 0, operand: str = "exact", trace: bool = False):
     """Returns (loss, grads[layer][proj] = (dA, dB)).  layers hold quantized params.
     operand: how activations and gradients enter the frozen-base products
-    (lora.base_operand); "bf16" is the stack with fp32 activations on bf16 matrix cores."""
+    (lora.base_operand); "bf16" is the stack with fp32 activations on bf16 matrix cores.
+    trace: also return {"inputs", "outputs", "d_outputs", "d_inputs"}, per layer: the
+    block's input and output activations and the loss gradients at its output and input
+    (the values this composition already forms, kept for layer-by-layer comparisons)."""
     rk = lora.RngKey(seed=seed, step=step, micro=micro)
     h = glob["emb"][toks].astype(np.float64)
     bounds = []
+    outputs = []
     for li, qp in enumerate(layers):
         bounds.append(h)
         h, _ = block.forward(h, qp, shape, li, alpha, p, rk, operand)
+        outputs.append(h)
     hn, rinv = block.rmsnorm(h, glob["lnf"].astype(np.float64))
     logits = hn @ glob["lm"].astype(np.float64).T
     loss, dlog = loss_and_dlogits(logits, toks)
     dhn = dlog @ glob["lm"].astype(np.float64)
     dh = block.rmsnorm_bwd(h, glob["lnf"].astype(np.float64), rinv, dhn)
     grads: List[Dict[str, tuple]] = [None] * len(layers)
+    d_out, d_in = [None] * len(layers), [None] * len(layers)
     for li in reversed(range(len(layers))):
         qp = layers[li]
         _, cache = block.forward(bounds[li], qp, shape, li, alpha, p, rk, operand)  # recompute
+        d_out[li] = dh
         dh, grads[li] = block.backward(dh, cache, qp, shape, li, alpha, p, rk, operand)
+        d_in[li] = dh
+    if trace:
+        return loss, grads, {"inputs": bounds, "outputs": outputs, "d_outputs": d_out, "d_inputs": d_in}
     return loss, grads
 
 

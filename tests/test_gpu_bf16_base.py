@@ -10,6 +10,8 @@ shape ("Current limitations", "bf16 LoRA").
     which checks the bf16 path at the full 32B projection shapes;
   * streamed == resident bitwise on a tiny stack (dropout on) and on the 64-layer 32B
     stack."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -20,7 +22,7 @@ from oracle import lora as olora
 from oracle import step as ostep
 
 from gpu_util import assert_parity, dev_bf16, dev_f32, host_f64
-from test_gpu_stack import STACK_TOL, TINY, _shape
+from test_gpu_stack import OPERAND, TINY, _shape, chain_tolerance
 
 pytestmark = pytest.mark.gpu
 msq = pytest.importorskip("memory_streamed_qlora_amd")
@@ -127,21 +129,24 @@ def test_bf16_stack_streamed_equals_resident_and_oracle():
     # the first step's gradients against the oracle's bf16-base step
     bl = [oblock.bf16_params(p) for p in layers]
     rloss, rgrads = ostep.forward_backward(bl, glob, mi.tokens(seed, 3, 0, T, TINY.vocab), TINY, lo.alpha,
-                                           lo.p_drop, seed, 0)
+                                           lo.p_drop, seed, 0, operand=OPERAND)
+    _, exact = ostep.forward_backward(bl, glob, mi.tokens(seed, 3, 0, T, TINY.vocab), TINY, lo.alpha, lo.p_drop, seed, 0)
+    tol = chain_tolerance(exact, rgrads)
     assert abs(la[0][0] - rloss) <= 2e-2 * abs(rloss)
     for l in range(TINY.layers):
         for proj in S.PROJS:
             for which, nm in ((0, "A"), (1, "B")):
-                assert_parity(host_f64(ga[f"{l}.{proj}.{nm}.grad"]), rgrads[l][proj][which], tol=STACK_TOL,
+                assert_parity(host_f64(ga[f"{l}.{proj}.{nm}.grad"]), rgrads[l][proj][which], tol=tol,
                               name=f"bf16 {l}.{proj}.d{nm}")
 
 
 @pytest.mark.slow
 def test_qwen32b_bf16_streamed_equals_resident():
-    """The 64-layer Qwen2.5-32B shape with a bf16 base (62.4 GB), window 4 x 3 slots,
-    dropout 0.0, 2 optimizer steps: streamed == resident on every surface.  The lm_head
-    stays on the device: the pinned bf16 base already takes the host's pinnable memory."""
-    shape = S.QWEN25_32B
+    """32 layers of the Qwen2.5-32B shape with a bf16 base (31.2 GB pinned), window 4 x 3
+    slots, dropout 0.0, 2 optimizer steps: streamed == resident on every surface.  Half the
+    64 layers: how much host memory a process may pin differs between hosts, and the whole
+    bf16 base (62.4 GB) does not fit everywhere.  The lm_head stays on the device."""
+    shape = dataclasses.replace(S.QWEN25_32B, layers=32)
     outs = []
     for mode in ("resident", "streamed"):
         print(f"[bf16 32B] building {mode}", flush=True)

@@ -57,8 +57,8 @@ def test_qwen05b_block_fwd_bwd_vs_oracle():
     torch.cuda.synchronize()
     qp = oblock.quantize_params(prm)
     rk = olora.RngKey(seed=seed, step=step)
-    ro, cache = oblock.forward(io["x"], qp, sh, 0, lo.alpha, lo.p_drop, rk)
-    rdx, grads = oblock.backward(io["dy"], cache, qp, sh, 0, lo.alpha, lo.p_drop, rk)
+    ro, cache = oblock.forward(io["x"], qp, sh, 0, lo.alpha, lo.p_drop, rk, OPERAND)
+    rdx, grads = oblock.backward(io["dy"], cache, qp, sh, 0, lo.alpha, lo.p_drop, rk, OPERAND)
     pairs = {"out": (host_f64(out), ro), "dx": (host_f64(x.grad), rdx)}
     for proj in S.PROJS:
         pairs[proj + ".dA"] = (host_f64(st.A[0][proj].grad), grads[proj][0])
@@ -79,18 +79,72 @@ def _tiny(seed=0, lo=mi.LoraSpec(8, 16.0, 0.1), w_std=0.02):
     return layers, glob
 
 
-# Tolerance of the multi-layer comparison.  Each library call is held to 2e-2*RMS
-# (test_gpu_linear) and so is the 0.5B block above.  Through a 3-layer chain at 32
-# tokens, the bf16 rounding of the MFMA operands alone (activations into the base
-# product forward, gradients into it backward) moves the adapter gradients by up to
-# 2.7e-2*RMS: the oracle re-run with exactly those roundings inserted (and nothing
-# else changed) shows that, see test_oracle_rounding.py.  The chain is held to twice
-# that envelope; loss and grad norm stay at 2e-2.
-STACK_TOL = 5.4e-2
+# Multi-layer comparisons run against the oracle step with the frozen-base products'
+# bf16 operands (operand="bf16": fp32 activations enter x W^T, and fp32 gradients enter
+# dy W, rounded to bf16, the arithmetic of the bf16 matrix cores; oracle/lora.py, pinned in
+# test_oracle_operand.py).
+#   * Every layer, on the oracle's own input activation and output gradient, is held to
+#     the 2e-2*RMS bar (test_tiny_stack_layers_on_oracle_inputs).
+#   * A whole chain is held to a bound derived from the rounding itself.  Rounding to bf16
+#     is discontinuous: a value within fp32 noise of a rounding midpoint rounds one way in
+#     fp32 and the other in fp64, a one-ulp (2^-8 relative) change of that operand.  One such
+#     flip perturbs the values downstream of it by ~1e-3 relative, a quarter of a bf16 ulp,
+#     so the roundings after it no longer coincide either: through a chain the GPU's bf16
+#     operands decorrelate from the oracle's.  Two independent roundings of the same values
+#     differ by at most sqrt(2) times what one rounding moves the result, and what one
+#     rounding moves the result is the distance between the oracle's "exact" and "bf16"
+#     readings on the same inputs.  So a chain is held to sqrt(2) * that distance, which the
+#     oracle computes per test (2.4e-2 to 4.8e-2 on these tiny stacks; an fp32 evaluation of
+#     the oracle's own arithmetic lands at 1.1e-2 to 2.2e-2 from its fp64 evaluation).
+OPERAND = "bf16"
+
+
+def chain_tolerance(exact_grads, bf16_grads) -> float:
+    """sqrt(2) * the largest max|exact - bf16| / RMS(bf16) over the adapter gradients of two
+    oracle runs that differ only in the operand reading (see above), at least 2e-2."""
+    env = max(float(np.max(np.abs(e[p][w] - b[p][w])) / np.sqrt(np.mean(b[p][w] ** 2)))
+              for e, b in zip(exact_grads, bf16_grads) for p in S.PROJS for w in (0, 1))
+    return max(2e-2, float(np.sqrt(2.0)) * env)
+
+
+def test_tiny_stack_layers_on_oracle_inputs():
+    """Each layer of a 3-layer stack, run by the GPU on the oracle's own input activation
+    and output gradient for that layer: output, input gradient and all 14 adapter
+    gradients at the 2e-2*RMS bar.  Every layer is compared on the same inputs, so the
+    rounding flips that two different fp32/fp64 histories provoke at the bf16 operands
+    (see the whole-step test below) do not enter."""
+    lo, seed, T = mi.LoraSpec(8, 16.0, 0.1), 1, 128
+    layers, glob = _tiny(seed, lo)
+    toks_np = mi.tokens(seed, 3, 0, T, TINY.vocab)
+    st = _build(TINY, T, layers, glob, lo, "resident", 1, seed)
+    qlayers = [oblock.quantize_params(p) for p in layers]
+    _, rgrads, tr = ostep.forward_backward(qlayers, glob, toks_np, TINY, lo.alpha, lo.p_drop, seed, 0,
+                                           operand=OPERAND, trace=True)
+    worst = 0.0
+    for l in range(TINY.layers):
+        for d in (st.A[l], st.B[l]):
+            for prm in d.values():
+                prm.grad = None
+        x = torch.from_numpy(tr["inputs"][l].astype(np.float32)).cuda().requires_grad_()
+        out = st.layer_forward(x, l, st._views(l), 0)
+        out.backward(torch.from_numpy(tr["d_outputs"][l].astype(np.float32)).cuda())
+        torch.cuda.synchronize()
+        pairs = {"out": (out, tr["outputs"][l]), "dx": (x.grad, tr["d_inputs"][l])}
+        for proj in S.PROJS:
+            pairs[proj + ".dA"] = (st.A[l][proj].grad, rgrads[l][proj][0])
+            pairs[proj + ".dB"] = (st.B[l][proj].grad, rgrads[l][proj][1])
+        ratios = {k: assert_parity(host_f64(g), r, name=f"layer {l} {k}") for k, (g, r) in pairs.items()}
+        top = sorted(ratios.items(), key=lambda kv: -kv[1])[:4]
+        print(f"layer {l} on oracle inputs:", {k: f"{v:.2e}" for k, v in top}, flush=True)
+        worst = max(worst, top[0][1])
+    print(f"layers on oracle inputs: worst max|diff|/RMS = {worst:.2e}", flush=True)
+    st.close()
 
 
 def test_tiny_stack_step_vs_oracle():
-    lo, seed, T = mi.LoraSpec(8, 16.0, 0.1), 1, 32
+    """The whole step end to end: loss, grad norm, every adapter gradient and the first
+    AdamW moments against the oracle's step."""
+    lo, seed, T = mi.LoraSpec(8, 16.0, 0.1), 1, 128
     layers, glob = _tiny(seed, lo)
     toks_np = mi.tokens(seed, 3, 0, T, TINY.vocab)
     st = _build(TINY, T, layers, glob, lo, "streamed", 2, seed)
@@ -98,28 +152,33 @@ def test_tiny_stack_step_vs_oracle():
     loss, gn = st.train_step(torch.from_numpy(toks_np).cuda())
     torch.cuda.synchronize()
     qlayers = [oblock.quantize_params(p) for p in layers]
-    rloss, rgrads = ostep.forward_backward(qlayers, glob, toks_np, TINY, lo.alpha, lo.p_drop, seed, 0)
+    rloss, rgrads = ostep.forward_backward(qlayers, glob, toks_np, TINY, lo.alpha, lo.p_drop, seed, 0,
+                                          operand=OPERAND)
+    _, exact = ostep.forward_backward(qlayers, glob, toks_np, TINY, lo.alpha, lo.p_drop, seed, 0)
+    tol = chain_tolerance(exact, rgrads)
     assert abs(loss.item() - rloss) <= 2e-2 * abs(rloss)
     assert abs(gn.item() - ostep.grad_norm(rgrads)) <= 2e-2 * ostep.grad_norm(rgrads)
     state = st.state_tensors()
+    worst = 0.0
     for l in range(TINY.layers):
         for proj in S.PROJS:
             for which, nm in ((0, "A"), (1, "B")):
                 g = rgrads[l][proj][which]
-                assert_parity(host_f64(state[f"{l}.{proj}.{nm}.grad"]), g, tol=STACK_TOL,
-                              name=f"{l}.{proj}.d{nm}")
+                worst = max(worst, assert_parity(host_f64(state[f"{l}.{proj}.{nm}.grad"]), g, tol=tol,
+                                                 name=f"{l}.{proj}.d{nm}"))
                 p0 = before[f"{l}.{proj}.{nm}"].cpu().numpy().astype(np.float64)
                 rp, rm, rv = ostep.adamw(p0, g, np.zeros_like(g), np.zeros_like(g), 1)
-                assert_parity(host_f64(state[f"{l}.{proj}.{nm}.exp_avg"]), rm, tol=STACK_TOL, name="m")
+                assert_parity(host_f64(state[f"{l}.{proj}.{nm}.exp_avg"]), rm, tol=tol, name="m")
                 # v ~ g^2: compare sqrt(v), the quantity the update divides by
-                assert_parity(np.sqrt(host_f64(state[f"{l}.{proj}.{nm}.exp_avg_sq"])), np.sqrt(rv),
-                              tol=STACK_TOL, name="sqrt(v)")
+                assert_parity(np.sqrt(host_f64(state[f"{l}.{proj}.{nm}.exp_avg_sq"])), np.sqrt(rv), tol=tol,
+                              name="sqrt(v)")
                 # AdamW's first update is +-lr*(1 + tiny) per element whatever |g| is, so a
                 # gradient within rounding noise of zero may flip its sign: allow that on a
                 # handful of elements, demand agreement to 0.1*lr everywhere else
                 dp = np.abs(host_f64(state[f"{l}.{proj}.{nm}"]) - rp)
                 assert dp.max() <= 2.01 * ostep.LR * (1 + 1e-3)
                 assert np.mean(dp > 0.1 * ostep.LR) < 0.01
+    print(f"tiny stack: worst adapter-gradient max|diff|/RMS = {worst:.2e} (chain bound {tol:.2e})", flush=True)
     st.close()
 
 
