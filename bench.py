@@ -59,6 +59,11 @@ def measured_traffic(kernel: str):
     return None
 
 
+# Qwen2.5 stacks of the workloads: (hidden, heads, kv heads, head dim, intermediate, layers,
+# dropout, default window slots)
+SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, 2), "32b": (5120, 40, 8, 128, 27648, 64, 0.0, 7),
+          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, 2)}
+
 PROJ_NAMES = {(5120, 5120): "q/o", (1024, 5120): "k/v", (27648, 5120): "gate/up", (5120, 27648): "down",
               (7168, 5120): "q+k+v", (55296, 5120): "gate+up"}
 
@@ -108,12 +113,12 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def h2d_ceiling_gbps(torch, nbytes=1 << 30, reps=10) -> float:
-    """Median pinned host->device copy rate of one 1 GiB buffer with nothing else running."""
+def h2d_ceiling_gbps(torch, s, nbytes=1 << 30, reps=10) -> float:
+    """Median pinned host->device copy rate of one 1 GiB buffer with nothing else running,
+    copied on stream s (the window's first copy stream)."""
     h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     h.fill_(1)
     d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    s = torch.cuda.Stream()
     ts = []
     for i in range(reps + 2):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -126,6 +131,33 @@ def h2d_ceiling_gbps(torch, nbytes=1 << 30, reps=10) -> float:
             ts.append(e0.elapsed_time(e1))
     ts.sort()
     del h, d
+    return nbytes / 1e6 / ts[len(ts) // 2]
+
+
+def h2d_ceiling_under_compute_gbps(torch, s, nbytes=1 << 30, reps=5) -> float:
+    """The same 1 GiB pinned copy while the compute stream runs bf16 GEMMs (queued before the
+    copy and lasting longer than it): the rate the window's copies can expect during a step."""
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    h.fill_(1)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    ts = []
+    for i in range(reps + 1):
+        torch.cuda.synchronize()
+        for _ in range(48):                      # ~50 ms of matrix work on the compute stream
+            torch.matmul(a, b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record()
+            d.copy_(h, non_blocking=True)
+            e1.record()
+        e1.synchronize()
+        torch.cuda.synchronize()
+        if i >= 1:
+            ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    del h, d, a, b
     return nbytes / 1e6 / ts[len(ts) // 2]
 
 
@@ -194,7 +226,10 @@ def h2d_busy(window, lm, ms_per_step: float, ceiling: float) -> dict:
     measured ceiling."""
     if not window or not window.get("copies_timed"):
         return {}
-    busy = window["copy_ms"] + (lm["ms"] if lm else 0.0)
+    # window copies: the union of their spans over the copy streams; the lm_head chunks are
+    # added on top (they may overlap window copies on another stream, so this is an upper
+    # bound on the busy time and a lower bound on the rate)
+    busy = window["busy_ms"] + (lm["ms"] if lm else 0.0)
     nbytes = window["bytes_copied"] + (lm["bytes"] if lm else 0.0)
     rate = nbytes / (busy * 1e-3) / 1e9 if busy > 0 else 0.0
     return {"copy_busy_ms_per_step": round(busy, 1), "copy_busy_frac": round(busy / ms_per_step, 3),
@@ -435,14 +470,19 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--layers", type=int, default=64, help="stack depth (64 = the 32B shape)")
+    ap.add_argument("--shape", choices=tuple(SHAPES), default="32b",
+                    help="Qwen2.5 stack shape: 32b (the headline), 7b or 72b (dropout 0.1, as their workloads state)")
+    ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the shape's)")
     ap.add_argument("--window-blocks", type=int, default=4,
                     help="layers per window slot (blocks per streamed window)")
-    ap.add_argument("--slots", type=int, default=7,
-                    help="window slots in the device arena: the deepest prefetch whose peak device memory "
-                         "stays under the pages' 10.95 GB streamed peak for this configuration")
-    ap.add_argument("--resident", action="store_true",
-                    help="also time the same step with the whole base resident in device memory")
+    ap.add_argument("--slots", type=int, default=None,
+                    help="window slots in the device arena (default 7 at 32b: the deepest prefetch whose peak "
+                         "device memory stays under the pages' 10.95 GB streamed peak; 2 at 7b and 72b)")
+    ap.add_argument("--copy-streams", type=int, default=2, help="copy streams of the window (layer l on stream l mod n)")
+    ap.add_argument("--no-resident", action="store_true",
+                    help="skip the resident leg (the same step with the whole base in device memory)")
+    ap.add_argument("--no-literal-window", action="store_true",
+                    help="skip the 32b leg with the two-slot window (4 layers x 2 slots)")
     ap.add_argument("--ga", type=int, default=1,
                     help="micro-batches of 512 tokens per optimizer step (gradient accumulation)")
     ap.add_argument("--order", choices=("block", "micro"), default="block",
@@ -471,15 +511,26 @@ def main() -> int:
     if args.skinny:
         return skinny()
 
+    import statistics
+
     import torch
 
     from memory_streamed_qlora_amd import ops, stack as S
 
     torch.cuda.set_device(0)
-    shape = S.Shape(5120, 40, 8, 128, 27648, args.layers)
+    hid, heads, kvh, hd, inter, nl, p_drop, slots_default = SHAPES[args.shape]
+    layers = args.layers or nl
+    slots = args.slots or slots_default
+    shape = S.Shape(hid, heads, kvh, hd, inter, layers)
+    size = args.shape.upper()
     T = 512
-    ceiling = h2d_ceiling_gbps(torch)
-    log(f"H2D ceiling (1 GiB pinned, median of 10): {ceiling:.1f} GB/s")
+    # the window's copy streams first: a HIP stream keeps the hardware queue it is given on
+    # first use (4 per process), so streams created before them could push one of them onto
+    # the compute stream's queue; the ceiling copies run on the first of them
+    cstreams = S.copy_streams(torch.device("cuda", 0), args.copy_streams)
+    ceiling = h2d_ceiling_gbps(torch, cstreams[0])
+    ceiling_busy = h2d_ceiling_under_compute_gbps(torch, cstreams[0])
+    log(f"H2D ceiling (1 GiB pinned, median of 10): {ceiling:.1f} GB/s; under concurrent GEMMs: {ceiling_busy:.1f} GB/s")
     copy_calibration(torch)
 
     def batch(st, s: int):
@@ -488,14 +539,14 @@ def main() -> int:
             return S.random_tokens(0, s, T, shape.vocab, "cpu")
         return torch.stack([S.random_tokens(0, s * args.ga + m, T, shape.vocab, "cpu") for m in range(args.ga)])
 
-    def run(mode: str, kernel_timing: bool):
+    def run(mode: str, kernel_timing: bool, n_slots: int):
         t_build = time.time()
-        st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=0.0,
-                            window_blocks=args.window_blocks, n_slots=args.slots, mode=mode, glue=args.glue,
+        st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=p_drop,
+                            window_blocks=args.window_blocks, n_slots=n_slots, mode=mode, glue=args.glue,
                             base=args.base, layer_release=not args.window_release,
-                            lm_stream=mode == "streamed" and not args.lm_resident)
+                            lm_stream=mode == "streamed" and not args.lm_resident, n_copy_streams=args.copy_streams)
         torch.cuda.synchronize()
-        log(f"{mode}: built {args.layers} layers in {time.time() - t_build:.1f}s "
+        log(f"{mode} ({args.window_blocks} x {n_slots}): built {layers} layers in {time.time() - t_build:.1f}s "
             f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
         for w in range(args.warmup):
             loss, gn = st.train_step(batch(st, w), order=args.order)
@@ -508,11 +559,16 @@ def main() -> int:
         torch.cuda.reset_peak_memory_stats()
         ops.timing_enable(kernel_timing)
         ops.timing_collect()
+        free0 = torch.cuda.mem_get_info()[0]
         torch.cuda.synchronize()
+        # one event per step boundary on the compute stream: per-step times without syncing
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         t0 = time.perf_counter()
+        evs[0].record()
         losses = []
         for s in range(args.steps):
             loss, gn = st.train_step(toks[s], order=args.order)
+            evs[s + 1].record()
             losses.append(loss)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
@@ -520,23 +576,32 @@ def main() -> int:
         kt = ops.timing_collect()
         stats1 = st.window.stats() if st.window else None
         lmc = st.lm_copy_stats()
-        out = {"seconds": dt, "losses": [l.item() for l in losses], "kernels": kt,
+        step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+        out = {"seconds": dt, "losses": [l.item() for l in losses], "kernels": kt, "step_ms": step_ms,
                "peak_alloc_gb": torch.cuda.max_memory_allocated() / 1e9,
+               "peak_reserved_gb": torch.cuda.max_memory_reserved() / 1e9,
                "window": None, "lm_copies": {k: v / args.steps for k, v in lmc.items()}}
         if stats0:
             out["window"] = {k: (stats1[k] - stats0[k]) / args.steps for k in stats1}
-        log(f"{mode}: {args.steps} steps in {dt:.3f}s -> {dt / args.steps * 1e3:.1f} ms/step; "
-            f"losses {[round(x, 4) for x in out['losses']]}")
+        log(f"{mode}: {args.steps} steps in {dt:.3f}s -> {dt / args.steps * 1e3:.1f} ms/step "
+            f"(median {statistics.median(step_ms):.1f}); losses {[round(x, 4) for x in out['losses']]}")
         st.close()
         del st
         torch.cuda.empty_cache()
         return out
 
+    def spread(step_ms):
+        return {"median_ms": round(statistics.median(step_ms), 2),
+                "std_ms": round(statistics.stdev(step_ms), 2) if len(step_ms) > 1 else 0.0,
+                "min_ms": round(min(step_ms), 2), "max_ms": round(max(step_ms), 2)}
+
     # The streamed step carries the per-launch event timing the roofline needs (its host
-    # issue time stays far below the copy-bound step).  The resident comparison is timed
-    # without it: there the extra host work per launch would make the step host-bound.
-    streamed = run("streamed", not args.no_kernel_timing)
-    resident = run("resident", False) if args.resident else None
+    # issue time stays far below the copy-bound step).  The other legs are timed without it:
+    # in the resident step the extra host work per launch would make the step host-bound.
+    streamed = run("streamed", not args.no_kernel_timing, slots)
+    literal = (run("streamed", False, 2) if args.shape == "32b" and slots != 2 and not args.no_literal_window
+               else None)
+    resident = run("resident", False, 2) if not args.no_resident else None
 
     ms = streamed["seconds"] / args.steps * 1e3
     value = T * args.ga * args.steps / streamed["seconds"]
@@ -554,7 +619,8 @@ def main() -> int:
         achieved = avg_flops / (avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma" if avg_flops > 0 else "hbm", "kernel": name, "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": measured_traffic(name), "avg_launch_ms": round(avg_ms, 4),
+                    "traffic": measured_traffic(name) if args.shape == "32b" else None,
+                    "avg_launch_ms": round(avg_ms, 4),
                     "algorithmic_gflop_per_launch": round(avg_flops / 1e9, 3)}
     kernels = {n: {"launches": v["launches"], "avg_ms": v["total_ms"] / v["launches"],
                    "tflops": v["total_flops"] / (v["total_ms"] * 1e-3) / 1e12,
@@ -574,20 +640,23 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(value / (T / PAGES_A100_S_PER_STEP), 3)
-                        if args.layers == 64 and args.ga == 1 and args.base == "nf4" else None),
+                        if args.shape == "32b" and layers == 64 and args.ga == 1 and args.base == "nf4" else None),
         "dtype": "bf16",
         "data": "synthetic (random N(0,0.02) NF4 base, random adapters, random tokens)",
-        "config": {"workload": "Qwen2.5-32B-shaped streamed NF4+LoRA train step", "layers": args.layers,
-                   "hidden": 5120, "heads": 40, "kv_heads": 8, "intermediate": 27648, "vocab": 152064,
-                   "seq_len": T, "batch": 1, "micro_batches": args.ga,
+        "config": {"workload": (f"Qwen2.5-{size}-shaped streamed NF4+LoRA train step, windows of "
+                                f"{args.window_blocks} layers x {slots} slots"),
+                   "layers": layers, "hidden": hid, "heads": heads, "kv_heads": kvh, "intermediate": inter,
+                   "vocab": 152064, "seq_len": T, "batch": 1, "micro_batches": args.ga,
                    **({"accumulation_order": args.order} if args.ga > 1 else {}),
-                   "window": {"layers_resident": args.window_blocks * args.slots,
-                              "slots": args.slots, "layers_per_slot": args.window_blocks},
-                   "lora_r": 16, "lora_alpha": 32,
-                   "dropout": 0.0, "optimizer": "AdamW", "base": args.base, "glue": args.glue, "parallelism": "single GPU"},
+                   "window_layers_per_slot": args.window_blocks, "window_slots": slots,
+                   "window_layers_resident": args.window_blocks * slots, "copy_streams": args.copy_streams,
+                   "lora_r": 16, "lora_alpha": 32, "dropout": p_drop, "optimizer": "AdamW", "base": args.base,
+                   "glue": args.glue, "parallelism": "single GPU"},
+        "step_time": spread(streamed["step_ms"]),
         "roofline": roofline,
         "h2d": {"bytes_per_step": int(h2d_bytes), "achieved_GBps": round(h2d_rate, 1),
-                "ceiling_GBps": round(ceiling, 1), "frac": round(h2d_rate / ceiling, 3),
+                "ceiling_GBps": round(ceiling, 1), "ceiling_under_compute_GBps": round(ceiling_busy, 1),
+                "frac": round(h2d_rate / ceiling, 3),
                 "windows_copied_per_step": streamed["window"]["windows_copied"] if streamed["window"] else 0,
                 "windows_reused_per_step": streamed["window"]["windows_reused"] if streamed["window"] else 0,
                 "lm_head_bytes_per_step": int(lm_bytes),
@@ -596,16 +665,26 @@ def main() -> int:
         "gemm_shapes": shapes,
         "hbm_kernels": hbm,
         "peak_vram_gb": round(streamed["peak_alloc_gb"], 2),
+        "peak_vram_reserved_gb": round(streamed["peak_reserved_gb"], 2),
         "baseline_context": {"value": round(T / PAGES_A100_S_PER_STEP, 1), "unit": "tokens/s",
                              "hardware": "NVIDIA A100 80GB PCIe", "s_per_step": PAGES_A100_S_PER_STEP},
     }
+    if literal:
+        lms = literal["seconds"] / args.steps * 1e3
+        lw = literal["window"]
+        result["window_2_slots"] = {"ms_per_step": round(lms, 2), **spread(literal["step_ms"]),
+                                    "tokens_per_s": round(T * args.ga * args.steps / literal["seconds"], 2),
+                                    "h2d_bytes_per_step": int(lw["bytes_copied"] + literal["lm_copies"]["bytes"]),
+                                    "peak_vram_gb": round(literal["peak_alloc_gb"], 2),
+                                    "losses_equal": literal["losses"] == streamed["losses"]}
     if resident:
         rms = resident["seconds"] / args.steps * 1e3
-        result["resident"] = {"ms_per_step": round(rms, 2), "tokens_per_s": round(T * args.ga * args.steps / resident["seconds"], 2),
+        result["resident"] = {"ms_per_step": round(rms, 2), **spread(resident["step_ms"]),
+                              "tokens_per_s": round(T * args.ga * args.steps / resident["seconds"], 2),
                               "peak_vram_gb": round(resident["peak_alloc_gb"], 2),
                               "streamed_over_resident": round(ms / rms, 3),
                               "losses_equal": resident["losses"] == streamed["losses"]}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.shape == "32b":
         result["cpu_baseline"] = cpu_baseline()
     result["host"] = {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
     print(json.dumps(result), flush=True)

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 10
+#define MSQ_ABI_VERSION 11
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -338,6 +338,17 @@ int msq_rmsnorm_apply_bwd(const float* dy, const float* h, const float* r, const
                           int64_t d, float* dh, float* hdot, msq_stream_t stream);
 
 /* ------------------------------------------------------------------------- */
+/* Pinned host memory for the frozen base ("Poros" research post: the base lives in
+ * host memory between its trips through the window, and host RAM is the other cost of
+ * streaming; memory paragraph).  msq_host_alloc pins `bytes` with hipHostMalloc, at
+ * that size (no rounding up to a power of two, as a caching allocator may do), and
+ * returns a host pointer aligned to at least 256 bytes; msq_host_free releases it (NULL
+ * is a no-op).  bytes == 0 or above 2^46, or a NULL out, is MSQ_E_INVAL; a failed
+ * allocation is MSQ_E_HIP. */
+int msq_host_alloc(size_t bytes, void** out);
+int msq_host_free(void* p);
+
+/* ------------------------------------------------------------------------- */
 /* Streamed quantizing load.
  * The pages' default loader stages one tensor at a time, quantizes it and evicts it
  * before the next, keeping the load-time device peak far below a standard load, with
@@ -383,33 +394,45 @@ int nf4_stream_load(const msq_quant_job* jobs, int n_jobs, int64_t chunk_rows, v
  * the next loads; more slots let the copies run further ahead).  With
  * window_blocks = 1 and n_slots = 2B the same arena as B-block windows double
  * buffered becomes a ring of single-layer slots, released and refilled layer by
- * layer.  Layer blobs live in pinned host memory (hipHostMalloc or equivalent) and
- * are copied with hipMemcpyAsync on copy_stream.  Each layer's device address is
- * its offset in the slot (blob offsets rounded up to 256 bytes).  The window object
- * owns only events and bookkeeping; it is not thread-safe.
+ * layer.  Layer blobs live in pinned host memory (msq_host_alloc, hipHostMalloc or
+ * registered memory; checked at creation) and are copied with hipMemcpyAsync, layer l
+ * on copy_streams[l % n_copy_streams].  Position q of a slot (the q-th layer of the
+ * window it holds) has a fixed byte range, as large as the largest layer at position q
+ * of any window (sizes rounded up to 256 bytes), so the ranges of different positions
+ * never overlap and a copy needs to wait only for the layer it overwrites.  The window
+ * object owns only events and bookkeeping; it is not thread-safe.
  *
  *   host_blobs  host array of n_layers pointers to pinned host memory
  *   blob_bytes  host array of n_layers sizes
  *   dev_arena   caller-owned device memory, 256-byte aligned, arena_bytes long;
  *               needs at least block_stream_arena_bytes(...) bytes, else
  *               MSQ_E_WINDOW (the message names the largest window that fits).
+ *   copy_streams host array of 1 .. MSQ_MAX_COPY_STREAMS streams (keep them at the
+ *               default priority).  Two streams let one layer's copy run while the next
+ *               waits for its position to be released.
+ * A blob that is not pinned host memory over its whole range is MSQ_E_INVAL (a HIP
+ * runtime that cannot tell, for instance with no GPU, is MSQ_E_HIP); every other
+ * argument is checked before that, without HIP calls.
  * The arrays are copied; the blobs and the arena must outlive the window. */
+#define MSQ_MAX_COPY_STREAMS 4
 typedef struct msq_window msq_window;
 
 typedef struct {
   uint64_t bytes_copied;    /* host-to-device bytes issued */
   uint64_t windows_copied;  /* window loads that issued copies */
   uint64_t windows_reused;  /* prefetches satisfied by a slot that still held the window */
-  double copy_ms;           /* time the copy stream spent in window copies (events around
-                               each window's copies, after its wait for the slot) */
-  uint64_t copies_timed;    /* window copies included in copy_ms */
+  double copy_ms;           /* summed durations of the layer copies (events around each
+                               copy, after its waits) */
+  uint64_t copies_timed;    /* layer copies included in copy_ms */
+  double busy_ms;           /* time at least one copy stream was copying: the union of the
+                               copies' spans (equals copy_ms with one copy stream) */
 } msq_window_stats;
 
 size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks,
                                 int n_slots);
 int block_stream_create(msq_window** out, const void* const* host_blobs, const size_t* blob_bytes,
                         int n_layers, int window_blocks, int n_slots, void* dev_arena,
-                        size_t arena_bytes, msq_stream_t copy_stream);
+                        size_t arena_bytes, const msq_stream_t* copy_streams, int n_copy_streams);
 /* Start loading the window that begins at first_layer (a multiple of
  * window_blocks) into a free slot (the least recently released one): the copy
  * stream first waits until the compute stream released that slot, then copies,
@@ -431,7 +454,8 @@ int block_stream_release(msq_window* w, int first_layer, msq_stream_t compute);
  * MSQ_E_ORDER. */
 int block_stream_release_layer(msq_window* w, int layer, msq_stream_t compute);
 /* Statistics since creation.  Waits for the issued copies to finish so that their
- * durations are included (call it outside timed regions). */
+ * durations are included (call it outside timed regions).  The other window calls
+ * never wait: a copy's duration is read from its events once they have completed. */
 int block_stream_stats(msq_window* w, msq_window_stats* out);
 /* Waits for the window's outstanding copies, then frees its events. */
 int block_stream_destroy(msq_window* w);

@@ -31,6 +31,7 @@ class RngKey(ctypes.Structure):
 MSQ_ACT_F32 = 1
 MSQ_OUT_F32 = 2
 MSQ_U_ONLY = 4
+MSQ_MAX_COPY_STREAMS = 4
 
 
 class LoraCfg(ctypes.Structure):
@@ -41,7 +42,7 @@ class LoraCfg(ctypes.Structure):
 class WindowStats(ctypes.Structure):
     _fields_ = [("bytes_copied", ctypes.c_uint64), ("windows_copied", ctypes.c_uint64),
                 ("windows_reused", ctypes.c_uint64), ("copy_ms", ctypes.c_double),
-                ("copies_timed", ctypes.c_uint64)]
+                ("copies_timed", ctypes.c_uint64), ("busy_ms", ctypes.c_double)]
 
 
 class QuantJob(ctypes.Structure):
@@ -108,13 +109,15 @@ _SIG = {
     "lora_group_bwd_workspace_size": (ctypes.c_size_t, [_I64, _I64, _P, ctypes.c_int, ctypes.c_int32]),
     "lora_bwd_group": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, LoraCfg, _P, ctypes.c_int, ctypes.c_int, _P,
                                       ctypes.c_size_t, _P]),
+    "msq_host_alloc": (ctypes.c_int, [ctypes.c_size_t, _P]),
+    "msq_host_free": (ctypes.c_int, [_P]),
     "nf4_stream_load_device_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "nf4_stream_load_host_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "nf4_stream_load": (ctypes.c_int, [_P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
                                        ctypes.c_int, _P]),
     "block_stream_arena_bytes": (ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "block_stream_create": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
-                                           ctypes.c_size_t, _P]),
+                                           ctypes.c_size_t, _P, ctypes.c_int]),
     "block_stream_prefetch": (ctypes.c_int, [_P, ctypes.c_int]),
     "block_stream_acquire": (ctypes.c_int, [_P, ctypes.c_int, _P, _P]),
     "block_stream_release": (ctypes.c_int, [_P, ctypes.c_int, _P]),
@@ -126,7 +129,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 10  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 11  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

@@ -1,4 +1,4 @@
-// Host-to-device block-prefetch window (double-buffered, event-ordered).
+// Host-to-device block-prefetch window (event-ordered slots of fixed layer positions).
 //
 // The pages' forward streams frozen blocks through a small GPU window with
 // asynchronous prefetch on side streams; the backward walks the blocks in reverse and
@@ -7,23 +7,33 @@
 // "Limitations", "Pretraining is out of scope").  Their block-size sweep (peak memory
 // at block sizes 1..16, "Poros" research post, memory paragraph) grows by two
 // blocks' worth per doubling, consistent with one window computing while the next
-// one loads: the default is two slots.  More slots let the copies run further ahead,
-// and single-layer slots let a slot be refilled as soon as its one layer is done.
+// one loads: at least two slots.  More slots let the copies run further ahead.
 //
-// Ordering is kept per layer position inside a slot: the copy stream waits on the
+// Layout.  A slot holds one window of window_blocks layers.  Position q of every slot
+// (the q-th layer of whichever window the slot holds) has one fixed byte range, as large
+// as the largest layer any window puts at position q; so the ranges of different
+// positions never overlap, whatever the layer sizes.
+//
+// Ordering is kept per (slot, position): the copy into a position waits on the
 // position's "freed" event (recorded on the compute stream when the layer that held it
-// was released) before overwriting it, and records the position's "ready" event after
-// its copy; acquire makes the compute stream wait on the layer's own "ready".  A window
-// is still claimed and copied as one unit, but its layers are copied in the order the
-// slot's previous layers were released (ascending after a forward, descending after a
-// backward), so the first layer of the next window lands as soon as the first layer of
-// the last one is done, and compute on a layer starts as soon as that layer has landed.
-// The host never blocks.  A prefetch of a window that a free slot still holds issues no
-// copy (the windows in the slots at the end of the forward are the first the backward
-// needs).
+// was released) and on its previous "ready" event (the last copy into it, in case that
+// copy ran on another copy stream), then records "ready" again after its copy; acquire
+// makes the compute stream wait on the layer's own "ready".  Since a position's byte range
+// belongs to it alone, these two waits are all a copy needs.  A window is still claimed
+// and copied as one unit, but its layers are copied in the order the slot's previous
+// layers were released (ascending after a forward, descending after a backward), so the
+// first layer of the next window lands as soon as the first layer of the last one is
+// done.  Layer l is copied on copy stream l % n_copy_streams: with two streams, one
+// layer's copy can run while the next one waits for its position to be released.
+//
+// The host never blocks on the hot path: copy durations are read from their events only
+// once the events have completed (polled without waiting), or when the statistics are
+// asked for.  A prefetch of a window that a free slot still holds issues no copy (the
+// windows in the slots at the end of the forward are the first the backward needs).
 #include <string.h>
 
 #include <algorithm>
+#include <deque>
 #include <vector>
 
 #include "../../include/msq.h"
@@ -35,59 +45,124 @@ namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 enum SlotState { SLOT_FREE = 0, SLOT_HELD = 1 };
+
+struct TimingPair {
+  hipEvent_t start = nullptr, end = nullptr;
+};
 }  // namespace
 
 struct msq_window {
   int n_layers = 0, window_blocks = 0, n_windows = 0, n_slots = 0;
   std::vector<const void*> host;
   std::vector<size_t> bytes;
-  std::vector<size_t> offset;  // offset of each layer inside its window's slot
+  std::vector<size_t> pos_off;  // byte offset of each position inside a slot
   size_t slot_bytes = 0;
   std::vector<char*> slot_base;
-  hipStream_t copy = nullptr;
+  std::vector<hipStream_t> copies;  // layer l is copied on copies[l % copies.size()]
   // per (slot, position) events, index slot * window_blocks + position
   std::vector<hipEvent_t> ready, freed;
-  std::vector<char> freed_recorded;
+  std::vector<char> ready_recorded, freed_recorded;
   std::vector<std::vector<int>> release_order;  // positions in the order they were released
   std::vector<std::vector<char>> released;      // per slot and position: released since claimed
   std::vector<int> slot_window;  // window whose bytes the slot holds (or will hold)
   std::vector<int> state;
   std::vector<uint64_t> release_tick;
   uint64_t tick = 0;
-  msq_window_stats stats = {0, 0, 0, 0.0, 0};
-  // copy timing: one (start, end) event pair per issued layer copy, from a ring; a pair is
-  // read (and its duration added to stats.copy_ms) when the ring comes round to it or when
-  // the statistics are asked for
-  static constexpr int TIMING_RING = 64;
-  hipEvent_t t_start[TIMING_RING] = {}, t_end[TIMING_RING] = {};
-  bool t_pending[TIMING_RING] = {};
-  int t_next = 0;
+  msq_window_stats stats = {0, 0, 0, 0.0, 0, 0.0};
+  // copy timing: a (start, end) event pair around each layer copy.  Pairs whose end has
+  // completed are read without waiting (hipEventQuery) and recycled; a copy takes a recycled
+  // pair or a new one.  Spans are measured from t_ref (recorded on copy stream 0 at creation
+  // and again after each statistics call, which has waited for every copy) so that the busy
+  // time can be the union of the spans of all copy streams.
+  std::deque<TimingPair> pending;
+  std::vector<TimingPair> spare;
+  std::vector<hipEvent_t> all_timing_events;
+  hipEvent_t t_ref = nullptr;
+  std::vector<std::pair<double, double>> spans;
 };
 
 namespace {
 
-size_t window_bytes(const size_t* blob_bytes, int n_layers, int first, int wb) {
-  size_t s = 0;
-  for (int l = first; l < first + wb && l < n_layers; ++l) s += align256(blob_bytes[l]);
+// Per-position range sizes: position q is as large as the largest layer at position q of
+// any window.
+std::vector<size_t> position_sizes(const size_t* blob_bytes, int n_layers, int wb) {
+  std::vector<size_t> s(wb, 0);
+  for (int l = 0; l < n_layers; ++l) s[l % wb] = std::max(s[l % wb], align256(blob_bytes[l]));
   return s;
 }
 
-size_t max_window_bytes(const size_t* blob_bytes, int n_layers, int wb) {
-  size_t m = 0;
-  for (int f = 0; f < n_layers; f += wb) m = std::max(m, window_bytes(blob_bytes, n_layers, f, wb));
-  return m;
+size_t slot_size(const size_t* blob_bytes, int n_layers, int wb) {
+  size_t t = 0;
+  for (size_t v : position_sizes(blob_bytes, n_layers, wb)) t += v;
+  return t;
 }
 
-// Adds the duration of timing pair i to the statistics once its copies are done.
-hipError_t collect_timing(msq_window* w, int i) {
-  if (!w->t_pending[i]) return hipSuccess;
-  hipError_t e = hipEventSynchronize(w->t_end[i]);
-  float ms = 0.0f;
-  if (e == hipSuccess) e = hipEventElapsedTime(&ms, w->t_start[i], w->t_end[i]);
+// Length of the union of the kept spans, which are then dropped; with `keep` > 0 the last
+// `keep` merged spans stay (later copies may still overlap them).
+double merge_spans(msq_window* w, size_t keep) {
+  std::vector<std::pair<double, double>>& v = w->spans;
+  std::sort(v.begin(), v.end());
+  std::vector<std::pair<double, double>> m;
+  for (const auto& s : v) {
+    if (!m.empty() && s.first <= m.back().second)
+      m.back().second = std::max(m.back().second, s.second);
+    else
+      m.push_back(s);
+  }
+  const size_t done = m.size() > keep ? m.size() - keep : 0;
+  double total = 0.0;
+  for (size_t i = 0; i < done; ++i) total += m[i].second - m[i].first;
+  v.assign(m.begin() + done, m.end());
+  return total;
+}
+
+// Adds a completed pair's duration and span to the statistics and recycles it.
+hipError_t account(msq_window* w, const TimingPair& p) {
+  float ms = 0.0f, t0 = 0.0f, t1 = 0.0f;
+  hipError_t e = hipEventElapsedTime(&ms, p.start, p.end);
+  if (e == hipSuccess) e = hipEventElapsedTime(&t0, w->t_ref, p.start);
+  if (e == hipSuccess) e = hipEventElapsedTime(&t1, w->t_ref, p.end);
   if (e != hipSuccess) return e;
   w->stats.copy_ms += ms;
   w->stats.copies_timed++;
-  w->t_pending[i] = false;
+  w->spans.emplace_back(t0, t1);
+  if (w->spans.size() > 4096) w->stats.busy_ms += merge_spans(w, 64);
+  w->spare.push_back(p);
+  return hipSuccess;
+}
+
+// Reads the pairs whose copies have completed, oldest first, without waiting; with `wait`,
+// waits for all of them.
+hipError_t harvest(msq_window* w, bool wait) {
+  while (!w->pending.empty()) {
+    const TimingPair p = w->pending.front();
+    hipError_t e = wait ? hipEventSynchronize(p.end) : hipEventQuery(p.end);
+    if (e == hipErrorNotReady) {
+      (void)hipGetLastError();  // not an error: the copy is still running
+      return hipSuccess;
+    }
+    if (e != hipSuccess) return e;
+    w->pending.pop_front();
+    e = account(w, p);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t take_pair(msq_window* w, TimingPair* out) {
+  if (!w->spare.empty()) {
+    *out = w->spare.back();
+    w->spare.pop_back();
+    return hipSuccess;
+  }
+  TimingPair p;
+  hipError_t e = hipEventCreate(&p.start);
+  if (e != hipSuccess) return e;
+  w->all_timing_events.push_back(p.start);
+  e = hipEventCreate(&p.end);
+  if (e != hipSuccess) return e;
+  w->all_timing_events.push_back(p.end);
+  *out = p;
   return hipSuccess;
 }
 
@@ -97,22 +172,61 @@ int find_slot(const msq_window* w, int win, int state) {
   return -1;
 }
 
+void destroy_events(msq_window* w) {
+  for (hipEvent_t e : w->ready)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : w->freed)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : w->all_timing_events)
+    if (e) (void)hipEventDestroy(e);
+  if (w->t_ref) (void)hipEventDestroy(w->t_ref);
+}
+
+// The blob must be pinned host memory over its whole range: the copies are asynchronous
+// DMA reads of it.
+int check_pinned(int l, const void* p, size_t n) {
+  const char* ends[2] = {(const char*)p, (const char*)p + n - 1};
+  for (const char* q : ends) {
+    hipPointerAttribute_t a;
+    memset(&a, 0, sizeof(a));
+    const hipError_t e = hipPointerGetAttributes(&a, q);
+    if (e == hipErrorInvalidValue || (e == hipSuccess && a.type != hipMemoryTypeHost)) {
+      (void)hipGetLastError();
+      return set_error(MSQ_E_INVAL,
+                       "block_stream_create: layer %d's blob (%p, %zu bytes) is not pinned host memory "
+                       "(hipHostMalloc or registered) over its whole range",
+                       l, p, n);
+    }
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return set_error(MSQ_E_HIP, "block_stream_create: cannot check that layer %d's blob is pinned host memory: %s (%d)",
+                       l, hipGetErrorString(e), (int)e);
+    }
+  }
+  return MSQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t block_stream_arena_bytes(const size_t* blob_bytes, int n_layers, int window_blocks,
                                 int n_slots) {
-  if (!blob_bytes || n_layers <= 0 || window_blocks <= 0 || n_slots < 2) return 0;
-  return (size_t)n_slots * max_window_bytes(blob_bytes, n_layers, window_blocks);
+  if (!blob_bytes || n_layers <= 0 || window_blocks <= 0 || window_blocks > n_layers || n_slots < 2 ||
+      n_slots > 1024)
+    return 0;
+  return (size_t)n_slots * slot_size(blob_bytes, n_layers, window_blocks);
 }
 
 int block_stream_create(msq_window** out, const void* const* host_blobs, const size_t* blob_bytes,
                         int n_layers, int window_blocks, int n_slots, void* dev_arena,
-                        size_t arena_bytes, msq_stream_t copy_stream) {
-  if (!out || !host_blobs || !blob_bytes || !dev_arena)
+                        size_t arena_bytes, const msq_stream_t* copy_streams, int n_copy_streams) {
+  if (!out || !host_blobs || !blob_bytes || !dev_arena || !copy_streams)
     return set_error(MSQ_E_INVAL, "block_stream_create: null pointer");
   *out = nullptr;
+  if (n_copy_streams < 1 || n_copy_streams > MSQ_MAX_COPY_STREAMS)
+    return set_error(MSQ_E_INVAL, "block_stream_create: n_copy_streams=%d outside [1, %d]", n_copy_streams,
+                     MSQ_MAX_COPY_STREAMS);
   if (n_layers <= 0 || window_blocks <= 0 || window_blocks > n_layers || n_slots < 2 || n_slots > 1024)
     return set_error(MSQ_E_INVAL, "block_stream_create: n_layers=%d window_blocks=%d n_slots=%d", n_layers,
                      window_blocks, n_slots);
@@ -121,11 +235,11 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
   for (int l = 0; l < n_layers; ++l)
     if (!host_blobs[l] || blob_bytes[l] == 0)
       return set_error(MSQ_E_INVAL, "block_stream_create: layer %d has no host blob", l);
-  const size_t need = (size_t)n_slots * max_window_bytes(blob_bytes, n_layers, window_blocks);
+  const size_t need = (size_t)n_slots * slot_size(blob_bytes, n_layers, window_blocks);
   if (arena_bytes < need) {
     int fit = 0;
     for (int wb = window_blocks - 1; wb >= 1; --wb)
-      if ((size_t)n_slots * max_window_bytes(blob_bytes, n_layers, wb) <= arena_bytes) {
+      if ((size_t)n_slots * slot_size(blob_bytes, n_layers, wb) <= arena_bytes) {
         fit = wb;
         break;
       }
@@ -135,20 +249,20 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
     return set_error(MSQ_E_WINDOW, "block_stream_create: arena %zu bytes < %zu needed for window_blocks=%d; not even one layer per window fits",
                      arena_bytes, need, window_blocks);
   }
+  // host-side validation is complete; the pinned check is the first HIP call
+  for (int l = 0; l < n_layers; ++l) {
+    const int rc = check_pinned(l, host_blobs[l], blob_bytes[l]);
+    if (rc) return rc;
+  }
   msq_window* w = new msq_window();
   w->n_layers = n_layers;
   w->window_blocks = window_blocks;
   w->n_windows = (n_layers + window_blocks - 1) / window_blocks;
   w->host.assign(host_blobs, host_blobs + n_layers);
   w->bytes.assign(blob_bytes, blob_bytes + n_layers);
-  w->offset.resize(n_layers);
-  for (int f = 0; f < n_layers; f += window_blocks) {
-    size_t o = 0;
-    for (int l = f; l < f + window_blocks && l < n_layers; ++l) {
-      w->offset[l] = o;
-      o += align256(blob_bytes[l]);
-    }
-  }
+  const std::vector<size_t> psz = position_sizes(blob_bytes, n_layers, window_blocks);
+  w->pos_off.assign(window_blocks, 0);
+  for (int q = 1; q < window_blocks; ++q) w->pos_off[q] = w->pos_off[q - 1] + psz[q - 1];
   w->n_slots = n_slots;
   w->slot_bytes = need / n_slots;
   w->slot_base.resize(n_slots);
@@ -156,33 +270,25 @@ int block_stream_create(msq_window** out, const void* const* host_blobs, const s
   const int ne = n_slots * window_blocks;
   w->ready.assign(ne, nullptr);
   w->freed.assign(ne, nullptr);
+  w->ready_recorded.assign(ne, 0);
   w->freed_recorded.assign(ne, 0);
   w->release_order.assign(n_slots, std::vector<int>());
   w->released.assign(n_slots, std::vector<char>(window_blocks, 0));
   w->slot_window.assign(n_slots, -1);
   w->state.assign(n_slots, SLOT_FREE);
   w->release_tick.assign(n_slots, 0);
-  w->copy = (hipStream_t)copy_stream;
+  for (int i = 0; i < n_copy_streams; ++i) w->copies.push_back((hipStream_t)copy_streams[i]);
   hipError_t e = hipSuccess;
   for (int i = 0; i < ne && e == hipSuccess; ++i) {
     e = hipEventCreateWithFlags(&w->ready[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&w->freed[i], hipEventDisableTiming);
   }
-  for (int i = 0; i < msq_window::TIMING_RING && e == hipSuccess; ++i) {
-    e = hipEventCreate(&w->t_start[i]);
-    if (e == hipSuccess) e = hipEventCreate(&w->t_end[i]);
-  }
+  if (e == hipSuccess) e = hipEventCreate(&w->t_ref);
+  if (e == hipSuccess) e = hipEventRecord(w->t_ref, w->copies[0]);
   if (e != hipSuccess) {
-    for (int j = 0; j < ne; ++j) {
-      if (w->ready[j]) (void)hipEventDestroy(w->ready[j]);
-      if (w->freed[j]) (void)hipEventDestroy(w->freed[j]);
-    }
-    for (int j = 0; j < msq_window::TIMING_RING; ++j) {
-      if (w->t_start[j]) (void)hipEventDestroy(w->t_start[j]);
-      if (w->t_end[j]) (void)hipEventDestroy(w->t_end[j]);
-    }
+    destroy_events(w);
     delete w;
-    return hip_error(e, "block_stream_create: hipEventCreate");
+    return hip_error(e, "block_stream_create: events");
   }
   *out = w;
   return MSQ_OK;
@@ -208,7 +314,7 @@ int block_stream_prefetch(msq_window* w, int first_layer) {
     if (w->state[i] == SLOT_FREE && (slot < 0 || w->release_tick[i] < w->release_tick[slot])) slot = i;
   if (slot < 0)
     return set_error(MSQ_E_ORDER, "block_stream_prefetch: no free slot for window %d (release a window first)", win);
-  hipError_t e = hipSuccess;
+  hipError_t e = harvest(w, false);  // completed copies' timings, without waiting
   // the slot's old contents are about to be overwritten
   w->slot_window[slot] = -1;
   const int wb = w->window_blocks;
@@ -223,16 +329,20 @@ int block_stream_prefetch(msq_window* w, int first_layer) {
     if (q >= count || e != hipSuccess) continue;
     const int l = first_layer + q;
     const int ev = slot * wb + q;
-    if (w->freed_recorded[ev]) e = hipStreamWaitEvent(w->copy, w->freed[ev], 0);
-    const int ti = w->t_next;
-    w->t_next = (w->t_next + 1) % msq_window::TIMING_RING;
-    if (e == hipSuccess) e = collect_timing(w, ti);  // the ring's oldest pair, long complete
-    if (e == hipSuccess) e = hipEventRecord(w->t_start[ti], w->copy);
+    hipStream_t cs = w->copies[l % w->copies.size()];
+    // the position's range is free once the compute stream released its last layer and
+    // the previous copy into it (possibly on another copy stream) is done
+    if (w->freed_recorded[ev]) e = hipStreamWaitEvent(cs, w->freed[ev], 0);
+    if (e == hipSuccess && w->ready_recorded[ev]) e = hipStreamWaitEvent(cs, w->ready[ev], 0);
+    TimingPair tp;
+    if (e == hipSuccess) e = take_pair(w, &tp);
+    if (e == hipSuccess) e = hipEventRecord(tp.start, cs);
     if (e == hipSuccess)
-      e = hipMemcpyAsync(w->slot_base[slot] + w->offset[l], w->host[l], w->bytes[l], hipMemcpyHostToDevice, w->copy);
-    if (e == hipSuccess) e = hipEventRecord(w->t_end[ti], w->copy);
-    if (e == hipSuccess) w->t_pending[ti] = true;
-    if (e == hipSuccess) e = hipEventRecord(w->ready[ev], w->copy);
+      e = hipMemcpyAsync(w->slot_base[slot] + w->pos_off[q], w->host[l], w->bytes[l], hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipEventRecord(tp.end, cs);
+    if (e == hipSuccess) w->pending.push_back(tp);
+    if (e == hipSuccess) e = hipEventRecord(w->ready[ev], cs);
+    if (e == hipSuccess) w->ready_recorded[ev] = 1;
     total += w->bytes[l];
   }
   if (e != hipSuccess) return hip_error(e, "block_stream_prefetch: copy");
@@ -251,10 +361,10 @@ int block_stream_acquire(msq_window* w, int layer, msq_stream_t compute, const v
   const int win = layer / w->window_blocks;
   const int slot = find_slot(w, win, SLOT_HELD);
   if (slot < 0) return set_error(MSQ_E_ORDER, "block_stream_acquire: window %d (layer %d) was not prefetched", win, layer);
-  const hipError_t e =
-      hipStreamWaitEvent((hipStream_t)compute, w->ready[slot * w->window_blocks + layer % w->window_blocks], 0);
+  const int q = layer % w->window_blocks;
+  const hipError_t e = hipStreamWaitEvent((hipStream_t)compute, w->ready[slot * w->window_blocks + q], 0);
   if (e != hipSuccess) return hip_error(e, "block_stream_acquire: hipStreamWaitEvent");
-  *dev_blob = w->slot_base[slot] + w->offset[layer];
+  *dev_blob = w->slot_base[slot] + w->pos_off[q];
   return MSQ_OK;
 }
 
@@ -311,10 +421,12 @@ int block_stream_release_layer(msq_window* w, int layer, msq_stream_t compute) {
 
 int block_stream_stats(msq_window* w, msq_window_stats* out) {
   if (!w || !out) return set_error(MSQ_E_INVAL, "block_stream_stats: null pointer");
-  for (int i = 0; i < msq_window::TIMING_RING; ++i) {
-    const hipError_t e = collect_timing(w, i);
-    if (e != hipSuccess) return hip_error(e, "block_stream_stats: copy timing");
-  }
+  hipError_t e = harvest(w, true);
+  if (e != hipSuccess) return hip_error(e, "block_stream_stats: copy timing");
+  w->stats.busy_ms += merge_spans(w, 0);
+  // every copy issued so far is done: later spans are measured from a fresh reference
+  e = hipEventRecord(w->t_ref, w->copies[0]);
+  if (e != hipSuccess) return hip_error(e, "block_stream_stats: hipEventRecord");
   *out = w->stats;
   return MSQ_OK;
 }
@@ -322,20 +434,44 @@ int block_stream_stats(msq_window* w, msq_window_stats* out) {
 int block_stream_destroy(msq_window* w) {
   if (!w) return MSQ_OK;
   hipError_t e = hipSuccess;
-  for (size_t i = 0; i < w->ready.size(); ++i) {
-    if (w->ready[i]) {
+  for (size_t i = 0; i < w->ready.size(); ++i)
+    if (w->ready[i] && w->ready_recorded[i]) {
       const hipError_t e1 = hipEventSynchronize(w->ready[i]);
       if (e == hipSuccess) e = e1;
-      (void)hipEventDestroy(w->ready[i]);
     }
-    if (w->freed[i]) (void)hipEventDestroy(w->freed[i]);
-  }
-  for (int i = 0; i < msq_window::TIMING_RING; ++i) {
-    if (w->t_start[i]) (void)hipEventDestroy(w->t_start[i]);
-    if (w->t_end[i]) (void)hipEventDestroy(w->t_end[i]);
-  }
+  destroy_events(w);
   delete w;
   return e == hipSuccess ? MSQ_OK : hip_error(e, "block_stream_destroy");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int msq_host_alloc(size_t bytes, void** out) {
+  if (!out) return set_error(MSQ_E_INVAL, "msq_host_alloc: out is NULL");
+  *out = nullptr;
+  if (bytes == 0 || bytes > ((size_t)1 << 46))
+    return set_error(MSQ_E_INVAL, "msq_host_alloc: bytes=%zu outside [1, 2^46]", bytes);
+  void* p = nullptr;
+  const hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(MSQ_E_HIP, "msq_host_alloc: hipHostMalloc of %zu bytes: %s (%d)", bytes, hipGetErrorString(e),
+                     (int)e);
+  }
+  if ((uintptr_t)p % 256) {
+    (void)hipHostFree(p);
+    return set_error(MSQ_E_HIP, "msq_host_alloc: hipHostMalloc returned %p, not 256-byte aligned", p);
+  }
+  *out = p;
+  return MSQ_OK;
+}
+
+int msq_host_free(void* p) {
+  if (!p) return MSQ_OK;
+  const hipError_t e = hipHostFree(p);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "msq_host_free");
 }
 
 }  // extern "C"

@@ -9,6 +9,7 @@ allocated with torch on the input's device.
 from __future__ import annotations
 
 import ctypes
+import sys
 from dataclasses import dataclass
 from typing import Optional, Sequence, Tuple
 
@@ -492,18 +493,36 @@ def nf4_stream_load(jobs: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tenso
     del staging, bounce
     return {"device_bytes": dev_need, "host_bytes": host_need, "chunk_rows": chunk_rows}
 
+def pinned_empty(nbytes: int) -> torch.Tensor:
+    """A uint8 CPU tensor of nbytes in pinned host memory from msq_host_alloc: exactly that
+    size (torch's pinned allocator rounds each block up to a power of two).  The memory is
+    released with msq_host_free when the last view of the tensor is gone."""
+    nbytes = int(nbytes)
+    p = ctypes.c_void_p()
+    check("msq_host_alloc", lib().msq_host_alloc(nbytes, ctypes.byref(p)))
+    addr = int(p.value)
+
+    def _release(_self, addr=addr):
+        if not sys.is_finalizing():
+            lib().msq_host_free(addr)
+
+    owner = type("PinnedHostBytes", (ctypes.c_uint8 * nbytes,), {"__del__": _release}).from_address(addr)
+    return torch.frombuffer(owner, dtype=torch.uint8)
+
+
 class BlockStreamWindow:
-    """block_stream_* over pinned host blobs and a caller-owned device arena."""
+    """block_stream_* over pinned host blobs and a caller-owned device arena; layer l is
+    copied on copy_streams[l % len(copy_streams)]."""
 
     def __init__(self, host_blobs: Sequence[torch.Tensor], window_blocks: int, n_slots: int = 2,
                  arena: Optional[torch.Tensor] = None, copy_stream: Optional[torch.cuda.Stream] = None,
-                 device=None):
+                 device=None, copy_streams: Optional[Sequence[torch.cuda.Stream]] = None):
         self.n_layers = len(host_blobs)
         self.window_blocks = int(window_blocks)
         self.n_slots = int(n_slots)
         for i, b in enumerate(host_blobs):
-            if b.device.type != "cpu" or not b.is_pinned() or b.dtype != torch.uint8 or not b.is_contiguous():
-                raise ValueError(f"host blob {i} must be a contiguous pinned uint8 CPU tensor")
+            if b.device.type != "cpu" or b.dtype != torch.uint8 or not b.is_contiguous():
+                raise ValueError(f"host blob {i} must be a contiguous uint8 CPU tensor (in pinned memory)")
         self.host_blobs = list(host_blobs)
         self._ptrs = (ctypes.c_void_p * self.n_layers)(*[b.data_ptr() for b in host_blobs])
         self._sizes = (ctypes.c_size_t * self.n_layers)(*[b.numel() for b in host_blobs])
@@ -518,11 +537,15 @@ class BlockStreamWindow:
         if arena.device.type != "cuda" or arena.dtype != torch.uint8:
             raise ValueError("arena must be a device uint8 tensor")
         self.arena = arena
-        self.copy_stream = copy_stream or torch.cuda.Stream(device=arena.device)
+        if copy_streams is None:
+            copy_streams = [copy_stream or torch.cuda.Stream(device=arena.device)]
+        self.copy_streams = list(copy_streams)
+        self.copy_stream = self.copy_streams[0]
+        self._streams = (ctypes.c_void_p * len(self.copy_streams))(*[cs.cuda_stream for cs in self.copy_streams])
         h = ctypes.c_void_p()
         check("block_stream_create", lib().block_stream_create(
             ctypes.byref(h), self._ptrs, self._sizes, self.n_layers, self.window_blocks, self.n_slots,
-            arena.data_ptr(), arena.numel(), self.copy_stream.cuda_stream))
+            arena.data_ptr(), arena.numel(), self._streams, len(self.copy_streams)))
         self._h = h
 
     def prefetch(self, first_layer: int) -> None:
@@ -550,7 +573,8 @@ class BlockStreamWindow:
         s = _abi.WindowStats()
         check("block_stream_stats", lib().block_stream_stats(self._h, ctypes.byref(s)))
         return {"bytes_copied": s.bytes_copied, "windows_copied": s.windows_copied,
-                "windows_reused": s.windows_reused, "copy_ms": s.copy_ms, "copies_timed": s.copies_timed}
+                "windows_reused": s.windows_reused, "copy_ms": s.copy_ms, "copies_timed": s.copies_timed,
+                "busy_ms": s.busy_ms}
 
     def close(self) -> None:
         if getattr(self, "_h", None):

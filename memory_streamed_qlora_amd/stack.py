@@ -296,6 +296,23 @@ def causal_gqa_attention(q, k, v, mask_rep):
     return o.view(H, T, D).permute(1, 0, 2).reshape(T, H * D)
 
 
+_COPY_STREAMS: Dict[Tuple[int, int], torch.cuda.Stream] = {}
+
+
+def copy_streams(device, n: int) -> List[torch.cuda.Stream]:
+    """n copy streams of a device, shared by every stack of the process: a stream keeps the
+    hardware queue it was first given, so fresh streams per stack could end up sharing the
+    compute stream's queue once earlier stacks hold the others."""
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    out = []
+    for i in range(n):
+        if (idx, i) not in _COPY_STREAMS:
+            _COPY_STREAMS[(idx, i)] = torch.cuda.Stream(device=torch.device("cuda", idx))
+        out.append(_COPY_STREAMS[(idx, i)])
+    return out
+
+
 @dataclass
 class StepResult:
     loss: float
@@ -310,7 +327,7 @@ class Stack:
     def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
                  window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
                  n_slots: int = 2, glue: str = "native", base: str = "nf4", group: bool = True,
-                 layer_release: bool = True, lm_stream: Optional[bool] = None):
+                 layer_release: bool = True, lm_stream: Optional[bool] = None, n_copy_streams: int = 2):
         assert mode in ("streamed", "resident")
         assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
@@ -323,6 +340,7 @@ class Stack:
         self.cfg = ops.Lora(r, alpha, p_drop)
         self.window_blocks = window_blocks
         self.n_slots = n_slots
+        self.n_copy_streams = n_copy_streams
         self.dev = torch.device(device or "cuda")
         self.layout = LayerLayout(shape, base)
         self.host_blobs: List[torch.Tensor] = []
@@ -349,7 +367,7 @@ class Stack:
         if self.mode == "resident":
             self.dev_blobs.append(blob_dev)
         else:
-            host = torch.empty(blob_dev.numel(), dtype=torch.uint8, pin_memory=True)
+            host = ops.pinned_empty(blob_dev.numel())
             host.copy_(blob_dev)
             self.host_blobs.append(host)
 
@@ -379,7 +397,7 @@ class Stack:
         device."""
         self.emb = emb.detach().to("cpu", torch.bfloat16).contiguous()
         if self.lm_stream:
-            self.lm_host = torch.empty(lm.shape, dtype=torch.bfloat16, pin_memory=True)
+            self.lm_host = ops.pinned_empty(lm.numel() * 2).view(torch.bfloat16).view(lm.shape)
             self.lm_host.copy_(lm)
             self.lm = None
             rows = min(self.LM_CHUNK, lm.shape[0])
@@ -408,10 +426,11 @@ class Stack:
         groups = [{"params": list(self.A[l].values()) + list(self.B[l].values())} for l in range(len(self.A))]
         self.opt = torch.optim.AdamW(groups, lr=LR, betas=BETAS, eps=ADAM_EPS, weight_decay=WD, foreach=True)
         if self.mode == "streamed" or self.lm_stream:
-            self.copy_stream = torch.cuda.Stream(device=self.dev)
+            self.copy_streams = copy_streams(self.dev, self.n_copy_streams)
+            self.copy_stream = self.copy_streams[0]
         if self.mode == "streamed":
             self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks, self.n_slots,
-                                                copy_stream=self.copy_stream, device=self.dev)
+                                                copy_streams=self.copy_streams, device=self.dev)
 
     @classmethod
     def random(cls, shape: Shape, seq: int, seed: int = 0, cfg_id: int = 0, w_std: float = 0.02,
@@ -491,7 +510,7 @@ class Stack:
         blobs = []
         for l in range(L):
             if loader == "streamed":
-                blob = torch.zeros(layout.nbytes, dtype=torch.uint8, pin_memory=True)
+                blob = ops.pinned_empty(layout.nbytes).zero_()
                 v = layout.views(blob)
                 ops.nf4_stream_load([(source(cls.tensor_name(l, p)), v[(p, "codes")], v[(p, "absmax")])
                                      for p in PROJS], chunk_bytes=chunk_bytes, host_threads=host_threads,
@@ -501,7 +520,7 @@ class Stack:
                 vd = layout.views(blob_dev)
                 for p in PROJS:
                     ops.nf4_quantize(W_dev.pop((l, p)), vd[(p, "codes")], vd[(p, "absmax")])
-                blob = torch.zeros(layout.nbytes, dtype=torch.uint8, pin_memory=True)
+                blob = ops.pinned_empty(layout.nbytes)
                 blob.copy_(blob_dev)
                 del blob_dev
                 v = layout.views(blob)

@@ -249,15 +249,70 @@ def test_window_rejects_small_arena_and_names_what_fits():
     assert L.block_stream_arena_bytes(sizes, n, 2, 3) == 3 * 2 * 1000 * 256
     assert L.block_stream_arena_bytes(sizes, n, 4, 1) == 0
     h = ctypes.c_void_p()
-    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need - 1, None)
+    cs = (ctypes.c_void_p * 2)(None, None)  # default streams: nothing here reaches a HIP call
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need - 1, cs, 2)
     assert rc == abi.MSQ_E_WINDOW
     assert "window_blocks=3" in _err()
-    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, 1000, None)
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, 1000, cs, 1)
     assert rc == abi.MSQ_E_WINDOW and "not even one layer" in _err()
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 9, 2, FAKE, need, None) == abi.MSQ_E_INVAL
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 1, FAKE, need, None) == abi.MSQ_E_INVAL
-    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE + 16, need, None) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 9, 2, FAKE, need, cs, 2) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 1, FAKE, need, cs, 2) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE + 16, need, cs, 2) == abi.MSQ_E_INVAL
+    # the copy streams: an array of 1 .. MSQ_MAX_COPY_STREAMS
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need, None, 1) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need, cs, 0) == abi.MSQ_E_INVAL
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 4, 2, FAKE, need, cs, 5) == abi.MSQ_E_INVAL
+    assert "n_copy_streams=5" in _err()
     assert L.block_stream_prefetch(None, 0) == abi.MSQ_E_INVAL
+
+
+def test_window_positions_have_fixed_ranges():
+    """Position q of a slot is as large as the largest layer any window puts at position q,
+    so the ranges of different positions never overlap whatever the sizes: with layers of
+    4096 + 256 i bytes in windows of 3, a slot is 4096+256*6 + 4096+256*7 + 4096+256*8
+    (the last window's layers, the largest at each position)."""
+    L = abi.lib()
+    n = 9
+    sizes = (ctypes.c_size_t * n)(*[4096 + 256 * i for i in range(n)])
+    assert L.block_stream_arena_bytes(sizes, n, 3, 2) == 2 * sum(4096 + 256 * i for i in (6, 7, 8))
+    # a short last window: 7 layers in windows of 3 -> positions sized by layers 6, 4, 5
+    assert L.block_stream_arena_bytes(sizes, 7, 3, 2) == 2 * sum(4096 + 256 * i for i in (6, 4, 5))
+    # sizes are rounded up to 256 bytes per position
+    odd = (ctypes.c_size_t * 4)(1000, 10, 300, 1)
+    assert L.block_stream_arena_bytes(odd, 4, 2, 3) == 3 * (1024 + 256)   # max(1000, 300), max(10, 1)
+    # one byte short of the fixed layout is too small, and the message names what fits
+    need = L.block_stream_arena_bytes(sizes, n, 3, 2)
+    h = ctypes.c_void_p()
+    cs = (ctypes.c_void_p * 1)(None)
+    ptrs = (ctypes.c_void_p * n)(*([FAKE] * n))
+    assert L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 3, 2, FAKE, need - 1, cs, 1) == abi.MSQ_E_WINDOW
+    assert "window_blocks=2" in _err()
+
+
+def test_window_checks_blobs_are_pinned():
+    """A blob in ordinary (pageable) host memory is refused once every other argument has
+    passed: MSQ_E_INVAL where the HIP runtime can tell, MSQ_E_HIP where it cannot (no GPU
+    here); either way no window is created."""
+    L = abi.lib()
+    n = 2
+    bufs = [ctypes.create_string_buffer(4096) for _ in range(n)]
+    ptrs = (ctypes.c_void_p * n)(*[ctypes.addressof(b) for b in bufs])
+    sizes = (ctypes.c_size_t * n)(4096, 4096)
+    need = L.block_stream_arena_bytes(sizes, n, 1, 2)
+    h = ctypes.c_void_p(12345)
+    cs = (ctypes.c_void_p * 1)(None)
+    rc = L.block_stream_create(ctypes.byref(h), ptrs, sizes, n, 1, 2, FAKE, need, cs, 1)
+    assert rc in (abi.MSQ_E_INVAL, abi.MSQ_E_HIP)
+    assert "pinned" in _err() and h.value is None
+
+
+def test_host_alloc_rejects_bad_sizes():
+    L = abi.lib()
+    p = ctypes.c_void_p()
+    assert L.msq_host_alloc(0, ctypes.byref(p)) == abi.MSQ_E_INVAL
+    assert L.msq_host_alloc(1 << 47, ctypes.byref(p)) == abi.MSQ_E_INVAL
+    assert L.msq_host_alloc(4096, None) == abi.MSQ_E_INVAL
+    assert L.msq_host_free(None) == abi.MSQ_OK
 
 
 def test_timing_collect_without_records():

@@ -319,10 +319,74 @@ def test_window_per_layer_release():
     assert e.value.code == MSQ_E_ORDER
     s = w.stats()
     assert s["windows_copied"] == 3 and s["windows_reused"] == 1 and s["copies_timed"] == 9
-    assert s["copy_ms"] > 0
+    assert 0 < s["busy_ms"] <= s["copy_ms"] * (1 + 1e-6)
     w.release(3)
     w.release(6)
     w.close()
+
+
+@pytest.mark.parametrize("n_streams", [1, 2, 3])
+def test_window_copy_streams(n_streams):
+    """Layers of unequal sizes (1 MiB + 4 KiB * i) in windows of 2 over 3 slots, spread over
+    one or several copy streams (layer l on stream l % n), each read on the compute stream
+    right after its acquire and released at once, through a forward-like and a
+    backward-like sweep with slot reuse and per-layer refills: every read sees the layer's
+    bytes.  With unequal sizes each position of a slot keeps one byte range for every
+    window, so a copy never overwrites a range another position's layer is still read
+    from.  The busy time is the union of the copies' spans."""
+    blobs = []
+    for i in range(12):
+        b = msq.ops.pinned_empty((1 << 20) + 4096 * i)
+        b.copy_(torch.arange(b.numel(), dtype=torch.int64).mul_(5).add_(13 * i).remainder_(241).to(torch.uint8))
+        blobs.append(b)
+    assert all(b.is_pinned() for b in blobs)
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+    w = msq.BlockStreamWindow(blobs, 2, n_slots=3, copy_streams=streams)
+    compute = torch.cuda.current_stream()
+    out = torch.empty(sum(b.numel() for b in blobs) * 2, dtype=torch.uint8, device="cuda")
+    o = 0
+    for rnd in range(2):                            # a forward-like then a backward-like sweep
+        starts = list(range(0, 12, 2) if rnd == 0 else range(10, -1, -2))
+        for f in starts[:3]:
+            w.prefetch(f)
+        for i, f in enumerate(starts):
+            for l in (f, f + 1) if rnd == 0 else (f + 1, f):
+                v = w.acquire_view(l)
+                out[o:o + v.numel()].copy_(v)       # read on the compute stream after the wait
+                o += v.numel()
+                w.release_layer(l, compute)
+            if i + 3 < len(starts):
+                w.prefetch(starts[i + 3])
+    torch.cuda.synchronize()
+    o = 0
+    for rnd in range(2):
+        ls = [l for f in range(0, 12, 2) for l in (f, f + 1)] if rnd == 0 else \
+             [l for f in range(10, -1, -2) for l in (f + 1, f)]
+        for l in ls:
+            assert torch.equal(out[o:o + blobs[l].numel()].cpu(), blobs[l]), (rnd, l)
+            o += blobs[l].numel()
+    s = w.stats()
+    assert s["windows_copied"] + s["windows_reused"] == 12 and s["windows_reused"] == 3
+    assert 0 < s["busy_ms"] <= s["copy_ms"] * (1 + 1e-6)
+    w.close()
+
+
+def test_window_refuses_pageable_blobs():
+    blobs = [torch.zeros(8192, dtype=torch.uint8) for _ in range(4)]   # ordinary host memory
+    with pytest.raises(MsqError) as e:
+        msq.BlockStreamWindow(blobs, 2)
+    assert e.value.code == msq._abi.MSQ_E_INVAL and "pinned" in str(e.value)
+
+
+def test_pinned_empty_is_exact_pinned_memory():
+    t = msq.ops.pinned_empty(3 * (1 << 20) + 256)
+    assert t.numel() == 3 * (1 << 20) + 256 and t.is_pinned() and t.data_ptr() % 256 == 0
+    t.fill_(9)
+    d = torch.empty(t.numel(), dtype=torch.uint8, device="cuda")
+    d.copy_(t, non_blocking=True)
+    torch.cuda.synchronize()
+    assert int(d.sum()) == 9 * t.numel()
+    del t
 
 
 def test_selective_recompute_gives_identical_gradients():
