@@ -10,7 +10,8 @@ package README, "How it works"):
   backward  windows in reverse: reload, recompute each block's forward with the same
             dropout keys (the counter-based masks replay exactly), then differentiate
             the adapters and the block input only
-  update    one AdamW step on the fp32 adapters, identical to the resident run's.
+  update    one AdamW step on the fp32 adapters, identical to the resident run's; each
+            layer's step runs as soon as its gradients are final, inside the backward.
 Resident mode runs the same code with every layer's blob already in device memory.
 Gradient accumulation over M micro-batches runs micro-batch by micro-batch or
 block-major (every micro-batch through a window before the next window), with the
@@ -359,7 +360,7 @@ class Stack:
         self.cos, self.sin = rope_tables(seq, shape.head_dim, self.dev)
         self.mask_add = torch.triu(torch.full((seq, seq), float("-inf"), device=self.dev), 1)
         self._mask_reps: Dict[int, torch.Tensor] = {}
-        self.opt: Optional[torch.optim.Optimizer] = None
+        self.opts: List[torch.optim.Optimizer] = []
         self.step_index = 0
 
     # -- construction ------------------------------------------------------------
@@ -420,11 +421,12 @@ class Stack:
         return rows.to(self.dev, non_blocking=True).float()
 
     def finalize(self) -> None:
-        # one parameter group per layer: the foreach update then allocates its temporaries
-        # one layer at a time instead of for all adapters at once (the per-element arithmetic
-        # is the same either way)
-        groups = [{"params": list(self.A[l].values()) + list(self.B[l].values())} for l in range(len(self.A))]
-        self.opt = torch.optim.AdamW(groups, lr=LR, betas=BETAS, eps=ADAM_EPS, weight_decay=WD, foreach=True)
+        # one AdamW per layer: a layer's update can run as soon as its gradients are final
+        # (inside the backward, overlapping the window's copies), and its foreach
+        # temporaries are one layer's; the per-element arithmetic is that of one optimizer
+        # over all adapters
+        self.opts = [torch.optim.AdamW(list(self.A[l].values()) + list(self.B[l].values()), lr=LR, betas=BETAS,
+                                       eps=ADAM_EPS, weight_decay=WD, foreach=True) for l in range(len(self.A))]
         if self.mode == "streamed" or self.lm_stream:
             self.copy_streams = copy_streams(self.dev, self.n_copy_streams)
             self.copy_stream = self.copy_streams[0]
@@ -623,13 +625,15 @@ class Stack:
         return self._forward_backward([tokens], step, [micro], 1.0)[0]
 
     def _forward_backward(self, toks: List[torch.Tensor], step: int, micros: List[int],
-                          scale: float) -> List[torch.Tensor]:
+                          scale: float, update_layers: bool = False) -> List[torch.Tensor]:
         """Block-major pass over the micro-batches toks (dropout keys micros): each window is
         fetched once and runs every micro-batch before the next window, forward and
         backward.  Streamed, each layer is acquired just before its first use and released
         right after its last, so a window's slot refills layer by layer.  Each micro-batch's loss is scaled by `scale` before its backward (1.0:
         no scaling op); gradients accumulate into .grad, for every adapter in micro-batch
-        order.  Returns the unscaled losses."""
+        order.  update_layers: run each layer's AdamW step as soon as the last micro-batch's
+        backward of that layer is done (its gradients are then final).  Returns the
+        unscaled losses."""
         L = self.shape.layers
         M = len(toks)
         wins = self._windows()
@@ -686,6 +690,8 @@ class Stack:
                     bounds[m][l] = None
                     if streamed and m == M - 1 and self.layer_release:
                         self.window.release_layer(l)
+                    if update_layers and m == M - 1:
+                        self.opts[l].step()
             if streamed and not self.layer_release:
                 self.window.release(w)
             if streamed and wi + ahead < len(rw):
@@ -828,22 +834,27 @@ class Stack:
         and every adapter gradient is summed in micro-batch order."""
         if order not in ("micro", "block"):
             raise ValueError(f"order must be 'micro' or 'block', got {order!r}")
-        self.opt.zero_grad(set_to_none=True)
+        for opt in self.opts:
+            opt.zero_grad(set_to_none=True)
+        updated = True  # each layer's AdamW ran inside the backward
         if tokens.dim() == 1:
-            loss = self.forward_backward(tokens, self.step_index)
+            loss = self._forward_backward([tokens], self.step_index, [0], 1.0, update_layers=True)[0]
         else:
             M = tokens.shape[0]
             scale = 1.0 / M
             if order == "micro":
                 losses = [self._forward_backward([tokens[m]], self.step_index, [m], scale)[0] for m in range(M)]
+                updated = False
             else:
                 losses = self._forward_backward([tokens[m] for m in range(M)], self.step_index, list(range(M)),
-                                                scale)
+                                                scale, update_layers=True)
             loss = losses[0] * scale
             for lm in losses[1:]:
                 loss = loss + lm * scale
         gn = self.grad_norm()
-        self.opt.step()
+        if not updated:
+            for opt in self.opts:
+                opt.step()
         self.step_index += 1
         return loss, gn
 
@@ -857,7 +868,7 @@ class Stack:
                     out[f"{l}.{p}.{nm}"] = prm.detach()
                     if prm.grad is not None:
                         out[f"{l}.{p}.{nm}.grad"] = prm.grad.detach()
-                    st = self.opt.state.get(prm, {})
+                    st = self.opts[l].state.get(prm, {})
                     for sk in ("exp_avg", "exp_avg_sq"):
                         if sk in st:
                             out[f"{l}.{p}.{nm}.{sk}"] = st[sk].detach()
