@@ -60,9 +60,12 @@ def measured_traffic(kernel: str):
 
 
 # Qwen2.5 stacks of the workloads: (hidden, heads, kv heads, head dim, intermediate, layers,
-# dropout, default window slots)
+# dropout, default window slots).  The 32B and 72B slot counts are the deepest prefetch whose
+# peak stays under the pages' streamed peaks for those sizes (10.95 GB, A100 results,
+# Benchmark matrix; 18.87 GB, "Poros" research post, memory paragraph); the 7B stack keeps
+# the plain double buffer (7 slots would hold all 28 of its layers).
 SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, 2), "32b": (5120, 40, 8, 128, 27648, 64, 0.0, 7),
-          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, 2)}
+          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, 7)}
 
 PROJ_NAMES = {(5120, 5120): "q/o", (1024, 5120): "k/v", (27648, 5120): "gate/up", (5120, 27648): "down",
               (7168, 5120): "q+k+v", (55296, 5120): "gate+up"}
@@ -476,8 +479,8 @@ def main() -> int:
     ap.add_argument("--window-blocks", type=int, default=4,
                     help="layers per window slot (blocks per streamed window)")
     ap.add_argument("--slots", type=int, default=None,
-                    help="window slots in the device arena (default 7 at 32b: the deepest prefetch whose peak "
-                         "device memory stays under the pages' 10.95 GB streamed peak; 2 at 7b and 72b)")
+                    help="window slots in the device arena (default 7 at 32b and 72b: the deepest prefetch whose "
+                         "peak stays under the pages' streamed peaks, 10.95 and 18.87 GB; 2 at 7b)")
     ap.add_argument("--copy-streams", type=int, default=2, help="copy streams of the window (layer l on stream l mod n)")
     ap.add_argument("--no-resident", action="store_true",
                     help="skip the resident leg (the same step with the whole base in device memory)")
