@@ -1,9 +1,10 @@
 """Benchmark: streamed NF4 + LoRA training step of a Qwen2.5-32B-shaped stack on one GPU.
 
 Workload: 64 decoder layers (hidden 5120, 40/8 heads, SwiGLU 27648), random N(0, 0.02)
-base quantized to NF4 and held in pinned host memory, streamed in windows of 4 blocks
-through a device arena of 7 window slots (one computing, the others prefetching), the
-frozen lm_head streamed from pinned host memory by the loss; LoRA r16
+base quantized to NF4 and held in pinned host memory, streamed in windows of 2 blocks
+through a device arena of 14 window slots (one computing, the others prefetching or kept
+for the turnaround), the frozen lm_head streamed from pinned host memory by the loss, each
+layer's adapter gradients dropped after its AdamW step; LoRA r16
 alpha32 dropout 0.0 on all seven projections;
 batch 1 x 512 random tokens over a 152064-entry vocabulary; one AdamW step per
 training step.  A step is the whole hot path: forward with streaming, loss, backward
@@ -60,12 +61,14 @@ def measured_traffic(kernel: str):
 
 
 # Qwen2.5 stacks of the workloads: (hidden, heads, kv heads, head dim, intermediate, layers,
-# dropout, default window slots).  The 32B and 72B slot counts are the deepest prefetch whose
-# peak stays under the pages' streamed peaks for those sizes (10.95 GB, A100 results,
-# Benchmark matrix; 18.87 GB, "Poros" research post, memory paragraph); the 7B stack keeps
-# the plain double buffer (7 slots would hold all 28 of its layers).
-SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, 2), "32b": (5120, 40, 8, 128, 27648, 64, 0.0, 7),
-          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, 7)}
+# dropout, default window: layers per slot, slots, checkpoint every n layers).  The 32B and
+# 72B windows hold the most layers whose peak stays under the pages' streamed peaks for those
+# sizes (10.95 GB, A100 results, Benchmark matrix; 18.87 GB, "Poros" research post, memory
+# paragraph); the 7B stack keeps the plain double buffer of 4-layer windows (7 slots would
+# hold all 28 of its layers).
+SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, (4, 2, 1)),
+          "32b": (5120, 40, 8, 128, 27648, 64, 0.0, (2, 14, 1)),
+          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, (4, 7, 1))}
 
 PROJ_NAMES = {(5120, 5120): "q/o", (1024, 5120): "k/v", (27648, 5120): "gate/up", (5120, 27648): "down",
               (7168, 5120): "q+k+v", (55296, 5120): "gate+up"}
@@ -476,11 +479,17 @@ def main() -> int:
     ap.add_argument("--shape", choices=tuple(SHAPES), default="32b",
                     help="Qwen2.5 stack shape: 32b (the headline), 7b or 72b (dropout 0.1, as their workloads state)")
     ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the shape's)")
-    ap.add_argument("--window-blocks", type=int, default=4,
-                    help="layers per window slot (blocks per streamed window)")
+    ap.add_argument("--window-blocks", type=int, default=None,
+                    help="layers per window slot (default: 2 at 32b, 4 at 7b and 72b)")
+    ap.add_argument("--checkpoint-every", type=int, default=None,
+                    help="the streamed step keeps every n-th layer's input for the backward and recomputes "
+                         "the others (default 1; must divide --window-blocks)")
+    ap.add_argument("--keep-grads", action="store_true",
+                    help="keep every adapter gradient until the step ends (default: a layer's gradients are "
+                         "dropped once its AdamW step inside the backward has used them)")
     ap.add_argument("--slots", type=int, default=None,
-                    help="window slots in the device arena (default 7 at 32b and 72b: the deepest prefetch whose "
-                         "peak stays under the pages' streamed peaks, 10.95 and 18.87 GB; 2 at 7b)")
+                    help="window slots in the device arena (default 14 at 32b, 7 at 72b: the most resident "
+                         "layers whose peak stays under the pages' streamed peaks, 10.95 and 18.87 GB; 2 at 7b)")
     ap.add_argument("--copy-streams", type=int, default=2, help="copy streams of the window (layer l on stream l mod n)")
     ap.add_argument("--no-resident", action="store_true",
                     help="skip the resident leg (the same step with the whole base in device memory)")
@@ -521,9 +530,11 @@ def main() -> int:
     from memory_streamed_qlora_amd import ops, stack as S
 
     torch.cuda.set_device(0)
-    hid, heads, kvh, hd, inter, nl, p_drop, slots_default = SHAPES[args.shape]
+    hid, heads, kvh, hd, inter, nl, p_drop, (wb_default, slots_default, ckpt_default) = SHAPES[args.shape]
     layers = args.layers or nl
     slots = args.slots or slots_default
+    wblocks = args.window_blocks or wb_default
+    ckpt = args.checkpoint_every or (ckpt_default if wblocks % ckpt_default == 0 else 1)
     shape = S.Shape(hid, heads, kvh, hd, inter, layers)
     size = args.shape.upper()
     T = 512
@@ -542,14 +553,16 @@ def main() -> int:
             return S.random_tokens(0, s, T, shape.vocab, "cpu")
         return torch.stack([S.random_tokens(0, s * args.ga + m, T, shape.vocab, "cpu") for m in range(args.ga)])
 
-    def run(mode: str, kernel_timing: bool, n_slots: int):
+    def run(mode: str, kernel_timing: bool, window_blocks: int, n_slots: int, checkpoint_every: int):
         t_build = time.time()
         st = S.Stack.random(shape, T, seed=0, cfg_id=4, r=16, alpha=32.0, p_drop=p_drop,
-                            window_blocks=args.window_blocks, n_slots=n_slots, mode=mode, glue=args.glue,
+                            window_blocks=window_blocks, n_slots=n_slots, mode=mode, glue=args.glue,
                             base=args.base, layer_release=not args.window_release,
-                            lm_stream=mode == "streamed" and not args.lm_resident, n_copy_streams=args.copy_streams)
+                            lm_stream=mode == "streamed" and not args.lm_resident, n_copy_streams=args.copy_streams,
+                            keep_grads=args.keep_grads, checkpoint_every=checkpoint_every)
         torch.cuda.synchronize()
-        log(f"{mode} ({args.window_blocks} x {n_slots}): built {layers} layers in {time.time() - t_build:.1f}s "
+        log(f"{mode} ({window_blocks} x {n_slots}, checkpoints every {checkpoint_every}): built {layers} layers "
+            f"in {time.time() - t_build:.1f}s "
             f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
         for w in range(args.warmup):
             loss, gn = st.train_step(batch(st, w), order=args.order)
@@ -559,6 +572,9 @@ def main() -> int:
         stats0 = st.window.stats() if st.window else None
         st.lm_copy_timing = st.lm_host is not None
         st.lm_copy_stats()
+        # the build's device temporaries leave the allocator's cache, so the reserved peak
+        # below is the step's own
+        torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
         ops.timing_enable(kernel_timing)
         ops.timing_collect()
@@ -601,10 +617,12 @@ def main() -> int:
     # The streamed step carries the per-launch event timing the roofline needs (its host
     # issue time stays far below the copy-bound step).  The other legs are timed without it:
     # in the resident step the extra host work per launch would make the step host-bound.
-    streamed = run("streamed", not args.no_kernel_timing, slots)
-    literal = (run("streamed", False, 2) if args.shape == "32b" and slots != 2 and not args.no_literal_window
-               else None)
-    resident = run("resident", False, 2) if not args.no_resident else None
+    streamed = run("streamed", not args.no_kernel_timing, wblocks, slots, ckpt)
+    literal = (run("streamed", False, 4, 2, 1)
+               if args.shape == "32b" and (wblocks, slots) != (4, 2) and not args.no_literal_window else None)
+    # the resident step keeps every checkpoint (it has the memory): its losses must still
+    # equal the streamed step's bit for bit
+    resident = run("resident", False, 4, 2, 1) if not args.no_resident else None
 
     ms = streamed["seconds"] / args.steps * 1e3
     value = T * args.ga * args.steps / streamed["seconds"]
@@ -647,13 +665,17 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (random N(0,0.02) NF4 base, random adapters, random tokens)",
         "config": {"workload": (f"Qwen2.5-{size}-shaped streamed NF4+LoRA train step, windows of "
-                                f"{args.window_blocks} layers x {slots} slots"),
+                                f"{wblocks} layers x {slots} slots"
+                                + (f", checkpoints every {ckpt} layers" if ckpt > 1 else "")),
                    "layers": layers, "hidden": hid, "heads": heads, "kv_heads": kvh, "intermediate": inter,
                    "vocab": 152064, "seq_len": T, "batch": 1, "micro_batches": args.ga,
                    **({"accumulation_order": args.order} if args.ga > 1 else {}),
-                   "window_layers_per_slot": args.window_blocks, "window_slots": slots,
-                   "window_layers_resident": args.window_blocks * slots, "copy_streams": args.copy_streams,
-                   "lora_r": 16, "lora_alpha": 32, "dropout": p_drop, "optimizer": "AdamW", "base": args.base,
+                   "window_layers_per_slot": wblocks, "window_slots": slots,
+                   "window_layers_resident": wblocks * slots, "checkpoint_every": ckpt,
+                   "copy_streams": args.copy_streams,
+                   "lora_r": 16, "lora_alpha": 32, "dropout": p_drop, "optimizer": "AdamW",
+                   "adapter_grads": "kept to the step's end" if args.keep_grads else "dropped after each layer's update",
+                   "base": args.base,
                    "glue": args.glue, "parallelism": "single GPU"},
         "step_time": spread(streamed["step_ms"]),
         "roofline": roofline,

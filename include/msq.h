@@ -308,7 +308,11 @@ int lora_bwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj_grad
  * msq_swiglu_bwd:  du = da * silu(g);  dg = ((da * u) * s) * (1 + g * (1 - s)),
  *                  s = 1 / (1 + exp(-g)), with 1 + g * (1 - s) one fused multiply-add
  *                  -- the product rule followed by the SiLU derivative, as the two
- *                  unfused steps compute them. */
+ *                  unfused steps compute them.  The one exception to the no-alias rule:
+ *                  dg may be g and du may be u (in place; each element's three inputs
+ *                  are read before its two outputs are written), so a backward that
+ *                  no longer needs g and u can take its gradients without new memory.
+ *                  Partial overlaps remain invalid. */
 int msq_swiglu_fwd(const float* g, const float* u, int64_t n, float* a, msq_stream_t stream);
 int msq_swiglu_bwd(const float* da, const float* g, const float* u, int64_t n, float* dg,
                    float* du, msq_stream_t stream);

@@ -46,9 +46,10 @@ __device__ __forceinline__ void swiglu_grad(float da, float g, float u, float& d
   dg = (t * s) * __builtin_fmaf(g, 1.0f - s, 1.0f);
 }
 
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ da, const float* __restrict__ g,
-                                                         const float* __restrict__ u, int64_t n,
-                                                         float* __restrict__ dg, float* __restrict__ du) {
+// dg may be g and du may be u (in place): g, u, dg and du are not declared non-aliasing,
+// and each element's inputs are loaded before its outputs are stored.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ da, const float* g,
+                                                         const float* u, int64_t n, float* dg, float* du) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= n) return;
   if (e + 4 <= n) {
@@ -62,7 +63,13 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
     *reinterpret_cast<float4*>(dg + e) = rg;
     *reinterpret_cast<float4*>(du + e) = ru;
   } else {
-    for (int64_t i = e; i < n; ++i) swiglu_grad(da[i], g[i], u[i], dg[i], du[i]);
+    for (int64_t i = e; i < n; ++i) {
+      const float a = da[i], gv = g[i], uv = u[i];
+      float rg, ru;
+      swiglu_grad(a, gv, uv, rg, ru);
+      dg[i] = rg;
+      du[i] = ru;
+    }
   }
 }
 

@@ -402,11 +402,11 @@ def swiglu_fwd(g: torch.Tensor, u: torch.Tensor, out: Optional[torch.Tensor] = N
     return a
 
 
-def swiglu_bwd(da: torch.Tensor, g: torch.Tensor, u: torch.Tensor, stream=None):
-    """(dg, du) of a = silu(g) * u."""
+def swiglu_bwd(da: torch.Tensor, g: torch.Tensor, u: torch.Tensor, in_place: bool = False, stream=None):
+    """(dg, du) of a = silu(g) * u; in_place writes dg over g and du over u."""
     for nm, t in (("da", da), ("g", g), ("u", u)):
         _req(t, nm, torch.float32, tuple(g.shape))
-    dg, du = torch.empty_like(g), torch.empty_like(g)
+    dg, du = (g, u) if in_place else (torch.empty_like(g), torch.empty_like(g))
     check("msq_swiglu_bwd", lib().msq_swiglu_bwd(_ptr(da), _ptr(g), _ptr(u), g.numel(), _ptr(dg), _ptr(du),
                                                  _stream(stream)))
     return dg, du

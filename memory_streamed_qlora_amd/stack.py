@@ -208,15 +208,21 @@ def lora_linear_group(x, specs, As, Bs, cfg: ops.Lora):
 
 
 class _SwiGLU(torch.autograd.Function):
+    """a = silu(g) * u.  in_place: the backward writes dg over g and du over u, for callers
+    whose g and u feed nothing else (the layer's gate and up outputs), which keeps two
+    [T, intermediate] fp32 buffers out of the backward's peak."""
+
     @staticmethod
-    def forward(ctx, g, u):
+    def forward(ctx, g, u, in_place=False):
         ctx.save_for_backward(g, u)
+        ctx.in_place = in_place
         return ops.swiglu_fwd(g, u)
 
     @staticmethod
     def backward(ctx, da):
         g, u = ctx.saved_tensors
-        return ops.swiglu_bwd(da.contiguous(), g, u)
+        dg, du = ops.swiglu_bwd(da.contiguous(), g, u, in_place=ctx.in_place)
+        return dg, du, None
 
 
 class _RMSNormApply(torch.autograd.Function):
@@ -328,7 +334,8 @@ class Stack:
     def __init__(self, shape: Shape, seq: int, r: int = 16, alpha: float = 32.0, p_drop: float = 0.0,
                  window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
                  n_slots: int = 2, glue: str = "native", base: str = "nf4", group: bool = True,
-                 layer_release: bool = True, lm_stream: Optional[bool] = None, n_copy_streams: int = 2):
+                 layer_release: bool = True, lm_stream: Optional[bool] = None, n_copy_streams: int = 2,
+                 keep_grads: bool = True, checkpoint_every: int = 1):
         assert mode in ("streamed", "resident")
         assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
@@ -342,6 +349,18 @@ class Stack:
         self.window_blocks = window_blocks
         self.n_slots = n_slots
         self.n_copy_streams = n_copy_streams
+        # False: a layer's gradients are dropped once its AdamW step (inside the backward)
+        # has used them, so only one layer's gradients are ever held
+        self.keep_grads = keep_grads
+        # the forward keeps the input of every checkpoint_every-th layer (layers l with
+        # l % checkpoint_every == 0); the backward recomputes the others from the checkpoint
+        # below them, in no-grad forwards, when it enters their group.  Groups never
+        # straddle a window, so a group's layers are all in the window being processed.
+        if checkpoint_every < 1 or window_blocks % checkpoint_every:
+            raise ValueError(f"checkpoint_every={checkpoint_every} must be >= 1 and divide "
+                             f"window_blocks={window_blocks}")
+        self.checkpoint_every = checkpoint_every
+        self._gnorms: List[Optional[torch.Tensor]] = []
         self.dev = torch.device(device or "cuda")
         self.layout = LayerLayout(shape, base)
         self.host_blobs: List[torch.Tensor] = []
@@ -606,7 +625,7 @@ class Stack:
         h1 = self._lin(att, l, views, "o", step, micro, residual=h)
         xn2 = norm(h1, self.ln2[l])
         g, u = self._lin_group(xn2, l, views, ("gate", "up"), step, micro)
-        a = _SwiGLU.apply(g, u) if self.glue == "native" else torch.nn.functional.silu(g) * u
+        a = _SwiGLU.apply(g, u, True) if self.glue == "native" else torch.nn.functional.silu(g) * u
         return self._lin(a, l, views, "down", step, micro, value_unused=recompute, residual=h1)
 
     # -- base residency --------------------------------------------------------------
@@ -652,7 +671,7 @@ class Stack:
                     for l in layers:
                         if l not in views:  # acquired just before first use: waits for this layer only
                             views[l] = self._views(l)
-                        bounds[m].append(hs[m])
+                        bounds[m].append(hs[m] if l % self.checkpoint_every == 0 else None)
                         hs[m] = self.layer_forward(hs[m], l, views[l], step, micros[m])
                         if streamed and m == M - 1 and self.layer_release:
                             self.window.release_layer(l)
@@ -670,7 +689,7 @@ class Stack:
             loss = self._lm_loss_backward(hn, toks[m], scale)
             dhs.append(hf.grad)
             losses.append(loss)
-        hs = None
+        hs = hf = hn = None
         rw = wins[::-1]
         if streamed:
             for w in rw[:ahead]:
@@ -680,18 +699,27 @@ class Stack:
             views = {}
             for m in range(M):
                 for l in reversed(layers):
+                    if bounds[m][l] is None:
+                        # the top of a checkpoint group: its inputs again from the checkpoint
+                        c = l - l % self.checkpoint_every
+                        with torch.no_grad():
+                            for j in range(c, l):
+                                if j not in views:
+                                    views[j] = self._views(j)
+                                bounds[m][j + 1] = self.layer_forward(bounds[m][j], j, views[j], step, micros[m])
                     if l not in views:
                         views[l] = self._views(l)
                     x_in = bounds[m][l].detach().requires_grad_()
+                    bounds[m][l] = None
                     with torch.enable_grad():
                         out = self.layer_forward(x_in, l, views[l], step, micros[m], recompute=True)
                     out.backward(dhs[m])
                     dhs[m] = x_in.grad
-                    bounds[m][l] = None
+                    x_in = out = None
                     if streamed and m == M - 1 and self.layer_release:
                         self.window.release_layer(l)
                     if update_layers and m == M - 1:
-                        self.opts[l].step()
+                        self._update_layer(l)
             if streamed and not self.layer_release:
                 self.window.release(w)
             if streamed and wi + ahead < len(rw):
@@ -818,9 +846,33 @@ class Stack:
     def params(self) -> List[torch.nn.Parameter]:
         return [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
 
+    def _layer_params(self, l: int) -> List[torch.nn.Parameter]:
+        return list(self.A[l].values()) + list(self.B[l].values())
+
+    def _layer_norms(self, l: int) -> None:
+        """The 2-norm of each of layer l's adapter gradients (final by now), kept for the
+        step's gradient norm."""
+        grads = [p.grad for p in self._layer_params(l) if p.grad is not None]
+        self._gnorms[l] = torch.stack(torch._foreach_norm(grads)) if grads else None
+
+    def _update_layer(self, l: int) -> None:
+        """Layer l's gradients are final: note their norms, run its AdamW step and, unless
+        the gradients are kept, drop them."""
+        self._layer_norms(l)
+        self.opts[l].step()
+        if not self.keep_grads:
+            self.opts[l].zero_grad(set_to_none=True)
+
     def grad_norm(self) -> torch.Tensor:
-        grads = [p.grad for p in self.params() if p.grad is not None]
-        return torch.linalg.vector_norm(torch.stack(torch._foreach_norm(grads)))
+        """The 2-norm over every adapter gradient of the step: the norm of the per-tensor
+        norms, layer by layer (each layer's A then B tensors)."""
+        if len(self._gnorms) != len(self.opts):
+            self._gnorms = [None] * len(self.opts)
+        for l in range(len(self._gnorms)):
+            if self._gnorms[l] is None:
+                self._layer_norms(l)
+        norms = [n for n in self._gnorms if n is not None]
+        return torch.linalg.vector_norm(torch.cat(norms))
 
     def train_step(self, tokens: torch.Tensor, order: str = "block") -> Tuple[torch.Tensor, torch.Tensor]:
         """One optimizer step; returns (loss, grad_norm) device scalars.
@@ -836,6 +888,7 @@ class Stack:
             raise ValueError(f"order must be 'micro' or 'block', got {order!r}")
         for opt in self.opts:
             opt.zero_grad(set_to_none=True)
+        self._gnorms = [None] * len(self.opts)
         updated = True  # each layer's AdamW ran inside the backward
         if tokens.dim() == 1:
             loss = self._forward_backward([tokens], self.step_index, [0], 1.0, update_layers=True)[0]

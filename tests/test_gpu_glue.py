@@ -61,6 +61,12 @@ def test_swiglu_bitwise_unfused_and_oracle(n):
     assert _bits_equal(a, ref.detach()), "swiglu_fwd != silu(g) * u"
     assert _bits_equal(dg, gr.grad), "swiglu_bwd dg != autograd of the unfused chain"
     assert _bits_equal(du, ur.grad), "swiglu_bwd du != autograd of the unfused chain"
+    # in place: dg over g, du over u, the same bits
+    gi, ui = g.clone(), u.clone()
+    dgi, dui = msq.swiglu_bwd(da, gi, ui, in_place=True)
+    torch.cuda.synchronize()
+    assert dgi.data_ptr() == gi.data_ptr() and dui.data_ptr() == ui.data_ptr()
+    assert _bits_equal(dgi, dg) and _bits_equal(dui, du), "in-place swiglu_bwd differs"
     if n == 0:
         return
     g64, u64, da64 = host_f64(g), host_f64(u), host_f64(da)

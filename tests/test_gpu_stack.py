@@ -24,9 +24,9 @@ def _shape(sh: mi.BlockShape) -> S.Shape:
 
 
 def _build(sh: mi.BlockShape, seq, layers_np, glob_np, lora: mi.LoraSpec, mode, window_blocks, seed,
-           n_slots=2):
+           n_slots=2, **kw):
     st = S.Stack(_shape(sh), seq, r=lora.r, alpha=lora.alpha, p_drop=lora.p_drop,
-                 window_blocks=window_blocks, mode=mode, seed=seed, n_slots=n_slots)
+                 window_blocks=window_blocks, mode=mode, seed=seed, n_slots=n_slots, **kw)
     for p in layers_np:
         W = {proj: dev_bf16(p[proj]["W"]) for proj in S.PROJS}
         bias = {proj: dev_bf16(p[proj]["bias"]) for proj in ("q", "k", "v")}
@@ -182,11 +182,12 @@ def test_tiny_stack_step_vs_oracle():
     st.close()
 
 
-def _run_steps(sh, layers, glob, lo, mode, window_blocks, seed, steps, T, n_slots=2):
-    st = _build(sh, T, layers, glob, lo, mode, window_blocks, seed, n_slots)
+def _run_steps(sh, layers, glob, lo, mode, window_blocks, seed, steps, T, n_slots=2, micro=1, **kw):
+    st = _build(sh, T, layers, glob, lo, mode, window_blocks, seed, n_slots, **kw)
     losses, norms = [], []
     for s in range(steps):
-        toks = torch.from_numpy(mi.tokens(seed, 3, s, T, sh.vocab)).cuda()
+        toks = torch.from_numpy(np.stack([mi.tokens(seed, 3, micro * s + m, T, sh.vocab) for m in range(micro)])
+                                if micro > 1 else mi.tokens(seed, 3, s, T, sh.vocab)).cuda()
         loss, gn = st.train_step(toks)
         losses.append(loss)
         norms.append(gn)
@@ -216,6 +217,27 @@ def test_tiny_streamed_equals_resident_bitwise(window_blocks, n_slots):
     _assert_bitwise(res, stm)
     assert res[0][0] != res[0][-1]           # the adapters actually train
     print("window stats", stm[3], flush=True)
+
+
+@pytest.mark.parametrize("micro", [1, 2])
+def test_checkpoint_groups_and_dropped_grads_bitwise(micro):
+    """Checkpoints kept at every second layer (the backward recomputes the others from the
+    one below) and gradients dropped after each layer's update change no bit of the loss
+    stream, the grad norms, the adapters or the AdamW moments: 5 layers (the last group
+    is a single layer), windows of 2, streamed and resident, one or two micro-batches."""
+    lo, seed, T = mi.LoraSpec(8, 16.0, 0.1), 4, 32
+    sh = mi.BlockShape(hidden=128, heads=2, kv_heads=1, head_dim=64, inter=256, layers=5, vocab=512)
+    layers = [mi.block_params(seed, 3, l, sh, lo) for l in range(sh.layers)]
+    glob = mi.stack_globals(seed, 3, sh, T)
+    ref = _run_steps(sh, layers, glob, lo, "resident", 2, seed, 6, T, micro=micro)
+    for mode in ("resident", "streamed"):
+        got = _run_steps(sh, layers, glob, lo, mode, 2, seed, 6, T, n_slots=2, micro=micro,
+                         checkpoint_every=2, keep_grads=False)
+        assert not any(k.endswith(".grad") for k in got[2])
+        kept = {k: v for k, v in ref[2].items() if not k.endswith(".grad")}
+        _assert_bitwise((ref[0], ref[1], kept, None), got)
+    with pytest.raises(ValueError):
+        S.Stack(_shape(sh), T, window_blocks=3, checkpoint_every=2)
 
 
 @pytest.mark.parametrize("window_blocks,n_slots", [(4, 2), (1, 8)])
