@@ -1,10 +1,11 @@
 """Benchmark: streamed NF4 + LoRA training step of a Qwen2.5-32B-shaped stack on one GPU.
 
 Workload: 64 decoder layers (hidden 5120, 40/8 heads, SwiGLU 27648), random N(0, 0.02)
-base quantized to NF4 and held in pinned host memory, streamed in windows of 2 blocks
-through a device arena of 14 window slots (one computing, the others prefetching or kept
-for the turnaround), the frozen lm_head streamed from pinned host memory by the loss, each
-layer's adapter gradients dropped after its AdamW step; LoRA r16
+base quantized to NF4 and held in pinned host memory, streamed one block at a time through
+a device arena of 31 slots (one computing, the others prefetching or kept for the
+turnaround), the block-boundary activations below the top 4 layers parked in pinned host
+memory between the forward and the backward, the frozen lm_head streamed from pinned host
+memory by the loss, each layer's adapter gradients dropped after its AdamW step; LoRA r16
 alpha32 dropout 0.0 on all seven projections;
 batch 1 x 512 random tokens over a 152064-entry vocabulary; one AdamW step per
 training step.  A step is the whole hot path: forward with streaming, loss, backward
@@ -61,14 +62,14 @@ def measured_traffic(kernel: str):
 
 
 # Qwen2.5 stacks of the workloads: (hidden, heads, kv heads, head dim, intermediate, layers,
-# dropout, default window: layers per slot, slots, checkpoint every n layers).  The 32B and
-# 72B windows hold the most layers whose peak stays under the pages' streamed peaks for those
-# sizes (10.95 GB, A100 results, Benchmark matrix; 18.87 GB, "Poros" research post, memory
-# paragraph); the 7B stack keeps the plain double buffer of 4-layer windows (7 slots would
-# hold all 28 of its layers).
-SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, (4, 2, 1)),
-          "32b": (5120, 40, 8, 128, 27648, 64, 0.0, (2, 14, 1)),
-          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, (4, 7, 1))}
+# dropout, default window: layers per slot, slots, checkpoint every n layers, boundaries
+# parked in host memory).  The 32B and 72B windows hold the most layers whose peak stays
+# under the pages' streamed peaks for those sizes (10.95 GB, A100 results, Benchmark matrix;
+# 18.87 GB, "Poros" research post, memory paragraph); the 7B stack keeps the plain double
+# buffer of 4-layer windows (7 slots would hold all 28 of its layers).
+SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, (4, 2, 1, False)),
+          "32b": (5120, 40, 8, 128, 27648, 64, 0.0, (1, 31, 1, True)),
+          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, (4, 7, 1, False))}
 
 PROJ_NAMES = {(5120, 5120): "q/o", (1024, 5120): "k/v", (27648, 5120): "gate/up", (5120, 27648): "down",
               (7168, 5120): "q+k+v", (55296, 5120): "gate+up"}
@@ -480,15 +481,19 @@ def main() -> int:
                     help="Qwen2.5 stack shape: 32b (the headline), 7b or 72b (dropout 0.1, as their workloads state)")
     ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the shape's)")
     ap.add_argument("--window-blocks", type=int, default=None,
-                    help="layers per window slot (default: 2 at 32b, 4 at 7b and 72b)")
+                    help="layers per window slot (default: 1 at 32b, 4 at 7b and 72b)")
     ap.add_argument("--checkpoint-every", type=int, default=None,
                     help="the streamed step keeps every n-th layer's input for the backward and recomputes "
                          "the others (default 1; must divide --window-blocks)")
+    ap.add_argument("--offload-bounds", choices=("on", "off"), default=None,
+                    help="park the block-boundary activations (all but the top --device-bounds layers') in "
+                         "pinned host memory during the forward (default: on at 32b, off at 7b and 72b)")
+    ap.add_argument("--device-bounds", type=int, default=4)
     ap.add_argument("--keep-grads", action="store_true",
                     help="keep every adapter gradient until the step ends (default: a layer's gradients are "
                          "dropped once its AdamW step inside the backward has used them)")
     ap.add_argument("--slots", type=int, default=None,
-                    help="window slots in the device arena (default 14 at 32b, 7 at 72b: the most resident "
+                    help="window slots in the device arena (default 31 at 32b, 7 at 72b: the most resident "
                          "layers whose peak stays under the pages' streamed peaks, 10.95 and 18.87 GB; 2 at 7b)")
     ap.add_argument("--copy-streams", type=int, default=2, help="copy streams of the window (layer l on stream l mod n)")
     ap.add_argument("--no-resident", action="store_true",
@@ -530,7 +535,8 @@ def main() -> int:
     from memory_streamed_qlora_amd import ops, stack as S
 
     torch.cuda.set_device(0)
-    hid, heads, kvh, hd, inter, nl, p_drop, (wb_default, slots_default, ckpt_default) = SHAPES[args.shape]
+    hid, heads, kvh, hd, inter, nl, p_drop, (wb_default, slots_default, ckpt_default, off_default) = SHAPES[args.shape]
+    offload = off_default if args.offload_bounds is None else args.offload_bounds == "on"
     layers = args.layers or nl
     slots = args.slots or slots_default
     wblocks = args.window_blocks or wb_default
@@ -559,7 +565,9 @@ def main() -> int:
                             window_blocks=window_blocks, n_slots=n_slots, mode=mode, glue=args.glue,
                             base=args.base, layer_release=not args.window_release,
                             lm_stream=mode == "streamed" and not args.lm_resident, n_copy_streams=args.copy_streams,
-                            keep_grads=args.keep_grads, checkpoint_every=checkpoint_every)
+                            keep_grads=args.keep_grads, checkpoint_every=checkpoint_every,
+                            offload_bounds=offload and mode == "streamed" and n_slots == slots,
+                            device_bounds=args.device_bounds)
         torch.cuda.synchronize()
         log(f"{mode} ({window_blocks} x {n_slots}, checkpoints every {checkpoint_every}): built {layers} layers "
             f"in {time.time() - t_build:.1f}s "
@@ -666,12 +674,15 @@ def main() -> int:
         "data": "synthetic (random N(0,0.02) NF4 base, random adapters, random tokens)",
         "config": {"workload": (f"Qwen2.5-{size}-shaped streamed NF4+LoRA train step, windows of "
                                 f"{wblocks} layers x {slots} slots"
-                                + (f", checkpoints every {ckpt} layers" if ckpt > 1 else "")),
+                                + (f", checkpoints every {ckpt} layers" if ckpt > 1 else "")
+                                + (f", boundaries below the top {args.device_bounds} layers parked in host memory"
+                                   if offload else "")),
                    "layers": layers, "hidden": hid, "heads": heads, "kv_heads": kvh, "intermediate": inter,
                    "vocab": 152064, "seq_len": T, "batch": 1, "micro_batches": args.ga,
                    **({"accumulation_order": args.order} if args.ga > 1 else {}),
                    "window_layers_per_slot": wblocks, "window_slots": slots,
                    "window_layers_resident": wblocks * slots, "checkpoint_every": ckpt,
+                   "boundaries_on_device": args.device_bounds if offload else layers,
                    "copy_streams": args.copy_streams,
                    "lora_r": 16, "lora_alpha": 32, "dropout": p_drop, "optimizer": "AdamW",
                    "adapter_grads": "kept to the step's end" if args.keep_grads else "dropped after each layer's update",

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 11
+#define MSQ_ABI_VERSION 12
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -340,6 +340,52 @@ int msq_rmsnorm_apply_fwd(const float* h, const float* r, const float* w, int64_
                           float* y, msq_stream_t stream);
 int msq_rmsnorm_apply_bwd(const float* dy, const float* h, const float* r, const float* w, int64_t t,
                           int64_t d, float* dh, float* hdot, msq_stream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* The optimizer step over the adapters ("Poros" research post, training-step paragraph:
+ * one optimizer step after the backward, the same step a resident run takes; only the
+ * adapters' optimizer state lives on the device).  The pages do not name the optimizer;
+ * this is AdamW with decoupled weight decay, for step t >= 1 and every element:
+ *   p <- p * (1 - lr * weight_decay)
+ *   m <- m + (1 - beta1) * (g - m)
+ *   v <- beta2 * v + (1 - beta2) * g^2
+ *   p <- p - (lr / (1 - beta1^t)) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * in fp32, the scalar factors formed in double precision on the host.
+ *
+ * tensors[i]: n elements of fp32 parameters p, their gradient g and the two moments m, v,
+ * each contiguous device memory, 16-byte aligned, no two of the four overlapping (and no
+ * tensor overlapping another).  The caller owns all of them; p, m and v are updated in
+ * place, g is only read.  Moments start at zero before step 1.
+ * gsq (optional, NULL to skip): receives msq_adamw_partials(tensors, n) floats, partial
+ * sums of g^2 over fixed ranges of elements in tensor order, each summed in a fixed order
+ * -- their sum is the squared 2-norm of all the gradients, the same bits on every run.
+ * Errors: n_tensors < 0, n < 0, step < 1, lr < 0, beta outside [0, 1), eps <= 0 or
+ * weight_decay < 0 -> MSQ_E_INVAL; a null or misaligned pointer of a non-empty tensor
+ * -> MSQ_E_INVAL.  Runs asynchronously on `stream`. */
+typedef struct msq_adamw_cfg {
+  double lr, beta1, beta2, eps, weight_decay; /* double: 1 - beta2 keeps its digits */
+} msq_adamw_cfg;
+typedef struct msq_adamw_tensor {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  int64_t n;
+} msq_adamw_tensor;
+int64_t msq_adamw_partials(const msq_adamw_tensor* tensors, int n_tensors);
+int msq_adamw_step(const msq_adamw_tensor* tensors, int n_tensors, msq_adamw_cfg cfg, int64_t step, float* gsq,
+                   msq_stream_t stream);
+
+/* Copy `bytes` from src to dst by a kernel on `stream` (in stream order): each side is
+ * device memory or pinned host memory (msq_host_alloc, hipHostMalloc), which the kernel
+ * reads or writes across the link with its own loads and stores -- no DMA engine, so the
+ * copy is not queued behind the window's engine copies ("Poros" research post,
+ * training-step paragraph: the block boundaries the forward keeps for the backward may be
+ * parked in host memory this way).  src and dst: 16-byte aligned, not overlapping;
+ * bytes a multiple of 16 (0 is a no-op).  A pointer that is neither device nor pinned
+ * host memory, a null or misaligned pointer, or a bad size -> MSQ_E_INVAL.  The caller
+ * owns both buffers and keeps them alive until the copy has run. */
+int msq_kernel_copy(const void* src, void* dst, size_t bytes, msq_stream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Pinned host memory for the frozen base ("Poros" research post: the base lives in

@@ -63,6 +63,16 @@ class LoraProjGrad(ctypes.Structure):
                 ("dy", ctypes.c_void_p), ("u", ctypes.c_void_p), ("dA", ctypes.c_void_p), ("dB", ctypes.c_void_p)]
 
 
+class AdamwCfg(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class AdamwTensor(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_void_p), ("g", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("n", ctypes.c_int64)]
+
+
 class KernelTiming(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_uint64),
                 ("total_ms", ctypes.c_double), ("total_flops", ctypes.c_double),
@@ -109,6 +119,9 @@ _SIG = {
     "lora_group_bwd_workspace_size": (ctypes.c_size_t, [_I64, _I64, _P, ctypes.c_int, ctypes.c_int32]),
     "lora_bwd_group": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, LoraCfg, _P, ctypes.c_int, ctypes.c_int, _P,
                                       ctypes.c_size_t, _P]),
+    "msq_kernel_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    "msq_adamw_partials": (_I64, [_P, ctypes.c_int]),
+    "msq_adamw_step": (ctypes.c_int, [_P, ctypes.c_int, AdamwCfg, _I64, _P, _P]),
     "msq_host_alloc": (ctypes.c_int, [ctypes.c_size_t, _P]),
     "msq_host_free": (ctypes.c_int, [_P]),
     "nf4_stream_load_device_bytes": (ctypes.c_size_t, [_I64, _I64]),
@@ -129,7 +142,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 11  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 12  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

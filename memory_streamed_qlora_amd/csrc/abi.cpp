@@ -7,6 +7,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
+#include <vector>
 
 #include "../../include/msq.h"
 #include "internal.hpp"
@@ -730,6 +732,100 @@ int msq_rmsnorm_apply_fwd(const float* h, const float* r, const float* w, int64_
 int msq_rmsnorm_apply_bwd(const float* dy, const float* h, const float* r, const float* w, int64_t t, int64_t d,
                           float* dh, float* hdot, msq_stream_t stream) {
   return rmsnorm_entry("msq_rmsnorm_apply_bwd", true, dy, h, r, w, t, d, dh, hdot, stream);
+}
+
+// The device-side address of p (device memory, or pinned host memory mapped for the
+// device), or null when p is neither.
+static const void* device_side(const void* p) {
+  hipPointerAttribute_t a;
+  memset(&a, 0, sizeof(a));
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice) return p;
+  if (a.type == hipMemoryTypeHost && a.devicePointer) {
+    // devicePointer and hostPointer describe the same place; keep p's offset from it
+    const char* hp = (const char*)a.hostPointer;
+    const ptrdiff_t off = hp ? (const char*)p - hp : 0;
+    return (const char*)a.devicePointer + off;
+  }
+  return nullptr;
+}
+
+int msq_kernel_copy(const void* src, void* dst, size_t bytes, msq_stream_t stream) {
+  const char* fn = "msq_kernel_copy";
+  if (bytes == 0) return MSQ_OK;
+  if (!src || !dst) return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
+  if (bytes % 16 || !aligned(src, 16) || !aligned(dst, 16))
+    return set_error(MSQ_E_INVAL, "%s: pointers must be 16-byte aligned and bytes (%zu) a multiple of 16", fn, bytes);
+  const char* s0 = (const char*)src;
+  const char* d0 = (const char*)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return set_error(MSQ_E_INVAL, "%s: src and dst overlap", fn);
+  const void* sd = device_side(src);
+  const void* se = device_side(s0 + bytes - 1);
+  const void* dd = device_side(dst);
+  const void* de = device_side(d0 + bytes - 1);
+  if (!sd || !se || (const char*)se - (const char*)sd != (ptrdiff_t)(bytes - 1))
+    return set_error(MSQ_E_INVAL, "%s: src (%p, %zu bytes) is not device or pinned host memory over its range", fn,
+                     src, bytes);
+  if (!dd || !de || (const char*)de - (const char*)dd != (ptrdiff_t)(bytes - 1))
+    return set_error(MSQ_E_INVAL, "%s: dst (%p, %zu bytes) is not device or pinned host memory over its range", fn,
+                     dst, bytes);
+  const hipError_t e = launch_kernel_copy(sd, (void*)dd, (int64_t)bytes, (hipStream_t)stream);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "msq_kernel_copy launch");
+}
+
+int64_t msq_adamw_partials(const msq_adamw_tensor* tensors, int n_tensors) {
+  if (n_tensors < 0 || (n_tensors > 0 && !tensors)) return -1;
+  std::vector<int64_t> n((size_t)n_tensors);
+  for (int i = 0; i < n_tensors; ++i) {
+    if (tensors[i].n < 0) return -1;
+    n[i] = tensors[i].n;
+  }
+  return adamw_workgroups(n.data(), n_tensors);
+}
+
+int msq_adamw_step(const msq_adamw_tensor* tensors, int n_tensors, msq_adamw_cfg cfg, int64_t step, float* gsq,
+                   msq_stream_t stream) {
+  const char* fn = "msq_adamw_step";
+  if (n_tensors < 0 || (n_tensors > 0 && !tensors)) return set_error(MSQ_E_INVAL, "%s: %d tensors", fn, n_tensors);
+  if (step < 1) return set_error(MSQ_E_INVAL, "%s: step %lld < 1", fn, (long long)step);
+  if (!(cfg.lr >= 0.0) || !(cfg.beta1 >= 0.0 && cfg.beta1 < 1.0) || !(cfg.beta2 >= 0.0 && cfg.beta2 < 1.0) ||
+      !(cfg.eps > 0.0) || !(cfg.weight_decay >= 0.0))
+    return set_error(MSQ_E_INVAL, "%s: lr %g, betas (%g, %g), eps %g, weight_decay %g out of range", fn, cfg.lr,
+                     cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay);
+  std::vector<float*> p, m, v;
+  std::vector<const float*> g;
+  std::vector<int64_t> n;
+  for (int i = 0; i < n_tensors; ++i) {
+    const msq_adamw_tensor& t = tensors[i];
+    if (t.n < 0) return set_error(MSQ_E_INVAL, "%s: tensor %d has n = %lld", fn, i, (long long)t.n);
+    if (t.n == 0) continue;
+    if (!t.p || !t.g || !t.m || !t.v) return set_error(MSQ_E_INVAL, "%s: tensor %d: null pointer", fn, i);
+    if (!aligned(t.p, 16) || !aligned(t.g, 16) || !aligned(t.m, 16) || !aligned(t.v, 16))
+      return set_error(MSQ_E_INVAL, "%s: tensor %d: misaligned pointer (16 bytes)", fn, i);
+    p.push_back(t.p);
+    g.push_back(t.g);
+    m.push_back(t.m);
+    v.push_back(t.v);
+    n.push_back(t.n);
+  }
+  // the partials of empty tensors are none, so the kept ones land where msq_adamw_partials counts them
+  const double lr = cfg.lr, b1 = cfg.beta1, b2 = cfg.beta2;
+  AdamwHyper h;
+  h.decay = (float)(1.0 - lr * cfg.weight_decay);
+  h.b1c = (float)(1.0 - b1);
+  h.b2 = (float)b2;
+  h.b2c = (float)(1.0 - b2);
+  h.bc2s = (float)std::sqrt(1.0 - std::pow(b2, (double)step));
+  h.eps = (float)cfg.eps;
+  h.step = (float)(lr / (1.0 - std::pow(b1, (double)step)));
+  if (p.empty()) return MSQ_OK;
+  const hipError_t e = launch_adamw(p.data(), g.data(), m.data(), v.data(), n.data(), (int)p.size(), h, gsq,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? MSQ_OK : hip_error(e, "msq_adamw_step launch");
 }
 
 }  // extern "C"

@@ -158,6 +158,20 @@ hipError_t launch_rope(bool backward, const float* x, const float* cs, const flo
 hipError_t launch_rmsnorm_apply(bool backward, const float* dy, const float* h, const float* r, const float* w,
                                 int64_t T, int64_t D, float* out, float* hdot, hipStream_t s);
 
+// Device <-> pinned host copy by a kernel (hostcopy.hip); src and dst are device-side
+// addresses, bytes a multiple of 16.
+hipError_t launch_kernel_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
+// AdamW over fp32 tensors (optim.hip).  The hyperparameters in the form the kernel uses
+// them, formed on the host in double precision for step t.
+struct AdamwHyper {
+  float decay, b1c, b2, b2c, bc2s, eps, step;
+};
+// Workgroups (= g^2 partials written) of one update over tensors of n[0..nt) elements.
+int64_t adamw_workgroups(const int64_t* n, int nt);
+hipError_t launch_adamw(float* const* p, const float* const* g, float* const* m, float* const* v,
+                        const int64_t* n, int nt, const AdamwHyper& h, float* gsq, hipStream_t s);
+
 
 // ---- timing -------------------------------------------------------------------
 bool timing_on();

@@ -460,6 +460,52 @@ def rmsnorm_apply_bwd(dy: torch.Tensor, h: torch.Tensor, r: torch.Tensor, w: tor
     return dh, hdot
 
 
+def kernel_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """dst <- src by a kernel (msq_kernel_copy): each side a device tensor or pinned host
+    memory (pinned_empty); same dtype and number of elements, contiguous."""
+    for nm, t in (("src", src), ("dst", dst)):
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous tensor")
+    if src.dtype != dst.dtype or src.numel() != dst.numel():
+        raise ValueError(f"src {src.dtype}[{src.numel()}] and dst {dst.dtype}[{dst.numel()}] differ")
+    check("msq_kernel_copy", lib().msq_kernel_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                                                   _stream(stream)))
+    return dst
+
+
+# ---------------------------------------------------------------------------------
+# optimizer step
+
+def _adamw_tensors(params, grads, ms, vs):
+    arr = (_abi.AdamwTensor * len(params))()
+    for i, (p, g, m, v) in enumerate(zip(params, grads, ms, vs)):
+        n = p.numel()
+        for nm, t in (("p", p), ("g", g), ("m", m), ("v", v)):
+            _req(t, nm, torch.float32, tuple(p.shape))
+        arr[i] = _abi.AdamwTensor(_ptr(p), _ptr(g), _ptr(m), _ptr(v), n)
+    return arr
+
+
+def adamw_partials(params: Sequence[torch.Tensor]) -> int:
+    """Number of g^2 partial sums adamw_step writes for these tensors."""
+    arr = (_abi.AdamwTensor * len(params))()
+    for i, p in enumerate(params):
+        arr[i].n = p.numel()
+    return int(lib().msq_adamw_partials(arr, len(params)))
+
+
+def adamw_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], ms: Sequence[torch.Tensor],
+               vs: Sequence[torch.Tensor], step: int, lr: float, betas: Tuple[float, float], eps: float,
+               weight_decay: float, gsq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """AdamW (msq_adamw_step) in place on fp32 params and moments; gsq, if given, receives
+    adamw_partials(params) partial sums of the gradients' squares."""
+    arr = _adamw_tensors(params, grads, ms, vs)
+    if gsq is not None:
+        _req(gsq, "gsq", torch.float32, (adamw_partials(params),))
+    cfg = _abi.AdamwCfg(lr, betas[0], betas[1], eps, weight_decay)
+    check("msq_adamw_step", lib().msq_adamw_step(arr, len(params), cfg, step, _ptr(gsq), _stream(stream)))
+
+
 def nf4_stream_load(jobs: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], chunk_bytes: int = 32 << 20,
                     host_threads: int = 8, stream=None, device=None) -> dict:
     """Streamed quantizing load: jobs of (w bf16 host [rows, cols], codes uint8 host

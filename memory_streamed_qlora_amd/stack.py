@@ -10,8 +10,10 @@ package README, "How it works"):
   backward  windows in reverse: reload, recompute each block's forward with the same
             dropout keys (the counter-based masks replay exactly), then differentiate
             the adapters and the block input only
-  update    one AdamW step on the fp32 adapters, identical to the resident run's; each
-            layer's step runs as soon as its gradients are final, inside the backward.
+  update    one AdamW step on the fp32 adapters (the library's msq_adamw_step), identical
+            to the resident run's; each layer's step runs as soon as its gradients are
+            final, inside the backward, and also yields the partial sums of the squared
+            gradients for the step's gradient norm.
 Resident mode runs the same code with every layer's blob already in device memory.
 Gradient accumulation over M micro-batches runs micro-batch by micro-batch or
 block-major (every micro-batch through a window before the next window), with the
@@ -26,8 +28,8 @@ projections) -- runs in the library too (glue="native"); each
 fused chain reproduces the unfused PyTorch chain element for element (the pages allow
 only such fusions, "Poros" README, Roadmap, "The Poros kernel"), and glue="torch" runs
 that unfused chain.  The rest -- RMSNorm's mean, causal GQA attention, embedding
-gather, lm_head and cross-entropy, AdamW -- holds reductions, so it stays unfused fp32
-PyTorch, deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and optimizer settings are
+gather, lm_head and cross-entropy -- holds reductions, so it stays unfused fp32 PyTorch,
+deterministic.  Block constants (eps 1e-6, RoPE base 1e6) and optimizer settings are
 readings of the Qwen2 family and of textbook AdamW; the pages name neither.
 """
 from __future__ import annotations
@@ -320,6 +322,15 @@ def copy_streams(device, n: int) -> List[torch.cuda.Stream]:
     return out
 
 
+class _HostBound:
+    """A block-boundary activation parked in pinned host memory during the forward."""
+
+    __slots__ = ("host",)
+
+    def __init__(self, host: torch.Tensor):
+        self.host = host
+
+
 @dataclass
 class StepResult:
     loss: float
@@ -335,7 +346,8 @@ class Stack:
                  window_blocks: int = 4, mode: str = "streamed", seed: int = 0, device=None,
                  n_slots: int = 2, glue: str = "native", base: str = "nf4", group: bool = True,
                  layer_release: bool = True, lm_stream: Optional[bool] = None, n_copy_streams: int = 2,
-                 keep_grads: bool = True, checkpoint_every: int = 1):
+                 keep_grads: bool = True, checkpoint_every: int = 1, offload_bounds: bool = False,
+                 device_bounds: int = 4):
         assert mode in ("streamed", "resident")
         assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
@@ -360,7 +372,15 @@ class Stack:
             raise ValueError(f"checkpoint_every={checkpoint_every} must be >= 1 and divide "
                              f"window_blocks={window_blocks}")
         self.checkpoint_every = checkpoint_every
-        self._gnorms: List[Optional[torch.Tensor]] = []
+        # offload_bounds: the forward parks every kept block-boundary activation except the
+        # top device_bounds layers' in pinned host memory, and the backward brings each back
+        # when it reaches it, both by kernel copies on the compute stream (msq_kernel_copy:
+        # the GPU's own loads and stores over the link, not queued behind the window's
+        # engine copies).  The bits do not change; the device then holds a few boundaries
+        # instead of all of them at the turnaround, the step's peak.
+        self.offload_bounds = offload_bounds
+        self.device_bounds = device_bounds
+        self._host_bounds: Optional[torch.Tensor] = None
         self.dev = torch.device(device or "cuda")
         self.layout = LayerLayout(shape, base)
         self.host_blobs: List[torch.Tensor] = []
@@ -379,7 +399,11 @@ class Stack:
         self.cos, self.sin = rope_tables(seq, shape.head_dim, self.dev)
         self.mask_add = torch.triu(torch.full((seq, seq), float("-inf"), device=self.dev), 1)
         self._mask_reps: Dict[int, torch.Tensor] = {}
-        self.opts: List[torch.optim.Optimizer] = []
+        # AdamW state per layer: the moments (created at the layer's first update, zeros) and
+        # the partial sums of g^2 its last update wrote
+        self._m: List[Optional[List[torch.Tensor]]] = []
+        self._v: List[Optional[List[torch.Tensor]]] = []
+        self._gsq: List[torch.Tensor] = []
         self.step_index = 0
 
     # -- construction ------------------------------------------------------------
@@ -440,15 +464,16 @@ class Stack:
         return rows.to(self.dev, non_blocking=True).float()
 
     def finalize(self) -> None:
-        # one AdamW per layer: a layer's update can run as soon as its gradients are final
-        # (inside the backward, overlapping the window's copies), and its foreach
-        # temporaries are one layer's; the per-element arithmetic is that of one optimizer
-        # over all adapters
-        self.opts = [torch.optim.AdamW(list(self.A[l].values()) + list(self.B[l].values()), lr=LR, betas=BETAS,
-                                       eps=ADAM_EPS, weight_decay=WD, foreach=True) for l in range(len(self.A))]
+        # one AdamW launch per layer: a layer's update runs as soon as its gradients are
+        # final (inside the backward, overlapping the window's copies)
+        L = len(self.A)
+        self._m, self._v = [None] * L, [None] * L
+        self._gsq = [torch.zeros(ops.adamw_partials(self._layer_params(l)), dtype=torch.float32, device=self.dev)
+                     for l in range(L)]
         if self.mode == "streamed" or self.lm_stream:
             self.copy_streams = copy_streams(self.dev, self.n_copy_streams)
             self.copy_stream = self.copy_streams[0]
+
         if self.mode == "streamed":
             self.window = ops.BlockStreamWindow(self.host_blobs, self.window_blocks, self.n_slots,
                                                 copy_streams=self.copy_streams, device=self.dev)
@@ -671,7 +696,8 @@ class Stack:
                     for l in layers:
                         if l not in views:  # acquired just before first use: waits for this layer only
                             views[l] = self._views(l)
-                        bounds[m].append(hs[m] if l % self.checkpoint_every == 0 else None)
+                        bounds[m].append(self._keep_bound(hs[m], m, l, M) if l % self.checkpoint_every == 0
+                                         else None)
                         hs[m] = self.layer_forward(hs[m], l, views[l], step, micros[m])
                         if streamed and m == M - 1 and self.layer_release:
                             self.window.release_layer(l)
@@ -706,10 +732,11 @@ class Stack:
                             for j in range(c, l):
                                 if j not in views:
                                     views[j] = self._views(j)
+                                bounds[m][j] = self._bound(bounds[m][j])
                                 bounds[m][j + 1] = self.layer_forward(bounds[m][j], j, views[j], step, micros[m])
                     if l not in views:
                         views[l] = self._views(l)
-                    x_in = bounds[m][l].detach().requires_grad_()
+                    x_in = self._bound(bounds[m][l]).detach().requires_grad_()
                     bounds[m][l] = None
                     with torch.enable_grad():
                         out = self.layer_forward(x_in, l, views[l], step, micros[m], recompute=True)
@@ -725,6 +752,26 @@ class Stack:
             if streamed and wi + ahead < len(rw):
                 self.window.prefetch(rw[wi + ahead])
         return losses
+
+    def _keep_bound(self, h: torch.Tensor, m: int, l: int, M: int):
+        """Layer l's input as the backward will need it: h itself, or (offloaded) parked in
+        pinned host memory by a kernel copy in stream order, after which h's memory is free."""
+        if not self.offload_bounds or l >= self.shape.layers - self.device_bounds:
+            return h
+        T, H = h.shape
+        L = self.shape.layers
+        need = M * L * T * H
+        if self._host_bounds is None or self._host_bounds.numel() < need:
+            self._host_bounds = ops.pinned_empty(need * 4).view(torch.float32)
+        host = self._host_bounds[(m * L + l) * T * H:(m * L + l + 1) * T * H].view(T, H)
+        ops.kernel_copy(h, host)
+        return _HostBound(host)
+
+    def _bound(self, b) -> torch.Tensor:
+        """A kept boundary on the device: as it is, or a parked one copied back."""
+        if isinstance(b, _HostBound):
+            return ops.kernel_copy(b.host, torch.empty(b.host.shape, dtype=b.host.dtype, device=self.dev))
+        return b
 
     LM_CHUNK = 4224  # vocabulary rows per lm_head chunk (152064 = 36 x 4224)
 
@@ -847,32 +894,28 @@ class Stack:
         return [p for d in self.A for p in d.values()] + [p for d in self.B for p in d.values()]
 
     def _layer_params(self, l: int) -> List[torch.nn.Parameter]:
+        """Layer l's adapters: A of every projection, then B, in PROJS order."""
         return list(self.A[l].values()) + list(self.B[l].values())
 
-    def _layer_norms(self, l: int) -> None:
-        """The 2-norm of each of layer l's adapter gradients (final by now), kept for the
-        step's gradient norm."""
-        grads = [p.grad for p in self._layer_params(l) if p.grad is not None]
-        self._gnorms[l] = torch.stack(torch._foreach_norm(grads)) if grads else None
-
     def _update_layer(self, l: int) -> None:
-        """Layer l's gradients are final: note their norms, run its AdamW step and, unless
-        the gradients are kept, drop them."""
-        self._layer_norms(l)
-        self.opts[l].step()
+        """Layer l's gradients are final: its AdamW step (one library launch, which also
+        writes the partial sums of g^2 into _gsq[l]) and, unless the gradients are kept,
+        dropping them."""
+        params = self._layer_params(l)
+        if self._m[l] is None:
+            self._m[l] = [torch.zeros_like(p) for p in params]
+            self._v[l] = [torch.zeros_like(p) for p in params]
+        grads = [p.grad if p.grad is not None else torch.zeros_like(p) for p in params]
+        ops.adamw_step([p.detach() for p in params], grads, self._m[l], self._v[l], self.step_index + 1, LR, BETAS,
+                       ADAM_EPS, WD, gsq=self._gsq[l])
         if not self.keep_grads:
-            self.opts[l].zero_grad(set_to_none=True)
+            for p in params:
+                p.grad = None
 
     def grad_norm(self) -> torch.Tensor:
-        """The 2-norm over every adapter gradient of the step: the norm of the per-tensor
-        norms, layer by layer (each layer's A then B tensors)."""
-        if len(self._gnorms) != len(self.opts):
-            self._gnorms = [None] * len(self.opts)
-        for l in range(len(self._gnorms)):
-            if self._gnorms[l] is None:
-                self._layer_norms(l)
-        norms = [n for n in self._gnorms if n is not None]
-        return torch.linalg.vector_norm(torch.cat(norms))
+        """The 2-norm over every adapter gradient of the last update: the square root of the
+        sum of the partial sums of g^2 the layers' updates wrote."""
+        return torch.sqrt(torch.cat(self._gsq).sum())
 
     def train_step(self, tokens: torch.Tensor, order: str = "block") -> Tuple[torch.Tensor, torch.Tensor]:
         """One optimizer step; returns (loss, grad_norm) device scalars.
@@ -886,10 +929,8 @@ class Stack:
         and every adapter gradient is summed in micro-batch order."""
         if order not in ("micro", "block"):
             raise ValueError(f"order must be 'micro' or 'block', got {order!r}")
-        for opt in self.opts:
-            opt.zero_grad(set_to_none=True)
-        self._gnorms = [None] * len(self.opts)
-        updated = True  # each layer's AdamW ran inside the backward
+        for p in self.params():
+            p.grad = None
         if tokens.dim() == 1:
             loss = self._forward_backward([tokens], self.step_index, [0], 1.0, update_layers=True)[0]
         else:
@@ -897,7 +938,8 @@ class Stack:
             scale = 1.0 / M
             if order == "micro":
                 losses = [self._forward_backward([tokens[m]], self.step_index, [m], scale)[0] for m in range(M)]
-                updated = False
+                for l in range(len(self.A)):
+                    self._update_layer(l)
             else:
                 losses = self._forward_backward([tokens[m] for m in range(M)], self.step_index, list(range(M)),
                                                 scale, update_layers=True)
@@ -905,9 +947,6 @@ class Stack:
             for lm in losses[1:]:
                 loss = loss + lm * scale
         gn = self.grad_norm()
-        if not updated:
-            for opt in self.opts:
-                opt.step()
         self.step_index += 1
         return loss, gn
 
@@ -915,16 +954,14 @@ class Stack:
         """Everything the bitwise gate compares: adapters, grads, AdamW moments."""
         out = {}
         for l in range(self.shape.layers):
-            for p in PROJS:
-                for nm, d in (("A", self.A), ("B", self.B)):
-                    prm = d[l][p]
-                    out[f"{l}.{p}.{nm}"] = prm.detach()
-                    if prm.grad is not None:
-                        out[f"{l}.{p}.{nm}.grad"] = prm.grad.detach()
-                    st = self.opts[l].state.get(prm, {})
-                    for sk in ("exp_avg", "exp_avg_sq"):
-                        if sk in st:
-                            out[f"{l}.{p}.{nm}.{sk}"] = st[sk].detach()
+            for i, (nm, p) in enumerate([("A", p) for p in PROJS] + [("B", p) for p in PROJS]):
+                prm = (self.A if nm == "A" else self.B)[l][p]
+                out[f"{l}.{p}.{nm}"] = prm.detach()
+                if prm.grad is not None:
+                    out[f"{l}.{p}.{nm}.grad"] = prm.grad.detach()
+                if self._m[l] is not None:
+                    out[f"{l}.{p}.{nm}.exp_avg"] = self._m[l][i].detach()
+                    out[f"{l}.{p}.{nm}.exp_avg_sq"] = self._v[l][i].detach()
         return out
 
     def close(self) -> None:

@@ -133,6 +133,51 @@ def test_glue_rejects_bad_arguments():
     assert L.msq_rmsnorm_apply_bwd(FAKE + 4, FAKE, FAKE, FAKE, 4, 64, FAKE, FAKE, None) == abi.MSQ_E_INVAL
 
 
+def _adam_tensors(*specs):
+    arr = (abi.AdamwTensor * len(specs))()
+    for i, (p, g, m, v, n) in enumerate(specs):
+        arr[i] = abi.AdamwTensor(p, g, m, v, n)
+    return arr
+
+
+def test_adamw_rejects_bad_arguments_and_counts_partials():
+    """msq_adamw_step validates everything on the host (nothing below reaches a launch);
+    msq_adamw_partials counts one partial per 8192 elements of each tensor."""
+    L = abi.lib()
+    cfg = abi.AdamwCfg(2e-4, 0.9, 0.999, 1e-8, 0.01)
+    ok = _adam_tensors((FAKE, FAKE + 256, FAKE + 512, FAKE + 768, 8))
+    assert L.msq_adamw_partials(_adam_tensors((0, 0, 0, 0, 8192), (0, 0, 0, 0, 8193), (0, 0, 0, 0, 0),
+                                              (0, 0, 0, 0, 1)), 4) == 1 + 2 + 0 + 1
+    assert L.msq_adamw_partials(_adam_tensors((0, 0, 0, 0, -1)), 1) == -1
+    assert L.msq_adamw_partials(None, 0) == 0
+    assert L.msq_adamw_step(None, 0, cfg, 1, None, None) == 0                   # nothing to do
+    assert L.msq_adamw_step(_adam_tensors((None, None, None, None, 0)), 1, cfg, 1, None, None) == 0
+    assert L.msq_adamw_step(ok, -1, cfg, 1, None, None) == abi.MSQ_E_INVAL
+    assert L.msq_adamw_step(ok, 1, cfg, 0, None, None) == abi.MSQ_E_INVAL
+    assert "step" in _err()
+    for bad in (abi.AdamwCfg(-1.0, 0.9, 0.999, 1e-8, 0.01), abi.AdamwCfg(2e-4, 1.0, 0.999, 1e-8, 0.01),
+                abi.AdamwCfg(2e-4, 0.9, -0.1, 1e-8, 0.01), abi.AdamwCfg(2e-4, 0.9, 0.999, 0.0, 0.01),
+                abi.AdamwCfg(2e-4, 0.9, 0.999, 1e-8, -0.01), abi.AdamwCfg(float("nan"), 0.9, 0.999, 1e-8, 0.0)):
+        assert L.msq_adamw_step(ok, 1, bad, 1, None, None) == abi.MSQ_E_INVAL
+    assert L.msq_adamw_step(_adam_tensors((FAKE, FAKE, FAKE, FAKE, -4)), 1, cfg, 1, None, None) == abi.MSQ_E_INVAL
+    assert L.msq_adamw_step(_adam_tensors((FAKE, None, FAKE, FAKE, 4)), 1, cfg, 1, None, None) == abi.MSQ_E_INVAL
+    assert "null" in _err()
+    assert L.msq_adamw_step(_adam_tensors((FAKE, FAKE, FAKE + 4, FAKE, 4)), 1, cfg, 1, None, None) == abi.MSQ_E_INVAL
+    assert "misaligned" in _err()
+
+
+def test_kernel_copy_rejects_bad_arguments():
+    """Size, null, alignment and overlap are checked before any pointer is looked at."""
+    L = abi.lib()
+    assert L.msq_kernel_copy(None, None, 0, None) == 0
+    assert L.msq_kernel_copy(None, FAKE, 16, None) == abi.MSQ_E_INVAL
+    assert L.msq_kernel_copy(FAKE, FAKE + 4096, 24, None) == abi.MSQ_E_INVAL
+    assert L.msq_kernel_copy(FAKE + 8, FAKE + 4096, 32, None) == abi.MSQ_E_INVAL
+    assert "aligned" in _err()
+    assert L.msq_kernel_copy(FAKE, FAKE + 16, 64, None) == abi.MSQ_E_INVAL
+    assert "overlap" in _err()
+
+
 def test_stream_load_rejects_bad_arguments():
     """The loader validates jobs and staging on the host before any HIP call."""
     L = abi.lib()

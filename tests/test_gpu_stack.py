@@ -240,6 +240,22 @@ def test_checkpoint_groups_and_dropped_grads_bitwise(micro):
         S.Stack(_shape(sh), T, window_blocks=3, checkpoint_every=2)
 
 
+@pytest.mark.parametrize("micro,ckpt", [(1, 1), (2, 2)])
+def test_host_parked_boundaries_bitwise(micro, ckpt):
+    """Block-boundary activations parked in pinned host memory during the forward (all but
+    the top layer's) and brought back in the backward change no bit of any surface,
+    streamed or resident, with one or two micro-batches and with checkpoint groups."""
+    lo, seed, T = mi.LoraSpec(8, 16.0, 0.1), 5, 32
+    sh = mi.BlockShape(hidden=128, heads=2, kv_heads=1, head_dim=64, inter=256, layers=6, vocab=512)
+    layers = [mi.block_params(seed, 3, l, sh, lo) for l in range(sh.layers)]
+    glob = mi.stack_globals(seed, 3, sh, T)
+    ref = _run_steps(sh, layers, glob, lo, "resident", 2, seed, 4, T, micro=micro)
+    for mode in ("resident", "streamed"):
+        got = _run_steps(sh, layers, glob, lo, mode, 2, seed, 4, T, n_slots=2, micro=micro,
+                         checkpoint_every=ckpt, offload_bounds=True, device_bounds=1)
+        _assert_bitwise(ref, got)
+
+
 @pytest.mark.parametrize("window_blocks,n_slots", [(4, 2), (1, 8)])
 def test_qwen7b_streamed_equals_resident_bitwise(window_blocks, n_slots):
     """Qwen2.5-7B-shaped stack (28 layers) streamed from pinned host memory through a
@@ -391,6 +407,21 @@ def test_window_copy_streams(n_streams):
     assert s["windows_copied"] + s["windows_reused"] == 12 and s["windows_reused"] == 3
     assert 0 < s["busy_ms"] <= s["copy_ms"] * (1 + 1e-6)
     w.close()
+
+
+def test_kernel_copy_between_device_and_pinned_host():
+    """msq_kernel_copy round-trips device -> pinned host -> device exactly, ragged sizes,
+    and refuses pageable host memory."""
+    for n in (4, 1000, 512 * 5120, 3 * 1024 * 1024 + 4):
+        src = torch.randn(n, device="cuda")
+        host = msq.ops.pinned_empty(n * 4).view(torch.float32)
+        back = torch.empty_like(src)
+        msq.kernel_copy(src, host)
+        msq.kernel_copy(host, back)
+        torch.cuda.synchronize()
+        assert torch.equal(back, src) and torch.equal(host, src.cpu())
+    with pytest.raises(MsqError):
+        msq.kernel_copy(torch.zeros(64), torch.zeros(64, device="cuda"))
 
 
 def test_window_refuses_pageable_blobs():
