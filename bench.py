@@ -69,7 +69,7 @@ def measured_traffic(kernel: str):
 # buffer of 4-layer windows (7 slots would hold all 28 of its layers).
 SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, (4, 2, 1, False)),
           "32b": (5120, 40, 8, 128, 27648, 64, 0.0, (1, 31, 1, True)),
-          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, (4, 7, 1, False))}
+          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, (1, 31, 1, True))}
 
 PROJ_NAMES = {(5120, 5120): "q/o", (1024, 5120): "k/v", (27648, 5120): "gate/up", (5120, 27648): "down",
               (7168, 5120): "q+k+v", (55296, 5120): "gate+up"}
@@ -481,19 +481,19 @@ def main() -> int:
                     help="Qwen2.5 stack shape: 32b (the headline), 7b or 72b (dropout 0.1, as their workloads state)")
     ap.add_argument("--layers", type=int, default=None, help="stack depth (default: the shape's)")
     ap.add_argument("--window-blocks", type=int, default=None,
-                    help="layers per window slot (default: 1 at 32b, 4 at 7b and 72b)")
+                    help="layers per window slot (default: 1 at 32b and 72b, 4 at 7b)")
     ap.add_argument("--checkpoint-every", type=int, default=None,
                     help="the streamed step keeps every n-th layer's input for the backward and recomputes "
                          "the others (default 1; must divide --window-blocks)")
     ap.add_argument("--offload-bounds", choices=("on", "off"), default=None,
                     help="park the block-boundary activations (all but the top --device-bounds layers') in "
-                         "pinned host memory during the forward (default: on at 32b, off at 7b and 72b)")
+                         "pinned host memory during the forward (default: on at 32b and 72b, off at 7b)")
     ap.add_argument("--device-bounds", type=int, default=4)
     ap.add_argument("--keep-grads", action="store_true",
                     help="keep every adapter gradient until the step ends (default: a layer's gradients are "
                          "dropped once its AdamW step inside the backward has used them)")
     ap.add_argument("--slots", type=int, default=None,
-                    help="window slots in the device arena (default 31 at 32b, 7 at 72b: the most resident "
+                    help="window slots in the device arena (default 31 at 32b and 72b: the most resident "
                          "layers whose peak stays under the pages' streamed peaks, 10.95 and 18.87 GB; 2 at 7b)")
     ap.add_argument("--copy-streams", type=int, default=2, help="copy streams of the window (layer l on stream l mod n)")
     ap.add_argument("--no-resident", action="store_true",
