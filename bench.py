@@ -463,9 +463,18 @@ def skinny(reps: int = 50) -> int:
                            "GBps": round(v["total_bytes"] / v["total_ms"] / 1e6, 1),
                            "hbm_frac": round(v["total_bytes"] / v["total_ms"] / 1e6 / PEAK_HBM_GBPS, 4),
                            **({"tflops": round(v["total_flops"] / v["total_ms"] / 1e9, 1)} if v["total_flops"] else {})}
+        # the method's own bytes: what the forward and the backward read and write at the
+        # boundary (x, the NF4 base, A, B, y, u; dy, x, base, A, B, u, dx, dA, dB), however
+        # the library stages them internally
+        r = 16
+        base_b, a_b, b_b = N * K * 0.5625, r * K * 4, N * r * 4
+        fwd_b = T * K * 2 + base_b + a_b + b_b + T * N * 2 + T * r * 4
+        bwd_b = T * N * 2 + T * K * 2 + base_b + a_b + b_b + T * r * 4 + T * K * 2 + a_b + b_b
+        method_gbps = (fwd_b + bwd_b) / (call_us * 1e-6) / 1e9
         rows.append({"shape": name, "t": T, "k": K, "n": N, "p_drop": p, "fwd_bwd_us": round(call_us, 1),
-                     "kernels": kern})
-        log(f"{name}: fwd+bwd {call_us:.1f} us")
+                     "method_MB": round((fwd_b + bwd_b) / 1e6, 3), "method_GBps": round(method_gbps, 1),
+                     "method_hbm_frac": round(method_gbps / PEAK_HBM_GBPS, 4), "kernels": kern})
+        log(f"{name}: fwd+bwd {call_us:.1f} us, the method's {(fwd_b + bwd_b) / 1e6:.2f} MB at {method_gbps:.0f} GB/s")
     print(json.dumps({"skinny": rows, "peak_hbm_GBps": PEAK_HBM_GBPS}))
     return 0
 
@@ -572,9 +581,18 @@ def main() -> int:
         log(f"{mode} ({window_blocks} x {n_slots}, checkpoints every {checkpoint_every}): built {layers} layers "
             f"in {time.time() - t_build:.1f}s "
             f"(blob {st.layout.nbytes / 1e6:.2f} MB/layer)")
+        per_step = 0
         for w in range(args.warmup):
+            # the last warmup step of a timed leg counts its launches (timing on, times dropped)
+            count = kernel_timing and w == args.warmup - 1
+            if count:
+                ops.timing_enable(True)
+                ops.timing_collect()
             loss, gn = st.train_step(batch(st, w), order=args.order)
             torch.cuda.synchronize()
+            if count:
+                per_step = sum(v["launches"] for v in ops.timing_collect().values())
+                ops.timing_enable(False)
             log(f"{mode}: warmup step {w} loss {loss.item():.4f} grad-norm {gn.item():.4e}")
         toks = [batch(st, 1000 + s) for s in range(args.steps)]
         stats0 = st.window.stats() if st.window else None
@@ -582,9 +600,16 @@ def main() -> int:
         st.lm_copy_stats()
         # the build's device temporaries leave the allocator's cache, so the reserved peak
         # below is the step's own
+        if kernel_timing:
+            # every timing event the timed steps need is made ahead (two per launch), so
+            # that no event is created inside the timed region
+            ops.timing_reserve(2 * max(per_step, 20000) * (args.steps + 1))
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
-        ops.timing_enable(kernel_timing)
+        # inside the timed region only the dense GEMM launches carry events (the roofline
+        # kernel); the per-launch bookkeeping on the ~10^4 small launches of a step would
+        # add host time to a step whose host issue is already close to its GPU time
+        ops.timing_enable(2 if kernel_timing else 0)
         ops.timing_collect()
         free0 = torch.cuda.mem_get_info()[0]
         torch.cuda.synchronize()
@@ -604,7 +629,19 @@ def main() -> int:
         stats1 = st.window.stats() if st.window else None
         lmc = st.lm_copy_stats()
         step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-        out = {"seconds": dt, "losses": [l.item() for l in losses], "kernels": kt, "step_ms": step_ms,
+        kt_all = {}
+        if kernel_timing:
+            # after the timed region: two more steps with every launch timed, for the
+            # memory-bound kernels' table
+            ops.timing_enable(1)
+            ops.timing_collect()
+            for s in range(2):
+                st.train_step(batch(st, 2000 + s), order=args.order)
+            torch.cuda.synchronize()
+            kt_all = ops.timing_collect()
+            ops.timing_enable(False)
+        out = {"seconds": dt, "losses": [l.item() for l in losses], "kernels": kt, "kernels_all": kt_all,
+               "step_ms": step_ms,
                "peak_alloc_gb": torch.cuda.max_memory_allocated() / 1e9,
                "peak_reserved_gb": torch.cuda.max_memory_reserved() / 1e9,
                "window": None, "lm_copies": {k: v / args.steps for k, v in lmc.items()}}
@@ -622,9 +659,9 @@ def main() -> int:
                 "std_ms": round(statistics.stdev(step_ms), 2) if len(step_ms) > 1 else 0.0,
                 "min_ms": round(min(step_ms), 2), "max_ms": round(max(step_ms), 2)}
 
-    # The streamed step carries the per-launch event timing the roofline needs (its host
-    # issue time stays far below the copy-bound step).  The other legs are timed without it:
-    # in the resident step the extra host work per launch would make the step host-bound.
+    # The streamed step carries the per-launch event timing the roofline needs, on the
+    # GEMM launches only.  The other legs are timed without it: in the resident step the
+    # extra host work per launch would make the step host-bound.
     streamed = run("streamed", not args.no_kernel_timing, wblocks, slots, ckpt)
     literal = (run("streamed", False, 4, 2, 1)
                if args.shape == "32b" and (wblocks, slots) != (4, 2) and not args.no_literal_window else None)
@@ -637,7 +674,7 @@ def main() -> int:
     # roofline: the kernel with the most time in the timed region (a dense dequant-MFMA
     # GEMM at this shape), against the MFMA bf16 peak
     shapes = gemm_shapes(streamed["kernels"], args.steps)
-    hbm = hbm_kernels(streamed["kernels"], args.steps)
+    hbm = hbm_kernels(streamed["kernels_all"], 2)
     kt = by_kernel(streamed["kernels"])
     roofline = None
     if kt:

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 12
+#define MSQ_ABI_VERSION 13
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -526,9 +526,16 @@ typedef struct {
   double total_bytes;  /* algorithmic HBM bytes: every input read once, every output written once */
 } msq_kernel_timing;
 
+/* on: 0 off, 1 every launch, 2 only the launches with algorithmic flops (the dense MFMA
+ * GEMMs), which keeps the per-launch host bookkeeping off the many small kernels. */
 int msq_timing_enable(int on);
 /* Fills up to max entries; *n_out = number of kernel names seen.  Resets. */
 int msq_timing_collect(msq_kernel_timing* out, int max, int* n_out);
+/* Creates timing events ahead of use until at least `events` are pooled (two per timed
+ * launch), so that a timed region creates none: creating an event costs host time that
+ * would otherwise slow the launches being timed.  events < 0 -> MSQ_E_INVAL; a HIP
+ * failure -> MSQ_E_HIP. */
+int msq_timing_reserve(int events);
 
 #ifdef __cplusplus
 }

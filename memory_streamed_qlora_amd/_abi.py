@@ -139,10 +139,11 @@ _SIG = {
     "block_stream_destroy": (ctypes.c_int, [_P]),
     "msq_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "msq_timing_collect": (ctypes.c_int, [_P, ctypes.c_int, _P]),
+    "msq_timing_reserve": (ctypes.c_int, [ctypes.c_int]),
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 12  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 13  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

@@ -175,6 +175,9 @@ hipError_t launch_adamw(float* const* p, const float* const* g, float* const* m,
 
 // ---- timing -------------------------------------------------------------------
 bool timing_on();
+// Whether a launch of this much algorithmic work is timed (timing on, and every launch or
+// only the ones with flops).
+bool timing_wants(double flops);
 // When timing is on, returns a record id and the two events the launch must record
 // (hipExtLaunchKernelGGL start/stop); otherwise -1 and null events.  flops and bytes
 // are the launch's algorithmic work (0 where it does not apply).
@@ -186,7 +189,7 @@ template <typename F, typename... Args>
 inline hipError_t timed_launch(const char* name, const char* shape, double flops, double bytes, F kern, dim3 grid,
                                dim3 block, hipStream_t s, Args... args) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (timing_on()) {
+  if (timing_wants(flops)) {
     char label[48];
     snprintf(label, sizeof(label), "%s %s", name, shape);
     timing_begin(label, flops, bytes, &e0, &e1);

@@ -274,15 +274,18 @@ __global__ __launch_bounds__(256) void lora_skinny_reduce(ReduceArgs ra) {
 //   h_i = drop_i(in_i), j < r, c < C_i
 // (dA = du^T drop(x) with out [r][K]; dB = s dy^T u with out [N][r]).  A workgroup owns 64
 // columns of one task and CG_J ranks over all T tokens, so nothing is written twice and no
-// second pass sums partials.  Thread = (column quad cq, token slice sl): slice sl runs over
-// tokens [sl*Ts, (sl+1)*Ts) in order (Ts = ceil(T / 16)), CG_UNROLL rows in flight, with
-// the rank coefficients of its tokens loaded straight from global memory (the 16 threads of
-// a slice share each row); the 16 slice sums are then added in slice order through LDS.
+// second pass sums partials.  The rank coefficients of CG_TB tokens at a time are staged in
+// LDS (one coalesced read per workgroup); thread = (column quad cq, token slice sl) takes
+// the block's tokens sl, sl + 16, sl + 32, ... in order, CG_INFL of them with their input
+// loads in flight at once, and reads each token's 16 coefficients from LDS (the 16 threads
+// of a slice read one address; the four slices of a wave read four consecutive rows, so
+// no bank conflicts).  Slice sums are added in a fixed order: the wave's four slices by a
+// butterfly, then the four waves in order.
 constexpr int CG_J = 16;
 constexpr int CG_COLS = 64;
 constexpr int CG_SLICES = 16;
-constexpr int CG_UNROLL = 4;
-constexpr int CG_PITCH = CG_COLS + 4;  // LDS row pitch in floats (keeps float4 alignment)
+constexpr int CG_TB = 256;   // tokens whose coefficients are staged in LDS at a time
+constexpr int CG_INFL = 8;   // tokens per thread with input loads in flight
 
 struct CgTaskDev {
   const void* in;
@@ -304,7 +307,8 @@ struct CgArgs {
 
 template <typename TIN>
 __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[CG_SLICES][CG_J][CG_PITCH];
+  __shared__ __attribute__((aligned(16))) float cfs[CG_TB][CG_J];
+  __shared__ __attribute__((aligned(16))) float red[4][CG_J][CG_COLS];
   // this workgroup's task (uniform): the last one whose first block is at or before it,
   // its fields picked at constant indices
   CgTaskDev tk = a.t[0];
@@ -320,57 +324,77 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
   const bool live = c < C;
   // rank rows as float4 when whole vectors of them stay in the row and are aligned
   const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tk.coef) & 15) == 0;
-  const int64_t ts = (T + CG_SLICES - 1) / CG_SLICES;
-  const int64_t t0 = min(T, (int64_t)sl * ts), t1 = min(T, t0 + ts);
   float acc[CG_J][4];
 #pragma unroll
   for (int j = 0; j < CG_J; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
-  if (live) {
-    for (int64_t tb = t0; tb < t1; tb += CG_UNROLL) {
-      float h[CG_UNROLL][4];
-      float cf[CG_UNROLL][CG_J];
+  for (int64_t tb0 = 0; tb0 < T; tb0 += CG_TB) {
+    const int nt = (int)min((int64_t)CG_TB, T - tb0);
+    __syncthreads();  // the previous block's coefficients are no longer read
+    for (int idx = tid; idx < nt * (CG_J / 4); idx += 256) {
+      const int t = idx >> 2, q4 = 4 * (idx & 3);
+      const float* src = tk.coef + (tb0 + t) * r + j0 + q4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (vec) {
+        if (j0 + q4 < r) v = *reinterpret_cast<const float4*>(src);
+      } else {
+        v.x = j0 + q4 < r ? src[0] : 0.0f;
+        v.y = j0 + q4 + 1 < r ? src[1] : 0.0f;
+        v.z = j0 + q4 + 2 < r ? src[2] : 0.0f;
+        v.w = j0 + q4 + 3 < r ? src[3] : 0.0f;
+      }
+      *reinterpret_cast<float4*>(&cfs[t][q4]) = v;
+    }
+    __syncthreads();
+    if (!live) continue;
+    for (int tt = sl; tt < nt; tt += CG_SLICES * CG_INFL) {
+      float h[CG_INFL][4];
 #pragma unroll
-      for (int u = 0; u < CG_UNROLL; ++u) {
-        const int64_t t = min(tb + u, t1 - 1);  // rows past the slice: loaded, weighted 0
-        load4(in + t * C + c, h[u]);
-        if (vec) {
-#pragma unroll
-          for (int j4 = 0; j4 < CG_J; j4 += 4) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j0 + j4 < r) v = *reinterpret_cast<const float4*>(tk.coef + t * r + j0 + j4);
-            cf[u][j4] = v.x;
-            cf[u][j4 + 1] = v.y;
-            cf[u][j4 + 2] = v.z;
-            cf[u][j4 + 3] = v.w;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < CG_J; ++j) cf[u][j] = j0 + j < r ? tk.coef[t * r + j0 + j] : 0.0f;
-        }
+      for (int u = 0; u < CG_INFL; ++u) {
+        const int t = min(tt + CG_SLICES * u, nt - 1);  // past the block: loaded, not used
+        load4(in + (tb0 + t) * C + c, h[u]);
       }
 #pragma unroll
-      for (int u = 0; u < CG_UNROLL; ++u) {
-        const int64_t t = tb + u;
-        if (t >= t1) break;
+      for (int u = 0; u < CG_INFL; ++u) {
+        const int t = tt + CG_SLICES * u;
+        if (t >= nt) break;
         if (tk.d.threshold != 0u) {
-          const uint32_t keep = keep4(tk.d, (uint64_t)t * (uint64_t)C + (uint64_t)c);
+          const uint32_t keep = keep4(tk.d, (uint64_t)(tb0 + t) * (uint64_t)C + (uint64_t)c);
 #pragma unroll
           for (int q = 0; q < 4; ++q) h[u][q] = ((keep >> q) & 1u) ? h[u][q] * tk.d.sigma : 0.0f;
         }
 #pragma unroll
-        for (int j = 0; j < CG_J; ++j)
+        for (int j4 = 0; j4 < CG_J; j4 += 4) {
+          const float4 cf = *reinterpret_cast<const float4*>(&cfs[t][j4]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(cf[u][j], h[u][q], acc[j][q]);
+          for (int q = 0; q < 4; ++q) {
+            acc[j4][q] = fmaf(cf.x, h[u][q], acc[j4][q]);
+            acc[j4 + 1][q] = fmaf(cf.y, h[u][q], acc[j4 + 1][q]);
+            acc[j4 + 2][q] = fmaf(cf.z, h[u][q], acc[j4 + 2][q]);
+            acc[j4 + 3][q] = fmaf(cf.w, h[u][q], acc[j4 + 3][q]);
+          }
+        }
       }
     }
   }
+  // the wave's four slices (lane bits 4, 5), then the four waves in order
 #pragma unroll
   for (int j = 0; j < CG_J; ++j)
-    *reinterpret_cast<float4*>(&red[sl][j][4 * cq]) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v = acc[j][q];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      acc[j][q] = v;
+    }
+  const int wave = tid >> 6;
+  if ((tid & 63) < 16) {
+#pragma unroll
+    for (int j = 0; j < CG_J; ++j)
+      *reinterpret_cast<float4*>(&red[wave][j][4 * cq]) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  }
   __syncthreads();
-  // 16 ranks x 64 columns of sums, 4 per thread; slices added in order
   const int64_t cbase = (int64_t)((int)blockIdx.x - tk.block0) * CG_COLS;
 #pragma unroll
   for (int k = 0; k < CG_J * CG_COLS / 256; ++k) {
@@ -378,10 +402,7 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
     // [r][C] output: consecutive threads take consecutive columns; [C][r]: consecutive ranks
     const int j = tk.out_cr ? (o & (CG_J - 1)) : (o / CG_COLS);
     const int cc = tk.out_cr ? (o / CG_J) : (o & (CG_COLS - 1));
-    float v = 0.0f;
-#pragma unroll
-    for (int q = 0; q < CG_SLICES; ++q) v += red[q][j][cc];
-    v *= tk.scale;
+    const float v = (((red[0][j][cc] + red[1][j][cc]) + red[2][j][cc]) + red[3][j][cc]) * tk.scale;
     const int64_t col = cbase + cc;
     if (j0 + j >= r || col >= C) continue;
     float* po = tk.out_cr ? tk.out + col * r + j0 + j : tk.out + (int64_t)(j0 + j) * C + col;

@@ -23,7 +23,7 @@ struct Rec {
 };
 
 std::mutex g_mu;
-bool g_on = false;
+int g_on = 0;  // 0 off, 1 every launch, 2 launches with flops only
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 hipError_t g_err = hipSuccess;
@@ -44,11 +44,12 @@ hipEvent_t take_event() {
 
 }  // namespace
 
-bool timing_on() { return g_on; }
+bool timing_on() { return g_on != 0; }
+bool timing_wants(double flops) { return g_on == 1 || (g_on == 2 && flops > 0.0); }
 
 int timing_begin(const char* name, double flops, double bytes, hipEvent_t* start, hipEvent_t* stop) {
   *start = *stop = nullptr;
-  if (!g_on) return -1;
+  if (!g_on || (g_on == 2 && !(flops > 0.0))) return -1;
   std::lock_guard<std::mutex> lk(g_mu);
   Rec r;
   snprintf(r.name, sizeof(r.name), "%s", name);
@@ -74,8 +75,21 @@ using namespace msq;
 extern "C" {
 
 int msq_timing_enable(int on) {
+  if (on < 0 || on > 2) return set_error(MSQ_E_INVAL, "msq_timing_enable: on = %d (0, 1 or 2)", on);
   std::lock_guard<std::mutex> lk(g_mu);
-  g_on = on != 0;
+  g_on = on;
+  return MSQ_OK;
+}
+
+int msq_timing_reserve(int events) {
+  if (events < 0) return set_error(MSQ_E_INVAL, "msq_timing_reserve: events = %d", events);
+  std::lock_guard<std::mutex> lk(g_mu);
+  while ((int)g_pool.size() < events) {
+    hipEvent_t e = nullptr;
+    const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
+    if (err != hipSuccess) return hip_error(err, "msq_timing_reserve: hipEventCreateWithFlags");
+    g_pool.push_back(e);
+  }
   return MSQ_OK;
 }
 

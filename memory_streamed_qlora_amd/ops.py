@@ -548,9 +548,11 @@ def pinned_empty(nbytes: int) -> torch.Tensor:
     check("msq_host_alloc", lib().msq_host_alloc(nbytes, ctypes.byref(p)))
     addr = int(p.value)
 
-    def _release(_self, addr=addr):
-        if not sys.is_finalizing():
-            lib().msq_host_free(addr)
+    def _release(_self, addr=addr, finalizing=sys.is_finalizing, free=lib().msq_host_free):
+        # at interpreter exit module globals may already be gone: everything this needs is
+        # bound here, and the process's pinned memory goes with the process anyway
+        if not finalizing():
+            free(addr)
 
     owner = type("PinnedHostBytes", (ctypes.c_uint8 * nbytes,), {"__del__": _release}).from_address(addr)
     return torch.frombuffer(owner, dtype=torch.uint8)
@@ -636,8 +638,14 @@ class BlockStreamWindow:
             pass
 
 
-def timing_enable(on: bool = True) -> None:
+def timing_enable(on=True) -> None:
+    """True/1: time every launch; 2: only the dense GEMM launches; False/0: off."""
     check("msq_timing_enable", lib().msq_timing_enable(int(on)))
+
+
+def timing_reserve(events: int) -> None:
+    """Pool at least `events` timing events ahead of a timed region (two per launch)."""
+    check("msq_timing_reserve", lib().msq_timing_reserve(int(events)))
 
 
 def timing_collect() -> dict:
