@@ -243,12 +243,12 @@ def h2d_busy(window, lm, ms_per_step: float, ceiling: float) -> dict:
             "GBps_while_copying": round(rate, 1), "frac_while_copying": round(rate / ceiling, 3)}
 
 
-def rocprof_summary(d: str, timed: int = 5, total: int = 7) -> int:
+def rocprof_summary(d: str, timed: int = 5, total: int = 7, first: int = -1) -> int:
     """Summarise rocprofv3 CSV output found under directory d (kernel stats, per-dispatch
     kernel traces, counter collections, memory-copy traces) as markdown on stdout.  For a
-    kernel trace of the bench, the GEMM kernels' average is also given over the last
-    timed/total of their dispatches: the timed steps of a run with `total` streamed steps
-    of which the last `timed` are timed (no resident leg)."""
+    kernel trace of the bench, the GEMM kernels' average is also given over the dispatches
+    of the timed steps: a run of `total` streamed steps (no resident leg) of which steps
+    first .. first+timed-1 are timed (first defaults to total - timed: the last ones)."""
     import csv
     import glob
 
@@ -269,12 +269,14 @@ def rocprof_summary(d: str, timed: int = 5, total: int = 7) -> int:
                 if f"::{k}(" in r["Kernel_Name"]:
                     durs.setdefault(k, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
         print(f"### GEMM dispatches ({os.path.relpath(path, d)})\n")
-        print(f"| kernel | dispatches | avg us (all) | dispatches in the last {timed}/{total} | avg us (those) |")
+        print(f"| kernel | dispatches | avg us (all) | dispatches of the {timed} timed of {total} steps | avg us (those) |")
         print("|---|---|---|---|---|")
         for k, v in sorted(durs.items()):
             v.sort()
             us = [(b - a) / 1e3 for a, b in v]
-            last = us[len(us) - len(us) // total * timed:]
+            per = len(us) // total
+            f0 = total - timed if first < 0 else first
+            last = us[f0 * per:(f0 + timed) * per]
             print(f"| {k} | {len(us)} | {sum(us) / len(us):.1f} | {len(last)} | {sum(last) / max(1, len(last)):.1f} |")
         print()
     for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
@@ -480,7 +482,7 @@ def skinny(reps: int = 50) -> int:
 
 
 def main() -> int:
-    if len(sys.argv) in (3, 5) and sys.argv[1] == "--rocprof-summary":
+    if len(sys.argv) in (3, 5, 6) and sys.argv[1] == "--rocprof-summary":
         return rocprof_summary(sys.argv[2], *[int(a) for a in sys.argv[3:]])
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
