@@ -524,56 +524,78 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
   }
 
   // ---- output ---------------------------------------------------------------------------
-  // One 32x32 block at a time (fenced for the scheduler so the accumulators are not all
-  // copied out at once); the in-range test is skipped for blocks wholly inside [M, Nc).
-  const bool rows_in = mw + 64 <= g.M;
+  // One 32x32 block at a time through LDS: the wave writes its block into a 32 x 36 fp32
+  // staging area (the W buffers are free once every wave has left the main loop), then
+  // stores whole rows as float4, four rows of the block per pass, guarded per row.  The
+  // per-element stores straight from the accumulator layout needed a branch per element
+  // and a separate copy of that code for each output form; the kernel then ran to ~15k
+  // instructions, most of them executed once per workgroup from a cold instruction cache.
+  // Column blocks are never partial: Nc is a multiple of 64.
+  __syncthreads();
+  constexpr int SP = 36;  // staging row pitch in floats (keeps float4 rows aligned)
+  float* stage = reinterpret_cast<float*>(&sB[0][0]) + wave * (32 * SP);
+  const int srow = lane >> 3, scol = 4 * (lane & 7);  // this lane's row (of 8) and column quad
+  auto store_block = [&](const f32x16_t& blk, int i, int jn) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t nb = n0 + 32 * jn;  // first column of the block
+    if (nb >= g.Nc) return;            // uniform
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int v = 0; v < 16; ++v) stage[(8 * (v >> 2) + 4 * hk + (v & 3)) * SP + r32] = blk[v];
+    const int64_t n = nb + scol;
+    float bn[4] = {0.f, 0.f, 0.f, 0.f};
+    if (MODE == 0 && g.bias && ga.splits == 1) {
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int64_t n = n0 + 32 * jn + r32;
-      const bool all_in = rows_in && n0 + 32 * jn + 32 <= g.Nc;
-      if (!all_in && n >= g.Nc) continue;
-      const int64_t mb = mw + 32 * i + 4 * hk;
+      for (int q = 0; q < 4; ++q) bn[q] = bf16_to_f32(g.bias[n + q]);
+    }
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      const int row = srow + 8 * pass;
+      const int64_t m = mw + 32 * i + row;
+      const float4 a4 = *reinterpret_cast<const float4*>(&stage[row * SP + scol]);
+      if (m >= g.M) continue;
       if (ga.splits > 1) {
-        float* po = reinterpret_cast<float*>(g.out) + ((int64_t)split * g.M) * g.Nc + n;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t m = mb + 8 * (v >> 2) + (v & 3);
-          if (all_in || m < g.M) po[m * g.Nc] = acc[i][jn][v];
-        }
+        float* po = reinterpret_cast<float*>(g.out) + ((int64_t)split * g.M + m) * g.Nc + n;
+        *reinterpret_cast<float4*>(po) = a4;
         continue;
       }
-      const float bn = (MODE == 0 && g.bias) ? bf16_to_f32(g.bias[n]) : 0.0f;
+      float val[4] = {a4.x + bn[0], a4.y + bn[1], a4.z + bn[2], a4.w + bn[3]};
       if (g.out_f32) {
-        float* po = reinterpret_cast<float*>(g.out) + n;
-        const float* pa = reinterpret_cast<const float*>(g.addend) + n;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t m = mb + 8 * (v >> 2) + (v & 3);
-          if (!(all_in || m < g.M)) continue;
-          const float val = acc[i][jn][v] + bn;
-          po[m * g.Nc] = g.addend ? pa[m * g.Nc] + val : val;
+        float* po = reinterpret_cast<float*>(g.out) + m * g.Nc + n;
+        if (g.addend) {
+          const float4 o = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g.addend) + m * g.Nc + n);
+          val[0] = o.x + val[0];
+          val[1] = o.y + val[1];
+          val[2] = o.z + val[2];
+          val[3] = o.w + val[3];
         }
+        *reinterpret_cast<float4*>(po) = make_float4(val[0], val[1], val[2], val[3]);
       } else {
-        uint16_t* po = reinterpret_cast<uint16_t*>(g.out) + n;
-        const uint16_t* pa = reinterpret_cast<const uint16_t*>(g.addend) + n;
+        uint16_t* po = reinterpret_cast<uint16_t*>(g.out) + m * g.Nc + n;
+        if (g.addend) {
+          // forward residual: y is rounded first, as a separate add would see it;
+          // backward accumulate: one rounding of the fp32 sum
+          const uint2 o = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.addend) + m * g.Nc + n);
+          const float old[4] = {bf16_to_f32(o.x & 0xffffu), bf16_to_f32(o.x >> 16), bf16_to_f32(o.y & 0xffffu),
+                                bf16_to_f32(o.y >> 16)};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t m = mb + 8 * (v >> 2) + (v & 3);
-          if (!(all_in || m < g.M)) continue;
-          float val = acc[i][jn][v] + bn;
-          if (g.addend) {
-            // forward residual: y is rounded first, as a separate add would see it;
-            // backward accumulate: one rounding of the fp32 sum
-            if (MODE == 0) val = bf16_to_f32(bf16_rne(val));
-            val = bf16_to_f32(pa[m * g.Nc]) + val;
+          for (int q = 0; q < 4; ++q) {
+            if (MODE == 0) val[q] = bf16_to_f32(bf16_rne(val[q]));
+            val[q] = old[q] + val[q];
           }
-          po[m * g.Nc] = (uint16_t)bf16_rne(val);
         }
+        *reinterpret_cast<uint2*>(po) =
+            make_uint2(bf16_rne(val[0]) | (bf16_rne(val[1]) << 16), bf16_rne(val[2]) | (bf16_rne(val[3]) << 16));
       }
     }
+  };
+  store_block(acc[0][0], 0, 0);
+  store_block(acc[0][1], 0, 1);
+  store_block(acc[0][2], 0, 2);
+  store_block(acc[0][3], 0, 3);
+  store_block(acc[1][0], 1, 0);
+  store_block(acc[1][1], 1, 1);
+  store_block(acc[1][2], 1, 2);
+  store_block(acc[1][3], 1, 3);
 }
 
 #define MSQ_GEMM_KERNEL(name, MODE, DROP, BF16W) \
