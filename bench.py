@@ -2,8 +2,8 @@
 
 Workload: 64 decoder layers (hidden 5120, 40/8 heads, SwiGLU 27648), random N(0, 0.02)
 base quantized to NF4 and held in pinned host memory, streamed one block at a time through
-a device arena of 31 slots (one computing, the others prefetching or kept for the
-turnaround), the block-boundary activations below the top 4 layers parked in pinned host
+a device arena of 32 slots (one computing, the others prefetching or kept for the
+turnaround), the block-boundary activations below the top 2 layers parked in pinned host
 memory between the forward and the backward, the frozen lm_head streamed from pinned host
 memory by the loss, each layer's adapter gradients dropped after its AdamW step; LoRA r16
 alpha32 dropout 0.0 on all seven projections;
@@ -24,6 +24,12 @@ import os
 import platform
 import sys
 import time
+
+# The vendor BLAS behind torch's products (the step's attention and lm_head products) keeps
+# one workspace per (handle, stream), 76 MiB each by default on this platform; these
+# products run with 4 MiB, and the ~150 MB goes to the window instead.  Read when the first
+# such product runs, so it is set before anything imports torch.
+os.environ.setdefault("HIPBLASLT_WORKSPACE_SIZE", "4096")  # KiB
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -63,13 +69,13 @@ def measured_traffic(kernel: str):
 
 # Qwen2.5 stacks of the workloads: (hidden, heads, kv heads, head dim, intermediate, layers,
 # dropout, default window: layers per slot, slots, checkpoint every n layers, boundaries
-# parked in host memory).  The 32B and 72B windows hold the most layers whose peak stays
+# parked in host memory, boundaries kept on the device when parking).  The 32B and 72B windows hold the most layers whose peak stays
 # under the pages' streamed peaks for those sizes (10.95 GB, A100 results, Benchmark matrix;
 # 18.87 GB, "Poros" research post, memory paragraph); the 7B stack keeps the plain double
 # buffer of 4-layer windows (7 slots would hold all 28 of its layers).
-SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, (4, 2, 1, False)),
-          "32b": (5120, 40, 8, 128, 27648, 64, 0.0, (1, 31, 1, True)),
-          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, (1, 31, 1, True))}
+SHAPES = {"7b": (3584, 28, 4, 128, 18944, 28, 0.1, (4, 2, 1, False, 4)),
+          "32b": (5120, 40, 8, 128, 27648, 64, 0.0, (1, 32, 1, True, 2)),
+          "72b": (8192, 64, 8, 128, 29568, 80, 0.1, (1, 31, 1, True, 4))}
 
 PROJ_NAMES = {(5120, 5120): "q/o", (1024, 5120): "k/v", (27648, 5120): "gate/up", (5120, 27648): "down",
               (7168, 5120): "q+k+v", (55296, 5120): "gate+up"}
@@ -499,12 +505,14 @@ def main() -> int:
     ap.add_argument("--offload-bounds", choices=("on", "off"), default=None,
                     help="park the block-boundary activations (all but the top --device-bounds layers') in "
                          "pinned host memory during the forward (default: on at 32b and 72b, off at 7b)")
-    ap.add_argument("--device-bounds", type=int, default=4)
+    ap.add_argument("--device-bounds", type=int, default=None,
+                    help="with --offload-bounds: the top layers whose boundaries stay on the device "
+                         "(default 2 at 32b, 4 at 72b)")
     ap.add_argument("--keep-grads", action="store_true",
                     help="keep every adapter gradient until the step ends (default: a layer's gradients are "
                          "dropped once its AdamW step inside the backward has used them)")
     ap.add_argument("--slots", type=int, default=None,
-                    help="window slots in the device arena (default 31 at 32b and 72b: the most resident "
+                    help="window slots in the device arena (default 32 at 32b, 31 at 72b: the most resident "
                          "layers whose peak stays under the pages' streamed peaks, 10.95 and 18.87 GB; 2 at 7b)")
     ap.add_argument("--copy-streams", type=int, default=2, help="copy streams of the window (layer l on stream l mod n)")
     ap.add_argument("--no-resident", action="store_true",
@@ -546,7 +554,10 @@ def main() -> int:
     from memory_streamed_qlora_amd import ops, stack as S
 
     torch.cuda.set_device(0)
-    hid, heads, kvh, hd, inter, nl, p_drop, (wb_default, slots_default, ckpt_default, off_default) = SHAPES[args.shape]
+    hid, heads, kvh, hd, inter, nl, p_drop, (wb_default, slots_default, ckpt_default, off_default,
+                                             dbounds_default) = SHAPES[args.shape]
+    if args.device_bounds is None:
+        args.device_bounds = dbounds_default
     offload = off_default if args.offload_bounds is None else args.offload_bounds == "on"
     layers = args.layers or nl
     slots = args.slots or slots_default

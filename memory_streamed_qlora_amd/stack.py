@@ -392,8 +392,7 @@ class Stack:
         self.B: List[Dict[str, torch.nn.Parameter]] = []
         self.emb = self.lm = self.lnf = None
         self.lm_host: Optional[torch.Tensor] = None
-        self._lm_ring: List[torch.Tensor] = []
-        self._lm_read: List[Optional[torch.cuda.Event]] = [None, None]
+        self._lm_ring = None
         self.lm_copy_timing = False  # time each lm_head chunk copy (events on the copy stream)
         self._lm_copy_log: List[Tuple[torch.cuda.Event, torch.cuda.Event, int]] = []
         self.cos, self.sin = rope_tables(seq, shape.head_dim, self.dev)
@@ -444,8 +443,6 @@ class Stack:
             self.lm_host = ops.pinned_empty(lm.numel() * 2).view(torch.bfloat16).view(lm.shape)
             self.lm_host.copy_(lm)
             self.lm = None
-            rows = min(self.LM_CHUNK, lm.shape[0])
-            self._lm_ring = [torch.empty(rows, lm.shape[1], dtype=torch.bfloat16, device=self.dev) for _ in range(2)]
         else:
             self.lm = lm.to(self.dev, torch.bfloat16).contiguous()
         self.lnf = lnf.to(self.dev, torch.float32)
@@ -682,6 +679,10 @@ class Stack:
         M = len(toks)
         wins = self._windows()
         streamed = self.mode == "streamed"
+        # the streamed lm_head's two-chunk ring, made before the forward's work so that its
+        # first copies need not wait for the compute stream to reach the loss, and dropped
+        # after the last loss so that the backward's peak does not hold it
+        self._lm_ring = self._lm_ring_make()
         hs = [self._embed(t) for t in toks]
         bounds: List[List[torch.Tensor]] = [[] for _ in range(M)]
         ahead = self.n_slots
@@ -716,6 +717,7 @@ class Stack:
             dhs.append(hf.grad)
             losses.append(loss)
         hs = hf = hn = None
+        self._lm_ring = None
         rw = wins[::-1]
         if streamed:
             for w in rw[:ahead]:
@@ -775,11 +777,24 @@ class Stack:
 
     LM_CHUNK = 4224  # vocabulary rows per lm_head chunk (152064 = 36 x 4224)
 
+    def _lm_ring_make(self):
+        """Two device buffers of LM_CHUNK lm_head rows and the event after which the copy
+        stream may write them (None when the lm_head is on the device)."""
+        if self.lm_host is None:
+            return None
+        rows = min(self.LM_CHUNK, self.shape.vocab)
+        ring = [torch.empty(rows, self.shape.hidden, dtype=torch.bfloat16, device=self.dev) for _ in range(2)]
+        made = torch.cuda.Event()
+        made.record(torch.cuda.current_stream(self.dev))
+        return ring, made
+
     def _lm_chunks(self):
         """(first row, lm_head rows) over the vocabulary in order: views of the device
         lm_head, or, with the lm_head in pinned host memory, chunks copied through a
         two-buffer device ring on the copy stream (a buffer is refilled only after the
-        work that read its previous chunk)."""
+        work that read its previous chunk).  The ring is made at the start of the step's
+        forward (see _forward_backward) and dropped after the loss, so its memory is free
+        again for the backward, where the step's peak sits."""
         V = self.shape.vocab
         starts = list(range(0, V, self.LM_CHUNK))
         if self.lm_host is None:
@@ -787,23 +802,24 @@ class Stack:
                 yield c0, self.lm[c0:c0 + self.LM_CHUNK]
             return
         cur = torch.cuda.current_stream(self.dev)
+        ring, made = self._lm_ring if self._lm_ring is not None else self._lm_ring_make()
+        read: List[Optional[torch.cuda.Event]] = [made, made]
         copied = {}
 
         def issue(i: int) -> None:
             b, c0 = i % 2, starts[i]
             rows = min(self.LM_CHUNK, V - c0)
             with torch.cuda.stream(self.copy_stream):
-                if self._lm_read[b] is not None:
-                    self.copy_stream.wait_event(self._lm_read[b])
+                self.copy_stream.wait_event(read[b])
                 t0 = None
                 if self.lm_copy_timing:
                     t0 = torch.cuda.Event(enable_timing=True)
                     t0.record(self.copy_stream)
-                self._lm_ring[b][:rows].copy_(self.lm_host[c0:c0 + rows], non_blocking=True)
+                ring[b][:rows].copy_(self.lm_host[c0:c0 + rows], non_blocking=True)
                 ev = torch.cuda.Event(enable_timing=self.lm_copy_timing)
                 ev.record(self.copy_stream)
                 if t0 is not None:
-                    self._lm_copy_log.append((t0, ev, self._lm_ring[b][:rows].nbytes))
+                    self._lm_copy_log.append((t0, ev, ring[b][:rows].nbytes))
             copied[i] = ev
 
         for i in range(min(2, len(starts))):
@@ -811,10 +827,10 @@ class Stack:
         for i, c0 in enumerate(starts):
             rows = min(self.LM_CHUNK, V - c0)
             cur.wait_event(copied.pop(i))
-            yield c0, self._lm_ring[i % 2][:rows]
+            yield c0, ring[i % 2][:rows]
             ev = torch.cuda.Event()
             ev.record(cur)
-            self._lm_read[i % 2] = ev
+            read[i % 2] = ev
             if i + 2 < len(starts):
                 issue(i + 2)
 
@@ -976,7 +992,6 @@ class Stack:
         self.host_blobs = []
         self.dev_blobs = []
         self.lm_host = None
-        self._lm_ring = []
         if had_host:
             torch._C._host_emptyCache()
 
