@@ -501,8 +501,9 @@ int lora_fwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj* pro
     u[i] = q.u_out ? q.u_out : (float*)(ws + p.off_u[i]);
     prods[i] = {q.A, make_dropout(q.key, cfg.p_drop), 1.0f, (float*)(ws + p.off_sk[i]), u[i], 0};
   }
-  e = launch_pack_products(x, act_f32, t, k, 0, r, prods, n_proj, xb, s);
-  if (e == hipSuccess) e = launch_product_reduce(prods, n_proj, t, r, s);
+  const PackInput xin{x, k, 0, r > 0 ? n_proj : 0};
+  e = launch_pack(&xin, 1, act_f32, t, 0, r, prods, xb, 0, s);
+  if (e == hipSuccess) e = launch_product_reduce(prods, r > 0 ? n_proj : 0, t, r, s);
   float* part = (float*)(ws + p.off_part);
   size_t part_off[GEMM_MAX_SEGS];
   if (e == hipSuccess) {
@@ -591,20 +592,23 @@ int lora_bwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj_grad
         u[i] = ut;
       }
     if (nu > 0) {
-      e = launch_pack_products(x, act_f32, t, k, 0, r, up, nu, nullptr, s);
+      const PackInput xin{x, k, 0, nu};
+      e = launch_pack(&xin, 1, act_f32, t, 0, r, up, nullptr, 0, s);
       if (e == hipSuccess) e = launch_product_reduce(up, nu, t, r, s);
     }
-    // dy_i into k-steps step0 .. of the shared operand, with the partials of du_i = s dy_i B_i;
-    // one launch then sums every du
+    // every dy_i in one launch, into k-steps step0_i .. of the shared operand, with the
+    // partials of du_i = s dy_i B_i; one launch then sums every du
     LoraProduct dp[GEMM_MAX_SEGS];
+    PackInput dyin[GEMM_MAX_SEGS];
     int step0 = 0;
-    for (int i = 0; i < n_proj && e == hipSuccess; ++i) {
+    for (int i = 0; i < n_proj; ++i) {
       const msq_lora_proj_grad& q = projs[i];
       dp[i] = {q.B, no_dropout(), lscale, (float*)(ws + p.off_sk[i]), du[i], 0};
-      e = launch_pack_products(q.dy, act_f32, t, q.n, 1, r, &dp[i], 1, act, s, steps, step0);
+      dyin[i] = {q.dy, q.n, step0, r > 0 ? 1 : 0};
       step0 += (int)(q.n / 64);
     }
-    if (e == hipSuccess) e = launch_product_reduce(dp, n_proj, t, r, s);
+    if (e == hipSuccess) e = launch_pack(dyin, n_proj, act_f32, t, 1, r, dp, act, steps, s);
+    if (e == hipSuccess) e = launch_product_reduce(dp, r > 0 ? n_proj : 0, t, r, s);
     float* part = (float*)(ws + p.off_part);
     if (e == hipSuccess) {
       GemmLaunch L;

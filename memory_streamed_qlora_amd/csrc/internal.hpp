@@ -106,11 +106,13 @@ hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, c
                             int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
                             hipStream_t s, int pack_steps = 0, int pack_step0 = 0);
 
-// The same pass with the rank-r products of up to GEMM_MAX_SEGS projections that read one
-// activation (each its own matrix, dropout mask, partial buffer and output), in two
-// launches: launch_pack_products (the packing and every product's chunk partials; sets
-// each nck) and launch_product_reduce (every product's chunks summed in order, scaled).
-// The reduction may also take products of different packing passes (their own nck).
+// The same pass over up to GEMM_MAX_SEGS activations in one launch (PackInput: input i
+// has C_i columns, fills k-steps pstep0_i .. of each group of `packed`, whose stride is
+// pack_steps (0: the inputs' k-steps summed), and owns the next nprod_i of prods), with the
+// rank-r products of up to GEMM_MAX_SEGS projections in all (each its own matrix, dropout
+// mask, partial buffer and output): launch_pack (the packing and every product's chunk
+// partials; sets each nck), then launch_product_reduce (every product's chunks summed in
+// order, scaled; it may also take products of different packing passes).
 struct LoraProduct {
   const float* mat;  // [r][C] (mat_kind 0) or [C][r] (mat_kind 1)
   Dropout drop;
@@ -119,9 +121,14 @@ struct LoraProduct {
   float* out;        // [T][r]
   int nck;
 };
-hipError_t launch_pack_products(const void* in, bool in_f32, int64_t T, int64_t C, int mat_kind, int r,
-                                LoraProduct* prods, int nprod, uint16_t* packed, hipStream_t s,
-                                int pack_steps = 0, int pack_step0 = 0);
+struct PackInput {
+  const void* in;
+  int64_t C;
+  int pstep0;
+  int nprod;
+};
+hipError_t launch_pack(const PackInput* ins, int nin, bool in_f32, int64_t T, int mat_kind, int r,
+                       LoraProduct* prods, uint16_t* packed, int pack_steps, hipStream_t s);
 hipError_t launch_product_reduce(const LoraProduct* prods, int nprod, int64_t T, int r, hipStream_t s);
 
 // Column gradients of the LoRA factors, up to COLGRAD_MAX_TASKS in one launch, each

@@ -72,13 +72,15 @@ __device__ __forceinline__ void round4(const uint16_t*, float a[4]) {
 }
 __device__ __forceinline__ void round4(const float*, float[4]) {}
 
-// Packing pass over an activation [T][C] (bf16 or fp32), fused with the rank-r products
-// of up to GEMM_MAX_SEGS projections that read it (each its own adapter and dropout mask).
-// One workgroup covers 32 rows x LORA_CHUNK columns (4 k-steps of 64), one projection and
-// its ranks j0..j0+15 (grid z over projection x rank group).  Thread t handles row t >> 3
-// and 8 consecutive columns (t & 7) of every k-step, loaded coalesced, and
-//   - writes them as bf16 in MFMA-fragment order (grid z 0 only, if `packed`):
-//     lane (row + 32 * (chunk >> 2)) of sub-step (chunk & 3), see launch_pack_frag;
+// Packing pass over up to GEMM_MAX_SEGS activations [T][C_i] (bf16 or fp32) in one launch,
+// fused with the rank-r products that read them (each its own adapter and dropout mask).
+// Grid x runs over the LORA_CHUNK-column chunks of the inputs in turn (input i owns x in
+// [blk0_i, blk0_i + nck_i)), y over 32-row token groups, z over (product of the input,
+// rank group of 16).  One workgroup covers 32 rows x LORA_CHUNK columns (4 k-steps of 64)
+// of one input, one product and its ranks j0..j0+15.  Thread t handles row t >> 3 and 8
+// consecutive columns (t & 7) of every k-step, loaded coalesced, and
+//   - writes them as bf16 in MFMA-fragment order (z == 0 only, if `packed`): lane
+//     (row + 32 * (ch >> 2)) of sub-step (ch & 3), k-step pstep0_i + step of its group;
 //   - accumulates h[t][c] * M(c, j) for its 16 ranks, h = drop(in) (the projection's
 //     dropout applied to the rank-r copy only), the adapter chunk staged in LDS rank-major;
 // then the 8 threads of a row combine their partials with a fixed butterfly and the
@@ -86,35 +88,52 @@ __device__ __forceinline__ void round4(const float*, float[4]) {}
 // chunks in order.
 constexpr int PK_STEPS = LORA_CHUNK / 64;
 
+struct PackSeg {
+  const void* in;
+  int64_t C;
+  int steps, blk0, pstep0, prod0, nprod;
+};
 struct PackProj {
   const float* mat;
   float* part;
   Dropout d;
 };
 struct PackArgs {
-  int64_t T, C;
-  int steps, r, rgroups;
+  int64_t T;
+  int r, rgroups, nseg;
   uint16_t* packed;
-  int pstride, pstep0;
+  int pstride;
+  PackSeg s[GEMM_MAX_SEGS];
   PackProj p[GEMM_MAX_SEGS];
 };
 
 template <typename TIN, int MAT_KIND>
-__global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, PackArgs a) {
+__global__ __launch_bounds__(256) void pack_lora(PackArgs a) {
   __shared__ __attribute__((aligned(16))) float ms[16][LORA_CHUNK + 4];
-  const int64_t T = a.T, C = a.C;
-  const int steps = a.steps, r = a.r;
-  // projection and rank group of this workgroup (uniform); fields picked at constant indices
-  const int pi = (int)blockIdx.z / a.rgroups, rg = (int)blockIdx.z % a.rgroups;
+  const int64_t T = a.T;
+  const int r = a.r;
+  // input, product and rank group of this workgroup (uniform); argument fields are picked
+  // at constant indices
+  const int bx = blockIdx.x;
+  const int si = (a.nseg > 2 && bx >= a.s[2].blk0) ? 2 : (a.nseg > 1 && bx >= a.s[1].blk0) ? 1 : 0;
+  PackSeg sg = a.s[0];
+  if (si == 1) sg = a.s[1];
+  if (si == 2) sg = a.s[2];
+  const int zp = (int)blockIdx.z / a.rgroups, rg = (int)blockIdx.z % a.rgroups;
+  if (r > 0 && zp >= sg.nprod) return;
+  const int pi = sg.prod0 + zp;
   const float* __restrict__ mat = pi == 0 ? a.p[0].mat : pi == 1 ? a.p[1].mat : a.p[2].mat;
   float* __restrict__ part = pi == 0 ? a.p[0].part : pi == 1 ? a.p[1].part : a.p[2].part;
   Dropout d = a.p[0].d;
   if (pi == 1) d = a.p[1].d;
   if (pi == 2) d = a.p[2].d;
-  uint16_t* __restrict__ packed = blockIdx.z == 0 ? a.packed : nullptr;
-  const int pstride = a.pstride, pstep0 = a.pstep0;
+  const TIN* __restrict__ in = (const TIN*)sg.in;
+  const int64_t C = sg.C;
+  const int steps = sg.steps;
+  uint16_t* __restrict__ packed = zp == 0 ? a.packed : nullptr;
+  const int pstride = a.pstride, pstep0 = sg.pstep0;
   const int tid = threadIdx.x, row = tid >> 3, ch = tid & 7;
-  const int grp = blockIdx.y, s0 = blockIdx.x * PK_STEPS;
+  const int grp = blockIdx.y, chunk = bx - sg.blk0, s0 = chunk * PK_STEPS;
   const int nst = min(PK_STEPS, steps - s0);
   const int j0 = rg * 16;
   const int64_t m = (int64_t)grp * 32 + row;
@@ -220,7 +239,7 @@ __global__ __launch_bounds__(256) void pack_lora(const TIN* __restrict__ in, Pac
       float v = 0.0f;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) v = (jj == j) ? acc[jj] : v;
-      if (j0 + j < r) part[((int64_t)blockIdx.x * T + m) * r + j0 + j] = v;
+      if (j0 + j < r) part[((int64_t)chunk * T + m) * r + j0 + j] = v;
     }
   }
 }
@@ -447,49 +466,71 @@ __global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ pa
 }
 
 template <typename TIN, int MAT_KIND>
-hipError_t pack_lora_dispatch(const TIN* in, const PackArgs& a, int nprod, bool packs, hipStream_t s) {
-  const dim3 grid((unsigned)((a.steps + PK_STEPS - 1) / PK_STEPS), (unsigned)((a.T + 31) / 32),
-                  (unsigned)(nprod * a.rgroups));
-  const double nck = (double)((a.C + LORA_CHUNK - 1) / LORA_CHUNK);
-  const double bytes = (double)a.T * a.C * sizeof(TIN) + (packs ? (double)frag_rows(a.T) * a.C * 2 : 0.0) +
-                       (a.r > 0 ? nprod * ((double)a.r * a.C * 4 + nck * a.T * a.r * 4) : 0.0);
-  char shape[40];
-  snprintf(shape, sizeof(shape), "%lldx%lld r%d p%d", (long long)a.T, (long long)a.C, a.r, nprod);
-  return timed_launch(packs ? "pack_lora" : "lora_product", shape, 0.0, bytes, pack_lora<TIN, MAT_KIND>, grid,
-                      dim3(256), s, in, a);
+hipError_t pack_dispatch(const PackArgs& a, dim3 grid, double bytes, const char* name, const char* shape,
+                         hipStream_t s) {
+  return timed_launch(name, shape, 0.0, bytes, pack_lora<TIN, MAT_KIND>, grid, dim3(256), s, a);
 }
 
 }  // namespace
 
-hipError_t launch_pack_products(const void* in, bool in_f32, int64_t T, int64_t C, int mat_kind, int r,
-                                LoraProduct* prods, int nprod, uint16_t* packed, hipStream_t s, int pack_steps,
-                                int pack_step0) {
-  if (nprod < 0 || nprod > GEMM_MAX_SEGS || (r > 0 && nprod < 1)) return hipErrorInvalidValue;
-  const int nck = (int)((C + LORA_CHUNK - 1) / LORA_CHUNK);
-  for (int i = 0; i < nprod; ++i) prods[i].nck = nck;
-  if (T == 0 || (r == 0 && !packed)) return hipSuccess;
+hipError_t launch_pack(const PackInput* ins, int nin, bool in_f32, int64_t T, int mat_kind, int r,
+                       LoraProduct* prods, uint16_t* packed, int pack_steps, hipStream_t s) {
+  if (nin < 1 || nin > GEMM_MAX_SEGS || r < 0 || T < 0) return hipErrorInvalidValue;
   PackArgs a;
   memset(&a, 0, sizeof(a));
   a.T = T;
-  a.C = C;
-  a.steps = (int)(C / 64);
   a.r = r;
   a.rgroups = r > 0 ? (r + 15) / 16 : 1;
+  a.nseg = nin;
   a.packed = packed;
-  a.pstride = pack_steps == 0 ? a.steps : pack_steps;
-  a.pstep0 = pack_step0;
-  if (a.pstep0 < 0 || a.pstep0 + a.steps > a.pstride) return hipErrorInvalidValue;
-  const int np = r > 0 ? nprod : 1;  // r == 0: a packing pass only
-  for (int i = 0; i < np && r > 0; ++i) {
+  int steps_total = 0, nprod = 0, zmax = 1;
+  for (int i = 0; i < nin; ++i) {
+    if (ins[i].C < 64 || ins[i].C % 64 || (r > 0 && ins[i].nprod < 1)) return hipErrorInvalidValue;
+    steps_total += (int)(ins[i].C / 64);
+    if (r > 0) {
+      nprod += ins[i].nprod;
+      zmax = std::max(zmax, ins[i].nprod);
+    }
+  }
+  if (nprod > GEMM_MAX_SEGS) return hipErrorInvalidValue;
+  a.pstride = pack_steps == 0 ? steps_total : pack_steps;
+  int blocks = 0, prod0 = 0;
+  double bytes = 0.0;
+  int64_t ctot = 0;
+  for (int i = 0; i < nin; ++i) {
+    PackSeg& g = a.s[i];
+    g.in = ins[i].in;
+    g.C = ins[i].C;
+    g.steps = (int)(g.C / 64);
+    g.blk0 = blocks;
+    g.pstep0 = ins[i].pstep0;
+    g.prod0 = prod0;
+    g.nprod = r > 0 ? ins[i].nprod : 0;
+    if (g.pstep0 < 0 || g.pstep0 + g.steps > a.pstride) return hipErrorInvalidValue;
+    const int nck = (int)((g.C + LORA_CHUNK - 1) / LORA_CHUNK);
+    for (int q = 0; q < g.nprod; ++q) prods[prod0 + q].nck = nck;
+    blocks += nck;
+    prod0 += g.nprod;
+    ctot += g.C;
+    // the input once, its packed copy, each product's adapter and chunk partials
+    bytes += (double)T * g.C * (in_f32 ? 4 : 2) + (packed ? (double)frag_rows(T) * g.C * 2 : 0.0) +
+             g.nprod * ((double)r * g.C * 4 + (double)nck * T * r * 4);
+  }
+  if (T == 0 || (r == 0 && !packed)) return hipSuccess;
+  for (int i = 0; i < nprod; ++i) {
     a.p[i].mat = prods[i].mat;
     a.p[i].part = prods[i].part;
     a.p[i].d = prods[i].drop;
   }
+  const dim3 grid((unsigned)blocks, (unsigned)((T + 31) / 32), (unsigned)(zmax * a.rgroups));
+  const char* name = packed ? "pack_lora" : "lora_product";
+  char shape[48];
+  snprintf(shape, sizeof(shape), "%lldx%lld r%d p%d i%d", (long long)T, (long long)ctot, r, nprod, nin);
   if (in_f32)
-    return mat_kind == 0 ? pack_lora_dispatch<float, 0>((const float*)in, a, np, packed != nullptr, s)
-                         : pack_lora_dispatch<float, 1>((const float*)in, a, np, packed != nullptr, s);
-  return mat_kind == 0 ? pack_lora_dispatch<uint16_t, 0>((const uint16_t*)in, a, np, packed != nullptr, s)
-                       : pack_lora_dispatch<uint16_t, 1>((const uint16_t*)in, a, np, packed != nullptr, s);
+    return mat_kind == 0 ? pack_dispatch<float, 0>(a, grid, bytes, name, shape, s)
+                         : pack_dispatch<float, 1>(a, grid, bytes, name, shape, s);
+  return mat_kind == 0 ? pack_dispatch<uint16_t, 0>(a, grid, bytes, name, shape, s)
+                       : pack_dispatch<uint16_t, 1>(a, grid, bytes, name, shape, s);
 }
 
 hipError_t launch_product_reduce(const LoraProduct* prods, int nprod, int64_t T, int r, hipStream_t s) {
@@ -515,8 +556,9 @@ hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, c
                             int r, float scale, const Dropout& d, uint16_t* packed, float* part, float* out,
                             hipStream_t s, int pack_steps, int pack_step0) {
   LoraProduct pr{mat, d, scale, part, out, 0};
-  hipError_t e = launch_pack_products(in, in_f32, T, C, mat_kind, r, &pr, 1, packed, s, pack_steps, pack_step0);
-  if (e == hipSuccess) e = launch_product_reduce(&pr, 1, T, r, s);
+  const PackInput pi{in, C, pack_step0, r > 0 ? 1 : 0};
+  hipError_t e = launch_pack(&pi, 1, in_f32, T, mat_kind, r, &pr, packed, pack_steps, s);
+  if (e == hipSuccess) e = launch_product_reduce(&pr, r > 0 ? 1 : 0, T, r, s);
   return e;
 }
 
