@@ -418,9 +418,10 @@ def skinny(reps: int = 50) -> int:
     the single 896 x 896 NF4 + LoRA linear (r 16, alpha 32, dropout 0.0) and the seven
     projections of a Qwen2.5-0.5B-shaped block (q/o 896x896, k/v 128x896, gate/up 4864x896,
     down 896x4864, dropout 0.1), all at T = 512, forward and backward through the library
-    entry points.  Per kernel: average launch time (HIP events on its launches), algorithmic
-    bytes per launch (as the library records them) and the GB/s and TFLOP/s they give.
-    Prints one JSON line."""
+    entry points on the path the library picks by shape (and, for comparison, the time on
+    each of the two paths, tiled and small-tile).  Per kernel: average launch time (HIP
+    events on its launches), algorithmic bytes per launch (as the library records them) and
+    the GB/s and TFLOP/s they give.  Prints one JSON line."""
     import torch
 
     from memory_streamed_qlora_amd import ops
@@ -442,20 +443,24 @@ def skinny(reps: int = 50) -> int:
         dy = torch.randn(T, N, generator=g, device="cuda").to(torch.bfloat16)
         key = ops.rng_key(0, 0, 0, 0, 0)
 
-        def step():
-            y, u = ops.nf4_lora_fwd(x, codes, absmax, None, A, B, cfg, key)
-            ops.nf4_lora_bwd(dy, x, codes, absmax, A, B, cfg, key, u=u)
+        def step(path="auto"):
+            y, u = ops.nf4_lora_fwd(x, codes, absmax, None, A, B, cfg, key, path=path)
+            ops.nf4_lora_bwd(dy, x, codes, absmax, A, B, cfg, key, u=u, path=path)
 
-        for _ in range(5):
-            step()
-        torch.cuda.synchronize()
-        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s_ev.record()
-        for _ in range(reps):
-            step()
-        e_ev.record()
-        torch.cuda.synchronize()
-        call_us = s_ev.elapsed_time(e_ev) / reps * 1e3
+        def timed(path):
+            for _ in range(5):
+                step(path)
+            torch.cuda.synchronize()
+            s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_ev.record()
+            for _ in range(reps):
+                step(path)
+            e_ev.record()
+            torch.cuda.synchronize()
+            return s_ev.elapsed_time(e_ev) / reps * 1e3
+
+        per_path = {p_: round(timed(p_), 1) for p_ in ("tiled", "small")}
+        call_us = timed("auto")
         ops.timing_enable(True)
         ops.timing_collect()
         for _ in range(reps):
@@ -480,9 +485,12 @@ def skinny(reps: int = 50) -> int:
         bwd_b = T * N * 2 + T * K * 2 + base_b + a_b + b_b + T * r * 4 + T * K * 2 + a_b + b_b
         method_gbps = (fwd_b + bwd_b) / (call_us * 1e-6) / 1e9
         rows.append({"shape": name, "t": T, "k": K, "n": N, "p_drop": p, "fwd_bwd_us": round(call_us, 1),
+                     "path": "small" if any(k_.startswith("small_") for k_ in kern) else "tiled",
+                     "fwd_bwd_us_tiled": per_path["tiled"], "fwd_bwd_us_small": per_path["small"],
                      "method_MB": round((fwd_b + bwd_b) / 1e6, 3), "method_GBps": round(method_gbps, 1),
                      "method_hbm_frac": round(method_gbps / PEAK_HBM_GBPS, 4), "kernels": kern})
-        log(f"{name}: fwd+bwd {call_us:.1f} us, the method's {(fwd_b + bwd_b) / 1e6:.2f} MB at {method_gbps:.0f} GB/s")
+        log(f"{name}: fwd+bwd {call_us:.1f} us ({rows[-1]['path']}; tiled {per_path['tiled']}, small "
+            f"{per_path['small']}), the method's {(fwd_b + bwd_b) / 1e6:.2f} MB at {method_gbps:.0f} GB/s")
     print(json.dumps({"skinny": rows, "peak_hbm_GBps": PEAK_HBM_GBPS}))
     return 0
 

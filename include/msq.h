@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 13
+#define MSQ_ABI_VERSION 14
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -123,11 +123,23 @@ typedef struct {
 #define MSQ_ACT_F32 1u
 #define MSQ_OUT_F32 2u
 #define MSQ_U_ONLY 4u
+/* Path of a single call (nf4_lora_fwd/bwd, bf16_lora_fwd/bwd; groups always take the
+ * tiled path and reject MSQ_PATH_SMALL):
+ *   tiled:  512-token x 128-column tiles with the reduction split across workgroups
+ *           (a packing pass, the rank-r product reduction, the GEMM, the split sum);
+ *   small:  64 x 64 tiles, each over the whole reduction (one launch per forward; the
+ *           backward's input gradient with du in one launch, then the column gradients).
+ * Neither flag: the small-tile path when r <= 32 with r % 4 == 0, t <= 1024 and k, n <= 1024
+ * (shapes at which the tiled launches are latency-bound), else the tiled path.
+ * MSQ_PATH_SMALL needs r <= 32 with r % 4 == 0 (MSQ_E_SHAPE otherwise).  The two paths agree within fp32 rounding order
+ * (the oracle's parity bar holds for both); each is bitwise reproducible on its own. */
+#define MSQ_PATH_TILED 8u
+#define MSQ_PATH_SMALL 16u
 typedef struct {
   int32_t r;      /* 0 .. 64 */
   float alpha;
   float p_drop;   /* dropout probability on the LoRA input, in [0, 1) */
-  uint32_t flags; /* MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY, other bits must be 0 */
+  uint32_t flags; /* MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY | MSQ_PATH_*, other bits 0 */
 } msq_lora_cfg;
 
 /* Bytes of scratch device memory one nf4_lora_fwd or nf4_lora_bwd call with

@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build", "msq")
 ARCH = os.environ.get("MSQ_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.cpp", "codebook.cpp", "window.cpp", "loader.cpp", "timing.cpp", "quant.hip",
-           "gemm.hip", "lora.hip", "glue.hip", "noalloc.hip", "optim.hip", "hostcopy.hip"]
+           "gemm.hip", "lora.hip", "glue.hip", "noalloc.hip", "optim.hip", "hostcopy.hip", "small.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

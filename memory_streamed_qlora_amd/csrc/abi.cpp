@@ -54,8 +54,22 @@ int check_linear(const char* fn, int64_t t, int64_t k, int64_t n, const msq_lora
   if (!(cfg.p_drop >= 0.0f && cfg.p_drop < 1.0f)) return set_error(MSQ_E_DROPOUT, "%s: p_drop=%g outside [0, 1)", fn, (double)cfg.p_drop);
   if (cfg.r > 0 && !isfinite(cfg.alpha)) return set_error(MSQ_E_DROPOUT, "%s: alpha is not finite", fn);
   if (key.proj >= 16 || key.layer >= (1u << 28)) return set_error(MSQ_E_INVAL, "%s: rng key proj must be < 16 and layer < 2^28", fn);
-  if (cfg.flags & ~(MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY)) return set_error(MSQ_E_INVAL, "%s: unknown flags 0x%x", fn, cfg.flags);
+  if (cfg.flags & ~(MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY | MSQ_PATH_TILED | MSQ_PATH_SMALL))
+    return set_error(MSQ_E_INVAL, "%s: unknown flags 0x%x", fn, cfg.flags);
+  if ((cfg.flags & MSQ_PATH_TILED) && (cfg.flags & MSQ_PATH_SMALL))
+    return set_error(MSQ_E_INVAL, "%s: MSQ_PATH_TILED and MSQ_PATH_SMALL together", fn);
+  if ((cfg.flags & MSQ_PATH_SMALL) && (cfg.r > SMALL_MAX_R || cfg.r % 4))
+    return set_error(MSQ_E_SHAPE, "%s: the small-tile path holds r <= %d with r %% 4 == 0, not %d", fn, SMALL_MAX_R,
+                     cfg.r);
   return MSQ_OK;
+}
+
+// The small-tile path (one launch per forward) where the call asks for it, or where the
+// shape fits it and the call does not ask for the tiled path.
+bool use_small_path(const msq_lora_cfg& cfg, int64_t t, int64_t k, int64_t n) {
+  if (cfg.flags & MSQ_PATH_SMALL) return true;
+  if (cfg.flags & MSQ_PATH_TILED) return false;
+  return small_path_fits(t, k, n, cfg.r);
 }
 
 }  // namespace
@@ -208,6 +222,12 @@ int lora_fwd(const char* fn, const void* x, int64_t t, int64_t k, int64_t n, con
   const int r = cfg.r;
   const Dropout d = make_dropout(key, cfg.p_drop);
   const bool act_f32 = cfg.flags & MSQ_ACT_F32, out_f32 = cfg.flags & MSQ_OUT_F32;
+  if (use_small_path(cfg, t, k, n)) {
+    const SmallLinear L{t, k, n, base.codes, base.absmax, base.wbf, A, B, r, r > 0 ? cfg.alpha / (float)r : 0.0f,
+                        d, act_f32, out_f32};
+    const hipError_t e = launch_small_fwd(L, x, bias, residual, y, r > 0 ? u_out : nullptr, u_only, s);
+    return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
+  }
   float* u = u_out ? u_out : (float*)(ws + p.off_u_fwd);
   float* part = (float*)(ws + p.off_part_fwd);
   const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
@@ -278,6 +298,8 @@ int group_check(const char* fn, int64_t t, int64_t k, const msq_lora_proj* projs
   if (n_proj < 1 || n_proj > GEMM_MAX_SEGS || !projs)
     return set_error(MSQ_E_INVAL, "%s: n_proj=%d outside [1, %d]", fn, n_proj, GEMM_MAX_SEGS);
   if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY is not available for groups", fn);
+  if (cfg.flags & MSQ_PATH_SMALL)
+    return set_error(MSQ_E_INVAL, "%s: groups run on the tiled path (MSQ_PATH_SMALL is for single calls)", fn);
   int64_t ntot = 0;
   for (int i = 0; i < n_proj; ++i) {
     const msq_lora_proj& q = projs[i];
@@ -324,7 +346,23 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
   const Dropout d = make_dropout(key, cfg.p_drop);
   const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
   hipError_t e = hipSuccess;
-  if (t > 0) {
+  if (t > 0 && use_small_path(cfg, t, k, n)) {
+    // u (recomputed when not passed), then dx with du, then dA and dB from du and u
+    const bool act_f32 = cfg.flags & MSQ_ACT_F32, out_f32 = cfg.flags & MSQ_OUT_F32;
+    const SmallLinear L{t, k, n, base.codes, base.absmax, base.wbf, A, B, r, lscale, d, act_f32, out_f32};
+    float* du = (float*)(ws + p.off_du);
+    const float* uu = u;
+    if (r > 0 && !uu) {
+      float* ut = (float*)(ws + p.off_u_bwd);
+      e = launch_small_fwd(L, x, nullptr, nullptr, nullptr, ut, true, s);
+      uu = ut;
+    }
+    if (e == hipSuccess) e = launch_small_bwd(L, dy, dx, dx_accumulate, r > 0 ? du : nullptr, s);
+    if (e == hipSuccess && r > 0) {
+      const ColgradTask tasks[2] = {{x, du, dA, k, 1.0f, 0, d}, {dy, uu, dB, n, lscale, 1, no_dropout()}};
+      e = launch_colgrad(tasks, 2, act_f32, t, r, dAB_accumulate, s);
+    }
+  } else if (t > 0) {
     const bool act_f32 = cfg.flags & MSQ_ACT_F32, out_f32 = cfg.flags & MSQ_OUT_F32;
     float* part = (float*)(ws + p.off_part_bwd);
     float* du = (float*)(ws + p.off_du);
@@ -419,6 +457,8 @@ int group_bwd_check(const char* fn, int64_t t, int64_t k, const msq_lora_proj_gr
   if (n_proj < 1 || n_proj > GEMM_MAX_SEGS || !projs)
     return set_error(MSQ_E_INVAL, "%s: n_proj=%d outside [1, %d]", fn, n_proj, GEMM_MAX_SEGS);
   if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY is a forward flag", fn);
+  if (cfg.flags & MSQ_PATH_SMALL)
+    return set_error(MSQ_E_INVAL, "%s: groups run on the tiled path (MSQ_PATH_SMALL is for single calls)", fn);
   int64_t red = 0;
   for (int i = 0; i < n_proj; ++i) {
     const msq_lora_proj_grad& q = projs[i];

@@ -180,6 +180,37 @@ hipError_t launch_adamw(float* const* p, const float* const* g, float* const* m,
                         const int64_t* n, int nt, const AdamwHyper& h, float* gsq, hipStream_t s);
 
 
+// ---- small-tile path (small.hip) -------------------------------------------------
+// One launch for the forward, one (+ lora_colgrad) for the backward, at shapes where the
+// tiled path's launches are latency-bound: r <= SMALL_MAX_R with r % 4 == 0, t <= SMALL_MAX_T and k, n <=
+// SMALL_MAX_KN (then each launch is one round of at most 256 workgroups, and a wave runs
+// at most 4 of the 64-wide reduction steps).
+constexpr int SMALL_MAX_R = 32;
+constexpr int64_t SMALL_MAX_T = 1024;
+constexpr int64_t SMALL_MAX_KN = 1024;
+struct SmallLinear {
+  int64_t t, k, n;
+  const uint8_t* codes;   // NF4 base, or
+  const float* absmax;
+  const uint16_t* wbf;    // bf16 base
+  const float* A;         // [r][k]
+  const float* B;         // [n][r]
+  int r;
+  float lscale;
+  Dropout drop;
+  bool act_f32;
+  int out_f32;
+};
+bool small_path_fits(int64_t t, int64_t k, int64_t n, int r);
+// y = [residual +] (x W^T + bias + lscale u B^T) and u = drop(x) A^T (u may be null);
+// u_only: u alone (y, bias, residual unused).
+hipError_t launch_small_fwd(const SmallLinear& L, const void* x, const uint16_t* bias, const void* residual, void* y,
+                            float* u, bool u_only, hipStream_t s);
+// dx = [dx +] (dy W + keep * sigma * (du A)) with du = lscale dy B, written to du (may be
+// null).
+hipError_t launch_small_bwd(const SmallLinear& L, const void* dy, void* dx, int accumulate, float* du, hipStream_t s);
+
+
 // ---- timing -------------------------------------------------------------------
 bool timing_on();
 // Whether a launch of this much algorithmic work is timed (timing on, and every launch or

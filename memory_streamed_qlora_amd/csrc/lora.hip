@@ -291,20 +291,28 @@ __global__ __launch_bounds__(256) void lora_skinny_reduce(ReduceArgs ra) {
 // Column gradients of the LoRA factors, several in one launch:
 //   task i: out_i[j][c] (or out_i[c][j]) = [out_i +] scale_i * sum_t coef_i[t][j] * h_i[t][c],
 //   h_i = drop_i(in_i), j < r, c < C_i
-// (dA = du^T drop(x) with out [r][K]; dB = s dy^T u with out [N][r]).  A workgroup owns 64
-// columns of one task and CG_J ranks over all T tokens, so nothing is written twice and no
-// second pass sums partials.  The rank coefficients of CG_TB tokens at a time are staged in
-// LDS (one coalesced read per workgroup); thread = (column quad cq, token slice sl) takes
-// the block's tokens sl, sl + 16, sl + 32, ... in order, CG_INFL of them with their input
-// loads in flight at once, and reads each token's 16 coefficients from LDS (the 16 threads
-// of a slice read one address; the four slices of a wave read four consecutive rows, so
-// no bank conflicts).  Slice sums are added in a fixed order: the wave's four slices by a
-// butterfly, then the four waves in order.
+// (dA = du^T drop(x) with out [r][K]; dB = s dy^T u with out [N][r]).  A workgroup owns
+// `cols` columns of one task and CG_J ranks over all T tokens, so nothing is written twice
+// and no second pass sums partials.  The rank coefficients of CG_TB tokens at a time are
+// staged in LDS (one coalesced read per workgroup).  Thread = (column quad cq, rank group,
+// token slice sl of 16): it takes the block's tokens sl, sl + 16, sl + 32, ... in order,
+// CG_INFL of them with their input loads in flight at once, and reads each token's
+// coefficients from LDS (the threads of a slice read one address).  A wide task (64
+// columns per workgroup) gives each thread all 16 ranks of 4 columns; a narrow one (16
+// columns: four times the workgroups, for tasks whose wide grid would leave most CUs idle)
+// gives each thread 4 of the ranks, the 4 rank groups sitting in lane bits 2-3.  Slice sums
+// are added in a fixed order: the wave's four slices (lane bits 4, 5) by a butterfly, then
+// the four waves in order.  Both layouts run every output's multiply-adds and sums in the
+// same order, so a task's result does not depend on its layout or on the other tasks of
+// the launch.
 constexpr int CG_J = 16;
-constexpr int CG_COLS = 64;
+constexpr int CG_COLS = 64;  // columns of a wide task's workgroup
 constexpr int CG_SLICES = 16;
-constexpr int CG_TB = 256;   // tokens whose coefficients are staged in LDS at a time
+constexpr int CG_TB = 512;   // tokens whose coefficients are staged in LDS at a time
 constexpr int CG_INFL = 8;   // tokens per thread with input loads in flight
+
+// Columns per workgroup of a task: 16 when its 64-column grid would be small, else 64.
+inline int colgrad_cols(int64_t T, int64_t C) { return (C <= 4096 && T <= 4096) ? 16 : CG_COLS; }
 
 struct CgTaskDev {
   const void* in;
@@ -314,6 +322,7 @@ struct CgTaskDev {
   float scale;
   int out_cr;
   int block0;  // first workgroup of the task (blockIdx.x)
+  int cols;    // columns per workgroup: 16 or CG_COLS
   Dropout d;
 };
 struct CgArgs {
@@ -335,21 +344,36 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
   for (int i = 1; i < COLGRAD_MAX_TASKS; ++i)
     if (i < a.ntask && (int)blockIdx.x >= a.t[i].block0) tk = a.t[i];
   const TIN* in = (const TIN*)tk.in;
-  const int tid = threadIdx.x, cq = tid & 15, sl = tid >> 4;
-  const int64_t c = (int64_t)((int)blockIdx.x - tk.block0) * CG_COLS + 4 * cq;
+  const int cols = tk.cols;
+  const bool narrow = cols != CG_COLS;
+  const int tid = threadIdx.x, sl = tid >> 4;
+  const int cq = narrow ? (tid & 3) : (tid & 15);
+  const int jg = narrow ? ((tid >> 2) & 3) : 0;  // rank group (narrow: ranks 4 jg .. 4 jg + 3)
+  const int nj4 = narrow ? 1 : CG_J / 4;         // rank quads per thread
+  const int64_t c = (int64_t)((int)blockIdx.x - tk.block0) * cols + 4 * cq;
   const int j0 = blockIdx.y * CG_J;
   const int r = a.r;
   const int64_t T = a.T, C = tk.C;
   const bool live = c < C;
   // rank rows as float4 when whole vectors of them stay in the row and are aligned
   const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tk.coef) & 15) == 0;
-  float acc[CG_J][4];
+  float acc[CG_J][4];  // narrow: rows 0..3 hold ranks 4 jg .. 4 jg + 3
 #pragma unroll
   for (int j = 0; j < CG_J; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
+  float h[CG_INFL][4];
+  auto load_batch = [&](int64_t tb0, int tt, int nt) {
+#pragma unroll
+    for (int u = 0; u < CG_INFL; ++u) {
+      const int t = min(tt + CG_SLICES * u, nt - 1);  // past the block: loaded, not used
+      load4(in + (tb0 + t) * C + c, h[u]);
+    }
+  };
   for (int64_t tb0 = 0; tb0 < T; tb0 += CG_TB) {
     const int nt = (int)min((int64_t)CG_TB, T - tb0);
+    // the block's first inputs are in flight while its coefficients are staged
+    if (live) load_batch(tb0, sl, nt);
     __syncthreads();  // the previous block's coefficients are no longer read
     for (int idx = tid; idx < nt * (CG_J / 4); idx += 256) {
       const int t = idx >> 2, q4 = 4 * (idx & 3);
@@ -368,12 +392,7 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
     __syncthreads();
     if (!live) continue;
     for (int tt = sl; tt < nt; tt += CG_SLICES * CG_INFL) {
-      float h[CG_INFL][4];
-#pragma unroll
-      for (int u = 0; u < CG_INFL; ++u) {
-        const int t = min(tt + CG_SLICES * u, nt - 1);  // past the block: loaded, not used
-        load4(in + (tb0 + t) * C + c, h[u]);
-      }
+      if (tt != sl) load_batch(tb0, tt, nt);
 #pragma unroll
       for (int u = 0; u < CG_INFL; ++u) {
         const int t = tt + CG_SLICES * u;
@@ -385,13 +404,15 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
         }
 #pragma unroll
         for (int j4 = 0; j4 < CG_J; j4 += 4) {
-          const float4 cf = *reinterpret_cast<const float4*>(&cfs[t][j4]);
+          if (j4 < 4 * nj4) {  // uniform; the loop stays unrolled, acc statically indexed
+            const float4 cf = *reinterpret_cast<const float4*>(&cfs[t][j4 + 4 * jg]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[j4][q] = fmaf(cf.x, h[u][q], acc[j4][q]);
-            acc[j4 + 1][q] = fmaf(cf.y, h[u][q], acc[j4 + 1][q]);
-            acc[j4 + 2][q] = fmaf(cf.z, h[u][q], acc[j4 + 2][q]);
-            acc[j4 + 3][q] = fmaf(cf.w, h[u][q], acc[j4 + 3][q]);
+            for (int q = 0; q < 4; ++q) {
+              acc[j4][q] = fmaf(cf.x, h[u][q], acc[j4][q]);
+              acc[j4 + 1][q] = fmaf(cf.y, h[u][q], acc[j4 + 1][q]);
+              acc[j4 + 2][q] = fmaf(cf.z, h[u][q], acc[j4 + 2][q]);
+              acc[j4 + 3][q] = fmaf(cf.w, h[u][q], acc[j4 + 3][q]);
+            }
           }
         }
       }
@@ -399,28 +420,33 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
   }
   // the wave's four slices (lane bits 4, 5), then the four waves in order
 #pragma unroll
-  for (int j = 0; j < CG_J; ++j)
+  for (int j = 0; j < CG_J; ++j) {
+    if (j < 4 * nj4) {  // uniform
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float v = acc[j][q];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      acc[j][q] = v;
+      for (int q = 0; q < 4; ++q) {
+        float v = acc[j][q];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        acc[j][q] = v;
+      }
     }
+  }
   const int wave = tid >> 6;
   if ((tid & 63) < 16) {
 #pragma unroll
-    for (int j = 0; j < CG_J; ++j)
-      *reinterpret_cast<float4*>(&red[wave][j][4 * cq]) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    for (int j = 0; j < CG_J; ++j) {
+      if (j < 4 * nj4)
+        *reinterpret_cast<float4*>(&red[wave][j + 4 * jg][4 * cq]) =
+            make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    }
   }
   __syncthreads();
-  const int64_t cbase = (int64_t)((int)blockIdx.x - tk.block0) * CG_COLS;
-#pragma unroll
-  for (int k = 0; k < CG_J * CG_COLS / 256; ++k) {
+  const int64_t cbase = (int64_t)((int)blockIdx.x - tk.block0) * cols;
+  for (int k = 0; k < CG_J * cols / 256; ++k) {
     const int o = tid + 256 * k;
     // [r][C] output: consecutive threads take consecutive columns; [C][r]: consecutive ranks
-    const int j = tk.out_cr ? (o & (CG_J - 1)) : (o / CG_COLS);
-    const int cc = tk.out_cr ? (o / CG_J) : (o & (CG_COLS - 1));
+    const int j = tk.out_cr ? (o & (CG_J - 1)) : (o / cols);
+    const int cc = tk.out_cr ? (o / CG_J) : (o & (cols - 1));
     const float v = (((red[0][j][cc] + red[1][j][cc]) + red[2][j][cc]) + red[3][j][cc]) * tk.scale;
     const int64_t col = cbase + cc;
     if (j0 + j >= r || col >= C) continue;
@@ -586,7 +612,8 @@ hipError_t launch_colgrad(const ColgradTask* tasks, int ntask, bool in_f32, int6
     d.out_cr = q.out_cr;
     d.d = q.drop;
     d.block0 = blocks;
-    blocks += (int)((q.C + CG_COLS - 1) / CG_COLS);
+    d.cols = colgrad_cols(T, q.C);
+    blocks += (int)((q.C + d.cols - 1) / d.cols);
     bytes += (double)T * q.C * (in_f32 ? 4 : 2) + (double)T * r * 4 + (double)r * q.C * 4 * (accumulate ? 2 : 1);
     ctot += q.C;
   }

@@ -134,6 +134,17 @@ def _flags(act_dtype: torch.dtype, out_dtype: torch.dtype) -> int:
            (_abi.MSQ_OUT_F32 if out_dtype == torch.float32 else 0)
 
 
+_PATHS = {"auto": 0, "tiled": _abi.MSQ_PATH_TILED, "small": _abi.MSQ_PATH_SMALL}
+
+
+def _path_flags(path: str) -> int:
+    """Path flags of a single fused call: "auto" (the library picks by shape), "tiled" or
+    "small" (see MSQ_PATH_TILED / MSQ_PATH_SMALL)."""
+    if path not in _PATHS:
+        raise ValueError(f"path must be one of {sorted(_PATHS)}, not {path!r}")
+    return _PATHS[path]
+
+
 def rng_key(seed: int = 0, step: int = 0, micro: int = 0, layer: int = 0, proj: int = 0) -> RngKey:
     return RngKey(seed, step, micro, layer, proj)
 
@@ -153,12 +164,12 @@ def _base_args(base: Tuple[torch.Tensor, ...], k: int) -> Tuple[str, int, list]:
 
 
 def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype, u_only, residual,
-              noalloc=False):
+              noalloc=False, path="auto"):
     t, k = x.shape
     _req(x, "x", x.dtype, (t, k))
     fmt, n, bptr = _base_args(base, k)
     out_dtype = out_dtype or (y.dtype if y is not None else x.dtype)
-    flags = _flags(x.dtype, out_dtype)
+    flags = _flags(x.dtype, out_dtype) | _path_flags(path)
     if bias is not None:
         _req(bias, "bias", torch.bfloat16, (n,))
     r = cfg.r
@@ -199,13 +210,13 @@ def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream
 
 
 def _lora_bwd(base, dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_accumulate, workspace, stream,
-              out_dtype):
+              out_dtype, path="auto"):
     t, k = x.shape
     _req(x, "x", x.dtype, (t, k))
     fmt, n, bptr = _base_args(base, k)
     _req(dy, "dy", x.dtype, (t, n))
     out_dtype = out_dtype or (dx.dtype if dx is not None else x.dtype)
-    flags = _flags(x.dtype, out_dtype)
+    flags = _flags(x.dtype, out_dtype) | _path_flags(path)
     r = cfg.r
     if r > 0:
         _req(A, "A", torch.float32, (r, k))
@@ -330,15 +341,15 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
                  u_out: Optional[torch.Tensor] = None, want_u: bool = True,
                  workspace: Optional[Workspace] = None, stream=None,
                  out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
-                 residual: Optional[torch.Tensor] = None):
+                 residual: Optional[torch.Tensor] = None, path: str = "auto"):
     """y = [residual +] (x W^T + bias + (alpha/r) drop(x) A^T B^T), W the NF4 base.  Returns
     (y, u) (u None if not wanted).
 
     x may be bf16 or fp32; y is out_dtype (default: x's dtype, or y's if given).
     residual ([t, n], y's dtype) is added in the output pass, rounded as a separate add.
-    u_only: compute only u (y is None)."""
+    u_only: compute only u (y is None).  path: "auto" (by shape), "tiled" or "small"."""
     return _lora_fwd((codes, absmax), x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype,
-                     u_only, residual)
+                     u_only, residual, path=path)
 
 
 def nf4_lora_fwd_noalloc(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
@@ -346,12 +357,12 @@ def nf4_lora_fwd_noalloc(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Ten
                          cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
                          u_out: Optional[torch.Tensor] = None, want_u: bool = True, stream=None,
                          out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
-                         residual: Optional[torch.Tensor] = None):
+                         residual: Optional[torch.Tensor] = None, path: str = "auto"):
     """nf4_lora_fwd with the library's static per-GPU scratch in place of a workspace (the
     entry point for callers that cannot allocate).  Pass y (and u_out) to allocate nothing
     here either."""
     return _lora_fwd((codes, absmax), x, bias, A, B, cfg, key, y, u_out, want_u, None, stream, out_dtype,
-                     u_only, residual, noalloc=True)
+                     u_only, residual, noalloc=True, path=path)
 
 
 def bf16_lora_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], A: Optional[torch.Tensor],
@@ -359,10 +370,10 @@ def bf16_lora_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor]
                   u_out: Optional[torch.Tensor] = None, want_u: bool = True,
                   workspace: Optional[Workspace] = None, stream=None,
                   out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
-                  residual: Optional[torch.Tensor] = None):
+                  residual: Optional[torch.Tensor] = None, path: str = "auto"):
     """nf4_lora_fwd over a frozen base kept in bf16, w [n, k]."""
     return _lora_fwd((w,), x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype, u_only,
-                     residual)
+                     residual, path=path)
 
 
 def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
@@ -371,11 +382,12 @@ def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax:
                  dx_accumulate: bool = False, dA: Optional[torch.Tensor] = None,
                  dB: Optional[torch.Tensor] = None, dAB_accumulate: bool = False,
                  workspace: Optional[Workspace] = None, stream=None,
-                 out_dtype: Optional[torch.dtype] = None):
+                 out_dtype: Optional[torch.dtype] = None, path: str = "auto"):
     """Returns (dx, dA, dB); dA/dB are None when r == 0.  dy and x share one dtype (bf16
-    or fp32); dx is out_dtype (default: dx's dtype if given, else the activations')."""
+    or fp32); dx is out_dtype (default: dx's dtype if given, else the activations').
+    path: "auto" (by shape), "tiled" or "small"."""
     return _lora_bwd((codes, absmax), dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_accumulate,
-                     workspace, stream, out_dtype)
+                     workspace, stream, out_dtype, path=path)
 
 
 def bf16_lora_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, A: Optional[torch.Tensor],
@@ -383,10 +395,10 @@ def bf16_lora_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, A: Optiona
                   dx: Optional[torch.Tensor] = None, dx_accumulate: bool = False,
                   dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
                   dAB_accumulate: bool = False, workspace: Optional[Workspace] = None, stream=None,
-                  out_dtype: Optional[torch.dtype] = None):
+                  out_dtype: Optional[torch.dtype] = None, path: str = "auto"):
     """nf4_lora_bwd over a frozen base kept in bf16, w [n, k]."""
     return _lora_bwd((w,), dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_accumulate, workspace,
-                     stream, out_dtype)
+                     stream, out_dtype, path=path)
 
 
 # ---------------------------------------------------------------------------------

@@ -105,6 +105,27 @@ def test_linear_rejects_bad_residual():
     assert "residual" in _err()
 
 
+def test_path_flags():
+    L = abi.lib()
+    need = L.nf4_lora_workspace_size(8, 128, 128, 33)
+    args = lambda r, flags: (FAKE, 8, 128, 128, FAKE, FAKE, None, None, FAKE, FAKE,  # noqa: E731
+                             abi.LoraCfg(r, 32.0, 0.0, flags), abi.RngKey(0, 0, 0, 0, 0), FAKE, FAKE,
+                             FAKE, need, None)
+    assert L.nf4_lora_fwd(*args(16, abi.MSQ_PATH_TILED | abi.MSQ_PATH_SMALL)) == abi.MSQ_E_INVAL
+    assert "together" in _err()
+    assert L.nf4_lora_fwd(*args(33, abi.MSQ_PATH_SMALL)) == abi.MSQ_E_SHAPE
+    assert "r <= 32" in _err()
+    assert L.nf4_lora_fwd(*args(6, abi.MSQ_PATH_SMALL)) == abi.MSQ_E_SHAPE
+    assert L.nf4_lora_fwd(*args(16, 32)) == abi.MSQ_E_INVAL                 # an unknown bit
+    assert "unknown flags" in _err()
+    key = abi.RngKey(0, 0, 0, 0, 0)
+    one = (abi.LoraProj * 1)(abi.LoraProj(128, FAKE, FAKE, None, None, None, FAKE, FAKE, key, FAKE, None))
+    gneed = L.lora_group_workspace_size(8, 128, one, 1, 16)
+    assert L.lora_fwd_group(FAKE, 8, 128, one, 1, abi.LoraCfg(16, 32.0, 0.0, abi.MSQ_PATH_SMALL), FAKE, gneed,
+                            None) == abi.MSQ_E_INVAL
+    assert "tiled path" in _err()
+
+
 def test_glue_rejects_bad_arguments():
     """The pointwise glue entries validate on the host; n == 0 / t == 0 is a no-op that
     touches no pointer."""

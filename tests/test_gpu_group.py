@@ -78,10 +78,10 @@ def test_group_equals_single_calls_without_split(fmt, out_dtype):
     for i, pr in enumerate(projs):
         if fmt == "nf4":
             y, u = msq.nf4_lora_fwd(x, pr["base"][0], pr["base"][1], pr["bias"], pr["A"], pr["B"], cfg, pr["key"],
-                                    out_dtype=out_dtype, residual=pr["residual"])
+                                    out_dtype=out_dtype, residual=pr["residual"], path="tiled")
         else:
             y, u = msq.bf16_lora_fwd(x, pr["base"][0], pr["bias"], pr["A"], pr["B"], cfg, pr["key"],
-                                     out_dtype=out_dtype, residual=pr["residual"])
+                                     out_dtype=out_dtype, residual=pr["residual"], path="tiled")
         torch.cuda.synchronize()
         iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
         assert torch.equal(outs[i][0].view(iv), y.view(iv)), f"projection {i}: y differs"
@@ -103,7 +103,7 @@ def test_group_at_32b_shapes(name, K, ns):
                       "B": torch.randn(n, r, generator=g, device="cuda") * 0.01, "key": msq.rng_key(1, 0, 0, 0, i)})
     outs = msq.lora_fwd_group(x, projs, cfg)
     for i, pr in enumerate(projs):
-        y, u = msq.nf4_lora_fwd(x, pr["base"][0], pr["base"][1], None, pr["A"], pr["B"], cfg, pr["key"])
+        y, u = msq.nf4_lora_fwd(x, pr["base"][0], pr["base"][1], None, pr["A"], pr["B"], cfg, pr["key"], path="tiled")
         torch.cuda.synchronize()
         assert torch.equal(outs[i][1], u)
         d = (outs[i][0] - y).abs().max().item()
@@ -189,7 +189,8 @@ def test_group_bwd_against_single_calls(fmt, p_drop):
     ref = torch.zeros(T, K, device="cuda")
     for pr, (dA, dB) in zip(projs, grads):
         bwd = msq.nf4_lora_bwd if fmt == "nf4" else msq.bf16_lora_bwd
-        dxi, sA, sB = bwd(pr["dy"], x, *pr["base"], pr["A"], pr["B"], cfg, pr["key"], out_dtype=torch.float32)
+        dxi, sA, sB = bwd(pr["dy"], x, *pr["base"], pr["A"], pr["B"], cfg, pr["key"], out_dtype=torch.float32,
+                          path="tiled")
         torch.cuda.synchronize()
         assert torch.equal(dA.view(torch.int32), sA.view(torch.int32))
         assert torch.equal(dB.view(torch.int32), sB.view(torch.int32))
@@ -230,7 +231,7 @@ def test_group_bwd_at_32b_shapes(name, ns):
     ref = torch.zeros(T, K, device="cuda")
     for pr, (dA, dB) in zip(projs, grads):
         dxi, sA, sB = msq.nf4_lora_bwd(pr["dy"], x, *pr["base"], pr["A"], pr["B"], cfg, pr["key"],
-                                       out_dtype=torch.float32)
+                                       out_dtype=torch.float32, path="tiled")
         torch.cuda.synchronize()
         assert torch.equal(dA, sA) and torch.equal(dB, sB)
         ref += dxi

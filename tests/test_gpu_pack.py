@@ -36,18 +36,20 @@ def _u_case(T, K, r, p, seed):
     return dev, ru
 
 
-def _u_call(c, T, r):
+def _u_call(c, T, r, path):
     u = torch.full((T, r), float("nan"), device="cuda")
     msq.nf4_lora_fwd(c["x"], c["codes"], c["absmax"], None, c["A"], c["B"], c["cfg"], c["key"], u_out=u,
-                     u_only=True)
+                     u_only=True, path=path)
     torch.cuda.synchronize()
     return u
 
 
-def test_u_written_on_every_call():
+@pytest.mark.parametrize("path", ["tiled", "small"])
+def test_u_written_on_every_call(path):
     # (T, K, r, p): ragged token groups over a narrow input; a wide input whose last chunk
-    # is one k-step, with three rank groups; a single ragged token group over the widest
-    shapes = [(1000, 896, 16, 0.1), (1000, 8256, 40, 0.1), (40, 27648, 16, 0.0)]
+    # is one k-step, with three rank groups (two ranks blocks, the second partial, on the
+    # small-tile path); a single ragged token group over the widest
+    shapes = [(1000, 896, 16, 0.1), (1000, 8256, 40 if path == "tiled" else 24, 0.1), (40, 27648, 16, 0.0)]
     cases = []
     for i, (T, K, r, p) in enumerate(shapes):
         print(f"[pack u] T={T} K={K} r={r} p={p}", flush=True)
@@ -55,7 +57,7 @@ def test_u_written_on_every_call():
     first = [None] * len(shapes)
     for rnd in range(3):
         for i, ((T, K, r, p), (c, ru)) in enumerate(zip(shapes, cases)):
-            u = _u_call(c, T, r)
+            u = _u_call(c, T, r, path)
             assert not torch.isnan(u).any(), f"round {rnd} shape {i}: u not written"
             if first[i] is None:
                 assert_parity(host_f64(u), ru, name=f"u T={T} K={K} r={r}")
@@ -100,7 +102,7 @@ def test_grouped_backward_mixed_widths_in_one_launch():
         assert_parity(host_f64(dB), rB, name=f"dB{i}")
     for pr, (dA, dB) in zip(projs, grads):
         _, sA, sB = msq.nf4_lora_bwd(pr["dy"], xd, *pr["base"], pr["A"], pr["B"], cfg, pr["key"],
-                                     out_dtype=torch.float32)
+                                     out_dtype=torch.float32, path="tiled")
         torch.cuda.synchronize()
         assert torch.equal(dA.view(torch.int32), sA.view(torch.int32))
         assert torch.equal(dB.view(torch.int32), sB.view(torch.int32))
@@ -111,3 +113,25 @@ def test_grouped_backward_mixed_widths_in_one_launch():
     for (dA, dB), (gA, gB) in zip(grads, grads2):
         assert torch.equal(gA.view(torch.int32), dA.view(torch.int32))
         assert torch.equal(gB.view(torch.int32), dB.view(torch.int32))
+
+
+def test_column_gradient_layouts_agree():
+    """dA = du^T x over K = 4096 input columns (the narrow 16-column workgroups) equals the
+    first 4096 columns of the same product over K = 4160 (64-column workgroups) bit for bit:
+    both layouts run each output's multiply-adds and sums in the same order."""
+    T, N, r = 512, 256, 16
+    g = torch.Generator(device="cuda").manual_seed(41)
+    x_wide = torch.randn(T, 4160, generator=g, device="cuda").to(torch.bfloat16)
+    dy = torch.randn(T, N, generator=g, device="cuda").to(torch.bfloat16)
+    B = torch.randn(N, r, generator=g, device="cuda") * 0.01
+    cfg, key = msq.Lora(r, 32.0, 0.0), msq.rng_key(1, 0, 0, 0, 0)
+    out = []
+    for K in (4096, 4160):
+        W = (torch.randn(N, K, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        A = torch.randn(r, K, generator=g, device="cuda") * 0.01
+        u = torch.randn(T, r, generator=g, device="cuda")
+        _, dA, dB = msq.nf4_lora_bwd(dy, x_wide[:, :K].contiguous(), *msq.nf4_quantize(W), A, B, cfg, key, u=u,
+                                     path="tiled")
+        out.append((dA, dB))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0][0].view(torch.int32), out[1][0][:, :4096].contiguous().view(torch.int32))

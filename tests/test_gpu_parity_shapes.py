@@ -90,10 +90,11 @@ def _launch_case(shape, names, seed, T=512, p=0.1, samples=32):
         dx, dAB = msq.lora_bwd_group(xd, gp, cfg)
     else:
         pr, h = projs[0], host[0]
-        y, u = msq.nf4_lora_fwd(xd, pr["base"][0], pr["base"][1], pr["bias"], pr["A"], pr["B"], cfg, pr["key"])
+        y, u = msq.nf4_lora_fwd(xd, pr["base"][0], pr["base"][1], pr["bias"], pr["A"], pr["B"], cfg, pr["key"],
+                                path="tiled")
         outs = [(y, u)]
         dx, dA, dB = msq.nf4_lora_bwd(dev_bf16(h["dy"]), xd, pr["base"][0], pr["base"][1], pr["A"], pr["B"], cfg,
-                                      pr["key"], u=u)
+                                      pr["key"], u=u, path="tiled")
         dAB = [(dA, dB)]
     torch.cuda.synchronize()
     kcols = _sample(K, samples, rng)
@@ -181,10 +182,11 @@ def test_exact_integer_split_and_grouped_bitwise(ns):
     xd = dev_bf16(x)
     if len(ns) == 1:
         pr = projs[0]
-        y, u = msq.nf4_lora_fwd(xd, pr["base"][0], pr["base"][1], None, pr["A"], pr["B"], cfg, pr["key"])
+        y, u = msq.nf4_lora_fwd(xd, pr["base"][0], pr["base"][1], None, pr["A"], pr["B"], cfg, pr["key"],
+                                path="tiled")
         outs = [(y, u)]
         dx, dA, dB = msq.nf4_lora_bwd(dev_bf16(host[0][4]), xd, pr["base"][0], pr["base"][1], pr["A"], pr["B"],
-                                      cfg, pr["key"], u=u)
+                                      cfg, pr["key"], u=u, path="tiled")
         dAB = [(dA, dB)]
     else:
         outs = msq.lora_fwd_group(xd, projs, cfg)
