@@ -70,6 +70,72 @@ __device__ __forceinline__ uint4 sm_mask8(uint4 q, uint32_t keep) {
 // The register row (of a 32 x 32 MFMA result block) that lane half hk holds in register v.
 __device__ __forceinline__ int sm_row(int v, int hk) { return 8 * (v >> 2) + 4 * hk + (v & 3); }
 
+// The activation tile of a k-step (64 tokens x 64 columns, bf16 or fp32) is loaded with
+// whole rows per instruction (8 or 4 rows of 128 or 256 bytes per 64 lanes) into the wave's
+// own LDS tile, and the MFMA operands are read from there: a load whose 64 lanes each
+// fetch 16 bytes of a different row touches 32 cache lines and runs the vector memory
+// path at a fraction of its rate, which bounded the k-step before.  The LoRA factor's
+// rows (A in the forward, B in the backward) go through LDS the same way.  Each wave uses
+// only its own tiles: a fence and a wave barrier order its LDS stores before its reads
+// and its reads before the next k-step's stores.
+template <bool XF32>
+struct ActTile {
+  static constexpr int PITCH = XF32 ? 68 : 36;     // dwords per row (16-byte aligned rows)
+  static constexpr int WORDS = 64 * PITCH;
+  static constexpr int PIECES = XF32 ? 16 : 8;     // 16-byte loads per lane for the tile
+  static constexpr int ROWS_PER = XF32 ? 4 : 8;    // rows per 64-lane load
+  static constexpr int LANES_PER_ROW = XF32 ? 16 : 8;
+};
+constexpr int SM_FT = 32 * 68;  // a factor tile in floats: 32 ranks x 64 columns (+4 pad)
+// 16 bytes as a plain vector (a struct-typed copy of HIP's uint4 is lowered to a memory
+// copy that keeps the staged tile in scratch)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Loads of a tile: lane l, piece p -> row p * ROWS_PER + l / LANES_PER_ROW, 16 bytes at
+// column (l % LANES_PER_ROW) * 16 bytes.  Rows past `last` re-read `last` (in bounds).
+template <bool XF32>
+__device__ __forceinline__ void act_tile_load(u32x4_t (&q)[ActTile<XF32>::PIECES], const void* base, int64_t row0,
+                                              int64_t last, int64_t stride, int64_t col0, int lane) {
+  using AT = ActTile<XF32>;
+#pragma unroll
+  for (int p = 0; p < AT::PIECES; ++p) {
+    const int64_t row = min(row0 + p * AT::ROWS_PER + lane / AT::LANES_PER_ROW, last);
+    const int64_t e = row * stride + col0 + (lane % AT::LANES_PER_ROW) * (XF32 ? 4 : 8);  // element index
+    if (XF32)
+      q[p] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(base) + e);
+    else
+      q[p] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(base) + e);
+  }
+}
+template <bool XF32>
+__device__ __forceinline__ void act_tile_store(uint32_t* t, const u32x4_t (&q)[ActTile<XF32>::PIECES], int lane) {
+  using AT = ActTile<XF32>;
+#pragma unroll
+  for (int p = 0; p < AT::PIECES; ++p) {
+    const int row = p * AT::ROWS_PER + lane / AT::LANES_PER_ROW;
+    *reinterpret_cast<u32x4_t*>(&t[row * AT::PITCH + (lane % AT::LANES_PER_ROW) * 4]) = q[p];
+  }
+}
+// The 8 activation values of (tile row `row`, columns 32 hk + 8 c .. + 7) as the bf16
+// MFMA operand: the values themselves (bf16 tile), or their hi and lo parts (fp32 tile).
+template <bool XF32>
+__device__ __forceinline__ void act_operand(const uint32_t* t, int row, int hk, int c, bf16x8_t& hi, bf16x8_t& lo) {
+  using AT = ActTile<XF32>;
+  if (XF32) {
+    const float4 v0 = *reinterpret_cast<const float4*>(&t[row * AT::PITCH + 32 * hk + 8 * c]);
+    const float4 v1 = *reinterpret_cast<const float4*>(&t[row * AT::PITCH + 32 * hk + 8 * c + 4]);
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    sm_split8(v, hi, lo);
+  } else {
+    hi = *reinterpret_cast<const bf16x8_t*>(&t[row * AT::PITCH + 16 * hk + 4 * c]);
+  }
+}
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 struct SmallFwdArgs {
   const void* x;          // [T][K] bf16 or fp32
   const uint8_t* codes;   // NF4 base [N][K/2], absmax [N][K/64]; or
@@ -89,14 +155,22 @@ struct SmallFwdArgs {
   Nf4Lut lut;
 };
 
+// LDS of small_fwd: in the loop each wave has its activation tile and its A tile; after
+// it, the waves' partial blocks (6 per wave) and a u staging block per wave.
+template <bool XF32>
+struct FwdLds {
+  static constexpr int LOOP = SM_WAVES * (ActTile<XF32>::WORDS + SM_FT);
+  static constexpr int END = SM_WAVES * 6 * SM_BLK + SM_WAVES * 32 * 33;
+  static constexpr int WORDS = LOOP > END ? LOOP : END;
+};
+
 // MAIN: y is formed (false: u alone); LORA: r > 0.  Both are template parameters so that
 // every load of a k-step is unconditional and the compiler counts them exactly (a load
 // under a runtime branch makes it wait for all of them, the prefetched step included).
 template <bool XF32, bool BF16W, bool MAIN, bool LORA>
 __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
-  // the waves' partial tiles: [wave][block: y (i, j) as i + 2 j, then u row block 4 + i][v][lane]
-  __shared__ __attribute__((aligned(16))) float red[SM_WAVES * 6 * SM_BLK];
-  __shared__ __attribute__((aligned(16))) float ust[SM_WAVES][32 * 33];  // a wave's u block, [row][rank]
+  __shared__ __attribute__((aligned(16))) uint32_t lds[FwdLds<XF32>::WORDS];
+  using AT = ActTile<XF32>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hk = lane >> 5, r32 = lane & 31;
   const int64_t n0 = (int64_t)blockIdx.x * SM_C, m0 = (int64_t)blockIdx.y * SM_T;
@@ -104,12 +178,13 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
   const int steps = (int)(K / 64), r = a.r;
   constexpr bool main = MAIN, lora = LORA;
   const Dropout d = a.d;
-  // the lane's two token rows (clamped: rows past T only feed results that are dropped)
-  // and its two W rows; its rank in the u product
-  const int64_t mr0 = min(m0 + r32, T - 1), mr1 = min(m0 + 32 + r32, T - 1);
+  uint32_t* xt = lds + wave * (AT::WORDS + SM_FT);
+  float* at = reinterpret_cast<float*>(xt + AT::WORDS);
+  // the lane's two W rows; its rank in the u product; the rows of its activation operand
   const int64_t wn0 = n0 + r32, wn1 = n0 + 32 + r32;
-  const int rk = min(r32, max(r - 1, 0));
   const bool rk_ok = r32 < r;
+  const int rkc = min(r32, max(r - 1, 0));
+  const int64_t mr0 = min(m0 + r32, T - 1), mr1 = min(m0 + 32 + r32, T - 1);
 
   f32x16_t acc[2][2], ua[2];
 #pragma unroll
@@ -130,38 +205,29 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
       bpre[h][e] = (main && j < r) ? a.B[nc * r + j] : 0.0f;
     }
 
-  // One k-step's loads, straight into the MFMA operand layout: x (the lane's 32 columns of
-  // each of its two rows), the W rows' codes and scales (or bf16 values), A's row of the
-  // lane's rank.  The next k-step of the wave is loaded before this one is multiplied.
-  constexpr int XQ = XF32 ? 8 : 4;  // 16-byte pieces of a lane's 32 x values per row
+  // One k-step's loads: the activation tile (whole rows), the lane's two W rows (codes and
+  // scales, or bf16 values), the A tile (4 rank rows of 64 columns per 64-lane load; rows
+  // past r re-read row r - 1 and are never used).  The next k-step of the wave is loaded
+  // before this one is multiplied.
   constexpr int WQ = BF16W ? 4 : 1;
   struct Stage {
-    uint4 xq[2][XQ];
-    uint4 wq[2][WQ];
+    u32x4_t xq[AT::PIECES];
+    u32x4_t wq[2][WQ];
     float ws[2];
-    float4 aq[8];
+    f32x4_t aq[8];
   };
   auto load = [&](Stage& st, int s) {
-    const int64_t kc = (int64_t)s * 64 + 32 * hk;  // first column of this lane's 32
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-      if (XF32) {
-        st.xq[0][q] = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.x) + mr0 * K + kc)[q];
-        st.xq[1][q] = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.x) + mr1 * K + kc)[q];
-      } else {
-        st.xq[0][q] = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + mr0 * K + kc)[q];
-        st.xq[1][q] = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + mr1 * K + kc)[q];
-      }
-    }
+    const int64_t k0 = (int64_t)s * 64, kc = k0 + 32 * hk;
+    act_tile_load<XF32>(st.xq, a.x, m0, T - 1, K, k0, lane);
     if (main) {
 #pragma unroll
       for (int q = 0; q < WQ; ++q) {
         if (BF16W) {
-          st.wq[0][q] = reinterpret_cast<const uint4*>(a.wbf + wn0 * K + kc)[q];
-          st.wq[1][q] = reinterpret_cast<const uint4*>(a.wbf + wn1 * K + kc)[q];
+          st.wq[0][q] = reinterpret_cast<const u32x4_t*>(a.wbf + wn0 * K + kc)[q];
+          st.wq[1][q] = reinterpret_cast<const u32x4_t*>(a.wbf + wn1 * K + kc)[q];
         } else {
-          st.wq[0][q] = *reinterpret_cast<const uint4*>(a.codes + wn0 * (K / 2) + kc / 2);
-          st.wq[1][q] = *reinterpret_cast<const uint4*>(a.codes + wn1 * (K / 2) + kc / 2);
+          st.wq[0][q] = *reinterpret_cast<const u32x4_t*>(a.codes + wn0 * (K / 2) + kc / 2);
+          st.wq[1][q] = *reinterpret_cast<const u32x4_t*>(a.codes + wn1 * (K / 2) + kc / 2);
         }
       }
       if (!BF16W) {
@@ -171,11 +237,21 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
     }
     if (lora) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) st.aq[q] = reinterpret_cast<const float4*>(a.A + (int64_t)rk * K + kc)[q];
+      for (int q = 0; q < 8; ++q) {
+        const int rank = min(4 * q + (lane >> 4), r - 1);
+        st.aq[q] = *reinterpret_cast<const f32x4_t*>(a.A + (int64_t)rank * K + k0 + 4 * (lane & 15));
+      }
     }
   };
   auto compute = [&](const Stage& st, int s) {
     const int64_t kc = (int64_t)s * 64 + 32 * hk;
+    // the tiles into LDS (the previous k-step's reads of them are complete)
+    act_tile_store<XF32>(xt, st.xq, lane);
+    if (lora) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        *reinterpret_cast<f32x4_t*>(&at[(4 * q + (lane >> 4)) * 68 + 4 * (lane & 15)]) = st.aq[q];
+    }
     // W operands of the two column blocks, sub-steps 0..3
     uint32_t wb[2][16];
     if (main) {
@@ -191,7 +267,7 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
           }
         } else {
           const Nf4Planes P = nf4_planes(a.lut, st.ws[j]);
-          nf4_dequant32(P, st.wq[j][0], wb[j]);
+          nf4_dequant32(P, make_uint4(st.wq[j][0].x, st.wq[j][0].y, st.wq[j][0].z, st.wq[j][0].w), wb[j]);
         }
       }
     }
@@ -207,22 +283,12 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
         keep[i] = kb;
       }
     }
+    wave_sync_lds();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bf16x8_t ax[2], axl[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (XF32) {
-          const uint4 p0 = st.xq[i][2 * c], p1 = st.xq[i][2 * c + 1];
-          const uint32_t w8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-          float xv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xv[e] = __uint_as_float(w8[e]);
-          sm_split8(xv, ax[i], axl[i]);
-        } else {
-          ax[i] = __builtin_bit_cast(bf16x8_t, st.xq[i][c]);
-        }
-      }
+      for (int i = 0; i < 2; ++i) act_operand<XF32>(xt, 32 * i + r32, hk, c, ax[i], axl[i]);
       if (main) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -233,8 +299,9 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
         }
       }
       if (lora) {
-        const float av[8] = {st.aq[2 * c].x, st.aq[2 * c].y, st.aq[2 * c].z, st.aq[2 * c].w,
-                             st.aq[2 * c + 1].x, st.aq[2 * c + 1].y, st.aq[2 * c + 1].z, st.aq[2 * c + 1].w};
+        const float4 a0 = *reinterpret_cast<const float4*>(&at[rkc * 68 + 32 * hk + 8 * c]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&at[rkc * 68 + 32 * hk + 8 * c + 4]);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
         float avz[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) avz[e] = rk_ok ? av[e] : 0.0f;
@@ -254,6 +321,7 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
         }
       }
     }
+    wave_sync_lds();  // this k-step's tile reads are complete before the next one's stores
   };
   {
     Stage s0, s1;
@@ -273,6 +341,8 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
   }
 
   // ---- the waves' partials, summed in wave order ------------------------------------
+  __syncthreads();  // every wave is done with its loop tiles, which the partials overwrite
+  float* red = reinterpret_cast<float*>(lds);
   float* mine = red + wave * 6 * SM_BLK;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -307,12 +377,10 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
 
   // ---- LoRA term: y += (alpha / r) u B^T, u through LDS into the operand layout -------
   if (lora) {
-    float* us = &ust[wave][0];
+    float* us = red + SM_WAVES * 6 * SM_BLK + wave * 32 * 33;
 #pragma unroll
     for (int v = 0; v < 16; ++v) us[sm_row(v, hk) * 33 + r32] = a.lscale * uf[v];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (16 * h >= r) break;
@@ -330,7 +398,6 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
       y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ul, bh, y, 0, 0, 0);
     }
   }
-
   // ---- output: + bias, rounding, + residual (y rounded first, as a separate add) -------
   const float bn = a.bias ? bf16_to_f32(a.bias[nc]) : 0.0f;
 #pragma unroll
@@ -370,31 +437,37 @@ struct SmallBwdArgs {
   Nf4Lut lut;
 };
 
-// LDS of small_bwd: in the loop each wave has a W^T tile (64 input columns x 32 bf16 pairs
-// of W rows, pitch 36 dwords) and a B^T tile (32 ranks x 64 W rows fp32, pitch 68); after
-// it, the waves' partial blocks (6 per wave) and a u-side staging block per wave.
-constexpr int SB_WT = 64 * 36;      // dwords per wave
-constexpr int SB_BT = 32 * 68;      // floats per wave
-constexpr int SB_LOOP = SM_WAVES * (SB_WT + SB_BT);
-constexpr int SB_END = SM_WAVES * 6 * SM_BLK + SM_WAVES * 32 * 33;
-constexpr int SB_WORDS = SB_LOOP > SB_END ? SB_LOOP : SB_END;
+// LDS of small_bwd: in the loop each wave has its dy tile, a W^T tile (64 input columns x
+// 32 bf16 pairs of W rows, pitch 36 dwords) and a B^T tile (32 ranks x 64 W rows fp32,
+// pitch 68); after it, the waves' partial blocks (6 per wave) and a du staging block per
+// wave.
+constexpr int SB_WT = 64 * 36;  // dwords per wave
+template <bool XF32>
+struct BwdLds {
+  static constexpr int LOOP = SM_WAVES * (ActTile<XF32>::WORDS + SB_WT + SM_FT);
+  static constexpr int END = SM_WAVES * 6 * SM_BLK + SM_WAVES * 32 * 33;
+  static constexpr int WORDS = LOOP > END ? LOOP : END;
+};
 
-// LORA: r > 0 (then r % 4 == 0: B's rows are loaded as float4).  A template parameter for
-// the reason given at small_fwd.
+// LORA: r > 0 (then r % 4 == 0).  A template parameter for the reason given at small_fwd.
 template <bool XF32, bool BF16W, bool LORA>
 __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t lds[SB_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t lds[BwdLds<XF32>::WORDS];
+  using AT = ActTile<XF32>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hk = lane >> 5, r32 = lane & 31;
   const int64_t k0 = (int64_t)blockIdx.x * SM_C, m0 = (int64_t)blockIdx.y * SM_T;
   const int64_t T = a.T, K = a.K, N = a.N;
   const int steps = (int)(N / 64), r = a.r;
   constexpr bool lora = LORA;
-  const int64_t mr0 = min(m0 + r32, T - 1), mr1 = min(m0 + 32 + r32, T - 1);
-  uint32_t* wt = lds + wave * (SB_WT + SB_BT);
+  uint32_t* yt = lds + wave * (AT::WORDS + SB_WT + SM_FT);
+  uint32_t* wt = yt + AT::WORDS;
   float* bt = reinterpret_cast<float*>(wt + SB_WT);
   // the W rows this lane dequantizes: 2 (lane & 31) and the next, columns k0 + 32 hk ..
   const int pr = 2 * r32;
+  const bool rk_ok = r32 < r;
+  const int rkc = min(r32, max(r - 1, 0));
+  const int rq = max(r / 4, 1);  // 16-byte pieces of a B row
 
   f32x16_t acc[2][2], ua[2];
 #pragma unroll
@@ -414,58 +487,40 @@ __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
       apre[h][e] = j < r ? a.A[(int64_t)j * K + kc] : 0.0f;
     }
 
-  // One reduction step's loads: dy (the lane's 32 reduction columns of each of its two
-  // rows), two W rows over the lane's 32 input columns, B's row (64 per step, one per lane).
-  // The next step of the wave is loaded before this one is transposed and multiplied.
-  constexpr int XQ = XF32 ? 8 : 4;
+  // One reduction step's loads: the dy tile (whole rows), two W rows over the lane's 32
+  // input columns, the step's 64 rows of B (one contiguous block of 64 r floats: 16 bytes
+  // per lane and piece, pieces past the block re-read its last one and are not stored).
   constexpr int WQ = BF16W ? 8 : 1;
-  const int rq = max(r / 4, 1);  // float4 pieces of a B row
   struct Stage {
-    uint4 xq[2][XQ];
-    uint4 wq[2][WQ];
+    u32x4_t xq[AT::PIECES];
+    u32x4_t wq[2][WQ];
     float ws[2];
-    float bq[32];
+    f32x4_t bq[8];
   };
   auto load = [&](Stage& st, int s) {
-    const int64_t nr = (int64_t)s * 64 + 32 * hk;  // first reduction row of this lane's 32
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-      if (XF32) {
-        st.xq[0][q] = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.dy) + mr0 * N + nr)[q];
-        st.xq[1][q] = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.dy) + mr1 * N + nr)[q];
-      } else {
-        st.xq[0][q] = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.dy) + mr0 * N + nr)[q];
-        st.xq[1][q] = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.dy) + mr1 * N + nr)[q];
-      }
-    }
+    act_tile_load<XF32>(st.xq, a.dy, m0, T - 1, N, (int64_t)s * 64, lane);
     const int64_t wr = (int64_t)s * 64 + pr;
     const int64_t kk = k0 + 32 * hk;
     if (BF16W) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        st.wq[0][q] = reinterpret_cast<const uint4*>(a.wbf + wr * K + kk)[q];
-        st.wq[1][q] = reinterpret_cast<const uint4*>(a.wbf + (wr + 1) * K + kk)[q];
+        st.wq[0][q] = reinterpret_cast<const u32x4_t*>(a.wbf + wr * K + kk)[q];
+        st.wq[1][q] = reinterpret_cast<const u32x4_t*>(a.wbf + (wr + 1) * K + kk)[q];
       }
     } else {
-      st.wq[0][0] = *reinterpret_cast<const uint4*>(a.codes + wr * (K / 2) + kk / 2);
-      st.wq[1][0] = *reinterpret_cast<const uint4*>(a.codes + (wr + 1) * (K / 2) + kk / 2);
+      st.wq[0][0] = *reinterpret_cast<const u32x4_t*>(a.codes + wr * (K / 2) + kk / 2);
+      st.wq[1][0] = *reinterpret_cast<const u32x4_t*>(a.codes + (wr + 1) * (K / 2) + kk / 2);
       st.ws[0] = a.absmax[wr * (K / 64) + k0 / 64];
       st.ws[1] = a.absmax[(wr + 1) * (K / 64) + k0 / 64];
     }
     if (lora) {
-      // B row bn: pieces past r re-read the last one (in bounds) and are zeroed at use
-      const int64_t bn = (int64_t)s * 64 + lane;
+      const float* blk = a.B + (int64_t)s * 64 * r;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(a.B + bn * r + 4 * min(q, rq - 1));
-        st.bq[4 * q] = v.x;
-        st.bq[4 * q + 1] = v.y;
-        st.bq[4 * q + 2] = v.z;
-        st.bq[4 * q + 3] = v.w;
-      }
+      for (int q = 0; q < 8; ++q) st.bq[q] = *reinterpret_cast<const f32x4_t*>(blk + 4 * (64 * min(q, rq - 1) + lane));
     }
   };
   auto compute = [&](const Stage& st) {
+    act_tile_store<XF32>(yt, st.xq, lane);
     // W^T: input column 32 hk + e gets the bf16 pair (row 2 r32, row 2 r32 + 1) at pair r32
     uint32_t w0[16], w1[16];
     if (BF16W) {
@@ -475,8 +530,10 @@ __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
         w1[4 * q] = st.wq[1][q].x; w1[4 * q + 1] = st.wq[1][q].y; w1[4 * q + 2] = st.wq[1][q].z; w1[4 * q + 3] = st.wq[1][q].w;
       }
     } else {
-      nf4_dequant32(nf4_planes(a.lut, st.ws[0]), st.wq[0][0], w0);
-      nf4_dequant32(nf4_planes(a.lut, st.ws[1]), st.wq[1][0], w1);
+      nf4_dequant32(nf4_planes(a.lut, st.ws[0]),
+                    make_uint4(st.wq[0][0].x, st.wq[0][0].y, st.wq[0][0].z, st.wq[0][0].w), w0);
+      nf4_dequant32(nf4_planes(a.lut, st.ws[1]),
+                    make_uint4(st.wq[1][0].x, st.wq[1][0].y, st.wq[1][0].z, st.wq[1][0].w), w1);
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -484,28 +541,25 @@ __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
       wt[(32 * hk + 2 * q + 1) * 36 + r32] = __builtin_amdgcn_perm(w1[q], w0[q], 0x07060302u);
     }
     if (lora) {
+      // B block floats f = 4 (64 q + lane) + e: W row f / r of the step, rank f % r
 #pragma unroll
-      for (int j = 0; j < 32; ++j) bt[j * 68 + lane] = j < r ? st.bq[j] : 0.0f;
+      for (int q = 0; q < 8; ++q) {
+        if (q < rq) {  // uniform: no load under it
+          const int f = 4 * (64 * q + lane);
+          const int row = f / r, j = f - row * r;
+          bt[j * 68 + row] = st.bq[q].x;
+          bt[(j + 1) * 68 + row] = st.bq[q].y;
+          bt[(j + 2) * 68 + row] = st.bq[q].z;
+          bt[(j + 3) * 68 + row] = st.bq[q].w;
+        }
+      }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bf16x8_t ax[2], axl[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (XF32) {
-          const uint4 p0 = st.xq[i][2 * c], p1 = st.xq[i][2 * c + 1];
-          const uint32_t w8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-          float xv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xv[e] = __uint_as_float(w8[e]);
-          sm_split8(xv, ax[i], axl[i]);
-        } else {
-          ax[i] = __builtin_bit_cast(bf16x8_t, st.xq[i][c]);
-        }
-      }
+      for (int i = 0; i < 2; ++i) act_operand<XF32>(yt, 32 * i + r32, hk, c, ax[i], axl[i]);
       // W^T operand of column block j: column 32 j + r32, reduction rows 32 hk + 8 c .. + 7
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -514,11 +568,11 @@ __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
         for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax[i], b, acc[i][j], 0, 0, 0);
       }
       if (lora) {
-        float bv[8];
-        const float4 b0 = *reinterpret_cast<const float4*>(&bt[r32 * 68 + 32 * hk + 8 * c]);
-        const float4 b1 = *reinterpret_cast<const float4*>(&bt[r32 * 68 + 32 * hk + 8 * c + 4]);
-        bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w;
-        bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
+        const float4 b0 = *reinterpret_cast<const float4*>(&bt[rkc * 68 + 32 * hk + 8 * c]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&bt[rkc * 68 + 32 * hk + 8 * c + 4]);
+        float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = rk_ok ? bv[e] : 0.0f;
         bf16x8_t bh, bl;
         sm_split8(bv, bh, bl);
 #pragma unroll
@@ -529,10 +583,7 @@ __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
         }
       }
     }
-    // the tiles are rewritten by this wave's next step: its reads complete first
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();  // this step's tile reads are complete before the next one's stores
   };
   {
     Stage s0, s1;
