@@ -57,6 +57,26 @@ __device__ __forceinline__ void load4(const float* p, float f[4]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
 }
+// Four consecutive input values as one load (bf16 or fp32) and their fp32 values.
+template <typename TIN>
+struct CgRaw;
+template <>
+struct CgRaw<uint16_t> {
+  typedef uint32_t T __attribute__((ext_vector_type(2)));
+};
+template <>
+struct CgRaw<float> {
+  typedef float T __attribute__((ext_vector_type(4)));
+};
+__device__ __forceinline__ void cg_unpack(CgRaw<uint16_t>::T v, float f[4]) {
+  f[0] = bf16_to_f32(v.x & 0xffffu);
+  f[1] = bf16_to_f32(v.x >> 16);
+  f[2] = bf16_to_f32(v.y & 0xffffu);
+  f[3] = bf16_to_f32(v.y >> 16);
+}
+__device__ __forceinline__ void cg_unpack(CgRaw<float>::T v, float f[4]) {
+  f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+}
 // Four output values at p: one rounding to bf16, or stored as fp32.
 __device__ __forceinline__ void store4(uint16_t* p, const float a[4]) {
   *reinterpret_cast<uint2*>(p) =
@@ -296,7 +316,7 @@ __global__ __launch_bounds__(256) void lora_skinny_reduce(ReduceArgs ra) {
 // and no second pass sums partials.  The rank coefficients of CG_TB tokens at a time are
 // staged in LDS (one coalesced read per workgroup).  Thread = (column quad cq, rank group,
 // token slice sl of 16): it takes the block's tokens sl, sl + 16, sl + 32, ... in order,
-// CG_INFL of them with their input loads in flight at once, and reads each token's
+// in batches of CG_INFL whose loads are issued one batch ahead, and reads each token's
 // coefficients from LDS (the threads of a slice read one address).  A wide task (64
 // columns per workgroup) gives each thread all 16 ranks of 4 columns; a narrow one (16
 // columns: four times the workgroups, for tasks whose wide grid would leave most CUs idle)
@@ -333,7 +353,10 @@ struct CgArgs {
   int accumulate;
 };
 
-template <typename TIN>
+// VEC: r % 4 == 0 and every task's coefficient rows 16-byte aligned (float4 staging loads).
+// A template parameter: a runtime branch around the staging loads would leave the compiler
+// unsure which loads are in flight in the token loop, and it would wait for all of them.
+template <typename TIN, bool VEC>
 __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
   __shared__ __attribute__((aligned(16))) float cfs[CG_TB][CG_J];
   __shared__ __attribute__((aligned(16))) float red[4][CG_J][CG_COLS];
@@ -354,53 +377,40 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
   const int j0 = blockIdx.y * CG_J;
   const int r = a.r;
   const int64_t T = a.T, C = tk.C;
-  const bool live = c < C;
-  // rank rows as float4 when whole vectors of them stay in the row and are aligned
-  const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tk.coef) & 15) == 0;
+  // (C is a multiple of 64, so every thread's 4 columns exist; the clamp keeps the loads in
+  // bounds regardless, and the output stage stores only columns below C)
+  const int64_t cl = min(c, C - 4);
   float acc[CG_J][4];  // narrow: rows 0..3 hold ranks 4 jg .. 4 jg + 3
 #pragma unroll
   for (int j = 0; j < CG_J; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
-  float h[CG_INFL][4];
-  auto load_batch = [&](int64_t tb0, int tt, int nt) {
+  // a token's 4 input values as loaded (raw: converted where they are used, so that a
+  // prefetched batch is not waited for before the batch ahead of it is multiplied)
+  using Raw = typename CgRaw<TIN>::T;
+  Raw hb0[CG_INFL], hb1[CG_INFL];
+  auto load_batch = [&](Raw (&h)[CG_INFL], int64_t tb0, int tt, int nt) {
 #pragma unroll
     for (int u = 0; u < CG_INFL; ++u) {
       const int t = min(tt + CG_SLICES * u, nt - 1);  // past the block: loaded, not used
-      load4(in + (tb0 + t) * C + c, h[u]);
+      h[u] = *reinterpret_cast<const Raw*>(in + (tb0 + t) * C + cl);
     }
   };
-  for (int64_t tb0 = 0; tb0 < T; tb0 += CG_TB) {
-    const int nt = (int)min((int64_t)CG_TB, T - tb0);
-    // the block's first inputs are in flight while its coefficients are staged
-    if (live) load_batch(tb0, sl, nt);
-    __syncthreads();  // the previous block's coefficients are no longer read
-    for (int idx = tid; idx < nt * (CG_J / 4); idx += 256) {
-      const int t = idx >> 2, q4 = 4 * (idx & 3);
-      const float* src = tk.coef + (tb0 + t) * r + j0 + q4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (vec) {
-        if (j0 + q4 < r) v = *reinterpret_cast<const float4*>(src);
-      } else {
-        v.x = j0 + q4 < r ? src[0] : 0.0f;
-        v.y = j0 + q4 + 1 < r ? src[1] : 0.0f;
-        v.z = j0 + q4 + 2 < r ? src[2] : 0.0f;
-        v.w = j0 + q4 + 3 < r ? src[3] : 0.0f;
-      }
-      *reinterpret_cast<float4*>(&cfs[t][q4]) = v;
-    }
-    __syncthreads();
-    if (!live) continue;
-    for (int tt = sl; tt < nt; tt += CG_SLICES * CG_INFL) {
-      if (tt != sl) load_batch(tb0, tt, nt);
+  auto consume = [&](const Raw (&h)[CG_INFL], int64_t tb0, int tt, int nt) {
 #pragma unroll
-      for (int u = 0; u < CG_INFL; ++u) {
-        const int t = tt + CG_SLICES * u;
-        if (t >= nt) break;
+    for (int u = 0; u < CG_INFL; ++u) {
+      const int t = tt + CG_SLICES * u;
+      // consumed on every path (the empty asm takes the values, so the wait for the load
+      // does not sink under the guard): a load left unread on some path makes the compiler
+      // wait for every load in flight where its register is next written
+      float hv[4];
+      cg_unpack(h[u], hv);
+      asm volatile("" ::"v"(hv[0]), "v"(hv[1]), "v"(hv[2]), "v"(hv[3]));
+      if (t < nt) {
         if (tk.d.threshold != 0u) {
-          const uint32_t keep = keep4(tk.d, (uint64_t)(tb0 + t) * (uint64_t)C + (uint64_t)c);
+          const uint32_t keep = keep4(tk.d, (uint64_t)(tb0 + t) * (uint64_t)C + (uint64_t)cl);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) h[u][q] = ((keep >> q) & 1u) ? h[u][q] * tk.d.sigma : 0.0f;
+          for (int q = 0; q < 4; ++q) hv[q] = ((keep >> q) & 1u) ? hv[q] * tk.d.sigma : 0.0f;
         }
 #pragma unroll
         for (int j4 = 0; j4 < CG_J; j4 += 4) {
@@ -408,14 +418,65 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
             const float4 cf = *reinterpret_cast<const float4*>(&cfs[t][j4 + 4 * jg]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              acc[j4][q] = fmaf(cf.x, h[u][q], acc[j4][q]);
-              acc[j4 + 1][q] = fmaf(cf.y, h[u][q], acc[j4 + 1][q]);
-              acc[j4 + 2][q] = fmaf(cf.z, h[u][q], acc[j4 + 2][q]);
-              acc[j4 + 3][q] = fmaf(cf.w, h[u][q], acc[j4 + 3][q]);
+              acc[j4][q] = fmaf(cf.x, hv[q], acc[j4][q]);
+              acc[j4 + 1][q] = fmaf(cf.y, hv[q], acc[j4 + 1][q]);
+              acc[j4 + 2][q] = fmaf(cf.z, hv[q], acc[j4 + 2][q]);
+              acc[j4 + 3][q] = fmaf(cf.w, hv[q], acc[j4 + 3][q]);
             }
           }
         }
       }
+    }
+  };
+  constexpr int STEP = CG_SLICES * CG_INFL;  // tokens of one batch of the workgroup
+  for (int64_t tb0 = 0; tb0 < T; tb0 += CG_TB) {
+    const int nt = (int)min((int64_t)CG_TB, T - tb0);
+    // the block's first inputs are in flight while its coefficients are staged
+    load_batch(hb0, tb0, sl, nt);
+    if (VEC) {
+      // every load of the block's coefficients issued before any is stored (rows past the
+      // block and rank quads past r re-read valid ones; the quads are stored as zeros): one
+      // memory latency instead of one per pass of a load-store loop
+      constexpr int STG = CG_TB * (CG_J / 4) / 256;
+      f32x4_t cv[STG];
+#pragma unroll
+      for (int k = 0; k < STG; ++k) {
+        const int idx = tid + 256 * k, t = min(idx >> 2, nt - 1), q4 = 4 * (idx & 3);
+        cv[k] = *reinterpret_cast<const f32x4_t*>(tk.coef + (tb0 + t) * r + min(j0 + q4, r - 4));
+      }
+      __syncthreads();  // the previous block's coefficients are no longer read
+#pragma unroll
+      for (int k = 0; k < STG; ++k) {
+        const int idx = tid + 256 * k, t = idx >> 2, q4 = 4 * (idx & 3);
+        const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+        // (rows t >= nt, inside the CG_TB-row buffer, get row nt - 1 again and are never
+        // read; stored anyway, so every load is consumed on every path)
+        *reinterpret_cast<f32x4_t*>(&cfs[t][q4]) = j0 + q4 < r ? cv[k] : z;
+      }
+    } else {
+      __syncthreads();  // the previous block's coefficients are no longer read
+      for (int idx = tid; idx < nt * (CG_J / 4); idx += 256) {
+        const int t = idx >> 2, q4 = 4 * (idx & 3);
+        const float* src = tk.coef + (tb0 + t) * r + j0 + q4;
+        float4 v;
+        v.x = j0 + q4 < r ? src[0] : 0.0f;
+        v.y = j0 + q4 + 1 < r ? src[1] : 0.0f;
+        v.z = j0 + q4 + 2 < r ? src[2] : 0.0f;
+        v.w = j0 + q4 + 3 < r ? src[3] : 0.0f;
+        *reinterpret_cast<float4*>(&cfs[t][q4]) = v;
+      }
+    }
+    __syncthreads();
+    // two batches in turn: the next one's loads are issued before this one is multiplied.
+    // A batch past the block re-reads its last token (in bounds) and adds nothing.  The
+    // loop has one exit, on a workgroup-uniform count, so the compiler can tell that every
+    // batch it loaded was consumed when it comes round (a second, early exit had made it
+    // wait for all loads in flight at the top of every pass).
+    for (int base = 0; base < nt; base += 2 * STEP) {
+      load_batch(hb1, tb0, base + STEP + sl, nt);
+      consume(hb0, tb0, base + sl, nt);
+      load_batch(hb0, tb0, base + 2 * STEP + sl, nt);
+      consume(hb1, tb0, base + STEP + sl, nt);
     }
   }
   // the wave's four slices (lane bits 4, 5), then the four waves in order
@@ -600,9 +661,11 @@ hipError_t launch_colgrad(const ColgradTask* tasks, int ntask, bool in_f32, int6
   int blocks = 0;
   double bytes = 0.0;
   int64_t ctot = 0;
+  bool vec = r % 4 == 0;
   for (int i = 0; i < ntask; ++i) {
     const ColgradTask& q = tasks[i];
-    if (q.C < 1) return hipErrorInvalidValue;
+    if (q.C < 4 || q.C % 4) return hipErrorInvalidValue;
+    if (reinterpret_cast<uintptr_t>(q.coef) & 15) vec = false;
     CgTaskDev& d = a.t[i];
     d.in = q.in;
     d.coef = q.coef;
@@ -620,8 +683,11 @@ hipError_t launch_colgrad(const ColgradTask* tasks, int ntask, bool in_f32, int6
   const dim3 grid((unsigned)blocks, (unsigned)((r + CG_J - 1) / CG_J));
   char shape[40];
   snprintf(shape, sizeof(shape), "%lldx%lld r%d n%d", (long long)T, (long long)ctot, r, ntask);
-  return in_f32 ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float>, grid, dim3(256), s, a)
-                : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t>, grid, dim3(256), s, a);
+  if (vec)
+    return in_f32 ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float, true>, grid, dim3(256), s, a)
+                  : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t, true>, grid, dim3(256), s, a);
+  return in_f32 ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float, false>, grid, dim3(256), s, a)
+                : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t, false>, grid, dim3(256), s, a);
 }
 
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,

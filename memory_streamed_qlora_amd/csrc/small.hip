@@ -542,16 +542,17 @@ __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
     }
     if (lora) {
       // B block floats f = 4 (64 q + lane) + e: W row f / r of the step, rank f % r
+      // pieces past the block hold piece rq - 1 again and store the same values to the
+      // same places (unconditional: a load consumed under a branch would make the compiler
+      // wait for every load in flight at the top of the next step)
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        if (q < rq) {  // uniform: no load under it
-          const int f = 4 * (64 * q + lane);
-          const int row = f / r, j = f - row * r;
-          bt[j * 68 + row] = st.bq[q].x;
-          bt[(j + 1) * 68 + row] = st.bq[q].y;
-          bt[(j + 2) * 68 + row] = st.bq[q].z;
-          bt[(j + 3) * 68 + row] = st.bq[q].w;
-        }
+        const int f = 4 * (64 * min(q, rq - 1) + lane);
+        const int row = f / r, j = f - row * r;
+        bt[j * 68 + row] = st.bq[q].x;
+        bt[(j + 1) * 68 + row] = st.bq[q].y;
+        bt[(j + 2) * 68 + row] = st.bq[q].z;
+        bt[(j + 3) * 68 + row] = st.bq[q].w;
       }
     }
     wave_sync_lds();
