@@ -13,8 +13,10 @@
 //                   to the old dx (accumulating backward), and rounds once to bf16 (or
 //                   stores fp32); the LoRA term itself is folded into the GEMM's output
 //                   tiles.
-// Activations may be bf16 or fp32; with fp32 the rank-r products use the fp32
-// values and only the MFMA operand of the base product is rounded to bf16.
+// Activations may be bf16 or fp32.  The rank-r products keep fp32 accuracy: in the
+// packing pass they run on the MFMA with each fp32 operand split into bf16 hi and lo
+// parts, in the column gradients as fp32 FMAs; only the base product's MFMA operand is
+// rounded to bf16.
 // Every reduction has a fixed shape-determined order and no atomics, so results are
 // bitwise reproducible.  Dropout masks are regenerated from the Philox key wherever
 // they are needed; the same key gives the same mask in the forward, the recompute and
@@ -24,6 +26,7 @@
 #include <algorithm>
 
 #include "internal.hpp"
+#include "split_bf16.hpp"
 
 namespace msq {
 namespace {
@@ -97,15 +100,19 @@ __device__ __forceinline__ void round4(const float*, float[4]) {}
 // Grid x runs over the LORA_CHUNK-column chunks of the inputs in turn (input i owns x in
 // [blk0_i, blk0_i + nck_i)), y over 32-row token groups, z over (product of the input,
 // rank group of 16).  One workgroup covers 32 rows x LORA_CHUNK columns (4 k-steps of 64)
-// of one input, one product and its ranks j0..j0+15.  Thread t handles row t >> 3 and 8
-// consecutive columns (t & 7) of every k-step, loaded coalesced, and
+// of one input, one product and its ranks j0..j0+15.  Wave w takes the 16 rows from
+// 16 (w & 1) and the k-steps 2 (w >> 1), 2 (w >> 1) + 1; its lane (r16, kg) loads the 8
+// columns 32 kb + 8 kg .. of row r16 in both 32-column halves kb of each k-step
+// (coalesced), and
 //   - writes them as bf16 in MFMA-fragment order (z == 0 only, if `packed`): lane
-//     (row + 32 * (ch >> 2)) of sub-step (ch & 3), k-step pstep0_i + step of its group;
-//   - accumulates h[t][c] * M(c, j) for its 16 ranks, h = drop(in) (the projection's
-//     dropout applied to the rank-r copy only), the adapter chunk staged in LDS rank-major;
-// then the 8 threads of a row combine their partials with a fixed butterfly and the
-// chunk partial goes to the projection's part[chunk][t][j]; lora_skinny_reduce sums the
-// chunks in order.
+//     (row + 32 kb) of sub-step kg, k-step pstep0_i + step of its group;
+//   - multiplies them, masked by the projection's dropout (the rank-r copy only), with
+//     the adapter chunk staged in LDS rank-major: they are the A operand of a 16 x 16 x 32
+//     bf16 MFMA whose B operand is 8 consecutive columns of one rank row, each fp32
+//     operand split into bf16 hi and lo parts (hi*hi + hi*lo + lo*hi);
+// then the two waves of a row block add their fp32 results in k order and scale the sum
+// by the dropout's 1 / (1 - p), and the chunk partial goes to the projection's
+// part[chunk][t][j]; lora_skinny_reduce sums the chunks in order.
 constexpr int PK_STEPS = LORA_CHUNK / 64;
 
 struct PackSeg {
@@ -152,21 +159,28 @@ __global__ __launch_bounds__(256) void pack_lora(PackArgs a) {
   const int steps = sg.steps;
   uint16_t* __restrict__ packed = zp == 0 ? a.packed : nullptr;
   const int pstride = a.pstride, pstep0 = sg.pstep0;
-  const int tid = threadIdx.x, row = tid >> 3, ch = tid & 7;
+  // Lane (r16, kg) of wave w: row 16 (w & 1) + r16 of the group, k-steps 2 (w >> 1) and
+  // 2 (w >> 1) + 1 of the chunk, in each the columns 32 kb + 8 kg .. + 7 of both halves kb:
+  // exactly the A operand of a 16 x 16 x 32 MFMA (row r16, k-group kg), and a 16-byte piece
+  // of the packed fragment (lane row + 32 kb, sub-step kg).
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kg = lane >> 4, rb = wave & 1, kh = wave >> 1;
   const int grp = blockIdx.y, chunk = bx - sg.blk0, s0 = chunk * PK_STEPS;
   const int nst = min(PK_STEPS, steps - s0);
   const int j0 = rg * 16;
-  const int64_t m = (int64_t)grp * 32 + row;
+  const int row = 16 * rb + r16;
+  const int64_t m = (int64_t)grp * 32 + row, mc = min(m, T - 1);
+  const bool mrow = m < T;
   const int64_t c0 = (int64_t)s0 * 64;
-  // this thread's activation loads first (PK_STEPS x 8 elements in flight), so that their
-  // latency overlaps the staging of the adapter chunk below
-  float fa[PK_STEPS][8];
+  // this lane's activation loads first, so that their latency overlaps the staging of the
+  // adapter chunk below (k-steps past the chunk and rows past T re-read valid ones; their
+  // values are replaced by zeros)
+  float fx[2][2][8];
 #pragma unroll
-  for (int b = 0; b < PK_STEPS; ++b) {
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) fa[b][e] = 0.0f;
-    if (b < nst && m < T) load8(in + m * C + (int64_t)(s0 + b) * 64 + ch * 8, fa[b]);
-  }
+    for (int kb = 0; kb < 2; ++kb)
+      load8(in + mc * C + (int64_t)(s0 + min(2 * kh + b, nst - 1)) * 64 + 32 * kb + 8 * kg, fx[b][kb]);
   if (r > 0) {
     // the chunk of the adapter, staged rank-major: every load issued before any LDS store
     const int ncol = nst * 64;
@@ -200,67 +214,61 @@ __global__ __launch_bounds__(256) void pack_lora(PackArgs a) {
     }
     __syncthreads();
   }
-  float acc[16];
+  // the product over this wave's 128 columns: per 32-column block one MFMA per pair of
+  // bf16 parts (x hi and lo, the adapter's hi and lo; x lo is zero for bf16 inputs and
+  // skipped), accumulated in fp32
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  for (int b = 0; b < 2; ++b) {
+    const int sl = 2 * kh + b;  // k-step within the chunk (uniform per wave)
+    const bool sok = sl < nst;
 #pragma unroll
-  for (int b = 0; b < PK_STEPS; ++b) {
-    if (b >= nst) break;
-    const int step = s0 + b;
-    const int64_t c = (int64_t)step * 64 + ch * 8;
-    float* f = fa[b];
-    if (packed) {
-      const uint4 v = make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
-                                 bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
-      const int lane = row + 32 * (ch >> 2), sub = ch & 3;
-      *reinterpret_cast<uint4*>(packed + (((int64_t)grp * pstride + pstep0 + step) * 4 + sub) * 512 + lane * 8) = v;
-    }
-    if (r > 0) {
-      if (d.threshold != 0u && m < T) {
+    for (int kb = 0; kb < 2; ++kb) {
+      float f[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t keep = keep4(d, (uint64_t)m * (uint64_t)C + (uint64_t)(c + 4 * h));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) f[4 * h + q] = ((keep >> q) & 1u) ? f[4 * h + q] * d.sigma : 0.0f;
-        }
+      for (int e = 0; e < 8; ++e) f[e] = (sok && mrow) ? fx[b][kb][e] : 0.0f;
+      if (packed && sok) {
+        const uint4 v = make_uint4(bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16),
+                                   bf16_rne(f[4]) | (bf16_rne(f[5]) << 16), bf16_rne(f[6]) | (bf16_rne(f[7]) << 16));
+        *reinterpret_cast<uint4*>(packed + (((int64_t)grp * pstride + pstep0 + s0 + sl) * 4 + kg) * 512 +
+                                  (row + 32 * kb) * 8) = v;
       }
-      const int cl = b * 64 + ch * 8;
+      if (r > 0 && sok) {  // uniform
+        const int cl = sl * 64 + 32 * kb + 8 * kg;
+        if (d.threshold != 0u && mrow) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float4 a0 = *reinterpret_cast<const float4*>(&ms[j][cl]);
-        const float4 a1 = *reinterpret_cast<const float4*>(&ms[j][cl + 4]);
-        float v = acc[j];
-        v = fmaf(f[0], a0.x, v);
-        v = fmaf(f[1], a0.y, v);
-        v = fmaf(f[2], a0.z, v);
-        v = fmaf(f[3], a0.w, v);
-        v = fmaf(f[4], a1.x, v);
-        v = fmaf(f[5], a1.y, v);
-        v = fmaf(f[6], a1.z, v);
-        v = fmaf(f[7], a1.w, v);
-        acc[j] = v;
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t keep = keep4(d, (uint64_t)m * (uint64_t)C + (uint64_t)(c0 + cl + 4 * h));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) f[4 * h + q] = ((keep >> q) & 1u) ? f[4 * h + q] : 0.0f;
+          }
+        }
+        const float4 a0 = *reinterpret_cast<const float4*>(&ms[r16][cl]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&ms[r16][cl + 4]);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        bf16x8_t xh, xl, ah, al;
+        split8_bf16(f, xh, xl);
+        split8_bf16(av, ah, al);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, ah, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, al, acc, 0, 0, 0);
+        if (sizeof(TIN) == 4) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, ah, acc, 0, 0, 0);
       }
     }
   }
   if (r == 0) return;
+  // the two waves of a row block (k-step pairs 0 and 1) summed in that order; the dropout
+  // scale applied once to the sum.  Lane (r16, kg) holds rank r16 of rows 4 kg .. 4 kg + 3.
+  __shared__ f32x4_t red[2][64];
+  if (kh == 1) red[rb][lane] = acc;
+  __syncthreads();
+  if (kh == 1) return;
+  const f32x4_t o = red[rb][lane];
+  const float sc = d.threshold != 0u ? d.sigma : 1.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    float v = acc[j];
-    v += __shfl_xor(v, 1, 8);
-    v += __shfl_xor(v, 2, 8);
-    v += __shfl_xor(v, 4, 8);
-    acc[j] = v;
-  }
-  if (m < T) {
-    // lane ch writes ranks 2*ch, 2*ch+1 of the row
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int j = 2 * ch + q;
-      float v = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) v = (jj == j) ? acc[jj] : v;
-      if (j0 + j < r) part[((int64_t)chunk * T + m) * r + j0 + j] = v;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int64_t mi = (int64_t)grp * 32 + 16 * rb + 4 * kg + i;
+    const float v = (acc[i] + o[i]) * sc;
+    if (mi < T && j0 + r16 < r) part[((int64_t)chunk * T + mi) * r + j0 + r16] = v;
   }
 }
 

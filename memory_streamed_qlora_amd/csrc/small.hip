@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "internal.hpp"
+#include "split_bf16.hpp"
 
 namespace msq {
 namespace {
@@ -44,17 +45,6 @@ constexpr int SM_C = 64;       // output (forward) or input (backward) columns p
 constexpr int SM_WAVES = 4;
 constexpr int SM_BLK = 16 * 64;  // one 32 x 32 fp32 block in register order: [v][lane]
 
-// Eight fp32 values -> bf16 hi and lo operands (hi = rne(v), lo = rne(v - hi)).
-__device__ __forceinline__ void sm_split8(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    l[i] = pack_bf16x2(v[2 * i] - bf16_to_f32(h[i] & 0xffffu), v[2 * i + 1] - bf16_to_f32(h[i] >> 16));
-  }
-  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
-  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
-}
 
 // Zero the bf16 elements of a packed 8-element operand whose keep bit (bit e) is clear.
 __device__ __forceinline__ uint4 sm_mask8(uint4 q, uint32_t keep) {
@@ -125,7 +115,7 @@ __device__ __forceinline__ void act_operand(const uint32_t* t, int row, int hk, 
     const float4 v0 = *reinterpret_cast<const float4*>(&t[row * AT::PITCH + 32 * hk + 8 * c]);
     const float4 v1 = *reinterpret_cast<const float4*>(&t[row * AT::PITCH + 32 * hk + 8 * c + 4]);
     const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    sm_split8(v, hi, lo);
+    split8_bf16(v, hi, lo);
   } else {
     hi = *reinterpret_cast<const bf16x8_t*>(&t[row * AT::PITCH + 16 * hk + 4 * c]);
   }
@@ -306,7 +296,7 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) avz[e] = rk_ok ? av[e] : 0.0f;
         bf16x8_t ah, al;
-        sm_split8(avz, ah, al);
+        split8_bf16(avz, ah, al);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           bf16x8_t xm = ax[i], xml = axl[i];
@@ -391,8 +381,8 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
         uv[e] = j < r ? us[r32 * 33 + j] : 0.0f;
       }
       bf16x8_t uh, ul, bh, bl;
-      sm_split8(uv, uh, ul);
-      sm_split8(bpre[h], bh, bl);
+      split8_bf16(uv, uh, ul);
+      split8_bf16(bpre[h], bh, bl);
       y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uh, bh, y, 0, 0, 0);
       y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uh, bl, y, 0, 0, 0);
       y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ul, bh, y, 0, 0, 0);
@@ -575,7 +565,7 @@ __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) bv[e] = rk_ok ? bv[e] : 0.0f;
         bf16x8_t bh, bl;
-        sm_split8(bv, bh, bl);
+        split8_bf16(bv, bh, bl);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           ua[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax[i], bh, ua[i], 0, 0, 0);
@@ -657,8 +647,8 @@ __global__ __launch_bounds__(256) void small_bwd(SmallBwdArgs a) {
         uv[e] = j < r ? us[r32 * 33 + j] : 0.0f;
       }
       bf16x8_t uh, ul, ah, al;
-      sm_split8(uv, uh, ul);
-      sm_split8(apre[h], ah, al);
+      split8_bf16(uv, uh, ul);
+      split8_bf16(apre[h], ah, al);
       t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uh, ah, t, 0, 0, 0);
       t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uh, al, t, 0, 0, 0);
       t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ul, ah, t, 0, 0, 0);
