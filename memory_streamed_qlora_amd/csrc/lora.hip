@@ -60,26 +60,6 @@ __device__ __forceinline__ void load4(const float* p, float f[4]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
 }
-// Four consecutive input values as one load (bf16 or fp32) and their fp32 values.
-template <typename TIN>
-struct CgRaw;
-template <>
-struct CgRaw<uint16_t> {
-  typedef uint32_t T __attribute__((ext_vector_type(2)));
-};
-template <>
-struct CgRaw<float> {
-  typedef float T __attribute__((ext_vector_type(4)));
-};
-__device__ __forceinline__ void cg_unpack(CgRaw<uint16_t>::T v, float f[4]) {
-  f[0] = bf16_to_f32(v.x & 0xffffu);
-  f[1] = bf16_to_f32(v.x >> 16);
-  f[2] = bf16_to_f32(v.y & 0xffffu);
-  f[3] = bf16_to_f32(v.y >> 16);
-}
-__device__ __forceinline__ void cg_unpack(CgRaw<float>::T v, float f[4]) {
-  f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
-}
 // Four output values at p: one rounding to bf16, or stored as fp32.
 __device__ __forceinline__ void store4(uint16_t* p, const float a[4]) {
   *reinterpret_cast<uint2*>(p) =
@@ -320,27 +300,25 @@ __global__ __launch_bounds__(256) void lora_skinny_reduce(ReduceArgs ra) {
 //   task i: out_i[j][c] (or out_i[c][j]) = [out_i +] scale_i * sum_t coef_i[t][j] * h_i[t][c],
 //   h_i = drop_i(in_i), j < r, c < C_i
 // (dA = du^T drop(x) with out [r][K]; dB = s dy^T u with out [N][r]).  A workgroup owns
-// `cols` columns of one task and CG_J ranks over all T tokens, so nothing is written twice
-// and no second pass sums partials.  The rank coefficients of CG_TB tokens at a time are
-// staged in LDS (one coalesced read per workgroup).  Thread = (column quad cq, rank group,
-// token slice sl of 16): it takes the block's tokens sl, sl + 16, sl + 32, ... in order,
-// in batches of CG_INFL whose loads are issued one batch ahead, and reads each token's
-// coefficients from LDS (the threads of a slice read one address).  A wide task (64
-// columns per workgroup) gives each thread all 16 ranks of 4 columns; a narrow one (16
-// columns: four times the workgroups, for tasks whose wide grid would leave most CUs idle)
-// gives each thread 4 of the ranks, the 4 rank groups sitting in lane bits 2-3.  Slice sums
-// are added in a fixed order: the wave's four slices (lane bits 4, 5) by a butterfly, then
-// the four waves in order.  Both layouts run every output's multiply-adds and sums in the
-// same order, so a task's result does not depend on its layout or on the other tasks of
-// the launch.
+// 16 columns (narrow) or 64 (wide) of one task and 16 ranks over all T tokens, so nothing
+// is written twice and no second pass sums partials.  The product is a 16 x 16 x 32 bf16
+// MFMA per (16-column block, 32-token block): A = the coefficients transposed (ranks x
+// tokens, staged in LDS CG_TB tokens at a time), B = the inputs (tokens x columns, each
+// wave staging its own 32-token tile in LDS after a coalesced load, the next tile's loads
+// in flight meanwhile), fp32 operands split into bf16 hi and lo parts (hi*hi + lo*hi +
+// hi*lo; an input's lo part is zero for bf16 inputs and skipped).  Token block b goes to
+// wave b mod 4, and the four waves' sums are added in wave order: both widths run every
+// output's products and sums in the same order, so a task's result does not depend on the
+// width or on the other tasks of the launch.  The dropout mask zeroes inputs where they
+// are staged; its 1 / (1 - p) is applied with the task's scale.
 constexpr int CG_J = 16;
-constexpr int CG_COLS = 64;  // columns of a wide task's workgroup
-constexpr int CG_SLICES = 16;
-constexpr int CG_TB = 512;   // tokens whose coefficients are staged in LDS at a time
-constexpr int CG_INFL = 8;   // tokens per thread with input loads in flight
+constexpr int CG_TB = 512;  // tokens whose coefficients are staged in LDS at a time
+constexpr int CG_KB = 32;   // tokens of one MFMA k-block
+constexpr int CG_CTP = CG_TB + 4;  // LDS pitch of a transposed coefficient row (floats)
 
-// Columns per workgroup of a task: 16 when its 64-column grid would be small, else 64.
-inline int colgrad_cols(int64_t T, int64_t C) { return (C <= 4096 && T <= 4096) ? 16 : CG_COLS; }
+// Workgroup width of a launch: 64 columns when its tasks give enough 64-column workgroups
+// to fill the chip, else 16.
+inline bool colgrad_wide(int64_t ctot) { return ctot / 64 >= 512; }
 
 struct CgTaskDev {
   const void* in;
@@ -350,7 +328,6 @@ struct CgTaskDev {
   float scale;
   int out_cr;
   int block0;  // first workgroup of the task (blockIdx.x)
-  int cols;    // columns per workgroup: 16 or CG_COLS
   Dropout d;
 };
 struct CgArgs {
@@ -361,13 +338,27 @@ struct CgArgs {
   int accumulate;
 };
 
-// VEC: r % 4 == 0 and every task's coefficient rows 16-byte aligned (float4 staging loads).
-// A template parameter: a runtime branch around the staging loads would leave the compiler
-// unsure which loads are in flight in the token loop, and it would wait for all of them.
-template <typename TIN, bool VEC>
+// The input tile of one k-block as loaded: 32 tokens x COLS columns in 16-byte pieces.
+template <typename TIN, int COLS>
+struct CgTile {
+  static constexpr int EP = 16 / (int)sizeof(TIN);  // elements per piece
+  static constexpr int LPR = COLS / EP;              // lanes per token row
+  static constexpr int RPI = 64 / LPR;               // token rows per 64-lane load
+  static constexpr int NP = CG_KB / RPI;             // pieces per lane
+  static constexpr int PITCH = COLS + 2;             // fp32 LDS pitch (8-byte aligned rows)
+};
+
+// VEC: r % 4 == 0 and every task's coefficient rows 16-byte aligned (float4 staging loads);
+// WIDE: 64 columns per workgroup.  Template parameters, so that every load in the token
+// loop is unconditional and the compiler counts them exactly.
+template <typename TIN, bool VEC, bool WIDE>
 __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
-  __shared__ __attribute__((aligned(16))) float cfs[CG_TB][CG_J];
-  __shared__ __attribute__((aligned(16))) float red[4][CG_J][CG_COLS];
+  constexpr int COLS = WIDE ? 64 : 16, NCB = COLS / 16;
+  using TL = CgTile<TIN, COLS>;
+  __shared__ __attribute__((aligned(16))) float ct[CG_J * CG_CTP];  // [rank][token]
+  // per wave: its input tile [token][column] in the loop; after it, the partial sums
+  __shared__ __attribute__((aligned(16))) float wt[4 * CG_KB * TL::PITCH > 4 * NCB * 4 * 64 ? 4 * CG_KB * TL::PITCH
+                                                                                           : 4 * NCB * 4 * 64];
   // this workgroup's task (uniform): the last one whose first block is at or before it,
   // its fields picked at constant indices
   CgTaskDev tk = a.t[0];
@@ -375,76 +366,94 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
   for (int i = 1; i < COLGRAD_MAX_TASKS; ++i)
     if (i < a.ntask && (int)blockIdx.x >= a.t[i].block0) tk = a.t[i];
   const TIN* in = (const TIN*)tk.in;
-  const int cols = tk.cols;
-  const bool narrow = cols != CG_COLS;
-  const int tid = threadIdx.x, sl = tid >> 4;
-  const int cq = narrow ? (tid & 3) : (tid & 15);
-  const int jg = narrow ? ((tid >> 2) & 3) : 0;  // rank group (narrow: ranks 4 jg .. 4 jg + 3)
-  const int nj4 = narrow ? 1 : CG_J / 4;         // rank quads per thread
-  const int64_t c = (int64_t)((int)blockIdx.x - tk.block0) * cols + 4 * cq;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int64_t cbase = (int64_t)((int)blockIdx.x - tk.block0) * COLS;
   const int j0 = blockIdx.y * CG_J;
   const int r = a.r;
   const int64_t T = a.T, C = tk.C;
-  // (C is a multiple of 64, so every thread's 4 columns exist; the clamp keeps the loads in
-  // bounds regardless, and the output stage stores only columns below C)
-  const int64_t cl = min(c, C - 4);
-  float acc[CG_J][4];  // narrow: rows 0..3 hold ranks 4 jg .. 4 jg + 3
+  const bool drop = tk.d.threshold != 0u;
+  float* tile = wt + wave * CG_KB * TL::PITCH;
+  // this lane's pieces: token row p * RPI + lane / LPR of the k-block, columns
+  // (lane % LPR) * EP .. + EP - 1 of the workgroup's
+  const int prow = lane / TL::LPR, pcol = (lane % TL::LPR) * TL::EP;
+
+  f32x4_t acc[NCB];
 #pragma unroll
-  for (int j = 0; j < CG_J; ++j)
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 qa[TL::NP], qb[TL::NP];
+  // k-block kb of the staging block at tb0 (past the tokens: the last token again)
+  auto load = [&](u32x4 (&q)[TL::NP], int64_t tb0, int kb) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
-  // a token's 4 input values as loaded (raw: converted where they are used, so that a
-  // prefetched batch is not waited for before the batch ahead of it is multiplied)
-  using Raw = typename CgRaw<TIN>::T;
-  Raw hb0[CG_INFL], hb1[CG_INFL];
-  auto load_batch = [&](Raw (&h)[CG_INFL], int64_t tb0, int tt, int nt) {
-#pragma unroll
-    for (int u = 0; u < CG_INFL; ++u) {
-      const int t = min(tt + CG_SLICES * u, nt - 1);  // past the block: loaded, not used
-      h[u] = *reinterpret_cast<const Raw*>(in + (tb0 + t) * C + cl);
+    for (int p = 0; p < TL::NP; ++p) {
+      const int64_t t = min(tb0 + (int64_t)kb * CG_KB + p * TL::RPI + prow, T - 1);
+      q[p] = *reinterpret_cast<const u32x4*>(in + t * C + cbase + pcol);
     }
   };
-  auto consume = [&](const Raw (&h)[CG_INFL], int64_t tb0, int tt, int nt) {
+  // the pieces into the wave's tile as fp32: zero past T, masked by the dropout
+  auto stage = [&](const u32x4 (&q)[TL::NP], int64_t tb0, int kb) {
 #pragma unroll
-    for (int u = 0; u < CG_INFL; ++u) {
-      const int t = tt + CG_SLICES * u;
-      // consumed on every path (the empty asm takes the values, so the wait for the load
-      // does not sink under the guard): a load left unread on some path makes the compiler
-      // wait for every load in flight where its register is next written
-      float hv[4];
-      cg_unpack(h[u], hv);
-      asm volatile("" ::"v"(hv[0]), "v"(hv[1]), "v"(hv[2]), "v"(hv[3]));
-      if (t < nt) {
-        if (tk.d.threshold != 0u) {
-          const uint32_t keep = keep4(tk.d, (uint64_t)(tb0 + t) * (uint64_t)C + (uint64_t)cl);
+    for (int p = 0; p < TL::NP; ++p) {
+      const int row = p * TL::RPI + prow;
+      const int64_t t = tb0 + (int64_t)kb * CG_KB + row;
+      float v[TL::EP];
+      if (sizeof(TIN) == 4) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = ((keep >> q) & 1u) ? hv[q] * tk.d.sigma : 0.0f;
+        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(q[p][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = bf16_to_f32(q[p][e] & 0xffffu);
+          v[2 * e + 1] = bf16_to_f32(q[p][e] >> 16);
         }
+      }
+      uint32_t keep = t < T ? 0xffffffffu : 0u;
+      if (drop && t < T) {
+        uint32_t kb = 0;
 #pragma unroll
-        for (int j4 = 0; j4 < CG_J; j4 += 4) {
-          if (j4 < 4 * nj4) {  // uniform; the loop stays unrolled, acc statically indexed
-            const float4 cf = *reinterpret_cast<const float4*>(&cfs[t][j4 + 4 * jg]);
+        for (int g = 0; g < TL::EP / 4; ++g)
+          kb |= keep4(tk.d, (uint64_t)t * (uint64_t)C + (uint64_t)(cbase + pcol + 4 * g)) << (4 * g);
+        keep = kb;
+      }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              acc[j4][q] = fmaf(cf.x, hv[q], acc[j4][q]);
-              acc[j4 + 1][q] = fmaf(cf.y, hv[q], acc[j4 + 1][q]);
-              acc[j4 + 2][q] = fmaf(cf.z, hv[q], acc[j4 + 2][q]);
-              acc[j4 + 3][q] = fmaf(cf.w, hv[q], acc[j4 + 3][q]);
-            }
-          }
-        }
+      for (int e = 0; e < TL::EP; e += 2) {
+        const f32x2_t w = {((keep >> e) & 1u) ? v[e] : 0.0f, ((keep >> (e + 1)) & 1u) ? v[e + 1] : 0.0f};
+        *reinterpret_cast<f32x2_t*>(&tile[row * TL::PITCH + pcol + e]) = w;
       }
     }
   };
-  constexpr int STEP = CG_SLICES * CG_INFL;  // tokens of one batch of the workgroup
+  // the k-block's products: A = coefficients of ranks r16, tokens 8 kg .. (hi, lo), B =
+  // column 16 cb + r16 of the tile, the same tokens
+  auto multiply = [&](int kb) {
+    const float4 c0 = *reinterpret_cast<const float4*>(&ct[r16 * CG_CTP + kb * CG_KB + 8 * kg]);
+    const float4 c1 = *reinterpret_cast<const float4*>(&ct[r16 * CG_CTP + kb * CG_KB + 8 * kg + 4]);
+    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    bf16x8_t ch, cl;
+    split8_bf16(cv, ch, cl);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = tile[(8 * kg + e) * TL::PITCH + 16 * cb + r16];
+      bf16x8_t hh, hl;
+      split8_bf16(hv, hh, hl);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch, hh, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cl, hh, acc[cb], 0, 0, 0);
+      if (sizeof(TIN) == 4) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch, hl, acc[cb], 0, 0, 0);
+    }
+  };
+
   for (int64_t tb0 = 0; tb0 < T; tb0 += CG_TB) {
     const int nt = (int)min((int64_t)CG_TB, T - tb0);
-    // the block's first inputs are in flight while its coefficients are staged
-    load_batch(hb0, tb0, sl, nt);
+    const int nkb = (nt + CG_KB - 1) / CG_KB;
+    // the wave's first tile in flight while the coefficients are staged
+    load(qa, tb0, min(wave, nkb - 1));
+    __syncthreads();  // the previous block's coefficients are no longer read
+    // coefficients [token][rank] -> ct[rank][token], zero past the block or past r; every
+    // load issued before any store
     if (VEC) {
-      // every load of the block's coefficients issued before any is stored (rows past the
-      // block and rank quads past r re-read valid ones; the quads are stored as zeros): one
-      // memory latency instead of one per pass of a load-store loop
       constexpr int STG = CG_TB * (CG_J / 4) / 256;
       f32x4_t cv[STG];
 #pragma unroll
@@ -452,71 +461,57 @@ __global__ __launch_bounds__(256) void lora_colgrad(CgArgs a) {
         const int idx = tid + 256 * k, t = min(idx >> 2, nt - 1), q4 = 4 * (idx & 3);
         cv[k] = *reinterpret_cast<const f32x4_t*>(tk.coef + (tb0 + t) * r + min(j0 + q4, r - 4));
       }
-      __syncthreads();  // the previous block's coefficients are no longer read
 #pragma unroll
       for (int k = 0; k < STG; ++k) {
         const int idx = tid + 256 * k, t = idx >> 2, q4 = 4 * (idx & 3);
-        const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-        // (rows t >= nt, inside the CG_TB-row buffer, get row nt - 1 again and are never
-        // read; stored anyway, so every load is consumed on every path)
-        *reinterpret_cast<f32x4_t*>(&cfs[t][q4]) = j0 + q4 < r ? cv[k] : z;
+        const bool ok = t < nt && j0 + q4 < r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ct[(q4 + e) * CG_CTP + t] = ok ? cv[k][e] : 0.0f;
       }
     } else {
-      __syncthreads();  // the previous block's coefficients are no longer read
-      for (int idx = tid; idx < nt * (CG_J / 4); idx += 256) {
-        const int t = idx >> 2, q4 = 4 * (idx & 3);
-        const float* src = tk.coef + (tb0 + t) * r + j0 + q4;
-        float4 v;
-        v.x = j0 + q4 < r ? src[0] : 0.0f;
-        v.y = j0 + q4 + 1 < r ? src[1] : 0.0f;
-        v.z = j0 + q4 + 2 < r ? src[2] : 0.0f;
-        v.w = j0 + q4 + 3 < r ? src[3] : 0.0f;
-        *reinterpret_cast<float4*>(&cfs[t][q4]) = v;
+      for (int idx = tid; idx < CG_TB * CG_J; idx += 256) {
+        const int t = idx / CG_J, j = idx % CG_J;
+        ct[j * CG_CTP + t] = (t < nt && j0 + j < r) ? tk.coef[(tb0 + t) * r + j0 + j] : 0.0f;
       }
     }
     __syncthreads();
-    // two batches in turn: the next one's loads are issued before this one is multiplied.
-    // A batch past the block re-reads its last token (in bounds) and adds nothing.  The
-    // loop has one exit, on a workgroup-uniform count, so the compiler can tell that every
-    // batch it loaded was consumed when it comes round (a second, early exit had made it
-    // wait for all loads in flight at the top of every pass).
-    for (int base = 0; base < nt; base += 2 * STEP) {
-      load_batch(hb1, tb0, base + STEP + sl, nt);
-      consume(hb0, tb0, base + sl, nt);
-      load_batch(hb0, tb0, base + 2 * STEP + sl, nt);
-      consume(hb1, tb0, base + STEP + sl, nt);
+    // the wave's k-blocks wave, wave + 4, ...: two tiles in turn, the next one's loads
+    // issued before this one is staged and multiplied (one exit, on a wave-uniform count;
+    // every loaded tile is staged, a tile past the block re-reads valid tokens and is not
+    // multiplied)
+    for (int kb = wave; kb < nkb; kb += 8) {
+      load(qb, tb0, min(kb + 4, nkb - 1));
+      stage(qa, tb0, kb);
+      __builtin_amdgcn_wave_barrier();
+      multiply(kb);
+      __builtin_amdgcn_wave_barrier();
+      load(qa, tb0, min(kb + 8, nkb - 1));
+      stage(qb, tb0, kb + 4);
+      __builtin_amdgcn_wave_barrier();
+      if (kb + 4 < nkb) multiply(kb + 4);
+      __builtin_amdgcn_wave_barrier();
     }
   }
-  // the wave's four slices (lane bits 4, 5), then the four waves in order
+  // the four waves' sums in wave order; lane l of a wave holds ranks 4 (l >> 4) + i of
+  // column l & 15 of each block
+  __syncthreads();  // every wave is done with its tile, which the partials overwrite
 #pragma unroll
-  for (int j = 0; j < CG_J; ++j) {
-    if (j < 4 * nj4) {  // uniform
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v = acc[j][q];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        acc[j][q] = v;
-      }
-    }
-  }
-  const int wave = tid >> 6;
-  if ((tid & 63) < 16) {
-#pragma unroll
-    for (int j = 0; j < CG_J; ++j) {
-      if (j < 4 * nj4)
-        *reinterpret_cast<float4*>(&red[wave][j + 4 * jg][4 * cq]) =
-            make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-    }
-  }
+    for (int i = 0; i < 4; ++i) wt[((wave * NCB + cb) * 4 + i) * 64 + lane] = acc[cb][i];
   __syncthreads();
-  const int64_t cbase = (int64_t)((int)blockIdx.x - tk.block0) * cols;
-  for (int k = 0; k < CG_J * cols / 256; ++k) {
+  const float sc = tk.scale * (drop ? tk.d.sigma : 1.0f);
+#pragma unroll
+  for (int k = 0; k < NCB; ++k) {
     const int o = tid + 256 * k;
     // [r][C] output: consecutive threads take consecutive columns; [C][r]: consecutive ranks
-    const int j = tk.out_cr ? (o & (CG_J - 1)) : (o / cols);
-    const int cc = tk.out_cr ? (o / CG_J) : (o & (cols - 1));
-    const float v = (((red[0][j][cc] + red[1][j][cc]) + red[2][j][cc]) + red[3][j][cc]) * tk.scale;
+    const int j = tk.out_cr ? (o & (CG_J - 1)) : (o / COLS);
+    const int cc = tk.out_cr ? (o / CG_J) : (o & (COLS - 1));
+    const int cb = cc >> 4, l = 16 * (j >> 2) + (cc & 15), i = j & 3;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += wt[((w * NCB + cb) * 4 + i) * 64 + l];
+    v *= sc;
     const int64_t col = cbase + cc;
     if (j0 + j >= r || col >= C) continue;
     float* po = tk.out_cr ? tk.out + col * r + j0 + j : tk.out + (int64_t)(j0 + j) * C + col;
@@ -659,21 +654,27 @@ hipError_t launch_pack_lora(const void* in, bool in_f32, int64_t T, int64_t C, c
 
 hipError_t launch_colgrad(const ColgradTask* tasks, int ntask, bool in_f32, int64_t T, int r, int accumulate,
                           hipStream_t s) {
-  if (ntask < 1 || ntask > COLGRAD_MAX_TASKS || r < 1) return hipErrorInvalidValue;
+  if (ntask < 1 || ntask > COLGRAD_MAX_TASKS || r < 1 || T < 0) return hipErrorInvalidValue;
   CgArgs a;
   memset(&a, 0, sizeof(a));
   a.ntask = ntask;
   a.T = T;
   a.r = r;
   a.accumulate = accumulate;
-  int blocks = 0;
   double bytes = 0.0;
   int64_t ctot = 0;
   bool vec = r % 4 == 0;
   for (int i = 0; i < ntask; ++i) {
     const ColgradTask& q = tasks[i];
-    if (q.C < 4 || q.C % 4) return hipErrorInvalidValue;
+    if (q.C < 64 || q.C % 64) return hipErrorInvalidValue;  // whole 64-column groups
     if (reinterpret_cast<uintptr_t>(q.coef) & 15) vec = false;
+    ctot += q.C;
+  }
+  const bool wide = colgrad_wide(ctot);
+  const int cols = wide ? 64 : 16;
+  int blocks = 0;
+  for (int i = 0; i < ntask; ++i) {
+    const ColgradTask& q = tasks[i];
     CgTaskDev& d = a.t[i];
     d.in = q.in;
     d.coef = q.coef;
@@ -683,19 +684,21 @@ hipError_t launch_colgrad(const ColgradTask* tasks, int ntask, bool in_f32, int6
     d.out_cr = q.out_cr;
     d.d = q.drop;
     d.block0 = blocks;
-    d.cols = colgrad_cols(T, q.C);
-    blocks += (int)((q.C + d.cols - 1) / d.cols);
+    blocks += (int)(q.C / cols);
     bytes += (double)T * q.C * (in_f32 ? 4 : 2) + (double)T * r * 4 + (double)r * q.C * 4 * (accumulate ? 2 : 1);
-    ctot += q.C;
   }
   const dim3 grid((unsigned)blocks, (unsigned)((r + CG_J - 1) / CG_J));
   char shape[40];
   snprintf(shape, sizeof(shape), "%lldx%lld r%d n%d", (long long)T, (long long)ctot, r, ntask);
-  if (vec)
-    return in_f32 ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float, true>, grid, dim3(256), s, a)
-                  : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t, true>, grid, dim3(256), s, a);
-  return in_f32 ? timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<float, false>, grid, dim3(256), s, a)
-                : timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<uint16_t, false>, grid, dim3(256), s, a);
+#define MSQ_CG(TIN, VEC, WIDE) \
+  timed_launch("lora_colgrad", shape, 0.0, bytes, lora_colgrad<TIN, VEC, WIDE>, grid, dim3(256), s, a)
+  if (in_f32) {
+    if (vec) return wide ? MSQ_CG(float, true, true) : MSQ_CG(float, true, false);
+    return wide ? MSQ_CG(float, false, true) : MSQ_CG(float, false, false);
+  }
+  if (vec) return wide ? MSQ_CG(uint16_t, true, true) : MSQ_CG(uint16_t, true, false);
+  return wide ? MSQ_CG(uint16_t, false, true) : MSQ_CG(uint16_t, false, false);
+#undef MSQ_CG
 }
 
 hipError_t launch_split_reduce(const float* part, int splits, int64_t T, int64_t N,

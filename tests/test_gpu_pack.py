@@ -116,17 +116,18 @@ def test_grouped_backward_mixed_widths_in_one_launch():
 
 
 def test_column_gradient_layouts_agree():
-    """dA = du^T x over K = 4096 input columns (the narrow 16-column workgroups) equals the
-    first 4096 columns of the same product over K = 4160 (64-column workgroups) bit for bit:
-    both layouts run each output's multiply-adds and sums in the same order."""
+    """dA = du^T x over K = 4096 input columns (a launch of 16-column workgroups) equals the
+    first 4096 columns of the same product over K = 32768 (enough columns for 64-column
+    workgroups) bit for bit: both widths run each output's products and sums in the same
+    order."""
     T, N, r = 512, 256, 16
     g = torch.Generator(device="cuda").manual_seed(41)
-    x_wide = torch.randn(T, 4160, generator=g, device="cuda").to(torch.bfloat16)
+    x_wide = torch.randn(T, 32768, generator=g, device="cuda").to(torch.bfloat16)
     dy = torch.randn(T, N, generator=g, device="cuda").to(torch.bfloat16)
     B = torch.randn(N, r, generator=g, device="cuda") * 0.01
     cfg, key = msq.Lora(r, 32.0, 0.0), msq.rng_key(1, 0, 0, 0, 0)
     out = []
-    for K in (4096, 4160):
+    for K in (4096, 32768):
         W = (torch.randn(N, K, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
         A = torch.randn(r, K, generator=g, device="cuda") * 0.01
         u = torch.randn(T, r, generator=g, device="cuda")
