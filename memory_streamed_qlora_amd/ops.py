@@ -9,6 +9,7 @@ allocated with torch on the input's device.
 from __future__ import annotations
 
 import ctypes
+import functools
 import sys
 from dataclasses import dataclass
 from typing import Optional, Sequence, Tuple
@@ -35,6 +36,10 @@ def _stream(stream) -> int:
 
 
 def _req(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
+    # one combined test on the common path (a call checks ~10 tensors); the messages below
+    # name what is wrong
+    if type(t) is torch.Tensor and t.is_cuda and t.dtype is dtype and t.shape == shape and t.is_contiguous():
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.device.type != "cuda":
@@ -86,7 +91,9 @@ def nf4_dequantize(codes: torch.Tensor, absmax: torch.Tensor, out: Optional[torc
     return out
 
 
+@functools.lru_cache(maxsize=1024)
 def nf4_lora_workspace_size(t: int, k: int, n: int, r: int) -> int:
+    # a function of the shape alone (cached: the fused calls ask for it every time)
     return int(lib().nf4_lora_workspace_size(t, k, n, r))
 
 
@@ -107,10 +114,14 @@ class Workspace:
 _default_ws = {}
 
 
-def _workspace(device: torch.device, nbytes: int, ws: Optional[Workspace]) -> torch.Tensor:
+def _workspace(device: torch.device, nbytes: int, ws: Optional[Workspace], stream_handle: Optional[int] = None
+               ) -> torch.Tensor:
     if ws is None:
-        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
-        ws = _default_ws.setdefault(key, Workspace(device))
+        key = (device.index, stream_handle if stream_handle is not None
+               else torch.cuda.current_stream(device).cuda_stream)
+        ws = _default_ws.get(key)
+        if ws is None:
+            ws = _default_ws.setdefault(key, Workspace(device))
     return ws.get(nbytes)
 
 
@@ -200,12 +211,12 @@ def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream
         check("nf4_lora_fwd_noalloc", lib().nf4_lora_fwd_noalloc(*args, _stream(stream)))
         return y, u_out
     need = nf4_lora_workspace_size(t, k, n, r)
-    ws = _workspace(x.device, need, workspace)
+    sh = _stream(stream)
+    ws = _workspace(x.device, need, workspace, sh if stream is None else None)
     fn = f"{fmt}_lora_fwd"
     check(fn, getattr(lib(), fn)(
         _ptr(x), t, k, n, *bptr, _ptr(bias), _ptr(residual), _ptr(A) if r > 0 else None,
-        _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(),
-        _stream(stream)))
+        _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(), sh))
     return y, u_out
 
 
@@ -233,13 +244,14 @@ def _lora_bwd(base, dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_acc
         dx = torch.empty((t, k), dtype=out_dtype, device=x.device)
     _req(dx, "dx", out_dtype, (t, k))
     need = nf4_lora_workspace_size(t, k, n, r)
-    ws = _workspace(x.device, need, workspace)
+    sh = _stream(stream)
+    ws = _workspace(x.device, need, workspace, sh if stream is None else None)
     fn = f"{fmt}_lora_bwd"
     check(fn, getattr(lib(), fn)(
         _ptr(dy), _ptr(x), t, k, n, *bptr, _ptr(A) if r > 0 else None,
         _ptr(B) if r > 0 else None, cfg.c(flags), key, _ptr(u) if r > 0 else None, _ptr(dx),
         int(dx_accumulate), _ptr(dA) if r > 0 else None, _ptr(dB) if r > 0 else None,
-        int(dAB_accumulate), _ptr(ws), ws.numel(), _stream(stream)))
+        int(dAB_accumulate), _ptr(ws), ws.numel(), sh))
     return dx, (dA if r > 0 else None), (dB if r > 0 else None)
 
 
