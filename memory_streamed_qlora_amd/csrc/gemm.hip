@@ -172,9 +172,13 @@ struct WShare<true> {
 
 template <int MODE, bool DROP, bool BF16W>
 __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
-  __shared__ __attribute__((aligned(16))) uint16_t sB[3][BN * LDW];
-  // forward NF4: the codebook, and each thread's quarter of its row's bf16 table planes
-  constexpr bool QUAD_TABLE = MODE == 0 && !BF16W;
+  // W tiles [output column][k] with row pitch LDW; the backward's also start each group
+  // of 16 columns 8 elements further (BSKEW), so that the transposed stores of a wave's
+  // 8 column groups land on different banks
+  constexpr int BSKEW = MODE == 1 ? 8 : 0;
+  __shared__ __attribute__((aligned(16))) uint16_t sB[3][BN * LDW + BSKEW * (BN / 16)];
+  // NF4: the codebook, and each thread's quarter of its row's bf16 table planes
+  constexpr bool QUAD_TABLE = !BF16W;
   __shared__ __attribute__((aligned(16))) float sLut[QUAD_TABLE ? 16 : 1];
   __shared__ __attribute__((aligned(16))) uint2 sPl[QUAD_TABLE ? THREADS : 1];
 
@@ -231,7 +235,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
     // elements per k-step, as NF4 codes (one 8-byte load + the block's absmax) or bf16
     // values (two 16-byte loads).
     //   forward:  W row n0 + (tid >> 2), elements 16*(tid & 3) .. +15 of the step's block
-    //   backward: reduction row `lane` of the step, output columns n0 + 16*wave .. +15
+    //   backward: reduction row 8*wave + (lane >> 3) of the step, output columns
+    //             n0 + 16*(lane & 7) .. +15 (the 8 lanes of a row read its 64 code bytes, or
+    //             256 bf16 bytes, as one piece; the 4 lanes of a 64-column block share its
+    //             absmax, as in the forward)
     const uint8_t* cbase = nullptr;
     const float* sbase = nullptr;
     const uint16_t* wbase = nullptr;
@@ -250,13 +257,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
       }
     } else {
       // offsets within a projection's W; the projection and its row base follow the step
-      const int64_t col = n0 + 16 * wave < g.Nc ? n0 + 16 * wave : 0;
+      const int64_t wrow = 8 * wave + (lane >> 3), colq = n0 + 16 * (lane & 7);
+      const int64_t col = colq < g.Nc ? colq : 0;
       if constexpr (BF16W) {
-        woff = (int64_t)lane * g.K + col;
+        woff = wrow * g.K + col;
         wstride = (int64_t)BK * g.K;
       } else {
-        coff = (int64_t)lane * (g.K / 2) + col / 2;
-        soff = (int64_t)lane * (g.K / 64) + col / 64;
+        coff = wrow * (g.K / 2) + col / 2;
+        soff = wrow * (g.K / 64) + col / 64;
         cstride = (int64_t)BK * (g.K / 2);
         sstride = (int64_t)BK * (g.K / 64);
       }
@@ -305,7 +313,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
             make_uint4(out[0], out[1], out[2], out[3]);
       } else {
         // transpose into [output column][reduction row]
-        uint16_t* dst = &sB[buf][(16 * wave + 8 * h) * LDW + lane];
+        const int cg = lane & 7;
+        uint16_t* dst = &sB[buf][(16 * cg + 8 * h) * LDW + BSKEW * cg + 8 * wave + (lane >> 3)];
 #pragma unroll
         for (int e = 0; e < 8; ++e) dst[e * LDW] = (uint16_t)((e & 1) ? (out[e >> 1] >> 16) : out[e >> 1]);
       }
@@ -325,11 +334,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
       }
       store8(out, h, buf);
     };
-    // The forward's four threads of a W row (lanes 4r .. 4r+3 of one wave) share the row's
-    // block: each builds the table entries of codes 4q .. 4q+3 (q = tid & 3) and the quad
-    // exchanges them through LDS, in place of each building all 16.  A wave's LDS
-    // operations complete in order, so no barrier.  The backward's threads of one block
-    // sit in different waves and build the whole table.
+    // The four threads of a quad (lanes 4r .. 4r+3 of one wave) hold the same W row's
+    // block (forward: the row's four 16-element pieces; backward: four 16-column pieces of
+    // one 64-column block): each builds the table entries of codes 4q .. 4q+3 (q = tid & 3)
+    // and the quad exchanges them through LDS, in place of each building all 16.  A wave's
+    // LDS operations complete in order, so no barrier.
     auto planes = [&](const WShare<BF16W>& w) {
       Nf4Planes P;
       if constexpr (QUAD_TABLE) {
@@ -354,7 +363,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& ga) {
     auto read_b = [&](bf16x8_t(&b)[4], int c, int buf) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][(32 * j + r32) * LDW + 32 * hk + 8 * c]);
+        b[j] = *reinterpret_cast<const bf16x8_t*>(
+            &sB[buf][(32 * j + r32) * LDW + BSKEW * ((32 * j + r32) >> 4) + 32 * hk + 8 * c]);
     };
     // Column-major MFMA order: operand b[j] is dead after its second MFMA, so the LDS
     // read that refills it for the next sub-step can be issued six MFMAs before use.
