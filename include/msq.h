@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MSQ_ABI_VERSION 14
+#define MSQ_ABI_VERSION 15
 
 typedef void* msq_stream_t; /* hipStream_t */
 
@@ -113,7 +113,7 @@ typedef struct {
  *   MSQ_ACT_F32  x (forward and backward) and dy (backward) are fp32 instead of
  *                bf16.  The base-weight contraction still runs on bf16 MFMA: the
  *                library rounds the activation to bf16 (RNE) for that product only;
- *                the rank-r LoRA products use the fp32 values.
+ *                the rank-r LoRA products keep fp32 accuracy.
  *   MSQ_OUT_F32  y (forward) and dx (backward) are written (and, when
  *                accumulating, read) as fp32 instead of bf16.
  *   MSQ_U_ONLY   forward only: compute u = drop(x) A^T and skip y (y may be NULL).
@@ -123,6 +123,13 @@ typedef struct {
 #define MSQ_ACT_F32 1u
 #define MSQ_OUT_F32 2u
 #define MSQ_U_ONLY 4u
+/*   MSQ_U_GIVEN  forward only (single calls and groups): u_out holds u = drop(x) A^T from an
+ *                earlier call with the same x, A and key, and the call uses it instead of
+ *                forming it (u_out is read, not written).  For the recompute of a block whose
+ *                first forward kept its u: the recompute's y is the same as the first one's
+ *                without the rank-r product.  Needs r > 0 and u_out (every projection's, for
+ *                a group); not with MSQ_U_ONLY (MSQ_E_INVAL). */
+#define MSQ_U_GIVEN 32u
 /* Path of a single call (nf4_lora_fwd/bwd, bf16_lora_fwd/bwd; groups always take the
  * tiled path and reject MSQ_PATH_SMALL):
  *   tiled:  512-token x 128-column tiles with the reduction split across workgroups
@@ -139,7 +146,7 @@ typedef struct {
   int32_t r;      /* 0 .. 64 */
   float alpha;
   float p_drop;   /* dropout probability on the LoRA input, in [0, 1) */
-  uint32_t flags; /* MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY | MSQ_PATH_*, other bits 0 */
+  uint32_t flags; /* MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY | MSQ_U_GIVEN | MSQ_PATH_*, other bits 0 */
 } msq_lora_cfg;
 
 /* Bytes of scratch device memory one nf4_lora_fwd or nf4_lora_bwd call with

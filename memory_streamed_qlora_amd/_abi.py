@@ -31,6 +31,7 @@ class RngKey(ctypes.Structure):
 MSQ_ACT_F32 = 1
 MSQ_OUT_F32 = 2
 MSQ_U_ONLY = 4
+MSQ_U_GIVEN = 32
 MSQ_PATH_TILED = 8
 MSQ_PATH_SMALL = 16
 MSQ_MAX_COPY_STREAMS = 4
@@ -145,7 +146,7 @@ _SIG = {
 }
 EXPORTED = tuple(_SIG)
 
-ABI_VERSION = 14  # MSQ_ABI_VERSION of include/msq.h
+ABI_VERSION = 15  # MSQ_ABI_VERSION of include/msq.h
 _lib = None
 
 

@@ -54,8 +54,11 @@ int check_linear(const char* fn, int64_t t, int64_t k, int64_t n, const msq_lora
   if (!(cfg.p_drop >= 0.0f && cfg.p_drop < 1.0f)) return set_error(MSQ_E_DROPOUT, "%s: p_drop=%g outside [0, 1)", fn, (double)cfg.p_drop);
   if (cfg.r > 0 && !isfinite(cfg.alpha)) return set_error(MSQ_E_DROPOUT, "%s: alpha is not finite", fn);
   if (key.proj >= 16 || key.layer >= (1u << 28)) return set_error(MSQ_E_INVAL, "%s: rng key proj must be < 16 and layer < 2^28", fn);
-  if (cfg.flags & ~(MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY | MSQ_PATH_TILED | MSQ_PATH_SMALL))
+  if (cfg.flags & ~(MSQ_ACT_F32 | MSQ_OUT_F32 | MSQ_U_ONLY | MSQ_U_GIVEN | MSQ_PATH_TILED | MSQ_PATH_SMALL))
     return set_error(MSQ_E_INVAL, "%s: unknown flags 0x%x", fn, cfg.flags);
+  if ((cfg.flags & MSQ_U_GIVEN) && (cfg.flags & MSQ_U_ONLY))
+    return set_error(MSQ_E_INVAL, "%s: MSQ_U_GIVEN with MSQ_U_ONLY leaves nothing to compute", fn);
+  if ((cfg.flags & MSQ_U_GIVEN) && cfg.r == 0) return set_error(MSQ_E_INVAL, "%s: MSQ_U_GIVEN needs r > 0", fn);
   if ((cfg.flags & MSQ_PATH_TILED) && (cfg.flags & MSQ_PATH_SMALL))
     return set_error(MSQ_E_INVAL, "%s: MSQ_PATH_TILED and MSQ_PATH_SMALL together", fn);
   if ((cfg.flags & MSQ_PATH_SMALL) && (cfg.r > SMALL_MAX_R || cfg.r % 4))
@@ -203,11 +206,12 @@ int lora_fwd(const char* fn, const void* x, int64_t t, int64_t k, int64_t n, con
   if (rc) return rc;
   rc = check_base(fn, base);
   if (rc) return rc;
-  const bool u_only = cfg.flags & MSQ_U_ONLY;
+  const bool u_only = cfg.flags & MSQ_U_ONLY, u_given = cfg.flags & MSQ_U_GIVEN;
   if (!workspace || (t > 0 && (!x || (!y && !u_only))))
     return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
   if (u_only && (cfg.r == 0 || !u_out))
     return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY needs r > 0 and u_out", fn);
+  if (u_given && !u_out) return set_error(MSQ_E_INVAL, "%s: MSQ_U_GIVEN needs u_out (the given u)", fn);
   if (cfg.r > 0 && (!A || !B)) return set_error(MSQ_E_INVAL, "%s: r > 0 needs A and B", fn);
   if (u_only && residual) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY writes no y to add a residual to", fn);
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(bias, 8) || !aligned(residual, 16) || !aligned(A, 16) ||
@@ -225,7 +229,7 @@ int lora_fwd(const char* fn, const void* x, int64_t t, int64_t k, int64_t n, con
   if (use_small_path(cfg, t, k, n)) {
     const SmallLinear L{t, k, n, base.codes, base.absmax, base.wbf, A, B, r, r > 0 ? cfg.alpha / (float)r : 0.0f,
                         d, act_f32, out_f32};
-    const hipError_t e = launch_small_fwd(L, x, bias, residual, y, r > 0 ? u_out : nullptr, u_only, s);
+    const hipError_t e = launch_small_fwd(L, x, bias, residual, y, r > 0 ? u_out : nullptr, u_only, u_given, s);
     return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
   }
   float* u = u_out ? u_out : (float*)(ws + p.off_u_fwd);
@@ -233,7 +237,8 @@ int lora_fwd(const char* fn, const void* x, int64_t t, int64_t k, int64_t n, con
   const float lscale = r > 0 ? cfg.alpha / (float)r : 0.0f;
   hipError_t e = hipSuccess;
   uint16_t* xb = u_only ? nullptr : (uint16_t*)(ws + p.off_act_fwd);
-  e = launch_pack_lora(x, act_f32, t, k, A, 0, r, 1.0f, d, xb, (float*)(ws + p.off_sk_fwd), u, s);
+  // with u given, the pass only packs x (no rank-r product, no chunk reduction)
+  e = launch_pack_lora(x, act_f32, t, k, A, 0, u_given ? 0 : r, 1.0f, d, xb, (float*)(ws + p.off_sk_fwd), u, s);
   if (u_only) return e == hipSuccess ? MSQ_OK : hip_error(e, fn);
 
   if (e == hipSuccess) {
@@ -298,6 +303,9 @@ int group_check(const char* fn, int64_t t, int64_t k, const msq_lora_proj* projs
   if (n_proj < 1 || n_proj > GEMM_MAX_SEGS || !projs)
     return set_error(MSQ_E_INVAL, "%s: n_proj=%d outside [1, %d]", fn, n_proj, GEMM_MAX_SEGS);
   if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY is not available for groups", fn);
+  if (cfg.flags & MSQ_U_GIVEN)
+    for (int i = 0; i < n_proj; ++i)
+      if (!projs[i].u_out) return set_error(MSQ_E_INVAL, "%s: MSQ_U_GIVEN needs every projection's u_out", fn);
   if (cfg.flags & MSQ_PATH_SMALL)
     return set_error(MSQ_E_INVAL, "%s: groups run on the tiled path (MSQ_PATH_SMALL is for single calls)", fn);
   int64_t ntot = 0;
@@ -331,7 +339,7 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
   if (!workspace || (t > 0 && (!dy || !x || !dx)))
     return set_error(MSQ_E_INVAL, "%s: null pointer", fn);
   if (cfg.r > 0 && (!A || !B || !dA || !dB)) return set_error(MSQ_E_INVAL, "%s: r > 0 needs A, B, dA, dB", fn);
-  if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY is a forward flag", fn);
+  if (cfg.flags & (MSQ_U_ONLY | MSQ_U_GIVEN)) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY / MSQ_U_GIVEN are forward flags", fn);
   if ((dx_accumulate != 0 && dx_accumulate != 1) || (dAB_accumulate != 0 && dAB_accumulate != 1))
     return set_error(MSQ_E_INVAL, "%s: accumulate flags must be 0 or 1", fn);
   if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16) || !aligned(A, 16) || !aligned(B, 16) ||
@@ -354,7 +362,7 @@ int lora_bwd(const char* fn, const void* dy, const void* x, int64_t t, int64_t k
     const float* uu = u;
     if (r > 0 && !uu) {
       float* ut = (float*)(ws + p.off_u_bwd);
-      e = launch_small_fwd(L, x, nullptr, nullptr, nullptr, ut, true, s);
+      e = launch_small_fwd(L, x, nullptr, nullptr, nullptr, ut, true, false, s);
       uu = ut;
     }
     if (e == hipSuccess) e = launch_small_bwd(L, dy, dx, dx_accumulate, r > 0 ? du : nullptr, s);
@@ -456,7 +464,7 @@ int group_bwd_check(const char* fn, int64_t t, int64_t k, const msq_lora_proj_gr
                     const msq_lora_cfg& cfg, int64_t* ns) {
   if (n_proj < 1 || n_proj > GEMM_MAX_SEGS || !projs)
     return set_error(MSQ_E_INVAL, "%s: n_proj=%d outside [1, %d]", fn, n_proj, GEMM_MAX_SEGS);
-  if (cfg.flags & MSQ_U_ONLY) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY is a forward flag", fn);
+  if (cfg.flags & (MSQ_U_ONLY | MSQ_U_GIVEN)) return set_error(MSQ_E_INVAL, "%s: MSQ_U_ONLY / MSQ_U_GIVEN are forward flags", fn);
   if (cfg.flags & MSQ_PATH_SMALL)
     return set_error(MSQ_E_INVAL, "%s: groups run on the tiled path (MSQ_PATH_SMALL is for single calls)", fn);
   int64_t red = 0;
@@ -541,9 +549,12 @@ int lora_fwd_group(const void* x, int64_t t, int64_t k, const msq_lora_proj* pro
     u[i] = q.u_out ? q.u_out : (float*)(ws + p.off_u[i]);
     prods[i] = {q.A, make_dropout(q.key, cfg.p_drop), 1.0f, (float*)(ws + p.off_sk[i]), u[i], 0};
   }
-  const PackInput xin{x, k, 0, r > 0 ? n_proj : 0};
-  e = launch_pack(&xin, 1, act_f32, t, 0, r, prods, xb, 0, s);
-  if (e == hipSuccess) e = launch_product_reduce(prods, r > 0 ? n_proj : 0, t, r, s);
+  // with every u given (MSQ_U_GIVEN), the pass only packs x
+  const bool u_given = cfg.flags & MSQ_U_GIVEN;
+  const int rp = u_given ? 0 : r;
+  const PackInput xin{x, k, 0, rp > 0 ? n_proj : 0};
+  e = launch_pack(&xin, 1, act_f32, t, 0, rp, prods, xb, 0, s);
+  if (e == hipSuccess) e = launch_product_reduce(prods, rp > 0 ? n_proj : 0, t, rp, s);
   float* part = (float*)(ws + p.off_part);
   size_t part_off[GEMM_MAX_SEGS];
   if (e == hipSuccess) {

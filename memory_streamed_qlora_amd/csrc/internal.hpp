@@ -203,9 +203,9 @@ struct SmallLinear {
 };
 bool small_path_fits(int64_t t, int64_t k, int64_t n, int r);
 // y = [residual +] (x W^T + bias + lscale u B^T) and u = drop(x) A^T (u may be null);
-// u_only: u alone (y, bias, residual unused).
+// u_only: u alone (y, bias, residual unused); u_given: u holds u, read instead of formed.
 hipError_t launch_small_fwd(const SmallLinear& L, const void* x, const uint16_t* bias, const void* residual, void* y,
-                            float* u, bool u_only, hipStream_t s);
+                            float* u, bool u_only, bool u_given, hipStream_t s);
 // dx = [dx +] (dy W + keep * sigma * (du A)) with du = lscale dy B, written to du (may be
 // null).
 hipError_t launch_small_bwd(const SmallLinear& L, const void* dy, void* dx, int accumulate, float* du, hipStream_t s);

@@ -140,7 +140,7 @@ struct SmallFwdArgs {
   int64_t T, K, N;
   int r;
   float lscale;
-  int out_f32, u_only;
+  int out_f32, u_only, u_given;  // u_given: u holds u (read, not written)
   Dropout d;
   Nf4Lut lut;
 };
@@ -350,13 +350,20 @@ __global__ __launch_bounds__(256) void small_fwd(SmallFwdArgs a) {
   };
   f32x16_t y, uf;
   const float usig = d.threshold != 0u ? d.sigma : 1.0f;
+  const int64_t rb = m0 + 32 * oi;  // first token row of the block
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     y[v] = wsum(oi + 2 * oj, v);
     uf[v] = lora ? usig * wsum(4 + oi, v) : 0.0f;
   }
-  const int64_t rb = m0 + 32 * oi;  // first token row of the block
-  if (lora && a.u && blockIdx.x == 0 && oj == 0 && rk_ok) {
+  if (lora && a.u_given) {  // u from an earlier call in place of the one formed above
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = rb + sm_row(v, hk);
+      uf[v] = (rk_ok && m < T) ? a.u[m * r + r32] : 0.0f;
+    }
+  }
+  if (lora && a.u && !a.u_given && blockIdx.x == 0 && oj == 0 && rk_ok) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int64_t m = rb + sm_row(v, hk);
@@ -696,9 +703,10 @@ bool small_path_fits(int64_t t, int64_t k, int64_t n, int r) {
 }
 
 hipError_t launch_small_fwd(const SmallLinear& L, const void* x, const uint16_t* bias, const void* residual, void* y,
-                            float* u, bool u_only, hipStream_t s) {
+                            float* u, bool u_only, bool u_given, hipStream_t s) {
   if (L.t == 0) return hipSuccess;
   if (L.r > SMALL_MAX_R || L.r % 4 || L.k % 64 || L.n % 64) return hipErrorInvalidValue;
+  if (u_given && (u_only || !u || L.r == 0)) return hipErrorInvalidValue;
   SmallFwdArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
@@ -718,6 +726,7 @@ hipError_t launch_small_fwd(const SmallLinear& L, const void* x, const uint16_t*
   a.lscale = L.lscale;
   a.out_f32 = L.out_f32;
   a.u_only = u_only;
+  a.u_given = u_given;
   a.d = L.drop;
   a.lut = nf4_lut();
   const dim3 grid(u_only ? 1u : (unsigned)(L.n / SM_C), (unsigned)((L.t + SM_T - 1) / SM_T));

@@ -175,7 +175,7 @@ def _base_args(base: Tuple[torch.Tensor, ...], k: int) -> Tuple[str, int, list]:
 
 
 def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype, u_only, residual,
-              noalloc=False, path="auto"):
+              noalloc=False, path="auto", u_given=False):
     t, k = x.shape
     _req(x, "x", x.dtype, (t, k))
     fmt, n, bptr = _base_args(base, k)
@@ -187,6 +187,10 @@ def _lora_fwd(base, x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream
     if r > 0:
         _req(A, "A", torch.float32, (r, k))
         _req(B, "B", torch.float32, (n, r))
+    if u_given:
+        if u_only or r == 0 or u_out is None:
+            raise ValueError("u_given needs r > 0 and the given u as u_out, and excludes u_only")
+        flags |= _abi.MSQ_U_GIVEN
     if u_only:
         if r == 0:
             raise ValueError("u_only needs r > 0")
@@ -257,14 +261,19 @@ def _lora_bwd(base, dy, x, A, B, cfg, key, u, dx, dx_accumulate, dA, dB, dAB_acc
 
 def lora_fwd_group(x: torch.Tensor, projs: Sequence[dict], cfg: Lora, want_u: bool = True,
                    workspace: Optional[Workspace] = None, stream=None,
-                   out_dtype: Optional[torch.dtype] = None):
+                   out_dtype: Optional[torch.dtype] = None, u_given: bool = False):
     """Up to three projections of the same x in one pass (lora_fwd_group): each dict has
-    base ((codes, absmax) or (w,)), bias, A, B, key and optionally residual.  Returns a
-    list of (y, u)."""
+    base ((codes, absmax) or (w,)), bias, A, B, key and optionally residual; with u_given,
+    also "u": the projection's u from an earlier call, used instead of forming it.  Returns
+    a list of (y, u)."""
     t, k = x.shape
     _req(x, "x", x.dtype, (t, k))
     out_dtype = out_dtype or x.dtype
     flags = _flags(x.dtype, out_dtype)
+    if u_given:
+        if cfg.r == 0:
+            raise ValueError("u_given needs r > 0")
+        flags |= _abi.MSQ_U_GIVEN
     if not 1 <= len(projs) <= 3:
         raise ValueError("a group has 1 to 3 projections")
     arr = (_abi.LoraProj * len(projs))()
@@ -281,7 +290,11 @@ def lora_fwd_group(x: torch.Tensor, projs: Sequence[dict], cfg: Lora, want_u: bo
             _req(pr["A"], "A", torch.float32, (r, k))
             _req(pr["B"], "B", torch.float32, (n, r))
         y = torch.empty((t, n), dtype=out_dtype, device=x.device)
-        u = torch.empty((t, r), dtype=torch.float32, device=x.device) if (want_u and r > 0) else None
+        if u_given:
+            u = pr["u"]
+            _req(u, "u", torch.float32, (t, r))
+        else:
+            u = torch.empty((t, r), dtype=torch.float32, device=x.device) if (want_u and r > 0) else None
         codes, absmax, w = (bptr + [None])[:3] if fmt == "nf4" else (None, None, bptr[0])
         arr[i] = _abi.LoraProj(n, codes, absmax, w, _ptr(bias), _ptr(res), _ptr(pr["A"]) if r > 0 else None,
                                _ptr(pr["B"]) if r > 0 else None, pr["key"], _ptr(y), _ptr(u))
@@ -353,15 +366,17 @@ def nf4_lora_fwd(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
                  u_out: Optional[torch.Tensor] = None, want_u: bool = True,
                  workspace: Optional[Workspace] = None, stream=None,
                  out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
-                 residual: Optional[torch.Tensor] = None, path: str = "auto"):
+                 residual: Optional[torch.Tensor] = None, path: str = "auto", u_given: bool = False):
     """y = [residual +] (x W^T + bias + (alpha/r) drop(x) A^T B^T), W the NF4 base.  Returns
     (y, u) (u None if not wanted).
 
     x may be bf16 or fp32; y is out_dtype (default: x's dtype, or y's if given).
     residual ([t, n], y's dtype) is added in the output pass, rounded as a separate add.
-    u_only: compute only u (y is None).  path: "auto" (by shape), "tiled" or "small"."""
+    u_only: compute only u (y is None).  u_given: u_out holds u from an earlier call with the
+    same x, A and key, used instead of forming it.  path: "auto" (by shape), "tiled" or
+    "small"."""
     return _lora_fwd((codes, absmax), x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype,
-                     u_only, residual, path=path)
+                     u_only, residual, path=path, u_given=u_given)
 
 
 def nf4_lora_fwd_noalloc(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,
@@ -369,12 +384,12 @@ def nf4_lora_fwd_noalloc(x: torch.Tensor, codes: torch.Tensor, absmax: torch.Ten
                          cfg: Lora, key: RngKey, y: Optional[torch.Tensor] = None,
                          u_out: Optional[torch.Tensor] = None, want_u: bool = True, stream=None,
                          out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
-                         residual: Optional[torch.Tensor] = None, path: str = "auto"):
+                         residual: Optional[torch.Tensor] = None, path: str = "auto", u_given: bool = False):
     """nf4_lora_fwd with the library's static per-GPU scratch in place of a workspace (the
     entry point for callers that cannot allocate).  Pass y (and u_out) to allocate nothing
     here either."""
     return _lora_fwd((codes, absmax), x, bias, A, B, cfg, key, y, u_out, want_u, None, stream, out_dtype,
-                     u_only, residual, noalloc=True, path=path)
+                     u_only, residual, noalloc=True, path=path, u_given=u_given)
 
 
 def bf16_lora_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], A: Optional[torch.Tensor],
@@ -382,10 +397,10 @@ def bf16_lora_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor]
                   u_out: Optional[torch.Tensor] = None, want_u: bool = True,
                   workspace: Optional[Workspace] = None, stream=None,
                   out_dtype: Optional[torch.dtype] = None, u_only: bool = False,
-                  residual: Optional[torch.Tensor] = None, path: str = "auto"):
+                  residual: Optional[torch.Tensor] = None, path: str = "auto", u_given: bool = False):
     """nf4_lora_fwd over a frozen base kept in bf16, w [n, k]."""
     return _lora_fwd((w,), x, bias, A, B, cfg, key, y, u_out, want_u, workspace, stream, out_dtype, u_only,
-                     residual, path=path)
+                     residual, path=path, u_given=u_given)
 
 
 def nf4_lora_bwd(dy: torch.Tensor, x: torch.Tensor, codes: torch.Tensor, absmax: torch.Tensor,

@@ -37,7 +37,7 @@ from __future__ import annotations
 import math
 import time
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -132,12 +132,16 @@ def _bwd(base, dy, x, A, B, cfg, key, **kw):
 
 class _LoraLinear(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, A, B, base, bias, residual, cfg, key, value_unused):
+    def forward(ctx, x, A, B, base, bias, residual, cfg, key, value_unused, u_given):
         if value_unused:
             # selective recompute: the backward reads only x and u, never y, so the
-            # frozen-base product is skipped and y is a zero placeholder
-            _, u = _fwd(base, x, bias, A, B, cfg, key, u_only=True)
+            # frozen-base product is skipped and y is a zero placeholder (with u kept
+            # from the first forward, nothing runs at all)
+            u = u_given if u_given is not None else _fwd(base, x, bias, A, B, cfg, key, u_only=True)[1]
             y = x.new_zeros(()).expand(x.shape[0], base[0].shape[0])
+        elif u_given is not None:
+            # u kept from the first forward (the same bits the product would give again)
+            y, u = _fwd(base, x, bias, A, B, cfg, key, u_out=u_given, u_given=True, residual=residual)
         else:
             y, u = _fwd(base, x, bias, A, B, cfg, key, want_u=True, residual=residual)
         ctx.save_for_backward(x, A, B, u)
@@ -151,17 +155,24 @@ class _LoraLinear(torch.autograd.Function):
         dx, dA, dB = _bwd(ctx.base, dy, x, A, B, ctx.cfg, ctx.key, u=u)
         # y = residual + (...): the residual's gradient is dy itself
         dres = dy if ctx.needs_input_grad[5] else None
-        return dx, dA, dB, None, None, dres, None, None, None
+        return dx, dA, dB, None, None, dres, None, None, None, None
 
 
 def lora_linear(x, A, B, base: Tuple[torch.Tensor, ...], bias, cfg: ops.Lora, key,
-                value_unused: bool = False, residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+                value_unused: bool = False, residual: Optional[torch.Tensor] = None,
+                u_keep: Optional[list] = None, u_given: Optional[torch.Tensor] = None) -> torch.Tensor:
     """[residual +] the projection over an NF4 (codes, absmax) or bf16 (w,) frozen base;
-    with a residual the add happens in the library's output pass."""
+    with a residual the add happens in the library's output pass.  u_keep (a list, outside
+    autograd): u is appended to it; u_given: u from an earlier forward of the same x, used
+    instead of forming it."""
     if torch.is_grad_enabled() and (x.requires_grad or A.requires_grad or B.requires_grad or
                                     (residual is not None and residual.requires_grad)):
-        return _LoraLinear.apply(x, A, B, base, bias, residual, cfg, key, value_unused and cfg.r > 0)
-    y, _ = _fwd(base, x, bias, A, B, cfg, key, want_u=False, residual=residual)
+        return _LoraLinear.apply(x, A, B, base, bias, residual, cfg, key, value_unused and cfg.r > 0,
+                                 u_given if cfg.r > 0 else None)
+    want = u_keep is not None and cfg.r > 0
+    y, u = _fwd(base, x, bias, A, B, cfg, key, want_u=want, residual=residual)
+    if want:
+        u_keep.append(u)
     return y
 
 
@@ -180,10 +191,15 @@ class _LoraLinearGroup(torch.autograd.Function):
     GEMM over their concatenated rows, each projection's dA / dB as in a single call)."""
 
     @staticmethod
-    def forward(ctx, x, specs, cfg, *AB):
+    def forward(ctx, x, specs, cfg, us_given, *AB):
         projs = [{"base": sp.base, "bias": sp.bias, "key": sp.key, "A": AB[2 * i], "B": AB[2 * i + 1]}
                  for i, sp in enumerate(specs)]
-        outs = ops.lora_fwd_group(x, projs, cfg, want_u=True)
+        if us_given is not None:
+            for pr, u in zip(projs, us_given):
+                pr["u"] = u
+            outs = ops.lora_fwd_group(x, projs, cfg, u_given=True)
+        else:
+            outs = ops.lora_fwd_group(x, projs, cfg, want_u=True)
         ctx.save_for_backward(x, *AB, *[u for _, u in outs])
         ctx.specs, ctx.cfg = specs, cfg
         return tuple(y for y, _ in outs)
@@ -196,17 +212,23 @@ class _LoraLinearGroup(torch.autograd.Function):
         projs = [{"base": sp.base, "A": AB[2 * i], "B": AB[2 * i + 1], "key": sp.key, "dy": dys[i].contiguous(),
                   "u": us[i]} for i, sp in enumerate(ctx.specs)]
         dx, dAB = ops.lora_bwd_group(x, projs, ctx.cfg)
-        return (dx, None, None, *[g for pair in dAB for g in pair])
+        return (dx, None, None, None, *[g for pair in dAB for g in pair])
 
 
-def lora_linear_group(x, specs, As, Bs, cfg: ops.Lora):
-    """The projections of one input x, grouped: a tuple of outputs."""
+def lora_linear_group(x, specs, As, Bs, cfg: ops.Lora, u_keep: Optional[list] = None,
+                      us_given: Optional[Sequence[torch.Tensor]] = None):
+    """The projections of one input x, grouped: a tuple of outputs.  u_keep / us_given as
+    in lora_linear, one u per projection."""
     if torch.is_grad_enabled() and (x.requires_grad or any(a.requires_grad or b.requires_grad
                                                            for a, b in zip(As, Bs))):
         AB = [t for pair in zip(As, Bs) for t in pair]
-        return _LoraLinearGroup.apply(x, specs, cfg, *AB)
+        return _LoraLinearGroup.apply(x, specs, cfg, tuple(us_given) if (us_given and cfg.r > 0) else None, *AB)
     projs = [{"base": sp.base, "bias": sp.bias, "key": sp.key, "A": a, "B": b} for sp, a, b in zip(specs, As, Bs)]
-    return tuple(y for y, _ in ops.lora_fwd_group(x, projs, cfg, want_u=False))
+    want = u_keep is not None and cfg.r > 0
+    outs = ops.lora_fwd_group(x, projs, cfg, want_u=want)
+    if want:
+        u_keep.extend(u for _, u in outs)
+    return tuple(y for y, _ in outs)
 
 
 class _SwiGLU(torch.autograd.Function):
@@ -347,12 +369,17 @@ class Stack:
                  n_slots: int = 2, glue: str = "native", base: str = "nf4", group: bool = True,
                  layer_release: bool = True, lm_stream: Optional[bool] = None, n_copy_streams: int = 2,
                  keep_grads: bool = True, checkpoint_every: int = 1, offload_bounds: bool = False,
-                 device_bounds: int = 4):
+                 device_bounds: int = 4, keep_u: bool = True):
         assert mode in ("streamed", "resident")
         assert glue in ("native", "torch")
         self.shape, self.seq, self.mode, self.seed = shape, seq, mode, seed
         self.glue = glue
         self.group = group
+        # keep each projection's u from the step's first forward for the recompute (T x r
+        # fp32 per projection: 7 x 32 KB per layer at 512 tokens), which then skips the
+        # rank-r products
+        self.keep_u = keep_u
+        self._u_kept: Dict[Tuple[int, int], Dict[str, torch.Tensor]] = {}
         self.layer_release = layer_release
         # the frozen lm_head in pinned host memory, streamed by the loss (streamed stacks by
         # default); False keeps it on the device
@@ -606,35 +633,53 @@ class Stack:
         return ((views[(proj, "w")],) if self.layout.base == "bf16" else
                 (views[(proj, "codes")], views[(proj, "absmax")]))
 
-    def _lin_group(self, x, l, views, projs, step, micro):
-        """Projections of one input: one grouped pass (group=True) or one call each."""
+    def _lin_group(self, x, l, views, projs, step, micro, keep=None, given=None):
+        """Projections of one input: one grouped pass (group=True) or one call each.  keep:
+        a dict that receives each projection's u; given: such a dict from the first forward."""
         if not self.group:
-            return tuple(self._lin(x, l, views, p, step, micro) for p in projs)
+            return tuple(self._lin(x, l, views, p, step, micro, keep=keep, given=given) for p in projs)
         specs = [_Spec(self._base(views, p), views.get((p, "bias")), ops.rng_key(self.seed, step, micro, l, PROJ_ID[p]))
                  for p in projs]
-        return lora_linear_group(x, specs, [self.A[l][p] for p in projs], [self.B[l][p] for p in projs], self.cfg)
+        uk = [] if keep is not None else None
+        ys = lora_linear_group(x, specs, [self.A[l][p] for p in projs], [self.B[l][p] for p in projs], self.cfg,
+                               u_keep=uk, us_given=[given[p] for p in projs] if given else None)
+        if uk:
+            keep.update(zip(projs, uk))
+        return ys
 
-    def _lin(self, x, l, views, proj, step, micro, value_unused=False, residual=None):
+    def _lin(self, x, l, views, proj, step, micro, value_unused=False, residual=None, keep=None, given=None):
         key = ops.rng_key(self.seed, step, micro, l, PROJ_ID[proj])
         bias = views.get((proj, "bias"))
         base = self._base(views, proj)
+        uk = [] if keep is not None else None
+        ug = given[proj] if given else None
         if residual is not None and self.glue == "torch":
-            return residual + lora_linear(x, self.A[l][proj], self.B[l][proj], base, bias, self.cfg, key,
-                                          value_unused)
-        return lora_linear(x, self.A[l][proj], self.B[l][proj], base, bias, self.cfg, key, value_unused, residual)
+            y = residual + lora_linear(x, self.A[l][proj], self.B[l][proj], base, bias, self.cfg, key,
+                                       value_unused, u_keep=uk, u_given=ug)
+        else:
+            y = lora_linear(x, self.A[l][proj], self.B[l][proj], base, bias, self.cfg, key, value_unused, residual,
+                            u_keep=uk, u_given=ug)
+        if uk:
+            keep[proj] = uk[0]
+        return y
 
     def layer_forward(self, h: torch.Tensor, l: int, views, step: int, micro: int = 0,
-                      recompute: bool = False) -> torch.Tensor:
+                      recompute: bool = False, keep_u: bool = False) -> torch.Tensor:
         """Activations stay fp32; the library rounds them to bf16 only as MFMA operands.
 
         recompute=True (the backward's rerun, with autograd recording): the layer's
         output value is never read -- only its graph is -- so the down projection's
-        frozen-base product is skipped and the returned value is not the layer output."""
+        frozen-base product is skipped and the returned value is not the layer output.
+        keep_u (the step's first forward): each projection's u = drop(x) A^T is kept until
+        the recompute, which then uses it in place of forming it again (the same bits: the
+        same kernels on the same inputs)."""
         sh = self.shape
         T = h.shape[0]
+        keep = {} if (keep_u and self.keep_u and self.cfg.r > 0) else None
+        given = self._u_kept.pop((l, micro), None) if recompute else None
         norm = rmsnorm_native if self.glue == "native" else rmsnorm
         xn = norm(h, self.ln1[l])
-        q, k, v = self._lin_group(xn, l, views, ("q", "k", "v"), step, micro)
+        q, k, v = self._lin_group(xn, l, views, ("q", "k", "v"), step, micro, keep, given)
         q = q.view(T, sh.heads, sh.head_dim)
         k = k.view(T, sh.kv_heads, sh.head_dim)
         v = v.view(T, sh.kv_heads, sh.head_dim)
@@ -644,11 +689,15 @@ class Stack:
         else:
             q, k = rope(q, cos, sin), rope(k, cos, sin)
         att = causal_gqa_attention(q, k, v, self._mask_rep(T))
-        h1 = self._lin(att, l, views, "o", step, micro, residual=h)
+        h1 = self._lin(att, l, views, "o", step, micro, residual=h, keep=keep, given=given)
         xn2 = norm(h1, self.ln2[l])
-        g, u = self._lin_group(xn2, l, views, ("gate", "up"), step, micro)
+        g, u = self._lin_group(xn2, l, views, ("gate", "up"), step, micro, keep, given)
         a = _SwiGLU.apply(g, u, True) if self.glue == "native" else torch.nn.functional.silu(g) * u
-        return self._lin(a, l, views, "down", step, micro, value_unused=recompute, residual=h1)
+        out = self._lin(a, l, views, "down", step, micro, value_unused=recompute, residual=h1, keep=keep,
+                        given=given)
+        if keep is not None:
+            self._u_kept[(l, micro)] = keep
+        return out
 
     # -- base residency --------------------------------------------------------------
     def _views(self, l: int):
@@ -678,6 +727,7 @@ class Stack:
         L = self.shape.layers
         M = len(toks)
         wins = self._windows()
+        self._u_kept = {}
         streamed = self.mode == "streamed"
         # the streamed lm_head's two-chunk ring, made before the forward's work so that its
         # first copies need not wait for the compute stream to reach the loss, and dropped
@@ -699,7 +749,7 @@ class Stack:
                             views[l] = self._views(l)
                         bounds[m].append(self._keep_bound(hs[m], m, l, M) if l % self.checkpoint_every == 0
                                          else None)
-                        hs[m] = self.layer_forward(hs[m], l, views[l], step, micros[m])
+                        hs[m] = self.layer_forward(hs[m], l, views[l], step, micros[m], keep_u=True)
                         if streamed and m == M - 1 and self.layer_release:
                             self.window.release_layer(l)
                 if streamed and not self.layer_release:
@@ -753,6 +803,7 @@ class Stack:
                 self.window.release(w)
             if streamed and wi + ahead < len(rw):
                 self.window.prefetch(rw[wi + ahead])
+        self._u_kept = {}
         return losses
 
     def _keep_bound(self, h: torch.Tensor, m: int, l: int, M: int):

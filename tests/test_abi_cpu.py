@@ -116,7 +116,7 @@ def test_path_flags():
     assert L.nf4_lora_fwd(*args(33, abi.MSQ_PATH_SMALL)) == abi.MSQ_E_SHAPE
     assert "r <= 32" in _err()
     assert L.nf4_lora_fwd(*args(6, abi.MSQ_PATH_SMALL)) == abi.MSQ_E_SHAPE
-    assert L.nf4_lora_fwd(*args(16, 32)) == abi.MSQ_E_INVAL                 # an unknown bit
+    assert L.nf4_lora_fwd(*args(16, 64)) == abi.MSQ_E_INVAL                 # an unknown bit
     assert "unknown flags" in _err()
     key = abi.RngKey(0, 0, 0, 0, 0)
     one = (abi.LoraProj * 1)(abi.LoraProj(128, FAKE, FAKE, None, None, None, FAKE, FAKE, key, FAKE, None))
@@ -411,3 +411,30 @@ def test_missing_library_raises_on_use(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "libmsq.so not found" in r.stderr
+
+
+def test_u_given_flag():
+    """MSQ_U_GIVEN: a forward flag that needs r > 0 and the given u, and excludes
+    MSQ_U_ONLY; a group needs every projection's u."""
+    L = abi.lib()
+    need = L.nf4_lora_workspace_size(8, 128, 128, 16)
+    G = abi.MSQ_U_GIVEN
+    args = lambda r, flags, u: (FAKE, 8, 128, 128, FAKE, FAKE, None, None, FAKE, FAKE,  # noqa: E731
+                                abi.LoraCfg(r, 32.0, 0.0, flags), abi.RngKey(0, 0, 0, 0, 0), FAKE, u,
+                                FAKE, need, None)
+    assert L.nf4_lora_fwd(*args(16, G | abi.MSQ_U_ONLY, FAKE)) == abi.MSQ_E_INVAL
+    assert "nothing to compute" in _err()
+    assert L.nf4_lora_fwd(*args(0, G, FAKE)) == abi.MSQ_E_INVAL
+    assert "r > 0" in _err()
+    assert L.nf4_lora_fwd(*args(16, G, None)) == abi.MSQ_E_INVAL
+    assert "u_out" in _err()
+    bneed = L.nf4_lora_workspace_size(8, 128, 128, 16)
+    assert L.nf4_lora_bwd(FAKE, FAKE, 8, 128, 128, FAKE, FAKE, FAKE, FAKE, abi.LoraCfg(16, 32.0, 0.0, G),
+                          abi.RngKey(0, 0, 0, 0, 0), FAKE, FAKE, 0, FAKE, FAKE, 0, FAKE, bneed, None) == abi.MSQ_E_INVAL
+    assert "forward flags" in _err()
+    key = abi.RngKey(0, 0, 0, 0, 0)
+    two = (abi.LoraProj * 2)(abi.LoraProj(128, FAKE, FAKE, None, None, None, FAKE, FAKE, key, FAKE, FAKE),
+                             abi.LoraProj(64, FAKE, FAKE, None, None, None, FAKE, FAKE, key, FAKE, None))
+    gneed = L.lora_group_workspace_size(8, 128, two, 2, 16)
+    assert L.lora_fwd_group(FAKE, 8, 128, two, 2, abi.LoraCfg(16, 32.0, 0.0, G), FAKE, gneed, None) == abi.MSQ_E_INVAL
+    assert "every projection's u_out" in _err()
