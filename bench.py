@@ -305,19 +305,95 @@ def rocprof_summary(d: str, timed: int = 5, total: int = 7, first: int = -1) -> 
         cols = list(rows[0].keys())
         size_col = next((c for c in cols if c.lower() in ("bytes", "size", "copy_bytes")), None)
         print(f"### memory copies ({os.path.relpath(path, d)})\n\ncolumns: {', '.join(cols)}\n")
-        print("| direction | copies | total GB | busy ms | avg GB/s while copying | first-to-last span ms |")
-        print("|---|---|---|---|---|---|")
+        print("| direction | copies | total GB | summed copy ms | union busy ms | avg GB/s (union) | first-to-last span ms |")
+        print("|---|---|---|---|---|---|---|")
         by = {}
         for r in rows:
             by.setdefault(r.get("Direction", r.get("Kind", "?")), []).append(r)
+
+        def union_ms(iv):
+            iv = sorted(iv)
+            tot, (cs, ce) = 0, iv[0]
+            for a, b in iv[1:]:
+                if a > ce:
+                    tot, cs, ce = tot + ce - cs, a, b
+                else:
+                    ce = max(ce, b)
+            return (tot + ce - cs) / 1e6
+
         for direc, rs in sorted(by.items()):
-            t0 = [int(r["Start_Timestamp"]) for r in rs]
-            t1 = [int(r["End_Timestamp"]) for r in rs]
-            busy = sum(b - a for a, b in zip(t0, t1)) / 1e6
+            iv = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rs]
+            busy = sum(b - a for a, b in iv) / 1e6
+            ubusy = union_ms(iv)
             gb = sum(float(r[size_col]) for r in rs) / 1e9 if size_col else float("nan")
-            rate = gb / (busy / 1e3) if busy > 0 else float("nan")
-            print(f"| {direc} | {len(rs)} | {gb:.2f} | {busy:.1f} | {rate:.1f} | {(max(t1) - min(t0)) / 1e6:.1f} |")
+            rate = gb / (ubusy / 1e3) if ubusy > 0 else float("nan")
+            span = (max(b for _, b in iv) - min(a for a, _ in iv)) / 1e6
+            print(f"| {direc} | {len(rs)} | {gb:.2f} | {busy:.1f} | {ubusy:.1f} | {rate:.1f} | {span:.1f} |")
         print()
+        # per stream, in start order: copy durations (the trace holds no sizes)
+        print("| stream | copies | ms per copy: min | median | max |")
+        print("|---|---|---|---|---|")
+        bys = {}
+        for r in rows:
+            bys.setdefault(r.get("Stream_Id", "?"), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+        for sid, ds in sorted(bys.items()):
+            ds.sort()
+            print(f"| {sid} | {len(ds)} | {ds[0]:.2f} | {ds[len(ds) // 2]:.2f} | {ds[-1]:.2f} |")
+        print()
+    return 0
+
+
+def window_copies(layers: int = 16, slots: int = 8, steps: int = 2) -> int:
+    """The window's copies alone, for a profiler's memory-copy trace: `layers` pinned blobs of
+    the Qwen2.5-32B layer size (274.28 MB) streamed through one-layer windows in `slots`
+    slots on the stack's two copy streams, in a step's order (forward, then backward), each
+    layer acquired and released on the compute stream with no work in between.  The H2D
+    ceiling probes run first.  Prints one JSON line: bytes copied, copy busy time and GB/s,
+    against the ceilings."""
+    import torch
+
+    from memory_streamed_qlora_amd import ops, stack as S
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    cs = S.copy_streams(dev, 2)
+    ceiling = h2d_ceiling_gbps(torch, cs[0])
+    ceiling_busy = h2d_ceiling_under_compute_gbps(torch, cs[0])
+    layout = S.LayerLayout(S.QWEN25_32B, "nf4")
+    blobs = [ops.pinned_empty(layout.nbytes) for _ in range(layers)]
+    for b in blobs:
+        b.fill_(3)
+    w = ops.BlockStreamWindow(blobs, 1, slots, copy_streams=cs)
+    order = list(range(layers))
+    torch.cuda.synchronize()
+    s0 = w.stats()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for seq in (order, order[::-1]):
+            for l in seq[:slots]:
+                w.prefetch(l)
+            for i, l in enumerate(seq):
+                w.acquire(l)
+                w.release_layer(l)
+                if i + slots < len(seq):
+                    w.prefetch(seq[i + slots])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    s1 = w.stats()
+    w.close()
+    copied = s1["bytes_copied"] - s0["bytes_copied"]
+    busy = s1["busy_ms"] - s0["busy_ms"]
+    out = {"window_copies": {"layers": layers, "slots": slots, "copy_streams": 2, "steps": steps,
+                             "blob_MB": round(layout.nbytes / 1e6, 2), "bytes_copied": copied,
+                             "windows_copied": s1["windows_copied"] - s0["windows_copied"],
+                             "windows_reused": s1["windows_reused"] - s0["windows_reused"],
+                             "wall_s": round(dt, 3), "copy_busy_ms": round(busy, 1),
+                             "GBps_while_copying": round(copied / (busy * 1e-3) / 1e9, 1) if busy else None,
+                             "GBps_wall": round(copied / dt / 1e9, 1),
+                             "ceiling_GBps": round(ceiling, 1), "ceiling_under_compute_GBps": round(ceiling_busy, 1)}}
+    log(f"window copies: {copied / 1e9:.2f} GB in {dt * 1e3:.1f} ms ({out['window_copies']['GBps_wall']} GB/s; "
+        f"{out['window_copies']['GBps_while_copying']} GB/s while copying), ceiling {ceiling:.1f} GB/s")
+    print(json.dumps(out))
     return 0
 
 
@@ -570,6 +646,9 @@ def main() -> int:
                     help="keep the frozen lm_head on the device in the streamed step (instead of streaming it)")
     ap.add_argument("--skinny", action="store_true",
                     help="only time the small (HBM-bound) shapes: the 896x896 linear and the 0.5B block's projections")
+    ap.add_argument("--window-copies", action="store_true",
+                    help="only stream 32B-sized layer blobs through the window (no compute), e.g. under a "
+                         "profiler's memory-copy trace")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only compare the NF4 GEMMs with hipBLASLt's bf16 GEMM at the step's shapes")
     args = ap.parse_args()
@@ -580,6 +659,8 @@ def main() -> int:
         return vendor_gemm()
     if args.skinny:
         return skinny()
+    if args.window_copies:
+        return window_copies()
 
     import statistics
 
