@@ -4,6 +4,7 @@ Each test checks the oracle against something other than itself: a second
 inverse-normal routine, published codebook values, exact rational brute force,
 closed-form special cases and an independently written rounding path.
 """
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -12,15 +13,25 @@ import scipy.special as sp
 
 from oracle import nf4
 
-# NF4 values printed in the QLoRA paper (Dettmers et al. 2023, appendix listing
-# the NormalFloat data type).  They were computed from fp32 probabilities, so
-# they agree with a float64 construction to a few fp32 ulps, not bitwise.
-QLORA_PUBLISHED = [
-    -1.0, -0.6961928009986877, -0.5250730514526367, -0.39491748809814453,
-    -0.28444138169288635, -0.18477343022823334, -0.09105003625154495, 0.0,
-    0.07958029955625534, 0.16093020141124725, 0.24611230194568634, 0.33791524171829224,
-    0.44070982933044434, 0.5626170039176941, 0.7229568362236023, 1.0,
-]
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "nf4_levels_qlora.txt")
+
+
+def _published_levels():
+    """The NF4 values printed in the QLoRA paper (Dettmers et al. 2023, the appendix that
+    lists the NormalFloat data type), from tests/golden.  They were computed from fp32
+    probabilities, so they agree with a float64 construction to a few fp32 ulps, not
+    bitwise."""
+    vals = {}
+    for line in open(GOLDEN):
+        if line.startswith("#") or not line.strip():
+            continue
+        i, v = line.split()
+        vals[int(i)] = float(v)
+    assert sorted(vals) == list(range(16))
+    return [vals[i] for i in range(16)]
+
+
+QLORA_PUBLISHED = _published_levels()
 
 
 def test_codebook_invariants():

@@ -1,20 +1,28 @@
 """Pins for the oracle's counter-based dropout (CPU only)."""
+import os
 from fractions import Fraction
 
 import numpy as np
 
 from oracle import philox
 
-# Known-answer vectors for Philox4x32-10 distributed with the authors' Random123
-# library (Salmon et al., SC'11): (counter, key) -> output.
-KAT = [
-    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
-     (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
-    ((0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF), (0xFFFFFFFF, 0xFFFFFFFF),
-     (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
-    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
-     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
-]
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
+
+
+def _kat():
+    """Known-answer vectors of Philox4x32-10 distributed with its authors' Random123
+    library (Salmon et al., SC'11), from tests/golden: (counter, key) -> output."""
+    out = []
+    for line in open(GOLDEN):
+        if line.startswith("#") or not line.strip():
+            continue
+        w = [int(x, 16) for x in line.split()]
+        assert len(w) == 10
+        out.append((tuple(w[0:4]), tuple(w[4:6]), tuple(w[6:10])))
+    return out
+
+
+KAT = _kat()
 
 
 def _round_f32(q: Fraction) -> np.float32:
@@ -30,6 +38,7 @@ def _round_f32(q: Fraction) -> np.float32:
 
 
 def test_known_answers():
+    assert len(KAT) == 3
     for ctr, key, want in KAT:
         got = philox.philox4x32_10(ctr, key)
         assert tuple(int(g) for g in got) == want
