@@ -11,8 +11,8 @@ batch 1 x 512 random tokens over a 152064-entry vocabulary; one AdamW step per
 training step.  A step is the whole hot path: forward with streaming, loss, backward
 with reload + recompute, AdamW.  tokens/s = 512 * steps / timed seconds.
 
-Prints one JSON line (see the fields below); --gpus N > 1 exits: this build runs on
-one GPU.  --vendor-gemm instead compares the library's NF4 GEMMs at the step's projection
+Prints one JSON line (see the fields below); --gpus N > 1 exits: the library's path
+runs on one GPU (no collectives).  --vendor-gemm instead compares the library's NF4 GEMMs at the step's projection
 shapes with the vendor library's plain bf16 GEMM (torch.matmul -> hipBLASLt) of the same
 dimensions.
 """
@@ -653,7 +653,7 @@ def main() -> int:
                     help="only compare the NF4 GEMMs with hipBLASLt's bf16 GEMM at the step's shapes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs the hot path on one GPU only; --gpus must be 1", file=sys.stderr)
+        print("bench.py: the hot path runs on one GPU (the library has no multi-GPU path); --gpus must be 1", file=sys.stderr)
         return 2
     if args.vendor_gemm:
         return vendor_gemm()
